@@ -1,0 +1,221 @@
+"""fp64 CPU oracle (ctypes front-end of ``oracle/oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
+and the CPU-baseline leg of ``bench.py``. The HIP product package never
+imports it, and it imports nothing from the product package.
+
+Every function evaluates the plain per-timestep recurrence in double precision
+(see the header of ``oracle.c`` for the definition and the page citations).
+Inputs are the float32 storage values both sides read (bf16 inputs arrive as
+their exact float32 upcast).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+_f32p = ctypes.POINTER(ctypes.c_float)
+_f64p = ctypes.POINTER(ctypes.c_double)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_i64 = ctypes.c_int64
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, no fast-math, OpenMP)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fno-fast-math", "-fopenmp", "-fPIC", "-shared",
+                               "-std=c11", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if _LIB_OVERRIDE:
+            L = ctypes.CDLL(_LIB_OVERRIDE)
+        else:
+            build(force=False)
+            L = ctypes.CDLL(_LIB)
+        L.oracle_selective_scan_f64.restype = ctypes.c_int
+        L.oracle_selective_scan_f64.argtypes = [
+            _i64, _i64, _i64, _i64, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p,
+            _f64p, ctypes.c_int, _i64p, _i64, _f64p, _f64p]
+        L.oracle_ssd_f64.restype = ctypes.c_int
+        L.oracle_ssd_f64.argtypes = [
+            _i64, _i64, _i64, _i64, _i64, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p,
+            _f32p, _f64p, ctypes.c_int, _i64p, _i64, _f64p, _f64p]
+        L.oracle_causal_conv1d_f64.restype = ctypes.c_int
+        L.oracle_causal_conv1d_f64.argtypes = [_i64, _i64, _i64, _i64, _f32p, _f32p, _f32p,
+                                               ctypes.c_int, _f64p]
+        L.oracle_num_threads.restype = ctypes.c_int
+        L.oracle_set_num_threads.argtypes = [ctypes.c_int]
+        _lib = L
+    return _lib
+
+
+class using_library:
+    """Context manager that points this module at another build of the oracle
+    (the mutation tests load deliberately broken copies through it)."""
+
+    def __init__(self, path: str):
+        self.path = path
+
+    def __enter__(self):
+        global _lib
+        self.saved = lib()
+        _lib = None
+        globals()["_LIB_OVERRIDE"] = self.path
+        return self
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self.saved
+        globals()["_LIB_OVERRIDE"] = None
+        return False
+
+
+_LIB_OVERRIDE = None
+
+
+def num_threads() -> int:
+    return lib().oracle_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    lib().oracle_set_num_threads(int(n))
+
+
+def _f64(a, shape=None):
+    if a is None:
+        return None, None
+    arr = np.ascontiguousarray(a, dtype=np.float64)
+    if shape is not None and arr.shape != tuple(shape):
+        raise ValueError("oracle input has shape %s, expected %s" % (arr.shape, tuple(shape)))
+    return arr, arr.ctypes.data_as(_f64p)
+
+
+def _f32(a, shape=None):
+    if a is None:
+        return None, None
+    arr = np.ascontiguousarray(a, dtype=np.float32)
+    if shape is not None and arr.shape != tuple(shape):
+        raise ValueError("oracle input has shape %s, expected %s" % (arr.shape, tuple(shape)))
+    return arr, arr.ctypes.data_as(_f32p)
+
+
+def selective_scan(x, delta, A, Bm, Cm, Dskip=None, z=None, delta_bias=None, h0=None,
+                   delta_softplus: bool = True, channels: Optional[Sequence[int]] = None):
+    """Reference selective scan in fp64.
+
+    Shapes: x, delta, z (batch, L, D); Bm, Cm (batch, L, N); A (D, N);
+    Dskip, delta_bias (D,); h0 (batch, D, N).
+    Returns ``(y, h_final)``. With ``channels`` (ids ``b*D + d``) the outputs are
+    ``y (len(channels), L)`` and ``h_final (len(channels), N)``; otherwise
+    ``y (batch, L, D)`` and ``h_final (batch, D, N)``.
+    """
+    batch, L, D = np.shape(x)
+    N = np.shape(A)[1]
+    keep = []
+    xs, xp = _f32(x, (batch, L, D)); keep.append(xs)
+    ds, dp = _f32(delta, (batch, L, D)); keep.append(ds)
+    zs, zp = _f32(z, (batch, L, D)); keep.append(zs)
+    bs, bp = _f32(Bm, (batch, L, N)); keep.append(bs)
+    cs, cp = _f32(Cm, (batch, L, N)); keep.append(cs)
+    as_, ap = _f32(A, (D, N)); keep.append(as_)
+    bis, bip = _f32(delta_bias, (D,)); keep.append(bis)
+    dks, dkp = _f32(Dskip, (D,)); keep.append(dks)
+    hs, hp = _f64(h0, (batch, D, N)); keep.append(hs)
+    if channels is None:
+        chp, nch = None, 0
+        y = np.empty((batch, L, D), dtype=np.float64)
+        hf = np.empty((batch, D, N), dtype=np.float64)
+    else:
+        ch = np.ascontiguousarray(channels, dtype=np.int64)
+        keep.append(ch)
+        chp, nch = ch.ctypes.data_as(_i64p), len(ch)
+        y = np.empty((nch, L), dtype=np.float64)
+        hf = np.empty((nch, N), dtype=np.float64)
+    rc = lib().oracle_selective_scan_f64(batch, L, D, N, xp, dp, zp, bp, cp, ap, bip, dkp, hp,
+                                         int(bool(delta_softplus)), chp, nch,
+                                         y.ctypes.data_as(_f64p), hf.ctypes.data_as(_f64p))
+    if rc != 0:
+        raise ValueError("oracle_selective_scan_f64 rejected its arguments")
+    return y, hf
+
+
+def ssd(x, dt, A, Bm, Cm, Dskip=None, z=None, dt_bias=None, h0=None,
+        dt_softplus: bool = True, channels: Optional[Sequence[int]] = None):
+    """Reference scalar-A (SSD) form in fp64, evaluated as the plain recurrence.
+
+    Shapes: x, z (batch, L, H, P); dt (batch, L, H); A, Dskip, dt_bias (H,);
+    Bm, Cm (batch, L, N); h0 (batch, H, P, N). ``channels`` are ids
+    ``(b*H + h)*P + p``; outputs as for :func:`selective_scan`.
+    """
+    batch, L, H, P = np.shape(x)
+    N = np.shape(Bm)[2]
+    keep = []
+    xs, xp = _f32(x, (batch, L, H, P)); keep.append(xs)
+    ds, dp = _f32(dt, (batch, L, H)); keep.append(ds)
+    bis, bip = _f32(dt_bias, (H,)); keep.append(bis)
+    as_, ap = _f32(A, (H,)); keep.append(as_)
+    bs, bp = _f32(Bm, (batch, L, N)); keep.append(bs)
+    cs, cp = _f32(Cm, (batch, L, N)); keep.append(cs)
+    dks, dkp = _f32(Dskip, (H,)); keep.append(dks)
+    zs, zp = _f32(z, (batch, L, H, P)); keep.append(zs)
+    hs, hp = _f64(h0, (batch, H, P, N)); keep.append(hs)
+    if channels is None:
+        chp, nch = None, 0
+        y = np.empty((batch, L, H, P), dtype=np.float64)
+        hf = np.empty((batch, H, P, N), dtype=np.float64)
+    else:
+        ch = np.ascontiguousarray(channels, dtype=np.int64)
+        keep.append(ch)
+        chp, nch = ch.ctypes.data_as(_i64p), len(ch)
+        y = np.empty((nch, L), dtype=np.float64)
+        hf = np.empty((nch, N), dtype=np.float64)
+    rc = lib().oracle_ssd_f64(batch, L, H, P, N, xp, dp, bip, ap, bp, cp, dkp, zp, hp,
+                              int(bool(dt_softplus)), chp, nch,
+                              y.ctypes.data_as(_f64p), hf.ctypes.data_as(_f64p))
+    if rc != 0:
+        raise ValueError("oracle_ssd_f64 rejected its arguments")
+    return y, hf
+
+
+def causal_conv1d(x, w, bias=None, apply_silu: bool = True):
+    """Reference causal depthwise conv1d (+ SiLU) in fp64. x (batch, L, D), w (D, K)."""
+    batch, L, D = np.shape(x)
+    K = np.shape(w)[1]
+    xs, xp = _f32(x, (batch, L, D))
+    ws, wp = _f32(w, (D, K))
+    bs, bp = _f32(bias, (D,))
+    out = np.empty((batch, L, D), dtype=np.float64)
+    rc = lib().oracle_causal_conv1d_f64(batch, L, D, K, xp, wp, bp, int(bool(apply_silu)),
+                                        out.ctypes.data_as(_f64p))
+    if rc != 0:
+        raise ValueError("oracle_causal_conv1d_f64 rejected its arguments")
+    del xs, ws, bs
+    return out
+
+
+def rel_l2(u, v) -> float:
+    """||u - v||_2 / ||v||_2 over the whole tensor, in fp64 (v is the reference)."""
+    u = np.asarray(u, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    den = np.linalg.norm(v.ravel())
+    num = np.linalg.norm((u - v).ravel())
+    if den == 0.0:
+        return 0.0 if num == 0.0 else float("inf")
+    return float(num / den)

@@ -1,0 +1,67 @@
+"""Plant plausible mistakes in copies of the oracle and require that every
+mutant fails at least one pin. This shows the pins constrain each term of the
+definition (a dropped term, a wrong sign, a wrong index, a swapped operand)."""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import oracle_pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+# (name, text in oracle.c, replacement, pins to run)
+MUTANTS = [
+    ("dt_dropped_from_decay", "exp(dt * (double)A[d * N + n])", "exp((double)A[d * N + n])", "scan"),
+    ("decay_sign", "exp(dt * (double)A[d * N + n])", "exp(-dt * (double)A[d * N + n])", "scan"),
+    ("A_transposed", "(double)A[d * N + n]", "(double)A[n * D + d]", "scan"),
+    ("dt_dropped_from_input", "const double bx = dt * (double)Bm[r + n] * xv;",
+     "const double bx = (double)Bm[r + n] * xv;", "scan"),
+    ("B_and_C_swapped", "const double bx = dt * (double)Bm[r + n] * xv;",
+     "const double bx = dt * (double)Cm[r + n] * xv;", "scan"),
+    ("B_not_time_varying", "const double bx = dt * (double)Bm[r + n] * xv;",
+     "const double bx = dt * (double)Bm[b * L * N + n] * xv;", "scan"),
+    ("decay_applied_to_input", "h[n] = abar * h[n] + bx;", "h[n] = abar * (h[n] + bx);", "scan"),
+    ("readout_before_update", "h[n] = abar * h[n] + bx;\n                acc += (double)Cm[r + n] * h[n];",
+     "acc += (double)Cm[r + n] * h[n];\n                h[n] = abar * h[n] + bx;", "scan"),
+    ("skip_dropped", "double out = acc + dsk * xv;\n            if (z) out *= silu_gate_f64((double)z[e]);\n            if (chans) y[i * L + t] = out;",
+     "double out = acc;\n            if (z) out *= silu_gate_f64((double)z[e]);\n            if (chans) y[i * L + t] = out;", "scan"),
+    ("gate_is_sigmoid", "return z / (1.0 + exp(-z));", "return 1.0 / (1.0 + exp(-z));", "scan"),
+    ("softplus_branch", "return v > 0.0 ? v + log1p(exp(-v)) : log1p(exp(v));",
+     "return v > 0.0 ? log1p(exp(-v)) : log1p(exp(v));", "scan"),
+    ("softplus_plain_log", "return v > 0.0 ? v + log1p(exp(-v)) : log1p(exp(v));",
+     "return log(1.0 + exp(v));", "scan"),
+    ("bias_ignored", "const double v = (double)delta[e] + bias;", "const double v = (double)delta[e];", "scan"),
+    ("h0_ignored", "h[n] = h0 ? h0[(b * D + d) * N + n] : 0.0;", "h[n] = 0.0;", "scan"),
+    ("h_final_index", "double *hf = chans ? h_final + i * N : h_final + (b * D + d) * N;",
+     "double *hf = chans ? h_final + i * N : h_final + (d * batch + b) * N;", "scan"),
+    ("ssd_dt_dropped_from_decay", "const double abar = exp(dtv * a);", "const double abar = exp(a);", "ssd"),
+    ("ssd_head_index", "(double)dt_raw[(b * L + t) * H + hh]", "(double)dt_raw[(b * L + t) * H]", "ssd"),
+    ("ssd_input_scale", "h[n] = abar * h[n] + dtv * (double)Bm[r + n] * xv;",
+     "h[n] = abar * h[n] + (double)Bm[r + n] * xv;", "ssd"),
+    ("ssd_x_layout", "const int64_t e = ((b * L + t) * H + hh) * P + p;",
+     "const int64_t e = ((b * L + t) * P + p) * H + hh;", "ssd"),
+    ("conv_not_causal", "const int64_t s = t - (K - 1) + k;", "const int64_t s = t - k;", "conv"),
+]
+
+PINS = {"scan": oracle_pins.SCAN_PINS, "ssd": oracle_pins.SSD_PINS, "conv": oracle_pins.CONV_PINS}
+
+
+@pytest.mark.parametrize("name,old,new,group", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, old, new, group):
+    src = open(SRC).read()
+    assert src.count(old) >= 1, "mutation anchor not found in oracle.c: %r" % old
+    path_c = tmp_path / ("%s.c" % name)
+    path_c.write_text(src.replace(old, new))
+    path_so = str(tmp_path / ("lib%s.so" % name))
+    subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-o",
+                           path_so, str(path_c), "-lm"])
+    failed = []
+    with oracle.using_library(path_so):
+        for pin in PINS[group]:
+            try:
+                pin()
+            except (AssertionError, ValueError, FloatingPointError):
+                failed.append(pin.__name__)
+    assert failed, "mutant %s passed every pin" % name
