@@ -1,0 +1,240 @@
+"""Benchmark of the selective-scan hot path on one MI355X.
+
+Default workload: the Mamba-130M-layer-shaped scan (batch 8, L 2048, D 1536,
+N 16, bf16 storage, fp32 state). One step = one selective_scan_fwd call over
+one batch of synthetic inputs already resident in HBM (every row of the path:
+stream in, softplus, discretise, recurrence, readout, gate, store, final state).
+Several input/output sets are rotated so that repeated steps cannot be served
+from the 256 MB Infinity Cache.
+
+Prints ONE JSON line on stdout. `value` is the effective HBM bandwidth over the
+algorithmic bytes (x, delta, z, y once per (b,t,d), B and C once per (b,t),
+parameters and the final state once). `roofline` relates the dominant kernel's
+measured time to its bound; `cpu_baseline` is the fp64 oracle timed on the
+host cores over the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import workloads  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix peak, TFLOP/s
+METRIC = "scan effective HBM GB/s (% of peak) + Gelem/s over B·L·D·N"
+
+
+def scan_alg_bytes(cfg) -> int:
+    """x, delta, z read and y written once per (b,t,d); B, C once per (b,t,n);
+    A, bias, D once; the fp32 final state written once."""
+    e = 2 if cfg.dtype == "bf16" else 4
+    bld = cfg.batch * cfg.seqlen * cfg.dim
+    bln = cfg.batch * cfg.seqlen * cfg.dstate
+    params = 4 * (cfg.dim * cfg.dstate + 2 * cfg.dim)
+    state = 4 * cfg.batch * cfg.dim * cfg.dstate
+    return 4 * e * bld + 2 * e * bln + params + state
+
+
+def ssd_alg_bytes(cfg) -> int:
+    e = 2
+    blhp = cfg.batch * cfg.seqlen * cfg.nheads * cfg.headdim
+    return (2 * e * blhp + e * cfg.batch * cfg.seqlen * cfg.nheads
+            + 2 * e * cfg.batch * cfg.seqlen * cfg.dstate + 3 * 4 * cfg.nheads
+            + 4 * cfg.batch * cfg.nheads * cfg.headdim * cfg.dstate)
+
+
+def ssd_alg_flops(cfg) -> float:
+    """Useful matrix flops of the chunked form, counting the causal half of the
+    two Q x Q products: C B^T, the masked product with x, the chunk states and
+    the carried-state readout."""
+    Q = cfg.chunk
+    nch = math.ceil(cfg.seqlen / Q)
+    b, H, P, N = cfg.batch, cfg.nheads, cfg.headdim, cfg.dstate
+    cb = 2.0 * b * nch * Q * Q * N / 2
+    diag = 2.0 * b * H * nch * Q * Q * P / 2
+    states = 2.0 * b * H * nch * Q * N * P
+    off = 2.0 * b * H * nch * Q * N * P
+    return cb + diag + states + off
+
+
+def _device_inputs(inp, torch, dev):
+    td = torch.bfloat16 if inp["dtype"] == "bf16" else torch.float32
+    out = {}
+    for k, v in inp.items():
+        if isinstance(v, np.ndarray):
+            t = torch.from_numpy(v).to(dev)
+            out[k] = t.to(td) if k in ("x", "delta", "dt", "z", "Bm", "Cm") else t
+    return out
+
+
+def time_scan(key, steps, warmup, torch, ssm):
+    cfg = workloads.CONFIGS[key]
+    dev = torch.device("cuda:0")
+    base = workloads.make_inputs(key)
+    ws_set = scan_alg_bytes(cfg)
+    nsets = max(2, math.ceil(768e6 / ws_set))
+    sets = []
+    for i in range(nsets):
+        t = _device_inputs(base, torch, dev)
+        if i:  # distinct buffers with the same statistics: roll along time
+            for k in ("x", "delta", "z"):
+                t[k] = torch.roll(t[k], shifts=97 * i, dims=1).contiguous()
+        t["y"] = torch.empty_like(t["x"])
+        t["hf"] = torch.empty((cfg.batch, cfg.dim, cfg.dstate), dtype=torch.float32, device=dev)
+        sets.append(t)
+    ws = torch.empty(max(1, ssm.scan_workspace_bytes(cfg.batch, cfg.seqlen, cfg.dim, cfg.dstate,
+                                                     sets[0]["x"].dtype)),
+                     dtype=torch.uint8, device=dev)
+
+    def step(i):
+        t = sets[i % nsets]
+        ssm.selective_scan_fwd(t["x"], t["delta"], t["A"], t["Bm"], t["Cm"], t["Dskip"], t["z"],
+                               t["delta_bias"], None, out=t["y"], final_state_out=t["hf"],
+                               workspace=ws)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_call = [a.elapsed_time(b) for a, b in ev]
+    return cfg, wall, per_call
+
+
+def time_ssd(steps, warmup, torch, ssm):
+    cfg = workloads.CONFIGS["S5"]
+    dev = torch.device("cuda:0")
+    base = workloads.make_inputs("S5")
+    nsets = max(2, math.ceil(768e6 / ssd_alg_bytes(cfg)))
+    sets = []
+    for i in range(nsets):
+        t = _device_inputs(base, torch, dev)
+        if i:
+            t["x"] = torch.roll(t["x"], shifts=97 * i, dims=1).contiguous()
+        t["y"] = torch.empty_like(t["x"])
+        t["hf"] = torch.empty((cfg.batch, cfg.nheads, cfg.headdim, cfg.dstate), dtype=torch.float32,
+                              device=dev)
+        sets.append(t)
+    ws = torch.empty(ssm.ssd_workspace_bytes(cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim,
+                                             cfg.dstate, cfg.chunk), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        t = sets[i % nsets]
+        ssm.ssd_chunked_fwd(t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], t["Dskip"], None,
+                            t["dt_bias"], None, chunk=cfg.chunk, out=t["y"],
+                            final_state_out=t["hf"], workspace=ws)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    return cfg, [a.elapsed_time(b) for a, b in ev]
+
+
+def cpu_baseline(key, budget_s=10.0):
+    """The fp64 oracle on the host cores over the same workload (all channels,
+    whole sequence), repeated until ~budget_s of wall time; effective GB/s on the
+    same algorithmic-bytes count as the GPU figure."""
+    import oracle
+    cfg = workloads.CONFIGS[key]
+    inp = workloads.make_inputs(key)
+    threads = oracle.num_threads()
+    runs, t0 = 0, time.perf_counter()
+    while True:
+        oracle.selective_scan(inp["x"], inp["delta"], inp["A"], inp["Bm"], inp["Cm"],
+                              inp["Dskip"], inp["z"], inp["delta_bias"])
+        runs += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or runs >= 20:
+            break
+    per = el / runs
+    return {"value": round(scan_alg_bytes(cfg) / per / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "full %s workload (all %d channels x L %d), fp64 C recurrence, %d run(s), "
+                      "%.2f s per run" % (key, cfg.batch * cfg.dim, cfg.seqlen, runs, per)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="S2", choices=["S1", "S2", "S3", "S4"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--extra", action="store_true",
+                    help="also time the other scan workloads and the SSD form (stderr + 'extra')")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(--gpus %d requested)." % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import selective_state_space_70_amd as ssm
+
+    cfg, wall, per_call = time_scan(args.config, args.steps, args.warmup, torch, ssm)
+    ms = sum(per_call) / len(per_call)
+    alg = scan_alg_bytes(cfg)
+    gbs = alg / (ms * 1e-3) / 1e9
+    gelem = cfg.elements / (ms * 1e-3) / 1e9
+    line = {
+        "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "%s %s" % (args.config, cfg.name), "batch": cfg.batch,
+                   "seq_len": cfg.seqlen, "dim": cfg.dim, "dstate": cfg.dstate,
+                   "storage": cfg.dtype, "state": "f32"},
+        "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "gelem_per_s": round(gelem, 2),
+        "wall_s_timed": round(wall, 4),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "selective_scan_fwd call (all kernels of one call)"},
+    }
+    if args.extra:
+        extra = {}
+        for key in ("S3", "S4"):
+            c2, _, pc = time_scan(key, max(5, args.steps // 3), 2, torch, ssm)
+            m2 = sum(pc) / len(pc)
+            extra[key] = {"ms": round(m2, 4), "GB/s": round(scan_alg_bytes(c2) / m2 / 1e6, 1),
+                          "Gelem/s": round(c2.elements / m2 / 1e6, 1)}
+        c5, pc5 = time_ssd(max(5, args.steps // 3), 2, torch, ssm)
+        m5 = sum(pc5) / len(pc5)
+        extra["S5"] = {"ms": round(m5, 4), "GB/s": round(ssd_alg_bytes(c5) / m5 / 1e6, 1),
+                       "TFLOP/s": round(ssd_alg_flops(c5) / m5 / 1e9, 1),
+                       "mfma_frac": round(ssd_alg_flops(c5) / m5 / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4)}
+        line["extra"] = extra
+        print(json.dumps(extra), file=sys.stderr)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args.config)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,160 @@
+/*
+ * ssm.h — C ABI of the MI355X (gfx950) selective-state-space library (libssm.so).
+ *
+ * Pages cited (titles as published; sections named as on the page):
+ *   [Mamba-2 page]  "Mamba-2：把状态空间模型和 Attention 统一到一个数学框架里"
+ *                   (aiplusplus.yigather.com/tech/05-27a2ce5d)
+ *   [SSM page]      "状态空间模型与 Mamba：不用注意力读取长序列的方法"
+ *                   (ai-trend.me/zh/study/state-space-models/)
+ *   [Juejin page]   SSM/Mamba engineering article (juejin.cn/post/7634002571020402707)
+ *   [Reading page]  "论文解读：Mamba — 线性时间的序列建模革命" (agent.eake.cn)
+ *   [Hybrid page]   "基础知识：Mamba 与混合 SSM 架构" (charles2530.github.io)
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor argument is a caller-owned DEVICE pointer to contiguous
+ *     row-major memory, last dimension fastest. The library never allocates,
+ *     frees or copies device memory on its own; scratch space is the caller's
+ *     `workspace`, sized by the matching *_workspace_bytes() query.
+ *   - All argument checks run on the host, synchronously, before anything is
+ *     enqueued. On any error nothing is launched, outputs are untouched, the
+ *     call returns a non-zero ssm_status and ssm_last_error() describes it.
+ *   - Work is enqueued on `stream` (0 = the null stream) and the call returns
+ *     without waiting for it. A device fault surfaces on that stream.
+ *   - Outputs must not alias inputs or each other. The library keeps no
+ *     mutable global state (the error text is thread-local), so concurrent
+ *     calls from several host threads are safe if their buffers are disjoint.
+ *   - Storage dtype SSM_BF16 means bfloat16 in memory; all arithmetic is fp32,
+ *     the recurrent state is fp32, and bf16 outputs are rounded to nearest-even.
+ *   - Byte offsets inside one batch row of a (batch, L, ...) tensor must fit in
+ *     31 bits; larger shapes return SSM_ENOTSUP.
+ */
+#ifndef SSM_H
+#define SSM_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSM_ABI_VERSION 1
+
+typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
+
+typedef enum {
+    SSM_OK = 0,
+    SSM_EINVAL = 1,   /* null required pointer, negative size, misalignment, short workspace */
+    SSM_ENOTSUP = 2,  /* well-formed but outside what the kernels implement (N, dtype, size) */
+    SSM_EHIP = 3      /* the HIP runtime refused a launch */
+} ssm_status;
+
+/*
+ * Selective scan (Mamba-1 form), per channel (b, d) with an N-dim fp32 state:
+ *   dt_t   = softplus(delta[b,t,d] + delta_bias[d])      (or delta + bias when
+ *                                                         delta_softplus == 0)
+ *   h_t[n] = exp(dt_t * A[d,n]) * h_{t-1}[n] + dt_t * Bm[b,t,n] * x[b,t,d]
+ *   y[b,t,d] = (sum_n Cm[b,t,n] h_t[n] + Dskip[d] * x[b,t,d]) * silu(z[b,t,d])
+ *   h_final[b,d,:] = h_L (not gated), the state a later call takes as h0.
+ * Sources: the discrete recurrence [Mamba-2 page, Background]; input-dependent
+ * Delta, B, C with softplus on Delta [Mamba-2 page, Core idea step 1; Reading
+ * page section 3]; the D x skip term [Juejin page, SSM basics]; the SiLU(z) gate
+ * [Reading page section 5; Hybrid page section 3]; a per-channel N-dim state
+ * [SSM page, how it works]; the state carried across calls for streaming
+ * [Juejin page, long-document streaming step(x, state)]. Abar = exp(dt A) and the
+ * Euler input term dt B x are the adopted discretisation.
+ *
+ * Layouts: x, delta, z, y: (batch, L, D), dtype. Bm, Cm: (batch, L, N), dtype, one
+ * group shared by every channel. A: (D, N) fp32 (diagonal, real; rows of the form
+ * A[d,n] = (n+1) A[d,0] are detected on the device and take a faster exact path).
+ * delta_bias, Dskip: (D) fp32. h0, h_final: (batch, D, N) fp32.
+ * Nullable: z (no gate), delta_bias (0), Dskip (0), h0 (zero state),
+ * h_final (not written). Supported: N in {16, 32, 64}; dtype F32 or BF16.
+ * batch == 0 is a no-op; L == 0 writes h_final = h0 (or zeros).
+ */
+typedef struct ssm_scan_args {
+    int64_t batch, seqlen, dim, dstate;   /* B, L, D, N */
+    ssm_dtype dtype;                      /* storage of x, delta, z, Bm, Cm, y */
+    int32_t delta_softplus;               /* 1: softplus(delta + bias); 0: delta + bias */
+    const void *x, *delta, *z;
+    const void *Bm, *Cm;
+    const float *A;
+    const float *delta_bias;
+    const float *Dskip;
+    const float *h0;
+    void *y;
+    float *h_final;
+    void *workspace;                      /* >= selective_scan_workspace_bytes(), 256-B aligned */
+    size_t workspace_bytes;
+} ssm_scan_args;
+
+/*
+ * Scalar-A state-space form (Mamba-2 "SSD"): H heads of P channels; a head shares
+ * one step dt[b,t,h] and one scalar A[h] < 0, B and C are one group shared by all
+ * heads, and every channel (h, p) keeps an N-dim state:
+ *   dt_t = softplus(dt[b,t,h] + dt_bias[h]);  a_t = exp(dt_t A[h])
+ *   S_t[h,p,:] = a_t S_{t-1}[h,p,:] + dt_t x[b,t,h,p] Bm[b,t,:]
+ *   y[b,t,h,p] = (Cm[b,t,:] . S_t[h,p,:] + Dskip[h] x[b,t,h,p]) * silu(z[b,t,h,p])
+ * computed in chunks of `chunk` steps through the semiseparable-matrix form:
+ * inside a chunk y = (L o C B^T o decay o dt) x on the matrix cores, and chunk
+ * states carry the rest [Mamba-2 page, Core idea step 2 and key points 1 and 3:
+ * the SSM as a structured (semiseparable) attention-like matrix that runs as
+ * matrix multiplication; selectivity restricted to keep that structure].
+ * Layouts: x, z, y: (batch, L, H, P) dtype; dt: (batch, L, H) dtype; Bm, Cm:
+ * (batch, L, N) dtype; dt_bias, A, Dskip: (H) fp32; h0, h_final: (batch, H, P, N) fp32.
+ * Nullable: z, dt_bias, Dskip, h0, h_final. Supported: dtype BF16; N in
+ * {64, 128, 256}; P == 64; chunk in {64, 128, 256}. Any L >= 0 (the last chunk
+ * may be short); results do not depend on `chunk` beyond rounding.
+ */
+typedef struct ssm_ssd_args {
+    int64_t batch, seqlen, nheads, headdim, dstate, chunk;  /* B, L, H, P, N, Q */
+    ssm_dtype dtype;
+    int32_t dt_softplus;                  /* 1: softplus(dt + bias); 0: dt + bias */
+    const void *x;
+    const void *dt;
+    const float *dt_bias;
+    const float *A;
+    const void *Bm, *Cm;
+    const float *Dskip;
+    const void *z;
+    const float *h0;
+    void *y;
+    float *h_final;
+    void *workspace;                      /* >= ssd_chunked_workspace_bytes(), 256-B aligned */
+    size_t workspace_bytes;
+} ssm_ssd_args;
+
+/* Enqueue the selective scan. Errors: SSM_EINVAL, SSM_ENOTSUP (before any launch),
+ * SSM_EHIP (a launch was refused; earlier kernels of this call may have run). */
+ssm_status selective_scan_fwd(const ssm_scan_args *args, hipStream_t stream);
+
+/* Host-only check of `args` (no HIP call): the status selective_scan_fwd would
+ * return from its argument checks, ignoring the workspace pointer and size. */
+ssm_status selective_scan_validate(const ssm_scan_args *args);
+
+/* Workspace bytes selective_scan_fwd needs for these sizes (0 if none). Host-only. */
+size_t selective_scan_workspace_bytes(const ssm_scan_args *args);
+
+/* Enqueue the chunked scalar-A (SSD) form. Errors as for selective_scan_fwd. */
+ssm_status ssd_chunked_fwd(const ssm_ssd_args *args, hipStream_t stream);
+
+/* Host-only argument check of the SSD form, ignoring the workspace. */
+ssm_status ssd_chunked_validate(const ssm_ssd_args *args);
+
+/* Workspace bytes ssd_chunked_fwd needs for these sizes. Host-only. */
+size_t ssd_chunked_workspace_bytes(const ssm_ssd_args *args);
+
+/* Static name of a status code ("SSM_OK", ...). */
+const char *ssm_status_str(ssm_status s);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if none). */
+const char *ssm_last_error(void);
+
+/* SSM_ABI_VERSION of the built library. */
+int ssm_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SSM_H */

@@ -1,0 +1,189 @@
+"""MI355X (gfx950) selective state-space scan and scalar-A SSD form.
+
+Thin binding over the C ABI of ``libssm.so`` (see ``include/ssm.h``): it checks
+torch tensors, allocates outputs and workspace with torch, and passes raw
+device pointers and torch's current HIP stream. Every arithmetic step runs in
+the HIP kernels; there is no CPU or PyTorch fallback, and a missing library
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Tuple
+
+import torch
+
+from . import _capi
+from ._capi import SSMError
+
+__all__ = ["selective_scan_fwd", "ssd_chunked_fwd", "scan_workspace_bytes",
+           "ssd_workspace_bytes", "abi_version", "SSMError"]
+
+_DT = {torch.float32: _capi.SSM_F32, torch.bfloat16: _capi.SSM_BF16}
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _need(t, name, shape, dtype, device):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if t.dtype != dtype:
+        raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def abi_version() -> int:
+    return _capi.lib().ssm_abi_version()
+
+
+def _scan_args(x, delta, A, Bm, Cm, Dskip, z, delta_bias, h0, delta_softplus, y, h_final):
+    batch, L, D = x.shape
+    N = A.shape[1]
+    a = _capi.ScanArgs()
+    a.batch, a.seqlen, a.dim, a.dstate = batch, L, D, N
+    a.dtype = _DT[x.dtype]
+    a.delta_softplus = 1 if delta_softplus else 0
+    a.x, a.delta, a.z = _ptr(x), _ptr(delta), _ptr(z)
+    a.Bm, a.Cm, a.A = _ptr(Bm), _ptr(Cm), _ptr(A)
+    a.delta_bias, a.Dskip, a.h0 = _ptr(delta_bias), _ptr(Dskip), _ptr(h0)
+    a.y, a.h_final = _ptr(y), _ptr(h_final)
+    return a
+
+
+def scan_workspace_bytes(batch: int, seqlen: int, dim: int, dstate: int,
+                         dtype=torch.bfloat16) -> int:
+    a = _capi.ScanArgs()
+    a.batch, a.seqlen, a.dim, a.dstate, a.dtype = batch, seqlen, dim, dstate, _DT[dtype]
+    return _capi.lib().selective_scan_workspace_bytes(ctypes.byref(a))
+
+
+def selective_scan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm: torch.Tensor,
+                       Cm: torch.Tensor, Dskip: Optional[torch.Tensor] = None,
+                       z: Optional[torch.Tensor] = None, delta_bias: Optional[torch.Tensor] = None,
+                       h0: Optional[torch.Tensor] = None, delta_softplus: bool = True,
+                       return_final_state: bool = True, out: Optional[torch.Tensor] = None,
+                       final_state_out: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None
+                       ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Selective scan. x, delta, z: (batch, L, D); Bm, Cm: (batch, L, N), all
+    fp32 or all bf16; A: (D, N) fp32; Dskip, delta_bias: (D,) fp32;
+    h0: (batch, D, N) fp32. Returns (y (batch, L, D) in x's dtype,
+    h_final (batch, D, N) fp32 or None)."""
+    if x.dim() != 3 or A.dim() != 2:
+        raise ValueError("x must be (batch, L, D) and A (D, N)")
+    if x.dtype not in _DT:
+        raise TypeError("x must be float32 or bfloat16")
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a HIP device (got %s)" % dev)
+    batch, L, D = x.shape
+    N = A.shape[1]
+    _need(x, "x", (batch, L, D), x.dtype, dev)
+    _need(delta, "delta", (batch, L, D), x.dtype, dev)
+    _need(z, "z", (batch, L, D), x.dtype, dev)
+    _need(Bm, "Bm", (batch, L, N), x.dtype, dev)
+    _need(Cm, "Cm", (batch, L, N), x.dtype, dev)
+    _need(A, "A", (D, N), torch.float32, dev)
+    _need(Dskip, "Dskip", (D,), torch.float32, dev)
+    _need(delta_bias, "delta_bias", (D,), torch.float32, dev)
+    _need(h0, "h0", (batch, D, N), torch.float32, dev)
+    y = out if out is not None else torch.empty((batch, L, D), dtype=x.dtype, device=dev)
+    _need(y, "out", (batch, L, D), x.dtype, dev)
+    hf = None
+    if return_final_state:
+        hf = (final_state_out if final_state_out is not None
+              else torch.empty((batch, D, N), dtype=torch.float32, device=dev))
+        _need(hf, "final_state_out", (batch, D, N), torch.float32, dev)
+    a = _scan_args(x, delta, A, Bm, Cm, Dskip, z, delta_bias, h0, delta_softplus, y, hf)
+    L_ = _capi.lib()
+    _capi.check(L_.selective_scan_validate(ctypes.byref(a)))
+    need = L_.selective_scan_workspace_bytes(ctypes.byref(a))
+    if need:
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        a.workspace, a.workspace_bytes = workspace.data_ptr(), need
+    _capi.check(L_.selective_scan_fwd(ctypes.byref(a), _stream(dev)))
+    return y, hf
+
+
+def _ssd_args(x, dt, A, Bm, Cm, Dskip, z, dt_bias, h0, chunk, dt_softplus, y, h_final):
+    batch, L, H, P = x.shape
+    a = _capi.SSDArgs()
+    a.batch, a.seqlen, a.nheads, a.headdim = batch, L, H, P
+    a.dstate, a.chunk = Bm.shape[2], chunk
+    a.dtype = _DT[x.dtype]
+    a.dt_softplus = 1 if dt_softplus else 0
+    a.x, a.dt, a.dt_bias, a.A = _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A)
+    a.Bm, a.Cm, a.Dskip, a.z, a.h0 = _ptr(Bm), _ptr(Cm), _ptr(Dskip), _ptr(z), _ptr(h0)
+    a.y, a.h_final = _ptr(y), _ptr(h_final)
+    return a
+
+
+def ssd_workspace_bytes(batch: int, seqlen: int, nheads: int, headdim: int, dstate: int,
+                        chunk: int = 256) -> int:
+    a = _capi.SSDArgs()
+    a.batch, a.seqlen, a.nheads, a.headdim, a.dstate, a.chunk = (batch, seqlen, nheads, headdim,
+                                                                  dstate, chunk)
+    a.dtype = _capi.SSM_BF16
+    return _capi.lib().ssd_chunked_workspace_bytes(ctypes.byref(a))
+
+
+def ssd_chunked_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, Bm: torch.Tensor,
+                    Cm: torch.Tensor, Dskip: Optional[torch.Tensor] = None,
+                    z: Optional[torch.Tensor] = None, dt_bias: Optional[torch.Tensor] = None,
+                    h0: Optional[torch.Tensor] = None, chunk: int = 256, dt_softplus: bool = True,
+                    return_final_state: bool = True, out: Optional[torch.Tensor] = None,
+                    final_state_out: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None
+                    ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Scalar-A (SSD) form. x, z: (batch, L, H, P) bf16; dt: (batch, L, H) bf16;
+    Bm, Cm: (batch, L, N) bf16; A, Dskip, dt_bias: (H,) fp32; h0: (batch, H, P, N)
+    fp32. Returns (y (batch, L, H, P) bf16, h_final (batch, H, P, N) fp32 or None)."""
+    if x.dim() != 4 or Bm.dim() != 3:
+        raise ValueError("x must be (batch, L, H, P) and Bm (batch, L, N)")
+    if x.dtype not in _DT:
+        raise TypeError("x must be float32 or bfloat16")
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a HIP device (got %s)" % dev)
+    batch, L, H, P = x.shape
+    N = Bm.shape[2]
+    _need(dt, "dt", (batch, L, H), x.dtype, dev)
+    _need(z, "z", (batch, L, H, P), x.dtype, dev)
+    _need(Bm, "Bm", (batch, L, N), x.dtype, dev)
+    _need(Cm, "Cm", (batch, L, N), x.dtype, dev)
+    _need(A, "A", (H,), torch.float32, dev)
+    _need(Dskip, "Dskip", (H,), torch.float32, dev)
+    _need(dt_bias, "dt_bias", (H,), torch.float32, dev)
+    _need(h0, "h0", (batch, H, P, N), torch.float32, dev)
+    _need(x, "x", (batch, L, H, P), x.dtype, dev)
+    y = out if out is not None else torch.empty((batch, L, H, P), dtype=x.dtype, device=dev)
+    _need(y, "out", (batch, L, H, P), x.dtype, dev)
+    hf = None
+    if return_final_state:
+        hf = (final_state_out if final_state_out is not None
+              else torch.empty((batch, H, P, N), dtype=torch.float32, device=dev))
+        _need(hf, "final_state_out", (batch, H, P, N), torch.float32, dev)
+    a = _ssd_args(x, dt, A, Bm, Cm, Dskip, z, dt_bias, h0, chunk, dt_softplus, y, hf)
+    L_ = _capi.lib()
+    _capi.check(L_.ssd_chunked_validate(ctypes.byref(a)))
+    need = L_.ssd_chunked_workspace_bytes(ctypes.byref(a))
+    if need:
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        a.workspace, a.workspace_bytes = workspace.data_ptr(), need
+    _capi.check(L_.ssd_chunked_fwd(ctypes.byref(a), _stream(dev)))
+    return y, hf

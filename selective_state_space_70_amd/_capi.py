@@ -1,0 +1,93 @@
+"""ctypes view of include/ssm.h (structs, enums, exported symbols) and the loader
+of the in-tree libssm.so. No compute happens here."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libssm.so")
+
+SSM_F32, SSM_BF16 = 0, 1
+SSM_OK, SSM_EINVAL, SSM_ENOTSUP, SSM_EHIP = 0, 1, 2, 3
+
+# Every symbol include/ssm.h declares.
+EXPORTS = [
+    "selective_scan_fwd", "selective_scan_validate", "selective_scan_workspace_bytes",
+    "ssd_chunked_fwd", "ssd_chunked_validate", "ssd_chunked_workspace_bytes",
+    "ssm_status_str", "ssm_last_error", "ssm_abi_version",
+]
+ABI_VERSION = 1
+
+_p = ctypes.c_void_p
+
+
+class ScanArgs(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("dim", ctypes.c_int64),
+        ("dstate", ctypes.c_int64), ("dtype", ctypes.c_int), ("delta_softplus", ctypes.c_int32),
+        ("x", _p), ("delta", _p), ("z", _p), ("Bm", _p), ("Cm", _p),
+        ("A", _p), ("delta_bias", _p), ("Dskip", _p), ("h0", _p),
+        ("y", _p), ("h_final", _p), ("workspace", _p), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class SSDArgs(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64),
+        ("headdim", ctypes.c_int64), ("dstate", ctypes.c_int64), ("chunk", ctypes.c_int64),
+        ("dtype", ctypes.c_int), ("dt_softplus", ctypes.c_int32),
+        ("x", _p), ("dt", _p), ("dt_bias", _p), ("A", _p), ("Bm", _p), ("Cm", _p),
+        ("Dskip", _p), ("z", _p), ("h0", _p), ("y", _p), ("h_final", _p),
+        ("workspace", _p), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libssm.so. Raises if it has not been built: there is no fallback."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                "libssm.so is not built (%s). Build it with "
+                "`python -c 'import __graft_entry__ as g; g.build()'` or "
+                "`python selective_state_space_70_amd/build.py`." % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        for name, argt in (("selective_scan_fwd", ScanArgs), ("ssd_chunked_fwd", SSDArgs)):
+            f = getattr(L, name)
+            f.restype = ctypes.c_int
+            f.argtypes = [ctypes.POINTER(argt), _p]
+        for name, argt in (("selective_scan_validate", ScanArgs), ("ssd_chunked_validate", SSDArgs)):
+            f = getattr(L, name)
+            f.restype = ctypes.c_int
+            f.argtypes = [ctypes.POINTER(argt)]
+        for name, argt in (("selective_scan_workspace_bytes", ScanArgs),
+                           ("ssd_chunked_workspace_bytes", SSDArgs)):
+            f = getattr(L, name)
+            f.restype = ctypes.c_size_t
+            f.argtypes = [ctypes.POINTER(argt)]
+        L.ssm_status_str.restype = ctypes.c_char_p
+        L.ssm_status_str.argtypes = [ctypes.c_int]
+        L.ssm_last_error.restype = ctypes.c_char_p
+        L.ssm_last_error.argtypes = []
+        L.ssm_abi_version.restype = ctypes.c_int
+        L.ssm_abi_version.argtypes = []
+        if L.ssm_abi_version() != ABI_VERSION:
+            raise RuntimeError("libssm.so ABI version %d, binding expects %d"
+                               % (L.ssm_abi_version(), ABI_VERSION))
+        _lib = L
+    return _lib
+
+
+class SSMError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__("%s: %s" % (lib().ssm_status_str(status).decode(), detail))
+
+
+def check(status: int) -> None:
+    if status != SSM_OK:
+        raise SSMError(status, lib().ssm_last_error().decode(errors="replace"))

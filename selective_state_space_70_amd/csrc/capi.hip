@@ -1,0 +1,174 @@
+// C ABI of libssm.so: argument checks (host only, before any HIP call), plans,
+// and dispatch to the kernel launchers. See include/ssm.h for the contract.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "internal.h"
+#include "ssm.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+ssm_status fail(ssm_status s, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+size_t esize(ssm_dtype t) { return t == SSM_BF16 ? 2 : 4; }
+
+constexpr int64_t kMaxRowBytes = (int64_t)1 << 31;
+
+ssm_status check_scan(const ssm_scan_args *a) {
+    if (!a) return fail(SSM_EINVAL, "selective_scan: args is NULL");
+    if (a->batch < 0 || a->seqlen < 0 || a->dim <= 0 || a->dstate <= 0)
+        return fail(SSM_EINVAL, "selective_scan: need batch >= 0, seqlen >= 0, dim > 0, dstate > 0 "
+                    "(got %lld, %lld, %lld, %lld)", (long long)a->batch, (long long)a->seqlen,
+                    (long long)a->dim, (long long)a->dstate);
+    if (a->dtype != SSM_F32 && a->dtype != SSM_BF16)
+        return fail(SSM_EINVAL, "selective_scan: unknown dtype %d", (int)a->dtype);
+    if (a->dstate != 16 && a->dstate != 32 && a->dstate != 64)
+        return fail(SSM_ENOTSUP, "selective_scan: dstate %lld not supported (16, 32, 64)",
+                    (long long)a->dstate);
+    if (a->batch > 65535 || a->dim > (1 << 30))
+        return fail(SSM_ENOTSUP, "selective_scan: batch <= 65535 and dim <= 2^30 supported");
+    const size_t es = esize(a->dtype);
+    if (a->seqlen * a->dim * (int64_t)es >= kMaxRowBytes)
+        return fail(SSM_ENOTSUP, "selective_scan: seqlen*dim*elem_size must be < 2^31 bytes");
+    if (a->batch == 0) return SSM_OK;
+    if (!a->A) return fail(SSM_EINVAL, "selective_scan: A is NULL");
+    if (!aligned(a->A, 4) || !aligned(a->delta_bias, 4) || !aligned(a->Dskip, 4) ||
+        !aligned(a->h0, 4) || !aligned(a->h_final, 4))
+        return fail(SSM_EINVAL, "selective_scan: fp32 parameter/state pointers must be 4-byte aligned");
+    if (a->seqlen == 0) return SSM_OK;
+    if (!a->x || !a->delta || !a->Bm || !a->Cm || !a->y)
+        return fail(SSM_EINVAL, "selective_scan: x, delta, Bm, Cm and y are required");
+    if (!aligned(a->x, es) || !aligned(a->delta, es) || !aligned(a->z, es) || !aligned(a->y, es))
+        return fail(SSM_EINVAL, "selective_scan: x, delta, z, y must be aligned to the element size");
+    // B/C rows are fetched with scalar loads of whole dwords
+    if (!aligned(a->Bm, 4) || !aligned(a->Cm, 4))
+        return fail(SSM_EINVAL, "selective_scan: Bm and Cm must be 4-byte aligned");
+    return SSM_OK;
+}
+
+ssm_status check_ssd(const ssm_ssd_args *a) {
+    if (!a) return fail(SSM_EINVAL, "ssd_chunked: args is NULL");
+    if (a->batch < 0 || a->seqlen < 0 || a->nheads <= 0 || a->headdim <= 0 || a->dstate <= 0 ||
+        a->chunk <= 0)
+        return fail(SSM_EINVAL, "ssd_chunked: need batch, seqlen >= 0 and nheads, headdim, "
+                    "dstate, chunk > 0");
+    if (a->dtype != SSM_F32 && a->dtype != SSM_BF16)
+        return fail(SSM_EINVAL, "ssd_chunked: unknown dtype %d", (int)a->dtype);
+    if (a->dtype != SSM_BF16)
+        return fail(SSM_ENOTSUP, "ssd_chunked: only bf16 storage is implemented (matrix cores)");
+    if (a->headdim != 64)
+        return fail(SSM_ENOTSUP, "ssd_chunked: headdim %lld not supported (64)", (long long)a->headdim);
+    if (a->dstate != 64 && a->dstate != 128 && a->dstate != 256)
+        return fail(SSM_ENOTSUP, "ssd_chunked: dstate %lld not supported (64, 128, 256)",
+                    (long long)a->dstate);
+    if (a->chunk != 64 && a->chunk != 128 && a->chunk != 256)
+        return fail(SSM_ENOTSUP, "ssd_chunked: chunk %lld not supported (64, 128, 256)",
+                    (long long)a->chunk);
+    if (a->batch > 65535 || a->nheads > 65535)
+        return fail(SSM_ENOTSUP, "ssd_chunked: batch and nheads must be <= 65535");
+    if (a->seqlen * a->nheads * a->headdim * 2 >= kMaxRowBytes)
+        return fail(SSM_ENOTSUP, "ssd_chunked: seqlen*nheads*headdim*2 must be < 2^31 bytes");
+    if ((a->seqlen + a->chunk - 1) / a->chunk > 65535)
+        return fail(SSM_ENOTSUP, "ssd_chunked: at most 65535 chunks");
+    if (a->batch == 0) return SSM_OK;
+    if (!a->A) return fail(SSM_EINVAL, "ssd_chunked: A is NULL");
+    if (!aligned(a->A, 4) || !aligned(a->dt_bias, 4) || !aligned(a->Dskip, 4) ||
+        !aligned(a->h0, 4) || !aligned(a->h_final, 4))
+        return fail(SSM_EINVAL, "ssd_chunked: fp32 parameter/state pointers must be 4-byte aligned");
+    if (a->seqlen == 0) return SSM_OK;
+    if (!a->x || !a->dt || !a->Bm || !a->Cm || !a->y)
+        return fail(SSM_EINVAL, "ssd_chunked: x, dt, Bm, Cm and y are required");
+    // matrix-core tiles read 16-byte vectors of x, z, B and C and write 4-byte pairs of y
+    if (!aligned(a->x, 16) || !aligned(a->z, 16) || !aligned(a->Bm, 16) || !aligned(a->Cm, 16) ||
+        !aligned(a->y, 16) || !aligned(a->dt, 2))
+        return fail(SSM_EINVAL, "ssd_chunked: x, z, y, Bm, Cm must be 16-byte aligned, dt 2-byte");
+    return SSM_OK;
+}
+
+ssm_status check_workspace(void *ws, size_t have, size_t need, const char *who) {
+    if (need == 0) return SSM_OK;
+    if (!ws) return fail(SSM_EINVAL, "%s: workspace of %zu bytes required", who, need);
+    if (have < need)
+        return fail(SSM_EINVAL, "%s: workspace too small (%zu < %zu bytes)", who, have, need);
+    if (!aligned(ws, 256)) return fail(SSM_EINVAL, "%s: workspace must be 256-byte aligned", who);
+    return SSM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ssm_status selective_scan_validate(const ssm_scan_args *a) {
+    const ssm_status s = check_scan(a);
+    if (s == SSM_OK) g_err[0] = 0;
+    return s;
+}
+
+size_t selective_scan_workspace_bytes(const ssm_scan_args *a) {
+    if (check_scan(a) != SSM_OK) return 0;
+    return ssm::scan_plan(*a).bytes;
+}
+
+ssm_status selective_scan_fwd(const ssm_scan_args *a, hipStream_t stream) {
+    ssm_status s = check_scan(a);
+    if (s != SSM_OK) return s;
+    const ssm::ScanPlan plan = ssm::scan_plan(*a);
+    if (a->batch > 0 && a->seqlen > 0) {
+        s = check_workspace(a->workspace, a->workspace_bytes, plan.bytes, "selective_scan");
+        if (s != SSM_OK) return s;
+    }
+    s = ssm::scan_launch(*a, plan, stream, g_err, sizeof g_err);
+    if (s == SSM_OK) g_err[0] = 0;
+    return s;
+}
+
+ssm_status ssd_chunked_validate(const ssm_ssd_args *a) {
+    const ssm_status s = check_ssd(a);
+    if (s == SSM_OK) g_err[0] = 0;
+    return s;
+}
+
+size_t ssd_chunked_workspace_bytes(const ssm_ssd_args *a) {
+    if (check_ssd(a) != SSM_OK) return 0;
+    return ssm::ssd_plan(*a).bytes;
+}
+
+ssm_status ssd_chunked_fwd(const ssm_ssd_args *a, hipStream_t stream) {
+    ssm_status s = check_ssd(a);
+    if (s != SSM_OK) return s;
+    const ssm::SSDPlan plan = ssm::ssd_plan(*a);
+    if (a->batch > 0 && a->seqlen > 0) {
+        s = check_workspace(a->workspace, a->workspace_bytes, plan.bytes, "ssd_chunked");
+        if (s != SSM_OK) return s;
+    }
+    s = ssm::ssd_launch(*a, plan, stream, g_err, sizeof g_err);
+    if (s == SSM_OK) g_err[0] = 0;
+    return s;
+}
+
+const char *ssm_status_str(ssm_status s) {
+    switch (s) {
+        case SSM_OK: return "SSM_OK";
+        case SSM_EINVAL: return "SSM_EINVAL";
+        case SSM_ENOTSUP: return "SSM_ENOTSUP";
+        case SSM_EHIP: return "SSM_EHIP";
+    }
+    return "SSM_UNKNOWN";
+}
+
+const char *ssm_last_error(void) { return g_err; }
+
+int ssm_abi_version(void) { return SSM_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,84 @@
+// Device helpers shared by the gfx950 kernels of libssm.so.
+//
+// Storage types: float (fp32) and uint16_t holding bfloat16 bits. All arithmetic
+// is fp32. bf16 -> fp32 is a 16-bit shift (exact); fp32 -> bf16 uses the native
+// round-to-nearest-even conversion of gfx950.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssm {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Pointer into the constant address space: uniform loads through it become
+// scalar (s_load) loads, so a value shared by the whole wave (B_t, C_t) lands
+// in SGPRs and costs no vector instruction to broadcast. Only used for buffers
+// that no kernel of the same launch writes.
+typedef const __attribute__((address_space(4))) uint32_t cu32;
+
+__device__ __forceinline__ cu32 *as_const(const void *p) { return (cu32 *)(p); }
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(uint16_t v) { return __uint_as_float(uint32_t(v) << 16); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float v) {
+    __bf16 b = (__bf16)v;  // v_cvt_pk_bf16_f32: round to nearest even
+    return __builtin_bit_cast(uint16_t, b);
+}
+__device__ __forceinline__ void store_val(float *p, float v) { *p = v; }
+__device__ __forceinline__ void store_val(uint16_t *p, float v) { *p = f32_to_bf16(v); }
+
+__device__ __forceinline__ float fast_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
+__device__ __forceinline__ float fast_log2(float v) { return __builtin_amdgcn_logf(v); }
+__device__ __forceinline__ float fast_rcp(float v) { return __builtin_amdgcn_rcpf(v); }
+
+// softplus(v) = log(1 + e^v) = max(v, 0) + log1p(e^{-|v|}).
+// log1p(u) for u in (0, 1] is taken as log(w) + (u - (w - 1)) with w = 1 + u:
+// the second term is the exact rounding error of 1 + u, so small steps keep
+// their full relative precision (a plain log(1 + e^v) loses it below ~1e-3).
+__device__ __forceinline__ float softplus_f32(float v) {
+    const float u = fast_exp2(-fabsf(v) * kLog2e);
+    const float w = 1.0f + u;
+    const float c = u - (w - 1.0f);
+    return fmaxf(v, 0.0f) + fmaf(fast_log2(w), kLn2, c);
+}
+
+// silu(z) = z / (1 + e^{-z}); for z -> -inf the reciprocal of +inf is 0.
+__device__ __forceinline__ float silu_f32(float z) {
+    return z * fast_rcp(1.0f + fast_exp2(-z * kLog2e));
+}
+
+// One row of a (L, N) B or C matrix shared by the whole wave, loaded with scalar
+// loads and widened to fp32 (SGPR-resident).
+template <typename T, int N>
+struct SharedRow;
+
+template <int N>
+struct SharedRow<uint16_t, N> {
+    __device__ __forceinline__ static void load(const uint16_t *row, float (&out)[N]) {
+        cu32 *p = as_const(row);
+#pragma unroll
+        for (int j = 0; j < N / 2; ++j) {
+            const uint32_t w = p[j];
+            out[2 * j] = bf16_lo(w);
+            out[2 * j + 1] = bf16_hi(w);
+        }
+    }
+};
+
+template <int N>
+struct SharedRow<float, N> {
+    __device__ __forceinline__ static void load(const float *row, float (&out)[N]) {
+        cu32 *p = as_const(row);
+#pragma unroll
+        for (int j = 0; j < N; ++j) out[j] = __uint_as_float(p[j]);
+    }
+};
+
+}  // namespace ssm

@@ -1,0 +1,40 @@
+// Host-side interfaces between the C ABI (capi.hip) and the kernel launchers.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "ssm.h"
+
+namespace ssm {
+
+// How one selective-scan call is split along time.
+//   chunks     : number of time chunks G (1 = no split)
+//   chunk_len  : steps per chunk (the last one may be shorter)
+// Workspace (when G > 1): carry[G-1][B][D][N] fp32, then dsum[G-1][B][D] fp64.
+struct ScanPlan {
+    int64_t chunks;
+    int64_t chunk_len;
+    size_t carry_offset;
+    size_t dsum_offset;
+    size_t bytes;
+};
+
+ScanPlan scan_plan(const ssm_scan_args &a);
+// Enqueue the kernels of one call; returns SSM_EHIP with `err` filled on a refused launch.
+ssm_status scan_launch(const ssm_scan_args &a, const ScanPlan &plan, hipStream_t stream,
+                       char *err, size_t errlen);
+
+// SSD (scalar A per head) plan: chunk states and the carried state per chunk.
+struct SSDPlan {
+    int64_t nchunks;
+    size_t states_offset;   // fp32 [B][nchunks][H][N][P]
+    size_t decay_offset;    // fp32 [B][H][nchunks]
+    size_t bytes;
+};
+
+SSDPlan ssd_plan(const ssm_ssd_args &a);
+ssm_status ssd_launch(const ssm_ssd_args &a, const SSDPlan &plan, hipStream_t stream,
+                      char *err, size_t errlen);
+
+}  // namespace ssm

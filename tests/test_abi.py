@@ -1,0 +1,167 @@
+"""C ABI of libssm.so on the CPU: the library loads without a GPU, exports every
+symbol include/ssm.h declares, and its host-side argument checks return the
+documented status codes before any HIP call. No compute call is made here."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from selective_state_space_70_amd import _capi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssm.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^[A-Za-z_][\w\s\*]*?\b(\w+)\s*\([^;{]*\)\s*;", text, flags=re.M)
+
+
+def test_header_declarations_match_binding():
+    decl = declared_functions()
+    assert sorted(decl) == sorted(_capi.EXPORTS), decl
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _capi.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_status_names():
+    lib = _capi.lib()
+    assert lib.ssm_abi_version() == _capi.ABI_VERSION == 1
+    names = [lib.ssm_status_str(s).decode() for s in range(4)]
+    assert names == ["SSM_OK", "SSM_EINVAL", "SSM_ENOTSUP", "SSM_EHIP"]
+    assert lib.ssm_status_str(99).decode() == "SSM_UNKNOWN"
+
+
+FAKE = 0x10000000  # never dereferenced: only host-side checks run
+
+
+def scan_args(**kw):
+    a = _capi.ScanArgs()
+    a.batch, a.seqlen, a.dim, a.dstate = 2, 100, 96, 16
+    a.dtype, a.delta_softplus = _capi.SSM_BF16, 1
+    for name in ("x", "delta", "z", "Bm", "Cm", "A", "delta_bias", "Dskip", "h0", "y", "h_final"):
+        setattr(a, name, FAKE)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def ssd_args(**kw):
+    a = _capi.SSDArgs()
+    a.batch, a.seqlen, a.nheads, a.headdim, a.dstate, a.chunk = 2, 500, 8, 64, 128, 256
+    a.dtype, a.dt_softplus = _capi.SSM_BF16, 1
+    for name in ("x", "dt", "dt_bias", "A", "Bm", "Cm", "Dskip", "z", "h0", "y", "h_final"):
+        setattr(a, name, FAKE)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def scan_status(a):
+    return _capi.lib().selective_scan_validate(ctypes.byref(a))
+
+
+def ssd_status(a):
+    return _capi.lib().ssd_chunked_validate(ctypes.byref(a))
+
+
+@pytest.mark.parametrize("kw,want", [
+    ({}, _capi.SSM_OK),
+    ({"dtype": _capi.SSM_F32}, _capi.SSM_OK),
+    ({"z": None, "delta_bias": None, "Dskip": None, "h0": None, "h_final": None}, _capi.SSM_OK),
+    ({"dstate": 32}, _capi.SSM_OK),
+    ({"dstate": 64}, _capi.SSM_OK),
+    ({"x": None}, _capi.SSM_EINVAL),
+    ({"delta": None}, _capi.SSM_EINVAL),
+    ({"Bm": None}, _capi.SSM_EINVAL),
+    ({"y": None}, _capi.SSM_EINVAL),
+    ({"A": None}, _capi.SSM_EINVAL),
+    ({"batch": -1}, _capi.SSM_EINVAL),
+    ({"seqlen": -5}, _capi.SSM_EINVAL),
+    ({"dim": 0}, _capi.SSM_EINVAL),
+    ({"dtype": 7}, _capi.SSM_EINVAL),
+    ({"y": FAKE + 1}, _capi.SSM_EINVAL),                       # bf16 needs 2-byte alignment
+    ({"dtype": _capi.SSM_F32, "x": FAKE + 2}, _capi.SSM_EINVAL),  # fp32 needs 4
+    ({"Bm": FAKE + 2}, _capi.SSM_EINVAL),
+    ({"h0": FAKE + 2}, _capi.SSM_EINVAL),
+    ({"dstate": 8}, _capi.SSM_ENOTSUP),
+    ({"dstate": 128}, _capi.SSM_ENOTSUP),
+    ({"batch": 70000}, _capi.SSM_ENOTSUP),
+    ({"seqlen": 1 << 20, "dim": 1 << 12}, _capi.SSM_ENOTSUP),   # row of 8 GiB
+    ({"batch": 0, "x": None, "y": None}, _capi.SSM_OK),        # empty batch: nothing to read
+    ({"seqlen": 0, "x": None, "y": None, "Bm": None}, _capi.SSM_OK),
+])
+def test_scan_validation(kw, want):
+    assert scan_status(scan_args(**kw)) == want
+    msg = _capi.lib().ssm_last_error().decode()
+    assert (msg == "") == (want == _capi.SSM_OK)
+
+
+@pytest.mark.parametrize("kw,want", [
+    ({}, _capi.SSM_OK),
+    ({"dstate": 64, "chunk": 64}, _capi.SSM_OK),
+    ({"dstate": 256, "chunk": 128}, _capi.SSM_OK),
+    ({"z": None, "dt_bias": None, "Dskip": None, "h0": None, "h_final": None}, _capi.SSM_OK),
+    ({"x": None}, _capi.SSM_EINVAL),
+    ({"dt": None}, _capi.SSM_EINVAL),
+    ({"A": None}, _capi.SSM_EINVAL),
+    ({"chunk": 0}, _capi.SSM_EINVAL),
+    ({"x": FAKE + 8}, _capi.SSM_EINVAL),                      # 16-byte vectors
+    ({"Cm": FAKE + 4}, _capi.SSM_EINVAL),
+    ({"dtype": _capi.SSM_F32}, _capi.SSM_ENOTSUP),
+    ({"headdim": 32}, _capi.SSM_ENOTSUP),
+    ({"dstate": 96}, _capi.SSM_ENOTSUP),
+    ({"chunk": 100}, _capi.SSM_ENOTSUP),
+    ({"batch": 0, "x": None}, _capi.SSM_OK),
+])
+def test_ssd_validation(kw, want):
+    assert ssd_status(ssd_args(**kw)) == want
+
+
+def test_fwd_rejects_before_any_hip_call():
+    lib = _capi.lib()
+    assert lib.selective_scan_fwd(ctypes.byref(scan_args(x=None)), None) == _capi.SSM_EINVAL
+    assert lib.ssd_chunked_fwd(ctypes.byref(ssd_args(dt=None)), None) == _capi.SSM_EINVAL
+    assert lib.selective_scan_fwd(None, None) == _capi.SSM_EINVAL
+    # a call that needs workspace but gets none is refused on the host
+    a = scan_args(batch=8, seqlen=2048, dim=1536)
+    assert lib.selective_scan_workspace_bytes(ctypes.byref(a)) > 0
+    assert lib.selective_scan_fwd(ctypes.byref(a), None) == _capi.SSM_EINVAL
+    assert "workspace" in lib.ssm_last_error().decode()
+    a.workspace, a.workspace_bytes = FAKE + 64, 1 << 30
+    assert lib.selective_scan_fwd(ctypes.byref(a), None) == _capi.SSM_EINVAL  # not 256-aligned
+    s = ssd_args()
+    assert lib.ssd_chunked_fwd(ctypes.byref(s), None) == _capi.SSM_EINVAL
+    # batch == 0 is a no-op that returns before touching HIP
+    assert lib.selective_scan_fwd(ctypes.byref(scan_args(batch=0)), None) == _capi.SSM_OK
+
+
+def test_workspace_sizes():
+    lib = _capi.lib()
+    # one (b, d) block and a short sequence: no time split, no workspace
+    assert lib.selective_scan_workspace_bytes(ctypes.byref(scan_args(batch=1, seqlen=64, dim=64))) == 0
+    # long sequence, few channels: split along time, carry + summed-step slots
+    a = scan_args(batch=1, seqlen=131072, dim=2048)
+    ws = lib.selective_scan_workspace_bytes(ctypes.byref(a))
+    assert ws > 0 and ws % 256 == 0
+    # SSD: fp32 chunk states (B * chunks * H * N * P) plus per-chunk decays
+    s = ssd_args(batch=2, seqlen=8192, nheads=64, dstate=128, chunk=256)
+    need = lib.ssd_chunked_workspace_bytes(ctypes.byref(s))
+    assert need >= 2 * 32 * 64 * 128 * 64 * 4
+    assert lib.ssd_chunked_workspace_bytes(ctypes.byref(ssd_args(headdim=32))) == 0
+
+
+def test_binding_rejects_host_tensors():
+    import selective_state_space_70_amd as ssm
+    x = torch.zeros(1, 4, 64)
+    A = torch.zeros(64, 16)
+    B = torch.zeros(1, 4, 16)
+    with pytest.raises(ValueError):
+        ssm.selective_scan_fwd(x, x, A, B, B)

@@ -1,0 +1,131 @@
+"""Selective scan on the GPU vs the fp64 oracle, element by element.
+
+Tolerances: relative L2 <= 1e-5 for fp32 inputs, <= 3e-3 for bf16 inputs
+(fp32 state), on y and on the final state separately."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import TOL, oracle_scan, report, run_scan, sample_channels, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(name, inp, softplus=True, tol=None):
+    y, hf = run_scan(inp, softplus)
+    yo, ho = oracle_scan(inp, softplus)
+    ey, eh = oracle.rel_l2(y, yo), oracle.rel_l2(hf, ho)
+    report(name, ey, eh)
+    tol = tol or TOL[inp["dtype"]]
+    assert ey <= tol and eh <= tol, (name, ey, eh)
+    assert np.isfinite(y).all()
+
+
+def test_tiny_fp32_config():
+    """The tiny fp32 workload: batch 1, L 256, D 64, N 16."""
+    _check("S1", workloads.make_inputs("S1"))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("L", [1, 2, 63, 257, 1000])
+def test_ragged_lengths(dtype, L):
+    inp = workloads.scan_inputs(3, L, 100, 16, dtype, seed=L, with_h0=True)
+    _check("L=%d %s" % (L, dtype), inp)
+
+
+@pytest.mark.parametrize("N", [16, 32, 64])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_state_sizes(N, dtype):
+    inp = workloads.scan_inputs(2, 300, 130, N, dtype, seed=N, with_h0=True)
+    _check("N=%d %s" % (N, dtype), inp)
+
+
+@pytest.mark.parametrize("drop", ["z", "Dskip", "delta_bias", "h0"])
+def test_optional_inputs_absent(drop):
+    inp = workloads.scan_inputs(2, 200, 64, 16, "f32", seed=3, with_h0=True)
+    inp[drop] = None
+    _check("no %s" % drop, inp)
+
+
+def test_softplus_off():
+    """dt = delta + bias used as is: a positive raw step and no bias (the
+    inverse-softplus bias of the generator is negative)."""
+    inp = workloads.scan_inputs(2, 150, 64, 16, "f32", seed=4, with_bias=False)
+    inp["delta"] = np.abs(inp["delta"]) * np.float32(0.2)
+    _check("softplus off", inp, softplus=False)
+
+
+def test_general_A_rows():
+    """Rows of A that are not (n+1) * A[d,0] take the exponential-per-state path;
+    mix both kinds in one wave and in separate waves."""
+    inp = workloads.scan_inputs(2, 333, 192, 16, "f32", seed=5, with_h0=True)
+    rng = np.random.default_rng(5)
+    A = inp["A"].copy()
+    A[64:128] = -rng.uniform(0.1, 4.0, size=(64, 16)).astype(np.float32)   # a whole wave
+    A[130] = -rng.uniform(0.1, 4.0, size=16).astype(np.float32)             # one lane of a wave
+    inp["A"] = A
+    _check("general A", inp)
+    inp2 = dict(inp, dtype="bf16", **{k: workloads.round_bf16(inp[k]) for k in
+                                      ("x", "delta", "z", "Bm", "Cm")})
+    _check("general A bf16", inp2)
+
+
+@pytest.mark.parametrize("chunks", [2, 5, 17])
+def test_forced_time_chunks(monkeypatch, chunks):
+    """The time split (chunk end states, carry, rerun) with a ragged last chunk."""
+    monkeypatch.setenv("SSM_SCAN_CHUNKS", str(chunks))
+    inp = workloads.scan_inputs(2, 517, 70, 16, "f32", seed=chunks, with_h0=True)
+    _check("G=%d" % chunks, inp)
+
+
+def test_split_invariance_on_gpu():
+    """Handing the GPU final state of x[0:L1] to a second call equals one call."""
+    inp = workloads.scan_inputs(2, 400, 64, 16, "f32", seed=9, with_h0=True)
+    y, hf = run_scan(inp)
+    L1 = 157
+    a = {k: (v[:, :L1] if isinstance(v, np.ndarray) and v.ndim == 3 and v.shape[1] == 400 else v)
+         for k, v in inp.items()}
+    b = {k: (v[:, L1:] if isinstance(v, np.ndarray) and v.ndim == 3 and v.shape[1] == 400 else v)
+         for k, v in inp.items()}
+    y1, h1 = run_scan(a)
+    b["h0"] = h1
+    y2, h2 = run_scan(b)
+    assert oracle.rel_l2(np.concatenate([y1, y2], axis=1), y) < 1e-6
+    assert oracle.rel_l2(h2, hf) < 1e-6
+
+
+def test_empty_sequence_copies_state():
+    inp = workloads.scan_inputs(2, 0, 64, 16, "f32", seed=1, with_h0=True)
+    y, hf = run_scan(inp)
+    assert y.shape == (2, 0, 64)
+    np.testing.assert_array_equal(hf, inp["h0"])
+
+
+def test_deterministic():
+    inp = workloads.scan_inputs(4, 700, 200, 16, "bf16", seed=11, with_h0=True)
+    y1, h1 = run_scan(inp)
+    y2, h2 = run_scan(inp)
+    assert np.array_equal(y1, y2) and np.array_equal(h1, h2)
+
+
+@pytest.mark.parametrize("key", ["S2", "S3", "S4"])
+def test_full_size_sampled(key):
+    """Full-size workloads in the launch configuration the benchmark times; the
+    oracle evaluates a sample of channels over the whole sequence."""
+    cfg = workloads.CONFIGS[key]
+    print("generating %s" % key, flush=True)
+    inp = workloads.make_inputs(key)
+    y, hf = run_scan(inp)
+    ch = sample_channels(cfg.batch * cfg.dim, 24 if key == "S4" else 48, seed=cfg.index)
+    yo, ho = oracle_scan(inp, channels=ch)
+    b, d = ch // cfg.dim, ch % cfg.dim
+    ys = y[b, :, d]                       # (channels, L)
+    hs = hf.reshape(-1, cfg.dstate)[ch]
+    ey, eh = oracle.rel_l2(ys, yo), oracle.rel_l2(hs, ho)
+    report(key + " sampled", ey, eh)
+    assert ey <= TOL["bf16"] and eh <= TOL["bf16"]
+    assert np.isfinite(y).all() and np.isfinite(hf).all()

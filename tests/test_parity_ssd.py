@@ -1,0 +1,84 @@
+"""Scalar-A (SSD) chunked form on the GPU matrix cores vs the fp64 oracle
+(plain per-step recurrence). bf16 inputs, fp32 state: relative L2 <= 3e-3 on y
+and on the final state."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_util import TOL, oracle_ssd, report, run_ssd, sample_channels
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(name, inp, chunk, softplus=True):
+    y, hf = run_ssd(inp, chunk, softplus)
+    yo, ho = oracle_ssd(inp, softplus)
+    ey, eh = oracle.rel_l2(y, yo), oracle.rel_l2(hf, ho)
+    report(name, ey, eh)
+    assert ey <= TOL["bf16"] and eh <= TOL["bf16"], (name, ey, eh)
+    assert np.isfinite(y).all()
+    return y, hf
+
+
+@pytest.mark.parametrize("chunk", [64, 128, 256])
+@pytest.mark.parametrize("L", [1, 64, 150, 600])
+def test_lengths_and_chunks(L, chunk):
+    inp = workloads.ssd_inputs(1, L, 3, 64, 128, "bf16", seed=L + chunk, with_h0=True)
+    _check("L=%d Q=%d" % (L, chunk), inp, chunk)
+
+
+@pytest.mark.parametrize("N", [64, 128, 256])
+def test_state_sizes(N):
+    inp = workloads.ssd_inputs(2, 300, 4, 64, N, "bf16", seed=N, with_h0=True)
+    _check("N=%d" % N, inp, 128)
+
+
+def test_gate_and_no_skip():
+    inp = workloads.ssd_inputs(2, 333, 3, 64, 64, "bf16", seed=21, with_z=True, with_D=False)
+    _check("z, no D", inp, 64)
+
+
+def test_no_bias_softplus_off():
+    inp = workloads.ssd_inputs(1, 260, 2, 64, 64, "bf16", seed=22, with_bias=False)
+    inp["dt"] = workloads.round_bf16(np.abs(inp["dt"]) * np.float32(0.1))
+    _check("softplus off", inp, 128, softplus=False)
+
+
+def test_chunk_invariance():
+    inp = workloads.ssd_inputs(1, 1024, 2, 64, 128, "bf16", seed=23, with_h0=True)
+    ya, ha = run_ssd(inp, 64)
+    yb, hb = run_ssd(inp, 256)
+    # both are within tolerance of the oracle; they also agree with each other
+    assert oracle.rel_l2(ya, yb) <= 3e-3 and oracle.rel_l2(ha, hb) <= 3e-3
+
+
+def test_empty_sequence_copies_state():
+    inp = workloads.ssd_inputs(1, 0, 2, 64, 64, "bf16", seed=1, with_h0=True)
+    y, hf = run_ssd(inp, 64)
+    assert y.shape == (1, 0, 2, 64)
+    np.testing.assert_array_equal(hf, inp["h0"])
+
+
+def test_deterministic():
+    inp = workloads.ssd_inputs(1, 700, 4, 64, 128, "bf16", seed=24)
+    y1, h1 = run_ssd(inp, 256)
+    y2, h2 = run_ssd(inp, 256)
+    assert np.array_equal(y1, y2) and np.array_equal(h1, h2)
+
+
+def test_full_size_sampled():
+    """The Mamba-2 SSD workload (batch 2, L 8192, 64 heads x 64, N 128, chunk 256);
+    the oracle runs the recurrence for a sample of (b, h, p) channels."""
+    cfg = workloads.CONFIGS["S5"]
+    inp = workloads.make_inputs("S5")
+    y, hf = run_ssd(inp, cfg.chunk)
+    total = cfg.batch * cfg.nheads * cfg.headdim
+    ch = sample_channels(total, 64, seed=cfg.index)
+    yo, ho = oracle_ssd(inp, channels=ch)
+    ys = y.transpose(0, 2, 3, 1).reshape(total, cfg.seqlen)[ch]
+    hs = hf.reshape(total, cfg.dstate)[ch]
+    ey, eh = oracle.rel_l2(ys, yo), oracle.rel_l2(hs, ho)
+    report("S5 sampled", ey, eh)
+    assert ey <= TOL["bf16"] and eh <= TOL["bf16"]
+    assert np.isfinite(y).all()
