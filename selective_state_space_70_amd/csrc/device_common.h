@@ -34,6 +34,27 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float v) {
 __device__ __forceinline__ void store_val(float *p, float v) { *p = v; }
 __device__ __forceinline__ void store_val(uint16_t *p, float v) { *p = f32_to_bf16(v); }
 
+// Raw buffer access: the base and size live in a wave-uniform resource (SGPRs),
+// the row offset is a uniform byte offset (soffset) and the lane adds a fixed
+// byte offset (voffset), so streaming along time needs no vector address math.
+// Reads at or past `bytes` return 0 (hardware range check on the vector offset).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void buf_load(rsrc_t r, uint32_t voff, uint32_t soff, uint16_t &v) {
+    v = __builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, 0);
+}
+__device__ __forceinline__ void buf_load(rsrc_t r, uint32_t voff, uint32_t soff, float &v) {
+    v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0));
+}
+__device__ __forceinline__ void buf_store(rsrc_t r, uint32_t voff, uint32_t soff, uint16_t v) {
+    __builtin_amdgcn_raw_buffer_store_b16(v, r, (int)voff, (int)soff, 0);
+}
+__device__ __forceinline__ void buf_store(rsrc_t r, uint32_t voff, uint32_t soff, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, (int)voff, (int)soff, 0);
+}
+
 __device__ __forceinline__ float fast_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
 __device__ __forceinline__ float fast_log2(float v) { return __builtin_amdgcn_logf(v); }
 __device__ __forceinline__ float fast_rcp(float v) { return __builtin_amdgcn_rcpf(v); }
