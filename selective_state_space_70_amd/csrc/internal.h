@@ -11,12 +11,12 @@ namespace ssm {
 // How one selective-scan call is split along time.
 //   chunks     : number of time chunks G (1 = no split)
 //   chunk_len  : steps per chunk (the last one may be shorter)
-// Workspace (when G > 1): carry[G-1][B][D][N] fp32, then dsum[G-1][B][D] fp64.
+// Workspace (when G > 1), per chain of 64 channels: aggregates[G-1][N+1][64]
+// (fp32 end state from a zero state, then the summed step).
 struct ScanPlan {
     int64_t chunks;
     int64_t chunk_len;
-    size_t carry_offset;
-    size_t dsum_offset;
+    size_t agg_offset;
     size_t bytes;
 };
 

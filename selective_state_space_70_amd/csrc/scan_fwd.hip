@@ -32,6 +32,7 @@
 #include <cstdio>
 #include <cstdlib>
 
+#include "chain.h"
 #include "device_common.h"
 #include "internal.h"
 
@@ -43,13 +44,13 @@ struct ScanK {
     const float *A, *bias, *Dskip, *h0;
     void *y;
     float *h_final;
-    float *carry;     // [G-1][B][D][N]
-    double *dsum;     // [G-1][B][D]
+    float *agg;       // [chains][G-1][N+1][64]: end state from zero, then summed step
     int64_t L;
     int64_t chunk_len;
     int32_t D;
     int32_t batch;
-    int32_t chunks;
+    int32_t chunks;     // G
+    int32_t dblocks;    // ceil(D / 64)
     int32_t softplus;
 };
 
@@ -331,15 +332,29 @@ __device__ __forceinline__ Chan<N> load_chan(const ScanK &p, int dc) {
     return c;
 }
 
-// Pass 1: end state and summed step of chunk j (0 <= j < G-1) from a zero state.
+// exp(A[d, n] * s) for all n (the decay a chunk with summed step s applies).
+template <int N, bool FAST>
+__device__ __forceinline__ void chunk_decay(const Chan<N> &c, float s, float (&P)[N]) {
+    if constexpr (FAST) {
+        powers<N>(fast_exp2(c.Al2[0] * s), P);
+    } else {
+#pragma unroll
+        for (int n = 0; n < N; ++n) P[n] = fast_exp2(c.Al2[n] * s);
+    }
+}
+
+// Pass 1: the end state of chunk k (k < G-1) from a zero state and its summed
+// step, stored for the chunks after it (layout [chain][k][n][lane]: one
+// contiguous 256-byte row per state index).
 template <typename T, int N>
 __global__ __launch_bounds__(64) void scan_chunk_state_kernel(const ScanK p) {
-    const int d = blockIdx.x * 64 + threadIdx.x;
-    const int b = blockIdx.y;
-    const int j = blockIdx.z;
-    const bool act = d < p.D;
-    const int dc = act ? d : p.D - 1;
-    const int t0 = (int)((int64_t)j * p.chunk_len);
+    const ChainSlot slot = chain_slot(p.batch * p.dblocks, p.chunks - 1);
+    if (!slot.valid) return;
+    const int b = slot.chain / p.dblocks;
+    const int d = (slot.chain % p.dblocks) * 64 + threadIdx.x;
+    const int dc = d < p.D ? d : p.D - 1;
+    const int k = slot.pos;
+    const int t0 = (int)((int64_t)k * p.chunk_len);
     const int t1 = (int)min(p.L, (int64_t)t0 + p.chunk_len);
     const Chan<N> c = load_chan<N>(p, dc);
     float S[N];
@@ -349,78 +364,76 @@ __global__ __launch_bounds__(64) void scan_chunk_state_kernel(const ScanK p) {
     const double ds = __all(row_is_geometric<N>(p.A + (int64_t)dc * N))
                           ? run_aggregate<T, N, true>(p, b, dc, t0, t1, S, c)
                           : run_aggregate<T, N, false>(p, b, dc, t0, t1, S, c);
-    if (act) {
-        const int64_t ci = ((int64_t)j * p.batch + b) * p.D + d;
-        float *out = p.carry + ci * N;
+    float *a = p.agg + ((size_t)slot.chain * (p.chunks - 1) + k) * (N + 1) * 64 + threadIdx.x;
 #pragma unroll
-        for (int n = 0; n < N; ++n) out[n] = S[n];
-        p.dsum[ci] = ds;
-    }
+    for (int n = 0; n < N; ++n) a[n * 64] = S[n];
+    a[N * 64] = (float)ds;
 }
 
-// Pass 2: sequential composition over chunks, one thread per (b, d, n). Slot j is
-// overwritten with the state entering chunk j+1. The slots and summed steps of
-// a batch of chunks are loaded together so their latencies overlap.
-__global__ __launch_bounds__(256) void scan_carry_kernel(const ScanK p, int N) {
-    constexpr int K = 8;
-    const int64_t per = (int64_t)p.batch * p.D * N;
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= per) return;
-    const int64_t n = i % N;
-    const int64_t bd = i / N;
-    const int64_t d = bd % p.D;
-    const double al2 = (double)p.A[d * N + n] * 1.4426950408889634;
-    const int64_t bdn = (int64_t)p.batch * p.D;
-    float h = p.h0 ? p.h0[i] : 0.0f;
-    const int nslots = p.chunks - 1;
-    for (int j0 = 0; j0 < nslots; j0 += K) {
-        float sv[K];
-        double ds[K];
+// State entering chunk k: h0 (or zero) carried through chunks 0..k-1 by their
+// affine maps h -> exp(A sum dt) o h + S_j, in order. The aggregates of one chain
+// were written by workgroups on the same XCD, so these reads hit its L2; the loads
+// of a group of chunks are issued together.
+template <int N, bool FAST>
+__device__ __forceinline__ void enter_state(const ScanK &p, const Chan<N> &c, int chain, int k,
+                                            float (&h)[N]) {
+    constexpr int K = 4;
+    const float *a0 = p.agg + (size_t)chain * (p.chunks - 1) * (N + 1) * 64 + threadIdx.x;
+    for (int j0 = 0; j0 < k; j0 += K) {
+        float S[K][N], ds[K];
 #pragma unroll
         for (int u = 0; u < K; ++u) {
-            const int j = min(j0 + u, nslots - 1);
-            sv[u] = p.carry[(int64_t)j * per + i];
-            ds[u] = p.dsum[(int64_t)j * bdn + bd];
+            const float *a = a0 + (size_t)min(j0 + u, k - 1) * (N + 1) * 64;
+#pragma unroll
+            for (int n = 0; n < N; ++n) S[u][n] = a[n * 64];
+            ds[u] = a[N * 64];
         }
 #pragma unroll
         for (int u = 0; u < K; ++u) {
-            if (j0 + u < nslots) {
-                h = fmaf(fast_exp2((float)(al2 * ds[u])), h, sv[u]);
-                p.carry[(int64_t)(j0 + u) * per + i] = h;
+            if (j0 + u < k) {
+                float P[N];
+                chunk_decay<N, FAST>(c, ds[u], P);
+#pragma unroll
+                for (int n = 0; n < N; ++n) h[n] = fmaf(P[n], h[n], S[u][n]);
             }
         }
     }
 }
 
-// Pass 3: every chunk from its entering state, with readout, gate and store.
-template <typename T, int N, bool HAS_Z>
-__global__ __launch_bounds__(64) void scan_main_kernel(const ScanK p) {
-    const int d = blockIdx.x * 64 + threadIdx.x;
-    const int b = blockIdx.y;
-    const int k = blockIdx.z;
-    const bool act = d < p.D;
-    const int dc = act ? d : p.D - 1;
+// Pass 2: every chunk from its entering state, with readout, gate and store; the
+// last chunk writes h_final.
+template <typename T, int N, bool HAS_Z, bool FAST>
+__device__ __forceinline__ void scan_chunk(const ScanK &p, const Chan<N> &c, int chain, int k, int b,
+                                           int dc, bool act) {
     const int t0 = (int)((int64_t)k * p.chunk_len);
     const int t1 = (int)min(p.L, (int64_t)t0 + p.chunk_len);
     const int64_t ci = (int64_t)b * p.D + dc;
-    const float *hin = nullptr;
-    if (k == 0)
-        hin = p.h0 ? p.h0 + ci * N : nullptr;
-    else
-        hin = p.carry + ((int64_t)(k - 1) * p.batch * p.D + ci) * N;
     float h[N];
 #pragma unroll
-    for (int n = 0; n < N; ++n) h[n] = hin ? hin[n] : 0.0f;
-    const Chan<N> c = load_chan<N>(p, dc);
-    if (__all(row_is_geometric<N>(p.A + (int64_t)dc * N)))
-        run_readout<T, N, true, HAS_Z>(p, b, dc, act, t0, t1, h, c);
-    else
-        run_readout<T, N, false, HAS_Z>(p, b, dc, act, t0, t1, h, c);
+    for (int n = 0; n < N; ++n) h[n] = p.h0 ? p.h0[ci * N + n] : 0.0f;
+    if (k > 0) enter_state<N, FAST>(p, c, chain, k, h);
+    run_readout<T, N, FAST, HAS_Z>(p, b, dc, act, t0, t1, h, c);
     if (k == p.chunks - 1 && p.h_final && act) {
         float *out = p.h_final + ci * N;
 #pragma unroll
         for (int n = 0; n < N; ++n) out[n] = h[n];
     }
+}
+
+template <typename T, int N, bool HAS_Z>
+__global__ __launch_bounds__(64) void scan_main_kernel(const ScanK p) {
+    const ChainSlot slot = chain_slot(p.batch * p.dblocks, p.chunks);
+    if (!slot.valid) return;
+    const int b = slot.chain / p.dblocks;
+    const int d = (slot.chain % p.dblocks) * 64 + threadIdx.x;
+    const bool act = d < p.D;
+    const int dc = act ? d : p.D - 1;
+    const Chan<N> c = load_chan<N>(p, dc);
+    // wave-uniform choice of the exact fast path
+    if (__all(row_is_geometric<N>(p.A + (int64_t)dc * N)))
+        scan_chunk<T, N, HAS_Z, true>(p, c, slot.chain, slot.pos, b, dc, act);
+    else
+        scan_chunk<T, N, HAS_Z, false>(p, c, slot.chain, slot.pos, b, dc, act);
 }
 
 // L == 0: the final state is the initial one.
@@ -430,22 +443,16 @@ __global__ __launch_bounds__(256) void copy_state_kernel(const float *h0, float 
 }
 
 template <typename T, int N>
-ssm_status launch_typed(const ScanK &k, const ScanPlan &plan, hipStream_t s) {
-    const dim3 blk(64);
-    const unsigned dblocks = (unsigned)((k.D + 63) / 64);
-    if (plan.chunks > 1) {
-        hipLaunchKernelGGL((scan_chunk_state_kernel<T, N>),
-                           dim3(dblocks, k.batch, (unsigned)(plan.chunks - 1)), blk, 0, s, k);
-        const int64_t per = (int64_t)k.batch * k.D * N;
-        hipLaunchKernelGGL(scan_carry_kernel, dim3((unsigned)((per + 255) / 256)), dim3(256), 0,
-                           s, k, N);
-    }
+ssm_status launch_typed(const ScanK &k, hipStream_t s) {
+    const int chains = k.batch * k.dblocks;
+    if (k.chunks > 1)
+        hipLaunchKernelGGL((scan_chunk_state_kernel<T, N>), dim3(chain_grid(chains, k.chunks - 1)),
+                           dim3(64), 0, s, k);
+    const int grid = chain_grid(chains, k.chunks);
     if (k.z)
-        hipLaunchKernelGGL((scan_main_kernel<T, N, true>), dim3(dblocks, k.batch, (unsigned)plan.chunks),
-                           blk, 0, s, k);
+        hipLaunchKernelGGL((scan_main_kernel<T, N, true>), dim3(grid), dim3(64), 0, s, k);
     else
-        hipLaunchKernelGGL((scan_main_kernel<T, N, false>), dim3(dblocks, k.batch, (unsigned)plan.chunks),
-                           blk, 0, s, k);
+        hipLaunchKernelGGL((scan_main_kernel<T, N, false>), dim3(grid), dim3(64), 0, s, k);
     return SSM_OK;
 }
 
@@ -472,10 +479,11 @@ ScanPlan scan_plan(const ssm_scan_args &a) {
     if (G > 1) pl.chunk_len = (pl.chunk_len + 7) / 8 * 8;   // whole 8-step blocks
     pl.chunks = (a.seqlen + pl.chunk_len - 1) / pl.chunk_len;
     if (pl.chunks > 1) {
-        const int64_t slots = (pl.chunks - 1) * a.batch * a.dim;
-        pl.carry_offset = 0;
-        pl.dsum_offset = ((size_t)(slots * a.dstate) * sizeof(float) + 255) & ~(size_t)255;
-        pl.bytes = pl.dsum_offset + (((size_t)slots * sizeof(double) + 255) & ~(size_t)255);
+        auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
+        const size_t chains = (size_t)a.batch * ((a.dim + 63) / 64);
+        const size_t G = (size_t)pl.chunks;
+        pl.agg_offset = 0;
+        pl.bytes = up(chains * (G - 1) * (a.dstate + 1) * 64 * sizeof(float));
     }
     return pl;
 }
@@ -495,16 +503,16 @@ ssm_status scan_launch(const ssm_scan_args &a, const ScanPlan &plan, hipStream_t
         k.x = a.x; k.delta = a.delta; k.z = a.z; k.Bm = a.Bm; k.Cm = a.Cm;
         k.A = a.A; k.bias = a.delta_bias; k.Dskip = a.Dskip; k.h0 = a.h0;
         k.y = a.y; k.h_final = a.h_final;
-        k.carry = plan.chunks > 1 ? (float *)((char *)a.workspace + plan.carry_offset) : nullptr;
-        k.dsum = plan.chunks > 1 ? (double *)((char *)a.workspace + plan.dsum_offset) : nullptr;
+        k.agg = plan.chunks > 1 ? (float *)((char *)a.workspace + plan.agg_offset) : nullptr;
         k.L = a.seqlen; k.chunk_len = plan.chunk_len; k.D = (int32_t)a.dim;
         k.batch = (int32_t)a.batch; k.chunks = (int32_t)plan.chunks;
+        k.dblocks = (int32_t)((a.dim + 63) / 64);
         k.softplus = a.delta_softplus ? 1 : 0;
         const bool bf = a.dtype == SSM_BF16;
         switch (a.dstate) {
-            case 16: bf ? launch_typed<uint16_t, 16>(k, plan, s) : launch_typed<float, 16>(k, plan, s); break;
-            case 32: bf ? launch_typed<uint16_t, 32>(k, plan, s) : launch_typed<float, 32>(k, plan, s); break;
-            case 64: bf ? launch_typed<uint16_t, 64>(k, plan, s) : launch_typed<float, 64>(k, plan, s); break;
+            case 16: bf ? launch_typed<uint16_t, 16>(k, s) : launch_typed<float, 16>(k, s); break;
+            case 32: bf ? launch_typed<uint16_t, 32>(k, s) : launch_typed<float, 32>(k, s); break;
+            case 64: bf ? launch_typed<uint16_t, 64>(k, s) : launch_typed<float, 64>(k, s); break;
             default: return SSM_ENOTSUP;
         }
     }

@@ -145,12 +145,15 @@ def test_fwd_rejects_before_any_hip_call():
 
 def test_workspace_sizes():
     lib = _capi.lib()
-    # one (b, d) block and a short sequence: no time split, no workspace
-    assert lib.selective_scan_workspace_bytes(ctypes.byref(scan_args(batch=1, seqlen=64, dim=64))) == 0
-    # long sequence, few channels: split along time, carry + summed-step slots
+    # a sequence too short to split, or enough channels to fill the GPU: no workspace
+    assert lib.selective_scan_workspace_bytes(ctypes.byref(scan_args(batch=1, seqlen=31, dim=64))) == 0
+    assert lib.selective_scan_workspace_bytes(ctypes.byref(scan_args(batch=64, seqlen=512, dim=4096))) == 0
+    # long sequence, few channels: split along time; one (N+1) x 64 fp32 aggregate
+    # per chain of 64 channels and chunk but the last
     a = scan_args(batch=1, seqlen=131072, dim=2048)
     ws = lib.selective_scan_workspace_bytes(ctypes.byref(a))
-    assert ws > 0 and ws % 256 == 0
+    chains, chunks = 2048 // 64, 4096 // (2048 // 64)
+    assert ws % 256 == 0 and ws >= chains * (chunks - 1) * 17 * 64 * 4
     # SSD: fp32 chunk states (B * chunks * H * N * P) plus per-chunk decays
     s = ssd_args(batch=2, seqlen=8192, nheads=64, dstate=128, chunk=256)
     need = lib.ssd_chunked_workspace_bytes(ctypes.byref(s))

@@ -74,12 +74,22 @@ def test_general_A_rows():
     _check("general A bf16", inp2)
 
 
-@pytest.mark.parametrize("chunks", [2, 5, 17])
-def test_forced_time_chunks(monkeypatch, chunks):
-    """The time split (chunk end states, carry, rerun) with a ragged last chunk."""
+@pytest.mark.parametrize("chunks,L", [(2, 517), (5, 517), (17, 517), (100, 2000)])
+def test_forced_time_chunks(monkeypatch, chunks, L):
+    """The time split (chunk aggregates, look-back hand-off, rerun) with a ragged
+    last chunk; 100 chunks of 24 steps exercise look-back past 64 predecessors."""
     monkeypatch.setenv("SSM_SCAN_CHUNKS", str(chunks))
-    inp = workloads.scan_inputs(2, 517, 70, 16, "f32", seed=chunks, with_h0=True)
+    inp = workloads.scan_inputs(2, L, 70, 16, "f32", seed=chunks, with_h0=True)
     _check("G=%d" % chunks, inp)
+
+
+@pytest.mark.parametrize("chunks", [3, 40])
+def test_forced_chunks_general_A_bf16(monkeypatch, chunks):
+    monkeypatch.setenv("SSM_SCAN_CHUNKS", str(chunks))
+    inp = workloads.scan_inputs(3, 900, 130, 32, "bf16", seed=40 + chunks, with_h0=True)
+    rng = np.random.default_rng(chunks)
+    inp["A"] = (-rng.uniform(0.05, 3.0, size=inp["A"].shape)).astype(np.float32)
+    _check("G=%d general bf16" % chunks, inp)
 
 
 def test_split_invariance_on_gpu():
