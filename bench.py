@@ -12,6 +12,15 @@ algorithmic bytes (x, delta, z, y once per (b,t,d), B and C once per (b,t),
 parameters and the final state once). `roofline` relates the dominant kernel's
 measured time to its bound; `cpu_baseline` is the fp64 oracle timed on the
 host cores over the same workload.
+
+The scan is bound by plain fp32 vector arithmetic, not by HBM: per (b,t,d,n)
+element the recurrence needs exp(dt A) (a multiply and an exponential, which
+issues at half rate: 2 slots), dt B x (a multiply once dt x is formed), the
+state FMA and the readout FMA, i.e. ALU_SLOTS_PER_ELEM = 6 issue slots. The
+peak is 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 39.3 T slots/s (no packed
+fp32). The dominant kernel is the apply pass (readout over every element); its
+duration is measured live with HIP events around selective_scan_apply calls on
+the stream the kernels run on.
 """
 from __future__ import annotations
 
@@ -31,6 +40,15 @@ import workloads  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix peak, TFLOP/s
+ALU_PEAK_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12   # non-packed fp32 VALU issue slots, T/s
+ALU_SLOTS_PER_ELEM = 6
+
+# HBM bytes of one apply-pass launch on the default workload, from rocprofv3
+# --pmc FETCH_SIZE and WRITE_SIZE runs (KiB per dispatch) scaled by what the
+# same counters read for a plain 256 MiB device copy (FETCH x2.0, WRITE x1.0;
+# see profiles/). Keyed by a hash of the scan kernel sources: any change to them
+# turns the figure into null until it is measured again.
+TRAFFIC = {("S2", "aa8657ca0033819f"): 89860 * 1024 * 2 + 49920 * 1024}
 METRIC = "scan effective HBM GB/s (% of peak) + Gelem/s over B·L·D·N"
 
 
@@ -77,7 +95,17 @@ def _device_inputs(inp, torch, dev):
     return out
 
 
-def time_scan(key, steps, warmup, torch, ssm):
+def scan_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha1()
+    csrc = os.path.join(ROOT, "selective_state_space_70_amd", "csrc")
+    for name in ("scan_fwd.hip", "device_common.h", "chain.h", "internal.h"):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def time_scan(key, steps, warmup, torch, ssm, passes="all"):
     cfg = workloads.CONFIGS[key]
     dev = torch.device("cuda:0")
     base = workloads.make_inputs(key)
@@ -92,18 +120,17 @@ def time_scan(key, steps, warmup, torch, ssm):
         t["y"] = torch.empty_like(t["x"])
         t["hf"] = torch.empty((cfg.batch, cfg.dim, cfg.dstate), dtype=torch.float32, device=dev)
         sets.append(t)
-    ws = torch.empty(max(1, ssm.scan_workspace_bytes(cfg.batch, cfg.seqlen, cfg.dim, cfg.dstate,
-                                                     sets[0]["x"].dtype)),
-                     dtype=torch.uint8, device=dev)
-
-    def step(i):
+    def call(i, which):
         t = sets[i % nsets]
         ssm.selective_scan_fwd(t["x"], t["delta"], t["A"], t["Bm"], t["Cm"], t["Dskip"], t["z"],
                                t["delta_bias"], None, out=t["y"], final_state_out=t["hf"],
-                               workspace=ws)
+                               workspace=ws[i % nsets], passes=which)
 
+    ws = [torch.empty(max(1, ssm.scan_workspace_bytes(cfg.batch, cfg.seqlen, cfg.dim, cfg.dstate,
+                                                      sets[0]["x"].dtype)),
+                      dtype=torch.uint8, device=dev) for _ in range(nsets)]
     for i in range(warmup):
-        step(i)
+        call(i, "all")
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -111,12 +138,29 @@ def time_scan(key, steps, warmup, torch, ssm):
     t0 = time.perf_counter()
     for i in range(steps):
         ev[i][0].record(stream)
-        step(i)
+        call(i, "all")
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     per_call = [a.elapsed_time(b) for a, b in ev]
-    return cfg, wall, per_call
+    if passes != "split":
+        return cfg, wall, per_call
+    # the two passes timed separately (same inputs, workspace per set)
+    ev1 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    ev2 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for i in range(steps):
+        ev1[i][0].record(stream)
+        call(i, "chunk_states")
+        ev1[i][1].record(stream)
+        ev2[i][0].record(stream)
+        call(i, "apply")
+        ev2[i][1].record(stream)
+    torch.cuda.synchronize()
+    states = [a.elapsed_time(b) for a, b in ev1]
+    apply_ = [a.elapsed_time(b) for a, b in ev2]
+    return cfg, wall, per_call, states, apply_
 
 
 def time_ssd(steps, warmup, torch, ssm):
@@ -170,7 +214,7 @@ def cpu_baseline(key, budget_s=10.0):
                               inp["Dskip"], inp["z"], inp["delta_bias"])
         runs += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or runs >= 20:
+        if el >= budget_s or runs >= 200:
             break
     per = el / runs
     return {"value": round(scan_alg_bytes(cfg) / per / 1e9, 3), "unit": "GB/s", "cores": threads,
@@ -188,7 +232,24 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--extra", action="store_true",
                     help="also time the other scan workloads and the SSD form (stderr + 'extra')")
+    ap.add_argument("--ssd-only", action="store_true",
+                    help="time only the Mamba-2 SSD workload and print its own JSON line "
+                         "(for profiling the SSD kernels; not the headline line)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run three plain 256 MiB device-to-device copies (the reference "
+                         "kernel of known size that calibrates the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
+    if args.copy_probe:
+        import torch
+        n = 256 * 1024 * 1024
+        a = torch.empty(n // 2, dtype=torch.bfloat16, device="cuda")
+        a.fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "copies": 3}))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(--gpus %d requested)." % args.gpus, file=sys.stderr)
@@ -197,11 +258,26 @@ def main():
     import torch
     import selective_state_space_70_amd as ssm
 
-    cfg, wall, per_call = time_scan(args.config, args.steps, args.warmup, torch, ssm)
+    if args.ssd_only:
+        c5, pc5 = time_ssd(args.steps, args.warmup, torch, ssm)
+        m5 = sum(pc5) / len(pc5)
+        tf = ssd_alg_flops(c5) / m5 / 1e9
+        print(json.dumps({"workload": "S5 " + c5.name, "ms_per_call": round(m5, 5),
+                          "GB/s": round(ssd_alg_bytes(c5) / m5 / 1e6, 1), "TFLOP/s": round(tf, 1),
+                          "mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}), flush=True)
+        return
+
+    cfg, wall, per_call, t_states, t_apply = time_scan(args.config, args.steps, args.warmup, torch,
+                                                       ssm, passes="split")
     ms = sum(per_call) / len(per_call)
+    ms_states = sum(t_states) / len(t_states)
+    ms_apply = sum(t_apply) / len(t_apply)
     alg = scan_alg_bytes(cfg)
     gbs = alg / (ms * 1e-3) / 1e9
     gelem = cfg.elements / (ms * 1e-3) / 1e9
+    slots = ALU_SLOTS_PER_ELEM * cfg.elements / (ms_apply * 1e-3) / 1e12
+    src_hash = scan_source_hash()
+    tr = TRAFFIC.get((args.config, src_hash))
     line = {
         "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
@@ -213,9 +289,16 @@ def main():
         "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4),
         "gelem_per_s": round(gelem, 2),
         "wall_s_timed": round(wall, 4),
-        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "selective_scan_fwd call (all kernels of one call)"},
+        "roofline": {"bound": "alu", "achieved": round(slots, 3), "peak": round(ALU_PEAK_TSLOTS, 2),
+                     "unit": "T VALU issue slots/s (fp32, non-packed)",
+                     "frac": round(slots / ALU_PEAK_TSLOTS, 4),
+                     "traffic": tr,
+                     "kernel": "scan_main_kernel (selective_scan_apply)",
+                     "kernel_ms": round(ms_apply, 5),
+                     "alg_per_unit": "%d slots per (b,t,d,n) element x %d elements"
+                                     % (ALU_SLOTS_PER_ELEM, cfg.elements),
+                     "source_hash": src_hash},
+        "passes_ms": {"chunk_states": round(ms_states, 5), "apply": round(ms_apply, 5)},
     }
     if args.extra:
         extra = {}

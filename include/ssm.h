@@ -129,11 +129,28 @@ typedef struct ssm_ssd_args {
  * SSM_EHIP (a launch was refused; earlier kernels of this call may have run). */
 ssm_status selective_scan_fwd(const ssm_scan_args *args, hipStream_t stream);
 
+/* The same computation in its two passes, for callers that time or schedule them
+ * separately (or exchange chunk states between devices of a sequence-sharded
+ * scan, where the state entering a shard is that shard's h0):
+ *   selective_scan_chunk_states: the end state of every time chunk but the last,
+ *     started from a zero state, plus its summed step, into `workspace`
+ *     (nothing when the call is not split in time).
+ *   selective_scan_apply: carries h0 through those chunk maps to get the state
+ *     entering each chunk, then runs every chunk again with readout: writes y
+ *     and h_final. Needs the workspace filled by selective_scan_chunk_states with
+ *     the same arguments (same sizes, inputs and workspace).
+ * selective_scan_fwd == selective_scan_chunk_states followed by selective_scan_apply.
+ * Errors as for selective_scan_fwd. */
+ssm_status selective_scan_chunk_states(const ssm_scan_args *args, hipStream_t stream);
+ssm_status selective_scan_apply(const ssm_scan_args *args, hipStream_t stream);
+
 /* Host-only check of `args` (no HIP call): the status selective_scan_fwd would
  * return from its argument checks, ignoring the workspace pointer and size. */
 ssm_status selective_scan_validate(const ssm_scan_args *args);
 
-/* Workspace bytes selective_scan_fwd needs for these sizes (0 if none). Host-only. */
+/* Workspace bytes selective_scan_fwd needs for these sizes (0 if none, or if the
+ * sizes, dtype or state size are invalid). Reads only batch, seqlen, dim, dstate
+ * and dtype; the pointers may be NULL. Host-only. */
 size_t selective_scan_workspace_bytes(const ssm_scan_args *args);
 
 /* Enqueue the chunked scalar-A (SSD) form. Errors as for selective_scan_fwd. */
@@ -142,7 +159,8 @@ ssm_status ssd_chunked_fwd(const ssm_ssd_args *args, hipStream_t stream);
 /* Host-only argument check of the SSD form, ignoring the workspace. */
 ssm_status ssd_chunked_validate(const ssm_ssd_args *args);
 
-/* Workspace bytes ssd_chunked_fwd needs for these sizes. Host-only. */
+/* Workspace bytes ssd_chunked_fwd needs for these sizes (0 if invalid). Reads only
+ * the sizes and dtype; the pointers may be NULL. Host-only. */
 size_t ssd_chunked_workspace_bytes(const ssm_ssd_args *args);
 
 /* Static name of a status code ("SSM_OK", ...). */

@@ -76,12 +76,17 @@ def selective_scan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm
                        h0: Optional[torch.Tensor] = None, delta_softplus: bool = True,
                        return_final_state: bool = True, out: Optional[torch.Tensor] = None,
                        final_state_out: Optional[torch.Tensor] = None,
-                       workspace: Optional[torch.Tensor] = None
+                       workspace: Optional[torch.Tensor] = None, passes: str = "all"
                        ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Selective scan. x, delta, z: (batch, L, D); Bm, Cm: (batch, L, N), all
     fp32 or all bf16; A: (D, N) fp32; Dskip, delta_bias: (D,) fp32;
     h0: (batch, D, N) fp32. Returns (y (batch, L, D) in x's dtype,
-    h_final (batch, D, N) fp32 or None)."""
+    h_final (batch, D, N) fp32 or None).
+
+    ``passes`` selects the C entry point: "all" (selective_scan_fwd),
+    "chunk_states" (selective_scan_chunk_states: fills ``workspace`` only) or
+    "apply" (selective_scan_apply: needs the ``workspace`` a "chunk_states" call
+    with the same arguments filled)."""
     if x.dim() != 3 or A.dim() != 2:
         raise ValueError("x must be (batch, L, D) and A (D, N)")
     if x.dtype not in _DT:
@@ -111,11 +116,15 @@ def selective_scan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm
     L_ = _capi.lib()
     _capi.check(L_.selective_scan_validate(ctypes.byref(a)))
     need = L_.selective_scan_workspace_bytes(ctypes.byref(a))
+    entry = {"all": L_.selective_scan_fwd, "chunk_states": L_.selective_scan_chunk_states,
+             "apply": L_.selective_scan_apply}[passes]
     if need:
         if workspace is None or workspace.numel() * workspace.element_size() < need:
+            if passes == "apply":
+                raise ValueError("passes='apply' needs the workspace filled by 'chunk_states'")
             workspace = torch.empty(need, dtype=torch.uint8, device=dev)
         a.workspace, a.workspace_bytes = workspace.data_ptr(), need
-    _capi.check(L_.selective_scan_fwd(ctypes.byref(a), _stream(dev)))
+    _capi.check(entry(ctypes.byref(a), _stream(dev)))
     return y, hf
 
 

@@ -25,7 +25,8 @@ size_t esize(ssm_dtype t) { return t == SSM_BF16 ? 2 : 4; }
 
 constexpr int64_t kMaxRowBytes = (int64_t)1 << 31;
 
-ssm_status check_scan(const ssm_scan_args *a) {
+// Sizes, dtype and supported shapes only (what the workspace query depends on).
+ssm_status check_scan_sizes(const ssm_scan_args *a) {
     if (!a) return fail(SSM_EINVAL, "selective_scan: args is NULL");
     if (a->batch < 0 || a->seqlen < 0 || a->dim <= 0 || a->dstate <= 0)
         return fail(SSM_EINVAL, "selective_scan: need batch >= 0, seqlen >= 0, dim > 0, dstate > 0 "
@@ -41,6 +42,13 @@ ssm_status check_scan(const ssm_scan_args *a) {
     const size_t es = esize(a->dtype);
     if (a->seqlen * a->dim * (int64_t)es >= kMaxRowBytes)
         return fail(SSM_ENOTSUP, "selective_scan: seqlen*dim*elem_size must be < 2^31 bytes");
+    return SSM_OK;
+}
+
+ssm_status check_scan(const ssm_scan_args *a) {
+    const ssm_status st = check_scan_sizes(a);
+    if (st != SSM_OK) return st;
+    const size_t es = esize(a->dtype);
     if (a->batch == 0) return SSM_OK;
     if (!a->A) return fail(SSM_EINVAL, "selective_scan: A is NULL");
     if (!aligned(a->A, 4) || !aligned(a->delta_bias, 4) || !aligned(a->Dskip, 4) ||
@@ -57,7 +65,7 @@ ssm_status check_scan(const ssm_scan_args *a) {
     return SSM_OK;
 }
 
-ssm_status check_ssd(const ssm_ssd_args *a) {
+ssm_status check_ssd_sizes(const ssm_ssd_args *a) {
     if (!a) return fail(SSM_EINVAL, "ssd_chunked: args is NULL");
     if (a->batch < 0 || a->seqlen < 0 || a->nheads <= 0 || a->headdim <= 0 || a->dstate <= 0 ||
         a->chunk <= 0)
@@ -81,6 +89,12 @@ ssm_status check_ssd(const ssm_ssd_args *a) {
         return fail(SSM_ENOTSUP, "ssd_chunked: seqlen*nheads*headdim*2 must be < 2^31 bytes");
     if ((a->seqlen + a->chunk - 1) / a->chunk > 65535)
         return fail(SSM_ENOTSUP, "ssd_chunked: at most 65535 chunks");
+    return SSM_OK;
+}
+
+ssm_status check_ssd(const ssm_ssd_args *a) {
+    const ssm_status st = check_ssd_sizes(a);
+    if (st != SSM_OK) return st;
     if (a->batch == 0) return SSM_OK;
     if (!a->A) return fail(SSM_EINVAL, "ssd_chunked: A is NULL");
     if (!aligned(a->A, 4) || !aligned(a->dt_bias, 4) || !aligned(a->Dskip, 4) ||
@@ -117,11 +131,11 @@ ssm_status selective_scan_validate(const ssm_scan_args *a) {
 }
 
 size_t selective_scan_workspace_bytes(const ssm_scan_args *a) {
-    if (check_scan(a) != SSM_OK) return 0;
+    if (check_scan_sizes(a) != SSM_OK) return 0;
     return ssm::scan_plan(*a).bytes;
 }
 
-ssm_status selective_scan_fwd(const ssm_scan_args *a, hipStream_t stream) {
+static ssm_status scan_passes(const ssm_scan_args *a, hipStream_t stream, int passes) {
     ssm_status s = check_scan(a);
     if (s != SSM_OK) return s;
     const ssm::ScanPlan plan = ssm::scan_plan(*a);
@@ -129,9 +143,21 @@ ssm_status selective_scan_fwd(const ssm_scan_args *a, hipStream_t stream) {
         s = check_workspace(a->workspace, a->workspace_bytes, plan.bytes, "selective_scan");
         if (s != SSM_OK) return s;
     }
-    s = ssm::scan_launch(*a, plan, stream, g_err, sizeof g_err);
+    s = ssm::scan_launch(*a, plan, stream, passes, g_err, sizeof g_err);
     if (s == SSM_OK) g_err[0] = 0;
     return s;
+}
+
+ssm_status selective_scan_fwd(const ssm_scan_args *a, hipStream_t stream) {
+    return scan_passes(a, stream, 3);
+}
+
+ssm_status selective_scan_chunk_states(const ssm_scan_args *a, hipStream_t stream) {
+    return scan_passes(a, stream, 1);
+}
+
+ssm_status selective_scan_apply(const ssm_scan_args *a, hipStream_t stream) {
+    return scan_passes(a, stream, 2);
 }
 
 ssm_status ssd_chunked_validate(const ssm_ssd_args *a) {
@@ -141,7 +167,7 @@ ssm_status ssd_chunked_validate(const ssm_ssd_args *a) {
 }
 
 size_t ssd_chunked_workspace_bytes(const ssm_ssd_args *a) {
-    if (check_ssd(a) != SSM_OK) return 0;
+    if (check_ssd_sizes(a) != SSM_OK) return 0;
     return ssm::ssd_plan(*a).bytes;
 }
 

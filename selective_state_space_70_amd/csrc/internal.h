@@ -22,13 +22,15 @@ struct ScanPlan {
 
 ScanPlan scan_plan(const ssm_scan_args &a);
 // Enqueue the kernels of one call; returns SSM_EHIP with `err` filled on a refused launch.
+// `passes`: bit 0 = chunk states, bit 1 = apply (readout).
 ssm_status scan_launch(const ssm_scan_args &a, const ScanPlan &plan, hipStream_t stream,
-                       char *err, size_t errlen);
+                       int passes, char *err, size_t errlen);
 
 // SSD (scalar A per head) plan: chunk states and the carried state per chunk.
 struct SSDPlan {
     int64_t nchunks;
-    size_t states_offset;   // fp32 [B][nchunks][H][N][P]
+    size_t states_offset;   // fp32 [B][nchunks][H][P][N]: chunk states from a zero state
+    size_t sin_offset;      // bf16 [B][nchunks][H][P][N]: state entering each chunk
     size_t decay_offset;    // fp32 [B][H][nchunks]
     size_t bytes;
 };

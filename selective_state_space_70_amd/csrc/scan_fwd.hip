@@ -443,11 +443,12 @@ __global__ __launch_bounds__(256) void copy_state_kernel(const float *h0, float 
 }
 
 template <typename T, int N>
-ssm_status launch_typed(const ScanK &k, hipStream_t s) {
+ssm_status launch_typed(const ScanK &k, hipStream_t s, int passes) {
     const int chains = k.batch * k.dblocks;
-    if (k.chunks > 1)
+    if (k.chunks > 1 && (passes & 1))
         hipLaunchKernelGGL((scan_chunk_state_kernel<T, N>), dim3(chain_grid(chains, k.chunks - 1)),
                            dim3(64), 0, s, k);
+    if (!(passes & 2)) return SSM_OK;
     const int grid = chain_grid(chains, k.chunks);
     if (k.z)
         hipLaunchKernelGGL((scan_main_kernel<T, N, true>), dim3(grid), dim3(64), 0, s, k);
@@ -488,12 +489,12 @@ ScanPlan scan_plan(const ssm_scan_args &a) {
     return pl;
 }
 
-ssm_status scan_launch(const ssm_scan_args &a, const ScanPlan &plan, hipStream_t s, char *err,
-                       size_t errlen) {
+ssm_status scan_launch(const ssm_scan_args &a, const ScanPlan &plan, hipStream_t s, int passes,
+                       char *err, size_t errlen) {
     if (a.batch == 0) return SSM_OK;
     (void)hipGetLastError();  // clear a stale error so the check below is ours
     if (a.seqlen == 0) {
-        if (a.h_final) {
+        if (a.h_final && (passes & 2)) {
             const int64_t n = a.batch * a.dim * a.dstate;
             hipLaunchKernelGGL(copy_state_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
                                s, a.h0, a.h_final, n);
@@ -510,9 +511,9 @@ ssm_status scan_launch(const ssm_scan_args &a, const ScanPlan &plan, hipStream_t
         k.softplus = a.delta_softplus ? 1 : 0;
         const bool bf = a.dtype == SSM_BF16;
         switch (a.dstate) {
-            case 16: bf ? launch_typed<uint16_t, 16>(k, s) : launch_typed<float, 16>(k, s); break;
-            case 32: bf ? launch_typed<uint16_t, 32>(k, s) : launch_typed<float, 32>(k, s); break;
-            case 64: bf ? launch_typed<uint16_t, 64>(k, s) : launch_typed<float, 64>(k, s); break;
+            case 16: bf ? launch_typed<uint16_t, 16>(k, s, passes) : launch_typed<float, 16>(k, s, passes); break;
+            case 32: bf ? launch_typed<uint16_t, 32>(k, s, passes) : launch_typed<float, 32>(k, s, passes); break;
+            case 64: bf ? launch_typed<uint16_t, 64>(k, s, passes) : launch_typed<float, 64>(k, s, passes); break;
             default: return SSM_ENOTSUP;
         }
     }

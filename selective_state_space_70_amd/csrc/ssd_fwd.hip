@@ -4,7 +4,7 @@
 // inside a chunk of Q steps, y = (L o C B^T o exp(cs_t - cs_s) o dt_s) x, and the
 // influence of everything before the chunk passes through one N x P state per
 // head [Mamba-2 page "Mamba-2：把状态空间模型和 Attention 统一到一个数学框架里", Core
-// idea step 2 (SSM as a structured attention-like matrix y = (L o M) x) and key
+// idea step 2 (the SSM as a structured attention-like matrix y = (L o M) x) and key
 // point 1 (semiseparable: every off-diagonal block is low rank, O(L) storage)].
 // With cs_t = sum_{k<=t in chunk} A dt_k:
 //   state of chunk c  : S_c = sum_s exp(cs_end - cs_s) dt_s B_s (x) x_s   (N x P)
@@ -12,20 +12,26 @@
 //   output            : y_t = sum_{s<=t} (C_t.B_s) exp(cs_t - cs_s) dt_s x_s
 //                            + exp(cs_t) C_t . Sin_c + D x_t,   then * silu(z_t)
 //
-// Kernels (one call):
-//   1. ssd_chunk_state : per (b, chunk, head), S_c on the MFMA units
-//      (v_mfma_f32_16x16x32_bf16, K = time), the decay exp(cs_end) of the chunk.
-//   2. ssd_state_pass  : sequential over chunks per (b, h, n, p) element.
-//   3. ssd_chunk_out   : per (b, chunk, head). For each 16-row time tile the
-//      transposed score tile G^T = B C^T is computed on the MFMA units, masked and
-//      scaled in registers, rounded to bf16 and used directly as the A operand of
-//      Y += M X: the accumulator layout of a 16x16 tile gives each lane 4
-//      consecutive s of one t, two tiles give 8, which is an A-operand fragment
-//      once X is fetched with the same permutation of s. The carried state enters
-//      through Y += exp(cs_t) (C Sin) on the same units.
-// The contraction over s is insensitive to which 8 values of s a lane group holds
-// as long as the A and B fragments use the same order; that freedom is what lets
-// the accumulator fragment be reused without going through LDS.
+// Three kernels per call (v_mfma_f32_16x16x32_bf16, fp32 accumulation):
+//   1. ssd_chunk_state: per (batch, chunk, 4 heads). B of the chunk is transposed
+//      into LDS once and shared by the 4 heads (one wave each); x is transposed
+//      and scaled by exp(cs_end - cs_s) dt_s while staging. S_c is written in fp32,
+//      layout [p][n].
+//   2. ssd_state_pass: sequential over chunks per (batch, head, p, 4 n); writes the
+//      entering state of every chunk already rounded to bf16 in the [p][n] layout
+//      the output kernel reads as MFMA B fragments, and h_final in fp32.
+//   3. ssd_chunk_out: per (batch, chunk, head). x of the chunk is transposed into
+//      LDS once; each wave then takes 16-row time tiles on its own. For each tile
+//      and 32-row block of s the transposed score tile G^T = B C^T is computed on
+//      the MFMA units, masked and scaled in registers and rounded to bf16 straight
+//      into the A operand of Y += M X (the 16x16
+//      accumulator layout gives a lane 4 consecutive s of one t; two tiles give the
+//      8 an A fragment holds, and X is fetched with the same order of s, which the
+//      contraction over s does not care about). The carried state enters as
+//      Y = exp(cs_t) (C Sin) on the same units; D x and the gate are applied
+//      exactly in fp32 when the tile is written.
+// Transposes into LDS move 4 x 8 register blocks with byte permutes and 8-byte
+// LDS writes.
 #include <algorithm>
 #include <cstdio>
 
@@ -53,299 +59,380 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
     return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }
 
+// (lo halves of a, b) and (hi halves of a, b) as packed bf16 pairs.
+__device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) {
+    return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) {
+    return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+// Write a 4 x 8 block (4 rows, 8 columns, each row one u32x4 of packed bf16) to
+// LDS transposed: T[c][r0 .. r0+3] for the 8 columns c0 .. c0+7.
+__device__ __forceinline__ void store_transposed(const u32x4 (&r)[4], uint16_t *T, int ldt, int c0,
+                                                 int r0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const u32x2 lo = u32x2{lo_pair(r[0][j], r[1][j]), lo_pair(r[2][j], r[3][j])};
+        const u32x2 hi = u32x2{hi_pair(r[0][j], r[1][j]), hi_pair(r[2][j], r[3][j])};
+        *(u32x2 *)&T[(c0 + 2 * j) * ldt + r0] = lo;
+        *(u32x2 *)&T[(c0 + 2 * j + 1) * ldt + r0] = hi;
+    }
+}
+
 struct SSDK {
     const uint16_t *x, *dt, *Bm, *Cm, *z;
     const float *dt_bias, *A, *Dskip, *h0;
     uint16_t *y;
     float *h_final;
-    float *states;   // [B][nc][H][N][P]
-    float *decay;    // [B][H][nc]
+    float *states;      // fp32 [B][nc][H][P][N]: state of each chunk from zero
+    uint16_t *sin;      // bf16 [B][nc][H][P][N]: state entering each chunk
+    float *decay;       // fp32 [B][H][nc]: exp(cs_end) of each chunk
     int64_t L;
     int32_t H;
     int32_t nc;
     int32_t softplus;
 };
 
-// Inclusive prefix sum over the 256 threads of a block (values of threads past
-// the chunk are zero). Uses wave shuffles and one LDS exchange of wave totals.
-__device__ __forceinline__ float block_inclusive_scan(float v, float *wave_tot) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+// dt and the inclusive in-chunk cumulative log-decay A*dt for the steps of chunk
+// c of head h; lane l owns steps l*SPL .. l*SPL+SPL-1 (SPL = Q/64). Steps past the
+// sequence get dt = 0. Returns the chunk total (the last cs) to every lane.
+template <int Q>
+__device__ __forceinline__ float head_dt_cs(const SSDK &p, int b, int h, int c, float (&dtv)[Q / 64],
+                                            float (&cs)[Q / 64]) {
+    constexpr int SPL = Q / 64;
+    const int lane = threadIdx.x & 63;
+    const float bias = p.dt_bias ? p.dt_bias[h] : 0.0f;
+    const float a = p.A[h];
+    float run = 0.0f;
+#pragma unroll
+    for (int i = 0; i < SPL; ++i) {
+        const int64_t tg = (int64_t)c * Q + lane * SPL + i;
+        float d = 0.0f;
+        if (tg < p.L) {
+            const float v = to_f32(p.dt[((int64_t)b * p.L + tg) * p.H + h]) + bias;
+            d = p.softplus ? softplus_f32(v) : v;
+        }
+        dtv[i] = d;
+        run += a * d;
+        cs[i] = run;
+    }
+    float incl = run;   // inclusive scan of lane totals
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-        const float u = __shfl_up(v, o, 64);
-        if (lane >= o) v += u;
+        const float u = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += u;
     }
-    if (lane == 63) wave_tot[w] = v;
-    __syncthreads();
-    float add = 0.0f;
-    for (int i = 0; i < w; ++i) add += wave_tot[i];
-    __syncthreads();
-    return v + add;
-}
-
-// dt and the in-chunk cumulative log-decay for step t of chunk c (thread t).
-// Returns dt (0 past the end of the sequence) and writes cs to *cs_out.
-__device__ __forceinline__ float chunk_dt_cs(const SSDK &p, int b, int h, int c, int Q,
-                                             float *wave_tot, float *cs_out) {
-    const int t = threadIdx.x;
-    const int64_t tg = (int64_t)c * Q + t;
-    float dtv = 0.0f;
-    if (t < Q && tg < p.L) {
-        const float v = to_f32(p.dt[((int64_t)b * p.L + tg) * p.H + h]) +
-                        (p.dt_bias ? p.dt_bias[h] : 0.0f);
-        dtv = p.softplus ? softplus_f32(v) : v;
-    }
-    *cs_out = block_inclusive_scan(p.A[h] * dtv, wave_tot);
-    return dtv;
+    const float excl = incl - run;
+#pragma unroll
+    for (int i = 0; i < SPL; ++i) cs[i] += excl;
+    return __shfl(incl, 63, 64);
 }
 
 // ---------------------------------------------------------------- chunk states
 template <int N, int Q>
 __global__ __launch_bounds__(kThreads) void ssd_chunk_state_kernel(const SSDK p) {
-    constexpr int SB = 64;              // time rows staged per step
-    constexpr int PAD = 8;              // bf16 padding per LDS row
-    constexpr int NT = N / 16;          // n tiles
-    constexpr int NT_W = NT / 4;        // n tiles per wave
-    __shared__ float wave_tot[4];
-    __shared__ float w_s[Q];
-    __shared__ __attribute__((aligned(16))) uint16_t BwT[N][SB + PAD];
-    __shared__ __attribute__((aligned(16))) uint16_t XT[kP][SB + PAD];
+    constexpr int SB = 64;                    // time rows staged per step
+    constexpr int LDT = SB + 8;               // padded LDS row (bf16)
+    constexpr int NPASS = N > 128 ? N / 128 : 1;
+    constexpr int NP = N / NPASS;             // states handled per pass (<= 128)
+    constexpr int NT = NP / 16;               // n tiles per pass
+    constexpr int SPL = Q / 64;
+    __shared__ float wsh[4][Q];
+    __shared__ __attribute__((aligned(16))) uint16_t BT[NP][LDT];
+    __shared__ __attribute__((aligned(16))) uint16_t XT[4][kP][LDT];
 
-    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int c = blockIdx.x, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int r16 = lane & 15, kb = lane >> 4;
-
-    float cs;
-    const float dtv = chunk_dt_cs(p, b, h, c, Q, wave_tot, &cs);
-    __shared__ float cs_end_sh;
-    if (tid == Q - 1) cs_end_sh = cs;
-    __syncthreads();
-    const float cs_end = cs_end_sh;
-    if (tid < Q) w_s[tid] = fast_exp2((cs_end - cs) * kLog2e) * dtv;
-    if (tid == 0) p.decay[((int64_t)b * p.H + h) * p.nc + c] = fast_exp2(cs_end * kLog2e);
-
-    f32x4 acc[NT_W][4];
-#pragma unroll
-    for (int i = 0; i < NT_W; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
+    const int h = blockIdx.y * 4 + wv;
+    const bool head_ok = h < p.H;
+    const int hc = head_ok ? h : p.H - 1;
     const int64_t t_base = (int64_t)c * Q;
-    for (int s0 = 0; s0 < Q; s0 += SB) {
-        __syncthreads();
-        // B rows -> BwT[n][s] scaled by w_s (bf16). N*SB/8 vectors of 8 n.
-        for (int v = tid; v < SB * N / 8; v += kThreads) {
-            const int s = v / (N / 8), ng = v % (N / 8);
-            const int64_t tg = t_base + s0 + s;
-            u32x4 raw = u32x4{0u, 0u, 0u, 0u};
-            if (tg < p.L) raw = *(const u32x4 *)(p.Bm + ((int64_t)b * p.L + tg) * N + ng * 8);
-            const float ws = w_s[s0 + s];
+
+    {   // per-head weights w_s = exp(cs_end - cs_s) dt_s and the chunk decay
+        float dtv[SPL], cs[SPL];
+        const float cs_end = head_dt_cs<Q>(p, b, hc, c, dtv, cs);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                BwT[ng * 8 + 2 * e][s] = f32_to_bf16(bf16_lo(raw[e]) * ws);
-                BwT[ng * 8 + 2 * e + 1][s] = f32_to_bf16(bf16_hi(raw[e]) * ws);
+        for (int i = 0; i < SPL; ++i)
+            wsh[wv][lane * SPL + i] = fast_exp2((cs_end - cs[i]) * kLog2e) * dtv[i];
+        if (lane == 0 && head_ok) p.decay[((int64_t)b * p.H + h) * p.nc + c] = fast_exp2(cs_end * kLog2e);
+    }
+
+    for (int pass = 0; pass < NPASS; ++pass) {
+        f32x4 acc[NT][4];
+#pragma unroll
+        for (int i = 0; i < NT; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        for (int s0 = 0; s0 < Q; s0 += SB) {
+            __syncthreads();
+            // B rows s0..s0+63, states pass*NP .. +NP  ->  BT[n][s] (4 x 8 blocks)
+            for (int blk = tid; blk < (SB / 4) * (NP / 8); blk += kThreads) {
+                const int rs = (blk / (NP / 8)) * 4, cn = (blk % (NP / 8)) * 8;
+                u32x4 r[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int64_t tg = t_base + s0 + rs + i;
+                    r[i] = tg < p.L ? *(const u32x4 *)(p.Bm + ((int64_t)b * p.L + tg) * N + pass * NP + cn)
+                                    : u32x4{0u, 0u, 0u, 0u};
+                }
+                store_transposed(r, &BT[0][0], LDT, cn, rs);
+            }
+            // x rows of this wave's head, scaled by w_s  ->  XT[wave][p][s]
+            for (int blk = lane; blk < (SB / 4) * (kP / 8); blk += 64) {
+                const int rs = (blk / (kP / 8)) * 4, cp = (blk % (kP / 8)) * 8;
+                u32x4 r[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int64_t tg = t_base + s0 + rs + i;
+                    u32x4 v = u32x4{0u, 0u, 0u, 0u};
+                    if (tg < p.L)
+                        v = *(const u32x4 *)(p.x + (((int64_t)b * p.L + tg) * p.H + hc) * kP + cp);
+                    const float w = wsh[wv][s0 + rs + i];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = pack_bf16(bf16_lo(v[e]) * w, bf16_hi(v[e]) * w);
+                    r[i] = v;
+                }
+                store_transposed(r, &XT[wv][0][0], LDT, cp, rs);
+            }
+            __syncthreads();
+#pragma unroll
+            for (int kk = 0; kk < SB / 32; ++kk) {
+                const int sk = kk * 32 + kb * 8;
+                bf16x8 bfr[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) bfr[j] = as_bf16x8(*(const u32x4 *)&XT[wv][j * 16 + r16][sk]);
+#pragma unroll
+                for (int i = 0; i < NT; ++i) {
+                    const bf16x8 afr = as_bf16x8(*(const u32x4 *)&BT[i * 16 + r16][sk]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(afr, bfr[j], acc[i][j]);
+                }
             }
         }
-        // x rows -> XT[p][s]
-        for (int v = tid; v < SB * kP / 8; v += kThreads) {
-            const int s = v / (kP / 8), pg = v % (kP / 8);
-            const int64_t tg = t_base + s0 + s;
-            u32x4 raw = u32x4{0u, 0u, 0u, 0u};
-            if (tg < p.L)
-                raw = *(const u32x4 *)(p.x + (((int64_t)b * p.L + tg) * p.H + h) * kP + pg * 8);
+        // S_c[p][n]: lane holds n = pass*NP + 16i + 4kb + e, p = 16j + r16 -> 16-byte stores
+        if (head_ok) {
+            float *out = p.states + (((int64_t)b * p.nc + c) * p.H + h) * (int64_t)kP * N;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                XT[pg * 8 + 2 * e][s] = (uint16_t)(raw[e] & 0xffffu);
-                XT[pg * 8 + 2 * e + 1][s] = (uint16_t)(raw[e] >> 16);
-            }
-        }
-        __syncthreads();
+            for (int i = 0; i < NT; ++i)
 #pragma unroll
-        for (int kk = 0; kk < SB / 32; ++kk) {
-            const int sk = kk * 32 + kb * 8;
-            bf16x8 bfr[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) bfr[j] = as_bf16x8(*(const u32x4 *)&XT[j * 16 + r16][sk]);
-#pragma unroll
-            for (int i = 0; i < NT_W; ++i) {
-                const int nrow = (wv * NT_W + i) * 16 + r16;
-                const bf16x8 afr = as_bf16x8(*(const u32x4 *)&BwT[nrow][sk]);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(afr, bfr[j], acc[i][j]);
-            }
+                for (int j = 0; j < 4; ++j)
+                    *(f32x4 *)(out + (j * 16 + r16) * N + pass * NP + i * 16 + kb * 4) = acc[i][j];
         }
     }
-    // S_c[n][p]: lane holds rows n = tile*16 + 4*kb + e, column p = j*16 + r16
-    float *out = p.states + ((((int64_t)b * p.nc + c) * p.H + h) * N) * kP;
-#pragma unroll
-    for (int i = 0; i < NT_W; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int n = (wv * NT_W + i) * 16 + 4 * kb + e;
-                out[n * kP + j * 16 + r16] = acc[i][j][e];
-            }
 }
 
 // ---------------------------------------------------------------- state passing
-// One thread per (b, h, n, p); slot c becomes the state entering chunk c.
+// One thread per (b, h, p, 4 consecutive n). Loads of a group of chunks are
+// issued together so their latencies overlap.
 __global__ __launch_bounds__(256) void ssd_state_pass_kernel(const SSDK p, int N, int64_t total) {
+    constexpr int K = 8;
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= total) return;
-    const int64_t per_bh = (int64_t)N * kP;
-    const int64_t np = i % per_bh;            // n*P + p
+    const int64_t per_bh = (int64_t)kP * N / 4;
     const int64_t bh = i / per_bh;            // b*H + h
+    const int64_t pn = (i % per_bh) * 4;      // p*N + n
     const int64_t b = bh / p.H, h = bh % p.H;
-    const int64_t n = np / kP, pp = np % kP;
-    const int64_t hidx = (bh * kP + pp) * N + n;    // (b, h, p, n)
-    float s = p.h0 ? p.h0[hidx] : 0.0f;
-    const float *dec = p.decay + bh * p.nc;
-    for (int c = 0; c < p.nc; ++c) {
-        float *slot = p.states + (((b * p.nc + c) * p.H + h) * per_bh) + np;
-        const float sc = *slot;
-        *slot = s;
-        s = fmaf(dec[c], s, sc);
+    const int64_t hidx = bh * kP * N + pn;    // (b, h, p, n) of h0 / h_final
+    f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (p.h0) {   // h0 and h_final are only 4-byte aligned
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[e] = p.h0[hidx + e];
     }
-    if (p.h_final) p.h_final[hidx] = s;
+    const float *dec = p.decay + bh * p.nc;
+    const int64_t cstride = (int64_t)p.H * kP * N;
+    const int64_t base = (b * p.nc * p.H + h) * kP * N + pn;
+    for (int c0 = 0; c0 < p.nc; c0 += K) {
+        f32x4 sc[K];
+        float dc[K];
+#pragma unroll
+        for (int u = 0; u < K; ++u) {
+            const int cc = min(c0 + u, p.nc - 1);
+            sc[u] = *(const f32x4 *)(p.states + base + cc * cstride);
+            dc[u] = dec[cc];
+        }
+#pragma unroll
+        for (int u = 0; u < K; ++u) {
+            if (c0 + u < p.nc) {
+                *(u32x2 *)(p.sin + base + (c0 + u) * cstride) = u32x2{pack_bf16(s[0], s[1]), pack_bf16(s[2], s[3])};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s[e] = fmaf(dc[u], s[e], sc[u][e]);
+            }
+        }
+    }
+    if (p.h_final) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p.h_final[hidx + e] = s[e];
+    }
 }
 
 // ---------------------------------------------------------------- chunk output
+// One workgroup per (batch, chunk, head). x of the chunk is transposed into LDS
+// once; then every wave works through its own 16-row time tiles (w, w+4, ...,
+// which balances the causal triangle) without further barriers. B and C
+// fragments are read in their natural [s][n] / [t][n] layout straight from L2
+// (the chunk's B and C are shared by all heads).
 template <int N, int Q>
 __global__ __launch_bounds__(kThreads) void ssd_chunk_out_kernel(const SSDK p) {
-    constexpr int PADX = 8, PADS = 8;
-    constexpr int TT = Q / 16;                  // time tiles in a chunk
-    __shared__ float wave_tot[4];
-    __shared__ float cs_s[Q];
-    __shared__ float dt_s[Q];
-    __shared__ __attribute__((aligned(16))) uint16_t XT[kP][Q + PADX];
-    __shared__ __attribute__((aligned(16))) uint16_t SinT[kP][N + PADS];
+    constexpr int LDX = Q + 8;
+    constexpr int SPL = Q / 64;
+    constexpr int TPW = Q / 64;               // time tiles per wave
+    constexpr int KN = N / 32;                // k steps over the state dimension
+    __shared__ float cs2[Q];                  // cs * log2(e)
+    __shared__ float dts[Q];                  // dt (0 past the end of the sequence)
+    __shared__ __attribute__((aligned(16))) uint16_t XT[kP][LDX];
+    __shared__ __attribute__((aligned(16))) float Ot[4][16][kP + 4];
 
     const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int r16 = lane & 15, kb = lane >> 4;
     const int64_t t_base = (int64_t)c * Q;
-    const int T = (int)std::min<int64_t>(Q, p.L - t_base);    // valid steps in this chunk
+    const int T = (int)std::min<int64_t>(Q, p.L - t_base);
 
-    float cs;
-    const float dtv = chunk_dt_cs(p, b, h, c, Q, wave_tot, &cs);
-    if (tid < Q) {
-        cs_s[tid] = cs;
-        dt_s[tid] = dtv;
-    }
-    // x chunk -> XT[p][s]
-    for (int v = tid; v < Q * kP / 8; v += kThreads) {
-        const int s = v / (kP / 8), pg = v % (kP / 8);
-        u32x4 raw = u32x4{0u, 0u, 0u, 0u};
-        if (s < T) raw = *(const u32x4 *)(p.x + (((int64_t)b * p.L + t_base + s) * p.H + h) * kP + pg * 8);
+    if (wv == 0) {
+        float dtv[SPL], cs[SPL];
+        head_dt_cs<Q>(p, b, h, c, dtv, cs);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            XT[pg * 8 + 2 * e][s] = (uint16_t)(raw[e] & 0xffffu);
-            XT[pg * 8 + 2 * e + 1][s] = (uint16_t)(raw[e] >> 16);
+        for (int i = 0; i < SPL; ++i) {
+            cs2[lane * SPL + i] = cs[i] * kLog2e;
+            dts[lane * SPL + i] = dtv[i];
         }
     }
-    // entering state Sin[n][p] (fp32) -> SinT[p][n] (bf16)
-    const float *sin = p.states + ((((int64_t)b * p.nc + c) * p.H + h) * N) * kP;
-    for (int v = tid; v < N * kP / 4; v += kThreads) {
-        const int n = v / (kP / 4), pg = v % (kP / 4);
-        const float4 s4 = *(const float4 *)(sin + n * kP + pg * 4);
-        SinT[pg * 4 + 0][n] = f32_to_bf16(s4.x);
-        SinT[pg * 4 + 1][n] = f32_to_bf16(s4.y);
-        SinT[pg * 4 + 2][n] = f32_to_bf16(s4.z);
-        SinT[pg * 4 + 3][n] = f32_to_bf16(s4.w);
+    for (int blk = tid; blk < (Q / 4) * (kP / 8); blk += kThreads) {
+        const int rs = (blk / (kP / 8)) * 4, cp = (blk % (kP / 8)) * 8;
+        u32x4 r[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            r[i] = rs + i < T ? *(const u32x4 *)(p.x + (((int64_t)b * p.L + t_base + rs + i) * p.H + h) * kP + cp)
+                              : u32x4{0u, 0u, 0u, 0u};
+        store_transposed(r, &XT[0][0], LDX, cp, rs);
     }
     __syncthreads();
 
-    const uint16_t *Bb = p.Bm + ((int64_t)b * p.L + t_base) * N;
-    const uint16_t *Cb = p.Cm + ((int64_t)b * p.L + t_base) * N;
+    const uint16_t *Brow = p.Bm + ((int64_t)b * p.L + t_base) * N;
+    const uint16_t *Crow = p.Cm + ((int64_t)b * p.L + t_base) * N;
+    const uint16_t *sin_h = p.sin + (((int64_t)b * p.nc + c) * p.H + h) * (int64_t)kP * N;
     const float dsk = p.Dskip ? p.Dskip[h] : 0.0f;
 
-    for (int tt = wv; tt < TT; tt += 4) {
-        const int t0 = tt * 16;
+    for (int m = 0; m < TPW; ++m) {
+        const int t0 = (wv + 4 * m) * 16;
         if (t0 >= T) break;
-        // C rows of this tile as fragments (row t0 + r16, n = 32*k + 8*kb .. +7)
-        bf16x8 cfr[N / 32];
         const int trow = std::min(t0 + r16, T - 1);
+        bf16x8 cfr[KN];
 #pragma unroll
-        for (int k = 0; k < N / 32; ++k)
-            cfr[k] = as_bf16x8(*(const u32x4 *)(Cb + (int64_t)trow * N + k * 32 + kb * 8));
-
-        // carried state: Y = C Sin, rows scaled by exp(cs_t) afterwards
+        for (int k = 0; k < KN; ++k)
+            cfr[k] = as_bf16x8(*(const u32x4 *)(Crow + (int64_t)trow * N + 32 * k + 8 * kb));
+        // carried state: Y = exp(cs_t) * (C Sin)
         f32x4 yacc[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int q = 0; q < 4; ++q) {
+            bf16x8 sfr[KN];
+#pragma unroll
+            for (int k = 0; k < KN; ++k)
+                sfr[k] = as_bf16x8(*(const u32x4 *)(sin_h + (q * 16 + r16) * N + 32 * k + 8 * kb));
             f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int k = 0; k < N / 32; ++k)
-                a = mfma16x16x32(cfr[k], as_bf16x8(*(const u32x4 *)&SinT[j * 16 + r16][k * 32 + kb * 8]), a);
-            yacc[j] = a;
+            for (int k = 0; k < KN; ++k) a = mfma16x16x32(cfr[k], sfr[k], a);
+            yacc[q] = a;
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int t = t0 + 4 * kb + e;
-            const float sc = fast_exp2(cs_s[std::min(t, Q - 1)] * kLog2e);
+            const float sc = fast_exp2(cs2[std::min(t0 + 4 * kb + e, Q - 1)]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) yacc[j][e] *= sc;
+            for (int q = 0; q < 4; ++q) yacc[q][e] *= sc;
         }
 
-        // diagonal block: s in [0, t0 + 16), 32 at a time
-        const int tcol = t0 + r16;                 // the t this lane's G^T column holds
-        const float cs_t = cs_s[tcol];
-        for (int s0 = 0; s0 < t0 + 16; s0 += 32) {
-            f32x4 g[2];
+        // diagonal part: s in 32-row blocks up to the tile's last row
+        const int tcol = t0 + r16;
+        const float ct = cs2[tcol];
+        bf16x8 bfr[2][KN];
+        auto load_b = [&](int s0) {
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const int srow = std::min(s0 + 16 * u + r16, T - 1);
-                f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int k = 0; k < N / 32; ++k) {
-                    const bf16x8 bfr = as_bf16x8(*(const u32x4 *)(Bb + (int64_t)srow * N + k * 32 + kb * 8));
-                    a = mfma16x16x32(bfr, cfr[k], a);
-                }
-                g[u] = a;
+                for (int k = 0; k < KN; ++k)
+                    bfr[u][k] = as_bf16x8(*(const u32x4 *)(Brow + (int64_t)srow * N + 32 * k + 8 * kb));
             }
-            // mask, decay and dt scale; element (u, e) is s = s0 + 16u + 4kb + e
-            uint32_t m[4];
+        };
+        load_b(0);
+        for (int s0 = 0; s0 <= t0 + 15; s0 += 32) {
+            // G^T[s][t]: lane holds s = s0+16u+4kb+e, t = t0+r16
+            f32x4 g[2];
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-                float vals[4];
+                f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int k = 0; k < KN; ++k) a = mfma16x16x32(bfr[u][k], cfr[k], a);
+                g[u] = a;
+            }
+            if (s0 + 32 <= t0 + 15) load_b(s0 + 32);   // next block's B while this one finishes
+            const bool diag = s0 + 31 > t0;
+            uint32_t mw[4];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const f32x4 cd = *(const f32x4 *)&cs2[s0 + 16 * u + 4 * kb];
+                const f32x4 dd = *(const f32x4 *)&dts[s0 + 16 * u + 4 * kb];
+                float v[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int s = s0 + 16 * u + 4 * kb + e;
-                    float val = 0.0f;
-                    if (s <= tcol && s < T)
-                        val = g[u][e] * fast_exp2((cs_t - cs_s[s]) * kLog2e) * dt_s[s];
-                    vals[e] = val;
+                    float val = g[u][e] * fast_exp2(ct - cd[e]) * dd[e];
+                    if (diag && s0 + 16 * u + 4 * kb + e > tcol) val = 0.0f;
+                    v[e] = val;
                 }
-                m[2 * u] = pack_bf16(vals[0], vals[1]);
-                m[2 * u + 1] = pack_bf16(vals[2], vals[3]);
+                mw[2 * u] = pack_bf16(v[0], v[1]);
+                mw[2 * u + 1] = pack_bf16(v[2], v[3]);
             }
-            const bf16x8 mfr = as_bf16x8(u32x4{m[0], m[1], m[2], m[3]});
+            const bf16x8 mfr = as_bf16x8(u32x4{mw[0], mw[1], mw[2], mw[3]});
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint16_t *xr = &XT[j * 16 + r16][0];
-                const u32x2 lo = *(const u32x2 *)(xr + s0 + 4 * kb);
-                const u32x2 hi = *(const u32x2 *)(xr + s0 + 16 + 4 * kb);
-                const bf16x8 xfr = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
-                yacc[j] = mfma16x16x32(mfr, xfr, yacc[j]);
+            for (int q = 0; q < 4; ++q) {
+                const uint16_t *xr = &XT[q * 16 + r16][s0];
+                const u32x2 lo = *(const u32x2 *)(xr + 4 * kb);
+                const u32x2 hi = *(const u32x2 *)(xr + 16 + 4 * kb);
+                yacc[q] = mfma16x16x32(mfr, as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), yacc[q]);
             }
         }
 
-        // y = Y + D x, gate, store. Lane holds rows t0 + 4kb + e, column j*16 + r16.
+        // y = Y + D x, gated by silu(z): the tile goes through this wave's LDS
+        // slot so that each lane writes rows of 8 bf16.
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int t = t0 + 4 * kb + e;
-            if (t >= T) continue;
-            const int64_t rowoff = (((int64_t)b * p.L + t_base + t) * p.H + h) * kP;
+        for (int q = 0; q < 4; ++q)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int pp = j * 16 + r16;
-                const float xv = to_f32(XT[pp][t]);
-                float yv = fmaf(dsk, xv, yacc[j][e]);
-                if (p.z) yv *= silu_f32(to_f32(p.z[rowoff + pp]));
-                p.y[rowoff + pp] = f32_to_bf16(yv);
+            for (int e = 0; e < 4; ++e) Ot[wv][4 * kb + e][q * 16 + r16] = yacc[q][e];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+            const int row = rr * 8 + (lane >> 3), c8 = (lane & 7) * 8;
+            const int t = t0 + row;
+            if (t < T) {
+                const int64_t off = (((int64_t)b * p.L + t_base + t) * p.H + h) * kP + c8;
+                const u32x4 xv = *(const u32x4 *)(p.x + off);
+                u32x4 zv = u32x4{0u, 0u, 0u, 0u};
+                if (p.z) zv = *(const u32x4 *)(p.z + off);
+                const f32x4 o0 = *(const f32x4 *)&Ot[wv][row][c8];
+                const f32x4 o1 = *(const f32x4 *)&Ot[wv][row][c8 + 4];
+                const float o[8] = {o0[0], o0[1], o0[2], o0[3], o1[0], o1[1], o1[2], o1[3]};
+                u32x4 outv;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float y0 = fmaf(dsk, bf16_lo(xv[e]), o[2 * e]);
+                    float y1 = fmaf(dsk, bf16_hi(xv[e]), o[2 * e + 1]);
+                    if (p.z) {
+                        y0 *= silu_f32(bf16_lo(zv[e]));
+                        y1 *= silu_f32(bf16_hi(zv[e]));
+                    }
+                    outv[e] = pack_bf16(y0, y1);
+                }
+                *(u32x4 *)(p.y + off) = outv;
             }
         }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 }
 
@@ -356,12 +443,13 @@ __global__ __launch_bounds__(256) void ssd_copy_state_kernel(const float *h0, fl
 
 template <int N, int Q>
 void launch_nq(const SSDK &k, int batch, hipStream_t s) {
-    const dim3 grid((unsigned)k.nc, (unsigned)k.H, (unsigned)batch);
-    hipLaunchKernelGGL((ssd_chunk_state_kernel<N, Q>), grid, dim3(kThreads), 0, s, k);
-    const int64_t total = (int64_t)batch * k.H * N * kP;
+    hipLaunchKernelGGL((ssd_chunk_state_kernel<N, Q>), dim3((unsigned)k.nc, (unsigned)((k.H + 3) / 4), (unsigned)batch),
+                       dim3(kThreads), 0, s, k);
+    const int64_t total = (int64_t)batch * k.H * kP * N / 4;
     hipLaunchKernelGGL(ssd_state_pass_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
                        k, N, total);
-    hipLaunchKernelGGL((ssd_chunk_out_kernel<N, Q>), grid, dim3(kThreads), 0, s, k);
+    hipLaunchKernelGGL((ssd_chunk_out_kernel<N, Q>), dim3((unsigned)k.nc, (unsigned)k.H, (unsigned)batch),
+                       dim3(kThreads), 0, s, k);
 }
 
 template <int N>
@@ -378,12 +466,13 @@ void launch_n(const SSDK &k, int batch, int Q, hipStream_t s) {
 SSDPlan ssd_plan(const ssm_ssd_args &a) {
     SSDPlan pl{};
     if (a.batch <= 0 || a.seqlen <= 0 || a.chunk <= 0) return pl;
+    auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
     pl.nchunks = (a.seqlen + a.chunk - 1) / a.chunk;
-    const size_t states = (size_t)a.batch * pl.nchunks * a.nheads * a.dstate * a.headdim * sizeof(float);
+    const size_t elems = (size_t)a.batch * pl.nchunks * a.nheads * a.dstate * a.headdim;
     pl.states_offset = 0;
-    pl.decay_offset = (states + 255) & ~(size_t)255;
-    const size_t dec = (size_t)a.batch * a.nheads * pl.nchunks * sizeof(float);
-    pl.bytes = pl.decay_offset + ((dec + 255) & ~(size_t)255);
+    pl.sin_offset = up(elems * sizeof(float));
+    pl.decay_offset = pl.sin_offset + up(elems * sizeof(uint16_t));
+    pl.bytes = pl.decay_offset + up((size_t)a.batch * a.nheads * pl.nchunks * sizeof(float));
     return pl;
 }
 
@@ -404,6 +493,7 @@ ssm_status ssd_launch(const ssm_ssd_args &a, const SSDPlan &plan, hipStream_t s,
         k.dt_bias = a.dt_bias; k.A = a.A; k.Dskip = a.Dskip; k.h0 = a.h0;
         k.y = (uint16_t *)a.y; k.h_final = a.h_final;
         k.states = (float *)((char *)a.workspace + plan.states_offset);
+        k.sin = (uint16_t *)((char *)a.workspace + plan.sin_offset);
         k.decay = (float *)((char *)a.workspace + plan.decay_offset);
         k.L = a.seqlen; k.H = (int32_t)a.nheads; k.nc = (int32_t)plan.nchunks;
         k.softplus = a.dt_softplus ? 1 : 0;

@@ -139,3 +139,23 @@ def test_full_size_sampled(key):
     report(key + " sampled", ey, eh)
     assert ey <= TOL["bf16"] and eh <= TOL["bf16"]
     assert np.isfinite(y).all() and np.isfinite(hf).all()
+
+
+def test_two_pass_entry_points_match_fwd(monkeypatch):
+    """selective_scan_chunk_states followed by selective_scan_apply is the same
+    computation as selective_scan_fwd, bit for bit."""
+    import selective_state_space_70_amd as ssm
+    monkeypatch.setenv("SSM_SCAN_CHUNKS", "9")
+    inp = workloads.scan_inputs(2, 700, 130, 16, "bf16", seed=12, with_h0=True)
+    t = to_dev(inp)
+    args = (t["x"], t["delta"], t["A"], t["Bm"], t["Cm"], t["Dskip"], t["z"], t["delta_bias"], t["h0"])
+    need = ssm.scan_workspace_bytes(2, 700, 130, 16, torch.bfloat16)
+    assert need > 0
+    ws = torch.empty(need, dtype=torch.uint8, device=t["x"].device)
+    y1, h1 = ssm.selective_scan_fwd(*args)
+    y2 = torch.empty_like(y1)
+    h2 = torch.empty_like(h1)
+    ssm.selective_scan_fwd(*args, out=y2, final_state_out=h2, workspace=ws, passes="chunk_states")
+    ssm.selective_scan_fwd(*args, out=y2, final_state_out=h2, workspace=ws, passes="apply")
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(h1, h2)
