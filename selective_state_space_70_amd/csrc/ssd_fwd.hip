@@ -20,10 +20,10 @@
 //   2. ssd_state_pass: sequential over chunks per (batch, head, p, 4 n); writes the
 //      entering state of every chunk already rounded to bf16 in the [p][n] layout
 //      the output kernel reads as MFMA B fragments, and h_final in fp32.
-//   3. ssd_chunk_out: per (batch, chunk, head). x of the chunk is transposed into
-//      LDS once; each wave then takes 16-row time tiles on its own. For each tile
-//      and 32-row block of s the transposed score tile G^T = B C^T is computed on
-//      the MFMA units, masked and scaled in registers and rounded to bf16 straight
+//   3. ssd_chunk_out: per (batch, chunk, head, 64 rows of time), one 16-row tile
+//      per wave; B and x stream through double-buffered LDS in 32-row blocks of s.
+//      For each block the transposed score tile G^T = B C^T is computed on the
+//      MFMA units, masked and scaled in registers and rounded to bf16 straight
 //      into the A operand of Y += M X (the 16x16
 //      accumulator layout gives a lane 4 consecutive s of one t; two tiles give the
 //      8 an A fragment holds, and X is fetched with the same order of s, which the
@@ -269,27 +269,42 @@ __global__ __launch_bounds__(256) void ssd_state_pass_kernel(const SSDK p, int N
 }
 
 // ---------------------------------------------------------------- chunk output
-// One workgroup per (batch, chunk, head). x of the chunk is transposed into LDS
-// once; then every wave works through its own 16-row time tiles (w, w+4, ...,
-// which balances the causal triangle) without further barriers. B and C
-// fragments are read in their natural [s][n] / [t][n] layout straight from L2
-// (the chunk's B and C are shared by all heads).
+// One workgroup per (batch, chunk, head, 64-row block of time); wave w owns the
+// 16 rows 64*tb + 16*w. The entering state of the head is staged in LDS once. The
+// s dimension is streamed in 32-row blocks: B (natural [s][n] layout, the A
+// operand of G^T = B C^T) and x (transposed, the B operand of Y += M X) go
+// through double-buffered LDS shared by the four waves, the next block being
+// loaded into registers while the current one is computed.
 template <int N, int Q>
 __global__ __launch_bounds__(kThreads) void ssd_chunk_out_kernel(const SSDK p) {
-    constexpr int LDX = Q + 8;
+    constexpr int SBK = 32;                   // s rows per block
+    constexpr int LDB = N + 8;                // padded LDS rows (bf16)
+    constexpr int LDX = SBK + 8;
     constexpr int SPL = Q / 64;
-    constexpr int TPW = Q / 64;               // time tiles per wave
     constexpr int KN = N / 32;                // k steps over the state dimension
+    constexpr int TBS = Q / 64;               // 64-row time blocks per chunk
+    constexpr int BV = SBK * N / 8 / kThreads;   // 16-byte B vectors per thread per block
+    static_assert(BV >= 1, "B block smaller than one vector per thread");
     __shared__ float cs2[Q];                  // cs * log2(e)
     __shared__ float dts[Q];                  // dt (0 past the end of the sequence)
-    __shared__ __attribute__((aligned(16))) uint16_t XT[kP][LDX];
-    __shared__ __attribute__((aligned(16))) float Ot[4][16][kP + 4];
+    __shared__ __attribute__((aligned(16))) uint16_t SinL[kP][LDB];
+    // the B double buffer and, after the s loop, the output tile share this space
+    constexpr int BB_BYTES = 2 * SBK * LDB * 2;
+    constexpr int OT_BYTES = 4 * 16 * (kP + 4) * 4;
+    __shared__ __attribute__((aligned(16))) uint8_t bo_space[BB_BYTES > OT_BYTES ? BB_BYTES : OT_BYTES];
+    __shared__ __attribute__((aligned(16))) uint16_t XTb[2][kP][LDX];
+    uint16_t (*Bb)[SBK][LDB] = reinterpret_cast<uint16_t (*)[SBK][LDB]>(bo_space);
+    float (*Ot)[16][kP + 4] = reinterpret_cast<float (*)[16][kP + 4]>(bo_space);
 
-    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int c = blockIdx.x / TBS, tb = blockIdx.x % TBS, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int r16 = lane & 15, kb = lane >> 4;
     const int64_t t_base = (int64_t)c * Q;
     const int T = (int)std::min<int64_t>(Q, p.L - t_base);
+    const int t0 = tb * 64 + wv * 16;                 // this wave's first row
+    const int blk_end = std::min(tb * 64 + 64, T);    // rows of this workgroup end here
+    if (tb * 64 >= T) return;                         // whole block past the sequence (uniform)
+    const int nsb = (blk_end + SBK - 1) / SBK;        // s blocks that reach this time block
 
     if (wv == 0) {
         float dtv[SPL], cs[SPL];
@@ -300,75 +315,89 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_out_kernel(const SSDK p) {
             dts[lane * SPL + i] = dtv[i];
         }
     }
-    for (int blk = tid; blk < (Q / 4) * (kP / 8); blk += kThreads) {
-        const int rs = (blk / (kP / 8)) * 4, cp = (blk % (kP / 8)) * 8;
-        u32x4 r[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            r[i] = rs + i < T ? *(const u32x4 *)(p.x + (((int64_t)b * p.L + t_base + rs + i) * p.H + h) * kP + cp)
-                              : u32x4{0u, 0u, 0u, 0u};
-        store_transposed(r, &XT[0][0], LDX, cp, rs);
+    const uint16_t *sin_h = p.sin + (((int64_t)b * p.nc + c) * p.H + h) * (int64_t)kP * N;
+    for (int v = tid; v < kP * N / 8; v += kThreads) {
+        const int pp = v / (N / 8), n8 = (v % (N / 8)) * 8;
+        *(u32x4 *)&SinL[pp][n8] = *(const u32x4 *)(sin_h + pp * N + n8);
     }
-    __syncthreads();
-
     const uint16_t *Brow = p.Bm + ((int64_t)b * p.L + t_base) * N;
     const uint16_t *Crow = p.Cm + ((int64_t)b * p.L + t_base) * N;
-    const uint16_t *sin_h = p.sin + (((int64_t)b * p.nc + c) * p.H + h) * (int64_t)kP * N;
-    const float dsk = p.Dskip ? p.Dskip[h] : 0.0f;
+    const uint16_t *Xrow = p.x + ((int64_t)b * p.L + t_base) * p.H * kP + (int64_t)h * kP;
+    const int64_t xstride = (int64_t)p.H * kP;
 
-    for (int m = 0; m < TPW; ++m) {
-        const int t0 = (wv + 4 * m) * 16;
-        if (t0 >= T) break;
-        const int trow = std::min(t0 + r16, T - 1);
-        bf16x8 cfr[KN];
+    // one s block into registers: BV 16-byte vectors of B; x as 4 x 8 blocks
+    // (threads < 64 own one block each: 8 row-quads x 8 column-octets)
+    u32x4 breg[BV], xreg[4];
+    auto fetch = [&](int sb) {
+        const int s0 = sb * SBK;
+#pragma unroll
+        for (int i = 0; i < BV; ++i) {
+            const int v = tid + i * kThreads;
+            const int s = v / (N / 8), n8 = (v % (N / 8)) * 8;
+            breg[i] = s0 + s < T ? *(const u32x4 *)(Brow + (int64_t)(s0 + s) * N + n8) : u32x4{0u, 0u, 0u, 0u};
+        }
+        if (tid < 64) {
+            const int rs = (tid / 8) * 4, cp = (tid % 8) * 8;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                xreg[i] = s0 + rs + i < T ? *(const u32x4 *)(Xrow + (int64_t)(s0 + rs + i) * xstride + cp)
+                                          : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    auto stash = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < BV; ++i) {
+            const int v = tid + i * kThreads;
+            const int s = v / (N / 8), n8 = (v % (N / 8)) * 8;
+            *(u32x4 *)&Bb[buf][s][n8] = breg[i];
+        }
+        if (tid < 64) store_transposed(xreg, &XTb[buf][0][0], LDX, (tid % 8) * 8, (tid / 8) * 4);
+    };
+
+    fetch(0);
+    const bool live = t0 < T;                          // this wave has rows to produce
+    const int trow = std::min(t0 + r16, T - 1);
+    bf16x8 cfr[KN];
+#pragma unroll
+    for (int k = 0; k < KN; ++k)
+        cfr[k] = as_bf16x8(*(const u32x4 *)(Crow + (int64_t)trow * N + 32 * k + 8 * kb));
+    stash(0);
+    __syncthreads();
+
+    // carried state: Y = exp(cs_t) * (C Sin)
+    f32x4 yacc[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int k = 0; k < KN; ++k)
-            cfr[k] = as_bf16x8(*(const u32x4 *)(Crow + (int64_t)trow * N + 32 * k + 8 * kb));
-        // carried state: Y = exp(cs_t) * (C Sin)
-        f32x4 yacc[4];
+            a = mfma16x16x32(cfr[k], as_bf16x8(*(const u32x4 *)&SinL[q * 16 + r16][32 * k + 8 * kb]), a);
+        yacc[q] = a;
+    }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            bf16x8 sfr[KN];
+    for (int e = 0; e < 4; ++e) {
+        const float sc = fast_exp2(cs2[std::min(t0 + 4 * kb + e, Q - 1)]);
 #pragma unroll
-            for (int k = 0; k < KN; ++k)
-                sfr[k] = as_bf16x8(*(const u32x4 *)(sin_h + (q * 16 + r16) * N + 32 * k + 8 * kb));
-            f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int k = 0; k < KN; ++k) a = mfma16x16x32(cfr[k], sfr[k], a);
-            yacc[q] = a;
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float sc = fast_exp2(cs2[std::min(t0 + 4 * kb + e, Q - 1)]);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) yacc[q][e] *= sc;
-        }
+        for (int q = 0; q < 4; ++q) yacc[q][e] *= sc;
+    }
 
-        // diagonal part: s in 32-row blocks up to the tile's last row
-        const int tcol = t0 + r16;
-        const float ct = cs2[tcol];
-        bf16x8 bfr[2][KN];
-        auto load_b = [&](int s0) {
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int srow = std::min(s0 + 16 * u + r16, T - 1);
-#pragma unroll
-                for (int k = 0; k < KN; ++k)
-                    bfr[u][k] = as_bf16x8(*(const u32x4 *)(Brow + (int64_t)srow * N + 32 * k + 8 * kb));
-            }
-        };
-        load_b(0);
-        for (int s0 = 0; s0 <= t0 + 15; s0 += 32) {
+    const int tcol = std::min(t0 + r16, Q - 1);
+    const float ct = cs2[tcol];
+    for (int sb = 0; sb < nsb; ++sb) {
+        const int buf = sb & 1;
+        if (sb + 1 < nsb) fetch(sb + 1);
+        const int s0 = sb * SBK;
+        if (live && s0 <= t0 + 15) {
             // G^T[s][t]: lane holds s = s0+16u+4kb+e, t = t0+r16
             f32x4 g[2];
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int k = 0; k < KN; ++k) a = mfma16x16x32(bfr[u][k], cfr[k], a);
+                for (int k = 0; k < KN; ++k)
+                    a = mfma16x16x32(as_bf16x8(*(const u32x4 *)&Bb[buf][16 * u + r16][32 * k + 8 * kb]), cfr[k], a);
                 g[u] = a;
             }
-            if (s0 + 32 <= t0 + 15) load_b(s0 + 32);   // next block's B while this one finishes
             const bool diag = s0 + 31 > t0;
             uint32_t mw[4];
 #pragma unroll
@@ -388,51 +417,50 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_out_kernel(const SSDK p) {
             const bf16x8 mfr = as_bf16x8(u32x4{mw[0], mw[1], mw[2], mw[3]});
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const uint16_t *xr = &XT[q * 16 + r16][s0];
+                const uint16_t *xr = &XTb[buf][q * 16 + r16][0];
                 const u32x2 lo = *(const u32x2 *)(xr + 4 * kb);
                 const u32x2 hi = *(const u32x2 *)(xr + 16 + 4 * kb);
                 yacc[q] = mfma16x16x32(mfr, as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), yacc[q]);
             }
         }
+        if (sb + 1 < nsb) stash(buf ^ 1);
+        __syncthreads();
+    }
 
-        // y = Y + D x, gated by silu(z): the tile goes through this wave's LDS
-        // slot so that each lane writes rows of 8 bf16.
+    // y = Y + D x, gated by silu(z): the tile goes through LDS (reusing the B
+    // buffers) so that each lane writes rows of 8 bf16.
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < 4; ++q)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) Ot[wv][4 * kb + e][q * 16 + r16] = yacc[q][e];
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        for (int e = 0; e < 4; ++e) Ot[wv][4 * kb + e][q * 16 + r16] = yacc[q][e];
+    __syncthreads();
+    if (!live) return;
+    const float dsk = p.Dskip ? p.Dskip[h] : 0.0f;
 #pragma unroll
-        for (int rr = 0; rr < 2; ++rr) {
-            const int row = rr * 8 + (lane >> 3), c8 = (lane & 7) * 8;
-            const int t = t0 + row;
-            if (t < T) {
-                const int64_t off = (((int64_t)b * p.L + t_base + t) * p.H + h) * kP + c8;
-                const u32x4 xv = *(const u32x4 *)(p.x + off);
-                u32x4 zv = u32x4{0u, 0u, 0u, 0u};
-                if (p.z) zv = *(const u32x4 *)(p.z + off);
-                const f32x4 o0 = *(const f32x4 *)&Ot[wv][row][c8];
-                const f32x4 o1 = *(const f32x4 *)&Ot[wv][row][c8 + 4];
-                const float o[8] = {o0[0], o0[1], o0[2], o0[3], o1[0], o1[1], o1[2], o1[3]};
-                u32x4 outv;
+    for (int rr = 0; rr < 2; ++rr) {
+        const int row = rr * 8 + (lane >> 3), c8 = (lane & 7) * 8;
+        const int t = t0 + row;
+        if (t < T) {
+            const int64_t off = (((int64_t)b * p.L + t_base + t) * p.H + h) * kP + c8;
+            const u32x4 xv = *(const u32x4 *)(p.x + off);
+            u32x4 zv = u32x4{0u, 0u, 0u, 0u};
+            if (p.z) zv = *(const u32x4 *)(p.z + off);
+            const f32x4 o0 = *(const f32x4 *)&Ot[wv][row][c8];
+            const f32x4 o1 = *(const f32x4 *)&Ot[wv][row][c8 + 4];
+            const float o[8] = {o0[0], o0[1], o0[2], o0[3], o1[0], o1[1], o1[2], o1[3]};
+            u32x4 outv;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    float y0 = fmaf(dsk, bf16_lo(xv[e]), o[2 * e]);
-                    float y1 = fmaf(dsk, bf16_hi(xv[e]), o[2 * e + 1]);
-                    if (p.z) {
-                        y0 *= silu_f32(bf16_lo(zv[e]));
-                        y1 *= silu_f32(bf16_hi(zv[e]));
-                    }
-                    outv[e] = pack_bf16(y0, y1);
+            for (int e = 0; e < 4; ++e) {
+                float y0 = fmaf(dsk, bf16_lo(xv[e]), o[2 * e]);
+                float y1 = fmaf(dsk, bf16_hi(xv[e]), o[2 * e + 1]);
+                if (p.z) {
+                    y0 *= silu_f32(bf16_lo(zv[e]));
+                    y1 *= silu_f32(bf16_hi(zv[e]));
                 }
-                *(u32x4 *)(p.y + off) = outv;
+                outv[e] = pack_bf16(y0, y1);
             }
+            *(u32x4 *)(p.y + off) = outv;
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 }
 
@@ -448,7 +476,7 @@ void launch_nq(const SSDK &k, int batch, hipStream_t s) {
     const int64_t total = (int64_t)batch * k.H * kP * N / 4;
     hipLaunchKernelGGL(ssd_state_pass_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
                        k, N, total);
-    hipLaunchKernelGGL((ssd_chunk_out_kernel<N, Q>), dim3((unsigned)k.nc, (unsigned)k.H, (unsigned)batch),
+    hipLaunchKernelGGL((ssd_chunk_out_kernel<N, Q>), dim3((unsigned)(k.nc * (Q / 64)), (unsigned)k.H, (unsigned)batch),
                        dim3(kThreads), 0, s, k);
 }
 
