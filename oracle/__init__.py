@@ -59,7 +59,7 @@ def lib():
             _f32p, _f64p, ctypes.c_int, _i64p, _i64, _f64p, _f64p]
         L.oracle_causal_conv1d_f64.restype = ctypes.c_int
         L.oracle_causal_conv1d_f64.argtypes = [_i64, _i64, _i64, _i64, _f32p, _f32p, _f32p,
-                                               ctypes.c_int, _f64p]
+                                               _f32p, ctypes.c_int, _f64p, _f64p]
         L.oracle_num_threads.restype = ctypes.c_int
         L.oracle_set_num_threads.argtypes = [ctypes.c_int]
         _lib = L
@@ -194,20 +194,47 @@ def ssd(x, dt, A, Bm, Cm, Dskip=None, z=None, dt_bias=None, h0=None,
     return y, hf
 
 
-def causal_conv1d(x, w, bias=None, apply_silu: bool = True):
-    """Reference causal depthwise conv1d (+ SiLU) in fp64. x (batch, L, D), w (D, K)."""
+def causal_conv1d(x, w, bias=None, apply_silu: bool = True, x0=None, return_state: bool = False):
+    """Reference causal depthwise conv1d (+ SiLU) in fp64. x (batch, L, D), w (D, K),
+    bias (D,), x0 (batch, K-1, D) the inputs before t = 0 (zeros when None).
+    Returns out (batch, L, D), and with ``return_state`` also the last K-1 inputs
+    of [x0; x] as (batch, K-1, D)."""
     batch, L, D = np.shape(x)
     K = np.shape(w)[1]
     xs, xp = _f32(x, (batch, L, D))
     ws, wp = _f32(w, (D, K))
     bs, bp = _f32(bias, (D,))
+    x0s, x0p = _f32(x0, (batch, K - 1, D))
     out = np.empty((batch, L, D), dtype=np.float64)
-    rc = lib().oracle_causal_conv1d_f64(batch, L, D, K, xp, wp, bp, int(bool(apply_silu)),
-                                        out.ctypes.data_as(_f64p))
+    fs = np.empty((batch, K - 1, D), dtype=np.float64)
+    rc = lib().oracle_causal_conv1d_f64(batch, L, D, K, xp, wp, bp, x0p, int(bool(apply_silu)),
+                                        out.ctypes.data_as(_f64p), fs.ctypes.data_as(_f64p))
     if rc != 0:
         raise ValueError("oracle_causal_conv1d_f64 rejected its arguments")
-    del xs, ws, bs
-    return out
+    del xs, ws, bs, x0s
+    return (out, fs) if return_state else out
+
+
+def selective_state_update(state, x, delta, A, Bm, Cm, Dskip=None, z=None, delta_bias=None,
+                           delta_softplus: bool = True):
+    """One decode step of the selective scan: by definition the scan over a
+    sequence of length 1 that starts from ``state`` [Juejin page, streaming
+    step(x, state) -> (y, state)]. Shapes: state (batch, D, N); x, delta, z
+    (batch, D); Bm, Cm (batch, N). Returns (y (batch, D), new_state (batch, D, N))."""
+    col = lambda a: None if a is None else np.asarray(a)[:, None]
+    y, hf = selective_scan(col(x), col(delta), A, col(Bm), col(Cm), Dskip, col(z), delta_bias,
+                           state, delta_softplus)
+    return y[:, 0], hf
+
+
+def ssd_state_update(state, x, dt, A, Bm, Cm, Dskip=None, z=None, dt_bias=None,
+                     dt_softplus: bool = True):
+    """One decode step of the scalar-A (SSD) form: the recurrence over one step
+    from ``state``. Shapes: state (batch, H, P, N); x, z (batch, H, P); dt (batch, H);
+    Bm, Cm (batch, N). Returns (y (batch, H, P), new_state (batch, H, P, N))."""
+    col = lambda a: None if a is None else np.asarray(a)[:, None]
+    y, hf = ssd(col(x), col(dt), A, col(Bm), col(Cm), Dskip, col(z), dt_bias, state, dt_softplus)
+    return y[:, 0], hf
 
 
 def rel_l2(u, v) -> float:

@@ -210,15 +210,27 @@ int oracle_ssd_f64(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
  * Causal depthwise convolution along time followed by SiLU, fp64.
  * [Reading page section 5 and Hybrid page section 3: the x branch passes a
  * short depthwise Conv1d and SiLU before the scan; Juejin page "基本使用":
- * kernel width d_conv = 4.]
+ * kernel width d_conv = 4; Juejin page, streaming step(x, state): a call may
+ * continue from the history an earlier call left.]
  *   x: (batch, L, D); w: (D, K); bias: (D) NULL -> 0; out (batch, L, D)
- *   out[b,t,d] = silu( bias[d] + sum_{k=0}^{K-1} w[d,k] * x[b, t-(K-1)+k, d] ),
- *   terms with a negative time index are zero (causal zero padding).
+ *   x0: (batch, K-1, D) the K-1 inputs before t = 0, oldest first; NULL -> zeros
+ *   With xx = [x0 ; x] along time (xx_s = x0[K-1+s] for -(K-1) <= s < 0):
+ *   out[b,t,d] = silu( bias[d] + sum_{k=0}^{K-1} w[d,k] * xx[b, t-(K-1)+k, d] ).
  *   apply_silu = 0 leaves the convolution output ungated.
+ *   final_state (batch, K-1, D), NULL -> not written: the last K-1 entries of xx,
+ *   which is the x0 of a call that continues this sequence.
  */
+static double conv_input(const float *x, const float *x0, int64_t b, int64_t s, int64_t L,
+                         int64_t D, int64_t K, int64_t d)
+{
+    if (s >= 0) return (double)x[(b * L + s) * D + d];
+    if (x0 && s >= -(K - 1)) return (double)x0[(b * (K - 1) + (K - 1) + s) * D + d];
+    return 0.0;
+}
+
 int oracle_causal_conv1d_f64(int64_t batch, int64_t L, int64_t D, int64_t K,
                              const float *x, const float *w, const float *bias,
-                             int apply_silu, double *out)
+                             const float *x0, int apply_silu, double *out, double *final_state)
 {
     if (batch < 0 || L < 0 || D <= 0 || K <= 0) return -1;
 #pragma omp parallel for schedule(static)
@@ -228,9 +240,13 @@ int oracle_causal_conv1d_f64(int64_t batch, int64_t L, int64_t D, int64_t K,
             double acc = bias ? (double)bias[d] : 0.0;
             for (int64_t k = 0; k < K; ++k) {
                 const int64_t s = t - (K - 1) + k;
-                if (s >= 0) acc += (double)w[d * K + k] * (double)x[(b * L + s) * D + d];
+                acc += (double)w[d * K + k] * conv_input(x, x0, b, s, L, D, K, d);
             }
             out[(b * L + t) * D + d] = apply_silu ? silu_gate_f64(acc) : acc;
+        }
+        if (final_state) {
+            for (int64_t j = 0; j < K - 1; ++j)
+                final_state[(b * (K - 1) + j) * D + d] = conv_input(x, x0, b, L - (K - 1) + j, L, D, K, d);
         }
     }
     return 0;

@@ -410,10 +410,78 @@ def pin_conv1d_numpy(seed=15):
     assert _rel(raw, want) < TOL and _rel(out, _silu_tanh(want)) < TOL, "conv1d differs"
 
 
+def pin_conv1d_history(seed=16):
+    """With a history x0 the output is numpy's convolution of [x0; x] with the
+    first K-1 outputs dropped; the returned state is the last K-1 inputs."""
+    rng = np.random.default_rng(seed)
+    for batch, L, D, K in ((2, 9, 3, 4), (1, 2, 2, 4), (2, 5, 2, 3)):
+        x = _f32(rng.standard_normal((batch, L, D)))
+        x0 = _f32(rng.standard_normal((batch, K - 1, D)))
+        w = _f32(rng.standard_normal((D, K)))
+        bias = _f32(rng.standard_normal(D))
+        out, fs = oracle.causal_conv1d(x, w, bias, x0=x0, return_state=True)
+        want = np.empty_like(out)
+        for b in range(batch):
+            for d in range(D):
+                xx = np.concatenate([x0[b, :, d], x[b, :, d]]).astype(np.float64)
+                c = np.convolve(xx, w[d, ::-1].astype(np.float64))[K - 1:K - 1 + L]
+                want[b, :, d] = _silu_tanh(c + float(bias[d]))
+        xx_all = np.concatenate([x0, x], axis=1).astype(np.float64)
+        assert _rel(out, want) < TOL, "conv1d with history differs"
+        assert np.array_equal(fs, xx_all[:, -(K - 1):]), "conv1d final state is not the last inputs"
+
+
+def pin_conv1d_streaming(seed=17):
+    """Two calls chained through the state equal one call over the whole sequence."""
+    rng = np.random.default_rng(seed)
+    batch, L, D, K = 2, 23, 3, 4
+    x = _f32(rng.standard_normal((batch, L, D)))
+    w = _f32(rng.standard_normal((D, K)))
+    bias = _f32(rng.standard_normal(D))
+    full, fs_full = oracle.causal_conv1d(x, w, bias, return_state=True)
+    for cut in (1, 2, 11):
+        a, st = oracle.causal_conv1d(x[:, :cut], w, bias, return_state=True)
+        b, st2 = oracle.causal_conv1d(x[:, cut:], w, bias, x0=_f32(st), return_state=True)
+        assert _rel(np.concatenate([a, b], axis=1), full) < 1e-15, "conv1d streaming differs"
+        assert np.array_equal(st2, fs_full)
+
+
+def pin_decode_steps_equal_scan(seed=18):
+    """Decode steps chained through the state reproduce the scan over the same
+    tokens: outputs per step and the final state (the recurrence is a semigroup)."""
+    rng = np.random.default_rng(seed)
+    batch, L, D, N = 2, 6, 3, 4
+    x, z, Dsk, A, _, Bm, Cm = _rand_case(rng, batch, L, D, N)
+    delta = _f32(rng.normal(0.0, 0.5, size=(batch, L, D)))
+    bias = _f32(rng.uniform(-3.0, -1.0, size=D))
+    h0 = rng.standard_normal((batch, D, N))
+    y, hf = oracle.selective_scan(x, delta, A, Bm, Cm, Dsk, z, bias, h0)
+    st = h0
+    for t in range(L):
+        yt, st = oracle.selective_state_update(st, x[:, t], delta[:, t], A, Bm[:, t], Cm[:, t],
+                                               Dsk, z[:, t], bias)
+        assert _rel(yt, y[:, t]) < TOL, "decode step %d differs from the scan" % t
+    assert _rel(st, hf) < TOL, "decode state differs from the scan's final state"
+
+
+def pin_ssd_decode_steps_equal_ssd(seed=19):
+    rng = np.random.default_rng(seed)
+    batch, L, H, P, N = 2, 5, 3, 2, 4
+    x, dt, bias, A, Bm, Cm, Dsk, z, h0 = _ssd_case(rng, batch, L, H, P, N)
+    y, hf = oracle.ssd(x, dt, A, Bm, Cm, Dskip=Dsk, z=z, dt_bias=bias, h0=h0)
+    st = h0
+    for t in range(L):
+        yt, st = oracle.ssd_state_update(st, x[:, t], dt[:, t], A, Bm[:, t], Cm[:, t], Dskip=Dsk,
+                                         z=z[:, t], dt_bias=bias)
+        assert _rel(yt, y[:, t]) < TOL, "SSD decode step %d differs" % t
+    assert _rel(st, hf) < TOL
+
+
 SCAN_PINS = [pin_lti_convolution, pin_lti_lfilter, pin_semiseparable, pin_small_step_keeps_state,
              pin_large_step_forgets, pin_zero_input_pure_decay, pin_split_invariance,
              pin_linearity, pin_geometric_series, pin_softplus_identities, pin_gate_identity,
-             pin_skip_only, pin_channel_subset]
-SSD_PINS = [pin_ssd_semiseparable, pin_ssd_is_broadcast_scan, pin_ssd_channel_subset]
-CONV_PINS = [pin_conv1d_numpy]
+             pin_skip_only, pin_channel_subset, pin_decode_steps_equal_scan]
+SSD_PINS = [pin_ssd_semiseparable, pin_ssd_is_broadcast_scan, pin_ssd_channel_subset,
+            pin_ssd_decode_steps_equal_ssd]
+CONV_PINS = [pin_conv1d_numpy, pin_conv1d_history, pin_conv1d_streaming]
 ALL_PINS = SCAN_PINS + SSD_PINS + CONV_PINS

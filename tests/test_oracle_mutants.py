@@ -43,6 +43,10 @@ MUTANTS = [
     ("ssd_x_layout", "const int64_t e = ((b * L + t) * H + hh) * P + p;",
      "const int64_t e = ((b * L + t) * P + p) * H + hh;", "ssd"),
     ("conv_not_causal", "const int64_t s = t - (K - 1) + k;", "const int64_t s = t - k;", "conv"),
+    ("conv_history_reversed", "x0[(b * (K - 1) + (K - 1) + s) * D + d]", "x0[(b * (K - 1) - 1 - s) * D + d]",
+     "conv"),
+    ("conv_state_off_by_one", "conv_input(x, x0, b, L - (K - 1) + j, L, D, K, d)",
+     "conv_input(x, x0, b, L - K + j, L, D, K, d)", "conv"),
 ]
 
 PINS = {"scan": oracle_pins.SCAN_PINS, "ssd": oracle_pins.SSD_PINS, "conv": oracle_pins.CONV_PINS}
