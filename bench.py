@@ -200,6 +200,80 @@ def time_ssd(steps, warmup, torch, ssm):
     return cfg, [a.elapsed_time(b) for a, b in ev]
 
 
+def _time_rotating(call, nsets, steps, warmup, torch):
+    """Mean HIP-event time (ms) of call(i) over `steps` calls, rotating i over the sets."""
+    for i in range(warmup):
+        call(i % nsets)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record(stream)
+        call(i % nsets)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in ev) / steps
+
+
+def time_next_rows(steps, warmup, torch, ssm):
+    """Decode steps and the short convolution at serving / layer shapes: effective
+    GB/s over their algorithmic bytes (each input and output once; the state read
+    and written once)."""
+    dev = torch.device("cuda:0")
+    bf = torch.bfloat16
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    rn = lambda *s, dt=bf: torch.randn(*s, generator=g, device=dev, dtype=torch.float32).to(dt)
+    out = {}
+    # per-channel decode step: batch 256, D 5120, N 16 (state 84 MB)
+    Bt, D, N = 256, 5120, 16
+    A = -torch.arange(1, N + 1, device=dev, dtype=torch.float32).repeat(D, 1).contiguous()
+    par = [rn(D, dt=torch.float32) for _ in range(2)]
+    sets = []
+    for _ in range(4):
+        sets.append(dict(st=rn(Bt, D, N, dt=torch.float32), x=rn(Bt, D), dl=rn(Bt, D) * 0.5, z=rn(Bt, D),
+                         B=rn(Bt, N), C=rn(Bt, N), y=torch.empty(Bt, D, dtype=bf, device=dev)))
+    ms = _time_rotating(lambda i: ssm.selective_state_update(
+        sets[i]["st"], sets[i]["x"], sets[i]["dl"], A, sets[i]["B"], sets[i]["C"], par[0], sets[i]["z"],
+        par[1] - 3.0, out=sets[i]["y"]), 4, steps, warmup, torch)
+    alg = 8 * Bt * D * N + 2 * 4 * Bt * D + 2 * 2 * Bt * N + 4 * D * N + 8 * D
+    out["decode_B256_D5120_N16"] = {"ms": round(ms, 5), "GB/s": round(alg / ms / 1e6, 1),
+                                    "hbm_frac": round(alg / ms / 1e6 / HBM_PEAK_GBS, 4)}
+    del sets
+    # scalar-A decode step: batch 32, 64 heads x P 64, N 128 (state 134 MB)
+    Bt, H, P, N = 32, 64, 64, 128
+    Ah = -torch.rand(H, generator=g, device=dev) * 15.0 - 1.0
+    hp = [rn(H, dt=torch.float32) for _ in range(2)]
+    sets = []
+    for _ in range(3):
+        sets.append(dict(st=rn(Bt, H, P, N, dt=torch.float32), x=rn(Bt, H, P), dt=rn(Bt, H) * 0.5,
+                         B=rn(Bt, N), C=rn(Bt, N), y=torch.empty(Bt, H, P, dtype=bf, device=dev)))
+    ms = _time_rotating(lambda i: ssm.ssd_state_update(
+        sets[i]["st"], sets[i]["x"], sets[i]["dt"], Ah, sets[i]["B"], sets[i]["C"], hp[0], None,
+        hp[1] - 3.0, out=sets[i]["y"]), 3, steps, warmup, torch)
+    alg = 8 * Bt * H * P * N + 2 * 2 * Bt * H * P + 2 * Bt * H + 2 * 2 * Bt * N + 12 * H
+    out["ssd_decode_B32_H64_P64_N128"] = {"ms": round(ms, 5), "GB/s": round(alg / ms / 1e6, 1),
+                                          "hbm_frac": round(alg / ms / 1e6 / HBM_PEAK_GBS, 4)}
+    del sets
+    # conv1d (width 4) + SiLU at the scan workload shapes
+    for key in ("S2", "S3"):
+        c = workloads.CONFIGS[key]
+        w = rn(c.dim, 4, dt=torch.float32)
+        bias = rn(c.dim, dt=torch.float32)
+        nsets = max(2, math.ceil(768e6 / (4 * c.batch * c.seqlen * c.dim)))
+        xs = [rn(c.batch, c.seqlen, c.dim) for _ in range(nsets)]
+        ys = [torch.empty_like(xs[0]) for _ in range(nsets)]
+        ms = _time_rotating(lambda i: ssm.causal_conv1d_fwd(xs[i], w, bias, out=ys[i]), nsets, steps,
+                            warmup, torch)
+        alg = 2 * 2 * c.batch * c.seqlen * c.dim + 5 * 4 * c.dim
+        out["conv1d_%s_B%d_L%d_D%d" % (key, c.batch, c.seqlen, c.dim)] = {
+            "ms": round(ms, 5), "GB/s": round(alg / ms / 1e6, 1),
+            "hbm_frac": round(alg / ms / 1e6 / HBM_PEAK_GBS, 4)}
+        del xs, ys
+    return out
+
+
 def cpu_baseline(key, budget_s=10.0):
     """The fp64 oracle on the host cores over the same workload (all channels,
     whole sequence), repeated until ~budget_s of wall time; effective GB/s on the
@@ -235,6 +309,8 @@ def main():
     ap.add_argument("--ssd-only", action="store_true",
                     help="time only the Mamba-2 SSD workload and print its own JSON line "
                          "(for profiling the SSD kernels; not the headline line)")
+    ap.add_argument("--next-only", action="store_true",
+                    help="time only the decode steps and the short convolution (own JSON line)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run three plain 256 MiB device-to-device copies (the reference "
                          "kernel of known size that calibrates the FETCH_SIZE / WRITE_SIZE counters)")
@@ -257,6 +333,10 @@ def main():
 
     import torch
     import selective_state_space_70_amd as ssm
+
+    if args.next_only:
+        print(json.dumps(time_next_rows(args.steps, args.warmup, torch, ssm)), flush=True)
+        return
 
     if args.ssd_only:
         c5, pc5 = time_ssd(args.steps, args.warmup, torch, ssm)
@@ -312,6 +392,7 @@ def main():
         extra["S5"] = {"ms": round(m5, 4), "GB/s": round(ssd_alg_bytes(c5) / m5 / 1e6, 1),
                        "TFLOP/s": round(ssd_alg_flops(c5) / m5 / 1e9, 1),
                        "mfma_frac": round(ssd_alg_flops(c5) / m5 / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4)}
+        extra.update(time_next_rows(max(10, args.steps), 3, torch, ssm))
         line["extra"] = extra
         print(json.dumps(extra), file=sys.stderr)
     if not args.no_cpu_baseline:

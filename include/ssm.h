@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 1
+#define SSM_ABI_VERSION 2
 
 typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
 
@@ -162,6 +162,94 @@ ssm_status ssd_chunked_validate(const ssm_ssd_args *args);
 /* Workspace bytes ssd_chunked_fwd needs for these sizes (0 if invalid). Reads only
  * the sizes and dtype; the pointers may be NULL. Host-only. */
 size_t ssd_chunked_workspace_bytes(const ssm_ssd_args *args);
+
+/*
+ * One decode step of the selective scan (a sequence of length 1), the state read
+ * and written in place:
+ *   dt = softplus(delta[b,d] + delta_bias[d])     (delta + bias if delta_softplus == 0)
+ *   state[b,d,n] <- exp(dt A[d,n]) state[b,d,n] + dt Bm[b,n] x[b,d]
+ *   y[b,d] = (sum_n Cm[b,n] state[b,d,n] + Dskip[d] x[b,d]) * silu(z[b,d])
+ * This is selective_scan_fwd over one token with h0 = state and h_final written
+ * back to state [Juejin page, long-document streaming: step(x, state) returns the
+ * output and the next state; SSM page, how it works: inference keeps a fixed-size
+ * state per channel and advances it token by token].
+ * Layouts: x, delta, z, y: (batch, D) dtype; Bm, Cm: (batch, N) dtype; A: (D, N)
+ * fp32; delta_bias, Dskip: (D) fp32; state: (batch, D, N) fp32, 16-byte aligned
+ * (the layout of h0 / h_final above). Nullable: z, delta_bias, Dskip.
+ * Supported: N in {16, 32, 64, 128, 256}; dtype F32 or BF16. batch == 0 is a no-op.
+ */
+typedef struct ssm_scan_step_args {
+    int64_t batch, dim, dstate;           /* B, D, N */
+    ssm_dtype dtype;                      /* storage of x, delta, z, Bm, Cm, y */
+    int32_t delta_softplus;
+    const void *x, *delta, *z;
+    const void *Bm, *Cm;
+    const float *A;
+    const float *delta_bias;
+    const float *Dskip;
+    float *state;                         /* in/out */
+    void *y;
+} ssm_scan_step_args;
+
+ssm_status selective_state_update(const ssm_scan_step_args *args, hipStream_t stream);
+
+/*
+ * One decode step of the scalar-A (SSD) form, state in place: per head h,
+ *   dt = softplus(dt[b,h] + dt_bias[h]);  a = exp(dt A[h])
+ *   state[b,h,p,n] <- a state[b,h,p,n] + dt Bm[b,n] x[b,h,p]
+ *   y[b,h,p] = (sum_n Cm[b,n] state[b,h,p,n] + Dskip[h] x[b,h,p]) * silu(z[b,h,p])
+ * [Mamba-2 page, Background: the discrete recurrence, here with one scalar decay
+ * per head; Juejin page, step(x, state)]. ssd_chunked_fwd over one token with
+ * h0 = state and h_final written back to state.
+ * Layouts: x, z, y: (batch, H, P) dtype; dt: (batch, H) dtype; Bm, Cm: (batch, N)
+ * dtype; dt_bias, A, Dskip: (H) fp32; state: (batch, H, P, N) fp32, 16-byte aligned.
+ * Nullable: z, dt_bias, Dskip. Supported: any P >= 1; N in {16, 32, 64, 128, 256};
+ * dtype F32 or BF16.
+ */
+typedef struct ssm_ssd_step_args {
+    int64_t batch, nheads, headdim, dstate;   /* B, H, P, N */
+    ssm_dtype dtype;
+    int32_t dt_softplus;
+    const void *x;
+    const void *dt;
+    const float *dt_bias;
+    const float *A;
+    const void *Bm, *Cm;
+    const float *Dskip;
+    const void *z;
+    float *state;                             /* in/out */
+    void *y;
+} ssm_ssd_step_args;
+
+ssm_status ssd_state_update(const ssm_ssd_step_args *args, hipStream_t stream);
+
+/*
+ * Causal depthwise convolution along time with bias and SiLU, the short Conv1d the
+ * x branch passes before the scan [Reading page section 5 and Hybrid page section
+ * 3: Conv1d then SiLU ahead of the SSM; Juejin page, basic usage: width d_conv = 4]:
+ *   xx = [init_state ; x] along time (zeros when init_state is NULL)
+ *   y[b,t,d] = silu(bias[d] + sum_{k<K} weight[d,k] xx[b, t-(K-1)+k, d])
+ *   (apply_silu == 0: no SiLU)
+ *   final_state[b,:,d] = the last K-1 entries of xx: the init_state of a call that
+ *   continues the same sequence.
+ * Layouts: x, y: (batch, L, D) dtype; weight: (D, K) fp32; bias: (D) fp32;
+ * init_state, final_state: (batch, K-1, D) dtype. Nullable: bias, init_state,
+ * final_state. final_state must not alias init_state or x. Supported: K in
+ * {2, 3, 4}; dtype F32 or BF16. L == 0 writes final_state = init_state (or zeros).
+ */
+typedef struct ssm_conv_args {
+    int64_t batch, seqlen, dim, width;    /* B, L, D, K */
+    ssm_dtype dtype;
+    int32_t apply_silu;
+    const void *x;
+    const float *weight;
+    const float *bias;
+    const void *init_state;
+    void *y;
+    void *final_state;
+} ssm_conv_args;
+
+ssm_status causal_conv1d_fwd(const ssm_conv_args *args, hipStream_t stream);
 
 /* Static name of a status code ("SSM_OK", ...). */
 const char *ssm_status_str(ssm_status s);

@@ -16,8 +16,9 @@ import torch
 from . import _capi
 from ._capi import SSMError
 
-__all__ = ["selective_scan_fwd", "ssd_chunked_fwd", "scan_workspace_bytes",
-           "ssd_workspace_bytes", "abi_version", "SSMError"]
+__all__ = ["selective_scan_fwd", "ssd_chunked_fwd", "selective_state_update", "ssd_state_update",
+           "causal_conv1d_fwd", "scan_workspace_bytes", "ssd_workspace_bytes", "abi_version",
+           "SSMError"]
 
 _DT = {torch.float32: _capi.SSM_F32, torch.bfloat16: _capi.SSM_BF16}
 
@@ -196,3 +197,111 @@ def ssd_chunked_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, Bm: torc
         a.workspace, a.workspace_bytes = workspace.data_ptr(), need
     _capi.check(L_.ssd_chunked_fwd(ctypes.byref(a), _stream(dev)))
     return y, hf
+
+
+def _device_of(x: torch.Tensor):
+    if x.dtype not in _DT:
+        raise TypeError("inputs must be float32 or bfloat16")
+    if x.device.type != "cuda":
+        raise ValueError("tensors must be on a HIP device (got %s)" % x.device)
+    return x.device
+
+
+def selective_state_update(state: torch.Tensor, x: torch.Tensor, delta: torch.Tensor,
+                           A: torch.Tensor, Bm: torch.Tensor, Cm: torch.Tensor,
+                           Dskip: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+                           delta_bias: Optional[torch.Tensor] = None, delta_softplus: bool = True,
+                           out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One decode step; ``state`` (batch, D, N) fp32 is updated in place.
+    x, delta, z: (batch, D); Bm, Cm: (batch, N), all in one dtype; A (D, N),
+    Dskip, delta_bias (D,) fp32. Returns y (batch, D) in x's dtype."""
+    dev = _device_of(x)
+    if x.dim() != 2 or A.dim() != 2:
+        raise ValueError("x must be (batch, D) and A (D, N)")
+    batch, D = x.shape
+    N = A.shape[1]
+    _need(x, "x", (batch, D), x.dtype, dev)
+    _need(delta, "delta", (batch, D), x.dtype, dev)
+    _need(z, "z", (batch, D), x.dtype, dev)
+    _need(Bm, "Bm", (batch, N), x.dtype, dev)
+    _need(Cm, "Cm", (batch, N), x.dtype, dev)
+    _need(A, "A", (D, N), torch.float32, dev)
+    _need(Dskip, "Dskip", (D,), torch.float32, dev)
+    _need(delta_bias, "delta_bias", (D,), torch.float32, dev)
+    _need(state, "state", (batch, D, N), torch.float32, dev)
+    y = out if out is not None else torch.empty((batch, D), dtype=x.dtype, device=dev)
+    _need(y, "out", (batch, D), x.dtype, dev)
+    a = _capi.ScanStepArgs()
+    a.batch, a.dim, a.dstate, a.dtype = batch, D, N, _DT[x.dtype]
+    a.delta_softplus = 1 if delta_softplus else 0
+    a.x, a.delta, a.z, a.Bm, a.Cm = _ptr(x), _ptr(delta), _ptr(z), _ptr(Bm), _ptr(Cm)
+    a.A, a.delta_bias, a.Dskip = _ptr(A), _ptr(delta_bias), _ptr(Dskip)
+    a.state, a.y = _ptr(state), _ptr(y)
+    _capi.check(_capi.lib().selective_state_update(ctypes.byref(a), _stream(dev)))
+    return y
+
+
+def ssd_state_update(state: torch.Tensor, x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor,
+                     Bm: torch.Tensor, Cm: torch.Tensor, Dskip: Optional[torch.Tensor] = None,
+                     z: Optional[torch.Tensor] = None, dt_bias: Optional[torch.Tensor] = None,
+                     dt_softplus: bool = True, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One decode step of the scalar-A form; ``state`` (batch, H, P, N) fp32 is
+    updated in place. x, z: (batch, H, P); dt: (batch, H); Bm, Cm: (batch, N);
+    A, Dskip, dt_bias: (H,) fp32. Returns y (batch, H, P) in x's dtype."""
+    dev = _device_of(x)
+    if x.dim() != 3 or Bm.dim() != 2:
+        raise ValueError("x must be (batch, H, P) and Bm (batch, N)")
+    batch, H, P = x.shape
+    N = Bm.shape[1]
+    _need(x, "x", (batch, H, P), x.dtype, dev)
+    _need(dt, "dt", (batch, H), x.dtype, dev)
+    _need(z, "z", (batch, H, P), x.dtype, dev)
+    _need(Bm, "Bm", (batch, N), x.dtype, dev)
+    _need(Cm, "Cm", (batch, N), x.dtype, dev)
+    _need(A, "A", (H,), torch.float32, dev)
+    _need(Dskip, "Dskip", (H,), torch.float32, dev)
+    _need(dt_bias, "dt_bias", (H,), torch.float32, dev)
+    _need(state, "state", (batch, H, P, N), torch.float32, dev)
+    y = out if out is not None else torch.empty((batch, H, P), dtype=x.dtype, device=dev)
+    _need(y, "out", (batch, H, P), x.dtype, dev)
+    a = _capi.SSDStepArgs()
+    a.batch, a.nheads, a.headdim, a.dstate, a.dtype = batch, H, P, N, _DT[x.dtype]
+    a.dt_softplus = 1 if dt_softplus else 0
+    a.x, a.dt, a.dt_bias, a.A = _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A)
+    a.Bm, a.Cm, a.Dskip, a.z = _ptr(Bm), _ptr(Cm), _ptr(Dskip), _ptr(z)
+    a.state, a.y = _ptr(state), _ptr(y)
+    _capi.check(_capi.lib().ssd_state_update(ctypes.byref(a), _stream(dev)))
+    return y
+
+
+def causal_conv1d_fwd(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                      init_state: Optional[torch.Tensor] = None, apply_silu: bool = True,
+                      return_final_state: bool = False, out: Optional[torch.Tensor] = None,
+                      final_state_out: Optional[torch.Tensor] = None):
+    """Causal depthwise conv1d + bias (+ SiLU). x: (batch, L, D) fp32 or bf16;
+    weight: (D, K) fp32; bias: (D,) fp32; init_state: (batch, K-1, D) in x's dtype.
+    Returns y (batch, L, D), and with ``return_final_state`` also the
+    (batch, K-1, D) state that continues the sequence."""
+    dev = _device_of(x)
+    if x.dim() != 3 or weight.dim() != 2:
+        raise ValueError("x must be (batch, L, D) and weight (D, K)")
+    batch, L, D = x.shape
+    K = weight.shape[1]
+    _need(x, "x", (batch, L, D), x.dtype, dev)
+    _need(weight, "weight", (D, K), torch.float32, dev)
+    _need(bias, "bias", (D,), torch.float32, dev)
+    _need(init_state, "init_state", (batch, K - 1, D), x.dtype, dev)
+    y = out if out is not None else torch.empty((batch, L, D), dtype=x.dtype, device=dev)
+    _need(y, "out", (batch, L, D), x.dtype, dev)
+    fs = None
+    if return_final_state:
+        fs = (final_state_out if final_state_out is not None
+              else torch.empty((batch, K - 1, D), dtype=x.dtype, device=dev))
+        _need(fs, "final_state_out", (batch, K - 1, D), x.dtype, dev)
+    a = _capi.ConvArgs()
+    a.batch, a.seqlen, a.dim, a.width, a.dtype = batch, L, D, K, _DT[x.dtype]
+    a.apply_silu = 1 if apply_silu else 0
+    a.x, a.weight, a.bias, a.init_state = _ptr(x), _ptr(weight), _ptr(bias), _ptr(init_state)
+    a.y, a.final_state = _ptr(y), _ptr(fs)
+    _capi.check(_capi.lib().causal_conv1d_fwd(ctypes.byref(a), _stream(dev)))
+    return (y, fs) if return_final_state else y

@@ -16,9 +16,10 @@ EXPORTS = [
     "selective_scan_fwd", "selective_scan_chunk_states", "selective_scan_apply",
     "selective_scan_validate", "selective_scan_workspace_bytes",
     "ssd_chunked_fwd", "ssd_chunked_validate", "ssd_chunked_workspace_bytes",
+    "selective_state_update", "ssd_state_update", "causal_conv1d_fwd",
     "ssm_status_str", "ssm_last_error", "ssm_abi_version",
 ]
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 _p = ctypes.c_void_p
 
@@ -44,6 +45,33 @@ class SSDArgs(ctypes.Structure):
     ]
 
 
+class ScanStepArgs(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("dim", ctypes.c_int64), ("dstate", ctypes.c_int64),
+        ("dtype", ctypes.c_int), ("delta_softplus", ctypes.c_int32),
+        ("x", _p), ("delta", _p), ("z", _p), ("Bm", _p), ("Cm", _p),
+        ("A", _p), ("delta_bias", _p), ("Dskip", _p), ("state", _p), ("y", _p),
+    ]
+
+
+class SSDStepArgs(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("nheads", ctypes.c_int64), ("headdim", ctypes.c_int64),
+        ("dstate", ctypes.c_int64), ("dtype", ctypes.c_int), ("dt_softplus", ctypes.c_int32),
+        ("x", _p), ("dt", _p), ("dt_bias", _p), ("A", _p), ("Bm", _p), ("Cm", _p),
+        ("Dskip", _p), ("z", _p), ("state", _p), ("y", _p),
+    ]
+
+
+class ConvArgs(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("dim", ctypes.c_int64),
+        ("width", ctypes.c_int64), ("dtype", ctypes.c_int), ("apply_silu", ctypes.c_int32),
+        ("x", _p), ("weight", _p), ("bias", _p), ("init_state", _p), ("y", _p),
+        ("final_state", _p),
+    ]
+
+
 _lib = None
 
 
@@ -58,7 +86,9 @@ def lib():
                 "`python selective_state_space_70_amd/build.py`." % LIB_PATH)
         L = ctypes.CDLL(LIB_PATH)
         for name, argt in (("selective_scan_fwd", ScanArgs), ("selective_scan_chunk_states", ScanArgs),
-                           ("selective_scan_apply", ScanArgs), ("ssd_chunked_fwd", SSDArgs)):
+                           ("selective_scan_apply", ScanArgs), ("ssd_chunked_fwd", SSDArgs),
+                           ("selective_state_update", ScanStepArgs), ("ssd_state_update", SSDStepArgs),
+                           ("causal_conv1d_fwd", ConvArgs)):
             f = getattr(L, name)
             f.restype = ctypes.c_int
             f.argtypes = [ctypes.POINTER(argt), _p]

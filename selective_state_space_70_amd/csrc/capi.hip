@@ -110,6 +110,84 @@ ssm_status check_ssd(const ssm_ssd_args *a) {
     return SSM_OK;
 }
 
+bool step_dstate_ok(int64_t n) { return n == 16 || n == 32 || n == 64 || n == 128 || n == 256; }
+
+ssm_status check_step(const ssm_scan_step_args *a) {
+    if (!a) return fail(SSM_EINVAL, "selective_state_update: args is NULL");
+    if (a->batch < 0 || a->dim <= 0 || a->dstate <= 0)
+        return fail(SSM_EINVAL, "selective_state_update: need batch >= 0, dim > 0, dstate > 0");
+    if (a->dtype != SSM_F32 && a->dtype != SSM_BF16)
+        return fail(SSM_EINVAL, "selective_state_update: unknown dtype %d", (int)a->dtype);
+    if (!step_dstate_ok(a->dstate))
+        return fail(SSM_ENOTSUP, "selective_state_update: dstate %lld not supported (16..256, power of 2)",
+                    (long long)a->dstate);
+    if (a->dim > (1 << 30) || a->batch * a->dim > ((int64_t)1 << 34))
+        return fail(SSM_ENOTSUP, "selective_state_update: dim <= 2^30 and batch*dim <= 2^34 supported");
+    if (a->batch == 0) return SSM_OK;
+    if (!a->x || !a->delta || !a->Bm || !a->Cm || !a->A || !a->state || !a->y)
+        return fail(SSM_EINVAL, "selective_state_update: x, delta, Bm, Cm, A, state and y are required");
+    const size_t es = esize(a->dtype);
+    if (!aligned(a->x, es) || !aligned(a->delta, es) || !aligned(a->z, es) || !aligned(a->Bm, es) ||
+        !aligned(a->Cm, es) || !aligned(a->y, es))
+        return fail(SSM_EINVAL, "selective_state_update: x, delta, z, Bm, Cm, y must be aligned to the element size");
+    if (!aligned(a->A, 4) || !aligned(a->delta_bias, 4) || !aligned(a->Dskip, 4))
+        return fail(SSM_EINVAL, "selective_state_update: fp32 parameters must be 4-byte aligned");
+    if (!aligned(a->state, 16))
+        return fail(SSM_EINVAL, "selective_state_update: state must be 16-byte aligned");
+    return SSM_OK;
+}
+
+ssm_status check_ssd_step(const ssm_ssd_step_args *a) {
+    if (!a) return fail(SSM_EINVAL, "ssd_state_update: args is NULL");
+    if (a->batch < 0 || a->nheads <= 0 || a->headdim <= 0 || a->dstate <= 0)
+        return fail(SSM_EINVAL, "ssd_state_update: need batch >= 0 and nheads, headdim, dstate > 0");
+    if (a->dtype != SSM_F32 && a->dtype != SSM_BF16)
+        return fail(SSM_EINVAL, "ssd_state_update: unknown dtype %d", (int)a->dtype);
+    if (!step_dstate_ok(a->dstate))
+        return fail(SSM_ENOTSUP, "ssd_state_update: dstate %lld not supported (16..256, power of 2)",
+                    (long long)a->dstate);
+    if (a->nheads > (1 << 20) || a->headdim > (1 << 20) || a->nheads * a->headdim > (1 << 30) ||
+        a->batch * a->nheads * a->headdim > ((int64_t)1 << 34))
+        return fail(SSM_ENOTSUP, "ssd_state_update: nheads*headdim <= 2^30 and batch*nheads*headdim <= 2^34");
+    if (a->batch == 0) return SSM_OK;
+    if (!a->x || !a->dt || !a->Bm || !a->Cm || !a->A || !a->state || !a->y)
+        return fail(SSM_EINVAL, "ssd_state_update: x, dt, Bm, Cm, A, state and y are required");
+    const size_t es = esize(a->dtype);
+    if (!aligned(a->x, es) || !aligned(a->dt, es) || !aligned(a->z, es) || !aligned(a->Bm, es) ||
+        !aligned(a->Cm, es) || !aligned(a->y, es))
+        return fail(SSM_EINVAL, "ssd_state_update: x, dt, z, Bm, Cm, y must be aligned to the element size");
+    if (!aligned(a->A, 4) || !aligned(a->dt_bias, 4) || !aligned(a->Dskip, 4))
+        return fail(SSM_EINVAL, "ssd_state_update: fp32 parameters must be 4-byte aligned");
+    if (!aligned(a->state, 16))
+        return fail(SSM_EINVAL, "ssd_state_update: state must be 16-byte aligned");
+    return SSM_OK;
+}
+
+ssm_status check_conv(const ssm_conv_args *a) {
+    if (!a) return fail(SSM_EINVAL, "causal_conv1d: args is NULL");
+    if (a->batch < 0 || a->seqlen < 0 || a->dim <= 0 || a->width <= 0)
+        return fail(SSM_EINVAL, "causal_conv1d: need batch, seqlen >= 0 and dim, width > 0");
+    if (a->dtype != SSM_F32 && a->dtype != SSM_BF16)
+        return fail(SSM_EINVAL, "causal_conv1d: unknown dtype %d", (int)a->dtype);
+    if (a->width < 2 || a->width > 4)
+        return fail(SSM_ENOTSUP, "causal_conv1d: width %lld not supported (2, 3, 4)", (long long)a->width);
+    if (a->batch > 65535 || a->dim > (1 << 30) || a->seqlen >= ((int64_t)1 << 31))
+        return fail(SSM_ENOTSUP, "causal_conv1d: batch <= 65535, dim <= 2^30, seqlen < 2^31 supported");
+    if (a->batch == 0) return SSM_OK;
+    if (!a->weight) return fail(SSM_EINVAL, "causal_conv1d: weight is NULL");
+    if (a->seqlen > 0 && (!a->x || !a->y))
+        return fail(SSM_EINVAL, "causal_conv1d: x and y are required");
+    const size_t es = esize(a->dtype);
+    if (!aligned(a->x, es) || !aligned(a->y, es) || !aligned(a->init_state, es) ||
+        !aligned(a->final_state, es))
+        return fail(SSM_EINVAL, "causal_conv1d: x, y and the states must be aligned to the element size");
+    if (!aligned(a->weight, 4) || !aligned(a->bias, 4))
+        return fail(SSM_EINVAL, "causal_conv1d: weight and bias must be 4-byte aligned");
+    if (a->final_state && (a->final_state == a->init_state || a->final_state == a->x))
+        return fail(SSM_EINVAL, "causal_conv1d: final_state must not alias init_state or x");
+    return SSM_OK;
+}
+
 ssm_status check_workspace(void *ws, size_t have, size_t need, const char *who) {
     if (need == 0) return SSM_OK;
     if (!ws) return fail(SSM_EINVAL, "%s: workspace of %zu bytes required", who, need);
@@ -180,6 +258,30 @@ ssm_status ssd_chunked_fwd(const ssm_ssd_args *a, hipStream_t stream) {
         if (s != SSM_OK) return s;
     }
     s = ssm::ssd_launch(*a, plan, stream, g_err, sizeof g_err);
+    if (s == SSM_OK) g_err[0] = 0;
+    return s;
+}
+
+ssm_status selective_state_update(const ssm_scan_step_args *a, hipStream_t stream) {
+    ssm_status s = check_step(a);
+    if (s != SSM_OK) return s;
+    s = ssm::step_launch(*a, stream, g_err, sizeof g_err);
+    if (s == SSM_OK) g_err[0] = 0;
+    return s;
+}
+
+ssm_status ssd_state_update(const ssm_ssd_step_args *a, hipStream_t stream) {
+    ssm_status s = check_ssd_step(a);
+    if (s != SSM_OK) return s;
+    s = ssm::ssd_step_launch(*a, stream, g_err, sizeof g_err);
+    if (s == SSM_OK) g_err[0] = 0;
+    return s;
+}
+
+ssm_status causal_conv1d_fwd(const ssm_conv_args *a, hipStream_t stream) {
+    ssm_status s = check_conv(a);
+    if (s != SSM_OK) return s;
+    s = ssm::conv_launch(*a, stream, g_err, sizeof g_err);
     if (s == SSM_OK) g_err[0] = 0;
     return s;
 }

@@ -39,4 +39,9 @@ SSDPlan ssd_plan(const ssm_ssd_args &a);
 ssm_status ssd_launch(const ssm_ssd_args &a, const SSDPlan &plan, hipStream_t stream,
                       char *err, size_t errlen);
 
+// Decode steps and the short convolution: no workspace, one kernel each.
+ssm_status step_launch(const ssm_scan_step_args &a, hipStream_t stream, char *err, size_t errlen);
+ssm_status ssd_step_launch(const ssm_ssd_step_args &a, hipStream_t stream, char *err, size_t errlen);
+ssm_status conv_launch(const ssm_conv_args &a, hipStream_t stream, char *err, size_t errlen);
+
 }  // namespace ssm

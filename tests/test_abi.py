@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_names():
     lib = _capi.lib()
-    assert lib.ssm_abi_version() == _capi.ABI_VERSION == 1
+    assert lib.ssm_abi_version() == _capi.ABI_VERSION == 2
     names = [lib.ssm_status_str(s).decode() for s in range(4)]
     assert names == ["SSM_OK", "SSM_EINVAL", "SSM_ENOTSUP", "SSM_EHIP"]
     assert lib.ssm_status_str(99).decode() == "SSM_UNKNOWN"
@@ -168,3 +168,88 @@ def test_binding_rejects_host_tensors():
     B = torch.zeros(1, 4, 16)
     with pytest.raises(ValueError):
         ssm.selective_scan_fwd(x, x, A, B, B)
+
+
+def step_args(**kw):
+    a = _capi.ScanStepArgs()
+    a.batch, a.dim, a.dstate, a.dtype, a.delta_softplus = 4, 96, 16, _capi.SSM_BF16, 1
+    for name in ("x", "delta", "z", "Bm", "Cm", "A", "delta_bias", "Dskip", "state", "y"):
+        setattr(a, name, FAKE)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def ssd_step_args(**kw):
+    a = _capi.SSDStepArgs()
+    a.batch, a.nheads, a.headdim, a.dstate, a.dtype, a.dt_softplus = 4, 8, 64, 128, _capi.SSM_BF16, 1
+    for name in ("x", "dt", "dt_bias", "A", "Bm", "Cm", "Dskip", "z", "state", "y"):
+        setattr(a, name, FAKE)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def conv_args(**kw):
+    a = _capi.ConvArgs()
+    a.batch, a.seqlen, a.dim, a.width, a.dtype, a.apply_silu = 2, 100, 96, 4, _capi.SSM_BF16, 1
+    a.x, a.weight, a.bias, a.init_state, a.y, a.final_state = FAKE, FAKE, FAKE, FAKE + 4096, FAKE + 8192, FAKE + 12288
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+# Only argument checks that fail run here: a passing check would launch a kernel.
+@pytest.mark.parametrize("kw,want", [
+    ({"x": None}, _capi.SSM_EINVAL),
+    ({"state": None}, _capi.SSM_EINVAL),
+    ({"A": None}, _capi.SSM_EINVAL),
+    ({"y": None}, _capi.SSM_EINVAL),
+    ({"batch": -1}, _capi.SSM_EINVAL),
+    ({"dim": 0}, _capi.SSM_EINVAL),
+    ({"dtype": 5}, _capi.SSM_EINVAL),
+    ({"state": FAKE + 4}, _capi.SSM_EINVAL),                  # state read as 16-byte vectors
+    ({"x": FAKE + 1}, _capi.SSM_EINVAL),
+    ({"dtype": _capi.SSM_F32, "Bm": FAKE + 2}, _capi.SSM_EINVAL),
+    ({"dstate": 8}, _capi.SSM_ENOTSUP),
+    ({"dstate": 48}, _capi.SSM_ENOTSUP),
+    ({"dstate": 512}, _capi.SSM_ENOTSUP),
+])
+def test_step_validation(kw, want):
+    lib = _capi.lib()
+    assert lib.selective_state_update(ctypes.byref(step_args(**kw)), None) == want
+    assert lib.ssm_last_error().decode() != ""
+
+
+@pytest.mark.parametrize("kw,want", [
+    ({"dt": None}, _capi.SSM_EINVAL),
+    ({"state": None}, _capi.SSM_EINVAL),
+    ({"headdim": 0}, _capi.SSM_EINVAL),
+    ({"state": FAKE + 8}, _capi.SSM_EINVAL),
+    ({"dstate": 100}, _capi.SSM_ENOTSUP),
+])
+def test_ssd_step_validation(kw, want):
+    assert _capi.lib().ssd_state_update(ctypes.byref(ssd_step_args(**kw)), None) == want
+
+
+@pytest.mark.parametrize("kw,want", [
+    ({"weight": None}, _capi.SSM_EINVAL),
+    ({"x": None}, _capi.SSM_EINVAL),
+    ({"y": None}, _capi.SSM_EINVAL),
+    ({"seqlen": -1}, _capi.SSM_EINVAL),
+    ({"width": 0}, _capi.SSM_EINVAL),
+    ({"y": FAKE + 1}, _capi.SSM_EINVAL),
+    ({"final_state": FAKE + 4096}, _capi.SSM_EINVAL),          # aliases init_state
+    ({"width": 5}, _capi.SSM_ENOTSUP),
+    ({"width": 1}, _capi.SSM_ENOTSUP),
+    ({"batch": 70000}, _capi.SSM_ENOTSUP),
+])
+def test_conv_validation(kw, want):
+    assert _capi.lib().causal_conv1d_fwd(ctypes.byref(conv_args(**kw)), None) == want
+
+
+def test_empty_batch_is_a_noop_for_steps_and_conv():
+    lib = _capi.lib()
+    assert lib.selective_state_update(ctypes.byref(step_args(batch=0, x=None)), None) == _capi.SSM_OK
+    assert lib.ssd_state_update(ctypes.byref(ssd_step_args(batch=0, x=None)), None) == _capi.SSM_OK
+    assert lib.causal_conv1d_fwd(ctypes.byref(conv_args(batch=0, x=None)), None) == _capi.SSM_OK

@@ -1,0 +1,93 @@
+"""Causal depthwise conv1d + SiLU on the GPU vs the fp64 oracle, element by
+element. Tolerances: relative L2 <= 1e-5 (fp32 storage), <= 3e-3 (bf16 storage:
+the output is rounded to bf16); the final state is a copy of inputs, so it must
+match bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import selective_state_space_70_amd as ssm
+import workloads
+from gpu_util import DEV, TOL
+
+pytestmark = pytest.mark.gpu
+_TD = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def _dev(a, dtype):
+    return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(DEV).to(dtype)
+
+
+def _run(inp, silu=True, state_out=True):
+    td = _TD[inp["dtype"]]
+    x = _dev(inp["x"], td)
+    w = _dev(inp["w"], torch.float32)
+    b = _dev(inp["bias"], torch.float32)
+    x0 = _dev(inp["x0"], td)
+    res = ssm.causal_conv1d_fwd(x, w, b, init_state=x0, apply_silu=silu, return_final_state=state_out)
+    torch.cuda.synchronize()
+    if state_out:
+        y, fs = res
+        return y.float().cpu().numpy(), fs.float().cpu().numpy()
+    return res.float().cpu().numpy(), None
+
+
+def _check(name, inp, silu=True):
+    y, fs = _run(inp, silu)
+    yo, fo = oracle.causal_conv1d(inp["x"], inp["w"], inp["bias"], apply_silu=silu, x0=inp["x0"],
+                                  return_state=True)
+    e = oracle.rel_l2(y, yo)
+    print("%s: rel_l2 y %.3e" % (name, e), flush=True)
+    assert e <= TOL[inp["dtype"]], (name, e)
+    assert np.array_equal(fs, fo.astype(np.float32)), name
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("batch,L,D,K", [
+    (2, 1, 64, 4), (3, 100, 96, 4), (2, 517, 203, 4), (1, 5, 30, 2), (2, 33, 64, 3),
+    (1, 2, 8, 4), (4, 300, 1000, 4), (1, 2049, 520, 4)])
+@pytest.mark.parametrize("state", [False, True])
+def test_sizes(dtype, batch, L, D, K, state):
+    """Ragged lengths and widths: D not a multiple of the 16-byte vector takes
+    the one-channel-per-lane path; L shorter than the window; segments of time
+    with a ragged last one."""
+    inp = workloads.conv_inputs(batch, L, D, K, dtype, seed=L * 7 + D, with_state=state)
+    _check("conv %s B%d L%d D%d K%d state=%s" % (dtype, batch, L, D, K, state), inp)
+
+
+def test_no_silu_no_bias():
+    inp = workloads.conv_inputs(2, 77, 128, 4, "f32", seed=3, with_bias=False, with_state=True)
+    _check("conv raw", inp, silu=False)
+
+
+@pytest.mark.parametrize("state", [False, True])
+def test_empty_sequence_passes_state_through(state):
+    inp = workloads.conv_inputs(2, 0, 64, 4, "bf16", seed=4, with_state=state)
+    y, fs = _run(inp)
+    assert y.shape == (2, 0, 64)
+    want = inp["x0"] if state else np.zeros((2, 3, 64), np.float32)
+    assert np.array_equal(fs, want)
+
+
+@pytest.mark.parametrize("cut", [1, 2, 3, 250])
+def test_streaming_is_bit_exact(cut):
+    """Two calls chained through the state give bit-identical outputs to one call."""
+    inp = workloads.conv_inputs(2, 600, 256, 4, "bf16", seed=5)
+    td = torch.bfloat16
+    x = _dev(inp["x"], td)
+    w = _dev(inp["w"], torch.float32)
+    b = _dev(inp["bias"], torch.float32)
+    full, fs_full = ssm.causal_conv1d_fwd(x, w, b, return_final_state=True)
+    a, st = ssm.causal_conv1d_fwd(x[:, :cut].contiguous(), w, b, return_final_state=True)
+    c, st2 = ssm.causal_conv1d_fwd(x[:, cut:].contiguous(), w, b, init_state=st, return_final_state=True)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([a, c], dim=1), full)
+    assert torch.equal(st2, fs_full)
+
+
+def test_mamba_130m_layer_shape():
+    """Batch 8, L 2048, D 1536, width 4, bf16: the shape of the scan workload it
+    feeds; every output compared."""
+    inp = workloads.conv_inputs(8, 2048, 1536, 4, "bf16", seed=6, with_state=True)
+    _check("conv B8 L2048 D1536", inp)

@@ -23,6 +23,8 @@ Recipe (stated once, used everywhere):
     spreads it by roughly e^{+-1} at two sigma. Nothing is clamped.
   * scan: ``A[d, n] = -(n + 1)``; SSD: ``A_h = -U(1, 16)``.
   * B and C have layout (batch, L, N): one group shared by every channel.
+  * short convolution: its own seed sequence spawned as ``[x, w, bias, x0]``;
+    ``x, x0 ~ N(0,1)``, ``w ~ N(0, 1/K)``, ``bias ~ N(0, 0.1^2)`` (fp32 weights).
 """
 from __future__ import annotations
 
@@ -34,7 +36,7 @@ import numpy as np
 
 __all__ = [
     "ScanConfig", "SSDConfig", "CONFIGS", "CONFIG_ORDER",
-    "round_bf16", "bf16_bits", "scan_inputs", "ssd_inputs", "make_inputs",
+    "round_bf16", "bf16_bits", "scan_inputs", "ssd_inputs", "make_inputs", "conv_inputs",
 ]
 
 
@@ -187,3 +189,17 @@ def make_inputs(key: str, seed: Optional[int] = None, **kw) -> dict:
                            (cfg.dt_min, cfg.dt_max), **kw)
     return ssd_inputs(cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.dstate, cfg.dtype,
                       seed, (cfg.dt_min, cfg.dt_max), (cfg.a_lo, cfg.a_hi), **kw)
+
+
+def conv_inputs(batch: int, seqlen: int, dim: int, width: int = 4, dtype: str = "bf16",
+                seed: int = 0, with_state: bool = False, with_bias: bool = True) -> dict:
+    """Inputs of one causal depthwise conv1d call: x (batch, L, D) in the storage
+    dtype, weight (D, K) and bias (D,) fp32, x0 (batch, K-1, D) history or None."""
+    kids = np.random.SeedSequence(seed).spawn(4)
+    r = [np.random.Generator(np.random.PCG64(c)) for c in kids]
+    out = {"dtype": dtype, "kind": "conv"}
+    out["x"] = _normal(r[0], (batch, seqlen, dim), 1.0, dtype)
+    out["w"] = r[1].standard_normal(size=(dim, width), dtype=np.float32) * np.float32(1.0 / math.sqrt(width))
+    out["bias"] = (r[2].standard_normal(size=dim, dtype=np.float32) * np.float32(0.1)) if with_bias else None
+    out["x0"] = _normal(r[3], (batch, width - 1, dim), 1.0, dtype) if with_state else None
+    return out
