@@ -89,6 +89,10 @@ ssm_status check_ssd_sizes(const ssm_ssd_args *a) {
         return fail(SSM_ENOTSUP, "ssd_chunked: seqlen*nheads*headdim*2 must be < 2^31 bytes");
     if ((a->seqlen + a->chunk - 1) / a->chunk > 65535)
         return fail(SSM_ENOTSUP, "ssd_chunked: at most 65535 chunks");
+    // workgroups of the output kernel: one per (batch, chunk, 4 heads, 64 rows)
+    if (a->batch * ((a->seqlen + a->chunk - 1) / a->chunk) * ((a->nheads + 3) / 4 + 8) * (a->chunk / 64) >=
+        ((int64_t)1 << 31))
+        return fail(SSM_ENOTSUP, "ssd_chunked: batch * chunks * heads too large for one launch");
     return SSM_OK;
 }
 

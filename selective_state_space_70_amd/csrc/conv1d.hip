@@ -48,7 +48,7 @@ struct Vec<uint16_t, 8> {
         u32x4 v;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            v[i] = (uint32_t)f32_to_bf16(o[2 * i]) | ((uint32_t)f32_to_bf16(o[2 * i + 1]) << 16);
+            v[i] = pack_bf16x2(o[2 * i], o[2 * i + 1]);
         *(u32x4 *)p = v;
     }
 };

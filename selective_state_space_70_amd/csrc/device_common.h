@@ -31,6 +31,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float v) {
     __bf16 b = (__bf16)v;  // v_cvt_pk_bf16_f32: round to nearest even
     return __builtin_bit_cast(uint16_t, b);
 }
+// Two fp32 values as a packed pair of bf16 (lo in bits 0..15), one v_cvt_pk_bf16_f32.
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
+
 __device__ __forceinline__ void store_val(float *p, float v) { *p = v; }
 __device__ __forceinline__ void store_val(uint16_t *p, float v) { *p = f32_to_bf16(v); }
 
@@ -40,7 +47,11 @@ __device__ __forceinline__ void store_val(uint16_t *p, float v) { *p = f32_to_bf
 // Reads at or past `bytes` return 0 (hardware range check on the vector offset).
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+    // the size is wave-uniform; readfirstlane keeps it in an SGPR even when the
+    // compiler computed it with a vector instruction (a resource in VGPRs would
+    // force a loop over lanes around every access)
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0,
+                                             (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 __device__ __forceinline__ void buf_load(rsrc_t r, uint32_t voff, uint32_t soff, uint16_t &v) {
     v = __builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, 0);

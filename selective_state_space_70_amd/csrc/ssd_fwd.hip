@@ -55,9 +55,12 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8 &a, const bf16x8 &b, 
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4 &v) { return __builtin_bit_cast(bf16x8, v); }
 
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+// 16 bytes through a buffer resource (0 outside its range)
+__device__ __forceinline__ u32x4 load16(rsrc_t r, uint32_t voff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
 }
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) { return pack_bf16x2(lo, hi); }
 
 // (lo halves of a, b) and (hi halves of a, b) as packed bf16 pairs.
 __device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) {
@@ -269,198 +272,345 @@ __global__ __launch_bounds__(256) void ssd_state_pass_kernel(const SSDK p, int N
 }
 
 // ---------------------------------------------------------------- chunk output
-// One workgroup per (batch, chunk, head, 64-row block of time); wave w owns the
-// 16 rows 64*tb + 16*w. The entering state of the head is staged in LDS once. The
-// s dimension is streamed in 32-row blocks: B (natural [s][n] layout, the A
-// operand of G^T = B C^T) and x (transposed, the B operand of Y += M X) go
-// through double-buffered LDS shared by the four waves, the next block being
-// loaded into registers while the current one is computed.
-template <int N, int Q>
-__global__ __launch_bounds__(kThreads) void ssd_chunk_out_kernel(const SSDK p) {
-    constexpr int SBK = 32;                   // s rows per block
-    constexpr int LDB = N + 8;                // padded LDS rows (bf16)
-    constexpr int LDX = SBK + 8;
-    constexpr int SPL = Q / 64;
-    constexpr int KN = N / 32;                // k steps over the state dimension
-    constexpr int TBS = Q / 64;               // 64-row time blocks per chunk
-    constexpr int BV = SBK * N / 8 / kThreads;   // 16-byte B vectors per thread per block
-    static_assert(BV >= 1, "B block smaller than one vector per thread");
-    __shared__ float cs2[Q];                  // cs * log2(e)
-    __shared__ float dts[Q];                  // dt (0 past the end of the sequence)
-    __shared__ __attribute__((aligned(16))) uint16_t SinL[kP][LDB];
-    // the B double buffer and, after the s loop, the output tile share this space
-    constexpr int BB_BYTES = 2 * SBK * LDB * 2;
-    constexpr int OT_BYTES = 4 * 16 * (kP + 4) * 4;
-    __shared__ __attribute__((aligned(16))) uint8_t bo_space[BB_BYTES > OT_BYTES ? BB_BYTES : OT_BYTES];
-    __shared__ __attribute__((aligned(16))) uint16_t XTb[2][kP][LDX];
-    uint16_t (*Bb)[SBK][LDB] = reinterpret_cast<uint16_t (*)[SBK][LDB]>(bo_space);
-    float (*Ot)[16][kP + 4] = reinterpret_cast<float (*)[16][kP + 4]>(bo_space);
+// One workgroup per (batch, chunk, group of HG heads, 64-row block of time); wave
+// w owns rows t0 = 64 tb + 16 w .. t0 + 15 for all HG heads of the group. The
+// score tile G^T = B C^T of a 64-row block of s is computed once per wave and
+// reused by every head of the group: only the decay weights differ per head.
+//
+// With r = 64 tb - 1 (the last step before this time block; cs_r = 0 for tb = 0)
+// the decay of s <= r < t factors as exp(cs_t - cs_s) = a_t w_s, a_t = exp(cs_t -
+// cs_r), w_s = exp(cs_r - cs_s), both <= 1. So for every block of s before the
+// time block, M = G o (w_s dt_s) needs no exponential per element; those blocks and
+// the entering state (exp(cs_t) C Sin = a_t exp(cs_r) C Sin) accumulate into one
+// tile that is scaled by a_t once, after which the diagonal block adds its terms
+// with the exact per-element weight exp(cs_t - cs_s) dt_s [s <= t].
+//
+// Layouts in LDS: B rows natural ([s][n], the A operand of G^T); x transposed per
+// head ([p][s], the B operand of Y += M X) with s permuted inside each 32-block so
+// that a lane's 8 k-values (s = 32a + 16h + 4kb + i, h, i in 0..1, 0..3 from the
+// accumulator layout of G^T) sit in 16 contiguous bytes. The next block of B and x
+// is loaded into registers while the current one is computed.
+template <int N>
+struct OutCfg {
+    static constexpr int HG = 2;   // heads per workgroup
+};
 
-    const int c = blockIdx.x / TBS, tb = blockIdx.x % TBS, h = blockIdx.y, b = blockIdx.z;
+// position of chunk-local s (its block of 64 aside) in the permuted x rows
+__device__ __forceinline__ int perm_s(int sl) {
+    return ((sl >> 5) << 5) | (((sl >> 2) & 3) << 3) | (((sl >> 4) & 1) << 2) | (sl & 3);
+}
+
+template <int N, int Q>
+__global__ __launch_bounds__(kThreads, 2) void ssd_chunk_out_kernel(const SSDK p, int nhg, int ngroups) {
+    constexpr int HG = OutCfg<N>::HG;
+    constexpr int TBS = Q / 64;               // 64-row time blocks per chunk
+    constexpr int KN = N / 32;                // k steps over the state dimension
+    constexpr int SPL = Q / 64;
+    constexpr int LDB = N + 8;                // padded bf16 rows of B and Sin
+    constexpr int LDX = 64 + 8;               // padded bf16 rows of transposed x
+    constexpr int LDO = kP + 4;               // padded fp32 rows of the output tile
+    constexpr int SIN_HEADS = 2;              // heads of Sin staged together
+    constexpr int BB_BYTES = 64 * LDB * 2;
+    constexpr int XT_BYTES = HG * kP * LDX * 2;
+    constexpr int SIN_BYTES = SIN_HEADS * kP * LDB * 2;
+    constexpr int OT_BYTES = 4 * 16 * LDO * 4;
+    constexpr int R0_BYTES = std::max(BB_BYTES, OT_BYTES);   // B block, later the output tile
+    constexpr int U_BYTES = std::max(R0_BYTES + XT_BYTES, SIN_BYTES);
+    constexpr int BV = 64 * N / 8 / kThreads;     // 16-byte B vectors per thread per block
+    constexpr int XB = HG * 128 / kThreads;       // 4x8 x blocks per thread per block
+    static_assert(BV >= 1 && XB >= 1, "staging split");
+    __shared__ float cs2[HG][Q];              // cs * log2(e) per head
+    __shared__ float dts[HG][Q];              // dt (0 past the end of the sequence)
+    __shared__ float wts[HG][Q];              // w_s dt_s for s before the time block
+    __shared__ __attribute__((aligned(16))) uint8_t ubuf[U_BYTES];
+    uint16_t (*Bb)[LDB] = reinterpret_cast<uint16_t (*)[LDB]>(ubuf);
+    uint16_t (*XT)[kP][LDX] = reinterpret_cast<uint16_t (*)[kP][LDX]>(ubuf + R0_BYTES);
+    uint16_t (*SinL)[kP][LDB] = reinterpret_cast<uint16_t (*)[kP][LDB]>(ubuf);
+    float (*Ot)[16][LDO] = reinterpret_cast<float (*)[16][LDO]>(ubuf);
+
+    // block -> (group, time block); the time blocks of one group share an XCD
+    int grp, tb;
+    if (TBS == 1) {
+        grp = blockIdx.x;
+        tb = 0;
+    } else {
+        const int id = blockIdx.x, rest = id / 8;
+        tb = rest % TBS;
+        grp = (rest / TBS) * 8 + id % 8;
+    }
+    if (grp >= ngroups) return;
+    const int hg = grp % nhg, c = (grp / nhg) % p.nc, b = grp / (nhg * p.nc);
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int r16 = lane & 15, kb = lane >> 4;
     const int64_t t_base = (int64_t)c * Q;
     const int T = (int)std::min<int64_t>(Q, p.L - t_base);
-    const int t0 = tb * 64 + wv * 16;                 // this wave's first row
-    const int blk_end = std::min(tb * 64 + 64, T);    // rows of this workgroup end here
     if (tb * 64 >= T) return;                         // whole block past the sequence (uniform)
-    const int nsb = (blk_end + SBK - 1) / SBK;        // s blocks that reach this time block
+    const int t0 = tb * 64 + wv * 16;                 // this wave's first row
+    const int h0 = hg * HG;
 
-    if (wv == 0) {
-        float dtv[SPL], cs[SPL];
-        head_dt_cs<Q>(p, b, h, c, dtv, cs);
-#pragma unroll
-        for (int i = 0; i < SPL; ++i) {
-            cs2[lane * SPL + i] = cs[i] * kLog2e;
-            dts[lane * SPL + i] = dtv[i];
-        }
-    }
-    const uint16_t *sin_h = p.sin + (((int64_t)b * p.nc + c) * p.H + h) * (int64_t)kP * N;
-    for (int v = tid; v < kP * N / 8; v += kThreads) {
-        const int pp = v / (N / 8), n8 = (v % (N / 8)) * 8;
-        *(u32x4 *)&SinL[pp][n8] = *(const u32x4 *)(sin_h + pp * N + n8);
-    }
     const uint16_t *Brow = p.Bm + ((int64_t)b * p.L + t_base) * N;
     const uint16_t *Crow = p.Cm + ((int64_t)b * p.L + t_base) * N;
-    const uint16_t *Xrow = p.x + ((int64_t)b * p.L + t_base) * p.H * kP + (int64_t)h * kP;
     const int64_t xstride = (int64_t)p.H * kP;
+    const uint16_t *Xrow = p.x + ((int64_t)b * p.L + t_base) * xstride;
 
-    // one s block into registers: BV 16-byte vectors of B; x as 4 x 8 blocks
-    // (threads < 64 own one block each: 8 row-quads x 8 column-octets)
-    u32x4 breg[BV], xreg[4];
+    // next block of B and x into registers. Buffer resources cover the rows of the
+    // block that exist (s < T), so rows past the sequence read as 0; a head past H
+    // gets an offset outside every resource.
+    u32x4 breg[BV], xreg[XB][4];
+    uint32_t boff[BV], xoff[XB][4];
+#pragma unroll
+    for (int i = 0; i < BV; ++i) {
+        const int v = tid + i * kThreads;
+        boff[i] = (uint32_t)(v / (N / 8) * N + (v % (N / 8)) * 8) * 2u;
+    }
+#pragma unroll
+    for (int i = 0; i < XB; ++i) {
+        const int blk = tid + i * kThreads;
+        const int j = blk >> 7, g = blk & 15, po = (blk & 127) >> 4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            xoff[i][e] = h0 + j < p.H ? (uint32_t)(((4 * g + e) * xstride + (h0 + j) * kP + po * 8) * 2) : 0x80000000u;
+    }
     auto fetch = [&](int sb) {
-        const int s0 = sb * SBK;
+        const int s0 = sb * 64;
+        const int rows = std::max(0, T - s0);
+        const rsrc_t rb = make_rsrc(Brow + (int64_t)s0 * N, (uint32_t)(rows * N * 2));
+        const rsrc_t rx = make_rsrc(Xrow + (int64_t)s0 * xstride, (uint32_t)(rows * xstride * 2));
+#pragma unroll
+        for (int i = 0; i < BV; ++i) breg[i] = load16(rb, boff[i]);
+#pragma unroll
+        for (int i = 0; i < XB; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) xreg[i][e] = load16(rx, xoff[i][e]);
+    };
+    auto stash = [&]() {
 #pragma unroll
         for (int i = 0; i < BV; ++i) {
             const int v = tid + i * kThreads;
-            const int s = v / (N / 8), n8 = (v % (N / 8)) * 8;
-            breg[i] = s0 + s < T ? *(const u32x4 *)(Brow + (int64_t)(s0 + s) * N + n8) : u32x4{0u, 0u, 0u, 0u};
+            *(u32x4 *)&Bb[v / (N / 8)][(v % (N / 8)) * 8] = breg[i];
         }
-        if (tid < 64) {
-            const int rs = (tid / 8) * 4, cp = (tid % 8) * 8;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                xreg[i] = s0 + rs + i < T ? *(const u32x4 *)(Xrow + (int64_t)(s0 + rs + i) * xstride + cp)
-                                          : u32x4{0u, 0u, 0u, 0u};
+        for (int i = 0; i < XB; ++i) {
+            const int blk = tid + i * kThreads;
+            const int j = blk >> 7, g = blk & 15, po = (blk & 127) >> 4;
+            store_transposed(xreg[i], &XT[j][0][0], LDX, po * 8, perm_s(4 * g));
         }
     };
-    auto stash = [&](int buf) {
+    // Sin of SIN_HEADS heads at a time through registers into LDS
+    constexpr int SV = SIN_HEADS * kP * N / 8 / kThreads;
+    const uint16_t *sin_c = p.sin + ((int64_t)b * p.nc + c) * p.H * (int64_t)kP * N;
+    u32x4 sreg[SV];
+    auto sin_fetch = [&](int j0) {
+        const int nh = std::max(0, std::min(SIN_HEADS, p.H - (h0 + j0)));
+        const rsrc_t rs = make_rsrc(sin_c + (int64_t)(h0 + j0) * kP * N, (uint32_t)(nh * kP * N * 2));
 #pragma unroll
-        for (int i = 0; i < BV; ++i) {
+        for (int i = 0; i < SV; ++i) sreg[i] = load16(rs, (uint32_t)(tid + i * kThreads) * 16u);
+    };
+    auto sin_stash = [&]() {
+#pragma unroll
+        for (int i = 0; i < SV; ++i) {
             const int v = tid + i * kThreads;
-            const int s = v / (N / 8), n8 = (v % (N / 8)) * 8;
-            *(u32x4 *)&Bb[buf][s][n8] = breg[i];
+            const int jj = v / (kP * N / 8), rem = v % (kP * N / 8);
+            *(u32x4 *)&SinL[jj][rem / (N / 8)][(rem % (N / 8)) * 8] = sreg[i];
         }
-        if (tid < 64) store_transposed(xreg, &XTb[buf][0][0], LDX, (tid % 8) * 8, (tid / 8) * 4);
     };
-
     fetch(0);
-    const bool live = t0 < T;                          // this wave has rows to produce
+    sin_fetch(0);
+
+    // per-head steps and cumulative log-decays (one wave per head)
+    if (wv < HG) {
+        float dtv[SPL], cs[SPL];
+        head_dt_cs<Q>(p, b, std::min(h0 + wv, p.H - 1), c, dtv, cs);
+#pragma unroll
+        for (int i = 0; i < SPL; ++i) {
+            cs2[wv][lane * SPL + i] = cs[i] * kLog2e;
+            dts[wv][lane * SPL + i] = dtv[i];
+        }
+    }
     const int trow = std::min(t0 + r16, T - 1);
     bf16x8 cfr[KN];
 #pragma unroll
     for (int k = 0; k < KN; ++k)
         cfr[k] = as_bf16x8(*(const u32x4 *)(Crow + (int64_t)trow * N + 32 * k + 8 * kb));
-    stash(0);
+    sin_stash();
+    if (HG > SIN_HEADS) sin_fetch(SIN_HEADS);
     __syncthreads();
-
-    // carried state: Y = exp(cs_t) * (C Sin)
-    f32x4 yacc[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int k = 0; k < KN; ++k)
-            a = mfma16x16x32(cfr[k], as_bf16x8(*(const u32x4 *)&SinL[q * 16 + r16][32 * k + 8 * kb]), a);
-        yacc[q] = a;
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const float sc = fast_exp2(cs2[std::min(t0 + 4 * kb + e, Q - 1)]);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) yacc[q][e] *= sc;
+    const int r = tb * 64 - 1;
+    for (int v = tid; v < HG * tb * 64; v += kThreads) {
+        const int j = v / (tb * 64), s = v % (tb * 64);
+        wts[j][s] = fast_exp2(cs2[j][r] - cs2[j][s]) * dts[j][s];
     }
 
-    const int tcol = std::min(t0 + r16, Q - 1);
-    const float ct = cs2[tcol];
-    for (int sb = 0; sb < nsb; ++sb) {
-        const int buf = sb & 1;
-        if (sb + 1 < nsb) fetch(sb + 1);
-        const int s0 = sb * SBK;
-        if (live && s0 <= t0 + 15) {
-            // G^T[s][t]: lane holds s = s0+16u+4kb+e, t = t0+r16
-            f32x4 g[2];
+    // entering state: Y = exp(cs_r) C Sin (scaled by a_t further down)
+    f32x4 yo[HG][4];
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
+    for (int j0 = 0; j0 < HG; j0 += SIN_HEADS) {
+        if (j0) {
+            __syncthreads();
+            sin_stash();
+            __syncthreads();
+            if (j0 + SIN_HEADS < HG) sin_fetch(j0 + SIN_HEADS);
+        }
+#pragma unroll
+        for (int jj = 0; jj < SIN_HEADS; ++jj) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
                 f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int k = 0; k < KN; ++k)
-                    a = mfma16x16x32(as_bf16x8(*(const u32x4 *)&Bb[buf][16 * u + r16][32 * k + 8 * kb]), cfr[k], a);
-                g[u] = a;
-            }
-            const bool diag = s0 + 31 > t0;
-            uint32_t mw[4];
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const f32x4 cd = *(const f32x4 *)&cs2[s0 + 16 * u + 4 * kb];
-                const f32x4 dd = *(const f32x4 *)&dts[s0 + 16 * u + 4 * kb];
-                float v[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    float val = g[u][e] * fast_exp2(ct - cd[e]) * dd[e];
-                    if (diag && s0 + 16 * u + 4 * kb + e > tcol) val = 0.0f;
-                    v[e] = val;
-                }
-                mw[2 * u] = pack_bf16(v[0], v[1]);
-                mw[2 * u + 1] = pack_bf16(v[2], v[3]);
-            }
-            const bf16x8 mfr = as_bf16x8(u32x4{mw[0], mw[1], mw[2], mw[3]});
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint16_t *xr = &XTb[buf][q * 16 + r16][0];
-                const u32x2 lo = *(const u32x2 *)(xr + 4 * kb);
-                const u32x2 hi = *(const u32x2 *)(xr + 16 + 4 * kb);
-                yacc[q] = mfma16x16x32(mfr, as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), yacc[q]);
+                    a = mfma16x16x32(cfr[k], as_bf16x8(*(const u32x4 *)&SinL[jj][q * 16 + r16][32 * k + 8 * kb]), a);
+                yo[j0 + jj][q] = a;
             }
         }
-        if (sb + 1 < nsb) stash(buf ^ 1);
-        __syncthreads();
+    }
+#pragma unroll
+    for (int j = 0; j < HG; ++j) {
+        const float er = tb ? fast_exp2(cs2[j][r]) : 1.0f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) yo[j][q] *= er;
+    }
+    __syncthreads();
+    stash();
+    __syncthreads();
+
+    for (int sb = 0; sb <= tb; ++sb) {
+        if (sb < tb) fetch(sb + 1);
+        const int s0 = sb * 64;
+        const bool diag = sb == tb;
+        // G^T[s][t]: lane holds s = s0 + 16u + 4kb + i, t = t0 + r16
+        f32x4 g[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            g[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (!diag || u <= wv) {
+#pragma unroll
+                for (int k = 0; k < KN; ++k)
+                    g[u] = mfma16x16x32(as_bf16x8(*(const u32x4 *)&Bb[16 * u + r16][32 * k + 8 * kb]), cfr[k], g[u]);
+            }
+        }
+        if (!diag) {
+#pragma unroll
+            for (int j = 0; j < HG; ++j) {
+#pragma unroll
+                for (int a = 0; a < 2; ++a) {
+                    const f32x4 w0 = *(const f32x4 *)&wts[j][s0 + 32 * a + 4 * kb];
+                    const f32x4 w1 = *(const f32x4 *)&wts[j][s0 + 32 * a + 16 + 4 * kb];
+                    const bf16x8 mfr = as_bf16x8(u32x4{
+                        pack_bf16(g[2 * a][0] * w0[0], g[2 * a][1] * w0[1]),
+                        pack_bf16(g[2 * a][2] * w0[2], g[2 * a][3] * w0[3]),
+                        pack_bf16(g[2 * a + 1][0] * w1[0], g[2 * a + 1][1] * w1[1]),
+                        pack_bf16(g[2 * a + 1][2] * w1[2], g[2 * a + 1][3] * w1[3])});
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        yo[j][q] = mfma16x16x32(mfr, as_bf16x8(*(const u32x4 *)&XT[j][q * 16 + r16][32 * a + 8 * kb]),
+                                                yo[j][q]);
+                }
+                __builtin_amdgcn_sched_barrier(0);   // keep one head's operands live at a time
+            }
+        } else {
+            const int tcol = t0 + r16;                // the A-operand row of this lane
+#pragma unroll
+            for (int j = 0; j < HG; ++j) {
+                const float cr = tb ? cs2[j][r] : 0.0f;
+                // a_t for the accumulator rows t0 + 4kb + i
+                const f32x4 crow = *(const f32x4 *)&cs2[j][t0 + 4 * kb];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float at = fast_exp2(crow[i] - cr);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) yo[j][q][i] *= at;
+                }
+                const float ct = cs2[j][tcol];
+#pragma unroll
+                for (int a = 0; a < 2; ++a) {
+                    if (32 * a > 16 * wv + 15) continue;   // every s of this half is after every row
+                    float v[8];
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const int sb0 = s0 + 32 * a + 16 * hh + 4 * kb;
+                        const f32x4 cd = *(const f32x4 *)&cs2[j][sb0];
+                        const f32x4 dd = *(const f32x4 *)&dts[j][sb0];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const float m = g[2 * a + hh][i] * fast_exp2(ct - cd[i]) * dd[i];
+                            v[4 * hh + i] = sb0 + i <= tcol ? m : 0.0f;
+                        }
+                    }
+                    const bf16x8 mfr = as_bf16x8(u32x4{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]),
+                                                       pack_bf16(v[4], v[5]), pack_bf16(v[6], v[7])});
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        yo[j][q] = mfma16x16x32(mfr, as_bf16x8(*(const u32x4 *)&XT[j][q * 16 + r16][32 * a + 8 * kb]),
+                                                yo[j][q]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        if (sb < tb) {
+            __syncthreads();
+            stash();
+            __syncthreads();
+        }
     }
 
-    // y = Y + D x, gated by silu(z): the tile goes through LDS (reusing the B
-    // buffers) so that each lane writes rows of 8 bf16.
+    // y = Y + D x, gated by silu(z). x of these rows is the last staged block
+    // (the diagonal one), still in LDS; z is fetched for every head at once. Each
+    // head's tile then goes through the wave's own LDS rows so that a lane writes
+    // rows of 8 bf16.
+    u32x4 zreg[HG][2];
+    if (p.z) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+        for (int j = 0; j < HG; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) Ot[wv][4 * kb + e][q * 16 + r16] = yacc[q][e];
-    __syncthreads();
-    if (!live) return;
-    const float dsk = p.Dskip ? p.Dskip[h] : 0.0f;
+            for (int rr = 0; rr < 2; ++rr) {
+                const int t = std::min(t0 + rr * 8 + (lane >> 3), T - 1), h = std::min(h0 + j, p.H - 1);
+                zreg[j][rr] = *(const u32x4 *)(p.z + (((int64_t)b * p.L + t_base + t) * p.H + h) * kP + (lane & 7) * 8);
+            }
+    }
 #pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
-        const int row = rr * 8 + (lane >> 3), c8 = (lane & 7) * 8;
-        const int t = t0 + row;
-        if (t < T) {
-            const int64_t off = (((int64_t)b * p.L + t_base + t) * p.H + h) * kP + c8;
-            const u32x4 xv = *(const u32x4 *)(p.x + off);
-            u32x4 zv = u32x4{0u, 0u, 0u, 0u};
-            if (p.z) zv = *(const u32x4 *)(p.z + off);
+    for (int j = 0; j < HG; ++j) {
+        const float dsk = (p.Dskip && h0 + j < p.H) ? p.Dskip[h0 + j] : 0.0f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const u32x2 xv = *(const u32x2 *)&XT[j][q * 16 + r16][perm_s(16 * wv + 4 * kb)];
+            yo[j][q][0] = fmaf(dsk, bf16_lo(xv[0]), yo[j][q][0]);
+            yo[j][q][1] = fmaf(dsk, bf16_hi(xv[0]), yo[j][q][1]);
+            yo[j][q][2] = fmaf(dsk, bf16_lo(xv[1]), yo[j][q][2]);
+            yo[j][q][3] = fmaf(dsk, bf16_hi(xv[1]), yo[j][q][3]);
+        }
+    }
+    __syncthreads();                                   // every wave is done with the B block
+#pragma unroll
+    for (int j = 0; j < HG; ++j) {
+        const int h = h0 + j;
+        if (h >= p.H) break;                           // uniform
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Ot[wv][4 * kb + i][q * 16 + r16] = yo[j][q][i];
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // the wave's own rows only
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+            const int row = rr * 8 + (lane >> 3), c8 = (lane & 7) * 8;
+            const int t = t0 + row;
             const f32x4 o0 = *(const f32x4 *)&Ot[wv][row][c8];
             const f32x4 o1 = *(const f32x4 *)&Ot[wv][row][c8 + 4];
-            const float o[8] = {o0[0], o0[1], o0[2], o0[3], o1[0], o1[1], o1[2], o1[3]};
-            u32x4 outv;
+            if (t < T) {
+                const float o[8] = {o0[0], o0[1], o0[2], o0[3], o1[0], o1[1], o1[2], o1[3]};
+                u32x4 outv;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                float y0 = fmaf(dsk, bf16_lo(xv[e]), o[2 * e]);
-                float y1 = fmaf(dsk, bf16_hi(xv[e]), o[2 * e + 1]);
-                if (p.z) {
-                    y0 *= silu_f32(bf16_lo(zv[e]));
-                    y1 *= silu_f32(bf16_hi(zv[e]));
+                for (int e = 0; e < 4; ++e) {
+                    float y0 = o[2 * e], y1 = o[2 * e + 1];
+                    if (p.z) {
+                        y0 *= silu_f32(bf16_lo(zreg[j][rr][e]));
+                        y1 *= silu_f32(bf16_hi(zreg[j][rr][e]));
+                    }
+                    outv[e] = pack_bf16(y0, y1);
                 }
-                outv[e] = pack_bf16(y0, y1);
+                *(u32x4 *)(p.y + (((int64_t)b * p.L + t_base + t) * p.H + h) * kP + c8) = outv;
             }
-            *(u32x4 *)(p.y + off) = outv;
         }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     }
 }
 
@@ -476,8 +626,11 @@ void launch_nq(const SSDK &k, int batch, hipStream_t s) {
     const int64_t total = (int64_t)batch * k.H * kP * N / 4;
     hipLaunchKernelGGL(ssd_state_pass_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
                        k, N, total);
-    hipLaunchKernelGGL((ssd_chunk_out_kernel<N, Q>), dim3((unsigned)(k.nc * (Q / 64)), (unsigned)k.H, (unsigned)batch),
-                       dim3(kThreads), 0, s, k);
+    const int nhg = (k.H + OutCfg<N>::HG - 1) / OutCfg<N>::HG;
+    const int64_t ngroups = (int64_t)batch * k.nc * nhg;
+    const int64_t nblocks = Q == 64 ? ngroups : (ngroups + 7) / 8 * 8 * (Q / 64);
+    hipLaunchKernelGGL((ssd_chunk_out_kernel<N, Q>), dim3((unsigned)nblocks), dim3(kThreads), 0, s, k, nhg,
+                       (int)ngroups);
 }
 
 template <int N>

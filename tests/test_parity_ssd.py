@@ -34,6 +34,15 @@ def test_state_sizes(N):
     _check("N=%d" % N, inp, 128)
 
 
+@pytest.mark.parametrize("batch,L,H,N,chunk", [(2, 700, 9, 128, 256), (2, 513, 5, 256, 128),
+                                                 (3, 200, 6, 64, 64), (1, 1000, 13, 128, 128)])
+def test_head_groups(batch, L, H, N, chunk):
+    """Head counts that leave the last group of heads partly empty, several batch
+    rows and chunks, every time block of a chunk."""
+    inp = workloads.ssd_inputs(batch, L, H, 64, N, "bf16", seed=H * 31 + N, with_h0=True, with_z=True)
+    _check("heads B%d L%d H%d N%d Q%d" % (batch, L, H, N, chunk), inp, chunk)
+
+
 def test_gate_and_no_skip():
     inp = workloads.ssd_inputs(2, 333, 3, 64, 64, "bf16", seed=21, with_z=True, with_D=False)
     _check("z, no D", inp, 64)
