@@ -51,11 +51,11 @@ def lib():
             L = ctypes.CDLL(_LIB)
         L.oracle_selective_scan_f64.restype = ctypes.c_int
         L.oracle_selective_scan_f64.argtypes = [
-            _i64, _i64, _i64, _i64, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p,
+            _i64, _i64, _i64, _i64, _i64, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p,
             _f64p, ctypes.c_int, _i64p, _i64, _f64p, _f64p]
         L.oracle_ssd_f64.restype = ctypes.c_int
         L.oracle_ssd_f64.argtypes = [
-            _i64, _i64, _i64, _i64, _i64, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p,
+            _i64, _i64, _i64, _i64, _i64, _i64, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p,
             _f32p, _f64p, ctypes.c_int, _i64p, _i64, _f64p, _f64p]
         L.oracle_causal_conv1d_f64.restype = ctypes.c_int
         L.oracle_causal_conv1d_f64.argtypes = [_i64, _i64, _i64, _i64, _f32p, _f32p, _f32p,
@@ -120,7 +120,8 @@ def selective_scan(x, delta, A, Bm, Cm, Dskip=None, z=None, delta_bias=None, h0=
                    delta_softplus: bool = True, channels: Optional[Sequence[int]] = None):
     """Reference selective scan in fp64.
 
-    Shapes: x, delta, z (batch, L, D); Bm, Cm (batch, L, N); A (D, N);
+    Shapes: x, delta, z (batch, L, D); Bm, Cm (batch, L, N), or (batch, L, G, N)
+    for G groups (channel d reads group d // (D // G)); A (D, N);
     Dskip, delta_bias (D,); h0 (batch, D, N).
     Returns ``(y, h_final)``. With ``channels`` (ids ``b*D + d``) the outputs are
     ``y (len(channels), L)`` and ``h_final (len(channels), N)``; otherwise
@@ -128,12 +129,13 @@ def selective_scan(x, delta, A, Bm, Cm, Dskip=None, z=None, delta_bias=None, h0=
     """
     batch, L, D = np.shape(x)
     N = np.shape(A)[1]
+    G = np.shape(Bm)[2] if np.ndim(Bm) == 4 else 1
     keep = []
     xs, xp = _f32(x, (batch, L, D)); keep.append(xs)
     ds, dp = _f32(delta, (batch, L, D)); keep.append(ds)
     zs, zp = _f32(z, (batch, L, D)); keep.append(zs)
-    bs, bp = _f32(Bm, (batch, L, N)); keep.append(bs)
-    cs, cp = _f32(Cm, (batch, L, N)); keep.append(cs)
+    bs, bp = _f32(np.reshape(Bm, (batch, L, G, N)), (batch, L, G, N)); keep.append(bs)
+    cs, cp = _f32(np.reshape(Cm, (batch, L, G, N)), (batch, L, G, N)); keep.append(cs)
     as_, ap = _f32(A, (D, N)); keep.append(as_)
     bis, bip = _f32(delta_bias, (D,)); keep.append(bis)
     dks, dkp = _f32(Dskip, (D,)); keep.append(dks)
@@ -148,7 +150,7 @@ def selective_scan(x, delta, A, Bm, Cm, Dskip=None, z=None, delta_bias=None, h0=
         chp, nch = ch.ctypes.data_as(_i64p), len(ch)
         y = np.empty((nch, L), dtype=np.float64)
         hf = np.empty((nch, N), dtype=np.float64)
-    rc = lib().oracle_selective_scan_f64(batch, L, D, N, xp, dp, zp, bp, cp, ap, bip, dkp, hp,
+    rc = lib().oracle_selective_scan_f64(batch, L, D, N, G, xp, dp, zp, bp, cp, ap, bip, dkp, hp,
                                          int(bool(delta_softplus)), chp, nch,
                                          y.ctypes.data_as(_f64p), hf.ctypes.data_as(_f64p))
     if rc != 0:
@@ -161,18 +163,20 @@ def ssd(x, dt, A, Bm, Cm, Dskip=None, z=None, dt_bias=None, h0=None,
     """Reference scalar-A (SSD) form in fp64, evaluated as the plain recurrence.
 
     Shapes: x, z (batch, L, H, P); dt (batch, L, H); A, Dskip, dt_bias (H,);
-    Bm, Cm (batch, L, N); h0 (batch, H, P, N). ``channels`` are ids
+    Bm, Cm (batch, L, N), or (batch, L, G, N) for G groups (head h reads group
+    h // (H // G)); h0 (batch, H, P, N). ``channels`` are ids
     ``(b*H + h)*P + p``; outputs as for :func:`selective_scan`.
     """
     batch, L, H, P = np.shape(x)
-    N = np.shape(Bm)[2]
+    G = np.shape(Bm)[2] if np.ndim(Bm) == 4 else 1
+    N = np.shape(Bm)[-1]
     keep = []
     xs, xp = _f32(x, (batch, L, H, P)); keep.append(xs)
     ds, dp = _f32(dt, (batch, L, H)); keep.append(ds)
     bis, bip = _f32(dt_bias, (H,)); keep.append(bis)
     as_, ap = _f32(A, (H,)); keep.append(as_)
-    bs, bp = _f32(Bm, (batch, L, N)); keep.append(bs)
-    cs, cp = _f32(Cm, (batch, L, N)); keep.append(cs)
+    bs, bp = _f32(np.reshape(Bm, (batch, L, G, N)), (batch, L, G, N)); keep.append(bs)
+    cs, cp = _f32(np.reshape(Cm, (batch, L, G, N)), (batch, L, G, N)); keep.append(cs)
     dks, dkp = _f32(Dskip, (H,)); keep.append(dks)
     zs, zp = _f32(z, (batch, L, H, P)); keep.append(zs)
     hs, hp = _f64(h0, (batch, H, P, N)); keep.append(hs)
@@ -186,7 +190,7 @@ def ssd(x, dt, A, Bm, Cm, Dskip=None, z=None, dt_bias=None, h0=None,
         chp, nch = ch.ctypes.data_as(_i64p), len(ch)
         y = np.empty((nch, L), dtype=np.float64)
         hf = np.empty((nch, N), dtype=np.float64)
-    rc = lib().oracle_ssd_f64(batch, L, H, P, N, xp, dp, bip, ap, bp, cp, dkp, zp, hp,
+    rc = lib().oracle_ssd_f64(batch, L, H, P, N, G, xp, dp, bip, ap, bp, cp, dkp, zp, hp,
                               int(bool(dt_softplus)), chp, nch,
                               y.ctypes.data_as(_f64p), hf.ctypes.data_as(_f64p))
     if rc != 0:

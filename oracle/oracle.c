@@ -78,7 +78,10 @@ void oracle_set_num_threads(int n)
 /*
  * Selective scan, Mamba-1 form.
  *   x, delta, z : (batch, L, D)  row-major, D fastest (float32 storage values)
- *   Bm, Cm      : (batch, L, N)  one group shared by all D channels
+ *   Bm, Cm      : (batch, L, G, N)  G groups; channel d reads group d / (D / G)
+ *                 (G = 1: one group shared by all D channels) [the pages' B_t,
+ *                 C_t are functions of the token; grouping channels so that each
+ *                 group has its own B, C is the multi-group variant]
  *   A           : (D, N)
  *   delta_bias, Dskip : (D)  (NULL -> 0)
  *   z           : NULL -> no gate
@@ -93,7 +96,7 @@ void oracle_set_num_threads(int n)
  *   h_final may be NULL.
  * Returns 0, or -1 on a bad size.
  */
-int oracle_selective_scan_f64(int64_t batch, int64_t L, int64_t D, int64_t N,
+int oracle_selective_scan_f64(int64_t batch, int64_t L, int64_t D, int64_t N, int64_t G,
                               const float *x, const float *delta, const float *z,
                               const float *Bm, const float *Cm, const float *A,
                               const float *delta_bias, const float *Dskip,
@@ -101,7 +104,7 @@ int oracle_selective_scan_f64(int64_t batch, int64_t L, int64_t D, int64_t N,
                               const int64_t *chans, int64_t nchan,
                               double *y, double *h_final)
 {
-    if (batch < 0 || L < 0 || D <= 0 || N <= 0 || N > 4096) return -1;
+    if (batch < 0 || L < 0 || D <= 0 || N <= 0 || N > 4096 || G <= 0 || D % G) return -1;
     const int64_t total = chans ? nchan : batch * D;
     int bad = 0;
 
@@ -110,6 +113,7 @@ int oracle_selective_scan_f64(int64_t batch, int64_t L, int64_t D, int64_t N,
         const int64_t c = chans ? chans[i] : i;
         if (c < 0 || c >= batch * D) { bad = 1; continue; }
         const int64_t b = c / D, d = c % D;
+        const int64_t g = d / (D / G);                  /* B, C group of this channel */
         double h[4096];
         for (int64_t n = 0; n < N; ++n)
             h[n] = h0 ? h0[(b * D + d) * N + n] : 0.0;
@@ -118,7 +122,7 @@ int oracle_selective_scan_f64(int64_t batch, int64_t L, int64_t D, int64_t N,
 
         for (int64_t t = 0; t < L; ++t) {
             const int64_t e = (b * L + t) * D + d;      /* (b, t, d) */
-            const int64_t r = (b * L + t) * N;          /* (b, t, :) */
+            const int64_t r = ((b * L + t) * G + g) * N;  /* (b, t, g, :) */
             const double xv = (double)x[e];
             const double v = (double)delta[e] + bias;
             const double dt = delta_softplus ? softplus_f64(v) : v;
@@ -150,7 +154,7 @@ int oracle_selective_scan_f64(int64_t batch, int64_t L, int64_t D, int64_t N,
  *   x, z   : (batch, L, H, P)     z NULL -> no gate
  *   dt     : (batch, L, H) raw    dt_bias (H) NULL -> 0
  *   A      : (H)                  Dskip (H) NULL -> 0
- *   Bm, Cm : (batch, L, N)        one group shared by all heads
+ *   Bm, Cm : (batch, L, G, N)     head h reads group h / (H / G)
  *   h0     : (batch, H, P, N) double, NULL -> zero
  *   chans  : ids c = (b*H + h)*P + p; NULL -> all
  * Outputs: chans == NULL: y (batch, L, H, P), h_final (batch, H, P, N);
@@ -158,14 +162,14 @@ int oracle_selective_scan_f64(int64_t batch, int64_t L, int64_t D, int64_t N,
  * This is the same recurrence as above with the step shared across a head; it
  * is written out separately in the SSD layout rather than by broadcasting.
  */
-int oracle_ssd_f64(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
+int oracle_ssd_f64(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G,
                    const float *x, const float *dt_raw, const float *dt_bias,
                    const float *A, const float *Bm, const float *Cm,
                    const float *Dskip, const float *z, const double *h0,
                    int dt_softplus, const int64_t *chans, int64_t nchan,
                    double *y, double *h_final)
 {
-    if (batch < 0 || L < 0 || H <= 0 || P <= 0 || N <= 0 || N > 4096) return -1;
+    if (batch < 0 || L < 0 || H <= 0 || P <= 0 || N <= 0 || N > 4096 || G <= 0 || H % G) return -1;
     const int64_t total = chans ? nchan : batch * H * P;
     int bad = 0;
 
@@ -174,6 +178,7 @@ int oracle_ssd_f64(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
         const int64_t c = chans ? chans[i] : i;
         if (c < 0 || c >= batch * H * P) { bad = 1; continue; }
         const int64_t b = c / (H * P), hh = (c / P) % H, p = c % P;
+        const int64_t g = hh / (H / G);
         double h[4096];
         for (int64_t n = 0; n < N; ++n)
             h[n] = h0 ? h0[c * N + n] : 0.0;
@@ -183,7 +188,7 @@ int oracle_ssd_f64(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
 
         for (int64_t t = 0; t < L; ++t) {
             const int64_t e = ((b * L + t) * H + hh) * P + p;   /* (b, t, h, p) */
-            const int64_t r = (b * L + t) * N;
+            const int64_t r = ((b * L + t) * G + g) * N;
             const double xv = (double)x[e];
             const double v = (double)dt_raw[(b * L + t) * H + hh] + bias;
             const double dtv = dt_softplus ? softplus_f64(v) : v;

@@ -477,11 +477,44 @@ def pin_ssd_decode_steps_equal_ssd(seed=19):
     assert _rel(st, hf) < TOL
 
 
+def pin_groups_split(seed=20):
+    """With G groups of B, C, the scan equals G separate single-group scans, one
+    per contiguous block of D / G channels with that group's B and C."""
+    rng = np.random.default_rng(seed)
+    batch, L, D, N, G = 2, 7, 6, 3, 3
+    x, z, Dsk, A, dt, _, _ = _rand_case(rng, batch, L, D, N)
+    Bg = _f32(rng.standard_normal((batch, L, G, N)))
+    Cg = _f32(rng.standard_normal((batch, L, G, N)))
+    h0 = rng.standard_normal((batch, D, N))
+    y, hf = oracle.selective_scan(x, dt, A, Bg, Cg, Dsk, z, None, h0, delta_softplus=False)
+    k = D // G
+    for g in range(G):
+        sl = slice(g * k, (g + 1) * k)
+        yg, hg = oracle.selective_scan(x[:, :, sl], dt[:, :, sl], A[sl], Bg[:, :, g], Cg[:, :, g],
+                                       Dsk[sl], z[:, :, sl], None, h0[:, sl], delta_softplus=False)
+        assert np.array_equal(y[:, :, sl], yg) and np.array_equal(hf[:, sl], hg), "group %d" % g
+
+
+def pin_ssd_groups_split(seed=21):
+    rng = np.random.default_rng(seed)
+    batch, L, H, P, N, G = 2, 6, 4, 2, 3, 2
+    x, dt, bias, A, _, _, Dsk, z, h0 = _ssd_case(rng, batch, L, H, P, N)
+    Bg = _f32(rng.standard_normal((batch, L, G, N)))
+    Cg = _f32(rng.standard_normal((batch, L, G, N)))
+    y, hf = oracle.ssd(x, dt, A, Bg, Cg, Dskip=Dsk, z=z, dt_bias=bias, h0=h0)
+    k = H // G
+    for g in range(G):
+        sl = slice(g * k, (g + 1) * k)
+        yg, hg = oracle.ssd(x[:, :, sl], dt[:, :, sl], A[sl], Bg[:, :, g], Cg[:, :, g], Dskip=Dsk[sl],
+                            z=z[:, :, sl], dt_bias=bias[sl], h0=h0[:, sl])
+        assert np.array_equal(y[:, :, sl], yg) and np.array_equal(hf[:, sl], hg), "SSD group %d" % g
+
+
 SCAN_PINS = [pin_lti_convolution, pin_lti_lfilter, pin_semiseparable, pin_small_step_keeps_state,
              pin_large_step_forgets, pin_zero_input_pure_decay, pin_split_invariance,
              pin_linearity, pin_geometric_series, pin_softplus_identities, pin_gate_identity,
-             pin_skip_only, pin_channel_subset, pin_decode_steps_equal_scan]
+             pin_skip_only, pin_channel_subset, pin_decode_steps_equal_scan, pin_groups_split]
 SSD_PINS = [pin_ssd_semiseparable, pin_ssd_is_broadcast_scan, pin_ssd_channel_subset,
-            pin_ssd_decode_steps_equal_ssd]
+            pin_ssd_decode_steps_equal_ssd, pin_ssd_groups_split]
 CONV_PINS = [pin_conv1d_numpy, pin_conv1d_history, pin_conv1d_streaming]
 ALL_PINS = SCAN_PINS + SSD_PINS + CONV_PINS

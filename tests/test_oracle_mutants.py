@@ -42,6 +42,8 @@ MUTANTS = [
      "h[n] = abar * h[n] + (double)Bm[r + n] * xv;", "ssd"),
     ("ssd_x_layout", "const int64_t e = ((b * L + t) * H + hh) * P + p;",
      "const int64_t e = ((b * L + t) * P + p) * H + hh;", "ssd"),
+    ("group_of_channel", "const int64_t g = d / (D / G);", "const int64_t g = d % G;", "scan"),
+    ("ssd_group_of_head", "const int64_t g = hh / (H / G);", "const int64_t g = hh % G;", "ssd"),
     ("conv_not_causal", "const int64_t s = t - (K - 1) + k;", "const int64_t s = t - k;", "conv"),
     ("conv_history_reversed", "x0[(b * (K - 1) + (K - 1) + s) * D + d]", "x0[(b * (K - 1) - 1 - s) * D + d]",
      "conv"),
