@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 2
+#define SSM_ABI_VERSION 3
 
 typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
 
@@ -65,8 +65,10 @@ typedef enum {
  * [Juejin page, long-document streaming step(x, state)]. Abar = exp(dt A) and the
  * Euler input term dt B x are the adopted discretisation.
  *
- * Layouts: x, delta, z, y: (batch, L, D), dtype. Bm, Cm: (batch, L, N), dtype, one
- * group shared by every channel. A: (D, N) fp32 (diagonal, real; rows of the form
+ * Layouts: x, delta, z, y: (batch, L, D), dtype. Bm, Cm: (batch, L, G, N), dtype:
+ * G groups of B, C (ngroups; 0 or 1 = one group shared by every channel), channel
+ * d reading group d / (D / G); G > 1 needs D / G to be a multiple of 64 (a wave
+ * of 64 channels reads one row). A: (D, N) fp32 (diagonal, real; rows of the form
  * A[d,n] = (n+1) A[d,0] are detected on the device and take a faster exact path).
  * delta_bias, Dskip: (D) fp32. h0, h_final: (batch, D, N) fp32.
  * Nullable: z (no gate), delta_bias (0), Dskip (0), h0 (zero state),
@@ -75,6 +77,7 @@ typedef enum {
  */
 typedef struct ssm_scan_args {
     int64_t batch, seqlen, dim, dstate;   /* B, L, D, N */
+    int64_t ngroups;                      /* G, groups of Bm/Cm (0 or 1: one) */
     ssm_dtype dtype;                      /* storage of x, delta, z, Bm, Cm, y */
     int32_t delta_softplus;               /* 1: softplus(delta + bias); 0: delta + bias */
     const void *x, *delta, *z;
@@ -102,13 +105,16 @@ typedef struct ssm_scan_args {
  * the SSM as a structured (semiseparable) attention-like matrix that runs as
  * matrix multiplication; selectivity restricted to keep that structure].
  * Layouts: x, z, y: (batch, L, H, P) dtype; dt: (batch, L, H) dtype; Bm, Cm:
- * (batch, L, N) dtype; dt_bias, A, Dskip: (H) fp32; h0, h_final: (batch, H, P, N) fp32.
+ * (batch, L, G, N) dtype, head h reading group h / (H / G) (ngroups 0 or 1: one
+ * group; H must be a multiple of G); dt_bias, A, Dskip: (H) fp32; h0, h_final:
+ * (batch, H, P, N) fp32.
  * Nullable: z, dt_bias, Dskip, h0, h_final. Supported: dtype BF16; N in
  * {64, 128, 256}; P == 64; chunk in {64, 128, 256}. Any L >= 0 (the last chunk
  * may be short); results do not depend on `chunk` beyond rounding.
  */
 typedef struct ssm_ssd_args {
     int64_t batch, seqlen, nheads, headdim, dstate, chunk;  /* B, L, H, P, N, Q */
+    int64_t ngroups;                                        /* G (0 or 1: one group) */
     ssm_dtype dtype;
     int32_t dt_softplus;                  /* 1: softplus(dt + bias); 0: dt + bias */
     const void *x;
@@ -173,13 +179,15 @@ size_t ssd_chunked_workspace_bytes(const ssm_ssd_args *args);
  * back to state [Juejin page, long-document streaming: step(x, state) returns the
  * output and the next state; SSM page, how it works: inference keeps a fixed-size
  * state per channel and advances it token by token].
- * Layouts: x, delta, z, y: (batch, D) dtype; Bm, Cm: (batch, N) dtype; A: (D, N)
- * fp32; delta_bias, Dskip: (D) fp32; state: (batch, D, N) fp32, 16-byte aligned
+ * Layouts: x, delta, z, y: (batch, D) dtype; Bm, Cm: (batch, G, N) dtype (channel d
+ * reads group d / (D / G)); A: (D, N) fp32; delta_bias, Dskip: (D) fp32; state:
+ * (batch, D, N) fp32, 16-byte aligned
  * (the layout of h0 / h_final above). Nullable: z, delta_bias, Dskip.
  * Supported: N in {16, 32, 64, 128, 256}; dtype F32 or BF16. batch == 0 is a no-op.
  */
 typedef struct ssm_scan_step_args {
     int64_t batch, dim, dstate;           /* B, D, N */
+    int64_t ngroups;                      /* G (0 or 1: one group); D % G == 0 */
     ssm_dtype dtype;                      /* storage of x, delta, z, Bm, Cm, y */
     int32_t delta_softplus;
     const void *x, *delta, *z;
@@ -201,13 +209,15 @@ ssm_status selective_state_update(const ssm_scan_step_args *args, hipStream_t st
  * [Mamba-2 page, Background: the discrete recurrence, here with one scalar decay
  * per head; Juejin page, step(x, state)]. ssd_chunked_fwd over one token with
  * h0 = state and h_final written back to state.
- * Layouts: x, z, y: (batch, H, P) dtype; dt: (batch, H) dtype; Bm, Cm: (batch, N)
- * dtype; dt_bias, A, Dskip: (H) fp32; state: (batch, H, P, N) fp32, 16-byte aligned.
+ * Layouts: x, z, y: (batch, H, P) dtype; dt: (batch, H) dtype; Bm, Cm: (batch, G, N)
+ * dtype (head h reads group h / (H / G)); dt_bias, A, Dskip: (H) fp32; state:
+ * (batch, H, P, N) fp32, 16-byte aligned.
  * Nullable: z, dt_bias, Dskip. Supported: any P >= 1; N in {16, 32, 64, 128, 256};
  * dtype F32 or BF16.
  */
 typedef struct ssm_ssd_step_args {
     int64_t batch, nheads, headdim, dstate;   /* B, H, P, N */
+    int64_t ngroups;                          /* G (0 or 1: one group); H % G == 0 */
     ssm_dtype dtype;
     int32_t dt_softplus;
     const void *x;

@@ -50,11 +50,18 @@ def abi_version() -> int:
     return _capi.lib().ssm_abi_version()
 
 
+def _groups(Bm: torch.Tensor, plain_dims: int) -> int:
+    """Number of B/C groups: Bm carries a group axis just before N when it has
+    one more dimension than the single-group layout."""
+    return Bm.shape[-2] if Bm.dim() == plain_dims + 1 else 1
+
+
 def _scan_args(x, delta, A, Bm, Cm, Dskip, z, delta_bias, h0, delta_softplus, y, h_final):
     batch, L, D = x.shape
     N = A.shape[1]
     a = _capi.ScanArgs()
     a.batch, a.seqlen, a.dim, a.dstate = batch, L, D, N
+    a.ngroups = _groups(Bm, 3)
     a.dtype = _DT[x.dtype]
     a.delta_softplus = 1 if delta_softplus else 0
     a.x, a.delta, a.z = _ptr(x), _ptr(delta), _ptr(z)
@@ -79,7 +86,8 @@ def selective_scan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm
                        final_state_out: Optional[torch.Tensor] = None,
                        workspace: Optional[torch.Tensor] = None, passes: str = "all"
                        ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Selective scan. x, delta, z: (batch, L, D); Bm, Cm: (batch, L, N), all
+    """Selective scan. x, delta, z: (batch, L, D); Bm, Cm: (batch, L, N), or
+    (batch, L, G, N) for G groups (channel d reads group d // (D // G)); all
     fp32 or all bf16; A: (D, N) fp32; Dskip, delta_bias: (D,) fp32;
     h0: (batch, D, N) fp32. Returns (y (batch, L, D) in x's dtype,
     h_final (batch, D, N) fp32 or None).
@@ -97,11 +105,12 @@ def selective_scan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm
         raise ValueError("tensors must be on a HIP device (got %s)" % dev)
     batch, L, D = x.shape
     N = A.shape[1]
+    bc = (batch, L, N) if Bm.dim() == 3 else (batch, L, Bm.shape[2], N)
     _need(x, "x", (batch, L, D), x.dtype, dev)
     _need(delta, "delta", (batch, L, D), x.dtype, dev)
     _need(z, "z", (batch, L, D), x.dtype, dev)
-    _need(Bm, "Bm", (batch, L, N), x.dtype, dev)
-    _need(Cm, "Cm", (batch, L, N), x.dtype, dev)
+    _need(Bm, "Bm", bc, x.dtype, dev)
+    _need(Cm, "Cm", bc, x.dtype, dev)
     _need(A, "A", (D, N), torch.float32, dev)
     _need(Dskip, "Dskip", (D,), torch.float32, dev)
     _need(delta_bias, "delta_bias", (D,), torch.float32, dev)
@@ -133,7 +142,8 @@ def _ssd_args(x, dt, A, Bm, Cm, Dskip, z, dt_bias, h0, chunk, dt_softplus, y, h_
     batch, L, H, P = x.shape
     a = _capi.SSDArgs()
     a.batch, a.seqlen, a.nheads, a.headdim = batch, L, H, P
-    a.dstate, a.chunk = Bm.shape[2], chunk
+    a.dstate, a.chunk = Bm.shape[-1], chunk
+    a.ngroups = _groups(Bm, 3)
     a.dtype = _DT[x.dtype]
     a.dt_softplus = 1 if dt_softplus else 0
     a.x, a.dt, a.dt_bias, a.A = _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A)
@@ -160,21 +170,23 @@ def ssd_chunked_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, Bm: torc
                     workspace: Optional[torch.Tensor] = None
                     ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Scalar-A (SSD) form. x, z: (batch, L, H, P) bf16; dt: (batch, L, H) bf16;
-    Bm, Cm: (batch, L, N) bf16; A, Dskip, dt_bias: (H,) fp32; h0: (batch, H, P, N)
+    Bm, Cm: (batch, L, N) bf16, or (batch, L, G, N) for G groups (head h reads
+    group h // (H // G)); A, Dskip, dt_bias: (H,) fp32; h0: (batch, H, P, N)
     fp32. Returns (y (batch, L, H, P) bf16, h_final (batch, H, P, N) fp32 or None)."""
-    if x.dim() != 4 or Bm.dim() != 3:
-        raise ValueError("x must be (batch, L, H, P) and Bm (batch, L, N)")
+    if x.dim() != 4 or Bm.dim() not in (3, 4):
+        raise ValueError("x must be (batch, L, H, P) and Bm (batch, L, [G,] N)")
     if x.dtype not in _DT:
         raise TypeError("x must be float32 or bfloat16")
     dev = x.device
     if dev.type != "cuda":
         raise ValueError("tensors must be on a HIP device (got %s)" % dev)
     batch, L, H, P = x.shape
-    N = Bm.shape[2]
+    N = Bm.shape[-1]
+    bc = (batch, L, N) if Bm.dim() == 3 else (batch, L, Bm.shape[2], N)
     _need(dt, "dt", (batch, L, H), x.dtype, dev)
     _need(z, "z", (batch, L, H, P), x.dtype, dev)
-    _need(Bm, "Bm", (batch, L, N), x.dtype, dev)
-    _need(Cm, "Cm", (batch, L, N), x.dtype, dev)
+    _need(Bm, "Bm", bc, x.dtype, dev)
+    _need(Cm, "Cm", bc, x.dtype, dev)
     _need(A, "A", (H,), torch.float32, dev)
     _need(Dskip, "Dskip", (H,), torch.float32, dev)
     _need(dt_bias, "dt_bias", (H,), torch.float32, dev)
@@ -213,18 +225,19 @@ def selective_state_update(state: torch.Tensor, x: torch.Tensor, delta: torch.Te
                            delta_bias: Optional[torch.Tensor] = None, delta_softplus: bool = True,
                            out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """One decode step; ``state`` (batch, D, N) fp32 is updated in place.
-    x, delta, z: (batch, D); Bm, Cm: (batch, N), all in one dtype; A (D, N),
+    x, delta, z: (batch, D); Bm, Cm: (batch, N) or (batch, G, N), all in one dtype; A (D, N),
     Dskip, delta_bias (D,) fp32. Returns y (batch, D) in x's dtype."""
     dev = _device_of(x)
     if x.dim() != 2 or A.dim() != 2:
         raise ValueError("x must be (batch, D) and A (D, N)")
     batch, D = x.shape
     N = A.shape[1]
+    bc = (batch, N) if Bm.dim() == 2 else (batch, Bm.shape[1], N)
     _need(x, "x", (batch, D), x.dtype, dev)
     _need(delta, "delta", (batch, D), x.dtype, dev)
     _need(z, "z", (batch, D), x.dtype, dev)
-    _need(Bm, "Bm", (batch, N), x.dtype, dev)
-    _need(Cm, "Cm", (batch, N), x.dtype, dev)
+    _need(Bm, "Bm", bc, x.dtype, dev)
+    _need(Cm, "Cm", bc, x.dtype, dev)
     _need(A, "A", (D, N), torch.float32, dev)
     _need(Dskip, "Dskip", (D,), torch.float32, dev)
     _need(delta_bias, "delta_bias", (D,), torch.float32, dev)
@@ -233,6 +246,7 @@ def selective_state_update(state: torch.Tensor, x: torch.Tensor, delta: torch.Te
     _need(y, "out", (batch, D), x.dtype, dev)
     a = _capi.ScanStepArgs()
     a.batch, a.dim, a.dstate, a.dtype = batch, D, N, _DT[x.dtype]
+    a.ngroups = _groups(Bm, 2)
     a.delta_softplus = 1 if delta_softplus else 0
     a.x, a.delta, a.z, a.Bm, a.Cm = _ptr(x), _ptr(delta), _ptr(z), _ptr(Bm), _ptr(Cm)
     a.A, a.delta_bias, a.Dskip = _ptr(A), _ptr(delta_bias), _ptr(Dskip)
@@ -246,18 +260,20 @@ def ssd_state_update(state: torch.Tensor, x: torch.Tensor, dt: torch.Tensor, A: 
                      z: Optional[torch.Tensor] = None, dt_bias: Optional[torch.Tensor] = None,
                      dt_softplus: bool = True, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """One decode step of the scalar-A form; ``state`` (batch, H, P, N) fp32 is
-    updated in place. x, z: (batch, H, P); dt: (batch, H); Bm, Cm: (batch, N);
+    updated in place. x, z: (batch, H, P); dt: (batch, H); Bm, Cm: (batch, N) or
+    (batch, G, N);
     A, Dskip, dt_bias: (H,) fp32. Returns y (batch, H, P) in x's dtype."""
     dev = _device_of(x)
-    if x.dim() != 3 or Bm.dim() != 2:
-        raise ValueError("x must be (batch, H, P) and Bm (batch, N)")
+    if x.dim() != 3 or Bm.dim() not in (2, 3):
+        raise ValueError("x must be (batch, H, P) and Bm (batch, [G,] N)")
     batch, H, P = x.shape
-    N = Bm.shape[1]
+    N = Bm.shape[-1]
+    bc = (batch, N) if Bm.dim() == 2 else (batch, Bm.shape[1], N)
     _need(x, "x", (batch, H, P), x.dtype, dev)
     _need(dt, "dt", (batch, H), x.dtype, dev)
     _need(z, "z", (batch, H, P), x.dtype, dev)
-    _need(Bm, "Bm", (batch, N), x.dtype, dev)
-    _need(Cm, "Cm", (batch, N), x.dtype, dev)
+    _need(Bm, "Bm", bc, x.dtype, dev)
+    _need(Cm, "Cm", bc, x.dtype, dev)
     _need(A, "A", (H,), torch.float32, dev)
     _need(Dskip, "Dskip", (H,), torch.float32, dev)
     _need(dt_bias, "dt_bias", (H,), torch.float32, dev)
@@ -266,6 +282,7 @@ def ssd_state_update(state: torch.Tensor, x: torch.Tensor, dt: torch.Tensor, A: 
     _need(y, "out", (batch, H, P), x.dtype, dev)
     a = _capi.SSDStepArgs()
     a.batch, a.nheads, a.headdim, a.dstate, a.dtype = batch, H, P, N, _DT[x.dtype]
+    a.ngroups = _groups(Bm, 2)
     a.dt_softplus = 1 if dt_softplus else 0
     a.x, a.dt, a.dt_bias, a.A = _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A)
     a.Bm, a.Cm, a.Dskip, a.z = _ptr(Bm), _ptr(Cm), _ptr(Dskip), _ptr(z)

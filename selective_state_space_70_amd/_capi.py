@@ -19,7 +19,7 @@ EXPORTS = [
     "selective_state_update", "ssd_state_update", "causal_conv1d_fwd",
     "ssm_status_str", "ssm_last_error", "ssm_abi_version",
 ]
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 _p = ctypes.c_void_p
 
@@ -27,7 +27,8 @@ _p = ctypes.c_void_p
 class ScanArgs(ctypes.Structure):
     _fields_ = [
         ("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("dim", ctypes.c_int64),
-        ("dstate", ctypes.c_int64), ("dtype", ctypes.c_int), ("delta_softplus", ctypes.c_int32),
+        ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64), ("dtype", ctypes.c_int),
+        ("delta_softplus", ctypes.c_int32),
         ("x", _p), ("delta", _p), ("z", _p), ("Bm", _p), ("Cm", _p),
         ("A", _p), ("delta_bias", _p), ("Dskip", _p), ("h0", _p),
         ("y", _p), ("h_final", _p), ("workspace", _p), ("workspace_bytes", ctypes.c_size_t),
@@ -38,7 +39,7 @@ class SSDArgs(ctypes.Structure):
     _fields_ = [
         ("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64),
         ("headdim", ctypes.c_int64), ("dstate", ctypes.c_int64), ("chunk", ctypes.c_int64),
-        ("dtype", ctypes.c_int), ("dt_softplus", ctypes.c_int32),
+        ("ngroups", ctypes.c_int64), ("dtype", ctypes.c_int), ("dt_softplus", ctypes.c_int32),
         ("x", _p), ("dt", _p), ("dt_bias", _p), ("A", _p), ("Bm", _p), ("Cm", _p),
         ("Dskip", _p), ("z", _p), ("h0", _p), ("y", _p), ("h_final", _p),
         ("workspace", _p), ("workspace_bytes", ctypes.c_size_t),
@@ -48,7 +49,7 @@ class SSDArgs(ctypes.Structure):
 class ScanStepArgs(ctypes.Structure):
     _fields_ = [
         ("batch", ctypes.c_int64), ("dim", ctypes.c_int64), ("dstate", ctypes.c_int64),
-        ("dtype", ctypes.c_int), ("delta_softplus", ctypes.c_int32),
+        ("ngroups", ctypes.c_int64), ("dtype", ctypes.c_int), ("delta_softplus", ctypes.c_int32),
         ("x", _p), ("delta", _p), ("z", _p), ("Bm", _p), ("Cm", _p),
         ("A", _p), ("delta_bias", _p), ("Dskip", _p), ("state", _p), ("y", _p),
     ]
@@ -57,7 +58,8 @@ class ScanStepArgs(ctypes.Structure):
 class SSDStepArgs(ctypes.Structure):
     _fields_ = [
         ("batch", ctypes.c_int64), ("nheads", ctypes.c_int64), ("headdim", ctypes.c_int64),
-        ("dstate", ctypes.c_int64), ("dtype", ctypes.c_int), ("dt_softplus", ctypes.c_int32),
+        ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64), ("dtype", ctypes.c_int),
+        ("dt_softplus", ctypes.c_int32),
         ("x", _p), ("dt", _p), ("dt_bias", _p), ("A", _p), ("Bm", _p), ("Cm", _p),
         ("Dskip", _p), ("z", _p), ("state", _p), ("y", _p),
     ]

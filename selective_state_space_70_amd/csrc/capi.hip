@@ -25,6 +25,8 @@ size_t esize(ssm_dtype t) { return t == SSM_BF16 ? 2 : 4; }
 
 constexpr int64_t kMaxRowBytes = (int64_t)1 << 31;
 
+int64_t groups(int64_t g) { return g <= 1 ? 1 : g; }
+
 // Sizes, dtype and supported shapes only (what the workspace query depends on).
 ssm_status check_scan_sizes(const ssm_scan_args *a) {
     if (!a) return fail(SSM_EINVAL, "selective_scan: args is NULL");
@@ -37,11 +39,19 @@ ssm_status check_scan_sizes(const ssm_scan_args *a) {
     if (a->dstate != 16 && a->dstate != 32 && a->dstate != 64)
         return fail(SSM_ENOTSUP, "selective_scan: dstate %lld not supported (16, 32, 64)",
                     (long long)a->dstate);
+    if (a->ngroups < 0 || a->dim % groups(a->ngroups))
+        return fail(SSM_EINVAL, "selective_scan: ngroups %lld must be >= 0 and divide dim %lld",
+                    (long long)a->ngroups, (long long)a->dim);
+    if (groups(a->ngroups) > 1 && (a->dim / groups(a->ngroups)) % 64)
+        return fail(SSM_ENOTSUP, "selective_scan: with several groups, dim / ngroups must be a "
+                    "multiple of 64");
     if (a->batch > 65535 || a->dim > (1 << 30))
         return fail(SSM_ENOTSUP, "selective_scan: batch <= 65535 and dim <= 2^30 supported");
     const size_t es = esize(a->dtype);
     if (a->seqlen * a->dim * (int64_t)es >= kMaxRowBytes)
         return fail(SSM_ENOTSUP, "selective_scan: seqlen*dim*elem_size must be < 2^31 bytes");
+    if (a->seqlen * groups(a->ngroups) * a->dstate * (int64_t)es >= kMaxRowBytes)
+        return fail(SSM_ENOTSUP, "selective_scan: seqlen*ngroups*dstate*elem_size must be < 2^31 bytes");
     return SSM_OK;
 }
 
@@ -83,6 +93,9 @@ ssm_status check_ssd_sizes(const ssm_ssd_args *a) {
     if (a->chunk != 64 && a->chunk != 128 && a->chunk != 256)
         return fail(SSM_ENOTSUP, "ssd_chunked: chunk %lld not supported (64, 128, 256)",
                     (long long)a->chunk);
+    if (a->ngroups < 0 || a->nheads % groups(a->ngroups))
+        return fail(SSM_EINVAL, "ssd_chunked: ngroups %lld must be >= 0 and divide nheads %lld",
+                    (long long)a->ngroups, (long long)a->nheads);
     if (a->batch > 65535 || a->nheads > 65535)
         return fail(SSM_ENOTSUP, "ssd_chunked: batch and nheads must be <= 65535");
     if (a->seqlen * a->nheads * a->headdim * 2 >= kMaxRowBytes)
@@ -90,7 +103,7 @@ ssm_status check_ssd_sizes(const ssm_ssd_args *a) {
     if ((a->seqlen + a->chunk - 1) / a->chunk > 65535)
         return fail(SSM_ENOTSUP, "ssd_chunked: at most 65535 chunks");
     // workgroups of the output kernel: one per (batch, chunk, 4 heads, 64 rows)
-    if (a->batch * ((a->seqlen + a->chunk - 1) / a->chunk) * ((a->nheads + 3) / 4 + 8) * (a->chunk / 64) >=
+    if (a->batch * ((a->seqlen + a->chunk - 1) / a->chunk) * (a->nheads + 8) * (a->chunk / 64) >=
         ((int64_t)1 << 31))
         return fail(SSM_ENOTSUP, "ssd_chunked: batch * chunks * heads too large for one launch");
     return SSM_OK;
@@ -125,6 +138,8 @@ ssm_status check_step(const ssm_scan_step_args *a) {
     if (!step_dstate_ok(a->dstate))
         return fail(SSM_ENOTSUP, "selective_state_update: dstate %lld not supported (16..256, power of 2)",
                     (long long)a->dstate);
+    if (a->ngroups < 0 || a->dim % groups(a->ngroups))
+        return fail(SSM_EINVAL, "selective_state_update: ngroups must be >= 0 and divide dim");
     if (a->dim > (1 << 30) || a->batch * a->dim > ((int64_t)1 << 34))
         return fail(SSM_ENOTSUP, "selective_state_update: dim <= 2^30 and batch*dim <= 2^34 supported");
     if (a->batch == 0) return SSM_OK;
@@ -150,6 +165,8 @@ ssm_status check_ssd_step(const ssm_ssd_step_args *a) {
     if (!step_dstate_ok(a->dstate))
         return fail(SSM_ENOTSUP, "ssd_state_update: dstate %lld not supported (16..256, power of 2)",
                     (long long)a->dstate);
+    if (a->ngroups < 0 || a->nheads % groups(a->ngroups))
+        return fail(SSM_EINVAL, "ssd_state_update: ngroups must be >= 0 and divide nheads");
     if (a->nheads > (1 << 20) || a->headdim > (1 << 20) || a->nheads * a->headdim > (1 << 30) ||
         a->batch * a->nheads * a->headdim > ((int64_t)1 << 34))
         return fail(SSM_ENOTSUP, "ssd_state_update: nheads*headdim <= 2^30 and batch*nheads*headdim <= 2^34");

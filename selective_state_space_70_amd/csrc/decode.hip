@@ -29,6 +29,8 @@ struct StepK {
     int32_t D;          // channels per batch row (dim, or H * P)
     int32_t P;          // channels per head (1 for the per-channel form)
     int32_t softplus;
+    int32_t G;          // groups of B, C
+    int32_t ppg;        // parameter rows (channels or heads) per group
 };
 
 typedef __attribute__((ext_vector_type(4))) float f32x4;
@@ -45,7 +47,8 @@ __global__ __launch_bounds__(256) void state_update_kernel(const StepK k) {
     const int h = HEADS ? d / k.P : d;     // parameter index: head or channel
     const int64_t dt_idx = HEADS ? b * (k.D / k.P) + h : c;
     const T *x = (const T *)k.x, *dtp = (const T *)k.dt, *z = (const T *)k.z;
-    const T *Bm = (const T *)k.Bm + b * N + 4 * q, *Cm = (const T *)k.Cm + b * N + 4 * q;
+    const int64_t row = (b * k.G + h / k.ppg) * N + 4 * q;     // (b, group, 4q..)
+    const T *Bm = (const T *)k.Bm + row, *Cm = (const T *)k.Cm + row;
 
     float v = to_f32(dtp[dt_idx]) + (k.dt_bias ? k.dt_bias[h] : 0.0f);
     const float dt = k.softplus ? softplus_f32(v) : v;
@@ -105,6 +108,8 @@ ssm_status step_launch(const ssm_scan_step_args &a, hipStream_t s, char *err, si
     k.state = a.state; k.y = a.y;
     k.channels = a.batch * a.dim; k.D = (int32_t)a.dim; k.P = 1;
     k.softplus = a.delta_softplus ? 1 : 0;
+    k.G = a.ngroups > 1 ? (int32_t)a.ngroups : 1;
+    k.ppg = (int32_t)(a.dim / k.G);
     if (a.dtype == SSM_BF16) launch_step<uint16_t, false>(k, (int)a.dstate, s);
     else launch_step<float, false>(k, (int)a.dstate, s);
     return finish("selective_state_update", err, errlen);
@@ -120,6 +125,8 @@ ssm_status ssd_step_launch(const ssm_ssd_step_args &a, hipStream_t s, char *err,
     k.channels = a.batch * a.nheads * a.headdim;
     k.D = (int32_t)(a.nheads * a.headdim); k.P = (int32_t)a.headdim;
     k.softplus = a.dt_softplus ? 1 : 0;
+    k.G = a.ngroups > 1 ? (int32_t)a.ngroups : 1;
+    k.ppg = (int32_t)(a.nheads / k.G);
     if (a.dtype == SSM_BF16) launch_step<uint16_t, true>(k, (int)a.dstate, s);
     else launch_step<float, true>(k, (int)a.dstate, s);
     return finish("ssd_state_update", err, errlen);

@@ -52,6 +52,8 @@ struct ScanK {
     int32_t chunks;     // G
     int32_t dblocks;    // ceil(D / 64)
     int32_t softplus;
+    int32_t G;          // groups of B, C
+    int32_t dpg;        // channels per group (a multiple of 64 when G > 1)
 };
 
 template <int N>
@@ -159,13 +161,16 @@ __device__ __forceinline__ void run_readout(const ScanK &p, int b, int dc, bool 
     const rsrc_t yr = make_rsrc((T *)p.y + base, bytes);
     const uint32_t lo = (uint32_t)dc * sizeof(T);         // lane byte offset
     const uint32_t rowb = (uint32_t)p.D * sizeof(T);      // bytes per time step
-    const T *Brow = (const T *)p.Bm + (int64_t)b * p.L * N;
-    const T *Crow = (const T *)p.Cm + (int64_t)b * p.L * N;
+    // the wave's group of B, C rows (every channel of a wave is in one group)
+    const int g = __builtin_amdgcn_readfirstlane(dc) / p.dpg;
+    const int GN = p.G * N;                               // elements per time step (< 2^31 / L)
+    const T *Brow = (const T *)p.Bm + ((int64_t)b * p.L * p.G + g) * N;
+    const T *Crow = (const T *)p.Cm + ((int64_t)b * p.L * p.G + g) * N;
     const bool softplus = p.softplus != 0;
 
     uint32_t bw[NW], cw[NW];
-    load_row<T, N>(as_const(Brow + (int64_t)t0 * N), bw);
-    load_row<T, N>(as_const(Crow + (int64_t)t0 * N), cw);
+    load_row<T, N>(as_const(Brow + t0 * GN), bw);
+    load_row<T, N>(as_const(Crow + t0 * GN), cw);
 
     int t = t0;
     if (t1 - t0 >= U) {
@@ -190,7 +195,7 @@ __device__ __forceinline__ void run_readout(const ScanK &p, int b, int dc, bool 
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 uint32_t bn[NW], cn[NW];
-                const int64_t rn = (int64_t)min(t + u + 1, t1 - 1) * N;
+                const int rn = min(t + u + 1, t1 - 1) * GN;
                 load_row<T, N>(as_const(Brow + rn), bn);
                 load_row<T, N>(as_const(Crow + rn), cn);
                 step_readout<T, N, FAST, HAS_Z>(c, softplus, xa[u], da[u], HAS_Z ? za[u] : xa[u],
@@ -208,7 +213,7 @@ __device__ __forceinline__ void run_readout(const ScanK &p, int b, int dc, bool 
     }
     for (; t < t1; ++t) {  // tail: fewer than U steps
         uint32_t bn[NW], cn[NW];
-        const int64_t rn = (int64_t)min(t + 1, t1 - 1) * N;
+        const int rn = min(t + 1, t1 - 1) * GN;
         load_row<T, N>(as_const(Brow + rn), bn);
         load_row<T, N>(as_const(Crow + rn), cn);
         const uint32_t so = (uint32_t)t * rowb;
@@ -238,7 +243,9 @@ __device__ __forceinline__ double run_aggregate(const ScanK &p, int b, int dc, i
     const rsrc_t dr = make_rsrc((const T *)p.delta + base, bytes);
     const uint32_t lo = (uint32_t)dc * sizeof(T);
     const uint32_t rowb = (uint32_t)p.D * sizeof(T);
-    const T *Brow = (const T *)p.Bm + (int64_t)b * p.L * N;
+    const int g = __builtin_amdgcn_readfirstlane(dc) / p.dpg;
+    const int GN = p.G * N;
+    const T *Brow = (const T *)p.Bm + ((int64_t)b * p.L * p.G + g) * N;
     const bool softplus = p.softplus != 0;
     double dsum = 0.0;
     float R = 1.0f;
@@ -269,7 +276,7 @@ __device__ __forceinline__ double run_aggregate(const ScanK &p, int b, int dc, i
         // backwards in time
         int t = t1 - 1;
         uint32_t bw[NW];
-        load_row<T, N>(as_const(Brow + (int64_t)t * N), bw);
+        load_row<T, N>(as_const(Brow + t * GN), bw);
         if (t - t0 + 1 >= U) {
             T xa[U], da[U];
 #pragma unroll
@@ -289,7 +296,7 @@ __device__ __forceinline__ double run_aggregate(const ScanK &p, int b, int dc, i
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     uint32_t bn[NW];
-                    load_row<T, N>(as_const(Brow + (int64_t)max(t - u - 1, t0) * N), bn);
+                    load_row<T, N>(as_const(Brow + max(t - u - 1, t0) * GN), bn);
                     one(xa[u], da[u], bw);
 #pragma unroll
                     for (int j = 0; j < NW; ++j) bw[j] = bn[j];
@@ -300,7 +307,7 @@ __device__ __forceinline__ double run_aggregate(const ScanK &p, int b, int dc, i
         }
         for (; t >= t0; --t) {
             uint32_t bn[NW];
-            load_row<T, N>(as_const(Brow + (int64_t)max(t - 1, t0) * N), bn);
+            load_row<T, N>(as_const(Brow + max(t - 1, t0) * GN), bn);
             T xv, dv;
             buf_load(xr, lo, (uint32_t)t * rowb, xv);
             buf_load(dr, lo, (uint32_t)t * rowb, dv);
@@ -311,7 +318,7 @@ __device__ __forceinline__ double run_aggregate(const ScanK &p, int b, int dc, i
     } else {
         for (int t = t0; t < t1; ++t) {
             uint32_t bw[NW];
-            load_row<T, N>(as_const(Brow + (int64_t)t * N), bw);
+            load_row<T, N>(as_const(Brow + t * GN), bw);
             T xv, dv;
             buf_load(xr, lo, (uint32_t)t * rowb, xv);
             buf_load(dr, lo, (uint32_t)t * rowb, dv);
@@ -509,6 +516,8 @@ ssm_status scan_launch(const ssm_scan_args &a, const ScanPlan &plan, hipStream_t
         k.batch = (int32_t)a.batch; k.chunks = (int32_t)plan.chunks;
         k.dblocks = (int32_t)((a.dim + 63) / 64);
         k.softplus = a.delta_softplus ? 1 : 0;
+        k.G = a.ngroups > 1 ? (int32_t)a.ngroups : 1;
+        k.dpg = (int32_t)(a.dim / k.G);
         const bool bf = a.dtype == SSM_BF16;
         switch (a.dstate) {
             case 16: bf ? launch_typed<uint16_t, 16>(k, s, passes) : launch_typed<float, 16>(k, s, passes); break;

@@ -95,6 +95,8 @@ struct SSDK {
     int32_t H;
     int32_t nc;
     int32_t softplus;
+    int32_t G;          // groups of B, C
+    int32_t hpg;        // heads per group
 };
 
 // dt and the inclusive in-chunk cumulative log-decay A*dt for the steps of chunk
@@ -148,9 +150,11 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_state_kernel(const SSDK p)
     const int c = blockIdx.x, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int r16 = lane & 15, kb = lane >> 4;
-    const int h = blockIdx.y * 4 + wv;
-    const bool head_ok = h < p.H;
-    const int hc = head_ok ? h : p.H - 1;
+    const int hb = (p.hpg + 3) / 4;                   // workgroups per group of heads
+    const int g = blockIdx.y / hb, hl = (blockIdx.y % hb) * 4 + wv;
+    const bool head_ok = hl < p.hpg;
+    const int h = g * p.hpg + (head_ok ? hl : p.hpg - 1);   // clamped into the group
+    const int hc = h;
     const int64_t t_base = (int64_t)c * Q;
 
     {   // per-head weights w_s = exp(cs_end - cs_s) dt_s and the chunk decay
@@ -178,7 +182,7 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_state_kernel(const SSDK p)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int64_t tg = t_base + s0 + rs + i;
-                    r[i] = tg < p.L ? *(const u32x4 *)(p.Bm + ((int64_t)b * p.L + tg) * N + pass * NP + cn)
+                    r[i] = tg < p.L ? *(const u32x4 *)(p.Bm + (((int64_t)b * p.L + tg) * p.G + g) * N + pass * NP + cn)
                                     : u32x4{0u, 0u, 0u, 0u};
                 }
                 store_transposed(r, &BT[0][0], LDT, cn, rs);
@@ -339,17 +343,21 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_out_kernel(const SSDK p
         grp = (rest / TBS) * 8 + id % 8;
     }
     if (grp >= ngroups) return;
-    const int hg = grp % nhg, c = (grp / nhg) % p.nc, b = grp / (nhg * p.nc);
+    // nhg: workgroups per group of B, C heads
+    const int hl = grp % nhg, gg = (grp / nhg) % p.G, c = (grp / (nhg * p.G)) % p.nc;
+    const int b = grp / (nhg * p.G * p.nc);
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int r16 = lane & 15, kb = lane >> 4;
     const int64_t t_base = (int64_t)c * Q;
     const int T = (int)std::min<int64_t>(Q, p.L - t_base);
     if (tb * 64 >= T) return;                         // whole block past the sequence (uniform)
     const int t0 = tb * 64 + wv * 16;                 // this wave's first row
-    const int h0 = hg * HG;
+    const int h0 = gg * p.hpg + hl * HG;               // first head of this workgroup
+    const int hend = (gg + 1) * p.hpg;                 // heads of the group end here
+    const int GN = p.G * N;                            // B, C elements per time step
 
-    const uint16_t *Brow = p.Bm + ((int64_t)b * p.L + t_base) * N;
-    const uint16_t *Crow = p.Cm + ((int64_t)b * p.L + t_base) * N;
+    const uint16_t *Brow = p.Bm + (((int64_t)b * p.L + t_base) * p.G + gg) * N;
+    const uint16_t *Crow = p.Cm + (((int64_t)b * p.L + t_base) * p.G + gg) * N;
     const int64_t xstride = (int64_t)p.H * kP;
     const uint16_t *Xrow = p.x + ((int64_t)b * p.L + t_base) * xstride;
 
@@ -361,7 +369,7 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_out_kernel(const SSDK p
 #pragma unroll
     for (int i = 0; i < BV; ++i) {
         const int v = tid + i * kThreads;
-        boff[i] = (uint32_t)(v / (N / 8) * N + (v % (N / 8)) * 8) * 2u;
+        boff[i] = (uint32_t)(v / (N / 8) * GN + (v % (N / 8)) * 8) * 2u;
     }
 #pragma unroll
     for (int i = 0; i < XB; ++i) {
@@ -369,12 +377,12 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_out_kernel(const SSDK p
         const int j = blk >> 7, g = blk & 15, po = (blk & 127) >> 4;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            xoff[i][e] = h0 + j < p.H ? (uint32_t)(((4 * g + e) * xstride + (h0 + j) * kP + po * 8) * 2) : 0x80000000u;
+            xoff[i][e] = h0 + j < hend ? (uint32_t)(((4 * g + e) * xstride + (h0 + j) * kP + po * 8) * 2) : 0x80000000u;
     }
     auto fetch = [&](int sb) {
         const int s0 = sb * 64;
         const int rows = std::max(0, T - s0);
-        const rsrc_t rb = make_rsrc(Brow + (int64_t)s0 * N, (uint32_t)(rows * N * 2));
+        const rsrc_t rb = make_rsrc(Brow + (int64_t)s0 * GN, (uint32_t)(rows * GN * 2));
         const rsrc_t rx = make_rsrc(Xrow + (int64_t)s0 * xstride, (uint32_t)(rows * xstride * 2));
 #pragma unroll
         for (int i = 0; i < BV; ++i) breg[i] = load16(rb, boff[i]);
@@ -401,7 +409,7 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_out_kernel(const SSDK p
     const uint16_t *sin_c = p.sin + ((int64_t)b * p.nc + c) * p.H * (int64_t)kP * N;
     u32x4 sreg[SV];
     auto sin_fetch = [&](int j0) {
-        const int nh = std::max(0, std::min(SIN_HEADS, p.H - (h0 + j0)));
+        const int nh = std::max(0, std::min(SIN_HEADS, hend - (h0 + j0)));
         const rsrc_t rs = make_rsrc(sin_c + (int64_t)(h0 + j0) * kP * N, (uint32_t)(nh * kP * N * 2));
 #pragma unroll
         for (int i = 0; i < SV; ++i) sreg[i] = load16(rs, (uint32_t)(tid + i * kThreads) * 16u);
@@ -420,7 +428,7 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_out_kernel(const SSDK p
     // per-head steps and cumulative log-decays (one wave per head)
     if (wv < HG) {
         float dtv[SPL], cs[SPL];
-        head_dt_cs<Q>(p, b, std::min(h0 + wv, p.H - 1), c, dtv, cs);
+        head_dt_cs<Q>(p, b, std::min(h0 + wv, hend - 1), c, dtv, cs);
 #pragma unroll
         for (int i = 0; i < SPL; ++i) {
             cs2[wv][lane * SPL + i] = cs[i] * kLog2e;
@@ -431,7 +439,7 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_out_kernel(const SSDK p
     bf16x8 cfr[KN];
 #pragma unroll
     for (int k = 0; k < KN; ++k)
-        cfr[k] = as_bf16x8(*(const u32x4 *)(Crow + (int64_t)trow * N + 32 * k + 8 * kb));
+        cfr[k] = as_bf16x8(*(const u32x4 *)(Crow + (int64_t)trow * GN + 32 * k + 8 * kb));
     sin_stash();
     if (HG > SIN_HEADS) sin_fetch(SIN_HEADS);
     __syncthreads();
@@ -563,13 +571,13 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_out_kernel(const SSDK p
         for (int j = 0; j < HG; ++j)
 #pragma unroll
             for (int rr = 0; rr < 2; ++rr) {
-                const int t = std::min(t0 + rr * 8 + (lane >> 3), T - 1), h = std::min(h0 + j, p.H - 1);
+                const int t = std::min(t0 + rr * 8 + (lane >> 3), T - 1), h = std::min(h0 + j, hend - 1);
                 zreg[j][rr] = *(const u32x4 *)(p.z + (((int64_t)b * p.L + t_base + t) * p.H + h) * kP + (lane & 7) * 8);
             }
     }
 #pragma unroll
     for (int j = 0; j < HG; ++j) {
-        const float dsk = (p.Dskip && h0 + j < p.H) ? p.Dskip[h0 + j] : 0.0f;
+        const float dsk = (p.Dskip && h0 + j < hend) ? p.Dskip[h0 + j] : 0.0f;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const u32x2 xv = *(const u32x2 *)&XT[j][q * 16 + r16][perm_s(16 * wv + 4 * kb)];
@@ -583,7 +591,7 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_out_kernel(const SSDK p
 #pragma unroll
     for (int j = 0; j < HG; ++j) {
         const int h = h0 + j;
-        if (h >= p.H) break;                           // uniform
+        if (h >= hend) break;                          // uniform
 #pragma unroll
         for (int q = 0; q < 4; ++q)
 #pragma unroll
@@ -621,13 +629,13 @@ __global__ __launch_bounds__(256) void ssd_copy_state_kernel(const float *h0, fl
 
 template <int N, int Q>
 void launch_nq(const SSDK &k, int batch, hipStream_t s) {
-    hipLaunchKernelGGL((ssd_chunk_state_kernel<N, Q>), dim3((unsigned)k.nc, (unsigned)((k.H + 3) / 4), (unsigned)batch),
+    hipLaunchKernelGGL((ssd_chunk_state_kernel<N, Q>), dim3((unsigned)k.nc, (unsigned)(k.G * ((k.hpg + 3) / 4)), (unsigned)batch),
                        dim3(kThreads), 0, s, k);
     const int64_t total = (int64_t)batch * k.H * kP * N / 4;
     hipLaunchKernelGGL(ssd_state_pass_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
                        k, N, total);
-    const int nhg = (k.H + OutCfg<N>::HG - 1) / OutCfg<N>::HG;
-    const int64_t ngroups = (int64_t)batch * k.nc * nhg;
+    const int nhg = (k.hpg + OutCfg<N>::HG - 1) / OutCfg<N>::HG;
+    const int64_t ngroups = (int64_t)batch * k.nc * k.G * nhg;
     const int64_t nblocks = Q == 64 ? ngroups : (ngroups + 7) / 8 * 8 * (Q / 64);
     hipLaunchKernelGGL((ssd_chunk_out_kernel<N, Q>), dim3((unsigned)nblocks), dim3(kThreads), 0, s, k, nhg,
                        (int)ngroups);
@@ -678,6 +686,8 @@ ssm_status ssd_launch(const ssm_ssd_args &a, const SSDPlan &plan, hipStream_t s,
         k.decay = (float *)((char *)a.workspace + plan.decay_offset);
         k.L = a.seqlen; k.H = (int32_t)a.nheads; k.nc = (int32_t)plan.nchunks;
         k.softplus = a.dt_softplus ? 1 : 0;
+        k.G = a.ngroups > 1 ? (int32_t)a.ngroups : 1;
+        k.hpg = (int32_t)(a.nheads / k.G);
         switch (a.dstate) {
             case 64: launch_n<64>(k, (int)a.batch, (int)a.chunk, s); break;
             case 128: launch_n<128>(k, (int)a.batch, (int)a.chunk, s); break;

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_names():
     lib = _capi.lib()
-    assert lib.ssm_abi_version() == _capi.ABI_VERSION == 2
+    assert lib.ssm_abi_version() == _capi.ABI_VERSION == 3
     names = [lib.ssm_status_str(s).decode() for s in range(4)]
     assert names == ["SSM_OK", "SSM_EINVAL", "SSM_ENOTSUP", "SSM_EHIP"]
     assert lib.ssm_status_str(99).decode() == "SSM_UNKNOWN"
@@ -95,6 +95,11 @@ def ssd_status(a):
     ({"dstate": 128}, _capi.SSM_ENOTSUP),
     ({"batch": 70000}, _capi.SSM_ENOTSUP),
     ({"seqlen": 1 << 20, "dim": 1 << 12}, _capi.SSM_ENOTSUP),   # row of 8 GiB
+    ({"ngroups": 1}, _capi.SSM_OK),
+    ({"ngroups": 2, "dim": 256}, _capi.SSM_OK),
+    ({"ngroups": 2}, _capi.SSM_ENOTSUP),                      # 48 channels per group
+    ({"ngroups": 5}, _capi.SSM_EINVAL),                       # does not divide 96
+    ({"ngroups": -1}, _capi.SSM_EINVAL),
     ({"batch": 0, "x": None, "y": None}, _capi.SSM_OK),        # empty batch: nothing to read
     ({"seqlen": 0, "x": None, "y": None, "Bm": None}, _capi.SSM_OK),
 ])
@@ -120,6 +125,9 @@ def test_scan_validation(kw, want):
     ({"dstate": 96}, _capi.SSM_ENOTSUP),
     ({"chunk": 100}, _capi.SSM_ENOTSUP),
     ({"batch": 0, "x": None}, _capi.SSM_OK),
+    ({"ngroups": 2}, _capi.SSM_OK),
+    ({"ngroups": 8}, _capi.SSM_OK),
+    ({"ngroups": 3}, _capi.SSM_EINVAL),
 ])
 def test_ssd_validation(kw, want):
     assert ssd_status(ssd_args(**kw)) == want
@@ -214,6 +222,7 @@ def conv_args(**kw):
     ({"dstate": 8}, _capi.SSM_ENOTSUP),
     ({"dstate": 48}, _capi.SSM_ENOTSUP),
     ({"dstate": 512}, _capi.SSM_ENOTSUP),
+    ({"ngroups": 7}, _capi.SSM_EINVAL),
 ])
 def test_step_validation(kw, want):
     lib = _capi.lib()
@@ -227,6 +236,7 @@ def test_step_validation(kw, want):
     ({"headdim": 0}, _capi.SSM_EINVAL),
     ({"state": FAKE + 8}, _capi.SSM_EINVAL),
     ({"dstate": 100}, _capi.SSM_ENOTSUP),
+    ({"ngroups": 3}, _capi.SSM_EINVAL),
 ])
 def test_ssd_step_validation(kw, want):
     assert _capi.lib().ssd_state_update(ctypes.byref(ssd_step_args(**kw)), None) == want

@@ -130,3 +130,24 @@ def test_ssd_step_serving_batch():
                                      inp["Bm"][:, 0], inp["Cm"][:, 0], inp["Dskip"], inp["z"][:, 0],
                                      inp["dt_bias"])
     _cmp("ssd step B32", "bf16", y, st, yo, so)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_scan_step_groups(dtype):
+    """B, C with 4 groups (25 channels each)."""
+    inp = workloads.scan_inputs(3, 1, 100, 16, dtype, seed=41, with_h0=True, ngroups=4)
+    y, st = _gpu_scan_step(inp)
+    torch.cuda.synchronize()
+    yo, so = _oracle_scan_step(inp, inp["h0"])
+    _cmp("step groups %s" % dtype, dtype, y, st, yo, so)
+
+
+def test_ssd_step_groups():
+    T = 3
+    inp = workloads.ssd_inputs(2, T, 6, 64, 128, "bf16", seed=42, with_h0=True, with_z=True, ngroups=3)
+    yo, ho = oracle.ssd(inp["x"], inp["dt"], inp["A"], inp["Bm"], inp["Cm"], inp["Dskip"], inp["z"],
+                        inp["dt_bias"], inp["h0"])
+    st = _dev(inp["h0"])
+    ys = [_gpu_ssd_step(inp, t, st).float() for t in range(T)]
+    torch.cuda.synchronize()
+    _cmp("ssd steps groups", "bf16", torch.stack(ys, dim=1), st, yo, ho)

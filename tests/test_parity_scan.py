@@ -51,6 +51,21 @@ def test_optional_inputs_absent(drop):
     _check("no %s" % drop, inp)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("D,N,G,L", [(256, 16, 2, 300), (384, 32, 3, 1000), (512, 64, 8, 77)])
+def test_groups(dtype, D, N, G, L):
+    """G groups of B, C (channel d reads group d // (D // G))."""
+    inp = workloads.scan_inputs(2, L, D, N, dtype, seed=D + G, with_h0=True, ngroups=G)
+    _check("groups D%d N%d G%d L%d %s" % (D, N, G, L, dtype), inp)
+
+
+def test_groups_forced_chunks(monkeypatch):
+    """Groups with the time split (aggregates read each group's B rows)."""
+    monkeypatch.setenv("SSM_SCAN_CHUNKS", "7")
+    inp = workloads.scan_inputs(1, 900, 256, 16, "bf16", seed=31, with_h0=True, ngroups=4)
+    _check("groups chunked", inp)
+
+
 def test_softplus_off():
     """dt = delta + bias used as is: a positive raw step and no bias (the
     inverse-softplus bias of the generator is negative)."""

@@ -43,6 +43,15 @@ def test_head_groups(batch, L, H, N, chunk):
     _check("heads B%d L%d H%d N%d Q%d" % (batch, L, H, N, chunk), inp, chunk)
 
 
+@pytest.mark.parametrize("H,N,G,chunk,L", [(8, 128, 2, 256, 600), (6, 64, 3, 64, 300),
+                                           (10, 128, 2, 128, 500), (8, 256, 8, 256, 300)])
+def test_groups(H, N, G, chunk, L):
+    """G groups of B, C shared by H / G heads each (odd heads per group leave
+    partly empty workgroups)."""
+    inp = workloads.ssd_inputs(2, L, H, 64, N, "bf16", seed=H + G * 7, with_h0=True, with_z=True, ngroups=G)
+    _check("groups H%d N%d G%d Q%d" % (H, N, G, chunk), inp, chunk)
+
+
 def test_gate_and_no_skip():
     inp = workloads.ssd_inputs(2, 333, 3, 64, 64, "bf16", seed=21, with_z=True, with_D=False)
     _check("z, no D", inp, 64)

@@ -133,11 +133,13 @@ def _bias_for(rng, count, lo, hi):
 
 def scan_inputs(batch: int, seqlen: int, dim: int, dstate: int, dtype: str = "f32",
                 seed: int = 0, dt_range=(1e-3, 1e-1), with_h0: bool = False,
-                with_z: bool = True, with_D: bool = True, with_bias: bool = True) -> dict:
+                with_z: bool = True, with_D: bool = True, with_bias: bool = True,
+                ngroups: int = 1) -> dict:
     """Inputs of one selective-scan call.
 
     Returns float32 numpy arrays (bf16-exact values when ``dtype == "bf16"``):
-    x, delta, z: (batch, L, D); Bm, Cm: (batch, L, N); A: (D, N);
+    x, delta, z: (batch, L, D); Bm, Cm: (batch, L, N), or (batch, L, G, N) with
+    ``ngroups`` G > 1; A: (D, N);
     delta_bias, Dskip: (D,); h0: (batch, D, N) or None.
     """
     r = _rngs(seed)
@@ -145,8 +147,9 @@ def scan_inputs(batch: int, seqlen: int, dim: int, dstate: int, dtype: str = "f3
     out["x"] = _normal(r["x"], (batch, seqlen, dim), 1.0, dtype)
     out["delta"] = _normal(r["delta"], (batch, seqlen, dim), 0.5, dtype)
     out["z"] = _normal(r["z"], (batch, seqlen, dim), 1.0, dtype) if with_z else None
-    out["Bm"] = _normal(r["B"], (batch, seqlen, dstate), 1.0, dtype)
-    out["Cm"] = _normal(r["C"], (batch, seqlen, dstate), 1.0, dtype)
+    bc = (batch, seqlen, dstate) if ngroups == 1 else (batch, seqlen, ngroups, dstate)
+    out["Bm"] = _normal(r["B"], bc, 1.0, dtype)
+    out["Cm"] = _normal(r["C"], bc, 1.0, dtype)
     out["Dskip"] = r["Dskip"].standard_normal(size=dim, dtype=np.float32) if with_D else None
     out["delta_bias"] = _bias_for(r["dt0"], dim, *dt_range) if with_bias else None
     out["A"] = np.ascontiguousarray(
@@ -159,19 +162,20 @@ def scan_inputs(batch: int, seqlen: int, dim: int, dstate: int, dtype: str = "f3
 def ssd_inputs(batch: int, seqlen: int, nheads: int, headdim: int, dstate: int,
                dtype: str = "bf16", seed: int = 0, dt_range=(1e-3, 1e-1),
                a_range=(1.0, 16.0), with_h0: bool = False, with_z: bool = False,
-               with_D: bool = True, with_bias: bool = True) -> dict:
+               with_D: bool = True, with_bias: bool = True, ngroups: int = 1) -> dict:
     """Inputs of one SSD (scalar A per head) call.
 
     x: (batch, L, H, P); dt: (batch, L, H) raw; dt_bias, A, Dskip: (H,);
-    Bm, Cm: (batch, L, N); z: (batch, L, H, P) or None; h0: (batch, H, P, N) or None.
+    Bm, Cm: (batch, L, N), or (batch, L, G, N) with ``ngroups`` G > 1; z: (batch, L, H, P) or None; h0: (batch, H, P, N) or None.
     """
     r = _rngs(seed)
     out = {"dtype": dtype, "kind": "ssd"}
     out["x"] = _normal(r["x"], (batch, seqlen, nheads, headdim), 1.0, dtype)
     out["dt"] = _normal(r["delta"], (batch, seqlen, nheads), 0.5, dtype)
     out["z"] = _normal(r["z"], (batch, seqlen, nheads, headdim), 1.0, dtype) if with_z else None
-    out["Bm"] = _normal(r["B"], (batch, seqlen, dstate), 1.0, dtype)
-    out["Cm"] = _normal(r["C"], (batch, seqlen, dstate), 1.0, dtype)
+    bc = (batch, seqlen, dstate) if ngroups == 1 else (batch, seqlen, ngroups, dstate)
+    out["Bm"] = _normal(r["B"], bc, 1.0, dtype)
+    out["Cm"] = _normal(r["C"], bc, 1.0, dtype)
     out["Dskip"] = r["Dskip"].standard_normal(size=nheads, dtype=np.float32) if with_D else None
     out["dt_bias"] = _bias_for(r["dt0"], nheads, *dt_range) if with_bias else None
     out["A"] = (-r["A"].uniform(a_range[0], a_range[1], size=nheads)).astype(np.float32)
