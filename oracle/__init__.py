@@ -57,6 +57,10 @@ def lib():
         L.oracle_ssd_f64.argtypes = [
             _i64, _i64, _i64, _i64, _i64, _i64, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p,
             _f32p, _f64p, ctypes.c_int, _i64p, _i64, _f64p, _f64p]
+        L.oracle_selective_scan_bwd_f64.restype = ctypes.c_int
+        L.oracle_selective_scan_bwd_f64.argtypes = [
+            _i64, _i64, _i64, _i64, _i64, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p,
+            _f64p, ctypes.c_int, _f32p, _f64p] + [_f64p] * 9
         L.oracle_causal_conv1d_f64.restype = ctypes.c_int
         L.oracle_causal_conv1d_f64.argtypes = [_i64, _i64, _i64, _i64, _f32p, _f32p, _f32p,
                                                _f32p, ctypes.c_int, _f64p, _f64p]
@@ -156,6 +160,46 @@ def selective_scan(x, delta, A, Bm, Cm, Dskip=None, z=None, delta_bias=None, h0=
     if rc != 0:
         raise ValueError("oracle_selective_scan_f64 rejected its arguments")
     return y, hf
+
+
+def selective_scan_bwd(x, delta, A, Bm, Cm, dy, Dskip=None, z=None, delta_bias=None, h0=None,
+                       dh_final=None, delta_softplus: bool = True) -> dict:
+    """Gradients of the selective scan in fp64 (reverse-mode through the
+    recurrence, see ``oracle_selective_scan_bwd_f64``) for the loss
+    sum(dy * y) + sum(dh_final * h_final). Shapes as :func:`selective_scan`;
+    dy (batch, L, D); dh_final (batch, D, N). Returns a dict with dx, ddelta, dz
+    (None without z), dB, dC (the shape of Bm), dA, dDskip, ddelta_bias, dh0."""
+    batch, L, D = np.shape(x)
+    N = np.shape(A)[1]
+    G = np.shape(Bm)[2] if np.ndim(Bm) == 4 else 1
+    keep = []
+    xs, xp = _f32(x, (batch, L, D)); keep.append(xs)
+    ds, dp = _f32(delta, (batch, L, D)); keep.append(ds)
+    zs, zp = _f32(z, (batch, L, D)); keep.append(zs)
+    bs, bp = _f32(np.reshape(Bm, (batch, L, G, N)), (batch, L, G, N)); keep.append(bs)
+    cs, cp = _f32(np.reshape(Cm, (batch, L, G, N)), (batch, L, G, N)); keep.append(cs)
+    as_, ap = _f32(A, (D, N)); keep.append(as_)
+    bis, bip = _f32(delta_bias, (D,)); keep.append(bis)
+    dks, dkp = _f32(Dskip, (D,)); keep.append(dks)
+    hs, hp = _f64(h0, (batch, D, N)); keep.append(hs)
+    dys, dyp = _f32(dy, (batch, L, D)); keep.append(dys)
+    dhs, dhp = _f64(dh_final, (batch, D, N)); keep.append(dhs)
+    out = {"dx": np.empty((batch, L, D)), "ddelta": np.empty((batch, L, D)),
+           "dz": np.empty((batch, L, D)) if z is not None else None,
+           "dB": np.empty((batch, L, G, N)), "dC": np.empty((batch, L, G, N)),
+           "dA": np.empty((D, N)), "dDskip": np.empty(D), "ddelta_bias": np.empty(D),
+           "dh0": np.empty((batch, D, N))}
+    ptr = lambda a: None if a is None else a.ctypes.data_as(_f64p)
+    rc = lib().oracle_selective_scan_bwd_f64(
+        batch, L, D, N, G, xp, dp, zp, bp, cp, ap, bip, dkp, hp, int(bool(delta_softplus)), dyp, dhp,
+        ptr(out["dx"]), ptr(out["ddelta"]), ptr(out["dz"]), ptr(out["dB"]), ptr(out["dC"]),
+        ptr(out["dA"]), ptr(out["dDskip"]), ptr(out["ddelta_bias"]), ptr(out["dh0"]))
+    if rc != 0:
+        raise ValueError("oracle_selective_scan_bwd_f64 rejected its arguments")
+    if np.ndim(Bm) == 3:
+        out["dB"] = out["dB"].reshape(batch, L, N)
+        out["dC"] = out["dC"].reshape(batch, L, N)
+    return out
 
 
 def ssd(x, dt, A, Bm, Cm, Dskip=None, z=None, dt_bias=None, h0=None,

@@ -41,6 +41,7 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 #ifdef _OPENMP
 #include <omp.h>
 #endif
@@ -55,6 +56,15 @@ static double softplus_f64(double v)
 static double silu_gate_f64(double z)
 {
     return z / (1.0 + exp(-z));
+}
+
+static int oracle_num_threads_in_team(void)
+{
+#ifdef _OPENMP
+    return omp_get_num_threads();
+#else
+    return 1;
+#endif
 }
 
 int oracle_num_threads(void)
@@ -253,6 +263,117 @@ int oracle_causal_conv1d_f64(int64_t batch, int64_t L, int64_t D, int64_t K,
             for (int64_t j = 0; j < K - 1; ++j)
                 final_state[(b * (K - 1) + j) * D + d] = conv_input(x, x0, b, L - (K - 1) + j, L, D, K, d);
         }
+    }
+    return 0;
+}
+
+/*
+ * Gradients of the selective scan (the training pass: the pages note that
+ * training runs the same scan, [Mamba-2 page, Core idea: Mamba-1's scan and
+ * training throughput]). Reverse-mode differentiation of the recurrence above,
+ * per channel, in fp64, with the loss L = sum dy * y + sum dh_final * h_final:
+ *   dyc_t  = dy_t * silu(z_t)                      (dyc_t = dy_t without a gate)
+ *   g_t    = C_t[n] dyc_t + abar_{t+1}[n] g_{t+1}[n]   (adjoint of h_t; the last step
+ *            adds dh_final instead of the term from t+1)
+ *   dC_t[n] += dyc_t h_t[n],  dB_t[n] += g_t[n] dt_t x_t      (summed over the
+ *            channels of the group)
+ *   dx_t   = dyc_t Dskip + dt_t sum_n g_t[n] B_t[n]
+ *   ddt_t  = sum_n g_t[n] (B_t[n] x_t + A[n] abar_t[n] h_{t-1}[n])
+ *   ddelta_t = ddt_t * sigmoid(v_t) (softplus) or ddt_t;  dbias += ddelta_t
+ *   dA[n] += g_t[n] dt_t abar_t[n] h_{t-1}[n];  dDskip += dyc_t x_t
+ *   dz_t   = dy_t (C_t.h_t + Dskip x_t) silu'(z_t),  silu' = s (1 + z (1 - s))
+ *   dh0[n] = abar_0[n] g_0[n]
+ * Inputs as oracle_selective_scan_f64 (h0 and dh_final double, NULL -> 0).
+ * Outputs (double, all required except dz when z is NULL): dx, ddelta, dz
+ * (batch, L, D); dB, dC (batch, L, G, N); dA (D, N); dDskip, dbias (D);
+ * dh0 (batch, D, N). Returns 0, or -1 on a bad size.
+ */
+int oracle_selective_scan_bwd_f64(int64_t batch, int64_t L, int64_t D, int64_t N, int64_t G,
+                                  const float *x, const float *delta, const float *z,
+                                  const float *Bm, const float *Cm, const float *A,
+                                  const float *delta_bias, const float *Dskip,
+                                  const double *h0, int delta_softplus,
+                                  const float *dy, const double *dh_final,
+                                  double *dx, double *ddelta, double *dz, double *dB, double *dC,
+                                  double *dA, double *dDskip, double *dbias, double *dh0)
+{
+    if (batch < 0 || L < 0 || D <= 0 || N <= 0 || N > 4096 || G <= 0 || D % G) return -1;
+    const int64_t nbc = batch * L * G * N;
+    for (int64_t i = 0; i < nbc; ++i) { dB[i] = 0.0; dC[i] = 0.0; }
+    for (int64_t i = 0; i < D * N; ++i) dA[i] = 0.0;
+    for (int64_t i = 0; i < D; ++i) { dDskip[i] = 0.0; dbias[i] = 0.0; }
+
+#pragma omp parallel
+    {
+        /* per-thread sums over channels, added in thread order at the end */
+        double *pB = (double *)calloc((size_t)nbc, sizeof(double));
+        double *pC = (double *)calloc((size_t)nbc, sizeof(double));
+        double *hs = (double *)malloc((size_t)(L + 1) * (size_t)N * sizeof(double));
+        double *dts = (double *)malloc((size_t)(L > 0 ? L : 1) * sizeof(double));
+        double g[4096];
+
+#pragma omp for schedule(static)
+        for (int64_t d = 0; d < D; ++d) {
+            const int64_t grp = d / (D / G);
+            const double bias = delta_bias ? (double)delta_bias[d] : 0.0;
+            const double dsk = Dskip ? (double)Dskip[d] : 0.0;
+            for (int64_t b = 0; b < batch; ++b) {
+                /* forward: hs[t+1] = h_t, hs[0] = h_{-1} = h0 */
+                for (int64_t n = 0; n < N; ++n) hs[n] = h0 ? h0[(b * D + d) * N + n] : 0.0;
+                for (int64_t t = 0; t < L; ++t) {
+                    const int64_t e = (b * L + t) * D + d;
+                    const int64_t r = ((b * L + t) * G + grp) * N;
+                    const double v = (double)delta[e] + bias;
+                    const double dt = delta_softplus ? softplus_f64(v) : v;
+                    dts[t] = dt;
+                    for (int64_t n = 0; n < N; ++n) {
+                        const double abar = exp(dt * (double)A[d * N + n]);
+                        hs[(t + 1) * N + n] = abar * hs[t * N + n] + dt * (double)Bm[r + n] * (double)x[e];
+                    }
+                }
+                /* reverse */
+                for (int64_t n = 0; n < N; ++n) g[n] = dh_final ? dh_final[(b * D + d) * N + n] : 0.0;
+                for (int64_t t = L - 1; t >= 0; --t) {
+                    const int64_t e = (b * L + t) * D + d;
+                    const int64_t r = ((b * L + t) * G + grp) * N;
+                    const double xv = (double)x[e], dt = dts[t];
+                    const double v = (double)delta[e] + bias;
+                    double yc = dsk * xv;
+                    for (int64_t n = 0; n < N; ++n) yc += (double)Cm[r + n] * hs[(t + 1) * N + n];
+                    double gate = 1.0, dyc = (double)dy[e];
+                    if (z) {
+                        const double zv = (double)z[e], s = 1.0 / (1.0 + exp(-zv));
+                        gate = zv * s;
+                        dz[e] = (double)dy[e] * yc * s * (1.0 + zv * (1.0 - s));
+                        dyc = (double)dy[e] * gate;
+                    }
+                    double gB = 0.0, ddt = 0.0;
+                    for (int64_t n = 0; n < N; ++n) {
+                        const double abar = exp(dt * (double)A[d * N + n]);
+                        const double gn = (double)Cm[r + n] * dyc + g[n];   /* g_t; g[n] held the term from t+1 */
+                        const double hprev = hs[t * N + n];
+                        pC[r + n] += dyc * hs[(t + 1) * N + n];
+                        pB[r + n] += gn * dt * xv;
+                        gB += gn * (double)Bm[r + n];
+                        ddt += gn * ((double)Bm[r + n] * xv + (double)A[d * N + n] * abar * hprev);
+                        dA[d * N + n] += gn * dt * abar * hprev;   /* channel d is this thread's */
+                        g[n] = abar * gn;                                  /* term for t-1 */
+                    }
+                    dx[e] = dyc * dsk + dt * gB;
+                    const double dd = delta_softplus ? ddt / (1.0 + exp(-v)) : ddt;
+                    ddelta[e] = dd;
+                    dbias[d] += dd;
+                    dDskip[d] += dyc * xv;
+                }
+                for (int64_t n = 0; n < N; ++n) dh0[(b * D + d) * N + n] = g[n];
+            }
+        }
+#pragma omp for ordered schedule(static, 1)
+        for (int th = 0; th < oracle_num_threads_in_team(); ++th) {
+#pragma omp ordered
+            for (int64_t i = 0; i < nbc; ++i) { dB[i] += pB[i]; dC[i] += pC[i]; }
+        }
+        free(pB); free(pC); free(hs); free(dts);
     }
     return 0;
 }

@@ -510,6 +510,93 @@ def pin_ssd_groups_split(seed=21):
         assert np.array_equal(y[:, :, sl], yg) and np.array_equal(hf[:, sl], hg), "SSD group %d" % g
 
 
+# ----------------------------------------------------------------------------- gradients
+
+def _bwd_case(rng, batch, L, D, N, G):
+    x = _f32(rng.standard_normal((batch, L, D)))
+    z = _f32(rng.standard_normal((batch, L, D)))
+    delta = _f32(rng.normal(0.0, 0.5, size=(batch, L, D)))
+    bias = _f32(rng.uniform(-3.0, -1.0, size=D))
+    A = _f32(-rng.uniform(0.3, 3.0, size=(D, N)))
+    Bm = _f32(rng.standard_normal((batch, L, G, N)))
+    Cm = _f32(rng.standard_normal((batch, L, G, N)))
+    Dsk = _f32(rng.standard_normal(D))
+    h0 = rng.standard_normal((batch, D, N))
+    dy = _f32(rng.standard_normal((batch, L, D)))
+    dhf = rng.standard_normal((batch, D, N))
+    return dict(x=x, delta=delta, A=A, Bm=Bm, Cm=Cm, Dskip=Dsk, z=z, delta_bias=bias, h0=h0,
+                dy=dy, dh_final=dhf)
+
+
+def _loss(c, softplus=True):
+    y, hf = oracle.selective_scan(c["x"], c["delta"], c["A"], c["Bm"], c["Cm"], c["Dskip"], c["z"],
+                                  c["delta_bias"], c["h0"], delta_softplus=softplus)
+    return float(np.sum(y * c["dy"].astype(np.float64)) + np.sum(hf * c["dh_final"]))
+
+
+def pin_bwd_finite_differences(seed=22):
+    """Every gradient of the backward oracle equals the central difference of the
+    forward oracle's loss sum(dy*y) + sum(dh_final*h_final). Steps of 2^-10 are
+    exact in the fp32 inputs; the truncation error is O(h^2)."""
+    rng = np.random.default_rng(seed)
+    for softplus, G in ((True, 2), (False, 1)):
+        c = _bwd_case(rng, 2, 5, 4, 3, G)
+        if not softplus:
+            c["delta"] = np.abs(c["delta"]) + _f32(0.05)
+            c["delta_bias"] = _f32(np.zeros(4))
+        gr = oracle.selective_scan_bwd(c["x"], c["delta"], c["A"], c["Bm"], c["Cm"], c["dy"], c["Dskip"],
+                                       c["z"], c["delta_bias"], c["h0"], c["dh_final"], softplus)
+        names = {"x": "dx", "delta": "ddelta", "z": "dz", "Bm": "dB", "Cm": "dC", "A": "dA",
+                 "Dskip": "dDskip", "delta_bias": "ddelta_bias", "h0": "dh0"}
+        for key, gname in names.items():
+            base = c[key]
+            step = 2.0 ** -10 if base.dtype == np.float32 else 1e-6
+            fd = np.empty(base.shape)
+            for idx in np.ndindex(base.shape):
+                orig = base[idx]
+                base[idx] = orig + step
+                lp = _loss(c, softplus)
+                base[idx] = orig - step
+                lm = _loss(c, softplus)
+                base[idx] = orig
+                fd[idx] = (lp - lm) / (2.0 * step)
+            got = np.reshape(gr[gname], fd.shape)
+            err = np.max(np.abs(got - fd)) / max(1e-12, np.max(np.abs(fd)))
+            assert err < 1e-4, "gradient %s differs from finite differences: %.3g" % (gname, err)
+
+
+def pin_bwd_autograd(seed=23):
+    """The backward oracle equals fp64 reverse-mode autodiff (torch, CPU) of a
+    separately written, vectorised forward recurrence."""
+    import torch
+    rng = np.random.default_rng(seed)
+    batch, L, D, N, G = 2, 9, 6, 4, 3
+    c = _bwd_case(rng, batch, L, D, N, G)
+    T = {k: torch.tensor(np.asarray(v, dtype=np.float64), requires_grad=True)
+         for k, v in c.items() if k not in ("dy", "dh_final")}
+    grp = torch.arange(D) // (D // G)
+    v = T["delta"] + T["delta_bias"]
+    dt = torch.nn.functional.softplus(v)
+    h = T["h0"]
+    ys = []
+    for t in range(L):
+        Bt = T["Bm"][:, t][:, grp]                     # (batch, D, N)
+        Ct = T["Cm"][:, t][:, grp]
+        h = torch.exp(dt[:, t, :, None] * T["A"]) * h + dt[:, t, :, None] * Bt * T["x"][:, t, :, None]
+        yc = (Ct * h).sum(-1) + T["Dskip"] * T["x"][:, t]
+        ys.append(yc * torch.sigmoid(T["z"][:, t]) * T["z"][:, t])
+    y = torch.stack(ys, dim=1)
+    loss = (y * torch.tensor(c["dy"], dtype=torch.float64)).sum() + (h * torch.tensor(c["dh_final"])).sum()
+    loss.backward()
+    gr = oracle.selective_scan_bwd(c["x"], c["delta"], c["A"], c["Bm"], c["Cm"], c["dy"], c["Dskip"],
+                                   c["z"], c["delta_bias"], c["h0"], c["dh_final"])
+    pairs = {"dx": "x", "ddelta": "delta", "dz": "z", "dB": "Bm", "dC": "Cm", "dA": "A",
+             "dDskip": "Dskip", "ddelta_bias": "delta_bias", "dh0": "h0"}
+    for gname, key in pairs.items():
+        want = T[key].grad.numpy()
+        assert _rel(np.reshape(gr[gname], want.shape), want) < 1e-11, "autograd differs on %s" % gname
+
+
 SCAN_PINS = [pin_lti_convolution, pin_lti_lfilter, pin_semiseparable, pin_small_step_keeps_state,
              pin_large_step_forgets, pin_zero_input_pure_decay, pin_split_invariance,
              pin_linearity, pin_geometric_series, pin_softplus_identities, pin_gate_identity,
@@ -517,4 +604,5 @@ SCAN_PINS = [pin_lti_convolution, pin_lti_lfilter, pin_semiseparable, pin_small_
 SSD_PINS = [pin_ssd_semiseparable, pin_ssd_is_broadcast_scan, pin_ssd_channel_subset,
             pin_ssd_decode_steps_equal_ssd, pin_ssd_groups_split]
 CONV_PINS = [pin_conv1d_numpy, pin_conv1d_history, pin_conv1d_streaming]
-ALL_PINS = SCAN_PINS + SSD_PINS + CONV_PINS
+BWD_PINS = [pin_bwd_finite_differences, pin_bwd_autograd]
+ALL_PINS = SCAN_PINS + SSD_PINS + CONV_PINS + BWD_PINS

@@ -44,6 +44,13 @@ MUTANTS = [
      "const int64_t e = ((b * L + t) * P + p) * H + hh;", "ssd"),
     ("group_of_channel", "const int64_t g = d / (D / G);", "const int64_t g = d % G;", "scan"),
     ("ssd_group_of_head", "const int64_t g = hh / (H / G);", "const int64_t g = hh % G;", "ssd"),
+    ("bwd_ddt_drops_decay_term", "ddt += gn * ((double)Bm[r + n] * xv + (double)A[d * N + n] * abar * hprev);",
+     "ddt += gn * ((double)Bm[r + n] * xv);", "bwd"),
+    ("bwd_adjoint_not_decayed", "g[n] = abar * gn;", "g[n] = gn;", "bwd"),
+    ("bwd_dx_drops_skip", "dx[e] = dyc * dsk + dt * gB;", "dx[e] = dt * gB;", "bwd"),
+    ("bwd_dC_previous_state", "pC[r + n] += dyc * hs[(t + 1) * N + n];", "pC[r + n] += dyc * hs[t * N + n];", "bwd"),
+    ("bwd_softplus_derivative", "ddt / (1.0 + exp(-v))", "ddt / (1.0 + exp(v))", "bwd"),
+    ("bwd_gate_derivative", "s * (1.0 + zv * (1.0 - s))", "s * (1.0 + zv * s)", "bwd"),
     ("conv_not_causal", "const int64_t s = t - (K - 1) + k;", "const int64_t s = t - k;", "conv"),
     ("conv_history_reversed", "x0[(b * (K - 1) + (K - 1) + s) * D + d]", "x0[(b * (K - 1) - 1 - s) * D + d]",
      "conv"),
@@ -51,7 +58,8 @@ MUTANTS = [
      "conv_input(x, x0, b, L - K + j, L, D, K, d)", "conv"),
 ]
 
-PINS = {"scan": oracle_pins.SCAN_PINS, "ssd": oracle_pins.SSD_PINS, "conv": oracle_pins.CONV_PINS}
+PINS = {"scan": oracle_pins.SCAN_PINS, "ssd": oracle_pins.SSD_PINS, "conv": oracle_pins.CONV_PINS,
+        "bwd": oracle_pins.BWD_PINS}
 
 
 @pytest.mark.parametrize("name,old,new,group", MUTANTS, ids=[m[0] for m in MUTANTS])
