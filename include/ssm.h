@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 3
+#define SSM_ABI_VERSION 4
 
 typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
 
@@ -158,6 +158,48 @@ ssm_status selective_scan_validate(const ssm_scan_args *args);
  * sizes, dtype or state size are invalid). Reads only batch, seqlen, dim, dstate
  * and dtype; the pointers may be NULL. Host-only. */
 size_t selective_scan_workspace_bytes(const ssm_scan_args *args);
+
+/*
+ * Gradients of the selective scan (training) for the loss
+ *   sum(dy * y) + sum(dh_final * h_final)
+ * with y, h_final as selective_scan_fwd computes them from the same inputs. The
+ * forward is recomputed, nothing from it is needed. [Mamba-2 page, Core idea:
+ * Mamba-1's scan, its training throughput.] Reverse-mode through the recurrence:
+ *   dyc_t = dy_t silu(z_t);  g_t = C_t dyc_t + exp(dt_{t+1} A) o g_{t+1}  (adjoint of h_t,
+ *   the last step adds dh_final);  dB_t += g_t dt_t x_t, dC_t += dyc_t h_t (summed over
+ *   the channels of a group);  dx_t = dyc_t Dskip + dt_t sum_n g_t B_t;
+ *   d dt_t = sum_n g_t (B_t x_t + A exp(dt_t A) h_{t-1});  ddelta = d dt * softplus';
+ *   dA += g_t dt_t exp(dt_t A) h_{t-1};  dDskip += dyc_t x_t;  dz_t = dy_t (C_t.h_t +
+ *   Dskip x_t) silu'(z_t);  dh0 = exp(dt_0 A) o g_0.
+ * Forward inputs exactly as ssm_scan_args (same layouts, same nullability; N in
+ * {16, 32, 64}). dy: (batch, L, D) dtype. dh_final: (batch, D, N) fp32, nullable (0).
+ * Outputs, all written in full (accumulated ones are zeroed first):
+ *   dx, ddelta: (batch, L, D) dtype; dz: (batch, L, D) dtype, required iff z != NULL;
+ *   dB, dC: (batch, L, G, N) fp32; dA: (D, N) fp32; dDskip, ddelta_bias: (D) fp32,
+ *   nullable (not computed); dh0: (batch, D, N) fp32, nullable.
+ * dB, dC, dA, dDskip and ddelta_bias are sums of float atomics: equal to the last
+ * bits only up to summation order, run to run.
+ */
+typedef struct ssm_scan_bwd_args {
+    int64_t batch, seqlen, dim, dstate;   /* B, L, D, N */
+    int64_t ngroups;
+    ssm_dtype dtype;
+    int32_t delta_softplus;
+    const void *x, *delta, *z;
+    const void *Bm, *Cm;
+    const float *A, *delta_bias, *Dskip, *h0;
+    const void *dy;
+    const float *dh_final;
+    void *dx, *ddelta, *dz;
+    float *dB, *dC, *dA, *dDskip, *ddelta_bias, *dh0;
+    void *workspace;                      /* >= selective_scan_bwd_workspace_bytes(), 256-B aligned */
+    size_t workspace_bytes;
+} ssm_scan_bwd_args;
+
+ssm_status selective_scan_bwd(const ssm_scan_bwd_args *args, hipStream_t stream);
+
+/* Workspace bytes selective_scan_bwd needs (sizes, dtype and dstate only; 0 if invalid). */
+size_t selective_scan_bwd_workspace_bytes(const ssm_scan_bwd_args *args);
 
 /* Enqueue the chunked scalar-A (SSD) form. Errors as for selective_scan_fwd. */
 ssm_status ssd_chunked_fwd(const ssm_ssd_args *args, hipStream_t stream);

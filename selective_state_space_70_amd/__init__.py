@@ -16,7 +16,7 @@ import torch
 from . import _capi
 from ._capi import SSMError
 
-__all__ = ["selective_scan_fwd", "ssd_chunked_fwd", "selective_state_update", "ssd_state_update",
+__all__ = ["selective_scan_fwd", "selective_scan_bwd", "ssd_chunked_fwd", "selective_state_update", "ssd_state_update",
            "causal_conv1d_fwd", "scan_workspace_bytes", "ssd_workspace_bytes", "abi_version",
            "SSMError"]
 
@@ -322,3 +322,55 @@ def causal_conv1d_fwd(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torc
     a.y, a.final_state = _ptr(y), _ptr(fs)
     _capi.check(_capi.lib().causal_conv1d_fwd(ctypes.byref(a), _stream(dev)))
     return (y, fs) if return_final_state else y
+
+
+def selective_scan_bwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm: torch.Tensor,
+                       Cm: torch.Tensor, dy: torch.Tensor, Dskip: Optional[torch.Tensor] = None,
+                       z: Optional[torch.Tensor] = None, delta_bias: Optional[torch.Tensor] = None,
+                       h0: Optional[torch.Tensor] = None, dh_final: Optional[torch.Tensor] = None,
+                       delta_softplus: bool = True, workspace: Optional[torch.Tensor] = None) -> dict:
+    """Gradients of :func:`selective_scan_fwd` for the loss sum(dy * y) +
+    sum(dh_final * h_final). Inputs as for the forward; dy (batch, L, D) in x's
+    dtype; dh_final (batch, D, N) fp32 or None. Returns a dict: dx, ddelta, dz
+    (x's dtype; dz None without z), dB, dC (fp32, Bm's shape), dA (fp32),
+    dDskip / ddelta_bias (fp32, None when that input is None), dh0 (fp32, None
+    without h0)."""
+    if x.dim() != 3 or A.dim() != 2:
+        raise ValueError("x must be (batch, L, D) and A (D, N)")
+    dev = _device_of(x)
+    batch, L, D = x.shape
+    N = A.shape[1]
+    bc = (batch, L, N) if Bm.dim() == 3 else (batch, L, Bm.shape[2], N)
+    for t, name, shape, dt in ((x, "x", (batch, L, D), x.dtype), (delta, "delta", (batch, L, D), x.dtype),
+                               (z, "z", (batch, L, D), x.dtype), (Bm, "Bm", bc, x.dtype),
+                               (Cm, "Cm", bc, x.dtype), (A, "A", (D, N), torch.float32),
+                               (Dskip, "Dskip", (D,), torch.float32),
+                               (delta_bias, "delta_bias", (D,), torch.float32),
+                               (h0, "h0", (batch, D, N), torch.float32), (dy, "dy", (batch, L, D), x.dtype),
+                               (dh_final, "dh_final", (batch, D, N), torch.float32)):
+        _need(t, name, shape, dt, dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = {"dx": torch.empty_like(x), "ddelta": torch.empty_like(x),
+           "dz": torch.empty_like(x) if z is not None else None,
+           "dB": torch.empty(bc, **f32), "dC": torch.empty(bc, **f32), "dA": torch.empty((D, N), **f32),
+           "dDskip": torch.empty((D,), **f32) if Dskip is not None else None,
+           "ddelta_bias": torch.empty((D,), **f32) if delta_bias is not None else None,
+           "dh0": torch.empty((batch, D, N), **f32) if h0 is not None else None}
+    a = _capi.ScanBwdArgs()
+    a.batch, a.seqlen, a.dim, a.dstate = batch, L, D, N
+    a.ngroups = _groups(Bm, 3)
+    a.dtype = _DT[x.dtype]
+    a.delta_softplus = 1 if delta_softplus else 0
+    a.x, a.delta, a.z, a.Bm, a.Cm = _ptr(x), _ptr(delta), _ptr(z), _ptr(Bm), _ptr(Cm)
+    a.A, a.delta_bias, a.Dskip, a.h0 = _ptr(A), _ptr(delta_bias), _ptr(Dskip), _ptr(h0)
+    a.dy, a.dh_final = _ptr(dy), _ptr(dh_final)
+    for k in ("dx", "ddelta", "dz", "dB", "dC", "dA", "dDskip", "ddelta_bias", "dh0"):
+        setattr(a, k, _ptr(out[k]))
+    L_ = _capi.lib()
+    need = L_.selective_scan_bwd_workspace_bytes(ctypes.byref(a))
+    if need:
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        a.workspace, a.workspace_bytes = workspace.data_ptr(), need
+    _capi.check(L_.selective_scan_bwd(ctypes.byref(a), _stream(dev)))
+    return out

@@ -16,10 +16,11 @@ EXPORTS = [
     "selective_scan_fwd", "selective_scan_chunk_states", "selective_scan_apply",
     "selective_scan_validate", "selective_scan_workspace_bytes",
     "ssd_chunked_fwd", "ssd_chunked_validate", "ssd_chunked_workspace_bytes",
+    "selective_scan_bwd", "selective_scan_bwd_workspace_bytes",
     "selective_state_update", "ssd_state_update", "causal_conv1d_fwd",
     "ssm_status_str", "ssm_last_error", "ssm_abi_version",
 ]
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 _p = ctypes.c_void_p
 
@@ -42,6 +43,20 @@ class SSDArgs(ctypes.Structure):
         ("ngroups", ctypes.c_int64), ("dtype", ctypes.c_int), ("dt_softplus", ctypes.c_int32),
         ("x", _p), ("dt", _p), ("dt_bias", _p), ("A", _p), ("Bm", _p), ("Cm", _p),
         ("Dskip", _p), ("z", _p), ("h0", _p), ("y", _p), ("h_final", _p),
+        ("workspace", _p), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class ScanBwdArgs(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("dim", ctypes.c_int64),
+        ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64), ("dtype", ctypes.c_int),
+        ("delta_softplus", ctypes.c_int32),
+        ("x", _p), ("delta", _p), ("z", _p), ("Bm", _p), ("Cm", _p),
+        ("A", _p), ("delta_bias", _p), ("Dskip", _p), ("h0", _p),
+        ("dy", _p), ("dh_final", _p),
+        ("dx", _p), ("ddelta", _p), ("dz", _p),
+        ("dB", _p), ("dC", _p), ("dA", _p), ("dDskip", _p), ("ddelta_bias", _p), ("dh0", _p),
         ("workspace", _p), ("workspace_bytes", ctypes.c_size_t),
     ]
 
@@ -89,6 +104,7 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         for name, argt in (("selective_scan_fwd", ScanArgs), ("selective_scan_chunk_states", ScanArgs),
                            ("selective_scan_apply", ScanArgs), ("ssd_chunked_fwd", SSDArgs),
+                           ("selective_scan_bwd", ScanBwdArgs),
                            ("selective_state_update", ScanStepArgs), ("ssd_state_update", SSDStepArgs),
                            ("causal_conv1d_fwd", ConvArgs)):
             f = getattr(L, name)
@@ -99,7 +115,8 @@ def lib():
             f.restype = ctypes.c_int
             f.argtypes = [ctypes.POINTER(argt)]
         for name, argt in (("selective_scan_workspace_bytes", ScanArgs),
-                           ("ssd_chunked_workspace_bytes", SSDArgs)):
+                           ("ssd_chunked_workspace_bytes", SSDArgs),
+                           ("selective_scan_bwd_workspace_bytes", ScanBwdArgs)):
             f = getattr(L, name)
             f.restype = ctypes.c_size_t
             f.argtypes = [ctypes.POINTER(argt)]

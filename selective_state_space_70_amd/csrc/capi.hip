@@ -209,6 +209,39 @@ ssm_status check_conv(const ssm_conv_args *a) {
     return SSM_OK;
 }
 
+ssm_status check_bwd_sizes(const ssm_scan_bwd_args *a) {
+    if (!a) return fail(SSM_EINVAL, "selective_scan_bwd: args is NULL");
+    ssm_scan_args f{};
+    f.batch = a->batch; f.seqlen = a->seqlen; f.dim = a->dim; f.dstate = a->dstate;
+    f.ngroups = a->ngroups; f.dtype = a->dtype;
+    const ssm_status st = check_scan_sizes(&f);
+    if (st != SSM_OK) return st;
+    if (a->seqlen > ((int64_t)1 << 30))
+        return fail(SSM_ENOTSUP, "selective_scan_bwd: seqlen must be <= 2^30");
+    return SSM_OK;
+}
+
+ssm_status check_bwd(const ssm_scan_bwd_args *a) {
+    const ssm_status st = check_bwd_sizes(a);
+    if (st != SSM_OK) return st;
+    if (a->batch == 0) return SSM_OK;
+    if (!a->A || !a->dA) return fail(SSM_EINVAL, "selective_scan_bwd: A and dA are required");
+    if (a->seqlen > 0 && (!a->x || !a->delta || !a->Bm || !a->Cm || !a->dy || !a->dx || !a->ddelta ||
+                          !a->dB || !a->dC))
+        return fail(SSM_EINVAL, "selective_scan_bwd: x, delta, Bm, Cm, dy, dx, ddelta, dB, dC are required");
+    if (a->z && !a->dz) return fail(SSM_EINVAL, "selective_scan_bwd: dz is required when z is given");
+    const size_t es = esize(a->dtype);
+    if (!aligned(a->x, es) || !aligned(a->delta, es) || !aligned(a->z, es) || !aligned(a->Bm, es) ||
+        !aligned(a->Cm, es) || !aligned(a->dy, es) || !aligned(a->dx, es) || !aligned(a->ddelta, es) ||
+        !aligned(a->dz, es))
+        return fail(SSM_EINVAL, "selective_scan_bwd: tensors must be aligned to the element size");
+    if (!aligned(a->A, 4) || !aligned(a->delta_bias, 4) || !aligned(a->Dskip, 4) || !aligned(a->h0, 4) ||
+        !aligned(a->dh_final, 4) || !aligned(a->dB, 4) || !aligned(a->dC, 4) || !aligned(a->dA, 4) ||
+        !aligned(a->dDskip, 4) || !aligned(a->ddelta_bias, 4) || !aligned(a->dh0, 4))
+        return fail(SSM_EINVAL, "selective_scan_bwd: fp32 tensors must be 4-byte aligned");
+    return SSM_OK;
+}
+
 ssm_status check_workspace(void *ws, size_t have, size_t need, const char *who) {
     if (need == 0) return SSM_OK;
     if (!ws) return fail(SSM_EINVAL, "%s: workspace of %zu bytes required", who, need);
@@ -303,6 +336,24 @@ ssm_status causal_conv1d_fwd(const ssm_conv_args *a, hipStream_t stream) {
     ssm_status s = check_conv(a);
     if (s != SSM_OK) return s;
     s = ssm::conv_launch(*a, stream, g_err, sizeof g_err);
+    if (s == SSM_OK) g_err[0] = 0;
+    return s;
+}
+
+size_t selective_scan_bwd_workspace_bytes(const ssm_scan_bwd_args *a) {
+    if (check_bwd_sizes(a) != SSM_OK) return 0;
+    return ssm::scan_bwd_plan(*a).bytes;
+}
+
+ssm_status selective_scan_bwd(const ssm_scan_bwd_args *a, hipStream_t stream) {
+    ssm_status s = check_bwd(a);
+    if (s != SSM_OK) return s;
+    const ssm::ScanBwdPlan plan = ssm::scan_bwd_plan(*a);
+    if (a->batch > 0 && a->seqlen > 0) {
+        s = check_workspace(a->workspace, a->workspace_bytes, plan.bytes, "selective_scan_bwd");
+        if (s != SSM_OK) return s;
+    }
+    s = ssm::scan_bwd_launch(*a, plan, stream, g_err, sizeof g_err);
     if (s == SSM_OK) g_err[0] = 0;
     return s;
 }

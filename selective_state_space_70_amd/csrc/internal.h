@@ -39,6 +39,20 @@ SSDPlan ssd_plan(const ssm_ssd_args &a);
 ssm_status ssd_launch(const ssm_ssd_args &a, const SSDPlan &plan, hipStream_t stream,
                       char *err, size_t errlen);
 
+// Gradients of the selective scan: chunks of 64 steps; workspace holds the
+// per-chunk aggregates (forward and adjoint) and the composed entering states.
+struct ScanBwdPlan {
+    int64_t chunks;
+    size_t aggF_offset;   // fp32 [chain][chunk][N+1][64]
+    size_t aggR_offset;   // fp32 [chain][chunk][N][64]
+    size_t hin_offset;    // fp32 [B][chunk][D][N]
+    size_t uin_offset;    // fp32 [B][chunk][D][N]
+    size_t bytes;
+};
+ScanBwdPlan scan_bwd_plan(const ssm_scan_bwd_args &a);
+ssm_status scan_bwd_launch(const ssm_scan_bwd_args &a, const ScanBwdPlan &plan, hipStream_t stream,
+                           char *err, size_t errlen);
+
 // Decode steps and the short convolution: no workspace, one kernel each.
 ssm_status step_launch(const ssm_scan_step_args &a, hipStream_t stream, char *err, size_t errlen);
 ssm_status ssd_step_launch(const ssm_ssd_step_args &a, hipStream_t stream, char *err, size_t errlen);

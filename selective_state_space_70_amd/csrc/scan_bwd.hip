@@ -1,0 +1,451 @@
+// Gradients of the selective scan (training; the pages note that training runs
+// the same scan [Mamba-2 page "Mamba-2：把状态空间模型和 Attention 统一到一个数学框架里",
+// Core idea: Mamba-1's scan and its training throughput]).
+//
+// Reverse-mode through h_t = a_t o h_{t-1} + dt_t x_t B_t, a_t = exp(dt_t A): the
+// adjoint g_t = dL/dh_t runs backwards in time, g_t = C_t dyc_t + a_{t+1} o g_{t+1}
+// (dyc_t = dy_t silu(z_t)), and every gradient is a local product of g_t with
+// forward quantities (h_{t-1}, h_t, dt_t, x_t, B_t). Both recurrences are linear
+// with the same decays, so time is cut into chunks of kChunk steps and each
+// chunk's entering state (from the left) and entering adjoint (from the right)
+// are composed from per-chunk aggregates:
+//   1. bwd_aggregate: per (64 channels, chunk), lane = channel, one pass forward
+//      through the chunk: end state from zero S_c, summed step, and the adjoint
+//      aggregate Q_c = sum_s (prod_{k=t0..s} a_k) C_s dyc_s;
+//   2. bwd_carry: per channel, sequential over chunks: h entering chunk c is
+//      h0 carried through the maps h -> exp(A sum dt) o h + S; the adjoint entering
+//      chunk c from the right is dh_final carried back through u -> exp(A sum dt) o u
+//      + Q. Both are stored per (batch, chunk, channel, n);
+//   3. bwd_main: per (chunk, 32/16/8 channels), lane = (channel, n) so that one
+//      lane holds one scalar state: the chunk is recomputed forward with every h_t
+//      kept in registers, then the adjoint sweeps it backwards. Sums over n (dx,
+//      dt, the readout) are DPP row reductions and permlane swaps; sums over
+//      channels (dB, dC, shared by the channels of a group) are permlane swaps,
+//      then LDS and global float atomics. Per-(t, channel) work (softplus, gate,
+//      dz, dx, ddelta) is done once per pair through LDS, not per lane.
+#include <algorithm>
+#include <cstdio>
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace ssm {
+namespace {
+
+constexpr int kChunk = 64;   // steps per chunk (states of a chunk live in VGPRs)
+constexpr int kWaves = 8;    // waves per workgroup of the main kernel
+
+struct BwdK {
+    const void *x, *delta, *z, *Bm, *Cm, *dy;
+    const float *A, *bias, *Dskip, *h0, *dh_final;
+    void *dx, *ddelta, *dz;
+    float *dB, *dC, *dA, *dDskip, *dbias, *dh0;
+    float *aggF;     // [chain][chunk][N+1][64]: end state from zero, then summed dt
+    float *aggR;     // [chain][chunk][N][64]: adjoint aggregate
+    float *hin;      // [batch][chunk][D][N]: state entering each chunk
+    float *uin;      // [batch][chunk][D][N]: adjoint entering each chunk from the right
+    int64_t L;
+    int32_t D, batch, nch, dblocks, softplus, G, dpg;
+};
+
+// ---------------------------------------------------------------- cross-lane sums
+template <int CTRL>
+__device__ __forceinline__ float ror(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
+}
+// sum over the 16 lanes of a DPP row, in every lane of the row (rotations 1, 2, 4, 8)
+__device__ __forceinline__ float row_sum(float v) {
+    v += ror<0x121>(v);
+    v += ror<0x122>(v);
+    v += ror<0x124>(v);
+    v += ror<0x128>(v);
+    return v;
+}
+// Row-swap sums: v_permlane16_swap exchanges the odd rows of its first operand
+// with the even rows of its second, v_permlane32_swap the upper half of the first
+// with the lower half of the second. With v as both operands the two results add
+// up to v[l] + v[l ^ 16] (v[l] + v[l ^ 32]) in every lane. The two results are
+// copied out as integers before use: reinterpreting the second element of the
+// returned pair in place reads the first one with this compiler.
+__device__ __forceinline__ float pl16_sum(float v) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, v);
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const uint32_t a = r[0], b = r[1];
+    return __uint_as_float(a) + __uint_as_float(b);
+}
+__device__ __forceinline__ float pl32_sum(float v) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, v);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const uint32_t a = r[0], b = r[1];
+    return __uint_as_float(a) + __uint_as_float(b);
+}
+// sum over the N lanes of one channel (lane = channel * N + n), in every lane
+template <int N>
+__device__ __forceinline__ float sum_n(float v) {
+    v = row_sum(v);
+    if constexpr (N >= 32) v = pl16_sum(v);
+    if constexpr (N >= 64) v = pl32_sum(v);
+    return v;
+}
+// sum over the 64 / N channels of a wave at equal n, in every lane
+template <int N>
+__device__ __forceinline__ float sum_ch(float v) {
+    if constexpr (N <= 16) v = pl16_sum(v);
+    if constexpr (N <= 32) v = pl32_sum(v);
+    return v;
+}
+
+__device__ __forceinline__ float sigmoid_f32(float v) { return fast_rcp(1.0f + fast_exp2(-v * kLog2e)); }
+
+// ---------------------------------------------------------------- 1. aggregates
+template <typename T, int N, bool HAS_Z>
+__global__ __launch_bounds__(64) void bwd_aggregate_kernel(const BwdK p) {
+    const int c = blockIdx.x, chain = blockIdx.y;
+    const int b = chain / p.dblocks;
+    const int d = (chain % p.dblocks) * 64 + threadIdx.x;
+    const int dc = d < p.D ? d : p.D - 1;
+    const int t0 = c * kChunk;
+    const int t1 = (int)std::min<int64_t>(p.L, (int64_t)t0 + kChunk);
+    float Al2[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) Al2[n] = p.A[(int64_t)dc * N + n] * kLog2e;
+    const float bias = p.bias ? p.bias[dc] : 0.0f;
+    const int g = __builtin_amdgcn_readfirstlane(dc) / p.dpg;
+    const int GN = p.G * N;
+    const T *Brow = (const T *)p.Bm + ((int64_t)b * p.L * p.G + g) * N;
+    const T *Crow = (const T *)p.Cm + ((int64_t)b * p.L * p.G + g) * N;
+    const T *X = (const T *)p.x, *Dl = (const T *)p.delta, *Z = (const T *)p.z, *DY = (const T *)p.dy;
+    float S[N], R[N], Q[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        S[n] = 0.0f;
+        R[n] = 1.0f;
+        Q[n] = 0.0f;
+    }
+    float dsum = 0.0f;
+    for (int t = t0; t < t1; ++t) {
+        const int64_t e = ((int64_t)b * p.L + t) * p.D + dc;
+        const float xv = to_f32(X[e]);
+        const float v = to_f32(Dl[e]) + bias;
+        const float dt = p.softplus ? softplus_f32(v) : v;
+        float dyc = to_f32(DY[e]);
+        if constexpr (HAS_Z) dyc *= silu_f32(to_f32(Z[e]));
+        float Bv[N], Cv[N];
+        SharedRow<T, N>::load(Brow + t * GN, Bv);
+        SharedRow<T, N>::load(Crow + t * GN, Cv);
+        const float dtx = dt * xv;
+        dsum += dt;
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            const float a = fast_exp2(dt * Al2[n]);
+            S[n] = fmaf(a, S[n], dtx * Bv[n]);
+            R[n] *= a;
+            Q[n] = fmaf(R[n], Cv[n] * dyc, Q[n]);
+        }
+    }
+    float *f = p.aggF + ((size_t)chain * p.nch + c) * (N + 1) * 64 + threadIdx.x;
+    float *r = p.aggR + ((size_t)chain * p.nch + c) * N * 64 + threadIdx.x;
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        f[n * 64] = S[n];
+        r[n * 64] = Q[n];
+    }
+    f[N * 64] = dsum;
+}
+
+// ---------------------------------------------------------------- 2. carry
+template <int N>
+__global__ __launch_bounds__(64) void bwd_carry_kernel(const BwdK p) {
+    const int chain = blockIdx.x;
+    const int b = chain / p.dblocks;
+    const int d = (chain % p.dblocks) * 64 + threadIdx.x;
+    const bool act = d < p.D;
+    const int dc = act ? d : p.D - 1;
+    float Al2[N], h[N];
+    const int64_t ci = (int64_t)b * p.D + dc;
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        Al2[n] = p.A[(int64_t)dc * N + n] * kLog2e;
+        h[n] = p.h0 ? p.h0[ci * N + n] : 0.0f;
+    }
+    const float *F = p.aggF + (size_t)chain * p.nch * (N + 1) * 64 + threadIdx.x;
+    const float *Rg = p.aggR + (size_t)chain * p.nch * N * 64 + threadIdx.x;
+    for (int c = 0; c < p.nch; ++c) {
+        float *o = p.hin + (((int64_t)b * p.nch + c) * p.D + dc) * N;
+        if (act) {
+#pragma unroll
+            for (int n = 0; n < N; ++n) o[n] = h[n];
+        }
+        if (c + 1 < p.nch) {
+            const float *f = F + (size_t)c * (N + 1) * 64;
+            const float ds = f[N * 64];
+#pragma unroll
+            for (int n = 0; n < N; ++n) h[n] = fmaf(fast_exp2(Al2[n] * ds), h[n], f[n * 64]);
+        }
+    }
+#pragma unroll
+    for (int n = 0; n < N; ++n) h[n] = p.dh_final ? p.dh_final[ci * N + n] : 0.0f;
+    for (int c = p.nch - 1; c >= 0; --c) {
+        float *o = p.uin + (((int64_t)b * p.nch + c) * p.D + dc) * N;
+        if (act) {
+#pragma unroll
+            for (int n = 0; n < N; ++n) o[n] = h[n];
+        }
+        if (c > 0) {
+            const float ds = F[(size_t)c * (N + 1) * 64 + N * 64];
+            const float *q = Rg + (size_t)c * N * 64;
+#pragma unroll
+            for (int n = 0; n < N; ++n) h[n] = fmaf(fast_exp2(Al2[n] * ds), h[n], q[n * 64]);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- 3. main
+template <typename T, int N, bool HAS_Z>
+__global__ __launch_bounds__(kWaves * 64) void bwd_main_kernel(const BwdK p) {
+    constexpr int CPW = 64 / N;               // channels per wave
+    constexpr int CPG = kWaves * CPW;         // channels per workgroup
+    constexpr int NT = kWaves * 64;
+    // per (step, channel): dt, dt x, dyc, x, d softplus, dy silu'(z)
+    __shared__ float pre[6][kChunk][CPG];
+    // per (step, channel): readout C.h, sum_n g B, sum_n A g a h_prev
+    __shared__ float post[3][kChunk][CPG];
+    __shared__ float Bs[kChunk][N], Cs[kChunk][N], dBa[kChunk][N], dCa[kChunk][N];
+    __shared__ float dDa[CPG], dba[CPG];
+
+    const int c = blockIdx.y, b = blockIdx.z;
+    const int d0 = blockIdx.x * CPG;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int t0 = c * kChunk;
+    const int nt = (int)std::min<int64_t>(kChunk, p.L - t0);   // steps in this chunk
+    const int g = d0 / p.dpg;                 // every channel of the workgroup is in one group
+    const int GN = p.G * N;
+    const T *X = (const T *)p.x, *Dl = (const T *)p.delta, *Z = (const T *)p.z, *DY = (const T *)p.dy;
+
+    // ---- stage per-step rows and per-(step, channel) quantities
+    for (int v = tid; v < kChunk * N; v += NT) {
+        const int i = v / N, nn = v % N;
+        float bv = 0.0f, cv = 0.0f;
+        if (i < nt) {
+            const int64_t r = (((int64_t)b * p.L + t0 + i) * p.G + g) * N + nn;
+            bv = to_f32(((const T *)p.Bm)[r]);
+            cv = to_f32(((const T *)p.Cm)[r]);
+        }
+        Bs[i][nn] = bv;
+        Cs[i][nn] = cv;
+        dBa[i][nn] = 0.0f;
+        dCa[i][nn] = 0.0f;
+    }
+    for (int v = tid; v < CPG; v += NT) {
+        dDa[v] = 0.0f;
+        dba[v] = 0.0f;
+    }
+    for (int v = tid; v < kChunk * CPG; v += NT) {
+        const int i = v / CPG, cc = v % CPG;
+        const int d = d0 + cc;
+        float dt = 0.0f, xv = 0.0f, dyc = 0.0f, sg = 0.0f, dzf = 0.0f;
+        if (i < nt && d < p.D) {
+            const int64_t e = ((int64_t)b * p.L + t0 + i) * p.D + d;
+            xv = to_f32(X[e]);
+            const float vv = to_f32(Dl[e]) + (p.bias ? p.bias[d] : 0.0f);
+            dt = p.softplus ? softplus_f32(vv) : vv;
+            sg = p.softplus ? sigmoid_f32(vv) : 1.0f;
+            const float dyv = to_f32(DY[e]);
+            dyc = dyv;
+            if constexpr (HAS_Z) {
+                const float zv = to_f32(Z[e]);
+                const float s = sigmoid_f32(zv);
+                dyc = dyv * zv * s;
+                dzf = dyv * s * fmaf(zv, 1.0f - s, 1.0f);
+            }
+        }
+        pre[0][i][cc] = dt;
+        pre[1][i][cc] = dt * xv;
+        pre[2][i][cc] = dyc;
+        pre[3][i][cc] = xv;
+        pre[4][i][cc] = sg;
+        pre[5][i][cc] = dzf;
+    }
+    __syncthreads();
+
+    // ---- lane = (channel, n): recompute the chunk forward, then the adjoint backwards
+    const int ch = wv * CPW + lane / N, n = lane % N;
+    const int d = d0 + ch;
+    const bool act = d < p.D;
+    const int dc = act ? d : p.D - 1;
+    const float An = p.A[(int64_t)dc * N + n];
+    const float A2 = An * kLog2e;
+    const int64_t si = (((int64_t)b * p.nch + c) * p.D + dc) * N + n;
+    const float hin = p.hin[si];
+    float v = p.uin[si];
+    float hs[kChunk];
+    {
+        float h = hin;
+#pragma unroll
+        for (int i = 0; i < kChunk; ++i) {
+            if (i < nt) {
+                const float a = fast_exp2(pre[0][i][ch] * A2);
+                h = fmaf(a, h, pre[1][i][ch] * Bs[i][n]);
+                hs[i] = h;
+                const float yc = sum_n<N>(Cs[i][n] * h);
+                if (n == 0) post[0][i][ch] = yc;
+            } else {
+                hs[i] = 0.0f;
+            }
+        }
+    }
+    float dAacc = 0.0f;
+#pragma unroll
+    for (int i = kChunk - 1; i >= 0; --i) {
+        if (i < nt) {
+            const float dt = pre[0][i][ch], dtx = pre[1][i][ch], dyc = pre[2][i][ch];
+            const float Bv = Bs[i][n];
+            const float a = fast_exp2(dt * A2);
+            const float gq = fmaf(Cs[i][n], dyc, v);          // g_t
+            const float hp = i > 0 ? hs[i - 1] : hin;         // h_{t-1}
+            const float gah = gq * a * hp;
+            dAacc = fmaf(gah, dt, dAacc);
+            const float sB = sum_n<N>(gq * Bv);
+            const float sA = sum_n<N>(An * gah);
+            if (n == 0) {
+                post[1][i][ch] = sB;
+                post[2][i][ch] = sA;
+            }
+            const float pB = sum_ch<N>(gq * dtx);
+            const float pC = sum_ch<N>(dyc * hs[i]);
+            if (lane < N) {
+                atomicAdd(&dBa[i][n], pB);
+                atomicAdd(&dCa[i][n], pC);
+            }
+            v = a * gq;                                       // the adjoint term for t-1
+        }
+    }
+    if (act) {
+        if (c == 0 && p.dh0) p.dh0[((int64_t)b * p.D + d) * N + n] = v;
+        atomicAdd(&p.dA[(int64_t)d * N + n], dAacc);
+    }
+    __syncthreads();
+
+    // ---- per (step, channel): dx, ddelta, dz; per-channel and per-row sums
+    for (int q = tid; q < kChunk * CPG; q += NT) {
+        const int i = q / CPG, cc = q % CPG;
+        const int dd = d0 + cc;
+        if (i < nt && dd < p.D) {
+            const int64_t e = ((int64_t)b * p.L + t0 + i) * p.D + dd;
+            const float dt = pre[0][i][cc], dyc = pre[2][i][cc], xv = pre[3][i][cc];
+            const float dsk = p.Dskip ? p.Dskip[dd] : 0.0f;
+            const float sB = post[1][i][cc], sA = post[2][i][cc];
+            const float gdt = fmaf(xv, sB, sA);
+            const float gdl = gdt * pre[4][i][cc];
+            store_val((T *)p.dx + e, fmaf(dyc, dsk, dt * sB));
+            store_val((T *)p.ddelta + e, gdl);
+            if constexpr (HAS_Z) store_val((T *)p.dz + e, pre[5][i][cc] * fmaf(dsk, xv, post[0][i][cc]));
+            atomicAdd(&dDa[cc], dyc * xv);
+            atomicAdd(&dba[cc], gdl);
+        }
+    }
+    __syncthreads();
+    for (int q = tid; q < nt * N; q += NT) {
+        const int i = q / N, nn = q % N;
+        const int64_t r = (((int64_t)b * p.L + t0 + i) * p.G + g) * N + nn;
+        atomicAdd(&p.dB[r], dBa[i][nn]);
+        atomicAdd(&p.dC[r], dCa[i][nn]);
+    }
+    for (int q = tid; q < CPG; q += NT) {
+        if (d0 + q < p.D) {
+            if (p.dDskip) atomicAdd(&p.dDskip[d0 + q], dDa[q]);
+            if (p.dbias) atomicAdd(&p.dbias[d0 + q], dba[q]);
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void fill_kernel(float *p, int64_t n, const float *src) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = src ? src[i] : 0.0f;
+}
+
+void fill(float *p, int64_t n, hipStream_t s, const float *src = nullptr) {
+    if (p && n > 0) hipLaunchKernelGGL(fill_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n, src);
+}
+
+template <typename T, int N>
+void launch_bwd(const BwdK &k, hipStream_t s) {
+    const int chains = k.batch * k.dblocks;
+    constexpr int CPG = kWaves * (64 / N);
+    if (k.z) {
+        hipLaunchKernelGGL((bwd_aggregate_kernel<T, N, true>), dim3(k.nch, chains), dim3(64), 0, s, k);
+    } else {
+        hipLaunchKernelGGL((bwd_aggregate_kernel<T, N, false>), dim3(k.nch, chains), dim3(64), 0, s, k);
+    }
+    hipLaunchKernelGGL((bwd_carry_kernel<N>), dim3(chains), dim3(64), 0, s, k);
+    const dim3 grid((unsigned)((k.D + CPG - 1) / CPG), (unsigned)k.nch, (unsigned)k.batch);
+    if (k.z)
+        hipLaunchKernelGGL((bwd_main_kernel<T, N, true>), grid, dim3(kWaves * 64), 0, s, k);
+    else
+        hipLaunchKernelGGL((bwd_main_kernel<T, N, false>), grid, dim3(kWaves * 64), 0, s, k);
+}
+
+}  // namespace
+
+ScanBwdPlan scan_bwd_plan(const ssm_scan_bwd_args &a) {
+    ScanBwdPlan pl{};
+    if (a.batch <= 0 || a.seqlen <= 0 || a.dim <= 0) return pl;
+    auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
+    const int64_t N = a.dstate;
+    pl.chunks = (a.seqlen + kChunk - 1) / kChunk;
+    const size_t chains = (size_t)a.batch * ((a.dim + 63) / 64);
+    pl.aggF_offset = 0;
+    pl.aggR_offset = up(chains * pl.chunks * (N + 1) * 64 * sizeof(float));
+    pl.hin_offset = pl.aggR_offset + up(chains * pl.chunks * N * 64 * sizeof(float));
+    const size_t st = (size_t)a.batch * pl.chunks * a.dim * N * sizeof(float);
+    pl.uin_offset = pl.hin_offset + up(st);
+    pl.bytes = pl.uin_offset + up(st);
+    return pl;
+}
+
+ssm_status scan_bwd_launch(const ssm_scan_bwd_args &a, const ScanBwdPlan &plan, hipStream_t s, char *err,
+                           size_t errlen) {
+    if (a.batch == 0) return SSM_OK;
+    (void)hipGetLastError();
+    const int64_t N = a.dstate;
+    // outputs accumulated with atomics start from zero
+    fill(a.dA, a.dim * N, s);
+    fill(a.dDskip, a.dim, s);
+    fill(a.ddelta_bias, a.dim, s);
+    const int64_t G = a.ngroups > 1 ? a.ngroups : 1;
+    fill(a.dB, a.batch * a.seqlen * G * N, s);
+    fill(a.dC, a.batch * a.seqlen * G * N, s);
+    if (a.seqlen == 0) {
+        fill(a.dh0, a.batch * a.dim * N, s, a.dh_final);
+    } else {
+        BwdK k{};
+        k.x = a.x; k.delta = a.delta; k.z = a.z; k.Bm = a.Bm; k.Cm = a.Cm; k.dy = a.dy;
+        k.A = a.A; k.bias = a.delta_bias; k.Dskip = a.Dskip; k.h0 = a.h0; k.dh_final = a.dh_final;
+        k.dx = a.dx; k.ddelta = a.ddelta; k.dz = a.dz;
+        k.dB = a.dB; k.dC = a.dC; k.dA = a.dA; k.dDskip = a.dDskip; k.dbias = a.ddelta_bias; k.dh0 = a.dh0;
+        char *ws = (char *)a.workspace;
+        k.aggF = (float *)(ws + plan.aggF_offset);
+        k.aggR = (float *)(ws + plan.aggR_offset);
+        k.hin = (float *)(ws + plan.hin_offset);
+        k.uin = (float *)(ws + plan.uin_offset);
+        k.L = a.seqlen; k.D = (int32_t)a.dim; k.batch = (int32_t)a.batch; k.nch = (int32_t)plan.chunks;
+        k.dblocks = (int32_t)((a.dim + 63) / 64);
+        k.softplus = a.delta_softplus ? 1 : 0;
+        k.G = (int32_t)G;
+        k.dpg = (int32_t)(a.dim / G);
+        const bool bf = a.dtype == SSM_BF16;
+        switch (a.dstate) {
+            case 16: bf ? launch_bwd<uint16_t, 16>(k, s) : launch_bwd<float, 16>(k, s); break;
+            case 32: bf ? launch_bwd<uint16_t, 32>(k, s) : launch_bwd<float, 32>(k, s); break;
+            default: bf ? launch_bwd<uint16_t, 64>(k, s) : launch_bwd<float, 64>(k, s); break;
+        }
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+        std::snprintf(err, errlen, "selective_scan_bwd: kernel launch failed: %s", hipGetErrorString(e));
+        return SSM_EHIP;
+    }
+    return SSM_OK;
+}
+
+}  // namespace ssm

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_names():
     lib = _capi.lib()
-    assert lib.ssm_abi_version() == _capi.ABI_VERSION == 3
+    assert lib.ssm_abi_version() == _capi.ABI_VERSION == 4
     names = [lib.ssm_status_str(s).decode() for s in range(4)]
     assert names == ["SSM_OK", "SSM_EINVAL", "SSM_ENOTSUP", "SSM_EHIP"]
     assert lib.ssm_status_str(99).decode() == "SSM_UNKNOWN"
@@ -263,3 +263,35 @@ def test_empty_batch_is_a_noop_for_steps_and_conv():
     assert lib.selective_state_update(ctypes.byref(step_args(batch=0, x=None)), None) == _capi.SSM_OK
     assert lib.ssd_state_update(ctypes.byref(ssd_step_args(batch=0, x=None)), None) == _capi.SSM_OK
     assert lib.causal_conv1d_fwd(ctypes.byref(conv_args(batch=0, x=None)), None) == _capi.SSM_OK
+
+
+def bwd_args(**kw):
+    a = _capi.ScanBwdArgs()
+    a.batch, a.seqlen, a.dim, a.dstate, a.dtype, a.delta_softplus = 2, 100, 96, 16, _capi.SSM_BF16, 1
+    for name in ("x", "delta", "z", "Bm", "Cm", "A", "delta_bias", "Dskip", "h0", "dy", "dh_final",
+                 "dx", "ddelta", "dz", "dB", "dC", "dA", "dDskip", "ddelta_bias", "dh0"):
+        setattr(a, name, FAKE)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,want", [
+    ({"dy": None}, _capi.SSM_EINVAL),
+    ({"dA": None}, _capi.SSM_EINVAL),
+    ({"dz": None}, _capi.SSM_EINVAL),                     # z given, dz missing
+    ({"dB": FAKE + 2}, _capi.SSM_EINVAL),
+    ({"dstate": 128}, _capi.SSM_ENOTSUP),
+    ({"ngroups": 2}, _capi.SSM_ENOTSUP),                  # 48 channels per group
+    ({}, _capi.SSM_EINVAL),                               # needs workspace
+])
+def test_bwd_validation(kw, want):
+    assert _capi.lib().selective_scan_bwd(ctypes.byref(bwd_args(**kw)), None) == want
+
+
+def test_bwd_workspace():
+    lib = _capi.lib()
+    need = lib.selective_scan_bwd_workspace_bytes(ctypes.byref(bwd_args(batch=8, seqlen=2048, dim=1536)))
+    # chunks of 64 steps: aggregates plus entering states and adjoints per (b, chunk, d, n)
+    assert need >= 2 * 8 * 32 * 1536 * 16 * 4
+    assert lib.selective_scan_bwd_workspace_bytes(ctypes.byref(bwd_args(dstate=8))) == 0
