@@ -274,6 +274,38 @@ def time_next_rows(steps, warmup, torch, ssm):
     return out
 
 
+def time_bwd(key, steps, warmup, torch, ssm):
+    """Gradients of the scan workload (selective_scan_bwd) with rotated inputs.
+    Algorithmic bytes: x, delta, z, dy read and dx, ddelta, dz written once per
+    (b,t,d); B, C read and dB, dC (fp32) written once per (b,t,n); parameters."""
+    cfg = workloads.CONFIGS[key]
+    dev = torch.device("cuda:0")
+    base = workloads.make_inputs(key)
+    es = 2 if cfg.dtype == "bf16" else 4
+    bld = cfg.batch * cfg.seqlen * cfg.dim
+    bln = cfg.batch * cfg.seqlen * cfg.dstate
+    alg = 7 * bld * es + 2 * bln * es + 2 * bln * 4 + 3 * cfg.dim * cfg.dstate * 4
+    nsets = max(2, math.ceil(768e6 / alg))
+    sets = []
+    g = torch.Generator(device=dev)
+    g.manual_seed(11)
+    for i in range(nsets):
+        t = _device_inputs(base, torch, dev)
+        if i:
+            t["x"] = torch.roll(t["x"], shifts=131 * i, dims=1).contiguous()
+        t["dy"] = torch.randn(t["x"].shape, generator=g, device=dev).to(t["x"].dtype)
+        sets.append(t)
+    ws = torch.empty(1, dtype=torch.uint8, device=dev)
+
+    def call(i):
+        t = sets[i]
+        ssm.selective_scan_bwd(t["x"], t["delta"], t["A"], t["Bm"], t["Cm"], t["dy"], t["Dskip"], t["z"],
+                               t["delta_bias"], None, None)
+
+    ms = _time_rotating(call, nsets, steps, warmup, torch)
+    return {"ms": round(ms, 4), "GB/s": round(alg / ms / 1e6, 1), "Gelem/s": round(cfg.elements / ms / 1e6, 1)}
+
+
 def cpu_baseline(key, budget_s=10.0):
     """The fp64 oracle on the host cores over the same workload (all channels,
     whole sequence), repeated until ~budget_s of wall time; effective GB/s on the
@@ -335,7 +367,9 @@ def main():
     import selective_state_space_70_amd as ssm
 
     if args.next_only:
-        print(json.dumps(time_next_rows(args.steps, args.warmup, torch, ssm)), flush=True)
+        out = time_next_rows(args.steps, args.warmup, torch, ssm)
+        out["bwd_S2"] = time_bwd("S2", args.steps, args.warmup, torch, ssm)
+        print(json.dumps(out), flush=True)
         return
 
     if args.ssd_only:
@@ -393,6 +427,7 @@ def main():
                        "TFLOP/s": round(ssd_alg_flops(c5) / m5 / 1e9, 1),
                        "mfma_frac": round(ssd_alg_flops(c5) / m5 / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4)}
         extra.update(time_next_rows(max(10, args.steps), 3, torch, ssm))
+        extra["bwd_S2"] = time_bwd("S2", max(10, args.steps // 2), 2, torch, ssm)
         line["extra"] = extra
         print(json.dumps(extra), file=sys.stderr)
     if not args.no_cpu_baseline:

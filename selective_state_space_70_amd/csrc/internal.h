@@ -47,6 +47,7 @@ struct ScanBwdPlan {
     size_t aggR_offset;   // fp32 [chain][chunk][N][64]
     size_t hin_offset;    // fp32 [B][chunk][D][N]
     size_t uin_offset;    // fp32 [B][chunk][D][N]
+    size_t dApart_offset; // fp32 [B][chunk][D][N]: per-chunk shares of dA
     size_t bytes;
 };
 ScanBwdPlan scan_bwd_plan(const ssm_scan_bwd_args &a);

@@ -44,6 +44,7 @@ struct BwdK {
     float *aggR;     // [chain][chunk][N][64]: adjoint aggregate
     float *hin;      // [batch][chunk][D][N]: state entering each chunk
     float *uin;      // [batch][chunk][D][N]: adjoint entering each chunk from the right
+    float *dApart;   // [batch][chunk][D][N]: each chunk's share of dA
     int64_t L;
     int32_t D, batch, nch, dblocks, softplus, G, dpg;
 };
@@ -201,17 +202,97 @@ __global__ __launch_bounds__(64) void bwd_carry_kernel(const BwdK p) {
 }
 
 // ---------------------------------------------------------------- 3. main
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+
+// Forward recompute and adjoint sweep of one chunk for lane (channel ch, state n).
+// Steps past the end of the sequence were staged with dt = dt x = dyc = 0: they
+// leave h and the adjoint unchanged and contribute nothing, so every chunk runs
+// all kChunk steps without guards. A first forward pass keeps h at the start of
+// each sub-block of SB steps; each sub-block, last first, is then recomputed with
+// its states and decays kept in registers and swept backwards. This holds 2 SB
+// values per lane instead of kChunk, which leaves room for more waves per SIMD.
+constexpr int kSB = 16;   // steps per sub-block of the backward sweep
+
+template <int N, int CPG>
+__device__ __forceinline__ void sweep(const f32x4 (*pre)[CPG], const f32x2 (*BC)[N], float (*post)[kChunk][CPG],
+                                      f32x2 (*bcw)[kSB][N], f32x2 (*bcacc)[N], int ch, int n, int lane, int wv,
+                                      float An, float hin, float &v, float &dAacc) {
+    constexpr int SB = kSB, NSB = kChunk / SB;
+    const float A2 = An * kLog2e;
+    float ck[NSB];
+    float h = hin;
+#pragma unroll
+    for (int sb = 0; sb < NSB; ++sb) {
+        ck[sb] = h;
+#pragma unroll
+        for (int j = 0; j < SB; ++j) {
+            const int i = sb * SB + j;
+            const f32x4 q = pre[i][ch];
+            h = fmaf(fast_exp2(q[0] * A2), h, q[1] * BC[i][n][0]);
+            if (j % 8 == 7) __builtin_amdgcn_sched_barrier(0);   // bound how far loads run ahead
+        }
+    }
+#pragma unroll
+    for (int sb = NSB - 1; sb >= 0; --sb) {
+        __builtin_amdgcn_sched_barrier(0);
+        float hs[SB], as[SB];
+        float hh = ck[sb];
+#pragma unroll
+        for (int j = 0; j < SB; ++j) {
+            const int i = sb * SB + j;
+            const f32x4 q = pre[i][ch];
+            as[j] = fast_exp2(q[0] * A2);
+            hh = fmaf(as[j], hh, q[1] * BC[i][n][0]);
+            hs[j] = hh;
+            if (j % 8 == 7) __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int j = SB - 1; j >= 0; --j) {
+            const int i = sb * SB + j;
+            const f32x4 q = pre[i][ch];                   // dt, dt x, dyc, x
+            const f32x2 bc = BC[i][n];                    // B, C
+            const float gq = fmaf(bc[1], q[2], v);        // g_t
+            const float hp = j > 0 ? hs[j - 1] : ck[sb];  // h_{t-1}
+            const float gah = gq * as[j] * hp;
+            dAacc = fmaf(gah, q[0], dAacc);
+            const float yc = sum_n<N>(bc[1] * hs[j]);
+            const float sB = sum_n<N>(gq * bc[0]);
+            const float sA = sum_n<N>(An * gah);
+            if (n == 0) {
+                post[0][i][ch] = yc;
+                post[1][i][ch] = sB;
+                post[2][i][ch] = sA;
+            }
+            const float pB = sum_ch<N>(gq * q[1]);
+            const float pC = sum_ch<N>(q[2] * hs[j]);
+            if (lane < N) bcw[wv][j][n] = f32x2{pB, pC};  // this wave's share of dB_t, dC_t
+            v = as[j] * gq;                               // the adjoint term for t-1
+            if (j % 4 == 0) __builtin_amdgcn_sched_barrier(0);
+        }
+        // sum the waves' shares of this sub-block (no atomics)
+        __syncthreads();
+        for (int q = threadIdx.x; q < SB * N; q += kWaves * 64) {
+            const int j = q / N, nn = q % N;
+            f32x2 acc = bcw[0][j][nn];
+#pragma unroll
+            for (int w = 1; w < kWaves; ++w) acc += bcw[w][j][nn];
+            bcacc[sb * SB + j][nn] = acc;
+        }
+        __syncthreads();
+    }
+}
+
 template <typename T, int N, bool HAS_Z>
-__global__ __launch_bounds__(kWaves * 64) void bwd_main_kernel(const BwdK p) {
+__global__ __launch_bounds__(kWaves * 64, 2) void bwd_main_kernel(const BwdK p) {
     constexpr int CPW = 64 / N;               // channels per wave
     constexpr int CPG = kWaves * CPW;         // channels per workgroup
     constexpr int NT = kWaves * 64;
-    // per (step, channel): dt, dt x, dyc, x, d softplus, dy silu'(z)
-    __shared__ float pre[6][kChunk][CPG];
-    // per (step, channel): readout C.h, sum_n g B, sum_n A g a h_prev
-    __shared__ float post[3][kChunk][CPG];
-    __shared__ float Bs[kChunk][N], Cs[kChunk][N], dBa[kChunk][N], dCa[kChunk][N];
-    __shared__ float dDa[CPG], dba[CPG];
+    __shared__ f32x4 pre[kChunk][CPG];        // per (step, channel): dt, dt x, dyc, x
+    __shared__ float post[3][kChunk][CPG];    // readout C.h, sum_n g B, sum_n A g a h_prev
+    __shared__ f32x2 BC[kChunk][N];           // B_t[n], C_t[n]
+    __shared__ f32x2 bcw[kWaves][kSB][N];     // per wave: its channels' dB_t[n], dC_t[n] (one sub-block)
+    __shared__ f32x2 bcacc[kChunk][N];        // all channels of the workgroup
 
     const int c = blockIdx.y, b = blockIdx.z;
     const int d0 = blockIdx.x * CPG;
@@ -219,52 +300,32 @@ __global__ __launch_bounds__(kWaves * 64) void bwd_main_kernel(const BwdK p) {
     const int t0 = c * kChunk;
     const int nt = (int)std::min<int64_t>(kChunk, p.L - t0);   // steps in this chunk
     const int g = d0 / p.dpg;                 // every channel of the workgroup is in one group
-    const int GN = p.G * N;
     const T *X = (const T *)p.x, *Dl = (const T *)p.delta, *Z = (const T *)p.z, *DY = (const T *)p.dy;
 
     // ---- stage per-step rows and per-(step, channel) quantities
     for (int v = tid; v < kChunk * N; v += NT) {
         const int i = v / N, nn = v % N;
-        float bv = 0.0f, cv = 0.0f;
+        f32x2 bc = f32x2{0.f, 0.f};
         if (i < nt) {
             const int64_t r = (((int64_t)b * p.L + t0 + i) * p.G + g) * N + nn;
-            bv = to_f32(((const T *)p.Bm)[r]);
-            cv = to_f32(((const T *)p.Cm)[r]);
+            bc = f32x2{to_f32(((const T *)p.Bm)[r]), to_f32(((const T *)p.Cm)[r])};
         }
-        Bs[i][nn] = bv;
-        Cs[i][nn] = cv;
-        dBa[i][nn] = 0.0f;
-        dCa[i][nn] = 0.0f;
-    }
-    for (int v = tid; v < CPG; v += NT) {
-        dDa[v] = 0.0f;
-        dba[v] = 0.0f;
+        BC[i][nn] = bc;
     }
     for (int v = tid; v < kChunk * CPG; v += NT) {
         const int i = v / CPG, cc = v % CPG;
         const int d = d0 + cc;
-        float dt = 0.0f, xv = 0.0f, dyc = 0.0f, sg = 0.0f, dzf = 0.0f;
+        f32x4 q = f32x4{0.f, 0.f, 0.f, 0.f};
         if (i < nt && d < p.D) {
             const int64_t e = ((int64_t)b * p.L + t0 + i) * p.D + d;
-            xv = to_f32(X[e]);
+            const float xv = to_f32(X[e]);
             const float vv = to_f32(Dl[e]) + (p.bias ? p.bias[d] : 0.0f);
-            dt = p.softplus ? softplus_f32(vv) : vv;
-            sg = p.softplus ? sigmoid_f32(vv) : 1.0f;
-            const float dyv = to_f32(DY[e]);
-            dyc = dyv;
-            if constexpr (HAS_Z) {
-                const float zv = to_f32(Z[e]);
-                const float s = sigmoid_f32(zv);
-                dyc = dyv * zv * s;
-                dzf = dyv * s * fmaf(zv, 1.0f - s, 1.0f);
-            }
+            const float dt = p.softplus ? softplus_f32(vv) : vv;
+            float dyc = to_f32(DY[e]);
+            if constexpr (HAS_Z) dyc *= silu_f32(to_f32(Z[e]));
+            q = f32x4{dt, dt * xv, dyc, xv};
         }
-        pre[0][i][cc] = dt;
-        pre[1][i][cc] = dt * xv;
-        pre[2][i][cc] = dyc;
-        pre[3][i][cc] = xv;
-        pre[4][i][cc] = sg;
-        pre[5][i][cc] = dzf;
+        pre[i][cc] = q;
     }
     __syncthreads();
 
@@ -274,55 +335,15 @@ __global__ __launch_bounds__(kWaves * 64) void bwd_main_kernel(const BwdK p) {
     const bool act = d < p.D;
     const int dc = act ? d : p.D - 1;
     const float An = p.A[(int64_t)dc * N + n];
-    const float A2 = An * kLog2e;
     const int64_t si = (((int64_t)b * p.nch + c) * p.D + dc) * N + n;
     const float hin = p.hin[si];
     float v = p.uin[si];
-    float hs[kChunk];
-    {
-        float h = hin;
-#pragma unroll
-        for (int i = 0; i < kChunk; ++i) {
-            if (i < nt) {
-                const float a = fast_exp2(pre[0][i][ch] * A2);
-                h = fmaf(a, h, pre[1][i][ch] * Bs[i][n]);
-                hs[i] = h;
-                const float yc = sum_n<N>(Cs[i][n] * h);
-                if (n == 0) post[0][i][ch] = yc;
-            } else {
-                hs[i] = 0.0f;
-            }
-        }
-    }
     float dAacc = 0.0f;
-#pragma unroll
-    for (int i = kChunk - 1; i >= 0; --i) {
-        if (i < nt) {
-            const float dt = pre[0][i][ch], dtx = pre[1][i][ch], dyc = pre[2][i][ch];
-            const float Bv = Bs[i][n];
-            const float a = fast_exp2(dt * A2);
-            const float gq = fmaf(Cs[i][n], dyc, v);          // g_t
-            const float hp = i > 0 ? hs[i - 1] : hin;         // h_{t-1}
-            const float gah = gq * a * hp;
-            dAacc = fmaf(gah, dt, dAacc);
-            const float sB = sum_n<N>(gq * Bv);
-            const float sA = sum_n<N>(An * gah);
-            if (n == 0) {
-                post[1][i][ch] = sB;
-                post[2][i][ch] = sA;
-            }
-            const float pB = sum_ch<N>(gq * dtx);
-            const float pC = sum_ch<N>(dyc * hs[i]);
-            if (lane < N) {
-                atomicAdd(&dBa[i][n], pB);
-                atomicAdd(&dCa[i][n], pC);
-            }
-            v = a * gq;                                       // the adjoint term for t-1
-        }
-    }
+    sweep<N, CPG>(pre, BC, post, bcw, bcacc, ch, n, lane, wv, An, hin, v, dAacc);
     if (act) {
         if (c == 0 && p.dh0) p.dh0[((int64_t)b * p.D + d) * N + n] = v;
-        atomicAdd(&p.dA[(int64_t)d * N + n], dAacc);
+        // this chunk's share of dA, summed over (batch, chunk) by bwd_reduce_dA
+        p.dApart[(((int64_t)b * p.nch + c) * p.D + d) * N + n] = dAacc;
     }
     __syncthreads();
 
@@ -332,31 +353,54 @@ __global__ __launch_bounds__(kWaves * 64) void bwd_main_kernel(const BwdK p) {
         const int dd = d0 + cc;
         if (i < nt && dd < p.D) {
             const int64_t e = ((int64_t)b * p.L + t0 + i) * p.D + dd;
-            const float dt = pre[0][i][cc], dyc = pre[2][i][cc], xv = pre[3][i][cc];
+            const f32x4 pr = pre[i][cc];
+            const float dt = pr[0], dyc = pr[2], xv = pr[3];
             const float dsk = p.Dskip ? p.Dskip[dd] : 0.0f;
             const float sB = post[1][i][cc], sA = post[2][i][cc];
-            const float gdt = fmaf(xv, sB, sA);
-            const float gdl = gdt * pre[4][i][cc];
+            float gdl = fmaf(xv, sB, sA);                     // d dt
+            if (p.softplus) gdl *= sigmoid_f32(to_f32(Dl[e]) + (p.bias ? p.bias[dd] : 0.0f));
             store_val((T *)p.dx + e, fmaf(dyc, dsk, dt * sB));
             store_val((T *)p.ddelta + e, gdl);
-            if constexpr (HAS_Z) store_val((T *)p.dz + e, pre[5][i][cc] * fmaf(dsk, xv, post[0][i][cc]));
-            atomicAdd(&dDa[cc], dyc * xv);
-            atomicAdd(&dba[cc], gdl);
+            if constexpr (HAS_Z) {
+                const float zv = to_f32(Z[e]), s = sigmoid_f32(zv);
+                const float dzf = to_f32(DY[e]) * s * fmaf(zv, 1.0f - s, 1.0f);
+                store_val((T *)p.dz + e, dzf * fmaf(dsk, xv, post[0][i][cc]));
+            }
+            post[1][i][cc] = dyc * xv;                       // this pair's dDskip and dbias terms
+            post[2][i][cc] = gdl;
+        } else {
+            post[1][i][cc] = 0.0f;
+            post[2][i][cc] = 0.0f;
         }
     }
     __syncthreads();
     for (int q = tid; q < nt * N; q += NT) {
         const int i = q / N, nn = q % N;
+        const f32x2 acc = bcacc[i][nn];
         const int64_t r = (((int64_t)b * p.L + t0 + i) * p.G + g) * N + nn;
-        atomicAdd(&p.dB[r], dBa[i][nn]);
-        atomicAdd(&p.dC[r], dCa[i][nn]);
+        atomicAdd(&p.dB[r], acc[0]);
+        atomicAdd(&p.dC[r], acc[1]);
     }
     for (int q = tid; q < CPG; q += NT) {
         if (d0 + q < p.D) {
-            if (p.dDskip) atomicAdd(&p.dDskip[d0 + q], dDa[q]);
-            if (p.dbias) atomicAdd(&p.dbias[d0 + q], dba[q]);
+            float sd = 0.0f, sb = 0.0f;
+            for (int i = 0; i < nt; ++i) {
+                sd += post[1][i][q];
+                sb += post[2][i][q];
+            }
+            if (p.dDskip) atomicAdd(&p.dDskip[d0 + q], sd);
+            if (p.dbias) atomicAdd(&p.dbias[d0 + q], sb);
         }
     }
+}
+
+// dA[d, n] = sum over (batch, chunk) of the per-chunk shares
+__global__ __launch_bounds__(256) void bwd_reduce_dA_kernel(const float *part, float *dA, int64_t dn, int64_t parts) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= dn) return;
+    float acc = 0.0f;
+    for (int64_t k = 0; k < parts; ++k) acc += part[k * dn + i];
+    dA[i] = acc;
 }
 
 __global__ __launch_bounds__(256) void fill_kernel(float *p, int64_t n, const float *src) {
@@ -383,6 +427,9 @@ void launch_bwd(const BwdK &k, hipStream_t s) {
         hipLaunchKernelGGL((bwd_main_kernel<T, N, true>), grid, dim3(kWaves * 64), 0, s, k);
     else
         hipLaunchKernelGGL((bwd_main_kernel<T, N, false>), grid, dim3(kWaves * 64), 0, s, k);
+    const int64_t dn = (int64_t)k.D * N;
+    hipLaunchKernelGGL(bwd_reduce_dA_kernel, dim3((unsigned)((dn + 255) / 256)), dim3(256), 0, s, k.dApart, k.dA,
+                       dn, (int64_t)k.batch * k.nch);
 }
 
 }  // namespace
@@ -399,7 +446,8 @@ ScanBwdPlan scan_bwd_plan(const ssm_scan_bwd_args &a) {
     pl.hin_offset = pl.aggR_offset + up(chains * pl.chunks * N * 64 * sizeof(float));
     const size_t st = (size_t)a.batch * pl.chunks * a.dim * N * sizeof(float);
     pl.uin_offset = pl.hin_offset + up(st);
-    pl.bytes = pl.uin_offset + up(st);
+    pl.dApart_offset = pl.uin_offset + up(st);
+    pl.bytes = pl.dApart_offset + up(st);
     return pl;
 }
 
@@ -409,7 +457,7 @@ ssm_status scan_bwd_launch(const ssm_scan_bwd_args &a, const ScanBwdPlan &plan, 
     (void)hipGetLastError();
     const int64_t N = a.dstate;
     // outputs accumulated with atomics start from zero
-    fill(a.dA, a.dim * N, s);
+    if (a.seqlen == 0) fill(a.dA, a.dim * N, s);
     fill(a.dDskip, a.dim, s);
     fill(a.ddelta_bias, a.dim, s);
     const int64_t G = a.ngroups > 1 ? a.ngroups : 1;
@@ -428,6 +476,7 @@ ssm_status scan_bwd_launch(const ssm_scan_bwd_args &a, const ScanBwdPlan &plan, 
         k.aggR = (float *)(ws + plan.aggR_offset);
         k.hin = (float *)(ws + plan.hin_offset);
         k.uin = (float *)(ws + plan.uin_offset);
+        k.dApart = (float *)(ws + plan.dApart_offset);
         k.L = a.seqlen; k.D = (int32_t)a.dim; k.batch = (int32_t)a.batch; k.nch = (int32_t)plan.chunks;
         k.dblocks = (int32_t)((a.dim + 63) / 64);
         k.softplus = a.delta_softplus ? 1 : 0;
