@@ -99,6 +99,92 @@ __device__ __forceinline__ float sum_ch(float v) {
 __device__ __forceinline__ float sigmoid_f32(float v) { return fast_rcp(1.0f + fast_exp2(-v * kLog2e)); }
 
 // ---------------------------------------------------------------- 1. aggregates
+// Rows A[d, n] = (n+1) A[d, 0] (checked exactly, in fp64) give exp(dt A[d, n]) =
+// r^(n+1) with r = exp(dt A[d, 0]): the decays are powers of one exponential, and
+// the running product of decays from the chunk start is a power of one scalar.
+template <int N>
+__device__ __forceinline__ bool geometric_row(const float *Arow) {
+    const double a0 = (double)Arow[0];
+    bool ok = true;
+#pragma unroll
+    for (int n = 1; n < N; ++n) ok = ok && ((double)Arow[n] == (double)(n + 1) * a0);
+    return ok;
+}
+
+// pw[n] = r^(n+1) by a product tree
+template <int N>
+__device__ __forceinline__ void powers_of(float r, float (&pw)[N]) {
+    pw[0] = r;
+#pragma unroll
+    for (int n = 1; n < N; ++n) pw[n] = pw[(n - 1) / 2] * pw[n / 2];
+}
+
+template <typename T, int N, bool HAS_Z, bool FAST>
+__device__ __forceinline__ void aggregate_chunk(const BwdK &p, int b, int dc, int t0, int t1, const float (&Al2)[N],
+                                                float bias, float (&S)[N], float (&Q)[N], float &dsum) {
+    const int g = __builtin_amdgcn_readfirstlane(dc) / p.dpg;
+    const int GN = p.G * N;
+    const T *Brow = (const T *)p.Bm + ((int64_t)b * p.L * p.G + g) * N;
+    const T *Crow = (const T *)p.Cm + ((int64_t)b * p.L * p.G + g) * N;
+    const T *X = (const T *)p.x, *Dl = (const T *)p.delta, *Z = (const T *)p.z, *DY = (const T *)p.dy;
+    float R[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        S[n] = 0.0f;
+        R[n] = 1.0f;
+        Q[n] = 0.0f;
+    }
+    float rho = 1.0f;   // FAST: product of r over the chunk so far
+    dsum = 0.0f;
+    constexpr int U = 8;   // steps whose loads are issued together
+    for (int t = t0; t < t1; t += U) {
+        float xs[U], vs[U], dys[U], zs[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t e = ((int64_t)b * p.L + min(t + u, t1 - 1)) * p.D + dc;
+            xs[u] = to_f32(X[e]);
+            vs[u] = to_f32(Dl[e]);
+            dys[u] = to_f32(DY[e]);
+            zs[u] = HAS_Z ? to_f32(Z[e]) : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (t + u < t1) {
+                const float v = vs[u] + bias;
+                const float dt = p.softplus ? softplus_f32(v) : v;
+                float dyc = dys[u];
+                if constexpr (HAS_Z) dyc *= silu_f32(zs[u]);
+                float Bv[N], Cv[N];
+                SharedRow<T, N>::load(Brow + (t + u) * GN, Bv);
+                SharedRow<T, N>::load(Crow + (t + u) * GN, Cv);
+                const float dtx = dt * xs[u];
+                dsum += dt;
+                if constexpr (FAST) {
+                    const float r = fast_exp2(dt * Al2[0]);
+                    rho *= r;
+                    float a[N];
+                    powers_of<N>(r, a);
+                    float q = rho * dyc;                      // rho^(n+1) dyc, built up over n
+#pragma unroll
+                    for (int n = 0; n < N; ++n) {
+                        S[n] = fmaf(a[n], S[n], dtx * Bv[n]);
+                        Q[n] = fmaf(Cv[n], q, Q[n]);
+                        q *= rho;
+                    }
+                } else {
+#pragma unroll
+                    for (int n = 0; n < N; ++n) {
+                        const float a = fast_exp2(dt * Al2[n]);
+                        S[n] = fmaf(a, S[n], dtx * Bv[n]);
+                        R[n] *= a;
+                        Q[n] = fmaf(R[n], Cv[n] * dyc, Q[n]);
+                    }
+                }
+            }
+        }
+    }
+}
+
 template <typename T, int N, bool HAS_Z>
 __global__ __launch_bounds__(64) void bwd_aggregate_kernel(const BwdK p) {
     const int c = blockIdx.x, chain = blockIdx.y;
@@ -111,39 +197,11 @@ __global__ __launch_bounds__(64) void bwd_aggregate_kernel(const BwdK p) {
 #pragma unroll
     for (int n = 0; n < N; ++n) Al2[n] = p.A[(int64_t)dc * N + n] * kLog2e;
     const float bias = p.bias ? p.bias[dc] : 0.0f;
-    const int g = __builtin_amdgcn_readfirstlane(dc) / p.dpg;
-    const int GN = p.G * N;
-    const T *Brow = (const T *)p.Bm + ((int64_t)b * p.L * p.G + g) * N;
-    const T *Crow = (const T *)p.Cm + ((int64_t)b * p.L * p.G + g) * N;
-    const T *X = (const T *)p.x, *Dl = (const T *)p.delta, *Z = (const T *)p.z, *DY = (const T *)p.dy;
-    float S[N], R[N], Q[N];
-#pragma unroll
-    for (int n = 0; n < N; ++n) {
-        S[n] = 0.0f;
-        R[n] = 1.0f;
-        Q[n] = 0.0f;
-    }
-    float dsum = 0.0f;
-    for (int t = t0; t < t1; ++t) {
-        const int64_t e = ((int64_t)b * p.L + t) * p.D + dc;
-        const float xv = to_f32(X[e]);
-        const float v = to_f32(Dl[e]) + bias;
-        const float dt = p.softplus ? softplus_f32(v) : v;
-        float dyc = to_f32(DY[e]);
-        if constexpr (HAS_Z) dyc *= silu_f32(to_f32(Z[e]));
-        float Bv[N], Cv[N];
-        SharedRow<T, N>::load(Brow + t * GN, Bv);
-        SharedRow<T, N>::load(Crow + t * GN, Cv);
-        const float dtx = dt * xv;
-        dsum += dt;
-#pragma unroll
-        for (int n = 0; n < N; ++n) {
-            const float a = fast_exp2(dt * Al2[n]);
-            S[n] = fmaf(a, S[n], dtx * Bv[n]);
-            R[n] *= a;
-            Q[n] = fmaf(R[n], Cv[n] * dyc, Q[n]);
-        }
-    }
+    float S[N], Q[N], dsum;
+    if (__all(geometric_row<N>(p.A + (int64_t)dc * N)))   // wave-uniform choice
+        aggregate_chunk<T, N, HAS_Z, true>(p, b, dc, t0, t1, Al2, bias, S, Q, dsum);
+    else
+        aggregate_chunk<T, N, HAS_Z, false>(p, b, dc, t0, t1, Al2, bias, S, Q, dsum);
     float *f = p.aggF + ((size_t)chain * p.nch + c) * (N + 1) * 64 + threadIdx.x;
     float *r = p.aggR + ((size_t)chain * p.nch + c) * N * 64 + threadIdx.x;
 #pragma unroll
@@ -216,7 +274,7 @@ constexpr int kSB = 16;   // steps per sub-block of the backward sweep
 
 template <int N, int CPG>
 __device__ __forceinline__ void sweep(const f32x4 (*pre)[CPG], const f32x2 (*BC)[N], float (*post)[kChunk][CPG],
-                                      f32x2 (*bcw)[kSB][N], f32x2 (*bcacc)[N], int ch, int n, int lane, int wv,
+                                      f32x2 (*bcw)[kSB][64], f32x2 (*bcacc)[N], int ch, int n, int lane, int wv,
                                       float An, float hin, float &v, float &dAacc) {
     constexpr int SB = kSB, NSB = kChunk / SB;
     const float A2 = An * kLog2e;
@@ -264,9 +322,7 @@ __device__ __forceinline__ void sweep(const f32x4 (*pre)[CPG], const f32x2 (*BC)
                 post[1][i][ch] = sB;
                 post[2][i][ch] = sA;
             }
-            const float pB = sum_ch<N>(gq * q[1]);
-            const float pC = sum_ch<N>(q[2] * hs[j]);
-            if (lane < N) bcw[wv][j][n] = f32x2{pB, pC};  // this wave's share of dB_t, dC_t
+            bcw[wv][j][lane] = f32x2{gq * q[1], q[2] * hs[j]};   // this lane's terms of dB_t, dC_t
             v = as[j] * gq;                               // the adjoint term for t-1
             if (j % 4 == 0) __builtin_amdgcn_sched_barrier(0);
         }
@@ -274,9 +330,11 @@ __device__ __forceinline__ void sweep(const f32x4 (*pre)[CPG], const f32x2 (*BC)
         __syncthreads();
         for (int q = threadIdx.x; q < SB * N; q += kWaves * 64) {
             const int j = q / N, nn = q % N;
-            f32x2 acc = bcw[0][j][nn];
+            f32x2 acc = f32x2{0.f, 0.f};
 #pragma unroll
-            for (int w = 1; w < kWaves; ++w) acc += bcw[w][j][nn];
+            for (int w = 0; w < kWaves; ++w)
+#pragma unroll
+                for (int c2 = 0; c2 < 64 / N; ++c2) acc += bcw[w][j][c2 * N + nn];
             bcacc[sb * SB + j][nn] = acc;
         }
         __syncthreads();
@@ -291,7 +349,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_main_kernel(const BwdK p) 
     __shared__ f32x4 pre[kChunk][CPG];        // per (step, channel): dt, dt x, dyc, x
     __shared__ float post[3][kChunk][CPG];    // readout C.h, sum_n g B, sum_n A g a h_prev
     __shared__ f32x2 BC[kChunk][N];           // B_t[n], C_t[n]
-    __shared__ f32x2 bcw[kWaves][kSB][N];     // per wave: its channels' dB_t[n], dC_t[n] (one sub-block)
+    __shared__ f32x2 bcw[kWaves][kSB][64];    // per lane: its dB_t, dC_t terms (one sub-block)
     __shared__ f32x2 bcacc[kChunk][N];        // all channels of the workgroup
 
     const int c = blockIdx.y, b = blockIdx.z;
@@ -398,9 +456,20 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_main_kernel(const BwdK p) 
 __global__ __launch_bounds__(256) void bwd_reduce_dA_kernel(const float *part, float *dA, int64_t dn, int64_t parts) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= dn) return;
-    float acc = 0.0f;
-    for (int64_t k = 0; k < parts; ++k) acc += part[k * dn + i];
-    dA[i] = acc;
+    constexpr int U = 8;   // independent loads in flight
+    float acc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc[u] = 0.0f;
+    int64_t k = 0;
+    for (; k + U <= parts; k += U) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc[u] += part[(k + u) * dn + i];
+    }
+    for (; k < parts; ++k) acc[0] += part[k * dn + i];
+    float sum = 0.0f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) sum += acc[u];
+    dA[i] = sum;
 }
 
 __global__ __launch_bounds__(256) void fill_kernel(float *p, int64_t n, const float *src) {
