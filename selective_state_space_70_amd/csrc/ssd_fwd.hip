@@ -136,7 +136,7 @@ __device__ __forceinline__ float head_dt_cs(const SSDK &p, int b, int h, int c, 
 
 // ---------------------------------------------------------------- chunk states
 template <int N, int Q>
-__global__ __launch_bounds__(kThreads) void ssd_chunk_state_kernel(const SSDK p) {
+__global__ __launch_bounds__(kThreads, N > 128 ? 1 : 2) void ssd_chunk_state_kernel(const SSDK p) {
     constexpr int SB = 64;                    // time rows staged per step
     constexpr int LDT = SB + 8;               // padded LDS row (bf16)
     constexpr int NPASS = N > 128 ? N / 128 : 1;
@@ -166,6 +166,48 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_state_kernel(const SSDK p)
         if (lane == 0 && head_ok) p.decay[((int64_t)b * p.H + h) * p.nc + c] = fast_exp2(cs_end * kLog2e);
     }
 
+    // One 64-row block of B (this pass's states) and of x (this wave's head) is
+    // loaded into registers while the previous one is multiplied. In the LDS
+    // transposes consecutive lanes take consecutive groups of 4 rows, so the
+    // 8-byte writes of 16 lanes cover all banks.
+    const int GN = p.G * N;
+    const int sg = tid & 15, co = tid >> 4;           // B block of this thread: 4 rows x 8 states
+    u32x4 breg[4], xreg[2][4];
+    auto fetch = [&](int pass, int s0) {
+        const int rows = (int)std::max<int64_t>(0, std::min<int64_t>(SB, p.L - t_base - s0));
+        const rsrc_t rb = make_rsrc(p.Bm + (((int64_t)b * p.L + t_base + s0) * p.G + g) * N + pass * NP,
+                                    (uint32_t)(rows * GN * 2));
+        const rsrc_t rx = make_rsrc(p.x + (((int64_t)b * p.L + t_base + s0) * p.H + hc) * kP,
+                                    (uint32_t)(rows * p.H * kP * 2));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) breg[i] = load16(rb, (uint32_t)(((sg * 4 + i) * GN + co * 8) * 2));
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int blk = lane + 64 * k, xg = blk & 15, po = blk >> 4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                xreg[k][i] = load16(rx, (uint32_t)(((xg * 4 + i) * p.H * kP + po * 8) * 2));
+        }
+    };
+    auto stash = [&](int s0) {
+        if (co < NP / 8) store_transposed(breg, &BT[0][0], LDT, co * 8, sg * 4);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int blk = lane + 64 * k, xg = blk & 15, po = blk >> 4;
+            u32x4 r[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float w = wsh[wv][s0 + xg * 4 + i];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    r[i][e] = pack_bf16(bf16_lo(xreg[k][i][e]) * w, bf16_hi(xreg[k][i][e]) * w);
+            }
+            store_transposed(r, &XT[wv][0][0], LDT, po * 8, xg * 4);
+        }
+    };
+
+    constexpr int NBLK = Q / SB;
+    fetch(0, 0);
     for (int pass = 0; pass < NPASS; ++pass) {
         f32x4 acc[NT][4];
 #pragma unroll
@@ -173,37 +215,13 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_state_kernel(const SSDK p)
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        for (int s0 = 0; s0 < Q; s0 += SB) {
-            __syncthreads();
-            // B rows s0..s0+63, states pass*NP .. +NP  ->  BT[n][s] (4 x 8 blocks)
-            for (int blk = tid; blk < (SB / 4) * (NP / 8); blk += kThreads) {
-                const int rs = (blk / (NP / 8)) * 4, cn = (blk % (NP / 8)) * 8;
-                u32x4 r[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int64_t tg = t_base + s0 + rs + i;
-                    r[i] = tg < p.L ? *(const u32x4 *)(p.Bm + (((int64_t)b * p.L + tg) * p.G + g) * N + pass * NP + cn)
-                                    : u32x4{0u, 0u, 0u, 0u};
-                }
-                store_transposed(r, &BT[0][0], LDT, cn, rs);
-            }
-            // x rows of this wave's head, scaled by w_s  ->  XT[wave][p][s]
-            for (int blk = lane; blk < (SB / 4) * (kP / 8); blk += 64) {
-                const int rs = (blk / (kP / 8)) * 4, cp = (blk % (kP / 8)) * 8;
-                u32x4 r[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int64_t tg = t_base + s0 + rs + i;
-                    u32x4 v = u32x4{0u, 0u, 0u, 0u};
-                    if (tg < p.L)
-                        v = *(const u32x4 *)(p.x + (((int64_t)b * p.L + tg) * p.H + hc) * kP + cp);
-                    const float w = wsh[wv][s0 + rs + i];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = pack_bf16(bf16_lo(v[e]) * w, bf16_hi(v[e]) * w);
-                    r[i] = v;
-                }
-                store_transposed(r, &XT[wv][0][0], LDT, cp, rs);
-            }
+        for (int blk = 0; blk < NBLK; ++blk) {
+            const int s0 = blk * SB;
+            __syncthreads();                              // previous block's MFMA reads are done
+            stash(s0);
+            // the next block (or the first of the next pass)
+            if (blk + 1 < NBLK) fetch(pass, s0 + SB);
+            else if (pass + 1 < NPASS) fetch(pass + 1, 0);
             __syncthreads();
 #pragma unroll
             for (int kk = 0; kk < SB / 32; ++kk) {
