@@ -242,6 +242,63 @@ def ssd(x, dt, A, Bm, Cm, Dskip=None, z=None, dt_bias=None, h0=None,
     return y, hf
 
 
+def ssd_bwd(x, dt, A, Bm, Cm, dy, Dskip=None, z=None, dt_bias=None, h0=None, dh_final=None,
+            dt_softplus: bool = True, heads: Optional[Sequence[int]] = None) -> dict:
+    """Gradients of the scalar-A (SSD) form in fp64 for the loss
+    sum(dy * y) + sum(dh_final * h_final).
+
+    The SSD form is the selective scan in which every channel p of head h shares
+    the head's raw step dt[:, :, h], decay A[h] (the same for every state n), skip
+    D[h] and bias [Mamba-2 page, key point 3: the decay becomes a scalar times the
+    identity]. By the chain rule the gradient of a shared parameter is the sum of
+    the gradients of its copies, so this runs :func:`selective_scan_bwd` on the
+    broadcast inputs (channel d = h*P + p, the layout of x) and sums the copies:
+    ddt over p, dA over (p, n), dDskip and ddt_bias over p.
+
+    Shapes as :func:`ssd`; dy (batch, L, H, P); dh_final (batch, H, P, N).
+    ``heads`` restricts the computation to a subset of heads: then dx, ddt, dz,
+    dh0 and the per-head gradients are those of the listed heads (in that order)
+    and dB, dC hold only the listed heads' share of the sum over heads.
+    Returns dx, ddt (batch, L, H'), dA, dDskip, ddt_bias (H',), dB, dC (the shape
+    of Bm), dz (None without z), dh0 (batch, H', P, N).
+    """
+    batch, L, H, P = np.shape(x)
+    G = np.shape(Bm)[2] if np.ndim(Bm) == 4 else 1
+    N = np.shape(Bm)[-1]
+    hs = np.arange(H) if heads is None else np.asarray(heads, dtype=np.int64)
+    Hs = len(hs)
+    take = lambda a, ax: None if a is None else np.take(np.asarray(a), hs, axis=ax)
+    xs = take(x, 2).reshape(batch, L, Hs * P)
+    ds = np.repeat(take(dt, 2), P, axis=2)
+    As = np.repeat(take(A, 0), P)[:, None] * np.ones((1, N))
+    bias = None if dt_bias is None else np.repeat(take(dt_bias, 0), P)
+    Dk = None if Dskip is None else np.repeat(take(Dskip, 0), P)
+    zs = None if z is None else take(z, 2).reshape(batch, L, Hs * P)
+    h0s = None if h0 is None else take(h0, 1).reshape(batch, Hs * P, N)
+    dhs = None if dh_final is None else take(dh_final, 1).reshape(batch, Hs * P, N)
+    dys = take(dy, 2).reshape(batch, L, Hs * P)
+    # channel d = i*P + p of the subset reads group hs[i] // (H/G): expand B, C so
+    # that every selected head sees its own group (one group per head)
+    Bg = np.reshape(Bm, (batch, L, G, N))[:, :, hs // (H // G)]
+    Cg = np.reshape(Cm, (batch, L, G, N))[:, :, hs // (H // G)]
+    o = selective_scan_bwd(xs, ds, As.astype(np.float32), Bg, Cg, dys, Dk, zs, bias, h0s, dhs, dt_softplus)
+    # dB, dC per selected head, summed back onto their groups
+    dB = np.zeros((batch, L, G, N))
+    dC = np.zeros((batch, L, G, N))
+    for i, h in enumerate(hs):
+        dB[:, :, h // (H // G)] += o["dB"][:, :, i]
+        dC[:, :, h // (H // G)] += o["dC"][:, :, i]
+    shape_bc = np.shape(Bm)
+    return {"dx": o["dx"].reshape(batch, L, Hs, P),
+            "ddt": o["ddelta"].reshape(batch, L, Hs, P).sum(-1),
+            "dA": o["dA"].reshape(Hs, P, N).sum((1, 2)),
+            "dDskip": None if Dskip is None else o["dDskip"].reshape(Hs, P).sum(1),
+            "ddt_bias": None if dt_bias is None else o["ddelta_bias"].reshape(Hs, P).sum(1),
+            "dB": dB.reshape(shape_bc), "dC": dC.reshape(shape_bc),
+            "dz": None if z is None else o["dz"].reshape(batch, L, Hs, P),
+            "dh0": o["dh0"].reshape(batch, Hs, P, N)}
+
+
 def causal_conv1d(x, w, bias=None, apply_silu: bool = True, x0=None, return_state: bool = False):
     """Reference causal depthwise conv1d (+ SiLU) in fp64. x (batch, L, D), w (D, K),
     bias (D,), x0 (batch, K-1, D) the inputs before t = 0 (zeros when None).

@@ -605,4 +605,73 @@ SSD_PINS = [pin_ssd_semiseparable, pin_ssd_is_broadcast_scan, pin_ssd_channel_su
             pin_ssd_decode_steps_equal_ssd, pin_ssd_groups_split]
 CONV_PINS = [pin_conv1d_numpy, pin_conv1d_history, pin_conv1d_streaming]
 BWD_PINS = [pin_bwd_finite_differences, pin_bwd_autograd]
-ALL_PINS = SCAN_PINS + SSD_PINS + CONV_PINS + BWD_PINS
+def _ssd_bwd_case(rng, batch, L, H, P, N, G):
+    return dict(x=_f32(rng.standard_normal((batch, L, H, P))),
+                dt=_f32(rng.normal(0.0, 0.5, size=(batch, L, H))),
+                A=_f32(-rng.uniform(0.5, 4.0, size=H)),
+                Bm=_f32(rng.standard_normal((batch, L, G, N))),
+                Cm=_f32(rng.standard_normal((batch, L, G, N))),
+                Dskip=_f32(rng.standard_normal(H)),
+                z=_f32(rng.standard_normal((batch, L, H, P))),
+                dt_bias=_f32(rng.uniform(-3.0, -1.0, size=H)),
+                h0=rng.standard_normal((batch, H, P, N)),
+                dy=_f32(rng.standard_normal((batch, L, H, P))),
+                dh_final=rng.standard_normal((batch, H, P, N)))
+
+
+def _ssd_loss(c, softplus=True):
+    y, hf = oracle.ssd(c["x"], c["dt"], c["A"], c["Bm"], c["Cm"], c["Dskip"], c["z"], c["dt_bias"],
+                       c["h0"], dt_softplus=softplus)
+    return float(np.sum(y * c["dy"].astype(np.float64)) + np.sum(hf * c["dh_final"]))
+
+
+def pin_ssd_bwd_finite_differences(seed=24):
+    """The SSD-form gradients (the scan gradients of the broadcast problem, summed
+    over each shared parameter's copies) equal central differences of the
+    separately written SSD forward oracle, for every input, with B/C groups."""
+    rng = np.random.default_rng(seed)
+    for softplus, H, G in ((True, 6, 3), (False, 4, 1)):
+        c = _ssd_bwd_case(rng, 2, 5, H, 2, 3, G)
+        if not softplus:
+            c["dt"] = np.abs(c["dt"]) + _f32(0.05)
+            c["dt_bias"] = _f32(np.zeros(H))
+        gr = oracle.ssd_bwd(c["x"], c["dt"], c["A"], c["Bm"], c["Cm"], c["dy"], c["Dskip"], c["z"],
+                            c["dt_bias"], c["h0"], c["dh_final"], softplus)
+        names = {"x": "dx", "dt": "ddt", "z": "dz", "Bm": "dB", "Cm": "dC", "A": "dA",
+                 "Dskip": "dDskip", "dt_bias": "ddt_bias", "h0": "dh0"}
+        for key, gname in names.items():
+            base = c[key]
+            step = 2.0 ** -10 if base.dtype == np.float32 else 1e-6
+            fd = np.empty(base.shape)
+            for idx in np.ndindex(base.shape):
+                orig = base[idx]
+                base[idx] = orig + step
+                lp = _ssd_loss(c, softplus)
+                base[idx] = orig - step
+                lm = _ssd_loss(c, softplus)
+                base[idx] = orig
+                fd[idx] = (lp - lm) / (2.0 * step)
+            got = np.reshape(gr[gname], fd.shape)
+            err = np.max(np.abs(got - fd)) / max(1e-12, np.max(np.abs(fd)))
+            assert err < 1e-4, "SSD gradient %s differs from finite differences: %.3g" % (gname, err)
+
+
+def pin_ssd_bwd_head_subset(seed=25):
+    """Restricting the SSD gradients to a subset of heads returns exactly those
+    heads' rows of the full result, and the shares of dB, dC over a partition of
+    the heads add up to the full dB, dC."""
+    rng = np.random.default_rng(seed)
+    c = _ssd_bwd_case(rng, 1, 7, 6, 2, 4, 3)
+    args = (c["x"], c["dt"], c["A"], c["Bm"], c["Cm"], c["dy"], c["Dskip"], c["z"], c["dt_bias"], c["h0"],
+            c["dh_final"])
+    full = oracle.ssd_bwd(*args)
+    parts = [oracle.ssd_bwd(*args, heads=hs) for hs in ([4, 0, 5], [1, 3, 2])]
+    for k, ax in (("dx", 2), ("ddt", 2), ("dz", 2), ("dh0", 1), ("dA", 0), ("dDskip", 0), ("ddt_bias", 0)):
+        assert np.array_equal(np.take(full[k], [4, 0, 5], axis=ax), parts[0][k]), k
+    for k in ("dB", "dC"):
+        assert _rel(parts[0][k] + parts[1][k], full[k]) < 1e-14, k
+
+
+SSD_BWD_PINS = [pin_ssd_bwd_finite_differences, pin_ssd_bwd_head_subset]
+
+ALL_PINS = SCAN_PINS + SSD_PINS + CONV_PINS + BWD_PINS + SSD_BWD_PINS

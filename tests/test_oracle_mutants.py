@@ -79,3 +79,32 @@ def test_mutant_is_caught(tmp_path, name, old, new, group):
             except (AssertionError, ValueError, FloatingPointError):
                 failed.append(pin.__name__)
     assert failed, "mutant %s passed every pin" % name
+
+
+# Mistakes in the SSD-form gradients (the composition in oracle/__init__.py over
+# the scan gradients): (name, text in ssd_bwd, replacement)
+SSD_BWD_MUTANTS = [
+    ("ssd_bwd_group_index", "hs // (H // G)]\n    Cg", "hs // G]\n    Cg"),
+    ("ssd_bwd_ddt_mean", '"ddt": o["ddelta"].reshape(batch, L, Hs, P).sum(-1)',
+     '"ddt": o["ddelta"].reshape(batch, L, Hs, P).mean(-1)'),
+    ("ssd_bwd_dt_tiled", "np.repeat(take(dt, 2), P, axis=2)", "np.tile(take(dt, 2), (1, 1, P))"),
+    ("ssd_bwd_dA_one_state", '"dA": o["dA"].reshape(Hs, P, N).sum((1, 2))',
+     '"dA": o["dA"].reshape(Hs, P, N).sum(1)[:, 0]'),
+]
+
+
+@pytest.mark.parametrize("name,old,new", SSD_BWD_MUTANTS, ids=[m[0] for m in SSD_BWD_MUTANTS])
+def test_ssd_bwd_mutant_is_caught(monkeypatch, name, old, new):
+    import inspect
+    src = inspect.getsource(oracle.ssd_bwd)
+    assert src.count(old) == 1, "mutation anchor not found in ssd_bwd: %r" % old
+    ns = dict(oracle.__dict__)
+    exec(src.replace(old, new), ns)
+    monkeypatch.setattr(oracle, "ssd_bwd", ns["ssd_bwd"])
+    failed = []
+    for pin in oracle_pins.SSD_BWD_PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError):
+            failed.append(pin.__name__)
+    assert failed, "mutant %s passed every pin" % name
