@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 4
+#define SSM_ABI_VERSION 5
 
 typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
 
@@ -210,6 +210,55 @@ ssm_status ssd_chunked_validate(const ssm_ssd_args *args);
 /* Workspace bytes ssd_chunked_fwd needs for these sizes (0 if invalid). Reads only
  * the sizes and dtype; the pointers may be NULL. Host-only. */
 size_t ssd_chunked_workspace_bytes(const ssm_ssd_args *args);
+
+/*
+ * Gradients of the scalar-A (SSD) form for the loss sum(dy * y) + sum(dh_final *
+ * h_final), with y, h_final as ssd_chunked_fwd computes them from the same inputs
+ * (recomputed; nothing from the forward is needed) [Mamba-2 page, Core idea:
+ * training throughput of the scan; key point 3: the scalar-times-identity decay
+ * that keeps the matrix form]. Per head h (channels p, states n), with
+ * g_t = dL/dS_t the adjoint state and dyc = dy silu(z):
+ *   g_t = C_t (x) dyc_t + a_{t+1} g_{t+1}  (the last step adds dh_final);
+ *   dx_t = dt_t g_t B_t + Dskip dyc_t;  dB_t += dt_t g_t^T x_t, dC_t += S_t^T dyc_t
+ *   (summed over the heads of a group);  d dt_t = sum_{p,n} g_t (x_t B_t^T + A a_t S_{t-1});
+ *   ddt = d dt * softplus';  dA += sum_{t,p,n} g_t dt_t a_t S_{t-1};  dDskip += dyc_t . x_t;
+ *   dz_t = dy_t (C_t S_t + Dskip x_t) silu'(z_t);  dh0 = a_0 g_0.
+ * Computed chunk by chunk on the matrix cores (dx, dB, dC, the adjoint states);
+ * the decay gradients come from fp32 sums of the chunk's (t, s) terms.
+ * Forward inputs exactly as ssm_ssd_args (dtype BF16, P == 64, chunk in {64, 128,
+ * 256}; N in {64, 128}). dy: (batch, L, H, P) bf16. dh_final: (batch, H, P, N) fp32,
+ * nullable (0). Outputs, all written in full:
+ *   dx: (batch, L, H, P) bf16; ddt: (batch, L, H) bf16 (gradient of the raw dt);
+ *   dz: (batch, L, H, P) bf16, required iff z != NULL; dB, dC: (batch, L, G, N) fp32;
+ *   dA: (H) fp32; dDskip, ddt_bias: (H) fp32, nullable (not computed); dh0:
+ *   (batch, H, P, N) fp32, nullable.
+ * dA, dDskip and ddt_bias are sums of float atomics: equal to the last bits only up
+ * to summation order, run to run; dx, ddt, dz, dB, dC and dh0 are deterministic.
+ */
+typedef struct ssm_ssd_bwd_args {
+    int64_t batch, seqlen, nheads, headdim, dstate, chunk;  /* B, L, H, P, N, Q */
+    int64_t ngroups;
+    ssm_dtype dtype;
+    int32_t dt_softplus;
+    const void *x, *dt;
+    const float *dt_bias, *A;
+    const void *Bm, *Cm;
+    const float *Dskip;
+    const void *z;
+    const float *h0;
+    const void *dy;
+    const float *dh_final;
+    void *dx, *ddt, *dz;
+    float *dB, *dC, *dA, *dDskip, *ddt_bias, *dh0;
+    void *workspace;                      /* >= ssd_chunked_bwd_workspace_bytes(), 256-B aligned */
+    size_t workspace_bytes;
+} ssm_ssd_bwd_args;
+
+ssm_status ssd_chunked_bwd(const ssm_ssd_bwd_args *args, hipStream_t stream);
+
+/* Workspace bytes ssd_chunked_bwd needs (sizes, dtype and whether z is given; 0 if
+ * invalid). Host-only. */
+size_t ssd_chunked_bwd_workspace_bytes(const ssm_ssd_bwd_args *args);
 
 /*
  * One decode step of the selective scan (a sequence of length 1), the state read

@@ -16,7 +16,7 @@ import torch
 from . import _capi
 from ._capi import SSMError
 
-__all__ = ["selective_scan_fwd", "selective_scan_bwd", "ssd_chunked_fwd", "selective_state_update", "ssd_state_update",
+__all__ = ["selective_scan_fwd", "selective_scan_bwd", "ssd_chunked_fwd", "ssd_chunked_bwd", "selective_state_update", "ssd_state_update",
            "causal_conv1d_fwd", "scan_workspace_bytes", "ssd_workspace_bytes", "abi_version",
            "SSMError"]
 
@@ -373,4 +373,55 @@ def selective_scan_bwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm
             workspace = torch.empty(need, dtype=torch.uint8, device=dev)
         a.workspace, a.workspace_bytes = workspace.data_ptr(), need
     _capi.check(L_.selective_scan_bwd(ctypes.byref(a), _stream(dev)))
+    return out
+
+
+def ssd_chunked_bwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, Bm: torch.Tensor,
+                    Cm: torch.Tensor, dy: torch.Tensor, Dskip: Optional[torch.Tensor] = None,
+                    z: Optional[torch.Tensor] = None, dt_bias: Optional[torch.Tensor] = None,
+                    h0: Optional[torch.Tensor] = None, dh_final: Optional[torch.Tensor] = None,
+                    chunk: int = 256, dt_softplus: bool = True,
+                    workspace: Optional[torch.Tensor] = None) -> dict:
+    """Gradients of :func:`ssd_chunked_fwd` for the loss sum(dy * y) +
+    sum(dh_final * h_final). Inputs as for the forward; dy (batch, L, H, P) bf16;
+    dh_final (batch, H, P, N) fp32 or None. Returns a dict: dx, ddt, dz (bf16; dz
+    None without z), dB, dC (fp32, Bm's shape), dA (fp32, (H,)), dDskip / ddt_bias
+    (fp32, None when that input is None), dh0 (fp32, None without h0)."""
+    if x.dim() != 4 or Bm.dim() not in (3, 4):
+        raise ValueError("x must be (batch, L, H, P) and Bm (batch, L, [G,] N)")
+    dev = _device_of(x)
+    batch, L, H, P = x.shape
+    N = Bm.shape[-1]
+    bc = (batch, L, N) if Bm.dim() == 3 else (batch, L, Bm.shape[2], N)
+    for t, name, shape, dty in ((x, "x", (batch, L, H, P), x.dtype), (dt, "dt", (batch, L, H), x.dtype),
+                                (z, "z", (batch, L, H, P), x.dtype), (Bm, "Bm", bc, x.dtype),
+                                (Cm, "Cm", bc, x.dtype), (A, "A", (H,), torch.float32),
+                                (Dskip, "Dskip", (H,), torch.float32), (dt_bias, "dt_bias", (H,), torch.float32),
+                                (h0, "h0", (batch, H, P, N), torch.float32),
+                                (dy, "dy", (batch, L, H, P), x.dtype),
+                                (dh_final, "dh_final", (batch, H, P, N), torch.float32)):
+        _need(t, name, shape, dty, dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = {"dx": torch.empty_like(x), "ddt": torch.empty_like(dt),
+           "dz": torch.empty_like(x) if z is not None else None,
+           "dB": torch.empty(bc, **f32), "dC": torch.empty(bc, **f32), "dA": torch.empty((H,), **f32),
+           "dDskip": torch.empty((H,), **f32) if Dskip is not None else None,
+           "ddt_bias": torch.empty((H,), **f32) if dt_bias is not None else None,
+           "dh0": torch.empty((batch, H, P, N), **f32) if h0 is not None else None}
+    a = _capi.SSDBwdArgs()
+    a.batch, a.seqlen, a.nheads, a.headdim, a.dstate, a.chunk = batch, L, H, P, N, chunk
+    a.ngroups = _groups(Bm, 3)
+    a.dtype = _DT[x.dtype]
+    a.dt_softplus = 1 if dt_softplus else 0
+    a.x, a.dt, a.dt_bias, a.A, a.Bm, a.Cm = _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(Bm), _ptr(Cm)
+    a.Dskip, a.z, a.h0, a.dy, a.dh_final = _ptr(Dskip), _ptr(z), _ptr(h0), _ptr(dy), _ptr(dh_final)
+    for k in ("dx", "ddt", "dz", "dB", "dC", "dA", "dDskip", "ddt_bias", "dh0"):
+        setattr(a, k, _ptr(out[k]))
+    L_ = _capi.lib()
+    need = L_.ssd_chunked_bwd_workspace_bytes(ctypes.byref(a))
+    if need:
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        a.workspace, a.workspace_bytes = workspace.data_ptr(), need
+    _capi.check(L_.ssd_chunked_bwd(ctypes.byref(a), _stream(dev)))
     return out

@@ -17,10 +17,11 @@ EXPORTS = [
     "selective_scan_validate", "selective_scan_workspace_bytes",
     "ssd_chunked_fwd", "ssd_chunked_validate", "ssd_chunked_workspace_bytes",
     "selective_scan_bwd", "selective_scan_bwd_workspace_bytes",
+    "ssd_chunked_bwd", "ssd_chunked_bwd_workspace_bytes",
     "selective_state_update", "ssd_state_update", "causal_conv1d_fwd",
     "ssm_status_str", "ssm_last_error", "ssm_abi_version",
 ]
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 _p = ctypes.c_void_p
 
@@ -57,6 +58,19 @@ class ScanBwdArgs(ctypes.Structure):
         ("dy", _p), ("dh_final", _p),
         ("dx", _p), ("ddelta", _p), ("dz", _p),
         ("dB", _p), ("dC", _p), ("dA", _p), ("dDskip", _p), ("ddelta_bias", _p), ("dh0", _p),
+        ("workspace", _p), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class SSDBwdArgs(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64),
+        ("headdim", ctypes.c_int64), ("dstate", ctypes.c_int64), ("chunk", ctypes.c_int64),
+        ("ngroups", ctypes.c_int64), ("dtype", ctypes.c_int), ("dt_softplus", ctypes.c_int32),
+        ("x", _p), ("dt", _p), ("dt_bias", _p), ("A", _p), ("Bm", _p), ("Cm", _p),
+        ("Dskip", _p), ("z", _p), ("h0", _p), ("dy", _p), ("dh_final", _p),
+        ("dx", _p), ("ddt", _p), ("dz", _p),
+        ("dB", _p), ("dC", _p), ("dA", _p), ("dDskip", _p), ("ddt_bias", _p), ("dh0", _p),
         ("workspace", _p), ("workspace_bytes", ctypes.c_size_t),
     ]
 
@@ -104,7 +118,7 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         for name, argt in (("selective_scan_fwd", ScanArgs), ("selective_scan_chunk_states", ScanArgs),
                            ("selective_scan_apply", ScanArgs), ("ssd_chunked_fwd", SSDArgs),
-                           ("selective_scan_bwd", ScanBwdArgs),
+                           ("selective_scan_bwd", ScanBwdArgs), ("ssd_chunked_bwd", SSDBwdArgs),
                            ("selective_state_update", ScanStepArgs), ("ssd_state_update", SSDStepArgs),
                            ("causal_conv1d_fwd", ConvArgs)):
             f = getattr(L, name)
@@ -116,7 +130,8 @@ def lib():
             f.argtypes = [ctypes.POINTER(argt)]
         for name, argt in (("selective_scan_workspace_bytes", ScanArgs),
                            ("ssd_chunked_workspace_bytes", SSDArgs),
-                           ("selective_scan_bwd_workspace_bytes", ScanBwdArgs)):
+                           ("selective_scan_bwd_workspace_bytes", ScanBwdArgs),
+                           ("ssd_chunked_bwd_workspace_bytes", SSDBwdArgs)):
             f = getattr(L, name)
             f.restype = ctypes.c_size_t
             f.argtypes = [ctypes.POINTER(argt)]

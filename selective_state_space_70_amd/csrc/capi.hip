@@ -127,6 +127,44 @@ ssm_status check_ssd(const ssm_ssd_args *a) {
     return SSM_OK;
 }
 
+ssm_ssd_args ssd_sizes_of(const ssm_ssd_bwd_args *a) {
+    ssm_ssd_args f{};
+    f.batch = a->batch; f.seqlen = a->seqlen; f.nheads = a->nheads; f.headdim = a->headdim;
+    f.dstate = a->dstate; f.chunk = a->chunk; f.ngroups = a->ngroups; f.dtype = a->dtype;
+    return f;
+}
+
+ssm_status check_ssd_bwd_sizes(const ssm_ssd_bwd_args *a) {
+    if (!a) return fail(SSM_EINVAL, "ssd_chunked_bwd: args is NULL");
+    const ssm_ssd_args f = ssd_sizes_of(a);
+    const ssm_status st = check_ssd_sizes(&f);
+    if (st != SSM_OK) return st;
+    if (a->dstate != 64 && a->dstate != 128)
+        return fail(SSM_ENOTSUP, "ssd_chunked_bwd: dstate %lld not supported (64, 128)", (long long)a->dstate);
+    return SSM_OK;
+}
+
+ssm_status check_ssd_bwd(const ssm_ssd_bwd_args *a) {
+    const ssm_status st = check_ssd_bwd_sizes(a);
+    if (st != SSM_OK) return st;
+    if (a->batch == 0) return SSM_OK;
+    if (!a->A || !a->dA) return fail(SSM_EINVAL, "ssd_chunked_bwd: A and dA are required");
+    if (!aligned(a->A, 4) || !aligned(a->dt_bias, 4) || !aligned(a->Dskip, 4) || !aligned(a->h0, 4) ||
+        !aligned(a->dh_final, 4) || !aligned(a->dA, 4) || !aligned(a->dDskip, 4) ||
+        !aligned(a->ddt_bias, 4) || !aligned(a->dh0, 4))
+        return fail(SSM_EINVAL, "ssd_chunked_bwd: fp32 parameters, states and their gradients must be 4-byte aligned");
+    if (a->seqlen == 0) return SSM_OK;
+    if (!a->x || !a->dt || !a->Bm || !a->Cm || !a->dy || !a->dx || !a->ddt || !a->dB || !a->dC)
+        return fail(SSM_EINVAL, "ssd_chunked_bwd: x, dt, Bm, Cm, dy, dx, ddt, dB, dC are required");
+    if (a->z && !a->dz) return fail(SSM_EINVAL, "ssd_chunked_bwd: dz is required when z is given");
+    if (!aligned(a->x, 16) || !aligned(a->z, 16) || !aligned(a->Bm, 16) || !aligned(a->Cm, 16) ||
+        !aligned(a->dy, 16) || !aligned(a->dx, 16) || !aligned(a->dz, 16) || !aligned(a->dt, 2) ||
+        !aligned(a->ddt, 2) || !aligned(a->dB, 16) || !aligned(a->dC, 16))
+        return fail(SSM_EINVAL, "ssd_chunked_bwd: x, z, Bm, Cm, dy, dx, dz, dB, dC must be 16-byte aligned, "
+                    "dt and ddt 2-byte");
+    return SSM_OK;
+}
+
 bool step_dstate_ok(int64_t n) { return n == 16 || n == 32 || n == 64 || n == 128 || n == 256; }
 
 ssm_status check_step(const ssm_scan_step_args *a) {
@@ -354,6 +392,24 @@ ssm_status selective_scan_bwd(const ssm_scan_bwd_args *a, hipStream_t stream) {
         if (s != SSM_OK) return s;
     }
     s = ssm::scan_bwd_launch(*a, plan, stream, g_err, sizeof g_err);
+    if (s == SSM_OK) g_err[0] = 0;
+    return s;
+}
+
+size_t ssd_chunked_bwd_workspace_bytes(const ssm_ssd_bwd_args *a) {
+    if (check_ssd_bwd_sizes(a) != SSM_OK) return 0;
+    return ssm::ssd_bwd_plan(*a).bytes;
+}
+
+ssm_status ssd_chunked_bwd(const ssm_ssd_bwd_args *a, hipStream_t stream) {
+    ssm_status s = check_ssd_bwd(a);
+    if (s != SSM_OK) return s;
+    const ssm::SSDBwdPlan plan = ssm::ssd_bwd_plan(*a);
+    if (a->batch > 0 && a->seqlen > 0) {
+        s = check_workspace(a->workspace, a->workspace_bytes, plan.bytes, "ssd_chunked_bwd");
+        if (s != SSM_OK) return s;
+    }
+    s = ssm::ssd_bwd_launch(*a, plan, stream, g_err, sizeof g_err);
     if (s == SSM_OK) g_err[0] = 0;
     return s;
 }

@@ -39,6 +39,36 @@ SSDPlan ssd_plan(const ssm_ssd_args &a);
 ssm_status ssd_launch(const ssm_ssd_args &a, const SSDPlan &plan, hipStream_t stream,
                       char *err, size_t errlen);
 
+// Pieces of the SSD forward the gradient pass reruns (what: 0 = split-precision
+// chunk states and the entering states, 1 = fp32 pre-gate output, 2 = adjoint
+// aggregates with exp(cs_t) weights). N in {64, 128}.
+struct SSDK;
+void ssd_recompute_launch(const SSDK &k, int batch, int Q, int N, int what, hipStream_t s);
+
+// Gradients of the SSD form (see ssd_bwd.hip for the buffers).
+struct SSDBwdPlan {
+    int64_t nchunks, slices_col, slices_row;
+    int32_t hs_col, hs_row;   // heads per workgroup of the column / row kernels
+    size_t sin32_offset;      // fp32 [B][nc][H][P][N]: chunk states, then entering states
+    size_t sin_offset;        // bf16 [B][nc][H][P][N]: entering states (forward output recompute)
+    size_t decay_offset;      // fp32 [B][H][nc]
+    size_t hfin_offset;       // fp32 [B][H][P][N]: final state of the recompute
+    size_t gout_offset;       // fp32 [B][nc][H][P][N]: adjoint aggregates, then adjoint at chunk ends
+    size_t kc_offset;         // fp32 [B][H][nc]: <adjoint, state> at each chunk end
+    size_t y32_offset;        // fp32 (B, L, H, P): pre-gate output (only with z)
+    size_t dych_offset;       // bf16 (B, L, H, P): dy silu(z), hi part (only with z)
+    size_t dycl_offset;       // bf16 (B, L, H, P): lo part (only with z)
+    size_t q_offset;          // fp32 (B, L, H): sum_p dyc (y - D x)
+    size_t dtdd_offset;       // fp32 (B, L, H): dt_t sum_{p,n} g_t x_t B_t
+    size_t dd_offset;         // fp32 (B, L, H): sum_{p,n} g_t x_t B_t
+    size_t dBp_offset;        // fp32 [slices_col][B][L][G][N]
+    size_t dCp_offset;        // fp32 [slices_row][B][L][G][N]
+    size_t bytes;
+};
+SSDBwdPlan ssd_bwd_plan(const ssm_ssd_bwd_args &a);
+ssm_status ssd_bwd_launch(const ssm_ssd_bwd_args &a, const SSDBwdPlan &plan, hipStream_t stream,
+                          char *err, size_t errlen);
+
 // Gradients of the selective scan: chunks of 64 steps; workspace holds the
 // per-chunk aggregates (forward and adjoint) and the composed entering states.
 struct ScanBwdPlan {

@@ -1,0 +1,122 @@
+// Device code shared by the scalar-A (SSD) kernels: the matrix-core fragment
+// helpers, LDS transposes, the per-head step and cumulative log-decay of a chunk,
+// and the kernel argument block.
+//
+// Fragments of v_mfma_f32_16x16x32_bf16 (lane l, r16 = l & 15, kb = l >> 4):
+//   A (16 x 32): row r16, k = 8 kb + e (e = 0..7, one 16-byte vector);
+//   B (32 x 16): column r16, k = 8 kb + e;
+//   D (16 x 16, fp32): rows 4 kb + i (i = 0..3), column r16.
+// Two D tiles over consecutive 16-blocks of a dimension j give a lane the 8 values
+// j = 16 h + 4 kb + i (h, i in 0..1, 0..3); used as the k values of an A fragment
+// they stand for k = 8 kb + 4 h + i, so the matching B operand is stored with its
+// k rows permuted by perm_s.
+#pragma once
+
+#include <algorithm>
+
+#include "device_common.h"
+
+namespace ssm {
+
+constexpr int kP = 64;          // head dimension handled by these kernels
+constexpr int kThreads = 256;   // 4 waves
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+__device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4 &v) { return __builtin_bit_cast(bf16x8, v); }
+
+// 16 bytes through a buffer resource (0 outside its range)
+__device__ __forceinline__ u32x4 load16(rsrc_t r, uint32_t voff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) { return pack_bf16x2(lo, hi); }
+
+// (lo halves of a, b) and (hi halves of a, b) as packed bf16 pairs.
+__device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) {
+    return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) {
+    return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+// Write a 4 x 8 block (4 rows, 8 columns, each row one u32x4 of packed bf16) to
+// LDS transposed: T[c][r0 .. r0+3] for the 8 columns c0 .. c0+7.
+__device__ __forceinline__ void store_transposed(const u32x4 (&r)[4], uint16_t *T, int ldt, int c0,
+                                                 int r0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const u32x2 lo = u32x2{lo_pair(r[0][j], r[1][j]), lo_pair(r[2][j], r[3][j])};
+        const u32x2 hi = u32x2{hi_pair(r[0][j], r[1][j]), hi_pair(r[2][j], r[3][j])};
+        *(u32x2 *)&T[(c0 + 2 * j) * ldt + r0] = lo;
+        *(u32x2 *)&T[(c0 + 2 * j + 1) * ldt + r0] = hi;
+    }
+}
+
+struct SSDK {
+    const uint16_t *x, *dt, *Bm, *Cm, *z;
+    const float *dt_bias, *A, *Dskip, *h0;
+    uint16_t *y;
+    float *h_final;
+    float *states;      // fp32 [B][nc][H][P][N]: state of each chunk from zero
+    uint16_t *sin;      // bf16 [B][nc][H][P][N]: state entering each chunk
+    float *decay;       // fp32 [B][H][nc]: exp(cs_end) of each chunk
+    float *sin32;       // optional fp32 copy of the entering states (may alias states)
+    float *y32;         // fp32 pre-gate output (B, L, H, P) of the recompute variant
+    const uint16_t *xlo;   // optional bf16 lo part of x (adjoint aggregates: dyc = hi + lo)
+    int64_t L;
+    int32_t H;
+    int32_t nc;
+    int32_t softplus;
+    int32_t G;          // groups of B, C
+    int32_t hpg;        // heads per group
+};
+
+// dt and the inclusive in-chunk cumulative log-decay A*dt for the steps of chunk
+// c of head h; lane l owns steps l*SPL .. l*SPL+SPL-1 (SPL = Q/64). Steps past the
+// sequence get dt = 0. Returns the chunk total (the last cs) to every lane.
+template <int Q>
+__device__ __forceinline__ float head_dt_cs(const SSDK &p, int b, int h, int c, float (&dtv)[Q / 64],
+                                            float (&cs)[Q / 64]) {
+    constexpr int SPL = Q / 64;
+    const int lane = threadIdx.x & 63;
+    const float bias = p.dt_bias ? p.dt_bias[h] : 0.0f;
+    const float a = p.A[h];
+    float run = 0.0f;
+#pragma unroll
+    for (int i = 0; i < SPL; ++i) {
+        const int64_t tg = (int64_t)c * Q + lane * SPL + i;
+        float d = 0.0f;
+        if (tg < p.L) {
+            const float v = to_f32(p.dt[((int64_t)b * p.L + tg) * p.H + h]) + bias;
+            d = p.softplus ? softplus_f32(v) : v;
+        }
+        dtv[i] = d;
+        run += a * d;
+        cs[i] = run;
+    }
+    float incl = run;   // inclusive scan of lane totals
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const float u = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += u;
+    }
+    const float excl = incl - run;
+#pragma unroll
+    for (int i = 0; i < SPL; ++i) cs[i] += excl;
+    return __shfl(incl, 63, 64);
+}
+
+// position of chunk-local s (its block of 64 aside) in the permuted x rows
+__device__ __forceinline__ int perm_s(int sl) {
+    return ((sl >> 5) << 5) | (((sl >> 2) & 3) << 3) | (((sl >> 4) & 1) << 2) | (sl & 3);
+}
+
+}  // namespace ssm

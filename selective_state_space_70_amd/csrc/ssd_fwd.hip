@@ -37,106 +37,22 @@
 
 #include "device_common.h"
 #include "internal.h"
+#include "ssd_common.h"
 
 namespace ssm {
 namespace {
 
-constexpr int kP = 64;          // head dimension handled by these kernels
-constexpr int kThreads = 256;   // 4 waves
-
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(4))) float f32x4;
-typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
-typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
-
-__device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4 &v) { return __builtin_bit_cast(bf16x8, v); }
-
-// 16 bytes through a buffer resource (0 outside its range)
-__device__ __forceinline__ u32x4 load16(rsrc_t r, uint32_t voff) {
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
-}
-
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) { return pack_bf16x2(lo, hi); }
-
-// (lo halves of a, b) and (hi halves of a, b) as packed bf16 pairs.
-__device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) {
-    return __builtin_amdgcn_perm(b, a, 0x05040100u);
-}
-__device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) {
-    return __builtin_amdgcn_perm(b, a, 0x07060302u);
-}
-
-// Write a 4 x 8 block (4 rows, 8 columns, each row one u32x4 of packed bf16) to
-// LDS transposed: T[c][r0 .. r0+3] for the 8 columns c0 .. c0+7.
-__device__ __forceinline__ void store_transposed(const u32x4 (&r)[4], uint16_t *T, int ldt, int c0,
-                                                 int r0) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const u32x2 lo = u32x2{lo_pair(r[0][j], r[1][j]), lo_pair(r[2][j], r[3][j])};
-        const u32x2 hi = u32x2{hi_pair(r[0][j], r[1][j]), hi_pair(r[2][j], r[3][j])};
-        *(u32x2 *)&T[(c0 + 2 * j) * ldt + r0] = lo;
-        *(u32x2 *)&T[(c0 + 2 * j + 1) * ldt + r0] = hi;
-    }
-}
-
-struct SSDK {
-    const uint16_t *x, *dt, *Bm, *Cm, *z;
-    const float *dt_bias, *A, *Dskip, *h0;
-    uint16_t *y;
-    float *h_final;
-    float *states;      // fp32 [B][nc][H][P][N]: state of each chunk from zero
-    uint16_t *sin;      // bf16 [B][nc][H][P][N]: state entering each chunk
-    float *decay;       // fp32 [B][H][nc]: exp(cs_end) of each chunk
-    int64_t L;
-    int32_t H;
-    int32_t nc;
-    int32_t softplus;
-    int32_t G;          // groups of B, C
-    int32_t hpg;        // heads per group
-};
-
-// dt and the inclusive in-chunk cumulative log-decay A*dt for the steps of chunk
-// c of head h; lane l owns steps l*SPL .. l*SPL+SPL-1 (SPL = Q/64). Steps past the
-// sequence get dt = 0. Returns the chunk total (the last cs) to every lane.
-template <int Q>
-__device__ __forceinline__ float head_dt_cs(const SSDK &p, int b, int h, int c, float (&dtv)[Q / 64],
-                                            float (&cs)[Q / 64]) {
-    constexpr int SPL = Q / 64;
-    const int lane = threadIdx.x & 63;
-    const float bias = p.dt_bias ? p.dt_bias[h] : 0.0f;
-    const float a = p.A[h];
-    float run = 0.0f;
-#pragma unroll
-    for (int i = 0; i < SPL; ++i) {
-        const int64_t tg = (int64_t)c * Q + lane * SPL + i;
-        float d = 0.0f;
-        if (tg < p.L) {
-            const float v = to_f32(p.dt[((int64_t)b * p.L + tg) * p.H + h]) + bias;
-            d = p.softplus ? softplus_f32(v) : v;
-        }
-        dtv[i] = d;
-        run += a * d;
-        cs[i] = run;
-    }
-    float incl = run;   // inclusive scan of lane totals
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const float u = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += u;
-    }
-    const float excl = incl - run;
-#pragma unroll
-    for (int i = 0; i < SPL; ++i) cs[i] += excl;
-    return __shfl(incl, 63, 64);
-}
-
 // ---------------------------------------------------------------- chunk states
-template <int N, int Q>
-__global__ __launch_bounds__(kThreads, N > 128 ? 1 : 2) void ssd_chunk_state_kernel(const SSDK p) {
+// MODE 0: S_c = sum_s exp(cs_end - cs_s) dt_s B_s (x) x_s, the weighted x rounded to
+//         bf16 (the forward);
+// MODE 1: the same with the weighted x split into bf16 hi + lo parts, two products
+//         (fp32-grade chunk states, for the gradient pass);
+// MODE 2: R_c = sum_t exp(cs_t) B_t (x) (x_t + xlo_t), split like MODE 1, no decay
+//         output (with x + xlo = dy silu(z) and B = C this is the adjoint aggregate
+//         of the gradient pass).
+template <int N, int Q, int MODE>
+__global__ __launch_bounds__(kThreads, (N > 128 || MODE != 0) ? 1 : 2) void ssd_chunk_state_kernel(const SSDK p) {
+    constexpr bool SPLIT = MODE != 0;
     constexpr int SB = 64;                    // time rows staged per step
     constexpr int LDT = SB + 8;               // padded LDS row (bf16)
     constexpr int NPASS = N > 128 ? N / 128 : 1;
@@ -146,6 +62,7 @@ __global__ __launch_bounds__(kThreads, N > 128 ? 1 : 2) void ssd_chunk_state_ker
     __shared__ float wsh[4][Q];
     __shared__ __attribute__((aligned(16))) uint16_t BT[NP][LDT];
     __shared__ __attribute__((aligned(16))) uint16_t XT[4][kP][LDT];
+    __shared__ __attribute__((aligned(16))) uint16_t XL[SPLIT ? 4 : 1][SPLIT ? kP : 1][SPLIT ? LDT : 8];
 
     const int c = blockIdx.x, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -162,8 +79,10 @@ __global__ __launch_bounds__(kThreads, N > 128 ? 1 : 2) void ssd_chunk_state_ker
         const float cs_end = head_dt_cs<Q>(p, b, hc, c, dtv, cs);
 #pragma unroll
         for (int i = 0; i < SPL; ++i)
-            wsh[wv][lane * SPL + i] = fast_exp2((cs_end - cs[i]) * kLog2e) * dtv[i];
-        if (lane == 0 && head_ok) p.decay[((int64_t)b * p.H + h) * p.nc + c] = fast_exp2(cs_end * kLog2e);
+            wsh[wv][lane * SPL + i] = MODE == 2 ? fast_exp2(cs[i] * kLog2e)
+                                                : fast_exp2((cs_end - cs[i]) * kLog2e) * dtv[i];
+        if (MODE != 2 && lane == 0 && head_ok)
+            p.decay[((int64_t)b * p.H + h) * p.nc + c] = fast_exp2(cs_end * kLog2e);
     }
 
     // One 64-row block of B (this pass's states) and of x (this wave's head) is
@@ -172,7 +91,8 @@ __global__ __launch_bounds__(kThreads, N > 128 ? 1 : 2) void ssd_chunk_state_ker
     // 8-byte writes of 16 lanes cover all banks.
     const int GN = p.G * N;
     const int sg = tid & 15, co = tid >> 4;           // B block of this thread: 4 rows x 8 states
-    u32x4 breg[4], xreg[2][4];
+    u32x4 breg[4], xreg[2][4], xlreg[MODE == 2 ? 2 : 1][4];
+    const bool has_lo = MODE == 2 && p.xlo != nullptr;
     auto fetch = [&](int pass, int s0) {
         const int rows = (int)std::max<int64_t>(0, std::min<int64_t>(SB, p.L - t_base - s0));
         const rsrc_t rb = make_rsrc(p.Bm + (((int64_t)b * p.L + t_base + s0) * p.G + g) * N + pass * NP,
@@ -188,21 +108,46 @@ __global__ __launch_bounds__(kThreads, N > 128 ? 1 : 2) void ssd_chunk_state_ker
             for (int i = 0; i < 4; ++i)
                 xreg[k][i] = load16(rx, (uint32_t)(((xg * 4 + i) * p.H * kP + po * 8) * 2));
         }
+        if constexpr (MODE == 2) {
+            if (has_lo) {
+                const rsrc_t rl = make_rsrc(p.xlo + (((int64_t)b * p.L + t_base + s0) * p.H + hc) * kP,
+                                            (uint32_t)(rows * p.H * kP * 2));
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    const int blk = lane + 64 * k, xg = blk & 15, po = blk >> 4;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        xlreg[k][i] = load16(rl, (uint32_t)(((xg * 4 + i) * p.H * kP + po * 8) * 2));
+                }
+            }
+        }
     };
     auto stash = [&](int s0) {
         if (co < NP / 8) store_transposed(breg, &BT[0][0], LDT, co * 8, sg * 4);
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             const int blk = lane + 64 * k, xg = blk & 15, po = blk >> 4;
-            u32x4 r[4];
+            u32x4 r[4], rl[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float w = wsh[wv][s0 + xg * 4 + i];
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    r[i][e] = pack_bf16(bf16_lo(xreg[k][i][e]) * w, bf16_hi(xreg[k][i][e]) * w);
+                for (int e = 0; e < 4; ++e) {
+                    float x0 = bf16_lo(xreg[k][i][e]), x1 = bf16_hi(xreg[k][i][e]);
+                    if constexpr (MODE == 2) {
+                        if (has_lo) {
+                            x0 += bf16_lo(xlreg[k][i][e]);
+                            x1 += bf16_hi(xlreg[k][i][e]);
+                        }
+                    }
+                    const float v0 = x0 * w, v1 = x1 * w;
+                    r[i][e] = pack_bf16(v0, v1);
+                    if constexpr (SPLIT)
+                        rl[i][e] = pack_bf16(v0 - bf16_lo(r[i][e]), v1 - bf16_hi(r[i][e]));
+                }
             }
             store_transposed(r, &XT[wv][0][0], LDT, po * 8, xg * 4);
+            if constexpr (SPLIT) store_transposed(rl, &XL[wv][0][0], LDT, po * 8, xg * 4);
         }
     };
 
@@ -234,6 +179,16 @@ __global__ __launch_bounds__(kThreads, N > 128 ? 1 : 2) void ssd_chunk_state_ker
                     const bf16x8 afr = as_bf16x8(*(const u32x4 *)&BT[i * 16 + r16][sk]);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(afr, bfr[j], acc[i][j]);
+                }
+                if constexpr (SPLIT) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) bfr[j] = as_bf16x8(*(const u32x4 *)&XL[wv][j * 16 + r16][sk]);
+#pragma unroll
+                    for (int i = 0; i < NT; ++i) {
+                        const bf16x8 afr = as_bf16x8(*(const u32x4 *)&BT[i * 16 + r16][sk]);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(afr, bfr[j], acc[i][j]);
+                    }
                 }
             }
         }
@@ -282,6 +237,9 @@ __global__ __launch_bounds__(256) void ssd_state_pass_kernel(const SSDK p, int N
         for (int u = 0; u < K; ++u) {
             if (c0 + u < p.nc) {
                 *(u32x2 *)(p.sin + base + (c0 + u) * cstride) = u32x2{pack_bf16(s[0], s[1]), pack_bf16(s[2], s[3])};
+                // fp32 copy; where it aliases the chunk states this overwrites a
+                // value this thread has already loaded
+                if (p.sin32) *(f32x4 *)(p.sin32 + base + (c0 + u) * cstride) = s;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) s[e] = fmaf(dc[u], s[e], sc[u][e]);
             }
@@ -317,12 +275,9 @@ struct OutCfg {
     static constexpr int HG = 2;   // heads per workgroup
 };
 
-// position of chunk-local s (its block of 64 aside) in the permuted x rows
-__device__ __forceinline__ int perm_s(int sl) {
-    return ((sl >> 5) << 5) | (((sl >> 2) & 3) << 3) | (((sl >> 4) & 1) << 2) | (sl & 3);
-}
-
-template <int N, int Q>
+// F32OUT: write the pre-gate output (C S + D x) in fp32 to y32 instead of the gated
+// bf16 y (the recompute the gradient pass needs for dz).
+template <int N, int Q, bool F32OUT>
 __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_out_kernel(const SSDK p, int nhg, int ngroups) {
     constexpr int HG = OutCfg<N>::HG;
     constexpr int TBS = Q / 64;               // 64-row time blocks per chunk
@@ -584,7 +539,7 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_out_kernel(const SSDK p
     // head's tile then goes through the wave's own LDS rows so that a lane writes
     // rows of 8 bf16.
     u32x4 zreg[HG][2];
-    if (p.z) {
+    if (!F32OUT && p.z) {
 #pragma unroll
         for (int j = 0; j < HG; ++j)
 #pragma unroll
@@ -621,7 +576,11 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_out_kernel(const SSDK p
             const int t = t0 + row;
             const f32x4 o0 = *(const f32x4 *)&Ot[wv][row][c8];
             const f32x4 o1 = *(const f32x4 *)&Ot[wv][row][c8 + 4];
-            if (t < T) {
+            if (F32OUT && t < T) {
+                float *dst = p.y32 + (((int64_t)b * p.L + t_base + t) * p.H + h) * kP + c8;
+                *(f32x4 *)dst = o0;
+                *(f32x4 *)(dst + 4) = o1;
+            } else if (t < T) {
                 const float o[8] = {o0[0], o0[1], o0[2], o0[3], o1[0], o1[1], o1[2], o1[3]};
                 u32x4 outv;
 #pragma unroll
@@ -647,7 +606,7 @@ __global__ __launch_bounds__(256) void ssd_copy_state_kernel(const float *h0, fl
 
 template <int N, int Q>
 void launch_nq(const SSDK &k, int batch, hipStream_t s) {
-    hipLaunchKernelGGL((ssd_chunk_state_kernel<N, Q>), dim3((unsigned)k.nc, (unsigned)(k.G * ((k.hpg + 3) / 4)), (unsigned)batch),
+    hipLaunchKernelGGL((ssd_chunk_state_kernel<N, Q, 0>), dim3((unsigned)k.nc, (unsigned)(k.G * ((k.hpg + 3) / 4)), (unsigned)batch),
                        dim3(kThreads), 0, s, k);
     const int64_t total = (int64_t)batch * k.H * kP * N / 4;
     hipLaunchKernelGGL(ssd_state_pass_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
@@ -655,7 +614,7 @@ void launch_nq(const SSDK &k, int batch, hipStream_t s) {
     const int nhg = (k.hpg + OutCfg<N>::HG - 1) / OutCfg<N>::HG;
     const int64_t ngroups = (int64_t)batch * k.nc * k.G * nhg;
     const int64_t nblocks = Q == 64 ? ngroups : (ngroups + 7) / 8 * 8 * (Q / 64);
-    hipLaunchKernelGGL((ssd_chunk_out_kernel<N, Q>), dim3((unsigned)nblocks), dim3(kThreads), 0, s, k, nhg,
+    hipLaunchKernelGGL((ssd_chunk_out_kernel<N, Q, false>), dim3((unsigned)nblocks), dim3(kThreads), 0, s, k, nhg,
                        (int)ngroups);
 }
 
@@ -668,7 +627,41 @@ void launch_n(const SSDK &k, int batch, int Q, hipStream_t s) {
     }
 }
 
+// pieces of the forward for the gradient pass
+template <int N, int Q>
+void recompute_nq(const SSDK &k, int batch, int what, hipStream_t s) {
+    const dim3 cs_grid((unsigned)k.nc, (unsigned)(k.G * ((k.hpg + 3) / 4)), (unsigned)batch);
+    if (what == 0) {          // split-precision chunk states, then the entering states
+        hipLaunchKernelGGL((ssd_chunk_state_kernel<N, Q, 1>), cs_grid, dim3(kThreads), 0, s, k);
+        const int64_t total = (int64_t)batch * k.H * kP * N / 4;
+        hipLaunchKernelGGL(ssd_state_pass_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
+                           k, N, total);
+    } else if (what == 1) {   // fp32 pre-gate output
+        const int nhg = (k.hpg + OutCfg<N>::HG - 1) / OutCfg<N>::HG;
+        const int64_t ngroups = (int64_t)batch * k.nc * k.G * nhg;
+        const int64_t nblocks = Q == 64 ? ngroups : (ngroups + 7) / 8 * 8 * (Q / 64);
+        hipLaunchKernelGGL((ssd_chunk_out_kernel<N, Q, true>), dim3((unsigned)nblocks), dim3(kThreads), 0, s, k,
+                           nhg, (int)ngroups);
+    } else {                  // adjoint aggregates (exp(cs_t) weights)
+        hipLaunchKernelGGL((ssd_chunk_state_kernel<N, Q, 2>), cs_grid, dim3(kThreads), 0, s, k);
+    }
+}
+
+template <int N>
+void recompute_n(const SSDK &k, int batch, int Q, int what, hipStream_t s) {
+    switch (Q) {
+        case 64: recompute_nq<N, 64>(k, batch, what, s); break;
+        case 128: recompute_nq<N, 128>(k, batch, what, s); break;
+        default: recompute_nq<N, 256>(k, batch, what, s); break;
+    }
+}
+
 }  // namespace
+
+void ssd_recompute_launch(const SSDK &k, int batch, int Q, int N, int what, hipStream_t s) {
+    if (N == 64) recompute_n<64>(k, batch, Q, what, s);
+    else recompute_n<128>(k, batch, Q, what, s);
+}
 
 SSDPlan ssd_plan(const ssm_ssd_args &a) {
     SSDPlan pl{};

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_names():
     lib = _capi.lib()
-    assert lib.ssm_abi_version() == _capi.ABI_VERSION == 4
+    assert lib.ssm_abi_version() == _capi.ABI_VERSION == 5
     names = [lib.ssm_status_str(s).decode() for s in range(4)]
     assert names == ["SSM_OK", "SSM_EINVAL", "SSM_ENOTSUP", "SSM_EHIP"]
     assert lib.ssm_status_str(99).decode() == "SSM_UNKNOWN"
@@ -295,3 +295,45 @@ def test_bwd_workspace():
     # chunks of 64 steps: aggregates plus entering states and adjoints per (b, chunk, d, n)
     assert need >= 2 * 8 * 32 * 1536 * 16 * 4
     assert lib.selective_scan_bwd_workspace_bytes(ctypes.byref(bwd_args(dstate=8))) == 0
+
+
+def ssd_bwd_args(**kw):
+    a = _capi.SSDBwdArgs()
+    a.batch, a.seqlen, a.nheads, a.headdim, a.dstate, a.chunk = 2, 300, 8, 64, 128, 256
+    a.dtype, a.dt_softplus = _capi.SSM_BF16, 1
+    for name in ("x", "dt", "dt_bias", "A", "Bm", "Cm", "Dskip", "z", "h0", "dy", "dh_final",
+                 "dx", "ddt", "dz", "dB", "dC", "dA", "dDskip", "ddt_bias", "dh0"):
+        setattr(a, name, FAKE)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,want", [
+    ({"dy": None}, _capi.SSM_EINVAL),
+    ({"dA": None}, _capi.SSM_EINVAL),
+    ({"dz": None}, _capi.SSM_EINVAL),                     # z given, dz missing
+    ({"dB": FAKE + 4}, _capi.SSM_EINVAL),                 # fp32 outputs are written as 16-byte vectors
+    ({"dx": FAKE + 2}, _capi.SSM_EINVAL),
+    ({"dstate": 256}, _capi.SSM_ENOTSUP),
+    ({"headdim": 32}, _capi.SSM_ENOTSUP),
+    ({"chunk": 100}, _capi.SSM_ENOTSUP),
+    ({"dtype": _capi.SSM_F32}, _capi.SSM_ENOTSUP),
+    ({"ngroups": 3}, _capi.SSM_EINVAL),                   # 8 heads in 3 groups
+    ({}, _capi.SSM_EINVAL),                               # needs workspace
+])
+def test_ssd_bwd_validation(kw, want):
+    assert _capi.lib().ssd_chunked_bwd(ctypes.byref(ssd_bwd_args(**kw)), None) == want
+
+
+def test_ssd_bwd_workspace():
+    lib = _capi.lib()
+    a = ssd_bwd_args(batch=2, seqlen=8192, nheads=64)
+    need = lib.ssd_chunked_bwd_workspace_bytes(ctypes.byref(a))
+    # fp32 entering states and chunk-end adjoints per (b, chunk, h, p, n), the
+    # fp32 pre-gate output and dyc (hi, lo) with z
+    st = 2 * 32 * 64 * 64 * 128
+    assert need >= st * 8 + 2 * 8192 * 64 * 64 * 8
+    a.z = None
+    assert lib.ssd_chunked_bwd_workspace_bytes(ctypes.byref(a)) < need
+    assert lib.ssd_chunked_bwd_workspace_bytes(ctypes.byref(ssd_bwd_args(dstate=256))) == 0
