@@ -85,6 +85,19 @@ def ssd_alg_flops(cfg) -> float:
     return cb + diag + states + off
 
 
+def ssd_bwd_alg_flops(cfg) -> float:
+    """Useful matrix flops of the chunked SSD gradients (single-precision count,
+    causal halves of the Q x Q products): per (batch, chunk, head) the tiles
+    (dyc_t.x_s), dx += M1 dyc, dB += M2 C, dC += M3 B (Q^2 P, Q^2 P, Q^2 N, Q^2 N)
+    and the chunk-state products (recomputed chunk states, adjoint aggregates, the
+    dx, dB, dC chunk-end terms: 5 x 2 Q N P); (C_t.B_s) once per group."""
+    Q = cfg.chunk
+    nch = math.ceil(cfg.seqlen / Q)
+    b, H, P, N = cfg.batch, cfg.nheads, cfg.headdim, cfg.dstate
+    per_head = Q * Q * (2 * P + 2 * N) + 5 * 2.0 * Q * N * P
+    return b * nch * (H * per_head + Q * Q * N)
+
+
 def _device_inputs(inp, torch, dev):
     td = torch.bfloat16 if inp["dtype"] == "bf16" else torch.float32
     out = {}
@@ -329,6 +342,32 @@ def cpu_baseline(key, budget_s=10.0):
                       "%.2f s per run" % (key, cfg.batch * cfg.dim, cfg.seqlen, runs, per)}
 
 
+def time_ssd_bwd(steps, warmup, torch, ssm):
+    """Gradients of the SSD workload (ssd_chunked_bwd) with rotated inputs."""
+    cfg = workloads.CONFIGS["S5"]
+    dev = torch.device("cuda:0")
+    base = workloads.make_inputs("S5")
+    nsets = 2
+    sets = []
+    g = torch.Generator(device=dev)
+    g.manual_seed(12)
+    for i in range(nsets):
+        t = _device_inputs(base, torch, dev)
+        if i:
+            t["x"] = torch.roll(t["x"], shifts=97 * i, dims=1).contiguous()
+        t["dy"] = torch.randn(t["x"].shape, generator=g, device=dev).to(t["x"].dtype)
+        sets.append(t)
+
+    def call(i):
+        t = sets[i]
+        ssm.ssd_chunked_bwd(t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], t["dy"], t["Dskip"], None,
+                            t["dt_bias"], None, None, chunk=cfg.chunk)
+
+    ms = _time_rotating(call, nsets, steps, warmup, torch)
+    tf = ssd_bwd_alg_flops(cfg) / ms / 1e9
+    return {"ms": round(ms, 4), "TFLOP/s": round(tf, 1), "mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -369,6 +408,7 @@ def main():
     if args.next_only:
         out = time_next_rows(args.steps, args.warmup, torch, ssm)
         out["bwd_S2"] = time_bwd("S2", args.steps, args.warmup, torch, ssm)
+        out["bwd_S5"] = time_ssd_bwd(args.steps, args.warmup, torch, ssm)
         print(json.dumps(out), flush=True)
         return
 
@@ -428,6 +468,7 @@ def main():
                        "mfma_frac": round(ssd_alg_flops(c5) / m5 / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4)}
         extra.update(time_next_rows(max(10, args.steps), 3, torch, ssm))
         extra["bwd_S2"] = time_bwd("S2", max(10, args.steps // 2), 2, torch, ssm)
+        extra["bwd_S5"] = time_ssd_bwd(max(10, args.steps // 2), 2, torch, ssm)
         line["extra"] = extra
         print(json.dumps(extra), file=sys.stderr)
     if not args.no_cpu_baseline:
