@@ -46,7 +46,7 @@
 namespace ssm {
 namespace {
 
-constexpr int kHsCol = 4;   // heads per workgroup, column kernel (a dx accumulator each)
+constexpr int kHsCol = 2;   // heads per workgroup, column kernel (a dx accumulator each)
 constexpr int kHsRow = 4;   // heads per workgroup, row kernel
 
 struct BwdK {
@@ -100,58 +100,41 @@ __device__ __forceinline__ void split8(const f32x4 &a, const f32x4 &b, u32x4 &hi
 }
 
 // ---------------------------------------------------------------- LDS staging
-// 64 rows x W bf16 columns (row stride rs elements in global) into LDS rows of ld
-// elements; rows at or past `rows` read as 0.
-template <int W>
-__device__ __forceinline__ void stage_nat(const uint16_t *src, int64_t rs, int rows, uint16_t *dst, int ld) {
-    constexpr int VPR = W / 8;                    // 16-byte vectors per row
-    const rsrc_t r = make_rsrc(src, (uint32_t)(std::max(0, rows) * rs * 2));
+// One 4 x 8 block of a bf16 tile (rows 4 rg .. +3 at row stride rs, columns gcol ..
+// +7) through a buffer resource (rows past its range read as 0), written to LDS in
+// natural layout nat[row][lcol ..] and/or transposed tr[lcol + c][perm_s(row)].
+__device__ __forceinline__ void block_both(rsrc_t r, int64_t rs, int rg, int gcol, uint16_t *nat, int ld,
+                                           uint16_t *tr, int ldt, int lcol) {
+    u32x4 v[4];
 #pragma unroll
-    for (int i = 0; i < 64 * VPR / 256; ++i) {
-        const int v = threadIdx.x + 256 * i, row = v / VPR, cv = v % VPR;
-        *(u32x4 *)&dst[row * ld + cv * 8] = load16(r, (uint32_t)((row * rs + cv * 8) * 2));
+    for (int i = 0; i < 4; ++i) v[i] = load16(r, (uint32_t)(((rg * 4 + i) * rs + gcol) * 2));
+    if (nat) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *(u32x4 *)&nat[(rg * 4 + i) * ld + lcol] = v[i];
     }
+    if (tr) store_transposed(v, tr, ldt, lcol, perm_s(rg * 4));
 }
-// The same block transposed, T[col][perm_s(row)], in 4 x 8 register blocks.
-template <int W>
-__device__ __forceinline__ void stage_tr(const uint16_t *src, int64_t rs, int rows, uint16_t *T, int ldt) {
-    constexpr int CB = W / 8;                     // column blocks of 8
-    const rsrc_t r = make_rsrc(src, (uint32_t)(std::max(0, rows) * rs * 2));
-    for (int blk = threadIdx.x; blk < 16 * CB; blk += 256) {
-        const int rg = blk % 16, cg = blk / 16;   // consecutive threads: consecutive row groups
-        u32x4 v[4];
+// One 4 x 8 block of an fp32 [64][rs] tile (rows 4 rg .., columns 8 cg ..) as bf16
+// hi and lo parts, natural [row][col] and/or transposed [col][row] (rows in order).
+__device__ __forceinline__ void block_split_both(const float *src, int64_t rs, int rg, int cg, uint16_t *nat_hi,
+                                                 uint16_t *nat_lo, int ld, uint16_t *tr_hi, uint16_t *tr_lo,
+                                                 int ldt) {
+    u32x4 hi[4], lo[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = load16(r, (uint32_t)(((rg * 4 + i) * rs + cg * 8) * 2));
-        store_transposed(v, T, ldt, cg * 8, perm_s(rg * 4));
+    for (int i = 0; i < 4; ++i) {
+        const float *q = src + (rg * 4 + i) * rs + cg * 8;
+        split8(*(const f32x4 *)q, *(const f32x4 *)(q + 4), hi[i], lo[i]);
     }
-}
-// An fp32 [64][W] block (row stride rs) as bf16 hi or lo part (PART 0 / 1), either
-// natural [row][col] (TR false) or transposed [col][row] (TR true, rows in order).
-template <int W, int PART, bool TR>
-__device__ __forceinline__ void stage_split(const float *src, int64_t rs, uint16_t *dst, int ld) {
-    constexpr int CB = W / 8;
-    if constexpr (!TR) {
-        for (int v = threadIdx.x; v < 64 * CB; v += 256) {
-            const int row = v / CB, cg = v % CB;
-            const f32x4 a = *(const f32x4 *)(src + row * rs + cg * 8);
-            const f32x4 b = *(const f32x4 *)(src + row * rs + cg * 8 + 4);
-            u32x4 hi, lo;
-            split8(a, b, hi, lo);
-            *(u32x4 *)&dst[row * ld + cg * 8] = PART ? lo : hi;
-        }
-    } else {
-        for (int blk = threadIdx.x; blk < 16 * CB; blk += 256) {
-            const int rg = blk % 16, cg = blk / 16;
-            u32x4 v[4];
+    if (nat_hi) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float *q = src + (rg * 4 + i) * rs + cg * 8;
-                u32x4 hi, lo;
-                split8(*(const f32x4 *)q, *(const f32x4 *)(q + 4), hi, lo);
-                v[i] = PART ? lo : hi;
-            }
-            store_transposed(v, dst, ld, cg * 8, rg * 4);
+        for (int i = 0; i < 4; ++i) {
+            *(u32x4 *)&nat_hi[(rg * 4 + i) * ld + cg * 8] = hi[i];
+            *(u32x4 *)&nat_lo[(rg * 4 + i) * ld + cg * 8] = lo[i];
         }
+    }
+    if (tr_hi) {
+        store_transposed(hi, tr_hi, ldt, cg * 8, rg * 4);
+        store_transposed(lo, tr_lo, ldt, cg * 8, rg * 4);
     }
 }
 
@@ -303,9 +286,10 @@ __global__ __launch_bounds__(256) void ssd_bwd_state_pass_kernel(const BwdK k, i
 
 // ---------------------------------------------------------------- row kernel
 // One workgroup per (b, chunk, group, slice of kHsRow heads, 64-row block tb of t);
-// wave w owns rows t = 64 tb + 16 w .. +15. For every block of s <= tb the score
-// tile (C_t.B_s) is formed once and reused by the heads of the slice; per head the
-// tile (x_s.dyc_t) gives W (summed over s into q) and, weighted, the A operand of
+// wave w owns rows t = 64 tb + 16 w .. +15. Each block of s <= tb is staged once
+// (B natural and transposed from one load, x of every head of the slice); the
+// score tile (B_s.C_t) is formed once and reused by the heads; per head the tile
+// (x_s.dyc_t) gives W (summed over s into q) and, weighted, the A operand of
 // dC += M3 B. Then per head the entering-state term exp(cs_t) dyc_t Sin (split
 // operands) adds to dC and, dotted with C_t, to q.
 template <int N, int Q, bool SPLIT>
@@ -313,14 +297,14 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_bwd_row_kernel(const BwdK k) 
     constexpr int HS = kHsRow;
     constexpr int TBS = Q / 64, KN = N / 32, NT = N / 16;
     constexpr int LDB = N + 8, LDT = 64 + 8, LDX = kP + 8;
-    constexpr int MAIN_BYTES = (64 * LDB + N * LDT + 64 * LDX) * 2;
+    constexpr int MAIN_BYTES = (64 * LDB + N * LDT + HS * 64 * LDX) * 2;
     constexpr int END_BYTES = (2 * N * LDT + 64 * LDB) * 2;
     __shared__ float cs2[HS][Q], dts[HS][Q];
     __shared__ float qsh[4][16];
     __shared__ __attribute__((aligned(16))) uint8_t ubuf[std::max(MAIN_BYTES, END_BYTES)];
     uint16_t *Bn = reinterpret_cast<uint16_t *>(ubuf);          // [64][LDB] B rows of the s block
     uint16_t *BT = Bn + 64 * LDB;                                  // [N][LDT] B^T, s permuted
-    uint16_t *Xn = BT + N * LDT;                                   // [64][LDX] x rows (one head)
+    uint16_t *Xn = BT + N * LDT;                                   // [HS][64][LDX] x rows per head
     uint16_t *ST = reinterpret_cast<uint16_t *>(ubuf);           // [2][N][LDT] Sin^T hi, lo
     uint16_t *Cn = ST + 2 * N * LDT;                               // [64][LDB] C rows of the t block
 
@@ -349,7 +333,7 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_bwd_row_kernel(const BwdK k) 
 #pragma unroll
         for (int kk = 0; kk < KN; ++kk) cfr[kk] = frag(rc, (uint32_t)((r16 * GN + 32 * kk + 8 * kb) * 2));
     }
-    // dyc of row t0 + r16 for head j (k = p): the B operand of x_s . dyc_t and the
+    // dyc of row t0 + r16 for head h (k = p): the B operand of x_s . dyc_t and the
     // A operand of dyc_t Sin
     const rsrc_t rdh = make_rsrc(k.dych + dbase + (int64_t)t0 * xs, (uint32_t)(std::max(0, T - t0) * xs * 2));
     const rsrc_t rdl = make_rsrc(SPLIT ? k.dycl + dbase + (int64_t)t0 * xs : k.dych, SPLIT ? (uint32_t)(std::max(0, T - t0) * xs * 2) : 0u);
@@ -375,8 +359,19 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_bwd_row_kernel(const BwdK k) 
         const int s0 = sb * 64;
         const bool diag = sb == tb;
         __syncthreads();
-        stage_nat<N>(Bbase + (int64_t)s0 * GN, GN, T - s0, Bn, LDB);
-        stage_tr<N>(Bbase + (int64_t)s0 * GN, GN, T - s0, BT, LDT);
+        {   // B block (natural + transposed from one load) and x of every head
+            const rsrc_t rb = make_rsrc(Bbase + (int64_t)s0 * GN, (uint32_t)(std::max(0, T - s0) * GN * 2));
+            for (int blk = tid; blk < 16 * (N / 8); blk += kThreads)
+                block_both(rb, GN, blk & 15, (blk >> 4) * 8, Bn, LDB, BT, LDT, (blk >> 4) * 8);
+            const rsrc_t rx = make_rsrc(Xbase + (int64_t)s0 * xs + hfirst * kP,
+                                        (uint32_t)(std::max(0, T - s0) * xs * 2));
+#pragma unroll
+            for (int i = 0; i < HS * 64 * 8 / kThreads; ++i) {
+                const int v = tid + kThreads * i, j = v >> 9, row = (v >> 3) & 63, cv = v & 7;
+                if (j < nh)
+                    *(u32x4 *)&Xn[(j * 64 + row) * LDX + cv * 8] = load16(rx, (uint32_t)((row * xs + j * kP + cv * 8) * 2));
+            }
+        }
         __syncthreads();
         // (B_s . C_t): lane holds s = s0 + 16u + 4kb + i, t = t0 + r16
         f32x4 cb[4];
@@ -393,11 +388,9 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_bwd_row_kernel(const BwdK k) 
         for (int j = 0; j < HS; ++j) {
             if (j >= nh) break;                                       // uniform
             const int h = hfirst + j;
-            __syncthreads();
-            stage_nat<kP>(Xbase + (int64_t)s0 * xs + h * kP, xs, T - s0, Xn, LDX);
-            __syncthreads();
             bf16x8 fh[2], fl[2];
             load_dyc(h, fh, fl);
+            const uint16_t *X = Xn + j * 64 * LDX;
             // (x_s . dyc_t), same layout as cb
             f32x4 xd[4];
 #pragma unroll
@@ -406,7 +399,7 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_bwd_row_kernel(const BwdK k) 
                 if (!diag || u <= wv) {
 #pragma unroll
                     for (int kk = 0; kk < 2; ++kk) {
-                        const bf16x8 xa = as_bf16x8(*(const u32x4 *)&Xn[(16 * u + r16) * LDX + 32 * kk + 8 * kb]);
+                        const bf16x8 xa = as_bf16x8(*(const u32x4 *)&X[(16 * u + r16) * LDX + 32 * kk + 8 * kb]);
                         xd[u] = mfma16x16x32(xa, fh[kk], xd[u]);
                         if constexpr (SPLIT) xd[u] = mfma16x16x32(xa, fl[kk], xd[u]);
                     }
@@ -414,7 +407,8 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_bwd_row_kernel(const BwdK k) 
             }
             // M3[t,s] = Lm dt_s (x_s.dyc_t); W = M3 (B_s.C_t)
             const float ct = cs2[j][tl_row];
-            const float at = diag ? 1.0f : fast_exp2(ct - cs2[j][r]);
+            const float cr = cs2[j][r];
+            const float at = diag ? 1.0f : fast_exp2(ct - cr);
             float wacc = 0.0f;
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
@@ -425,7 +419,7 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_bwd_row_kernel(const BwdK k) 
                 for (int i = 0; i < 4; ++i) {
                     float lw;
                     if (diag) lw = sl + i <= tl_row ? fast_exp2(ct - cs4[i]) : 0.0f;
-                    else lw = at * fast_exp2(cs2[j][r] - cs4[i]);
+                    else lw = at * fast_exp2(cr - cs4[i]);
                     const float m = lw * dt4[i] * xd[u][i];
                     wacc = fmaf(m, cb[u][i], wacc);
                     xd[u][i] = m;
@@ -446,7 +440,11 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_bwd_row_kernel(const BwdK k) 
 
     // entering-state term, per head
     __syncthreads();
-    stage_nat<N>(Cbase + (int64_t)(tb * 64) * GN, GN, T - tb * 64, Cn, LDB);
+    {
+        const rsrc_t rc = make_rsrc(Cbase + (int64_t)(tb * 64) * GN, (uint32_t)(std::max(0, T - tb * 64) * GN * 2));
+        for (int blk = tid; blk < 16 * (N / 8); blk += kThreads)
+            block_both(rc, GN, blk & 15, (blk >> 4) * 8, Cn, LDB, nullptr, 0, (blk >> 4) * 8);
+    }
     float qv[HS][4];
 #pragma unroll
     for (int j = 0; j < HS; ++j) {
@@ -454,8 +452,8 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_bwd_row_kernel(const BwdK k) 
         const int h = hfirst + j;
         const float *sinh = k.sin32 + ((((int64_t)b * p.nc + c) * p.H + h) * kP) * N;
         if (j) __syncthreads();
-        stage_split<N, 0, true>(sinh, N, ST, LDT);
-        stage_split<N, 1, true>(sinh, N, ST + N * LDT, LDT);
+        for (int blk = tid; blk < 16 * (N / 8); blk += kThreads)
+            block_split_both(sinh, N, blk & 15, blk >> 4, nullptr, nullptr, 0, ST, ST + N * LDT, LDT);
         __syncthreads();
         bf16x8 fh[2], fl[2];
         load_dyc(h, fh, fl);
@@ -521,29 +519,32 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_bwd_row_kernel(const BwdK k) 
 
 // ---------------------------------------------------------------- column kernel
 // One workgroup per (b, chunk, group, slice of kHsCol heads, 64-row block sb of s);
-// wave w owns rows s = 64 sb + 16 w .. +15. For every block of t >= sb the score
-// tile (C_t.B_s) is formed once for the slice; per head the tile (dyc_t.x_s) gives
-// W (summed over t into dtdd) and, weighted, the A operands of dx += M1 dyc and
-// dB += M2 C. Then per head the chunk-end terms e_s B_s Gout and e_s x_s Gout
-// (split operands) complete dx, dd, dtdd and dB.
+// wave w owns rows s = 64 sb + 16 w .. +15. Each block of t >= sb is staged once
+// (C natural and transposed, dyc of every head of the slice natural and
+// transposed, each from one load); the score tile (C_t.B_s) is formed once for
+// the slice; per head the tile (dyc_t.x_s) gives W (summed over t into dd) and,
+// weighted, the A operands of dx += M1 dyc and dB += M2 C. Then per head the
+// chunk-end terms e_s B_s Gout and e_s x_s Gout (split Gout) complete dx, dd, dtdd
+// and dB.
 template <int N, int Q, bool SPLIT>
 __global__ __launch_bounds__(kThreads, 2) void ssd_bwd_col_kernel(const BwdK k) {
     constexpr int HS = kHsCol;
     constexpr int TBS = Q / 64, KN = N / 32, NT = N / 16;
     constexpr int LDB = N + 8, LDT = 64 + 8, LDX = kP + 8, LDO = kP + 4;
-    constexpr int MAIN_BYTES = (64 * LDB + N * LDT + 2 * 64 * LDX + kP * LDT) * 2;
-    constexpr int END_BYTES = (kP * LDB + N * LDT) * 2 + 4 * 16 * LDO * 4;
+    constexpr int MAIN_BYTES = (64 * LDB + N * LDT + HS * 64 * LDX * (SPLIT ? 2 : 1) + HS * kP * LDT) * 2;
+    constexpr int END_BYTES = (2 * kP * LDB + 2 * N * LDT) * 2;
+    static_assert(4 * 16 * LDO * 4 <= 2 * kP * LDB * 2, "output tiles alias Gout rows");
     __shared__ float cs2[HS][Q], dts[HS][Q];
     __shared__ float qsh[4][16];
     __shared__ __attribute__((aligned(16))) uint8_t ubuf[std::max(MAIN_BYTES, END_BYTES)];
     uint16_t *Cn = reinterpret_cast<uint16_t *>(ubuf);           // [64][LDB] C rows of the t block
     uint16_t *CT = Cn + 64 * LDB;                                  // [N][LDT] C^T, t permuted
-    uint16_t *Dh = CT + N * LDT;                                   // [64][LDX] dyc rows (hi), one head
-    uint16_t *Dl = Dh + 64 * LDX;                                  // [64][LDX] dyc rows (lo)
-    uint16_t *DT = Dl + 64 * LDX;                                  // [P][LDT] dyc^T (hi), t permuted
-    uint16_t *Gn = reinterpret_cast<uint16_t *>(ubuf);           // [P][LDB] Gout rows (one part)
-    uint16_t *GT = Gn + kP * LDB;                                  // [N][LDT] Gout^T (one part)
-    float *Ot = reinterpret_cast<float *>(GT + N * LDT);          // [4][16][LDO] output tiles
+    uint16_t *Dh = CT + N * LDT;                                   // [HS][64][LDX] dyc rows (hi)
+    uint16_t *DT = Dh + HS * 64 * LDX;                             // [HS][P][LDT] dyc^T (hi), t permuted
+    uint16_t *Dl = DT + HS * kP * LDT;                             // [HS][64][LDX] dyc rows (lo)
+    uint16_t *Gn = reinterpret_cast<uint16_t *>(ubuf);           // [2][P][LDB] Gout rows hi, lo
+    uint16_t *GT = Gn + 2 * kP * LDB;                              // [2][N][LDT] Gout^T hi, lo
+    float *Ot = reinterpret_cast<float *>(ubuf);                   // [4][16][LDO] output tiles (after G)
 
     const SSDK &p = k.f;
     const Tile tl = decode_tile(blockIdx.x, TBS, k.nsl_col, p.G, p.nc);
@@ -595,8 +596,28 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_bwd_col_kernel(const BwdK k) 
         if (tb0 >= T) break;                                          // uniform
         const bool diag = tb == sb;
         __syncthreads();
-        stage_nat<N>(Cbase + (int64_t)tb0 * GN, GN, T - tb0, Cn, LDB);
-        stage_tr<N>(Cbase + (int64_t)tb0 * GN, GN, T - tb0, CT, LDT);
+        {   // C block, and dyc of every head (natural and transposed; lo natural)
+            const rsrc_t rc = make_rsrc(Cbase + (int64_t)tb0 * GN, (uint32_t)(std::max(0, T - tb0) * GN * 2));
+            for (int blk = tid; blk < 16 * (N / 8); blk += kThreads)
+                block_both(rc, GN, blk & 15, (blk >> 4) * 8, Cn, LDB, CT, LDT, (blk >> 4) * 8);
+            const rsrc_t rd = make_rsrc(k.dych + dbase + (int64_t)tb0 * xs + hfirst * kP,
+                                        (uint32_t)(std::max(0, T - tb0) * xs * 2));
+            for (int blk = tid; blk < HS * 128; blk += kThreads) {
+                const int j = blk >> 7, rg = blk & 15, cg = (blk >> 4) & 7;
+                if (j < nh)
+                    block_both(rd, xs, rg, j * kP + cg * 8, Dh + j * 64 * LDX, LDX, DT + j * kP * LDT, LDT, cg * 8);
+            }
+            if constexpr (SPLIT) {
+                const rsrc_t rl = make_rsrc(k.dycl + dbase + (int64_t)tb0 * xs + hfirst * kP,
+                                            (uint32_t)(std::max(0, T - tb0) * xs * 2));
+#pragma unroll
+                for (int i = 0; i < HS * 64 * 8 / kThreads; ++i) {
+                    const int v = tid + kThreads * i, j = v >> 9, row = (v >> 3) & 63, cv = v & 7;
+                    if (j < nh)
+                        *(u32x4 *)&Dl[(j * 64 + row) * LDX + cv * 8] = load16(rl, (uint32_t)((row * xs + j * kP + cv * 8) * 2));
+                }
+            }
+        }
         __syncthreads();
         // (C_t.B_s): lane holds t = tb0 + 16u + 4kb + i, s = s0w + r16
         f32x4 cb[4];
@@ -613,11 +634,7 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_bwd_col_kernel(const BwdK k) 
         for (int j = 0; j < HS; ++j) {
             if (j >= nh) break;                                       // uniform
             const int h = hfirst + j;
-            __syncthreads();
-            stage_nat<kP>(k.dych + dbase + (int64_t)tb0 * xs + h * kP, xs, T - tb0, Dh, LDX);
-            if constexpr (SPLIT) stage_nat<kP>(k.dycl + dbase + (int64_t)tb0 * xs + h * kP, xs, T - tb0, Dl, LDX);
-            stage_tr<kP>(k.dych + dbase + (int64_t)tb0 * xs + h * kP, xs, T - tb0, DT, LDT);
-            __syncthreads();
+            const uint16_t *Dhj = Dh + j * 64 * LDX, *Dlj = Dl + j * 64 * LDX, *DTj = DT + j * kP * LDT;
             bf16x8 xf[2];
             load_x(h, xf);
             // (dyc_t.x_s), same layout as cb
@@ -628,46 +645,48 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_bwd_col_kernel(const BwdK k) 
                 if (!diag || u >= wv) {
 #pragma unroll
                     for (int kk = 0; kk < 2; ++kk) {
-                        dx4[u] = mfma16x16x32(as_bf16x8(*(const u32x4 *)&Dh[(16 * u + r16) * LDX + 32 * kk + 8 * kb]), xf[kk], dx4[u]);
+                        dx4[u] = mfma16x16x32(as_bf16x8(*(const u32x4 *)&Dhj[(16 * u + r16) * LDX + 32 * kk + 8 * kb]), xf[kk], dx4[u]);
                         if constexpr (SPLIT)
-                            dx4[u] = mfma16x16x32(as_bf16x8(*(const u32x4 *)&Dl[(16 * u + r16) * LDX + 32 * kk + 8 * kb]), xf[kk], dx4[u]);
+                            dx4[u] = mfma16x16x32(as_bf16x8(*(const u32x4 *)&Dlj[(16 * u + r16) * LDX + 32 * kk + 8 * kb]), xf[kk], dx4[u]);
                     }
                 }
             }
             // M1[s,t] = Lm (C_t.B_s), M2[s,t] = Lm dt_s (dyc_t.x_s); W / dt_s = Lm (dyc_t.x_s) (C_t.B_s)
             const float cs_s = cs2[j][sl_col];
             const float dts_s = dts[j][sl_col];
-            const float ws = diag ? 1.0f : fast_exp2(cs2[j][rr] - cs_s);
+            const float crr = cs2[j][rr];
+            const float ws = diag ? 1.0f : fast_exp2(crr - cs_s);
             float wacc = 0.0f;
-            f32x4 m1[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int tlc = tb0 + 16 * u + 4 * kb;
-                const f32x4 ct4 = *(const f32x4 *)&cs2[j][tlc];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float lw;
-                    if (diag) lw = tlc + i >= sl_col ? fast_exp2(ct4[i] - cs_s) : 0.0f;
-                    else lw = ws * fast_exp2(ct4[i] - cs2[j][rr]);
-                    m1[u][i] = lw * cb[u][i];
-                    const float m = lw * dx4[u][i];
-                    wacc = fmaf(m, cb[u][i], wacc);                    // W / dt_s
-                    dx4[u][i] = m * dts_s;
-                }
-            }
-            wcol[j] += wacc;
 #pragma unroll
             for (int a = 0; a < 2; ++a) {
                 if (diag && 32 * a + 31 < 16 * wv) continue;          // every t of this half is before every row
-                const bf16x8 f1 = afrag(m1[2 * a], m1[2 * a + 1]);
+                f32x4 m1[2];
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int u = 2 * a + hh;
+                    const int tlc = tb0 + 16 * u + 4 * kb;
+                    const f32x4 ct4 = *(const f32x4 *)&cs2[j][tlc];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float lw;
+                        if (diag) lw = tlc + i >= sl_col ? fast_exp2(ct4[i] - cs_s) : 0.0f;
+                        else lw = ws * fast_exp2(ct4[i] - crr);
+                        m1[hh][i] = lw * cb[u][i];
+                        const float m = lw * dx4[u][i];
+                        wacc = fmaf(m, cb[u][i], wacc);                // W / dt_s
+                        dx4[u][i] = m * dts_s;
+                    }
+                }
+                const bf16x8 f1 = afrag(m1[0], m1[1]);
                 const bf16x8 f2 = afrag(dx4[2 * a], dx4[2 * a + 1]);
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    dxa[j][q] = mfma16x16x32(f1, as_bf16x8(*(const u32x4 *)&DT[(16 * q + r16) * LDT + 32 * a + 8 * kb]), dxa[j][q]);
+                    dxa[j][q] = mfma16x16x32(f1, as_bf16x8(*(const u32x4 *)&DTj[(16 * q + r16) * LDT + 32 * a + 8 * kb]), dxa[j][q]);
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt)
                     db[nt] = mfma16x16x32(f2, as_bf16x8(*(const u32x4 *)&CT[(16 * nt + r16) * LDT + 32 * a + 8 * kb]), db[nt]);
             }
+            wcol[j] += wacc;
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -678,6 +697,10 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_bwd_col_kernel(const BwdK k) 
         if (j >= nh) break;                                           // uniform
         const int h = hfirst + j;
         const float *gh = k.gout + ((((int64_t)b * p.nc + c) * p.H + h) * kP) * N;
+        __syncthreads();
+        for (int blk = tid; blk < 16 * (N / 8); blk += kThreads)
+            block_split_both(gh, N, blk & 15, blk >> 4, Gn, Gn + kP * LDB, LDB, GT, GT + N * LDT, LDT);
+        __syncthreads();
         bf16x8 xf[2];
         load_x(h, xf);
         f32x4 xi[4], bi[NT];
@@ -687,27 +710,19 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_bwd_col_kernel(const BwdK k) 
         for (int nt = 0; nt < NT; ++nt) bi[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int part = 0; part < 2; ++part) {
-            __syncthreads();
-            if (part == 0) {
-                stage_split<N, 0, false>(gh, N, Gn, LDB);
-                stage_split<N, 0, true>(gh, N, GT, LDT);
-            } else {
-                stage_split<N, 1, false>(gh, N, Gn, LDB);
-                stage_split<N, 1, true>(gh, N, GT, LDT);
-            }
-            __syncthreads();
+            const uint16_t *G1 = Gn + part * kP * LDB, *G2 = GT + part * N * LDT;
             // B_s Gout^T: rows s = s0w + 4kb + i, p = 16q + r16
 #pragma unroll
             for (int q = 0; q < 4; ++q)
 #pragma unroll
                 for (int kk = 0; kk < KN; ++kk)
-                    xi[q] = mfma16x16x32(bfr[kk], as_bf16x8(*(const u32x4 *)&Gn[(16 * q + r16) * LDB + 32 * kk + 8 * kb]), xi[q]);
+                    xi[q] = mfma16x16x32(bfr[kk], as_bf16x8(*(const u32x4 *)&G1[(16 * q + r16) * LDB + 32 * kk + 8 * kb]), xi[q]);
             // x_s Gout: rows s, n = 16nt + r16
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk)
-                    bi[nt] = mfma16x16x32(xf[kk], as_bf16x8(*(const u32x4 *)&GT[(16 * nt + r16) * LDT + 32 * kk + 8 * kb]), bi[nt]);
+                    bi[nt] = mfma16x16x32(xf[kk], as_bf16x8(*(const u32x4 *)&G2[(16 * nt + r16) * LDT + 32 * kk + 8 * kb]), bi[nt]);
         }
         // rows s = s0w + 4kb + i
         const float cend = cs2[j][Q - 1];
@@ -748,7 +763,9 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_bwd_col_kernel(const BwdK k) 
             k.dtdd[o] = dts[j][s0w + lane] * ddv;
         }
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        // dx = dt_s (the tile) + D dyc_s, through the wave's LDS rows for 16-byte stores
+        // dx = dt_s (the tile) + D dyc_s, through the wave's LDS rows for 16-byte
+        // stores (the rows alias Gout: every wave is done with it first)
+        __syncthreads();
         float *ot = Ot + wv * 16 * LDO;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
