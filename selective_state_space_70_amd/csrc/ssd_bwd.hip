@@ -25,7 +25,8 @@
 //   recompute (ssd_fwd.hip): chunk states with the weighted x split into bf16
 //     hi + lo, the entering states in fp32 (and bf16), and with z the fp32
 //     pre-gate output for dz;
-//   gate: dD, and with z: dz and dyc as bf16 hi + lo;
+//   gate (with z): dD, dz and dyc as bf16 hi + lo (without z the column kernel
+//     sums dD);
 //   adjoint aggregates (ssd_fwd.hip): R_c = sum_t exp(cs_t) dyc_t^T C_t (split);
 //   reverse state pass: Gout_c, <Gout_c, S_end,c>, dh0;
 //   row kernel: dC (partial sums over a slice of heads) and q;
@@ -178,8 +179,8 @@ __device__ __forceinline__ void head_tables(const SSDK &p, int b, int c, int hfi
 }
 
 // ---------------------------------------------------------------- gate
-// One workgroup per (head, 256 rows of (b, t)); a lane owns 8 consecutive p.
-template <bool HAS_Z>
+// With z: one workgroup per (head, 256 rows of (b, t)); a lane owns 8 consecutive
+// p. dyc = dy silu(z) as bf16 hi + lo, dz = dy (y_pre) silu'(z), dDskip.
 __global__ __launch_bounds__(256) void ssd_bwd_gate_kernel(const BwdK k, int64_t rows) {
     const int h = blockIdx.x, H = k.f.H;
     const int v = threadIdx.x & 7, rsub = threadIdx.x >> 3;
@@ -190,38 +191,30 @@ __global__ __launch_bounds__(256) void ssd_bwd_gate_kernel(const BwdK k, int64_t
         const int64_t e = (row * H + h) * kP + v * 8;
         const u32x4 xv = *(const u32x4 *)(k.f.x + e);
         const u32x4 dv = *(const u32x4 *)(k.dy + e);
-        if constexpr (HAS_Z) {
-            const u32x4 zv = *(const u32x4 *)(k.f.z + e);
-            const f32x4 y0 = *(const f32x4 *)(k.f.y32 + e), y1 = *(const f32x4 *)(k.f.y32 + e + 4);
-            const float yv[8] = {y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
-            u32x4 hi, lo, dzv;
+        const u32x4 zv = *(const u32x4 *)(k.f.z + e);
+        const f32x4 y0 = *(const f32x4 *)(k.f.y32 + e), y1 = *(const f32x4 *)(k.f.y32 + e + 4);
+        const float yv[8] = {y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
+        u32x4 hi, lo, dzv;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                float g2[2], dz2[2];
+        for (int q = 0; q < 4; ++q) {
+            float g2[2], dz2[2];
 #pragma unroll
-                for (int r = 0; r < 2; ++r) {
-                    const float zz = r ? bf16_hi(zv[q]) : bf16_lo(zv[q]);
-                    const float dyv = r ? bf16_hi(dv[q]) : bf16_lo(dv[q]);
-                    const float xx = r ? bf16_hi(xv[q]) : bf16_lo(xv[q]);
-                    const float sg = sigmoid_f32(zz);
-                    g2[r] = dyv * zz * sg;
-                    dz2[r] = dyv * yv[2 * q + r] * sg * (1.0f + zz * (1.0f - sg));
-                    dsum = fmaf(g2[r], xx, dsum);
-                }
-                hi[q] = pack_bf16(g2[0], g2[1]);
-                lo[q] = pack_bf16(g2[0] - bf16_lo(hi[q]), g2[1] - bf16_hi(hi[q]));
-                dzv[q] = pack_bf16(dz2[0], dz2[1]);
+            for (int r = 0; r < 2; ++r) {
+                const float zz = r ? bf16_hi(zv[q]) : bf16_lo(zv[q]);
+                const float dyv = r ? bf16_hi(dv[q]) : bf16_lo(dv[q]);
+                const float xx = r ? bf16_hi(xv[q]) : bf16_lo(xv[q]);
+                const float sg = sigmoid_f32(zz);
+                g2[r] = dyv * zz * sg;
+                dz2[r] = dyv * yv[2 * q + r] * sg * (1.0f + zz * (1.0f - sg));
+                dsum = fmaf(g2[r], xx, dsum);
             }
-            *(u32x4 *)(k.dych + e) = hi;
-            *(u32x4 *)(k.dycl + e) = lo;
-            *(u32x4 *)(k.dz + e) = dzv;
-        } else {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                dsum = fmaf(bf16_lo(dv[q]), bf16_lo(xv[q]), dsum);
-                dsum = fmaf(bf16_hi(dv[q]), bf16_hi(xv[q]), dsum);
-            }
+            hi[q] = pack_bf16(g2[0], g2[1]);
+            lo[q] = pack_bf16(g2[0] - bf16_lo(hi[q]), g2[1] - bf16_hi(hi[q]));
+            dzv[q] = pack_bf16(dz2[0], dz2[1]);
         }
+        *(u32x4 *)(k.dych + e) = hi;
+        *(u32x4 *)(k.dycl + e) = lo;
+        *(u32x4 *)(k.dz + e) = dzv;
     }
     if (!k.dD) return;
     __shared__ float red[4];
@@ -772,6 +765,7 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_bwd_col_kernel(const BwdK k) 
 #pragma unroll
             for (int i = 0; i < 4; ++i) ot[(4 * kb + i) * LDO + 16 * q + r16] = dxa[j][q][i] * d4[i];
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        float dsum = 0.0f;                             // dDskip share (no gate: dyc = dy)
 #pragma unroll
         for (int rh = 0; rh < 2; ++rh) {
             const int row = rh * 8 + (lane >> 3), c8 = (lane & 7) * 8;
@@ -781,6 +775,8 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_bwd_col_kernel(const BwdK k) 
                 const u32x4 gh8 = *(const u32x4 *)(k.dych + e);
                 u32x4 gl8 = u32x4{0u, 0u, 0u, 0u};
                 if constexpr (SPLIT) gl8 = *(const u32x4 *)(k.dycl + e);
+                u32x4 xv8 = u32x4{0u, 0u, 0u, 0u};
+                if (!SPLIT && k.dD) xv8 = *(const u32x4 *)(p.x + e);
                 const f32x4 o0 = *(const f32x4 *)&ot[row * LDO + c8];
                 const f32x4 o1 = *(const f32x4 *)&ot[row * LDO + c8 + 4];
                 const float o[8] = {o0[0], o0[1], o0[2], o0[3], o1[0], o1[1], o1[2], o1[3]};
@@ -790,9 +786,15 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_bwd_col_kernel(const BwdK k) 
                     const float g0 = bf16_lo(gh8[e2]) + bf16_lo(gl8[e2]);
                     const float g1 = bf16_hi(gh8[e2]) + bf16_hi(gl8[e2]);
                     outv[e2] = pack_bf16(fmaf(dsk, g0, o[2 * e2]), fmaf(dsk, g1, o[2 * e2 + 1]));
+                    dsum = fmaf(g0, bf16_lo(xv8[e2]), dsum);
+                    dsum = fmaf(g1, bf16_hi(xv8[e2]), dsum);
                 }
                 *(u32x4 *)(k.dx + e) = outv;
             }
+        }
+        if (!SPLIT && k.dD) {
+            dsum = wave_sum(dsum);
+            if (lane == 0) atomicAdd(k.dD + h, dsum);
         }
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     }
@@ -997,8 +999,8 @@ ssm_status ssd_bwd_launch(const ssm_ssd_bwd_args &a, const SSDBwdPlan &plan, hip
         // gate: dD (and dz, dyc with z)
         const int64_t rows = a.batch * a.seqlen;
         const dim3 ggrid((unsigned)a.nheads, (unsigned)((rows + 255) / 256));
-        if (a.z) hipLaunchKernelGGL(ssd_bwd_gate_kernel<true>, ggrid, dim3(256), 0, s, k, rows);
-        else if (a.dDskip) hipLaunchKernelGGL(ssd_bwd_gate_kernel<false>, ggrid, dim3(256), 0, s, k, rows);
+        if (a.z) hipLaunchKernelGGL(ssd_bwd_gate_kernel, ggrid, dim3(256), 0, s, k, rows);
+        // without z, dDskip is summed by the column kernel (dyc = dy)
         // adjoint aggregates: the chunk-state kernel with x := dyc, B := C, exp(cs_t)
         // weights, output into the Gout buffer
         {
