@@ -304,7 +304,8 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_bwd_row_kernel(const BwdK k) 
     const SSDK &p = k.f;
     const Tile tl = decode_tile(blockIdx.x, TBS, k.nsl_row, p.G, p.nc);
     const int b = tl.b, c = tl.c, g = tl.g, tb = tl.blk;
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r16 = lane & 15, kb = lane >> 4;
+    const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, kb = lane >> 4;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: addresses built from it stay scalar
     const int64_t t_base = (int64_t)c * Q;
     const int T = (int)std::min<int64_t>(Q, p.L - t_base);
     if (tb * 64 >= T) return;                                       // uniform
@@ -322,14 +323,14 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_bwd_row_kernel(const BwdK k) 
     // C_t of this lane's column t = t0 + r16 (B operand of B_s . C_t, k = n)
     bf16x8 cfr[KN];
     {
-        const rsrc_t rc = make_rsrc(Cbase + (int64_t)t0 * GN, (uint32_t)(std::max(0, T - t0) * GN * 2));
+        const rsrc_t rc = make_rsrc_u(Cbase + (int64_t)t0 * GN, (uint32_t)(std::max(0, T - t0) * GN * 2));
 #pragma unroll
         for (int kk = 0; kk < KN; ++kk) cfr[kk] = frag(rc, (uint32_t)((r16 * GN + 32 * kk + 8 * kb) * 2));
     }
     // dyc of row t0 + r16 for head h (k = p): the B operand of x_s . dyc_t and the
     // A operand of dyc_t Sin
-    const rsrc_t rdh = make_rsrc(k.dych + dbase + (int64_t)t0 * xs, (uint32_t)(std::max(0, T - t0) * xs * 2));
-    const rsrc_t rdl = make_rsrc(SPLIT ? k.dycl + dbase + (int64_t)t0 * xs : k.dych, SPLIT ? (uint32_t)(std::max(0, T - t0) * xs * 2) : 0u);
+    const rsrc_t rdh = make_rsrc_u(k.dych + dbase + (int64_t)t0 * xs, (uint32_t)(std::max(0, T - t0) * xs * 2));
+    const rsrc_t rdl = make_rsrc_u(SPLIT ? k.dycl + dbase + (int64_t)t0 * xs : k.dych, SPLIT ? (uint32_t)(std::max(0, T - t0) * xs * 2) : 0u);
     auto load_dyc = [&](int h, bf16x8 (&fh)[2], bf16x8 (&fl)[2]) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
@@ -353,10 +354,10 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_bwd_row_kernel(const BwdK k) 
         const bool diag = sb == tb;
         __syncthreads();
         {   // B block (natural + transposed from one load) and x of every head
-            const rsrc_t rb = make_rsrc(Bbase + (int64_t)s0 * GN, (uint32_t)(std::max(0, T - s0) * GN * 2));
+            const rsrc_t rb = make_rsrc_u(Bbase + (int64_t)s0 * GN, (uint32_t)(std::max(0, T - s0) * GN * 2));
             for (int blk = tid; blk < 16 * (N / 8); blk += kThreads)
                 block_both(rb, GN, blk & 15, (blk >> 4) * 8, Bn, LDB, BT, LDT, (blk >> 4) * 8);
-            const rsrc_t rx = make_rsrc(Xbase + (int64_t)s0 * xs + hfirst * kP,
+            const rsrc_t rx = make_rsrc_u(Xbase + (int64_t)s0 * xs + hfirst * kP,
                                         (uint32_t)(std::max(0, T - s0) * xs * 2));
 #pragma unroll
             for (int i = 0; i < HS * 64 * 8 / kThreads; ++i) {
@@ -434,7 +435,7 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_bwd_row_kernel(const BwdK k) 
     // entering-state term, per head
     __syncthreads();
     {
-        const rsrc_t rc = make_rsrc(Cbase + (int64_t)(tb * 64) * GN, (uint32_t)(std::max(0, T - tb * 64) * GN * 2));
+        const rsrc_t rc = make_rsrc_u(Cbase + (int64_t)(tb * 64) * GN, (uint32_t)(std::max(0, T - tb * 64) * GN * 2));
         for (int blk = tid; blk < 16 * (N / 8); blk += kThreads)
             block_both(rc, GN, blk & 15, (blk >> 4) * 8, Cn, LDB, nullptr, 0, (blk >> 4) * 8);
     }
@@ -542,7 +543,8 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_bwd_col_kernel(const BwdK k) 
     const SSDK &p = k.f;
     const Tile tl = decode_tile(blockIdx.x, TBS, k.nsl_col, p.G, p.nc);
     const int b = tl.b, c = tl.c, g = tl.g, sb = tl.blk;
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r16 = lane & 15, kb = lane >> 4;
+    const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, kb = lane >> 4;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: addresses built from it stay scalar
     const int64_t t_base = (int64_t)c * Q;
     const int T = (int)std::min<int64_t>(Q, p.L - t_base);
     if (sb * 64 >= T) return;                                       // uniform
@@ -560,11 +562,11 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_bwd_col_kernel(const BwdK k) 
     // operand of B_s Gout^T
     bf16x8 bfr[KN];
     {
-        const rsrc_t rb = make_rsrc(Bbase + (int64_t)s0w * GN, (uint32_t)(std::max(0, T - s0w) * GN * 2));
+        const rsrc_t rb = make_rsrc_u(Bbase + (int64_t)s0w * GN, (uint32_t)(std::max(0, T - s0w) * GN * 2));
 #pragma unroll
         for (int kk = 0; kk < KN; ++kk) bfr[kk] = frag(rb, (uint32_t)((r16 * GN + 32 * kk + 8 * kb) * 2));
     }
-    const rsrc_t rx = make_rsrc(p.x + dbase + (int64_t)s0w * xs, (uint32_t)(std::max(0, T - s0w) * xs * 2));
+    const rsrc_t rx = make_rsrc_u(p.x + dbase + (int64_t)s0w * xs, (uint32_t)(std::max(0, T - s0w) * xs * 2));
     auto load_x = [&](int h, bf16x8 (&xf)[2]) {     // x_s rows (k = p)
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) xf[kk] = frag(rx, (uint32_t)((r16 * xs + h * kP + 32 * kk + 8 * kb) * 2));
@@ -590,10 +592,10 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_bwd_col_kernel(const BwdK k) 
         const bool diag = tb == sb;
         __syncthreads();
         {   // C block, and dyc of every head (natural and transposed; lo natural)
-            const rsrc_t rc = make_rsrc(Cbase + (int64_t)tb0 * GN, (uint32_t)(std::max(0, T - tb0) * GN * 2));
+            const rsrc_t rc = make_rsrc_u(Cbase + (int64_t)tb0 * GN, (uint32_t)(std::max(0, T - tb0) * GN * 2));
             for (int blk = tid; blk < 16 * (N / 8); blk += kThreads)
                 block_both(rc, GN, blk & 15, (blk >> 4) * 8, Cn, LDB, CT, LDT, (blk >> 4) * 8);
-            const rsrc_t rd = make_rsrc(k.dych + dbase + (int64_t)tb0 * xs + hfirst * kP,
+            const rsrc_t rd = make_rsrc_u(k.dych + dbase + (int64_t)tb0 * xs + hfirst * kP,
                                         (uint32_t)(std::max(0, T - tb0) * xs * 2));
             for (int blk = tid; blk < HS * 128; blk += kThreads) {
                 const int j = blk >> 7, rg = blk & 15, cg = (blk >> 4) & 7;
@@ -601,7 +603,7 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_bwd_col_kernel(const BwdK k) 
                     block_both(rd, xs, rg, j * kP + cg * 8, Dh + j * 64 * LDX, LDX, DT + j * kP * LDT, LDT, cg * 8);
             }
             if constexpr (SPLIT) {
-                const rsrc_t rl = make_rsrc(k.dycl + dbase + (int64_t)tb0 * xs + hfirst * kP,
+                const rsrc_t rl = make_rsrc_u(k.dycl + dbase + (int64_t)tb0 * xs + hfirst * kP,
                                             (uint32_t)(std::max(0, T - tb0) * xs * 2));
 #pragma unroll
                 for (int i = 0; i < HS * 64 * 8 / kThreads; ++i) {
@@ -690,12 +692,22 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_bwd_col_kernel(const BwdK k) 
         if (j >= nh) break;                                           // uniform
         const int h = hfirst + j;
         const float *gh = k.gout + ((((int64_t)b * p.nc + c) * p.H + h) * kP) * N;
+        // x_s in the accumulator layout (rows s0w + 4kb + i, p = 16q + r16) and as the
+        // A operand, loaded before the staging barrier so their latency overlaps it
+        float xv[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int sl = s0w + 4 * kb + i;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                xv[i][q] = sl < T ? to_f32(p.x[(dbase + (int64_t)sl * xs) + h * kP + 16 * q + r16]) : 0.0f;
+        }
+        bf16x8 xf[2];
+        load_x(h, xf);
         __syncthreads();
         for (int blk = tid; blk < 16 * (N / 8); blk += kThreads)
             block_split_both(gh, N, blk & 15, blk >> 4, Gn, Gn + kP * LDB, LDB, GT, GT + N * LDT, LDT);
         __syncthreads();
-        bf16x8 xf[2];
-        load_x(h, xf);
         f32x4 xi[4], bi[NT];
 #pragma unroll
         for (int q = 0; q < 4; ++q) xi[q] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -725,13 +737,11 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_bwd_col_kernel(const BwdK k) 
         float xi_s[4], e_s[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int sl = s0w + 4 * kb + i;
             e_s[i] = fast_exp2(cend - c4[i]);
             float si = 0.0f;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const float xv = sl < T ? to_f32(p.x[(dbase + (int64_t)sl * xs) + h * kP + 16 * q + r16]) : 0.0f;
-                si = fmaf(xv, xi[q][i], si);
+                si = fmaf(xv[i][q], xi[q][i], si);
                 dxa[j][q][i] = fmaf(e_s[i], xi[q][i], dxa[j][q][i]);    // dx / dt before D dyc
             }
             xi_s[i] = row16_sum(si);

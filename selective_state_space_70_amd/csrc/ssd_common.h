@@ -32,6 +32,17 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8 &a, const bf16x8 &b, 
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4 &v) { return __builtin_bit_cast(bf16x8, v); }
 
+// Buffer resource from a wave-uniform base and size. Every call site passes values
+// that are the same in all lanes of the wave; readfirstlane on the base as well
+// keeps the resource in SGPRs even where the compiler built the address with
+// vector instructions (a resource in VGPRs costs a loop over lanes per access).
+__device__ __forceinline__ rsrc_t make_rsrc_u(const void *base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)base;
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    return make_rsrc((const void *)((hi << 32) | lo), bytes);
+}
+
 // 16 bytes through a buffer resource (0 outside its range)
 __device__ __forceinline__ u32x4 load16(rsrc_t r, uint32_t voff) {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));

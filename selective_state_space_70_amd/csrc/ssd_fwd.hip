@@ -65,7 +65,9 @@ __global__ __launch_bounds__(kThreads, (N > 128 || MODE != 0) ? 1 : 2) void ssd_
     __shared__ __attribute__((aligned(16))) uint16_t XL[SPLIT ? 4 : 1][SPLIT ? kP : 1][SPLIT ? LDT : 8];
 
     const int c = blockIdx.x, b = blockIdx.z;
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    // the wave index is uniform: readfirstlane keeps it (and every address built
+    // from it) in SGPRs, so buffer resources need no per-lane loop
+    const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r16 = lane & 15, kb = lane >> 4;
     const int hb = (p.hpg + 3) / 4;                   // workgroups per group of heads
     const int g = blockIdx.y / hb, hl = (blockIdx.y % hb) * 4 + wv;
@@ -95,9 +97,9 @@ __global__ __launch_bounds__(kThreads, (N > 128 || MODE != 0) ? 1 : 2) void ssd_
     const bool has_lo = MODE == 2 && p.xlo != nullptr;
     auto fetch = [&](int pass, int s0) {
         const int rows = (int)std::max<int64_t>(0, std::min<int64_t>(SB, p.L - t_base - s0));
-        const rsrc_t rb = make_rsrc(p.Bm + (((int64_t)b * p.L + t_base + s0) * p.G + g) * N + pass * NP,
+        const rsrc_t rb = make_rsrc_u(p.Bm + (((int64_t)b * p.L + t_base + s0) * p.G + g) * N + pass * NP,
                                     (uint32_t)(rows * GN * 2));
-        const rsrc_t rx = make_rsrc(p.x + (((int64_t)b * p.L + t_base + s0) * p.H + hc) * kP,
+        const rsrc_t rx = make_rsrc_u(p.x + (((int64_t)b * p.L + t_base + s0) * p.H + hc) * kP,
                                     (uint32_t)(rows * p.H * kP * 2));
 #pragma unroll
         for (int i = 0; i < 4; ++i) breg[i] = load16(rb, (uint32_t)(((sg * 4 + i) * GN + co * 8) * 2));
@@ -110,7 +112,7 @@ __global__ __launch_bounds__(kThreads, (N > 128 || MODE != 0) ? 1 : 2) void ssd_
         }
         if constexpr (MODE == 2) {
             if (has_lo) {
-                const rsrc_t rl = make_rsrc(p.xlo + (((int64_t)b * p.L + t_base + s0) * p.H + hc) * kP,
+                const rsrc_t rl = make_rsrc_u(p.xlo + (((int64_t)b * p.L + t_base + s0) * p.H + hc) * kP,
                                             (uint32_t)(rows * p.H * kP * 2));
 #pragma unroll
                 for (int k = 0; k < 2; ++k) {
@@ -319,7 +321,9 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_out_kernel(const SSDK p
     // nhg: workgroups per group of B, C heads
     const int hl = grp % nhg, gg = (grp / nhg) % p.G, c = (grp / (nhg * p.G)) % p.nc;
     const int b = grp / (nhg * p.G * p.nc);
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    // the wave index is uniform: readfirstlane keeps it (and every address built
+    // from it) in SGPRs, so buffer resources need no per-lane loop
+    const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r16 = lane & 15, kb = lane >> 4;
     const int64_t t_base = (int64_t)c * Q;
     const int T = (int)std::min<int64_t>(Q, p.L - t_base);
@@ -355,8 +359,8 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_out_kernel(const SSDK p
     auto fetch = [&](int sb) {
         const int s0 = sb * 64;
         const int rows = std::max(0, T - s0);
-        const rsrc_t rb = make_rsrc(Brow + (int64_t)s0 * GN, (uint32_t)(rows * GN * 2));
-        const rsrc_t rx = make_rsrc(Xrow + (int64_t)s0 * xstride, (uint32_t)(rows * xstride * 2));
+        const rsrc_t rb = make_rsrc_u(Brow + (int64_t)s0 * GN, (uint32_t)(rows * GN * 2));
+        const rsrc_t rx = make_rsrc_u(Xrow + (int64_t)s0 * xstride, (uint32_t)(rows * xstride * 2));
 #pragma unroll
         for (int i = 0; i < BV; ++i) breg[i] = load16(rb, boff[i]);
 #pragma unroll
@@ -383,7 +387,7 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_out_kernel(const SSDK p
     u32x4 sreg[SV];
     auto sin_fetch = [&](int j0) {
         const int nh = std::max(0, std::min(SIN_HEADS, hend - (h0 + j0)));
-        const rsrc_t rs = make_rsrc(sin_c + (int64_t)(h0 + j0) * kP * N, (uint32_t)(nh * kP * N * 2));
+        const rsrc_t rs = make_rsrc_u(sin_c + (int64_t)(h0 + j0) * kP * N, (uint32_t)(nh * kP * N * 2));
 #pragma unroll
         for (int i = 0; i < SV; ++i) sreg[i] = load16(rs, (uint32_t)(tid + i * kThreads) * 16u);
     };
