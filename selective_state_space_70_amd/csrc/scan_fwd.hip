@@ -210,8 +210,24 @@ __device__ __forceinline__ void run_readout(const ScanK &p, int b, int dc, bool 
                 if constexpr (HAS_Z) za[u] = zb[u];
             }
         }
+        // tail of fewer than U steps: their rows are already in xa (the last
+        // prefetch clamps to t1 - 1)
+#pragma unroll
+        for (int u = 0; u < U - 1; ++u) {
+            if (t + u < t1) {
+                uint32_t bn[NW], cn[NW];
+                const int rn = min(t + u + 1, t1 - 1) * GN;
+                load_row<T, N>(as_const(Brow + rn), bn);
+                load_row<T, N>(as_const(Crow + rn), cn);
+                step_readout<T, N, FAST, HAS_Z>(c, softplus, xa[u], da[u], HAS_Z ? za[u] : xa[u],
+                                                bw, cw, h, yr, lo, (uint32_t)(t + u) * rowb, act);
+#pragma unroll
+                for (int j = 0; j < NW; ++j) { bw[j] = bn[j]; cw[j] = cn[j]; }
+            }
+        }
+        t = t1;
     }
-    for (; t < t1; ++t) {  // tail: fewer than U steps
+    for (; t < t1; ++t) {  // a chunk shorter than U steps
         uint32_t bn[NW], cn[NW];
         const int rn = min(t + 1, t1 - 1) * GN;
         load_row<T, N>(as_const(Brow + rn), bn);
@@ -304,6 +320,19 @@ __device__ __forceinline__ double run_aggregate(const ScanK &p, int b, int dc, i
 #pragma unroll
                 for (int u = 0; u < U; ++u) { xa[u] = xb[u]; da[u] = db[u]; }
             }
+            // the first t - t0 + 1 < U steps of the chunk: already in xa (the last
+            // prefetch clamps to t0)
+#pragma unroll
+            for (int u = 0; u < U - 1; ++u) {
+                if (t - u >= t0) {
+                    uint32_t bn[NW];
+                    load_row<T, N>(as_const(Brow + max(t - u - 1, t0) * GN), bn);
+                    one(xa[u], da[u], bw);
+#pragma unroll
+                    for (int j = 0; j < NW; ++j) bw[j] = bn[j];
+                }
+            }
+            t = t0 - 1;
         }
         for (; t >= t0; --t) {
             uint32_t bn[NW];
@@ -484,7 +513,7 @@ ScanPlan scan_plan(const ssm_scan_args &a) {
     }
     G = std::max<int64_t>(1, std::min<int64_t>(G, std::min<int64_t>(a.seqlen, 65535)));
     pl.chunk_len = (a.seqlen + G - 1) / G;
-    if (G > 1) pl.chunk_len = (pl.chunk_len + 7) / 8 * 8;   // whole 8-step blocks
+    if (G > 1) pl.chunk_len = (pl.chunk_len + 3) / 4 * 4;
     pl.chunks = (a.seqlen + pl.chunk_len - 1) / pl.chunk_len;
     if (pl.chunks > 1) {
         auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
