@@ -104,3 +104,17 @@ def test_mamba_130m_layer_shape():
     inp["dy"] = workloads.round_bf16(rng.standard_normal((8, 2048, 1536)).astype(np.float32))
     inp["dh_final"] = None
     _check("S2 bwd", inp)
+
+
+def test_empty_sequence():
+    """L = 0: every gradient is zero except dh0, which is dh_final."""
+    inp = _case(2, 0, 64, 16, "f32", seed=14)
+    td = torch.float32
+    g = ssm.selective_scan_bwd(_dev(inp["x"], td), _dev(inp["delta"], td), _dev(inp["A"]),
+                               _dev(inp["Bm"], td), _dev(inp["Cm"], td), _dev(inp["dy"], td),
+                               _dev(inp.get("Dskip")), _dev(inp.get("z"), td), _dev(inp.get("delta_bias")),
+                               _dev(inp.get("h0")), _dev(inp.get("dh_final")))
+    torch.cuda.synchronize()
+    for k in ("dA", "dDskip", "ddelta_bias"):
+        assert torch.count_nonzero(g[k]) == 0, k
+    assert torch.equal(g["dh0"].cpu(), torch.from_numpy(inp["dh_final"])), "dh0"

@@ -132,3 +132,19 @@ def test_mamba2_layer_shape_sampled_heads():
 def test_all_heads_medium():
     """64 heads over 1024 steps: dB and dC (sums over all heads) element by element."""
     _check("H=64 L=1024", _case(1, 1024, 64, 128, seed=11), 256)
+
+
+def test_empty_sequence():
+    """L = 0: every gradient is zero except dh0, which is dh_final."""
+    inp = _case(2, 0, 4, 64, seed=12)
+    g = _gpu(inp, 64)
+    assert g["dx"].numel() == 0 and g["ddt"].numel() == 0
+    for k in ("dA", "dDskip", "ddt_bias"):
+        assert torch.count_nonzero(g[k]) == 0, k
+    assert torch.equal(g["dh0"].cpu(), torch.from_numpy(inp["dh_final"])), "dh0"
+
+
+def test_empty_batch():
+    inp = _case(0, 100, 4, 64, seed=13)
+    g = _gpu(inp, 64)
+    assert g["dx"].numel() == 0 and g["dh0"].numel() == 0
