@@ -337,3 +337,14 @@ def test_ssd_bwd_workspace():
     a.z = None
     assert lib.ssd_chunked_bwd_workspace_bytes(ctypes.byref(a)) < need
     assert lib.ssd_chunked_bwd_workspace_bytes(ctypes.byref(ssd_bwd_args(dstate=256))) == 0
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
+    """No CPU fallback: with the library missing every entry point raises."""
+    monkeypatch.setattr(_capi, "LIB_PATH", str(tmp_path / "libssm.so"))
+    monkeypatch.setattr(_capi, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        _capi.lib()
+    import selective_state_space_70_amd as ssm
+    with pytest.raises(RuntimeError, match="not built"):
+        ssm.abi_version()
