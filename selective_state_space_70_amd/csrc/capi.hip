@@ -24,6 +24,9 @@ bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 size_t esize(ssm_dtype t) { return t == SSM_BF16 ? 2 : 4; }
 
 constexpr int64_t kMaxRowBytes = (int64_t)1 << 31;
+// A launch's threads along one grid dimension (blocks * block size) must fit 32 bits;
+// the element-wise kernels use one thread per element (up to 256 per block).
+constexpr int64_t kMaxLaunchThreads = ((int64_t)1 << 32) - 256;
 
 int64_t groups(int64_t g) { return g <= 1 ? 1 : g; }
 
@@ -52,6 +55,8 @@ ssm_status check_scan_sizes(const ssm_scan_args *a) {
         return fail(SSM_ENOTSUP, "selective_scan: seqlen*dim*elem_size must be < 2^31 bytes");
     if (a->seqlen * groups(a->ngroups) * a->dstate * (int64_t)es >= kMaxRowBytes)
         return fail(SSM_ENOTSUP, "selective_scan: seqlen*ngroups*dstate*elem_size must be < 2^31 bytes");
+    if (a->batch * a->dim * a->dstate > kMaxLaunchThreads)
+        return fail(SSM_ENOTSUP, "selective_scan: batch*dim*dstate must be < 2^32 (one thread per state element)");
     return SSM_OK;
 }
 
@@ -102,10 +107,14 @@ ssm_status check_ssd_sizes(const ssm_ssd_args *a) {
         return fail(SSM_ENOTSUP, "ssd_chunked: seqlen*nheads*headdim*2 must be < 2^31 bytes");
     if ((a->seqlen + a->chunk - 1) / a->chunk > 65535)
         return fail(SSM_ENOTSUP, "ssd_chunked: at most 65535 chunks");
-    // workgroups of the output kernel: one per (batch, chunk, 4 heads, 64 rows)
-    if (a->batch * ((a->seqlen + a->chunk - 1) / a->chunk) * (a->nheads + 8) * (a->chunk / 64) >=
-        ((int64_t)1 << 31))
+    // workgroups of the output kernel (256 threads each): at most one per
+    // (batch, chunk, head, 64 rows), plus a partial head group per B/C group
+    if (a->batch * ((a->seqlen + a->chunk - 1) / a->chunk) * (a->nheads + 8) * (a->chunk / 64) * 256 >
+        kMaxLaunchThreads)
         return fail(SSM_ENOTSUP, "ssd_chunked: batch * chunks * heads too large for one launch");
+    // the state pass and the state copies run one thread per (4) state element(s)
+    if (a->batch * a->nheads * a->headdim * a->dstate > kMaxLaunchThreads)
+        return fail(SSM_ENOTSUP, "ssd_chunked: batch*nheads*headdim*dstate must be < 2^32");
     return SSM_OK;
 }
 
@@ -141,6 +150,9 @@ ssm_status check_ssd_bwd_sizes(const ssm_ssd_bwd_args *a) {
     if (st != SSM_OK) return st;
     if (a->dstate != 64 && a->dstate != 128)
         return fail(SSM_ENOTSUP, "ssd_chunked_bwd: dstate %lld not supported (64, 128)", (long long)a->dstate);
+    // dB and dC partial sums are reduced one thread per element
+    if (a->batch * a->seqlen * groups(a->ngroups) * a->dstate > kMaxLaunchThreads)
+        return fail(SSM_ENOTSUP, "ssd_chunked_bwd: batch*seqlen*ngroups*dstate must be < 2^32");
     return SSM_OK;
 }
 
@@ -254,8 +266,12 @@ ssm_status check_bwd_sizes(const ssm_scan_bwd_args *a) {
     f.ngroups = a->ngroups; f.dtype = a->dtype;
     const ssm_status st = check_scan_sizes(&f);
     if (st != SSM_OK) return st;
-    if (a->seqlen > ((int64_t)1 << 30))
-        return fail(SSM_ENOTSUP, "selective_scan_bwd: seqlen must be <= 2^30");
+    // chunks of 64 steps index the second grid dimension of the chunk kernels
+    if ((a->seqlen + 63) / 64 > 65535)
+        return fail(SSM_ENOTSUP, "selective_scan_bwd: seqlen must be <= 65535 * 64");
+    if (a->batch * a->seqlen * groups(a->ngroups) * a->dstate > kMaxLaunchThreads)
+        return fail(SSM_ENOTSUP, "selective_scan_bwd: batch*seqlen*ngroups*dstate must be < 2^32 "
+                    "(dB and dC are cleared one thread per element)");
     return SSM_OK;
 }
 

@@ -187,7 +187,7 @@ __device__ __forceinline__ void aggregate_chunk(const BwdK &p, int b, int dc, in
 
 template <typename T, int N, bool HAS_Z>
 __global__ __launch_bounds__(64) void bwd_aggregate_kernel(const BwdK p) {
-    const int c = blockIdx.x, chain = blockIdx.y;
+    const int chain = blockIdx.x, c = blockIdx.y;   // chains on x (no 65535 limit), chunks on y
     const int b = chain / p.dblocks;
     const int d = (chain % p.dblocks) * 64 + threadIdx.x;
     const int dc = d < p.D ? d : p.D - 1;
@@ -486,9 +486,9 @@ void launch_bwd(const BwdK &k, hipStream_t s) {
     const int chains = k.batch * k.dblocks;
     constexpr int CPG = kWaves * (64 / N);
     if (k.z) {
-        hipLaunchKernelGGL((bwd_aggregate_kernel<T, N, true>), dim3(k.nch, chains), dim3(64), 0, s, k);
+        hipLaunchKernelGGL((bwd_aggregate_kernel<T, N, true>), dim3(chains, k.nch), dim3(64), 0, s, k);
     } else {
-        hipLaunchKernelGGL((bwd_aggregate_kernel<T, N, false>), dim3(k.nch, chains), dim3(64), 0, s, k);
+        hipLaunchKernelGGL((bwd_aggregate_kernel<T, N, false>), dim3(chains, k.nch), dim3(64), 0, s, k);
     }
     hipLaunchKernelGGL((bwd_carry_kernel<N>), dim3(chains), dim3(64), 0, s, k);
     const dim3 grid((unsigned)((k.D + CPG - 1) / CPG), (unsigned)k.nch, (unsigned)k.batch);

@@ -182,11 +182,11 @@ __device__ __forceinline__ void head_tables(const SSDK &p, int b, int c, int hfi
 // With z: one workgroup per (head, 256 rows of (b, t)); a lane owns 8 consecutive
 // p. dyc = dy silu(z) as bf16 hi + lo, dz = dy (y_pre) silu'(z), dDskip.
 __global__ __launch_bounds__(256) void ssd_bwd_gate_kernel(const BwdK k, int64_t rows) {
-    const int h = blockIdx.x, H = k.f.H;
+    const int h = blockIdx.y, H = k.f.H;   // rows of (b, t) on x (no 65535 limit), heads on y
     const int v = threadIdx.x & 7, rsub = threadIdx.x >> 3;
     float dsum = 0.0f;
     for (int it = 0; it < 8; ++it) {
-        const int64_t row = (int64_t)blockIdx.y * 256 + it * 32 + rsub;
+        const int64_t row = (int64_t)blockIdx.x * 256 + it * 32 + rsub;
         if (row >= rows) break;
         const int64_t e = (row * H + h) * kP + v * 8;
         const u32x4 xv = *(const u32x4 *)(k.f.x + e);
@@ -1008,7 +1008,7 @@ ssm_status ssd_bwd_launch(const ssm_ssd_bwd_args &a, const SSDBwdPlan &plan, hip
         if (a.z) ssd_recompute_launch(f, (int)a.batch, Q, N, 1, s);   // fp32 pre-gate output
         // gate: dD (and dz, dyc with z)
         const int64_t rows = a.batch * a.seqlen;
-        const dim3 ggrid((unsigned)a.nheads, (unsigned)((rows + 255) / 256));
+        const dim3 ggrid((unsigned)((rows + 255) / 256), (unsigned)a.nheads);
         if (a.z) hipLaunchKernelGGL(ssd_bwd_gate_kernel, ggrid, dim3(256), 0, s, k, rows);
         // without z, dDskip is summed by the column kernel (dyc = dy)
         // adjoint aggregates: the chunk-state kernel with x := dyc, B := C, exp(cs_t)

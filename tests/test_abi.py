@@ -95,6 +95,8 @@ def ssd_status(a):
     ({"dstate": 128}, _capi.SSM_ENOTSUP),
     ({"batch": 70000}, _capi.SSM_ENOTSUP),
     ({"seqlen": 1 << 20, "dim": 1 << 12}, _capi.SSM_ENOTSUP),   # row of 8 GiB
+    ({"batch": 65535, "dim": 8192}, _capi.SSM_ENOTSUP),       # 2^33 state elements: one launch
+    ({"batch": 65535, "dim": 4096}, _capi.SSM_OK),            # just under 2^32
     ({"ngroups": 1}, _capi.SSM_OK),
     ({"ngroups": 2, "dim": 256}, _capi.SSM_OK),
     ({"ngroups": 2}, _capi.SSM_ENOTSUP),                      # 48 channels per group
@@ -128,6 +130,11 @@ def test_scan_validation(kw, want):
     ({"ngroups": 2}, _capi.SSM_OK),
     ({"ngroups": 8}, _capi.SSM_OK),
     ({"ngroups": 3}, _capi.SSM_EINVAL),
+    # 65535 * 128 heads of 64 x 128 states: more than 2^32 state elements in one launch
+    ({"batch": 65535, "nheads": 128, "seqlen": 1, "chunk": 64}, _capi.SSM_ENOTSUP),
+    ({"batch": 4096, "nheads": 64, "seqlen": 1, "chunk": 64}, _capi.SSM_OK),
+    # 2^23 steps in one head: the backward's dB reduction needs 2^33 threads, the forward fits
+    ({"batch": 8, "seqlen": 1 << 23, "nheads": 1}, _capi.SSM_OK),
 ])
 def test_ssd_validation(kw, want):
     assert ssd_status(ssd_args(**kw)) == want
@@ -283,6 +290,8 @@ def bwd_args(**kw):
     ({"dB": FAKE + 2}, _capi.SSM_EINVAL),
     ({"dstate": 128}, _capi.SSM_ENOTSUP),
     ({"ngroups": 2}, _capi.SSM_ENOTSUP),                  # 48 channels per group
+    ({"seqlen": 65535 * 64 + 1}, _capi.SSM_ENOTSUP),      # more than 65535 chunks of 64 steps
+    ({"batch": 65535, "seqlen": 5000}, _capi.SSM_ENOTSUP),  # dB, dC: more than 2^32 elements
     ({}, _capi.SSM_EINVAL),                               # needs workspace
 ])
 def test_bwd_validation(kw, want):
@@ -320,6 +329,7 @@ def ssd_bwd_args(**kw):
     ({"chunk": 100}, _capi.SSM_ENOTSUP),
     ({"dtype": _capi.SSM_F32}, _capi.SSM_ENOTSUP),
     ({"ngroups": 3}, _capi.SSM_EINVAL),                   # 8 heads in 3 groups
+    ({"batch": 8, "seqlen": 1 << 23, "nheads": 1}, _capi.SSM_ENOTSUP),  # dB, dC: 2^33 elements
     ({}, _capi.SSM_EINVAL),                               # needs workspace
 ])
 def test_ssd_bwd_validation(kw, want):
