@@ -107,9 +107,9 @@ ssm_status check_ssd_sizes(const ssm_ssd_args *a) {
         return fail(SSM_ENOTSUP, "ssd_chunked: seqlen*nheads*headdim*2 must be < 2^31 bytes");
     if ((a->seqlen + a->chunk - 1) / a->chunk > 65535)
         return fail(SSM_ENOTSUP, "ssd_chunked: at most 65535 chunks");
-    // workgroups of the output kernel (256 threads each): at most one per
-    // (batch, chunk, head, 64 rows), plus a partial head group per B/C group
-    if (a->batch * ((a->seqlen + a->chunk - 1) / a->chunk) * (a->nheads + 8) * (a->chunk / 64) * 256 >
+    // threads of the output kernel: 4 * chunk per (batch, chunk, pair of heads),
+    // the (batch, chunk) count rounded up to a multiple of 8
+    if ((a->batch * ((a->seqlen + a->chunk - 1) / a->chunk) + 7) * a->nheads * a->chunk * 4 >
         kMaxLaunchThreads)
         return fail(SSM_ENOTSUP, "ssd_chunked: batch * chunks * heads too large for one launch");
     // the state pass and the state copies run one thread per (4) state element(s)

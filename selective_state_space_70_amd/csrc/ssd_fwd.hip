@@ -15,14 +15,14 @@
 // Three kernels per call (v_mfma_f32_16x16x32_bf16, fp32 accumulation):
 //   1. ssd_chunk_state: per (batch, chunk, 4 heads). B of the chunk is transposed
 //      into LDS once and shared by the 4 heads (one wave each); x is transposed
-//      and scaled by exp(cs_end - cs_s) dt_s while staging. S_c is written in fp32,
-//      layout [p][n].
+//      and scaled by exp(cs_end - cs_s) dt_s while staging. S_c is written in bf16,
+//      layout [p][n] (fp32 in the gradient pass's recompute).
 //   2. ssd_state_pass: sequential over chunks per (batch, head, p, 4 n); writes the
 //      entering state of every chunk already rounded to bf16 in the [p][n] layout
 //      the output kernel reads as MFMA B fragments, and h_final in fp32.
-//   3. ssd_chunk_out: per (batch, chunk, head, 64 rows of time), one 16-row tile
-//      per wave; B and x stream through double-buffered LDS in 32-row blocks of s.
-//      For each block the transposed score tile G^T = B C^T is computed on the
+//   3. ssd_chunk_out: per (batch, chunk, pair of heads), one or two 16-row tiles
+//      per wave; B and x stream through LDS in 64-row blocks of s, each loaded
+//      once per workgroup. For each block the transposed score tile G^T = B C^T is computed on the
 //      MFMA units, masked and scaled in registers and rounded to bf16 straight
 //      into the A operand of Y += M X (the 16x16
 //      accumulator layout gives a lane 4 consecutive s of one t; two tiles give the
@@ -44,7 +44,8 @@ namespace {
 
 // ---------------------------------------------------------------- chunk states
 // MODE 0: S_c = sum_s exp(cs_end - cs_s) dt_s B_s (x) x_s, the weighted x rounded to
-//         bf16 (the forward);
+//         bf16, S_c stored in bf16 (the forward: the entering states it feeds are
+//         rounded to bf16 anyway);
 // MODE 1: the same with the weighted x split into bf16 hi + lo parts, two products
 //         (fp32-grade chunk states, for the gradient pass);
 // MODE 2: R_c = sum_t exp(cs_t) B_t (x) (x_t + xlo_t), split like MODE 1, no decay
@@ -194,14 +195,21 @@ __global__ __launch_bounds__(kThreads, (N > 128 || MODE != 0) ? 1 : 2) void ssd_
                 }
             }
         }
-        // S_c[p][n]: lane holds n = pass*NP + 16i + 4kb + e, p = 16j + r16 -> 16-byte stores
+        // S_c[p][n]: lane holds n = pass*NP + 16i + 4kb + e, p = 16j + r16 -> 16-byte
+        // stores (8-byte stores of bf16 in the forward)
         if (head_ok) {
-            float *out = p.states + (((int64_t)b * p.nc + c) * p.H + h) * (int64_t)kP * N;
+            const int64_t o = (((int64_t)b * p.nc + c) * p.H + h) * (int64_t)kP * N;
 #pragma unroll
             for (int i = 0; i < NT; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    *(f32x4 *)(out + (j * 16 + r16) * N + pass * NP + i * 16 + kb * 4) = acc[i][j];
+                for (int j = 0; j < 4; ++j) {
+                    const int e = (j * 16 + r16) * N + pass * NP + i * 16 + kb * 4;
+                    if constexpr (MODE == 0)
+                        *(u32x2 *)(p.states16 + o + e) = u32x2{pack_bf16(acc[i][j][0], acc[i][j][1]),
+                                                               pack_bf16(acc[i][j][2], acc[i][j][3])};
+                    else
+                        *(f32x4 *)(p.states + o + e) = acc[i][j];
+                }
         }
     }
 }
@@ -232,7 +240,12 @@ __global__ __launch_bounds__(256) void ssd_state_pass_kernel(const SSDK p, int N
 #pragma unroll
         for (int u = 0; u < K; ++u) {
             const int cc = min(c0 + u, p.nc - 1);
-            sc[u] = *(const f32x4 *)(p.states + base + cc * cstride);
+            if (p.states16) {   // bf16 chunk states (the forward)
+                const u32x2 v = *(const u32x2 *)(p.states16 + base + cc * cstride);
+                sc[u] = f32x4{bf16_lo(v[0]), bf16_hi(v[0]), bf16_lo(v[1]), bf16_hi(v[1])};
+            } else {
+                sc[u] = *(const f32x4 *)(p.states + base + cc * cstride);
+            }
             dc[u] = dec[cc];
         }
 #pragma unroll
@@ -254,18 +267,25 @@ __global__ __launch_bounds__(256) void ssd_state_pass_kernel(const SSDK p, int N
 }
 
 // ---------------------------------------------------------------- chunk output
-// One workgroup per (batch, chunk, group of HG heads, 64-row block of time); wave
-// w owns rows t0 = 64 tb + 16 w .. t0 + 15 for all HG heads of the group. The
-// score tile G^T = B C^T of a 64-row block of s is computed once per wave and
-// reused by every head of the group: only the decay weights differ per head.
+// One workgroup per (batch, chunk, pair of heads of one B/C group); each wave owns
+// 16 rows of the chunk, or for chunks of 256 steps 32 rows (two 16-row tiles of one
+// 64-row time block tb), for both heads, so every operand it reads from LDS feeds
+// the matrix-core products of both tiles. With 8 waves (chunk 256), waves w and w + 4
+// share a SIMD and take the row pairs w and 7 - w, which balances the causal work
+// per SIMD. The prologue of a chunk (dt and cumulative decays, the entering
+// states, C rows) is done once for all Q rows, and each 64-row block of B and x is
+// loaded once and used by every wave whose rows come at or after it. The score
+// tile G^T = B C^T is computed once per tile and reused by both heads: only the
+// decay weights differ per head.
 //
-// With r = 64 tb - 1 (the last step before this time block; cs_r = 0 for tb = 0)
+// With r = 64 tb - 1 (the last step before the time block; cs_r = 0 for tb = 0)
 // the decay of s <= r < t factors as exp(cs_t - cs_s) = a_t w_s, a_t = exp(cs_t -
 // cs_r), w_s = exp(cs_r - cs_s), both <= 1. So for every block of s before the
 // time block, M = G o (w_s dt_s) needs no exponential per element; those blocks and
 // the entering state (exp(cs_t) C Sin = a_t exp(cs_r) C Sin) accumulate into one
 // tile that is scaled by a_t once, after which the diagonal block adds its terms
-// with the exact per-element weight exp(cs_t - cs_s) dt_s [s <= t].
+// with the exact per-element weight exp(cs_t - cs_s) dt_s [s <= t]. w_s dt_s is
+// tabulated per time block.
 //
 // Layouts in LDS: B rows natural ([s][n], the A operand of G^T); x transposed per
 // head ([p][s], the B operand of Y += M X) with s permuted inside each 32-block so
@@ -279,9 +299,18 @@ struct OutCfg {
 
 // F32OUT: write the pre-gate output (C S + D x) in fp32 to y32 instead of the gated
 // bf16 y (the recompute the gradient pass needs for dz).
+// Two tiles per wave halve the LDS operand reads but leave 8 waves per CU at chunk
+// 256, which measured slower than 16 waves with one tile each: one tile per wave.
+template <int Q>
+constexpr int out_tiles_per_wave() { return 1; }
+
 template <int N, int Q, bool F32OUT>
-__global__ __launch_bounds__(kThreads, 2) void ssd_chunk_out_kernel(const SSDK p, int nhg, int ngroups) {
+__global__ __launch_bounds__(Q * 4 / out_tiles_per_wave<Q>(), 2) void ssd_chunk_out_kernel(const SSDK p, int nhg,
+                                                                                          int64_t nq) {
     constexpr int HG = OutCfg<N>::HG;
+    constexpr int TPW = out_tiles_per_wave<Q>();   // 16-row tiles per wave
+    constexpr int NW = Q / (16 * TPW);        // waves
+    constexpr int NTH = NW * 64;              // threads
     constexpr int TBS = Q / 64;               // 64-row time blocks per chunk
     constexpr int KN = N / 32;                // k steps over the state dimension
     constexpr int SPL = Q / 64;
@@ -292,43 +321,48 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_out_kernel(const SSDK p
     constexpr int BB_BYTES = 64 * LDB * 2;
     constexpr int XT_BYTES = HG * kP * LDX * 2;
     constexpr int SIN_BYTES = SIN_HEADS * kP * LDB * 2;
-    constexpr int OT_BYTES = 4 * 16 * LDO * 4;
-    constexpr int R0_BYTES = std::max(BB_BYTES, OT_BYTES);   // B block, later the output tile
+    constexpr int OT_BYTES = NW * 16 * LDO * 4;
+    constexpr int R0_BYTES = std::max(BB_BYTES, OT_BYTES);   // B block, later the output tiles
     constexpr int U_BYTES = std::max(R0_BYTES + XT_BYTES, SIN_BYTES);
-    constexpr int BV = 64 * N / 8 / kThreads;     // 16-byte B vectors per thread per block
-    constexpr int XB = HG * 128 / kThreads;       // 4x8 x blocks per thread per block
-    static_assert(BV >= 1 && XB >= 1, "staging split");
+    constexpr int NBV = 64 * N / 8;           // 16-byte B vectors per block
+    constexpr int BV = (NBV + NTH - 1) / NTH;
+    constexpr int NXV = HG * 64 * 8;          // 16-byte x vectors (8 p of one row) per block
+    constexpr int XV = (NXV + NTH - 1) / NTH;
+    constexpr int NSV = SIN_HEADS * kP * N / 8;   // 16-byte Sin vectors per staging
+    constexpr int SV = (NSV + NTH - 1) / NTH;
+    static_assert(NTH % 64 == 0 && NXV % 64 == 0, "staging split is per wave");
     __shared__ float cs2[HG][Q];              // cs * log2(e) per head
     __shared__ float dts[HG][Q];              // dt (0 past the end of the sequence)
-    __shared__ float wts[HG][Q];              // w_s dt_s for s before the time block
+    __shared__ float wts[TBS][HG][Q];         // w_s dt_s of time block tb (s < 64 tb)
     __shared__ __attribute__((aligned(16))) uint8_t ubuf[U_BYTES];
     uint16_t (*Bb)[LDB] = reinterpret_cast<uint16_t (*)[LDB]>(ubuf);
     uint16_t (*XT)[kP][LDX] = reinterpret_cast<uint16_t (*)[kP][LDX]>(ubuf + R0_BYTES);
     uint16_t (*SinL)[kP][LDB] = reinterpret_cast<uint16_t (*)[kP][LDB]>(ubuf);
     float (*Ot)[16][LDO] = reinterpret_cast<float (*)[16][LDO]>(ubuf);
 
-    // block -> (group, time block); the time blocks of one group share an XCD
-    int grp, tb;
-    if (TBS == 1) {
-        grp = blockIdx.x;
-        tb = 0;
-    } else {
-        const int id = blockIdx.x, rest = id / 8;
-        tb = rest % TBS;
-        grp = (rest / TBS) * 8 + id % 8;
-    }
-    if (grp >= ngroups) return;
-    // nhg: workgroups per group of B, C heads
-    const int hl = grp % nhg, gg = (grp / nhg) % p.G, c = (grp / (nhg * p.G)) % p.nc;
-    const int b = grp / (nhg * p.G * p.nc);
+    // block -> (chunk, head pair); the head pairs of one chunk share an XCD, so the
+    // chunk's B and C rows are shared in its L2
+    const int hpc = p.G * nhg;                         // head pairs per chunk
+    const int id = blockIdx.x, k8 = id >> 3;
+    const int64_t q = (int64_t)(k8 / hpc) * 8 + (id & 7);
+    if (q >= nq) return;                               // whole workgroup (uniform)
+    const int hp = k8 % hpc;
+    const int hl = hp % nhg, gg = hp / nhg;
+    const int c = (int)(q % p.nc), b = (int)(q / p.nc);
     // the wave index is uniform: readfirstlane keeps it (and every address built
     // from it) in SGPRs, so buffer resources need no per-lane loop
     const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r16 = lane & 15, kb = lane >> 4;
     const int64_t t_base = (int64_t)c * Q;
     const int T = (int)std::min<int64_t>(Q, p.L - t_base);
-    if (tb * 64 >= T) return;                         // whole block past the sequence (uniform)
-    const int t0 = tb * 64 + wv * 16;                 // this wave's first row
+    const int nsb = (T + 63) / 64;                     // 64-row blocks holding steps
+    // this wave's group of row tiles (two tiles: w and w + 4 share a SIMD, so they
+    // take groups w and 7 - w)
+    const int pi = (TPW == 2 && NW == 8 && wv >= 4) ? 11 - wv : wv;
+    const int t0 = pi * 16 * TPW;                      // this wave's first row
+    const int tb = t0 >> 6;                            // the time block of its tiles
+    const int tl0 = (t0 >> 4) & 3;                     // index of its first tile within it
+    const bool live = tb < nsb;                        // the block has steps (uniform)
     const int h0 = gg * p.hpg + hl * HG;               // first head of this workgroup
     const int hend = (gg + 1) * p.hpg;                 // heads of the group end here
     const int GN = p.G * N;                            // B, C elements per time step
@@ -340,21 +374,24 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_out_kernel(const SSDK p
 
     // next block of B and x into registers. Buffer resources cover the rows of the
     // block that exist (s < T), so rows past the sequence read as 0; a head past H
-    // gets an offset outside every resource.
-    u32x4 breg[BV], xreg[XB][4];
-    uint32_t boff[BV], xoff[XB][4];
+    // gets an offset outside every resource. Threads past the vectors of a block
+    // load nothing (whole waves, so the tests are uniform). A lane holds one row of
+    // 8 p of x (8 lanes read a 128-byte row) and writes its 8 values into the
+    // transposed rows one by one, starting at element pc so that the 8 lanes of a
+    // row write to 8 different p rows (different banks) at every step.
+    u32x4 breg[BV], xreg[XV];
+    uint32_t boff[BV], xoff[XV];
 #pragma unroll
     for (int i = 0; i < BV; ++i) {
-        const int v = tid + i * kThreads;
+        const int v = tid + i * NTH;
         boff[i] = (uint32_t)(v / (N / 8) * GN + (v % (N / 8)) * 8) * 2u;
     }
 #pragma unroll
-    for (int i = 0; i < XB; ++i) {
-        const int blk = tid + i * kThreads;
-        const int j = blk >> 7, g = blk & 15, po = (blk & 127) >> 4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            xoff[i][e] = h0 + j < hend ? (uint32_t)(((4 * g + e) * xstride + (h0 + j) * kP + po * 8) * 2) : 0x80000000u;
+    for (int i = 0; i < XV; ++i) {
+        const int v = tid + i * NTH;
+        const int pc = v & 7, sr = (v >> 3) & 63, j = v >> 9;
+        xoff[i] = (v < NXV && h0 + j < hend) ? (uint32_t)((sr * xstride + (h0 + j) * kP + pc * 8) * 2)
+                                             : 0x80000000u;
     }
     auto fetch = [&](int sb) {
         const int s0 = sb * 64;
@@ -362,41 +399,55 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_out_kernel(const SSDK p
         const rsrc_t rb = make_rsrc_u(Brow + (int64_t)s0 * GN, (uint32_t)(rows * GN * 2));
         const rsrc_t rx = make_rsrc_u(Xrow + (int64_t)s0 * xstride, (uint32_t)(rows * xstride * 2));
 #pragma unroll
-        for (int i = 0; i < BV; ++i) breg[i] = load16(rb, boff[i]);
+        for (int i = 0; i < BV; ++i)
+            if (wv * 64 + i * NTH < NBV) breg[i] = load16(rb, boff[i]);
 #pragma unroll
-        for (int i = 0; i < XB; ++i)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) xreg[i][e] = load16(rx, xoff[i][e]);
+        for (int i = 0; i < XV; ++i)
+            if (wv * 64 + i * NTH < NXV) xreg[i] = load16(rx, xoff[i]);
     };
     auto stash = [&]() {
 #pragma unroll
         for (int i = 0; i < BV; ++i) {
-            const int v = tid + i * kThreads;
-            *(u32x4 *)&Bb[v / (N / 8)][(v % (N / 8)) * 8] = breg[i];
+            const int v = tid + i * NTH;
+            if (wv * 64 + i * NTH < NBV) *(u32x4 *)&Bb[v / (N / 8)][(v % (N / 8)) * 8] = breg[i];
         }
 #pragma unroll
-        for (int i = 0; i < XB; ++i) {
-            const int blk = tid + i * kThreads;
-            const int j = blk >> 7, g = blk & 15, po = (blk & 127) >> 4;
-            store_transposed(xreg[i], &XT[j][0][0], LDX, po * 8, perm_s(4 * g));
+        for (int i = 0; i < XV; ++i) {
+            const int v = tid + i * NTH;
+            if (wv * 64 + i * NTH < NXV) {
+                const int pc = v & 7, sr = (v >> 3) & 63, j = v >> 9;
+                // rotate the 8 values so that element e is the row's element (e + pc) & 7
+                u32x4 w = xreg[i];
+                if (pc & 4) w = u32x4{w[2], w[3], w[0], w[1]};
+                if (pc & 2) w = u32x4{w[1], w[2], w[3], w[0]};
+                if (pc & 1)
+                    w = u32x4{__builtin_amdgcn_alignbit(w[1], w[0], 16), __builtin_amdgcn_alignbit(w[2], w[1], 16),
+                              __builtin_amdgcn_alignbit(w[3], w[2], 16), __builtin_amdgcn_alignbit(w[0], w[3], 16)};
+                uint16_t *col = &XT[j][pc * 8][perm_s(sr)];
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    col[((e + pc) & 7) * LDX] = (uint16_t)(e & 1 ? w[e >> 1] >> 16 : w[e >> 1]);
+            }
         }
     };
     // Sin of SIN_HEADS heads at a time through registers into LDS
-    constexpr int SV = SIN_HEADS * kP * N / 8 / kThreads;
     const uint16_t *sin_c = p.sin + ((int64_t)b * p.nc + c) * p.H * (int64_t)kP * N;
     u32x4 sreg[SV];
     auto sin_fetch = [&](int j0) {
         const int nh = std::max(0, std::min(SIN_HEADS, hend - (h0 + j0)));
         const rsrc_t rs = make_rsrc_u(sin_c + (int64_t)(h0 + j0) * kP * N, (uint32_t)(nh * kP * N * 2));
 #pragma unroll
-        for (int i = 0; i < SV; ++i) sreg[i] = load16(rs, (uint32_t)(tid + i * kThreads) * 16u);
+        for (int i = 0; i < SV; ++i)
+            if (wv * 64 + i * NTH < NSV) sreg[i] = load16(rs, (uint32_t)(tid + i * NTH) * 16u);
     };
     auto sin_stash = [&]() {
 #pragma unroll
         for (int i = 0; i < SV; ++i) {
-            const int v = tid + i * kThreads;
-            const int jj = v / (kP * N / 8), rem = v % (kP * N / 8);
-            *(u32x4 *)&SinL[jj][rem / (N / 8)][(rem % (N / 8)) * 8] = sreg[i];
+            const int v = tid + i * NTH;
+            if (wv * 64 + i * NTH < NSV) {
+                const int jj = v / (kP * N / 8), rem = v % (kP * N / 8);
+                *(u32x4 *)&SinL[jj][rem / (N / 8)][(rem % (N / 8)) * 8] = sreg[i];
+            }
         }
     };
     fetch(0);
@@ -412,22 +463,34 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_out_kernel(const SSDK p
             dts[wv][lane * SPL + i] = dtv[i];
         }
     }
-    const int trow = std::min(t0 + r16, T - 1);
-    bf16x8 cfr[KN];
+    bf16x8 cfr[TPW][KN];
+    if (live) {
 #pragma unroll
-    for (int k = 0; k < KN; ++k)
-        cfr[k] = as_bf16x8(*(const u32x4 *)(Crow + (int64_t)trow * GN + 32 * k + 8 * kb));
+        for (int tt = 0; tt < TPW; ++tt) {
+            const int trow = std::min(t0 + 16 * tt + r16, T - 1);
+#pragma unroll
+            for (int k = 0; k < KN; ++k)
+                cfr[tt][k] = as_bf16x8(*(const u32x4 *)(Crow + (int64_t)trow * GN + 32 * k + 8 * kb));
+        }
+    }
     sin_stash();
     if (HG > SIN_HEADS) sin_fetch(SIN_HEADS);
     __syncthreads();
-    const int r = tb * 64 - 1;
-    for (int v = tid; v < HG * tb * 64; v += kThreads) {
-        const int j = v / (tb * 64), s = v % (tb * 64);
-        wts[j][s] = fast_exp2(cs2[j][r] - cs2[j][s]) * dts[j][s];
+    // w_s dt_s of every time block after the first: r = 64 tb - 1, s <= r
+    for (int v = tid; v < (TBS - 1) * HG * Q; v += NTH) {
+        const int s = v % Q, j = (v / Q) % HG, tbi = v / (Q * HG) + 1;
+        if (s < 64 * tbi) wts[tbi][j][s] = fast_exp2(cs2[j][64 * tbi - 1] - cs2[j][s]) * dts[j][s];
     }
 
-    // entering state: Y = exp(cs_r) C Sin (scaled by a_t further down)
-    f32x4 yo[HG][4];
+    // entering state: Y = exp(cs_r) C Sin (scaled by a_t further down); each Sin
+    // operand feeds both tiles
+    f32x4 yo[TPW][HG][4];
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+        for (int j = 0; j < HG; ++j)
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) yo[tt][j][qq] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j0 = 0; j0 < HG; j0 += SIN_HEADS) {
         if (j0) {
@@ -436,170 +499,197 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_out_kernel(const SSDK p
             __syncthreads();
             if (j0 + SIN_HEADS < HG) sin_fetch(j0 + SIN_HEADS);
         }
+        if (live) {
 #pragma unroll
-        for (int jj = 0; jj < SIN_HEADS; ++jj) {
+            for (int jj = 0; jj < SIN_HEADS; ++jj) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int qq = 0; qq < 4; ++qq) {
 #pragma unroll
-                for (int k = 0; k < KN; ++k)
-                    a = mfma16x16x32(cfr[k], as_bf16x8(*(const u32x4 *)&SinL[jj][q * 16 + r16][32 * k + 8 * kb]), a);
-                yo[j0 + jj][q] = a;
+                    for (int k = 0; k < KN; ++k) {
+                        const bf16x8 sf = as_bf16x8(*(const u32x4 *)&SinL[jj][qq * 16 + r16][32 * k + 8 * kb]);
+#pragma unroll
+                        for (int tt = 0; tt < TPW; ++tt)
+                            yo[tt][j0 + jj][qq] = mfma16x16x32(cfr[tt][k], sf, yo[tt][j0 + jj][qq]);
+                    }
+                }
             }
         }
     }
+    const int r = tb * 64 - 1;
+    __syncthreads();                                   // the wts table is complete
+    if (live && tb) {
 #pragma unroll
-    for (int j = 0; j < HG; ++j) {
-        const float er = tb ? fast_exp2(cs2[j][r]) : 1.0f;
+        for (int j = 0; j < HG; ++j) {
+            const float er = fast_exp2(cs2[j][r]);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) yo[j][q] *= er;
+            for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) yo[tt][j][qq] *= er;
+        }
     }
-    __syncthreads();
     stash();
     __syncthreads();
 
-    for (int sb = 0; sb <= tb; ++sb) {
-        if (sb < tb) fetch(sb + 1);
-        const int s0 = sb * 64;
-        const bool diag = sb == tb;
-        // G^T[s][t]: lane holds s = s0 + 16u + 4kb + i, t = t0 + r16
-        f32x4 g[4];
+    for (int sb = 0; sb < nsb; ++sb) {
+        if (sb + 1 < nsb) fetch(sb + 1);
+        if (live && sb <= tb) {
+            const int s0 = sb * 64;
+            const bool diag = sb == tb;
+            if (diag) {
+                // scale what came before the time block by a_t (rows t0 + 16tt + 4kb + i)
+                // and add D x of these rows from the staged (diagonal) block of x
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            g[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (!diag || u <= wv) {
+                for (int j = 0; j < HG; ++j) {
+                    const float cr = tb ? cs2[j][r] : 0.0f;
+                    const float dsk = (p.Dskip && h0 + j < hend) ? p.Dskip[h0 + j] : 0.0f;
 #pragma unroll
-                for (int k = 0; k < KN; ++k)
-                    g[u] = mfma16x16x32(as_bf16x8(*(const u32x4 *)&Bb[16 * u + r16][32 * k + 8 * kb]), cfr[k], g[u]);
-            }
-        }
-        if (!diag) {
+                    for (int tt = 0; tt < TPW; ++tt) {
+                        const f32x4 crow = *(const f32x4 *)&cs2[j][t0 + 16 * tt + 4 * kb];
 #pragma unroll
-            for (int j = 0; j < HG; ++j) {
+                        for (int qq = 0; qq < 4; ++qq) {
+                            const u32x2 xv =
+                                *(const u32x2 *)&XT[j][qq * 16 + r16][perm_s(16 * (tl0 + tt) + 4 * kb)];
+                            const float xs[4] = {bf16_lo(xv[0]), bf16_hi(xv[0]), bf16_lo(xv[1]), bf16_hi(xv[1])};
 #pragma unroll
-                for (int a = 0; a < 2; ++a) {
-                    const f32x4 w0 = *(const f32x4 *)&wts[j][s0 + 32 * a + 4 * kb];
-                    const f32x4 w1 = *(const f32x4 *)&wts[j][s0 + 32 * a + 16 + 4 * kb];
-                    const bf16x8 mfr = as_bf16x8(u32x4{
-                        pack_bf16(g[2 * a][0] * w0[0], g[2 * a][1] * w0[1]),
-                        pack_bf16(g[2 * a][2] * w0[2], g[2 * a][3] * w0[3]),
-                        pack_bf16(g[2 * a + 1][0] * w1[0], g[2 * a + 1][1] * w1[1]),
-                        pack_bf16(g[2 * a + 1][2] * w1[2], g[2 * a + 1][3] * w1[3])});
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        yo[j][q] = mfma16x16x32(mfr, as_bf16x8(*(const u32x4 *)&XT[j][q * 16 + r16][32 * a + 8 * kb]),
-                                                yo[j][q]);
-                }
-                __builtin_amdgcn_sched_barrier(0);   // keep one head's operands live at a time
-            }
-        } else {
-            const int tcol = t0 + r16;                // the A-operand row of this lane
-#pragma unroll
-            for (int j = 0; j < HG; ++j) {
-                const float cr = tb ? cs2[j][r] : 0.0f;
-                // a_t for the accumulator rows t0 + 4kb + i
-                const f32x4 crow = *(const f32x4 *)&cs2[j][t0 + 4 * kb];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float at = fast_exp2(crow[i] - cr);
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) yo[j][q][i] *= at;
-                }
-                const float ct = cs2[j][tcol];
-#pragma unroll
-                for (int a = 0; a < 2; ++a) {
-                    if (32 * a > 16 * wv + 15) continue;   // every s of this half is after every row
-                    float v[8];
-#pragma unroll
-                    for (int hh = 0; hh < 2; ++hh) {
-                        const int sb0 = s0 + 32 * a + 16 * hh + 4 * kb;
-                        const f32x4 cd = *(const f32x4 *)&cs2[j][sb0];
-                        const f32x4 dd = *(const f32x4 *)&dts[j][sb0];
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const float m = g[2 * a + hh][i] * fast_exp2(ct - cd[i]) * dd[i];
-                            v[4 * hh + i] = sb0 + i <= tcol ? m : 0.0f;
+                            for (int i = 0; i < 4; ++i)
+                                yo[tt][j][qq][i] = fmaf(dsk, xs[i], yo[tt][j][qq][i] * fast_exp2(crow[i] - cr));
                         }
                     }
-                    const bf16x8 mfr = as_bf16x8(u32x4{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]),
-                                                       pack_bf16(v[4], v[5]), pack_bf16(v[6], v[7])});
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        yo[j][q] = mfma16x16x32(mfr, as_bf16x8(*(const u32x4 *)&XT[j][q * 16 + r16][32 * a + 8 * kb]),
-                                                yo[j][q]);
                 }
-                __builtin_amdgcn_sched_barrier(0);
+            }
+            // one 32-column half of s at a time: G^T[s][t] tiles u = 2a, 2a + 1 for
+            // every row tile of the wave; lane holds s = s0 + 16u + 4kb + i, t = t0 +
+            // 16tt + r16. On the diagonal block tile tt needs u <= tl0 + tt, and a half
+            // after all of its rows is skipped.
+#pragma unroll
+            for (int a = 0; a < 2; ++a) {
+                if (diag && 32 * a > 16 * (tl0 + TPW - 1) + 15) continue;   // every s after every row
+                bool need[TPW];
+#pragma unroll
+                for (int tt = 0; tt < TPW; ++tt) need[tt] = !diag || 32 * a <= 16 * (tl0 + tt) + 15;
+                f32x4 g[TPW][2];
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int u = 2 * a + hh;
+#pragma unroll
+                    for (int tt = 0; tt < TPW; ++tt) g[tt][hh] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    if (!diag || u <= tl0 + TPW - 1) {   // the last tile needs it
+#pragma unroll
+                        for (int k = 0; k < KN; ++k) {
+                            const bf16x8 bf = as_bf16x8(*(const u32x4 *)&Bb[16 * u + r16][32 * k + 8 * kb]);
+#pragma unroll
+                            for (int tt = 0; tt < TPW; ++tt)
+                                if (!diag || u <= tl0 + tt) g[tt][hh] = mfma16x16x32(bf, cfr[tt][k], g[tt][hh]);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < HG; ++j) {
+                    bf16x8 mfr[TPW];
+                    if (!diag) {
+                        const f32x4 w0 = *(const f32x4 *)&wts[tb][j][s0 + 32 * a + 4 * kb];
+                        const f32x4 w1 = *(const f32x4 *)&wts[tb][j][s0 + 32 * a + 16 + 4 * kb];
+#pragma unroll
+                        for (int tt = 0; tt < TPW; ++tt)
+                            mfr[tt] = as_bf16x8(u32x4{pack_bf16(g[tt][0][0] * w0[0], g[tt][0][1] * w0[1]),
+                                                      pack_bf16(g[tt][0][2] * w0[2], g[tt][0][3] * w0[3]),
+                                                      pack_bf16(g[tt][1][0] * w1[0], g[tt][1][1] * w1[1]),
+                                                      pack_bf16(g[tt][1][2] * w1[2], g[tt][1][3] * w1[3])});
+                    } else {
+#pragma unroll
+                        for (int tt = 0; tt < TPW; ++tt) {
+                            const int tcol = t0 + 16 * tt + r16;   // the A-operand row of this lane
+                            const float ct = cs2[j][tcol];
+                            float v[8];
+#pragma unroll
+                            for (int hh = 0; hh < 2; ++hh) {
+                                const int sb0 = s0 + 32 * a + 16 * hh + 4 * kb;
+                                const f32x4 cd = *(const f32x4 *)&cs2[j][sb0];
+                                const f32x4 dd = *(const f32x4 *)&dts[j][sb0];
+#pragma unroll
+                                for (int i = 0; i < 4; ++i) {
+                                    const float m = g[tt][hh][i] * fast_exp2(ct - cd[i]) * dd[i];
+                                    v[4 * hh + i] = sb0 + i <= tcol ? m : 0.0f;
+                                }
+                            }
+                            mfr[tt] = as_bf16x8(u32x4{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]),
+                                                      pack_bf16(v[4], v[5]), pack_bf16(v[6], v[7])});
+                        }
+                    }
+#pragma unroll
+                    for (int qq = 0; qq < 4; ++qq) {
+                        const bf16x8 xf = as_bf16x8(*(const u32x4 *)&XT[j][qq * 16 + r16][32 * a + 8 * kb]);
+#pragma unroll
+                        for (int tt = 0; tt < TPW; ++tt)
+                            if (need[tt]) yo[tt][j][qq] = mfma16x16x32(mfr[tt], xf, yo[tt][j][qq]);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);   // one head's operands live at a time
+                }
             }
         }
-        if (sb < tb) {
+        if (sb + 1 < nsb) {
             __syncthreads();
             stash();
             __syncthreads();
         }
     }
 
-    // y = Y + D x, gated by silu(z). x of these rows is the last staged block
-    // (the diagonal one), still in LDS; z is fetched for every head at once. Each
-    // head's tile then goes through the wave's own LDS rows so that a lane writes
-    // rows of 8 bf16.
-    u32x4 zreg[HG][2];
-    if (!F32OUT && p.z) {
+    // y = Y + D x, gated by silu(z); z is fetched for both tiles and heads at once.
+    // Each tile goes through the wave's own LDS rows so that a lane writes rows of
+    // 8 bf16.
+    u32x4 zreg[TPW][HG][2];
+    if (!F32OUT && p.z && live) {
 #pragma unroll
-        for (int j = 0; j < HG; ++j)
+        for (int tt = 0; tt < TPW; ++tt)
 #pragma unroll
-            for (int rr = 0; rr < 2; ++rr) {
-                const int t = std::min(t0 + rr * 8 + (lane >> 3), T - 1), h = std::min(h0 + j, hend - 1);
-                zreg[j][rr] = *(const u32x4 *)(p.z + (((int64_t)b * p.L + t_base + t) * p.H + h) * kP + (lane & 7) * 8);
-            }
-    }
+            for (int j = 0; j < HG; ++j)
 #pragma unroll
-    for (int j = 0; j < HG; ++j) {
-        const float dsk = (p.Dskip && h0 + j < hend) ? p.Dskip[h0 + j] : 0.0f;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const u32x2 xv = *(const u32x2 *)&XT[j][q * 16 + r16][perm_s(16 * wv + 4 * kb)];
-            yo[j][q][0] = fmaf(dsk, bf16_lo(xv[0]), yo[j][q][0]);
-            yo[j][q][1] = fmaf(dsk, bf16_hi(xv[0]), yo[j][q][1]);
-            yo[j][q][2] = fmaf(dsk, bf16_lo(xv[1]), yo[j][q][2]);
-            yo[j][q][3] = fmaf(dsk, bf16_hi(xv[1]), yo[j][q][3]);
-        }
+                for (int rr = 0; rr < 2; ++rr) {
+                    const int t = std::min(t0 + 16 * tt + rr * 8 + (lane >> 3), T - 1), h = std::min(h0 + j, hend - 1);
+                    zreg[tt][j][rr] =
+                        *(const u32x4 *)(p.z + (((int64_t)b * p.L + t_base + t) * p.H + h) * kP + (lane & 7) * 8);
+                }
     }
     __syncthreads();                                   // every wave is done with the B block
+    if (!live) return;                                 // uniform; no barrier follows
 #pragma unroll
-    for (int j = 0; j < HG; ++j) {
-        const int h = h0 + j;
-        if (h >= hend) break;                          // uniform
+    for (int tt = 0; tt < TPW; ++tt) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+        for (int j = 0; j < HG; ++j) {
+            const int h = h0 + j;
+            if (h >= hend) break;                      // uniform
 #pragma unroll
-            for (int i = 0; i < 4; ++i) Ot[wv][4 * kb + i][q * 16 + r16] = yo[j][q][i];
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // the wave's own rows only
+            for (int qq = 0; qq < 4; ++qq)
 #pragma unroll
-        for (int rr = 0; rr < 2; ++rr) {
-            const int row = rr * 8 + (lane >> 3), c8 = (lane & 7) * 8;
-            const int t = t0 + row;
-            const f32x4 o0 = *(const f32x4 *)&Ot[wv][row][c8];
-            const f32x4 o1 = *(const f32x4 *)&Ot[wv][row][c8 + 4];
-            if (F32OUT && t < T) {
-                float *dst = p.y32 + (((int64_t)b * p.L + t_base + t) * p.H + h) * kP + c8;
-                *(f32x4 *)dst = o0;
-                *(f32x4 *)(dst + 4) = o1;
-            } else if (t < T) {
-                const float o[8] = {o0[0], o0[1], o0[2], o0[3], o1[0], o1[1], o1[2], o1[3]};
-                u32x4 outv;
+                for (int i = 0; i < 4; ++i) Ot[wv][4 * kb + i][qq * 16 + r16] = yo[tt][j][qq][i];
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // the wave's own rows only
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    float y0 = o[2 * e], y1 = o[2 * e + 1];
-                    if (p.z) {
-                        y0 *= silu_f32(bf16_lo(zreg[j][rr][e]));
-                        y1 *= silu_f32(bf16_hi(zreg[j][rr][e]));
+            for (int rr = 0; rr < 2; ++rr) {
+                const int row = rr * 8 + (lane >> 3), c8 = (lane & 7) * 8;
+                const int t = t0 + 16 * tt + row;
+                const f32x4 o0 = *(const f32x4 *)&Ot[wv][row][c8];
+                const f32x4 o1 = *(const f32x4 *)&Ot[wv][row][c8 + 4];
+                if (F32OUT && t < T) {
+                    float *dst = p.y32 + (((int64_t)b * p.L + t_base + t) * p.H + h) * kP + c8;
+                    *(f32x4 *)dst = o0;
+                    *(f32x4 *)(dst + 4) = o1;
+                } else if (t < T) {
+                    const float o[8] = {o0[0], o0[1], o0[2], o0[3], o1[0], o1[1], o1[2], o1[3]};
+                    u32x4 outv;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        float y0 = o[2 * e], y1 = o[2 * e + 1];
+                        if (p.z) {
+                            y0 *= silu_f32(bf16_lo(zreg[tt][j][rr][e]));
+                            y1 *= silu_f32(bf16_hi(zreg[tt][j][rr][e]));
+                        }
+                        outv[e] = pack_bf16(y0, y1);
                     }
-                    outv[e] = pack_bf16(y0, y1);
+                    *(u32x4 *)(p.y + (((int64_t)b * p.L + t_base + t) * p.H + h) * kP + c8) = outv;
                 }
-                *(u32x4 *)(p.y + (((int64_t)b * p.L + t_base + t) * p.H + h) * kP + c8) = outv;
             }
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         }
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     }
 }
 
@@ -616,10 +706,10 @@ void launch_nq(const SSDK &k, int batch, hipStream_t s) {
     hipLaunchKernelGGL(ssd_state_pass_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
                        k, N, total);
     const int nhg = (k.hpg + OutCfg<N>::HG - 1) / OutCfg<N>::HG;
-    const int64_t ngroups = (int64_t)batch * k.nc * k.G * nhg;
-    const int64_t nblocks = Q == 64 ? ngroups : (ngroups + 7) / 8 * 8 * (Q / 64);
-    hipLaunchKernelGGL((ssd_chunk_out_kernel<N, Q, false>), dim3((unsigned)nblocks), dim3(kThreads), 0, s, k, nhg,
-                       (int)ngroups);
+    const int64_t nq = (int64_t)batch * k.nc;            // (batch, chunk) pairs
+    const int64_t nblocks = (nq + 7) / 8 * 8 * (k.G * nhg);
+    hipLaunchKernelGGL((ssd_chunk_out_kernel<N, Q, false>), dim3((unsigned)nblocks), dim3(Q * 4 / out_tiles_per_wave<Q>()), 0, s, k, nhg,
+                       nq);
 }
 
 template <int N>
@@ -642,10 +732,10 @@ void recompute_nq(const SSDK &k, int batch, int what, hipStream_t s) {
                            k, N, total);
     } else if (what == 1) {   // fp32 pre-gate output
         const int nhg = (k.hpg + OutCfg<N>::HG - 1) / OutCfg<N>::HG;
-        const int64_t ngroups = (int64_t)batch * k.nc * k.G * nhg;
-        const int64_t nblocks = Q == 64 ? ngroups : (ngroups + 7) / 8 * 8 * (Q / 64);
-        hipLaunchKernelGGL((ssd_chunk_out_kernel<N, Q, true>), dim3((unsigned)nblocks), dim3(kThreads), 0, s, k,
-                           nhg, (int)ngroups);
+        const int64_t nq = (int64_t)batch * k.nc;
+        const int64_t nblocks = (nq + 7) / 8 * 8 * (k.G * nhg);
+        hipLaunchKernelGGL((ssd_chunk_out_kernel<N, Q, true>), dim3((unsigned)nblocks), dim3(Q * 4 / out_tiles_per_wave<Q>()), 0, s, k,
+                           nhg, nq);
     } else {                  // adjoint aggregates (exp(cs_t) weights)
         hipLaunchKernelGGL((ssd_chunk_state_kernel<N, Q, 2>), cs_grid, dim3(kThreads), 0, s, k);
     }
@@ -674,7 +764,7 @@ SSDPlan ssd_plan(const ssm_ssd_args &a) {
     pl.nchunks = (a.seqlen + a.chunk - 1) / a.chunk;
     const size_t elems = (size_t)a.batch * pl.nchunks * a.nheads * a.dstate * a.headdim;
     pl.states_offset = 0;
-    pl.sin_offset = up(elems * sizeof(float));
+    pl.sin_offset = up(elems * sizeof(uint16_t));     // bf16 chunk states first
     pl.decay_offset = pl.sin_offset + up(elems * sizeof(uint16_t));
     pl.bytes = pl.decay_offset + up((size_t)a.batch * a.nheads * pl.nchunks * sizeof(float));
     return pl;
@@ -696,7 +786,7 @@ ssm_status ssd_launch(const ssm_ssd_args &a, const SSDPlan &plan, hipStream_t s,
         k.Bm = (const uint16_t *)a.Bm; k.Cm = (const uint16_t *)a.Cm; k.z = (const uint16_t *)a.z;
         k.dt_bias = a.dt_bias; k.A = a.A; k.Dskip = a.Dskip; k.h0 = a.h0;
         k.y = (uint16_t *)a.y; k.h_final = a.h_final;
-        k.states = (float *)((char *)a.workspace + plan.states_offset);
+        k.states16 = (uint16_t *)((char *)a.workspace + plan.states_offset);
         k.sin = (uint16_t *)((char *)a.workspace + plan.sin_offset);
         k.decay = (float *)((char *)a.workspace + plan.decay_offset);
         k.L = a.seqlen; k.H = (int32_t)a.nheads; k.nc = (int32_t)plan.nchunks;
