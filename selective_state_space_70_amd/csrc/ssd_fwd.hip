@@ -65,13 +65,15 @@ __global__ __launch_bounds__(kThreads, (N > 128 || MODE != 0) ? 1 : 2) void ssd_
     __shared__ __attribute__((aligned(16))) uint16_t XT[4][kP][LDT];
     __shared__ __attribute__((aligned(16))) uint16_t XL[SPLIT ? 4 : 1][SPLIT ? kP : 1][SPLIT ? LDT : 8];
 
-    const int c = blockIdx.x, b = blockIdx.z;
+    // head groups vary fastest: the workgroups of one chunk run together and read
+    // whole rows of x between them
+    const int c = blockIdx.y, b = blockIdx.z;
     // the wave index is uniform: readfirstlane keeps it (and every address built
     // from it) in SGPRs, so buffer resources need no per-lane loop
     const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r16 = lane & 15, kb = lane >> 4;
     const int hb = (p.hpg + 3) / 4;                   // workgroups per group of heads
-    const int g = blockIdx.y / hb, hl = (blockIdx.y % hb) * 4 + wv;
+    const int g = blockIdx.x / hb, hl = (blockIdx.x % hb) * 4 + wv;
     const bool head_ok = hl < p.hpg;
     const int h = g * p.hpg + (head_ok ? hl : p.hpg - 1);   // clamped into the group
     const int hc = h;
@@ -700,7 +702,7 @@ __global__ __launch_bounds__(256) void ssd_copy_state_kernel(const float *h0, fl
 
 template <int N, int Q>
 void launch_nq(const SSDK &k, int batch, hipStream_t s) {
-    hipLaunchKernelGGL((ssd_chunk_state_kernel<N, Q, 0>), dim3((unsigned)k.nc, (unsigned)(k.G * ((k.hpg + 3) / 4)), (unsigned)batch),
+    hipLaunchKernelGGL((ssd_chunk_state_kernel<N, Q, 0>), dim3((unsigned)(k.G * ((k.hpg + 3) / 4)), (unsigned)k.nc, (unsigned)batch),
                        dim3(kThreads), 0, s, k);
     const int64_t total = (int64_t)batch * k.H * kP * N / 4;
     hipLaunchKernelGGL(ssd_state_pass_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
@@ -724,7 +726,7 @@ void launch_n(const SSDK &k, int batch, int Q, hipStream_t s) {
 // pieces of the forward for the gradient pass
 template <int N, int Q>
 void recompute_nq(const SSDK &k, int batch, int what, hipStream_t s) {
-    const dim3 cs_grid((unsigned)k.nc, (unsigned)(k.G * ((k.hpg + 3) / 4)), (unsigned)batch);
+    const dim3 cs_grid((unsigned)(k.G * ((k.hpg + 3) / 4)), (unsigned)k.nc, (unsigned)batch);
     if (what == 0) {          // split-precision chunk states, then the entering states
         hipLaunchKernelGGL((ssd_chunk_state_kernel<N, Q, 1>), cs_grid, dim3(kThreads), 0, s, k);
         const int64_t total = (int64_t)batch * k.H * kP * N / 4;
