@@ -198,20 +198,38 @@ __global__ __launch_bounds__(kThreads, (N > 128 || MODE != 0) ? 1 : 2) void ssd_
             }
         }
         // S_c[p][n]: lane holds n = pass*NP + 16i + 4kb + e, p = 16j + r16 -> 16-byte
-        // stores (8-byte stores of bf16 in the forward)
+        // stores, 4 lanes covering 64 contiguous bytes of a row. In bf16 (the forward)
+        // lanes kb and kb ^ 1 trade halves of tiles i and i + 1 first, so that a lane
+        // holds 8 consecutive n: n = 16i + 8(kb / 2) .. for even kb, n = 16i + 16 +
+        // 8(kb / 2) .. for odd kb.
         if (head_ok) {
             const int64_t o = (((int64_t)b * p.nc + c) * p.H + h) * (int64_t)kP * N;
+            if constexpr (MODE == 0) {
+                static_assert(NT % 2 == 0, "tiles are paired");
+                const bool odd = kb & 1;
 #pragma unroll
-            for (int i = 0; i < NT; ++i)
+                for (int i = 0; i < NT; i += 2)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int e = (j * 16 + r16) * N + pass * NP + i * 16 + kb * 4;
-                    if constexpr (MODE == 0)
-                        *(u32x2 *)(p.states16 + o + e) = u32x2{pack_bf16(acc[i][j][0], acc[i][j][1]),
-                                                               pack_bf16(acc[i][j][2], acc[i][j][3])};
-                    else
-                        *(f32x4 *)(p.states + o + e) = acc[i][j];
-                }
+                    for (int j = 0; j < 4; ++j) {
+                        const u32x2 lo = u32x2{pack_bf16(acc[i][j][0], acc[i][j][1]),
+                                               pack_bf16(acc[i][j][2], acc[i][j][3])};
+                        const u32x2 hi = u32x2{pack_bf16(acc[i + 1][j][0], acc[i + 1][j][1]),
+                                               pack_bf16(acc[i + 1][j][2], acc[i + 1][j][3])};
+                        const u32x2 give = odd ? lo : hi;
+                        const u32x2 got = u32x2{(uint32_t)__shfl_xor((int)give[0], 16, 64),
+                                                (uint32_t)__shfl_xor((int)give[1], 16, 64)};
+                        const u32x4 out = odd ? u32x4{got[0], got[1], hi[0], hi[1]}
+                                              : u32x4{lo[0], lo[1], got[0], got[1]};
+                        const int n0 = pass * NP + i * 16 + (odd ? 16 : 0) + (kb >> 1) * 8;
+                        *(u32x4 *)(p.states16 + o + (j * 16 + r16) * N + n0) = out;
+                    }
+            } else {
+#pragma unroll
+                for (int i = 0; i < NT; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        *(f32x4 *)(p.states + o + (j * 16 + r16) * N + pass * NP + i * 16 + kb * 4) = acc[i][j];
+            }
         }
     }
 }
