@@ -323,13 +323,20 @@ struct OutCfg {
 // 256, which measured slower than 16 waves with one tile each: one tile per wave.
 template <int Q>
 constexpr int out_tiles_per_wave() { return 1; }
+// Workgroups per (chunk, head pair). At chunk 256 two 8-wave workgroups share the
+// chunk's time blocks (0 and 3, 1 and 2: equal causal work), so two of them fit a CU
+// and one's loads overlap the other's arithmetic. With N = 256 the C fragments do
+// not fit the 128 registers that takes.
+template <int N, int Q>
+constexpr int out_split() { return Q == 256 && N <= 128 ? 2 : 1; }
 
 template <int N, int Q, bool F32OUT>
-__global__ __launch_bounds__(Q * 4 / out_tiles_per_wave<Q>(), 2) void ssd_chunk_out_kernel(const SSDK p, int nhg,
-                                                                                          int64_t nq) {
+__global__ __launch_bounds__((Q * 4 / (out_tiles_per_wave<Q>() * out_split<N, Q>())), (out_split<N, Q>() == 2 ? 4 : 2))
+void ssd_chunk_out_kernel(const SSDK p, int nhg, int64_t nq) {
     constexpr int HG = OutCfg<N>::HG;
     constexpr int TPW = out_tiles_per_wave<Q>();   // 16-row tiles per wave
-    constexpr int NW = Q / (16 * TPW);        // waves
+    constexpr int SPLIT = out_split<N, Q>();  // workgroups per (chunk, head pair)
+    constexpr int NW = Q / (16 * TPW * SPLIT);   // waves
     constexpr int NTH = NW * 64;              // threads
     constexpr int TBS = Q / 64;               // 64-row time blocks per chunk
     constexpr int KN = N / 32;                // k steps over the state dimension
@@ -360,13 +367,14 @@ __global__ __launch_bounds__(Q * 4 / out_tiles_per_wave<Q>(), 2) void ssd_chunk_
     uint16_t (*SinL)[kP][LDB] = reinterpret_cast<uint16_t (*)[kP][LDB]>(ubuf);
     float (*Ot)[16][LDO] = reinterpret_cast<float (*)[16][LDO]>(ubuf);
 
-    // block -> (chunk, head pair); the head pairs of one chunk share an XCD, so the
-    // chunk's B and C rows are shared in its L2
-    const int hpc = p.G * nhg;                         // head pairs per chunk
+    // block -> (chunk, head pair, part); the workgroups of one chunk share an XCD, so
+    // the chunk's B and C rows (and a head pair's entering states) are shared in its L2
+    const int upc = p.G * nhg * SPLIT;                 // workgroups per chunk
     const int id = blockIdx.x, k8 = id >> 3;
-    const int64_t q = (int64_t)(k8 / hpc) * 8 + (id & 7);
+    const int64_t q = (int64_t)(k8 / upc) * 8 + (id & 7);
     if (q >= nq) return;                               // whole workgroup (uniform)
-    const int hp = k8 % hpc;
+    const int unit = k8 % upc;
+    const int part = unit % SPLIT, hp = unit / SPLIT;
     const int hl = hp % nhg, gg = hp / nhg;
     const int c = (int)(q % p.nc), b = (int)(q / p.nc);
     // the wave index is uniform: readfirstlane keeps it (and every address built
@@ -376,11 +384,15 @@ __global__ __launch_bounds__(Q * 4 / out_tiles_per_wave<Q>(), 2) void ssd_chunk_
     const int64_t t_base = (int64_t)c * Q;
     const int T = (int)std::min<int64_t>(Q, p.L - t_base);
     const int nsb = (T + 63) / 64;                     // 64-row blocks holding steps
-    // this wave's group of row tiles (two tiles: w and w + 4 share a SIMD, so they
-    // take groups w and 7 - w)
+    if (SPLIT == 2 && part == 1 && nsb <= 1) return;   // its blocks 1 and 2 are empty (uniform)
+    // this wave's group of row tiles. Two tiles: w and w + 4 share a SIMD, so they take
+    // groups w and 7 - w. Split chunk: waves 0-3 own the first time block of the part
+    // (0 or 1), waves 4-7 the second (3 or 2).
     const int pi = (TPW == 2 && NW == 8 && wv >= 4) ? 11 - wv : wv;
-    const int t0 = pi * 16 * TPW;                      // this wave's first row
+    const int t0 = SPLIT == 2 ? (wv < 4 ? part : 3 - part) * 64 + (wv & 3) * 16 : pi * 16 * TPW;
     const int tb = t0 >> 6;                            // the time block of its tiles
+    // blocks of s this workgroup stages: up to its last time block
+    const int nsw = std::min(nsb, SPLIT == 2 ? 4 - part : TBS);
     const int tl0 = (t0 >> 4) & 3;                     // index of its first tile within it
     const bool live = tb < nsb;                        // the block has steps (uniform)
     const int h0 = gg * p.hpg + hl * HG;               // first head of this workgroup
@@ -550,8 +562,8 @@ __global__ __launch_bounds__(Q * 4 / out_tiles_per_wave<Q>(), 2) void ssd_chunk_
     stash();
     __syncthreads();
 
-    for (int sb = 0; sb < nsb; ++sb) {
-        if (sb + 1 < nsb) fetch(sb + 1);
+    for (int sb = 0; sb < nsw; ++sb) {
+        if (sb + 1 < nsw) fetch(sb + 1);
         if (live && sb <= tb) {
             const int s0 = sb * 64;
             const bool diag = sb == tb;
@@ -647,7 +659,7 @@ __global__ __launch_bounds__(Q * 4 / out_tiles_per_wave<Q>(), 2) void ssd_chunk_
                 }
             }
         }
-        if (sb + 1 < nsb) {
+        if (sb + 1 < nsw) {
             __syncthreads();
             stash();
             __syncthreads();
@@ -727,9 +739,9 @@ void launch_nq(const SSDK &k, int batch, hipStream_t s) {
                        k, N, total);
     const int nhg = (k.hpg + OutCfg<N>::HG - 1) / OutCfg<N>::HG;
     const int64_t nq = (int64_t)batch * k.nc;            // (batch, chunk) pairs
-    const int64_t nblocks = (nq + 7) / 8 * 8 * (k.G * nhg);
-    hipLaunchKernelGGL((ssd_chunk_out_kernel<N, Q, false>), dim3((unsigned)nblocks), dim3(Q * 4 / out_tiles_per_wave<Q>()), 0, s, k, nhg,
-                       nq);
+    const int64_t nblocks = (nq + 7) / 8 * 8 * (k.G * nhg * out_split<N, Q>());
+    hipLaunchKernelGGL((ssd_chunk_out_kernel<N, Q, false>), dim3((unsigned)nblocks),
+                       dim3(Q * 4 / (out_tiles_per_wave<Q>() * out_split<N, Q>())), 0, s, k, nhg, nq);
 }
 
 template <int N>
@@ -753,9 +765,9 @@ void recompute_nq(const SSDK &k, int batch, int what, hipStream_t s) {
     } else if (what == 1) {   // fp32 pre-gate output
         const int nhg = (k.hpg + OutCfg<N>::HG - 1) / OutCfg<N>::HG;
         const int64_t nq = (int64_t)batch * k.nc;
-        const int64_t nblocks = (nq + 7) / 8 * 8 * (k.G * nhg);
-        hipLaunchKernelGGL((ssd_chunk_out_kernel<N, Q, true>), dim3((unsigned)nblocks), dim3(Q * 4 / out_tiles_per_wave<Q>()), 0, s, k,
-                           nhg, nq);
+        const int64_t nblocks = (nq + 7) / 8 * 8 * (k.G * nhg * out_split<N, Q>());
+        hipLaunchKernelGGL((ssd_chunk_out_kernel<N, Q, true>), dim3((unsigned)nblocks),
+                           dim3(Q * 4 / (out_tiles_per_wave<Q>() * out_split<N, Q>())), 0, s, k, nhg, nq);
     } else {                  // adjoint aggregates (exp(cs_t) weights)
         hipLaunchKernelGGL((ssd_chunk_state_kernel<N, Q, 2>), cs_grid, dim3(kThreads), 0, s, k);
     }
