@@ -35,56 +35,87 @@ struct StepK {
 
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
-template <typename T, int N, bool HEADS>
+// Each thread updates the same lane position of U channel groups, U blocks of
+// channels apart, so U independent state loads are in flight per lane.
+template <typename T, int N, bool HEADS, int U>
 __global__ __launch_bounds__(256) void state_update_kernel(const StepK k) {
     constexpr int G = N / 4;               // lanes per channel
     constexpr int CPB = 256 / G;           // channels per block
     const int tid = threadIdx.x, q = tid % G;
-    const int64_t c = (int64_t)blockIdx.x * CPB + tid / G;
-    if (c >= k.channels) return;           // whole channel groups leave together
-    const int64_t b = c / k.D;
-    const int d = (int)(c % k.D);
-    const int h = HEADS ? d / k.P : d;     // parameter index: head or channel
-    const int64_t dt_idx = HEADS ? b * (k.D / k.P) + h : c;
     const T *x = (const T *)k.x, *dtp = (const T *)k.dt, *z = (const T *)k.z;
-    const int64_t row = (b * k.G + h / k.ppg) * N + 4 * q;     // (b, group, 4q..)
-    const T *Bm = (const T *)k.Bm + row, *Cm = (const T *)k.Cm + row;
-
-    float v = to_f32(dtp[dt_idx]) + (k.dt_bias ? k.dt_bias[h] : 0.0f);
-    const float dt = k.softplus ? softplus_f32(v) : v;
-    const float xv = to_f32(x[c]);
-    const float dtx = dt * xv;
-
-    f32x4 *sp = (f32x4 *)(k.state + c * N + 4 * q);
-    f32x4 s = *sp;
-    float part = 0.0f;
+    int64_t cs[U];
+    bool ok[U];
+    float xv[U], dtx[U], dtv[U];
+    f32x4 st[U], bv[U], av[U];
+    int hs[U];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float a = HEADS ? k.A[h] : k.A[(int64_t)d * N + 4 * q + i];
-        const float decay = fast_exp2(dt * a * kLog2e);
-        s[i] = fmaf(decay, s[i], dtx * to_f32(Bm[i]));
-        part = fmaf(to_f32(Cm[i]), s[i], part);
+    for (int u = 0; u < U; ++u) {
+        const int64_t c = ((int64_t)blockIdx.x * U + u) * CPB + tid / G;
+        ok[u] = c < k.channels;            // whole channel groups drop out together
+        cs[u] = ok[u] ? c : 0;
     }
-    *sp = s;
+    // every load of the U channels first, then the arithmetic
 #pragma unroll
-    for (int o = 1; o < G; o <<= 1) part += __shfl_xor(part, o, 64);
-    if (q == 0) {
-        float out = fmaf(k.Dskip ? k.Dskip[h] : 0.0f, xv, part);
-        if (z) out *= silu_f32(to_f32(z[c]));
-        store_val((T *)k.y + c, out);
+    for (int u = 0; u < U; ++u) {
+        const int64_t c = cs[u];
+        const int64_t b = c / k.D;
+        const int d = (int)(c % k.D);
+        const int h = HEADS ? d / k.P : d;     // parameter index: head or channel
+        hs[u] = h;
+        const int64_t dt_idx = HEADS ? b * (k.D / k.P) + h : c;
+        const int64_t row = (b * k.G + h / k.ppg) * N + 4 * q;     // (b, group, 4q..)
+        const T *Bm = (const T *)k.Bm + row;
+        dtv[u] = to_f32(dtp[dt_idx]) + (k.dt_bias ? k.dt_bias[h] : 0.0f);
+        xv[u] = to_f32(x[c]);
+        st[u] = *(const f32x4 *)(k.state + c * N + 4 * q);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            bv[u][i] = to_f32(Bm[i]);
+            av[u][i] = HEADS ? k.A[h] : k.A[(int64_t)d * N + 4 * q + i];
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const float dt = k.softplus ? softplus_f32(dtv[u]) : dtv[u];
+        dtx[u] = dt * xv[u];
+        dtv[u] = dt;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t c = cs[u];
+        const int64_t b = c / k.D;
+        const int h = hs[u];
+        const T *Cm = (const T *)k.Cm + (b * k.G + h / k.ppg) * N + 4 * q;
+        f32x4 s = st[u];
+        float part = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float decay = fast_exp2(dtv[u] * av[u][i] * kLog2e);
+            s[i] = fmaf(decay, s[i], dtx[u] * bv[u][i]);
+            part = fmaf(to_f32(Cm[i]), s[i], part);
+        }
+        if (ok[u]) *(f32x4 *)(k.state + c * N + 4 * q) = s;
+#pragma unroll
+        for (int o = 1; o < G; o <<= 1) part += __shfl_xor(part, o, 64);
+        if (ok[u] && q == 0) {
+            float out = fmaf(k.Dskip ? k.Dskip[h] : 0.0f, xv[u], part);
+            if (z) out *= silu_f32(to_f32(z[c]));
+            store_val((T *)k.y + c, out);
+        }
     }
 }
 
 template <typename T, bool HEADS>
 void launch_step(const StepK &k, int N, hipStream_t s) {
-    const int64_t cpb = 256 / (N / 4);   // channels per block
-    const dim3 grid((unsigned)((k.channels + cpb - 1) / cpb));
+    constexpr int U = 2;                     // channel groups per thread (4 measured slower)
+    const int64_t cpb = 256 / (N / 4);       // channels per block
+    const dim3 grid((unsigned)((k.channels + cpb * U - 1) / (cpb * U)));
     switch (N) {
-        case 16: hipLaunchKernelGGL((state_update_kernel<T, 16, HEADS>), grid, dim3(256), 0, s, k); break;
-        case 32: hipLaunchKernelGGL((state_update_kernel<T, 32, HEADS>), grid, dim3(256), 0, s, k); break;
-        case 64: hipLaunchKernelGGL((state_update_kernel<T, 64, HEADS>), grid, dim3(256), 0, s, k); break;
-        case 128: hipLaunchKernelGGL((state_update_kernel<T, 128, HEADS>), grid, dim3(256), 0, s, k); break;
-        default: hipLaunchKernelGGL((state_update_kernel<T, 256, HEADS>), grid, dim3(256), 0, s, k); break;
+        case 16: hipLaunchKernelGGL((state_update_kernel<T, 16, HEADS, U>), grid, dim3(256), 0, s, k); break;
+        case 32: hipLaunchKernelGGL((state_update_kernel<T, 32, HEADS, U>), grid, dim3(256), 0, s, k); break;
+        case 64: hipLaunchKernelGGL((state_update_kernel<T, 64, HEADS, U>), grid, dim3(256), 0, s, k); break;
+        case 128: hipLaunchKernelGGL((state_update_kernel<T, 128, HEADS, U>), grid, dim3(256), 0, s, k); break;
+        default: hipLaunchKernelGGL((state_update_kernel<T, 256, HEADS, U>), grid, dim3(256), 0, s, k); break;
     }
 }
 

@@ -230,6 +230,7 @@ def conv_args(**kw):
     ({"dstate": 48}, _capi.SSM_ENOTSUP),
     ({"dstate": 512}, _capi.SSM_ENOTSUP),
     ({"ngroups": 7}, _capi.SSM_EINVAL),
+    ({"batch": 1 << 20, "dim": 1 << 14, "dstate": 256}, _capi.SSM_ENOTSUP),   # 2^39 states: one launch
 ])
 def test_step_validation(kw, want):
     lib = _capi.lib()
@@ -244,6 +245,7 @@ def test_step_validation(kw, want):
     ({"state": FAKE + 8}, _capi.SSM_EINVAL),
     ({"dstate": 100}, _capi.SSM_ENOTSUP),
     ({"ngroups": 3}, _capi.SSM_EINVAL),
+    ({"batch": 1 << 20, "nheads": 256, "dstate": 256}, _capi.SSM_ENOTSUP),   # 2^42 states: one launch
 ])
 def test_ssd_step_validation(kw, want):
     assert _capi.lib().ssd_state_update(ctypes.byref(ssd_step_args(**kw)), None) == want
