@@ -20,16 +20,16 @@
 //   2. ssd_state_pass: sequential over chunks per (batch, head, p, 4 n); writes the
 //      entering state of every chunk already rounded to bf16 in the [p][n] layout
 //      the output kernel reads as MFMA B fragments, and h_final in fp32.
-//   3. ssd_chunk_out: per (batch, chunk, pair of heads), one or two 16-row tiles
-//      per wave; B and x stream through LDS in 64-row blocks of s, each loaded
-//      once per workgroup. For each block the transposed score tile G^T = B C^T is computed on the
-//      MFMA units, masked and scaled in registers and rounded to bf16 straight
-//      into the A operand of Y += M X (the 16x16
-//      accumulator layout gives a lane 4 consecutive s of one t; two tiles give the
-//      8 an A fragment holds, and X is fetched with the same order of s, which the
-//      contraction over s does not care about). The carried state enters as
-//      Y = exp(cs_t) (C Sin) on the same units; D x and the gate are applied
-//      exactly in fp32 when the tile is written.
+//   3. ssd_chunk_out: per (batch, chunk, pair of heads), one 16-row tile per wave
+//      (at chunk 256 split over two workgroups); B and x stream through LDS in
+//      64-row blocks of s, each loaded once per workgroup. For each block the
+//      transposed score tile G^T = B C^T is computed on the MFMA units, masked and
+//      scaled in registers and rounded to bf16 straight into the A operand of
+//      Y += M X (the 16x16 accumulator layout gives a lane 4 consecutive s of one t;
+//      two tiles give the 8 an A fragment holds, and X is staged with the same
+//      order of s, which the contraction over s does not care about). The carried
+//      state enters as Y = exp(cs_t) (C Sin) on the same units; D x and the gate
+//      are applied exactly in fp32 when the tile is written.
 // Transposes into LDS move 4 x 8 register blocks with byte permutes and 8-byte
 // LDS writes.
 #include <algorithm>
@@ -287,16 +287,12 @@ __global__ __launch_bounds__(256) void ssd_state_pass_kernel(const SSDK p, int N
 }
 
 // ---------------------------------------------------------------- chunk output
-// One workgroup per (batch, chunk, pair of heads of one B/C group); each wave owns
-// 16 rows of the chunk, or for chunks of 256 steps 32 rows (two 16-row tiles of one
-// 64-row time block tb), for both heads, so every operand it reads from LDS feeds
-// the matrix-core products of both tiles. With 8 waves (chunk 256), waves w and w + 4
-// share a SIMD and take the row pairs w and 7 - w, which balances the causal work
-// per SIMD. The prologue of a chunk (dt and cumulative decays, the entering
-// states, C rows) is done once for all Q rows, and each 64-row block of B and x is
-// loaded once and used by every wave whose rows come at or after it. The score
-// tile G^T = B C^T is computed once per tile and reused by both heads: only the
-// decay weights differ per head.
+// Per (batch, chunk, pair of heads of one B/C group); each wave owns 16 rows of the
+// chunk for both heads. The prologue of a chunk (dt and cumulative decays, the
+// entering states, C rows) is done once per workgroup for all of its rows, and each
+// 64-row block of B and x is loaded once and used by every wave whose rows come at
+// or after it. The score tile G^T = B C^T is computed once per wave and reused by
+// both heads: only the decay weights differ per head.
 //
 // With r = 64 tb - 1 (the last step before the time block; cs_r = 0 for tb = 0)
 // the decay of s <= r < t factors as exp(cs_t - cs_s) = a_t w_s, a_t = exp(cs_t -
@@ -319,10 +315,6 @@ struct OutCfg {
 
 // F32OUT: write the pre-gate output (C S + D x) in fp32 to y32 instead of the gated
 // bf16 y (the recompute the gradient pass needs for dz).
-// Two tiles per wave halve the LDS operand reads but leave 8 waves per CU at chunk
-// 256, which measured slower than 16 waves with one tile each: one tile per wave.
-template <int Q>
-constexpr int out_tiles_per_wave() { return 1; }
 // Workgroups per (chunk, head pair). At chunk 256 two 8-wave workgroups share the
 // chunk's time blocks (0 and 3, 1 and 2: equal causal work), so two of them fit a CU
 // and one's loads overlap the other's arithmetic. With N = 256 the C fragments do
@@ -331,12 +323,11 @@ template <int N, int Q>
 constexpr int out_split() { return Q == 256 && N <= 128 ? 2 : 1; }
 
 template <int N, int Q, bool F32OUT>
-__global__ __launch_bounds__((Q * 4 / (out_tiles_per_wave<Q>() * out_split<N, Q>())), (out_split<N, Q>() == 2 ? 4 : 2))
+__global__ __launch_bounds__((Q * 4 / out_split<N, Q>()), (out_split<N, Q>() == 2 ? 4 : 2))
 void ssd_chunk_out_kernel(const SSDK p, int nhg, int64_t nq) {
     constexpr int HG = OutCfg<N>::HG;
-    constexpr int TPW = out_tiles_per_wave<Q>();   // 16-row tiles per wave
     constexpr int SPLIT = out_split<N, Q>();  // workgroups per (chunk, head pair)
-    constexpr int NW = Q / (16 * TPW * SPLIT);   // waves
+    constexpr int NW = Q / (16 * SPLIT);      // waves, 16 rows each
     constexpr int NTH = NW * 64;              // threads
     constexpr int TBS = Q / 64;               // 64-row time blocks per chunk
     constexpr int KN = N / 32;                // k steps over the state dimension
@@ -385,15 +376,13 @@ void ssd_chunk_out_kernel(const SSDK p, int nhg, int64_t nq) {
     const int T = (int)std::min<int64_t>(Q, p.L - t_base);
     const int nsb = (T + 63) / 64;                     // 64-row blocks holding steps
     if (SPLIT == 2 && part == 1 && nsb <= 1) return;   // its blocks 1 and 2 are empty (uniform)
-    // this wave's group of row tiles. Two tiles: w and w + 4 share a SIMD, so they take
-    // groups w and 7 - w. Split chunk: waves 0-3 own the first time block of the part
+    // this wave's 16 rows. Split chunk: waves 0-3 own the first time block of the part
     // (0 or 1), waves 4-7 the second (3 or 2).
-    const int pi = (TPW == 2 && NW == 8 && wv >= 4) ? 11 - wv : wv;
-    const int t0 = SPLIT == 2 ? (wv < 4 ? part : 3 - part) * 64 + (wv & 3) * 16 : pi * 16 * TPW;
-    const int tb = t0 >> 6;                            // the time block of its tiles
+    const int t0 = SPLIT == 2 ? (wv < 4 ? part : 3 - part) * 64 + (wv & 3) * 16 : wv * 16;
+    const int tb = t0 >> 6;                            // the time block of its rows
     // blocks of s this workgroup stages: up to its last time block
     const int nsw = std::min(nsb, SPLIT == 2 ? 4 - part : TBS);
-    const int tl0 = (t0 >> 4) & 3;                     // index of its first tile within it
+    const int tl0 = (t0 >> 4) & 3;                     // index of its 16 rows within it
     const bool live = tb < nsb;                        // the block has steps (uniform)
     const int h0 = gg * p.hpg + hl * HG;               // first head of this workgroup
     const int hend = (gg + 1) * p.hpg;                 // heads of the group end here
@@ -495,15 +484,12 @@ void ssd_chunk_out_kernel(const SSDK p, int nhg, int64_t nq) {
             dts[wv][lane * SPL + i] = dtv[i];
         }
     }
-    bf16x8 cfr[TPW][KN];
+    bf16x8 cfr[KN];
     if (live) {
+        const int trow = std::min(t0 + r16, T - 1);
 #pragma unroll
-        for (int tt = 0; tt < TPW; ++tt) {
-            const int trow = std::min(t0 + 16 * tt + r16, T - 1);
-#pragma unroll
-            for (int k = 0; k < KN; ++k)
-                cfr[tt][k] = as_bf16x8(*(const u32x4 *)(Crow + (int64_t)trow * GN + 32 * k + 8 * kb));
-        }
+        for (int k = 0; k < KN; ++k)
+            cfr[k] = as_bf16x8(*(const u32x4 *)(Crow + (int64_t)trow * GN + 32 * k + 8 * kb));
     }
     sin_stash();
     if (HG > SIN_HEADS) sin_fetch(SIN_HEADS);
@@ -514,15 +500,12 @@ void ssd_chunk_out_kernel(const SSDK p, int nhg, int64_t nq) {
         if (s < 64 * tbi) wts[tbi][j][s] = fast_exp2(cs2[j][64 * tbi - 1] - cs2[j][s]) * dts[j][s];
     }
 
-    // entering state: Y = exp(cs_r) C Sin (scaled by a_t further down); each Sin
-    // operand feeds both tiles
-    f32x4 yo[TPW][HG][4];
+    // entering state: Y = exp(cs_r) C Sin (scaled by a_t further down)
+    f32x4 yo[HG][4];
 #pragma unroll
-    for (int tt = 0; tt < TPW; ++tt)
+    for (int j = 0; j < HG; ++j)
 #pragma unroll
-        for (int j = 0; j < HG; ++j)
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq) yo[tt][j][qq] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int qq = 0; qq < 4; ++qq) yo[j][qq] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j0 = 0; j0 < HG; j0 += SIN_HEADS) {
         if (j0) {
@@ -537,26 +520,21 @@ void ssd_chunk_out_kernel(const SSDK p, int nhg, int64_t nq) {
 #pragma unroll
                 for (int qq = 0; qq < 4; ++qq) {
 #pragma unroll
-                    for (int k = 0; k < KN; ++k) {
-                        const bf16x8 sf = as_bf16x8(*(const u32x4 *)&SinL[jj][qq * 16 + r16][32 * k + 8 * kb]);
-#pragma unroll
-                        for (int tt = 0; tt < TPW; ++tt)
-                            yo[tt][j0 + jj][qq] = mfma16x16x32(cfr[tt][k], sf, yo[tt][j0 + jj][qq]);
-                    }
+                    for (int k = 0; k < KN; ++k)
+                        yo[j0 + jj][qq] = mfma16x16x32(
+                            cfr[k], as_bf16x8(*(const u32x4 *)&SinL[jj][qq * 16 + r16][32 * k + 8 * kb]), yo[j0 + jj][qq]);
                 }
             }
         }
     }
     const int r = tb * 64 - 1;
-    __syncthreads();                                   // the wts table is complete
+    __syncthreads();                                   // the wts table is complete, Sin is read
     if (live && tb) {
 #pragma unroll
         for (int j = 0; j < HG; ++j) {
             const float er = fast_exp2(cs2[j][r]);
 #pragma unroll
-            for (int tt = 0; tt < TPW; ++tt)
-#pragma unroll
-                for (int qq = 0; qq < 4; ++qq) yo[tt][j][qq] *= er;
+            for (int qq = 0; qq < 4; ++qq) yo[j][qq] *= er;
         }
     }
     stash();
@@ -567,94 +545,74 @@ void ssd_chunk_out_kernel(const SSDK p, int nhg, int64_t nq) {
         if (live && sb <= tb) {
             const int s0 = sb * 64;
             const bool diag = sb == tb;
+            const int tcol = t0 + r16;                // the A-operand row of this lane
             if (diag) {
-                // scale what came before the time block by a_t (rows t0 + 16tt + 4kb + i)
-                // and add D x of these rows from the staged (diagonal) block of x
+                // scale what came before the time block by a_t (rows t0 + 4kb + i) and
+                // add D x of these rows from the staged (diagonal) block of x
 #pragma unroll
                 for (int j = 0; j < HG; ++j) {
                     const float cr = tb ? cs2[j][r] : 0.0f;
+                    const f32x4 crow = *(const f32x4 *)&cs2[j][t0 + 4 * kb];
                     const float dsk = (p.Dskip && h0 + j < hend) ? p.Dskip[h0 + j] : 0.0f;
 #pragma unroll
-                    for (int tt = 0; tt < TPW; ++tt) {
-                        const f32x4 crow = *(const f32x4 *)&cs2[j][t0 + 16 * tt + 4 * kb];
+                    for (int qq = 0; qq < 4; ++qq) {
+                        const u32x2 xv = *(const u32x2 *)&XT[j][qq * 16 + r16][perm_s(16 * tl0 + 4 * kb)];
+                        const float xs[4] = {bf16_lo(xv[0]), bf16_hi(xv[0]), bf16_lo(xv[1]), bf16_hi(xv[1])};
 #pragma unroll
-                        for (int qq = 0; qq < 4; ++qq) {
-                            const u32x2 xv =
-                                *(const u32x2 *)&XT[j][qq * 16 + r16][perm_s(16 * (tl0 + tt) + 4 * kb)];
-                            const float xs[4] = {bf16_lo(xv[0]), bf16_hi(xv[0]), bf16_lo(xv[1]), bf16_hi(xv[1])};
-#pragma unroll
-                            for (int i = 0; i < 4; ++i)
-                                yo[tt][j][qq][i] = fmaf(dsk, xs[i], yo[tt][j][qq][i] * fast_exp2(crow[i] - cr));
-                        }
+                        for (int i = 0; i < 4; ++i)
+                            yo[j][qq][i] = fmaf(dsk, xs[i], yo[j][qq][i] * fast_exp2(crow[i] - cr));
                     }
                 }
             }
-            // one 32-column half of s at a time: G^T[s][t] tiles u = 2a, 2a + 1 for
-            // every row tile of the wave; lane holds s = s0 + 16u + 4kb + i, t = t0 +
-            // 16tt + r16. On the diagonal block tile tt needs u <= tl0 + tt, and a half
-            // after all of its rows is skipped.
+            // one 32-column half of s at a time: G^T[s][t] tiles u = 2a, 2a + 1, lane
+            // holds s = s0 + 16u + 4kb + i, t = tcol. On the diagonal block the wave
+            // needs u <= tl0, and a half after all of its rows is skipped.
 #pragma unroll
             for (int a = 0; a < 2; ++a) {
-                if (diag && 32 * a > 16 * (tl0 + TPW - 1) + 15) continue;   // every s after every row
-                bool need[TPW];
-#pragma unroll
-                for (int tt = 0; tt < TPW; ++tt) need[tt] = !diag || 32 * a <= 16 * (tl0 + tt) + 15;
-                f32x4 g[TPW][2];
+                if (diag && 32 * a > 16 * tl0 + 15) continue;   // every s after every row
+                f32x4 g[2];
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
                     const int u = 2 * a + hh;
+                    g[hh] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    if (!diag || u <= tl0) {
 #pragma unroll
-                    for (int tt = 0; tt < TPW; ++tt) g[tt][hh] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    if (!diag || u <= tl0 + TPW - 1) {   // the last tile needs it
-#pragma unroll
-                        for (int k = 0; k < KN; ++k) {
-                            const bf16x8 bf = as_bf16x8(*(const u32x4 *)&Bb[16 * u + r16][32 * k + 8 * kb]);
-#pragma unroll
-                            for (int tt = 0; tt < TPW; ++tt)
-                                if (!diag || u <= tl0 + tt) g[tt][hh] = mfma16x16x32(bf, cfr[tt][k], g[tt][hh]);
-                        }
+                        for (int k = 0; k < KN; ++k)
+                            g[hh] = mfma16x16x32(as_bf16x8(*(const u32x4 *)&Bb[16 * u + r16][32 * k + 8 * kb]), cfr[k],
+                                                 g[hh]);
                     }
                 }
 #pragma unroll
                 for (int j = 0; j < HG; ++j) {
-                    bf16x8 mfr[TPW];
+                    float v[8];
                     if (!diag) {
                         const f32x4 w0 = *(const f32x4 *)&wts[tb][j][s0 + 32 * a + 4 * kb];
                         const f32x4 w1 = *(const f32x4 *)&wts[tb][j][s0 + 32 * a + 16 + 4 * kb];
 #pragma unroll
-                        for (int tt = 0; tt < TPW; ++tt)
-                            mfr[tt] = as_bf16x8(u32x4{pack_bf16(g[tt][0][0] * w0[0], g[tt][0][1] * w0[1]),
-                                                      pack_bf16(g[tt][0][2] * w0[2], g[tt][0][3] * w0[3]),
-                                                      pack_bf16(g[tt][1][0] * w1[0], g[tt][1][1] * w1[1]),
-                                                      pack_bf16(g[tt][1][2] * w1[2], g[tt][1][3] * w1[3])});
+                        for (int i = 0; i < 4; ++i) {
+                            v[i] = g[0][i] * w0[i];
+                            v[4 + i] = g[1][i] * w1[i];
+                        }
                     } else {
+                        const float ct = cs2[j][tcol];
 #pragma unroll
-                        for (int tt = 0; tt < TPW; ++tt) {
-                            const int tcol = t0 + 16 * tt + r16;   // the A-operand row of this lane
-                            const float ct = cs2[j][tcol];
-                            float v[8];
+                        for (int hh = 0; hh < 2; ++hh) {
+                            const int sb0 = s0 + 32 * a + 16 * hh + 4 * kb;
+                            const f32x4 cd = *(const f32x4 *)&cs2[j][sb0];
+                            const f32x4 dd = *(const f32x4 *)&dts[j][sb0];
 #pragma unroll
-                            for (int hh = 0; hh < 2; ++hh) {
-                                const int sb0 = s0 + 32 * a + 16 * hh + 4 * kb;
-                                const f32x4 cd = *(const f32x4 *)&cs2[j][sb0];
-                                const f32x4 dd = *(const f32x4 *)&dts[j][sb0];
-#pragma unroll
-                                for (int i = 0; i < 4; ++i) {
-                                    const float m = g[tt][hh][i] * fast_exp2(ct - cd[i]) * dd[i];
-                                    v[4 * hh + i] = sb0 + i <= tcol ? m : 0.0f;
-                                }
+                            for (int i = 0; i < 4; ++i) {
+                                const float m = g[hh][i] * fast_exp2(ct - cd[i]) * dd[i];
+                                v[4 * hh + i] = sb0 + i <= tcol ? m : 0.0f;
                             }
-                            mfr[tt] = as_bf16x8(u32x4{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]),
-                                                      pack_bf16(v[4], v[5]), pack_bf16(v[6], v[7])});
                         }
                     }
+                    const bf16x8 mfr = as_bf16x8(u32x4{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]),
+                                                       pack_bf16(v[4], v[5]), pack_bf16(v[6], v[7])});
 #pragma unroll
-                    for (int qq = 0; qq < 4; ++qq) {
-                        const bf16x8 xf = as_bf16x8(*(const u32x4 *)&XT[j][qq * 16 + r16][32 * a + 8 * kb]);
-#pragma unroll
-                        for (int tt = 0; tt < TPW; ++tt)
-                            if (need[tt]) yo[tt][j][qq] = mfma16x16x32(mfr[tt], xf, yo[tt][j][qq]);
-                    }
+                    for (int qq = 0; qq < 4; ++qq)
+                        yo[j][qq] = mfma16x16x32(mfr, as_bf16x8(*(const u32x4 *)&XT[j][qq * 16 + r16][32 * a + 8 * kb]),
+                                                 yo[j][qq]);
                     __builtin_amdgcn_sched_barrier(0);   // one head's operands live at a time
                 }
             }
@@ -666,62 +624,56 @@ void ssd_chunk_out_kernel(const SSDK p, int nhg, int64_t nq) {
         }
     }
 
-    // y = Y + D x, gated by silu(z); z is fetched for both tiles and heads at once.
-    // Each tile goes through the wave's own LDS rows so that a lane writes rows of
-    // 8 bf16.
-    u32x4 zreg[TPW][HG][2];
+    // y = Y + D x, gated by silu(z); z is fetched for every head at once. Each
+    // head's tile then goes through the wave's own LDS rows so that a lane writes
+    // rows of 8 bf16.
+    u32x4 zreg[HG][2];
     if (!F32OUT && p.z && live) {
 #pragma unroll
-        for (int tt = 0; tt < TPW; ++tt)
+        for (int j = 0; j < HG; ++j)
 #pragma unroll
-            for (int j = 0; j < HG; ++j)
-#pragma unroll
-                for (int rr = 0; rr < 2; ++rr) {
-                    const int t = std::min(t0 + 16 * tt + rr * 8 + (lane >> 3), T - 1), h = std::min(h0 + j, hend - 1);
-                    zreg[tt][j][rr] =
-                        *(const u32x4 *)(p.z + (((int64_t)b * p.L + t_base + t) * p.H + h) * kP + (lane & 7) * 8);
-                }
+            for (int rr = 0; rr < 2; ++rr) {
+                const int t = std::min(t0 + rr * 8 + (lane >> 3), T - 1), h = std::min(h0 + j, hend - 1);
+                zreg[j][rr] = *(const u32x4 *)(p.z + (((int64_t)b * p.L + t_base + t) * p.H + h) * kP + (lane & 7) * 8);
+            }
     }
     __syncthreads();                                   // every wave is done with the B block
     if (!live) return;                                 // uniform; no barrier follows
 #pragma unroll
-    for (int tt = 0; tt < TPW; ++tt) {
+    for (int j = 0; j < HG; ++j) {
+        const int h = h0 + j;
+        if (h >= hend) break;                          // uniform
 #pragma unroll
-        for (int j = 0; j < HG; ++j) {
-            const int h = h0 + j;
-            if (h >= hend) break;                      // uniform
+        for (int qq = 0; qq < 4; ++qq)
 #pragma unroll
-            for (int qq = 0; qq < 4; ++qq)
+            for (int i = 0; i < 4; ++i) Ot[wv][4 * kb + i][qq * 16 + r16] = yo[j][qq][i];
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // the wave's own rows only
 #pragma unroll
-                for (int i = 0; i < 4; ++i) Ot[wv][4 * kb + i][qq * 16 + r16] = yo[tt][j][qq][i];
-            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // the wave's own rows only
+        for (int rr = 0; rr < 2; ++rr) {
+            const int row = rr * 8 + (lane >> 3), c8 = (lane & 7) * 8;
+            const int t = t0 + row;
+            const f32x4 o0 = *(const f32x4 *)&Ot[wv][row][c8];
+            const f32x4 o1 = *(const f32x4 *)&Ot[wv][row][c8 + 4];
+            if (F32OUT && t < T) {
+                float *dst = p.y32 + (((int64_t)b * p.L + t_base + t) * p.H + h) * kP + c8;
+                *(f32x4 *)dst = o0;
+                *(f32x4 *)(dst + 4) = o1;
+            } else if (t < T) {
+                const float o[8] = {o0[0], o0[1], o0[2], o0[3], o1[0], o1[1], o1[2], o1[3]};
+                u32x4 outv;
 #pragma unroll
-            for (int rr = 0; rr < 2; ++rr) {
-                const int row = rr * 8 + (lane >> 3), c8 = (lane & 7) * 8;
-                const int t = t0 + 16 * tt + row;
-                const f32x4 o0 = *(const f32x4 *)&Ot[wv][row][c8];
-                const f32x4 o1 = *(const f32x4 *)&Ot[wv][row][c8 + 4];
-                if (F32OUT && t < T) {
-                    float *dst = p.y32 + (((int64_t)b * p.L + t_base + t) * p.H + h) * kP + c8;
-                    *(f32x4 *)dst = o0;
-                    *(f32x4 *)(dst + 4) = o1;
-                } else if (t < T) {
-                    const float o[8] = {o0[0], o0[1], o0[2], o0[3], o1[0], o1[1], o1[2], o1[3]};
-                    u32x4 outv;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        float y0 = o[2 * e], y1 = o[2 * e + 1];
-                        if (p.z) {
-                            y0 *= silu_f32(bf16_lo(zreg[tt][j][rr][e]));
-                            y1 *= silu_f32(bf16_hi(zreg[tt][j][rr][e]));
-                        }
-                        outv[e] = pack_bf16(y0, y1);
+                for (int e = 0; e < 4; ++e) {
+                    float y0 = o[2 * e], y1 = o[2 * e + 1];
+                    if (p.z) {
+                        y0 *= silu_f32(bf16_lo(zreg[j][rr][e]));
+                        y1 *= silu_f32(bf16_hi(zreg[j][rr][e]));
                     }
-                    *(u32x4 *)(p.y + (((int64_t)b * p.L + t_base + t) * p.H + h) * kP + c8) = outv;
+                    outv[e] = pack_bf16(y0, y1);
                 }
+                *(u32x4 *)(p.y + (((int64_t)b * p.L + t_base + t) * p.H + h) * kP + c8) = outv;
             }
-            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     }
 }
 
@@ -741,7 +693,7 @@ void launch_nq(const SSDK &k, int batch, hipStream_t s) {
     const int64_t nq = (int64_t)batch * k.nc;            // (batch, chunk) pairs
     const int64_t nblocks = (nq + 7) / 8 * 8 * (k.G * nhg * out_split<N, Q>());
     hipLaunchKernelGGL((ssd_chunk_out_kernel<N, Q, false>), dim3((unsigned)nblocks),
-                       dim3(Q * 4 / (out_tiles_per_wave<Q>() * out_split<N, Q>())), 0, s, k, nhg, nq);
+                       dim3(Q * 4 / out_split<N, Q>()), 0, s, k, nhg, nq);
 }
 
 template <int N>
@@ -767,7 +719,7 @@ void recompute_nq(const SSDK &k, int batch, int what, hipStream_t s) {
         const int64_t nq = (int64_t)batch * k.nc;
         const int64_t nblocks = (nq + 7) / 8 * 8 * (k.G * nhg * out_split<N, Q>());
         hipLaunchKernelGGL((ssd_chunk_out_kernel<N, Q, true>), dim3((unsigned)nblocks),
-                           dim3(Q * 4 / (out_tiles_per_wave<Q>() * out_split<N, Q>())), 0, s, k, nhg, nq);
+                           dim3(Q * 4 / out_split<N, Q>()), 0, s, k, nhg, nq);
     } else {                  // adjoint aggregates (exp(cs_t) weights)
         hipLaunchKernelGGL((ssd_chunk_state_kernel<N, Q, 2>), cs_grid, dim3(kThreads), 0, s, k);
     }
