@@ -9,9 +9,13 @@ from the 256 MB Infinity Cache.
 
 Prints ONE JSON line on stdout. `value` is the effective HBM bandwidth over the
 algorithmic bytes (x, delta, z, y once per (b,t,d), B and C once per (b,t),
-parameters and the final state once). `roofline` relates the dominant kernel's
-measured time to its bound; `cpu_baseline` is the fp64 oracle timed on the
-host cores over the same workload.
+parameters and the final state once), from the mean time per call;
+`ms_median` and `ms_min` are over the same timed calls. `copy_GBps` is a 512 MiB
+device-to-device copy timed in the same run (bytes read + written per second),
+the practical HBM rate, and `copy_frac` the scan's rate relative to it.
+`roofline` relates the dominant kernel's measured time to its bound;
+`cpu_baseline` is the fp64 oracle timed on the host cores over the same
+workload.
 
 The scan is bound by plain fp32 vector arithmetic, not by HBM: per (b,t,d,n)
 element the recurrence needs exp(dt A) (a multiply and an exponential, which
@@ -213,6 +217,28 @@ def time_ssd(steps, warmup, torch, ssm):
     return cfg, [a.elapsed_time(b) for a, b in ev]
 
 
+def measure_copy_rate(torch):
+    """Device-to-device copy of 512 MiB, timed with HIP events: the practical HBM rate
+    (bytes read + written per second) to quote next to the 8 TB/s spec."""
+    n = 512 * 1024 * 1024
+    a = torch.empty(n // 2, dtype=torch.bfloat16, device="cuda")
+    a.fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(2):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        b.copy_(a)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)[len(ev) // 2]
+    del a, b
+    return 2 * n / (ms * 1e-3) / 1e9
+
+
 def _time_rotating(call, nsets, steps, warmup, torch):
     """Mean HIP-event time (ms) of call(i) over `steps` calls, rotating i over the sets."""
     for i in range(warmup):
@@ -371,7 +397,7 @@ def time_ssd_bwd(steps, warmup, torch, ssm):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="S2", choices=["S1", "S2", "S3", "S4"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -424,6 +450,9 @@ def main():
     cfg, wall, per_call, t_states, t_apply = time_scan(args.config, args.steps, args.warmup, torch,
                                                        ssm, passes="split")
     ms = sum(per_call) / len(per_call)
+    srt = sorted(per_call)
+    ms_median, ms_min = srt[len(srt) // 2], srt[0]
+    copy_gbs = measure_copy_rate(torch)
     ms_states = sum(t_states) / len(t_states)
     ms_apply = sum(t_apply) / len(t_apply)
     alg = scan_alg_bytes(cfg)
@@ -441,6 +470,9 @@ def main():
                    "seq_len": cfg.seqlen, "dim": cfg.dim, "dstate": cfg.dstate,
                    "storage": cfg.dtype, "state": "f32"},
         "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "copy_GBps": round(copy_gbs, 1),
+        "copy_frac": round(gbs / copy_gbs, 4),
+        "ms_median": round(ms_median, 5), "ms_min": round(ms_min, 5),
         "gelem_per_s": round(gelem, 2),
         "wall_s_timed": round(wall, 4),
         "roofline": {"bound": "alu", "achieved": round(slots, 3), "peak": round(ALU_PEAK_TSLOTS, 2),
