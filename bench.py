@@ -362,10 +362,29 @@ def cpu_baseline(key, budget_s=10.0):
         if el >= budget_s or runs >= 200:
             break
     per = el / runs
+    # one run on a single thread as well (the same call, OpenMP limited to 1)
+    oracle.set_num_threads(1)
+    t1 = time.perf_counter()
+    oracle.selective_scan(inp["x"], inp["delta"], inp["A"], inp["Bm"], inp["Cm"],
+                          inp["Dskip"], inp["z"], inp["delta_bias"])
+    single = time.perf_counter() - t1
+    oracle.set_num_threads(threads)
     return {"value": round(scan_alg_bytes(cfg) / per / 1e9, 3), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "single_thread_s": round(single, 3),
             "sample": "full %s workload (all %d channels x L %d), fp64 C recurrence, %d run(s), "
                       "%.2f s per run" % (key, cfg.batch * cfg.dim, cfg.seqlen, runs, per)}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def time_ssd_bwd(steps, warmup, torch, ssm):
