@@ -52,6 +52,16 @@ def test_groups(H, N, G, chunk, L):
     _check("groups H%d N%d G%d Q%d" % (H, N, G, chunk), inp, chunk)
 
 
+@pytest.mark.parametrize("N", [64, 128])
+def test_chunk256_two_workgroups(N):
+    """Chunk 256, where the output kernel splits each chunk's time blocks over two
+    workgroups (0 and 3, 1 and 2): a ragged last chunk of 88 steps (blocks 2 and 3
+    empty), an odd head count (a half-empty head pair), the gate and an initial
+    state."""
+    inp = workloads.ssd_inputs(2, 600, 3, 64, N, "bf16", seed=40 + N, with_h0=True, with_z=True)
+    _check("chunk 256 N=%d" % N, inp, 256)
+
+
 def test_gate_and_no_skip():
     inp = workloads.ssd_inputs(2, 333, 3, 64, 64, "bf16", seed=21, with_z=True, with_D=False)
     _check("z, no D", inp, 64)
