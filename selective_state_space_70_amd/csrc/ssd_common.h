@@ -78,6 +78,7 @@ struct SSDK {
     float *h_final;
     float *states;      // fp32 [B][nc][H][P][N]: state of each chunk from zero (gradient pass)
     uint16_t *states16; // bf16, same layout: the chunk states of the forward
+    float *states_last; // fp32 [B][H][P][N]: the forward's last chunk state (feeds h_final only)
     uint16_t *sin;      // bf16 [B][nc][H][P][N]: state entering each chunk
     float *decay;       // fp32 [B][H][nc]: exp(cs_end) of each chunk
     float *sin32;       // optional fp32 copy of the entering states (may alias states)

@@ -45,7 +45,8 @@ namespace {
 // ---------------------------------------------------------------- chunk states
 // MODE 0: S_c = sum_s exp(cs_end - cs_s) dt_s B_s (x) x_s, the weighted x rounded to
 //         bf16, S_c stored in bf16 (the forward: the entering states it feeds are
-//         rounded to bf16 anyway);
+//         rounded to bf16 anyway); the last chunk's, which only enters h_final, in
+//         fp32;
 // MODE 1: the same with the weighted x split into bf16 hi + lo parts, two products
 //         (fp32-grade chunk states, for the gradient pass);
 // MODE 2: R_c = sum_t exp(cs_t) B_t (x) (x_t + xlo_t), split like MODE 1, no decay
@@ -204,7 +205,15 @@ __global__ __launch_bounds__(kThreads, (N > 128 || MODE != 0) ? 1 : 2) void ssd_
         // 8(kb / 2) .. for odd kb.
         if (head_ok) {
             const int64_t o = (((int64_t)b * p.nc + c) * p.H + h) * (int64_t)kP * N;
-            if constexpr (MODE == 0) {
+            if (MODE == 0 && c == p.nc - 1) {
+                // the last chunk's state only enters h_final: kept in fp32
+                float *out = p.states_last + ((int64_t)b * p.H + h) * (int64_t)kP * N;
+#pragma unroll
+                for (int i = 0; i < NT; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        *(f32x4 *)(out + (j * 16 + r16) * N + pass * NP + i * 16 + kb * 4) = acc[i][j];
+            } else if constexpr (MODE == 0) {
                 static_assert(NT % 2 == 0, "tiles are paired");
                 const bool odd = kb & 1;
 #pragma unroll
@@ -260,7 +269,9 @@ __global__ __launch_bounds__(256) void ssd_state_pass_kernel(const SSDK p, int N
 #pragma unroll
         for (int u = 0; u < K; ++u) {
             const int cc = min(c0 + u, p.nc - 1);
-            if (p.states16) {   // bf16 chunk states (the forward)
+            if (p.states16 && cc == p.nc - 1) {   // the forward's last chunk, fp32
+                sc[u] = *(const f32x4 *)(p.states_last + bh * kP * N + pn);
+            } else if (p.states16) {              // bf16 chunk states (the forward)
                 const u32x2 v = *(const u32x2 *)(p.states16 + base + cc * cstride);
                 sc[u] = f32x4{bf16_lo(v[0]), bf16_hi(v[0]), bf16_lo(v[1]), bf16_hi(v[1])};
             } else {
@@ -741,6 +752,11 @@ void ssd_recompute_launch(const SSDK &k, int batch, int Q, int N, int what, hipS
     else recompute_n<128>(k, batch, Q, what, s);
 }
 
+// fp32 [B][H][P][N] after the decays: the last chunk's state (it feeds h_final only)
+static size_t last_state_offset(const ssm_ssd_args &a, const SSDPlan &pl) {
+    return pl.decay_offset + (((size_t)a.batch * a.nheads * pl.nchunks * sizeof(float) + 255) & ~(size_t)255);
+}
+
 SSDPlan ssd_plan(const ssm_ssd_args &a) {
     SSDPlan pl{};
     if (a.batch <= 0 || a.seqlen <= 0 || a.chunk <= 0) return pl;
@@ -750,7 +766,7 @@ SSDPlan ssd_plan(const ssm_ssd_args &a) {
     pl.states_offset = 0;
     pl.sin_offset = up(elems * sizeof(uint16_t));     // bf16 chunk states first
     pl.decay_offset = pl.sin_offset + up(elems * sizeof(uint16_t));
-    pl.bytes = pl.decay_offset + up((size_t)a.batch * a.nheads * pl.nchunks * sizeof(float));
+    pl.bytes = last_state_offset(a, pl) + up((size_t)a.batch * a.nheads * a.headdim * a.dstate * sizeof(float));
     return pl;
 }
 
@@ -771,6 +787,7 @@ ssm_status ssd_launch(const ssm_ssd_args &a, const SSDPlan &plan, hipStream_t s,
         k.dt_bias = a.dt_bias; k.A = a.A; k.Dskip = a.Dskip; k.h0 = a.h0;
         k.y = (uint16_t *)a.y; k.h_final = a.h_final;
         k.states16 = (uint16_t *)((char *)a.workspace + plan.states_offset);
+        k.states_last = (float *)((char *)a.workspace + last_state_offset(a, plan));
         k.sin = (uint16_t *)((char *)a.workspace + plan.sin_offset);
         k.decay = (float *)((char *)a.workspace + plan.decay_offset);
         k.L = a.seqlen; k.H = (int32_t)a.nheads; k.nc = (int32_t)plan.nchunks;
