@@ -79,8 +79,11 @@ def test_state_sizes(N):
     _check("N=%d" % N, _case(2, 200, 4, N, seed=N), 128)
 
 
-def test_gate():
-    _check("z", _case(2, 300, 4, 128, seed=3, z=True), 256)
+@pytest.mark.parametrize("N,H", [(128, 4), (64, 5)])
+def test_gate(N, H):
+    """With the gate the pass recomputes the pre-gate output (the forward's output
+    kernel, at chunk 256 split over two workgroups per chunk and head pair)."""
+    _check("z N=%d H=%d" % (N, H), _case(2, 300, H, N, seed=3 + N + H, z=True), 256)
 
 
 @pytest.mark.parametrize("H,G", [(6, 1), (5, 1), (8, 2), (9, 3)])
