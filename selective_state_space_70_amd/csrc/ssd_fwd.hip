@@ -324,8 +324,6 @@ struct OutCfg {
     static constexpr int HG = 2;   // heads per workgroup
 };
 
-// F32OUT: write the pre-gate output (C S + D x) in fp32 to y32 instead of the gated
-// bf16 y (the recompute the gradient pass needs for dz).
 // Workgroups per (chunk, head pair). At chunk 256 two 8-wave workgroups share the
 // chunk's time blocks (0 and 3, 1 and 2: equal causal work), so two of them fit a CU
 // and one's loads overlap the other's arithmetic. With N = 256 the C fragments do
@@ -333,6 +331,8 @@ struct OutCfg {
 template <int N, int Q>
 constexpr int out_split() { return Q == 256 && N <= 128 ? 2 : 1; }
 
+// F32OUT: write the pre-gate output (C S + D x) in fp32 to y32 instead of the gated
+// bf16 y (the recompute the gradient pass needs for dz).
 template <int N, int Q, bool F32OUT>
 __global__ __launch_bounds__((Q * 4 / out_split<N, Q>()), (out_split<N, Q>() == 2 ? 4 : 2))
 void ssd_chunk_out_kernel(const SSDK p, int nhg, int64_t nq) {
