@@ -48,8 +48,9 @@ ssm_status check_scan_sizes(const ssm_scan_args *a) {
     if (groups(a->ngroups) > 1 && (a->dim / groups(a->ngroups)) % 64)
         return fail(SSM_ENOTSUP, "selective_scan: with several groups, dim / ngroups must be a "
                     "multiple of 64");
-    if (a->batch > 65535 || a->dim > (1 << 30))
-        return fail(SSM_ENOTSUP, "selective_scan: batch <= 65535 and dim <= 2^30 supported");
+    // every operand is bounded before it enters a product, so no product below overflows
+    if (a->batch > 65535 || a->dim > (1 << 30) || a->seqlen >= kMaxRowBytes)
+        return fail(SSM_ENOTSUP, "selective_scan: batch <= 65535, dim <= 2^30 and seqlen < 2^31 supported");
     const size_t es = esize(a->dtype);
     if (a->seqlen * a->dim * (int64_t)es >= kMaxRowBytes)
         return fail(SSM_ENOTSUP, "selective_scan: seqlen*dim*elem_size must be < 2^31 bytes");
@@ -101,8 +102,9 @@ ssm_status check_ssd_sizes(const ssm_ssd_args *a) {
     if (a->ngroups < 0 || a->nheads % groups(a->ngroups))
         return fail(SSM_EINVAL, "ssd_chunked: ngroups %lld must be >= 0 and divide nheads %lld",
                     (long long)a->ngroups, (long long)a->nheads);
-    if (a->batch > 65535 || a->nheads > 65535)
-        return fail(SSM_ENOTSUP, "ssd_chunked: batch and nheads must be <= 65535");
+    // every operand is bounded before it enters a product, so no product below overflows
+    if (a->batch > 65535 || a->nheads > 65535 || a->seqlen >= kMaxRowBytes)
+        return fail(SSM_ENOTSUP, "ssd_chunked: batch and nheads must be <= 65535, seqlen < 2^31");
     if (a->seqlen * a->nheads * a->headdim * 2 >= kMaxRowBytes)
         return fail(SSM_ENOTSUP, "ssd_chunked: seqlen*nheads*headdim*2 must be < 2^31 bytes");
     if ((a->seqlen + a->chunk - 1) / a->chunk > 65535)
@@ -190,7 +192,8 @@ ssm_status check_step(const ssm_scan_step_args *a) {
                     (long long)a->dstate);
     if (a->ngroups < 0 || a->dim % groups(a->ngroups))
         return fail(SSM_EINVAL, "selective_state_update: ngroups must be >= 0 and divide dim");
-    if (a->dim > (1 << 30) || a->batch * a->dim > ((int64_t)1 << 34))
+    // batch * dim <= 2^34, tested by division so that the test itself cannot overflow
+    if (a->dim > (1 << 30) || a->batch > ((int64_t)1 << 34) / a->dim)
         return fail(SSM_ENOTSUP, "selective_state_update: dim <= 2^30 and batch*dim <= 2^34 supported");
     // one thread per 4 states of two channels (and the rest of its last block)
     if (a->batch * a->dim * a->dstate / 8 + 256 > kMaxLaunchThreads)
@@ -220,8 +223,9 @@ ssm_status check_ssd_step(const ssm_ssd_step_args *a) {
                     (long long)a->dstate);
     if (a->ngroups < 0 || a->nheads % groups(a->ngroups))
         return fail(SSM_EINVAL, "ssd_state_update: ngroups must be >= 0 and divide nheads");
+    // batch * nheads * headdim <= 2^34, tested by division so that the test cannot overflow
     if (a->nheads > (1 << 20) || a->headdim > (1 << 20) || a->nheads * a->headdim > (1 << 30) ||
-        a->batch * a->nheads * a->headdim > ((int64_t)1 << 34))
+        a->batch > ((int64_t)1 << 34) / (a->nheads * a->headdim))
         return fail(SSM_ENOTSUP, "ssd_state_update: nheads*headdim <= 2^30 and batch*nheads*headdim <= 2^34");
     if (a->batch * a->nheads * a->headdim * a->dstate / 8 + 256 > kMaxLaunchThreads)
         return fail(SSM_ENOTSUP, "ssd_state_update: batch*nheads*headdim*dstate must be < 2^35");

@@ -97,6 +97,8 @@ def ssd_status(a):
     ({"seqlen": 1 << 20, "dim": 1 << 12}, _capi.SSM_ENOTSUP),   # row of 8 GiB
     ({"batch": 65535, "dim": 8192}, _capi.SSM_ENOTSUP),       # 2^33 state elements: one launch
     ({"batch": 65535, "dim": 4096}, _capi.SSM_OK),            # just under 2^32
+    # seqlen * dim * 2 is 2^69 here, which wraps to 0 in 64 bits: seqlen is bounded first
+    ({"seqlen": 1 << 62, "dim": 64}, _capi.SSM_ENOTSUP),
     ({"ngroups": 1}, _capi.SSM_OK),
     ({"ngroups": 2, "dim": 256}, _capi.SSM_OK),
     ({"ngroups": 2}, _capi.SSM_ENOTSUP),                      # 48 channels per group
@@ -135,6 +137,8 @@ def test_scan_validation(kw, want):
     ({"batch": 4096, "nheads": 64, "seqlen": 1, "chunk": 64}, _capi.SSM_OK),
     # 2^23 steps in one head: the backward's dB reduction needs 2^33 threads, the forward fits
     ({"batch": 8, "seqlen": 1 << 23, "nheads": 1}, _capi.SSM_OK),
+    # seqlen * nheads * headdim * 2 would wrap in 64 bits: seqlen is bounded first
+    ({"seqlen": 1 << 62}, _capi.SSM_ENOTSUP),
 ])
 def test_ssd_validation(kw, want):
     assert ssd_status(ssd_args(**kw)) == want
@@ -231,6 +235,7 @@ def conv_args(**kw):
     ({"dstate": 512}, _capi.SSM_ENOTSUP),
     ({"ngroups": 7}, _capi.SSM_EINVAL),
     ({"batch": 1 << 20, "dim": 1 << 14, "dstate": 256}, _capi.SSM_ENOTSUP),   # 2^39 states: one launch
+    ({"batch": 1 << 40, "dim": 1 << 24}, _capi.SSM_ENOTSUP),   # batch * dim = 2^64 wraps to 0
 ])
 def test_step_validation(kw, want):
     lib = _capi.lib()
@@ -246,6 +251,7 @@ def test_step_validation(kw, want):
     ({"dstate": 100}, _capi.SSM_ENOTSUP),
     ({"ngroups": 3}, _capi.SSM_EINVAL),
     ({"batch": 1 << 20, "nheads": 256, "dstate": 256}, _capi.SSM_ENOTSUP),   # 2^42 states: one launch
+    ({"batch": 1 << 46, "nheads": 4096}, _capi.SSM_ENOTSUP),   # batch * nheads * headdim = 2^64 wraps to 0
 ])
 def test_ssd_step_validation(kw, want):
     assert _capi.lib().ssd_state_update(ctypes.byref(ssd_step_args(**kw)), None) == want
