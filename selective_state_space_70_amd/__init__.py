@@ -42,6 +42,29 @@ def _need(t, name, shape, dtype, device):
         raise ValueError("%s must be contiguous" % name)
 
 
+def _span(t: Optional[torch.Tensor]):
+    if t is None or t.numel() == 0:
+        return None
+    start = t.data_ptr()
+    return start, start + t.numel() * t.element_size()
+
+
+def _no_overlap(outs, ins):
+    """Raise if a written buffer shares memory with another written buffer or with an
+    input. The kernels read their inputs while the outputs are being written, so
+    aliasing gives wrong results, not an in-place update. ``outs`` and ``ins`` are
+    (name, tensor or None) pairs; tensors are contiguous, so byte ranges are exact."""
+    spans = [(n, _span(t)) for n, t in outs]
+    others = [(n, _span(t)) for n, t in ins]
+    for i, (n, s) in enumerate(spans):
+        if s is None:
+            continue
+        for m, r in spans[i + 1:] + others:
+            if r is not None and s[0] < r[1] and r[0] < s[1]:
+                raise ValueError("%s shares memory with %s: outputs must not alias inputs or "
+                                 "each other" % (n, m))
+
+
 def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
@@ -134,6 +157,9 @@ def selective_scan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm
                 raise ValueError("passes='apply' needs the workspace filled by 'chunk_states'")
             workspace = torch.empty(need, dtype=torch.uint8, device=dev)
         a.workspace, a.workspace_bytes = workspace.data_ptr(), need
+    _no_overlap([("out", y), ("final_state_out", hf), ("workspace", workspace if need else None)],
+                [("x", x), ("delta", delta), ("z", z), ("Bm", Bm), ("Cm", Cm), ("A", A),
+                 ("Dskip", Dskip), ("delta_bias", delta_bias), ("h0", h0)])
     _capi.check(entry(ctypes.byref(a), _stream(dev)))
     return y, hf
 
@@ -207,6 +233,9 @@ def ssd_chunked_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, Bm: torc
         if workspace is None or workspace.numel() * workspace.element_size() < need:
             workspace = torch.empty(need, dtype=torch.uint8, device=dev)
         a.workspace, a.workspace_bytes = workspace.data_ptr(), need
+    _no_overlap([("out", y), ("final_state_out", hf), ("workspace", workspace if need else None)],
+                [("x", x), ("dt", dt), ("z", z), ("Bm", Bm), ("Cm", Cm), ("A", A),
+                 ("Dskip", Dskip), ("dt_bias", dt_bias), ("h0", h0)])
     _capi.check(L_.ssd_chunked_fwd(ctypes.byref(a), _stream(dev)))
     return y, hf
 
@@ -251,6 +280,9 @@ def selective_state_update(state: torch.Tensor, x: torch.Tensor, delta: torch.Te
     a.x, a.delta, a.z, a.Bm, a.Cm = _ptr(x), _ptr(delta), _ptr(z), _ptr(Bm), _ptr(Cm)
     a.A, a.delta_bias, a.Dskip = _ptr(A), _ptr(delta_bias), _ptr(Dskip)
     a.state, a.y = _ptr(state), _ptr(y)
+    _no_overlap([("out", y), ("state", state)],
+                [("x", x), ("delta", delta), ("z", z), ("Bm", Bm), ("Cm", Cm), ("A", A),
+                 ("Dskip", Dskip), ("delta_bias", delta_bias)])
     _capi.check(_capi.lib().selective_state_update(ctypes.byref(a), _stream(dev)))
     return y
 
@@ -287,6 +319,9 @@ def ssd_state_update(state: torch.Tensor, x: torch.Tensor, dt: torch.Tensor, A: 
     a.x, a.dt, a.dt_bias, a.A = _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A)
     a.Bm, a.Cm, a.Dskip, a.z = _ptr(Bm), _ptr(Cm), _ptr(Dskip), _ptr(z)
     a.state, a.y = _ptr(state), _ptr(y)
+    _no_overlap([("out", y), ("state", state)],
+                [("x", x), ("dt", dt), ("z", z), ("Bm", Bm), ("Cm", Cm), ("A", A),
+                 ("Dskip", Dskip), ("dt_bias", dt_bias)])
     _capi.check(_capi.lib().ssd_state_update(ctypes.byref(a), _stream(dev)))
     return y
 
@@ -320,6 +355,8 @@ def causal_conv1d_fwd(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torc
     a.apply_silu = 1 if apply_silu else 0
     a.x, a.weight, a.bias, a.init_state = _ptr(x), _ptr(weight), _ptr(bias), _ptr(init_state)
     a.y, a.final_state = _ptr(y), _ptr(fs)
+    _no_overlap([("out", y), ("final_state_out", fs)],
+                [("x", x), ("weight", weight), ("bias", bias), ("init_state", init_state)])
     _capi.check(_capi.lib().causal_conv1d_fwd(ctypes.byref(a), _stream(dev)))
     return (y, fs) if return_final_state else y
 

@@ -366,3 +366,46 @@ def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
     import selective_state_space_70_amd as ssm
     with pytest.raises(RuntimeError, match="not built"):
         ssm.abi_version()
+
+
+def test_overlap_check_logic():
+    """The binding's aliasing check on plain CPU tensors: views that share bytes are
+    rejected, disjoint slices of one buffer and absent or empty tensors pass."""
+    from selective_state_space_70_amd import _no_overlap
+    buf = torch.zeros(64)
+    a, b = buf[:32], buf[32:]
+    _no_overlap([("out", a)], [("x", b), ("z", None), ("e", buf[:0])])
+    with pytest.raises(ValueError, match="out shares memory with x"):
+        _no_overlap([("out", buf[16:48])], [("x", b)])
+    with pytest.raises(ValueError, match="out shares memory with state"):
+        _no_overlap([("out", buf[:8]), ("state", buf[4:12])], [])
+    _no_overlap([("out", buf[:8]), ("state", buf[8:16])], [("x", buf[16:])])   # touching, not overlapping
+
+
+@pytest.mark.gpu
+def test_binding_rejects_aliased_outputs():
+    """Every entry point with caller-provided outputs refuses an output that shares
+    memory with an input before anything is launched."""
+    import selective_state_space_70_amd as ssm
+    dev = torch.device("cuda:0")
+    x = torch.randn(1, 64, 64, device=dev).to(torch.bfloat16)
+    A = -torch.ones(64, 16, device=dev)
+    B = torch.randn(1, 64, 16, device=dev).to(torch.bfloat16)
+    with pytest.raises(ValueError, match="out shares memory with x"):
+        ssm.selective_scan_fwd(x, x.clone(), A, B, B, out=x)
+    w = torch.randn(64, 4, device=dev)
+    with pytest.raises(ValueError, match="out shares memory with x"):
+        ssm.causal_conv1d_fwd(x, w, out=x)
+    st = torch.zeros(1, 64, 16, device=dev)
+    xs = torch.randn(1, 64, device=dev)
+    with pytest.raises(ValueError, match="out shares memory with state"):
+        ssm.selective_state_update(st, xs, xs.clone(), A, xs[:, :16].clone(), xs[:, :16].clone(),
+                                   out=st.view(-1)[:64].view(1, 64))
+    xh = torch.randn(1, 64, 2, 64, device=dev).to(torch.bfloat16)
+    dt = torch.randn(1, 64, 2, device=dev).to(torch.bfloat16)
+    Bh = torch.randn(1, 64, 64, device=dev).to(torch.bfloat16)
+    with pytest.raises(ValueError, match="final_state_out shares memory with h0"):
+        h0 = torch.zeros(1, 2, 64, 64, device=dev)
+        ssm.ssd_chunked_fwd(xh, dt, -torch.ones(2, device=dev), Bh, Bh, h0=h0, chunk=64,
+                            final_state_out=h0)
+    torch.cuda.synchronize()
