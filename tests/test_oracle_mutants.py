@@ -34,6 +34,11 @@ MUTANTS = [
      "return log(1.0 + exp(v));", "scan"),
     ("bias_ignored", "const double v = (double)delta[e] + bias;", "const double v = (double)delta[e];", "scan"),
     ("h0_ignored", "h[n] = h0 ? h0[(b * D + d) * N + n] : 0.0;", "h[n] = 0.0;", "scan"),
+    ("h0_layout", "h[n] = h0 ? h0[(b * D + d) * N + n] : 0.0;", "h[n] = h0 ? h0[(d * batch + b) * N + n] : 0.0;",
+     "scan"),
+    ("bias_from_channel_0", "(double)delta_bias[d]", "(double)delta_bias[0]", "scan"),
+    ("skip_from_channel_0", "const double dsk = Dskip ? (double)Dskip[d] : 0.0;",
+     "const double dsk = Dskip ? (double)Dskip[0] : 0.0;", "scan"),
     ("h_final_index", "double *hf = chans ? h_final + i * N : h_final + (b * D + d) * N;",
      "double *hf = chans ? h_final + i * N : h_final + (d * batch + b) * N;", "scan"),
     ("ssd_dt_dropped_from_decay", "const double abar = exp(dtv * a);", "const double abar = exp(a);", "ssd"),
@@ -51,6 +56,14 @@ MUTANTS = [
     ("bwd_dC_previous_state", "pC[r + n] += dyc * hs[(t + 1) * N + n];", "pC[r + n] += dyc * hs[t * N + n];", "bwd"),
     ("bwd_softplus_derivative", "ddt / (1.0 + exp(-v))", "ddt / (1.0 + exp(v))", "bwd"),
     ("bwd_gate_derivative", "s * (1.0 + zv * (1.0 - s))", "s * (1.0 + zv * s)", "bwd"),
+    ("bwd_dA_drops_dt", "dA[d * N + n] += gn * dt * abar * hprev;", "dA[d * N + n] += gn * abar * hprev;", "bwd"),
+    ("bwd_dB_drops_x", "pB[r + n] += gn * dt * xv;", "pB[r + n] += gn * dt;", "bwd"),
+    ("bwd_dDskip_ungated", "dDskip[d] += dyc * xv;", "dDskip[d] += (double)dy[e] * xv;", "bwd"),
+    ("bwd_dbias_before_softplus", "dbias[d] += dd;", "dbias[d] += ddt;", "bwd"),
+    ("bwd_dh0_not_decayed", "dh0[(b * D + d) * N + n] = g[n];",
+     "dh0[(b * D + d) * N + n] = L > 0 ? g[n] / exp(dts[0] * (double)A[d * N + n]) : g[n];", "bwd"),
+    ("bwd_dz_readout_previous_state", "yc += (double)Cm[r + n] * hs[(t + 1) * N + n];",
+     "yc += (double)Cm[r + n] * hs[t * N + n];", "bwd"),
     ("conv_not_causal", "const int64_t s = t - (K - 1) + k;", "const int64_t s = t - k;", "conv"),
     ("conv_history_reversed", "x0[(b * (K - 1) + (K - 1) + s) * D + d]", "x0[(b * (K - 1) - 1 - s) * D + d]",
      "conv"),
