@@ -47,6 +47,12 @@ MUTANTS = [
      "h[n] = abar * h[n] + (double)Bm[r + n] * xv;", "ssd"),
     ("ssd_x_layout", "const int64_t e = ((b * L + t) * H + hh) * P + p;",
      "const int64_t e = ((b * L + t) * P + p) * H + hh;", "ssd"),
+    ("ssd_skip_from_head_0", "const double dsk = Dskip ? (double)Dskip[hh] : 0.0;",
+     "const double dsk = Dskip ? (double)Dskip[0] : 0.0;", "ssd"),
+    ("ssd_bias_from_head_0", "(double)dt_bias[hh]", "(double)dt_bias[0]", "ssd"),
+    ("ssd_A_per_group", "const double a = (double)A[hh];", "const double a = (double)A[g];", "ssd"),
+    ("ssd_h0_layout", "h[n] = h0 ? h0[c * N + n] : 0.0;",
+     "h[n] = h0 ? h0[((p * H + hh) * batch + b) * N + n] : 0.0;", "ssd"),
     ("group_of_channel", "const int64_t g = d / (D / G);", "const int64_t g = d % G;", "scan"),
     ("ssd_group_of_head", "const int64_t g = hh / (H / G);", "const int64_t g = hh % G;", "ssd"),
     ("bwd_ddt_drops_decay_term", "ddt += gn * ((double)Bm[r + n] * xv + (double)A[d * N + n] * abar * hprev);",
