@@ -53,7 +53,8 @@ namespace {
 //         output (with x + xlo = dy silu(z) and B = C this is the adjoint aggregate
 //         of the gradient pass).
 template <int N, int Q, int MODE>
-__global__ __launch_bounds__(kThreads, (N > 128 || MODE != 0) ? 1 : 2) void ssd_chunk_state_kernel(const SSDK p) {
+__global__ __launch_bounds__(kThreads, (N > 128 || MODE != 0) ? 1 : 2) void ssd_chunk_state_kernel(const SSDK p,
+                                                                                                int64_t nq) {
     constexpr bool SPLIT = MODE != 0;
     constexpr int SB = 64;                    // time rows staged per step
     constexpr int LDT = SB + 8;               // padded LDS row (bf16)
@@ -66,15 +67,22 @@ __global__ __launch_bounds__(kThreads, (N > 128 || MODE != 0) ? 1 : 2) void ssd_
     __shared__ __attribute__((aligned(16))) uint16_t XT[4][kP][LDT];
     __shared__ __attribute__((aligned(16))) uint16_t XL[SPLIT ? 4 : 1][SPLIT ? kP : 1][SPLIT ? LDT : 8];
 
-    // head groups vary fastest: the workgroups of one chunk run together and read
-    // whole rows of x between them
-    const int c = blockIdx.y, b = blockIdx.z;
+    // block -> ((batch, chunk) q, head block). Workgroup i runs on XCD i % 8, and
+    // q % 8 = i % 8 here, so every head block of a chunk runs on one XCD: the chunk's
+    // B rows come into one L2 instead of all eight. Neighbouring ids are neighbouring
+    // chunks, so the workgroups of a chunk still run close together in time.
+    const int hb = (p.hpg + 3) / 4;                   // workgroups per group of heads
+    const int upc = p.G * hb;                         // workgroups per (batch, chunk)
+    const int k8 = blockIdx.x >> 3;
+    const int64_t q = (int64_t)(k8 / upc) * 8 + (blockIdx.x & 7);
+    if (q >= nq) return;                              // whole workgroup (uniform)
+    const int unit = k8 % upc;
+    const int c = (int)(q % p.nc), b = (int)(q / p.nc);
     // the wave index is uniform: readfirstlane keeps it (and every address built
     // from it) in SGPRs, so buffer resources need no per-lane loop
     const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r16 = lane & 15, kb = lane >> 4;
-    const int hb = (p.hpg + 3) / 4;                   // workgroups per group of heads
-    const int g = blockIdx.x / hb, hl = (blockIdx.x % hb) * 4 + wv;
+    const int g = unit / hb, hl = (unit % hb) * 4 + wv;
     const bool head_ok = hl < p.hpg;
     const int h = g * p.hpg + (head_ok ? hl : p.hpg - 1);   // clamped into the group
     const int hc = h;
@@ -693,15 +701,20 @@ __global__ __launch_bounds__(256) void ssd_copy_state_kernel(const float *h0, fl
     if (i < n) out[i] = h0 ? h0[i] : 0.0f;
 }
 
+// Workgroups of the chunk-state kernel: the (batch, chunk) count rounded up to 8, times
+// the head blocks of 4 per chunk (the kernel returns for ids past the last chunk).
+unsigned chunk_state_blocks(const SSDK &k, int64_t nq) {
+    return (unsigned)((nq + 7) / 8 * 8 * (k.G * ((k.hpg + 3) / 4)));
+}
+
 template <int N, int Q>
 void launch_nq(const SSDK &k, int batch, hipStream_t s) {
-    hipLaunchKernelGGL((ssd_chunk_state_kernel<N, Q, 0>), dim3((unsigned)(k.G * ((k.hpg + 3) / 4)), (unsigned)k.nc, (unsigned)batch),
-                       dim3(kThreads), 0, s, k);
+    const int64_t nq = (int64_t)batch * k.nc;            // (batch, chunk) pairs
+    hipLaunchKernelGGL((ssd_chunk_state_kernel<N, Q, 0>), dim3(chunk_state_blocks(k, nq)), dim3(kThreads), 0, s, k, nq);
     const int64_t total = (int64_t)batch * k.H * kP * N / 4;
     hipLaunchKernelGGL(ssd_state_pass_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
                        k, N, total);
     const int nhg = (k.hpg + OutCfg<N>::HG - 1) / OutCfg<N>::HG;
-    const int64_t nq = (int64_t)batch * k.nc;            // (batch, chunk) pairs
     const int64_t nblocks = (nq + 7) / 8 * 8 * (k.G * nhg * out_split<N, Q>());
     hipLaunchKernelGGL((ssd_chunk_out_kernel<N, Q, false>), dim3((unsigned)nblocks),
                        dim3(Q * 4 / out_split<N, Q>()), 0, s, k, nhg, nq);
@@ -719,20 +732,20 @@ void launch_n(const SSDK &k, int batch, int Q, hipStream_t s) {
 // pieces of the forward for the gradient pass
 template <int N, int Q>
 void recompute_nq(const SSDK &k, int batch, int what, hipStream_t s) {
-    const dim3 cs_grid((unsigned)(k.G * ((k.hpg + 3) / 4)), (unsigned)k.nc, (unsigned)batch);
+    const int64_t nq = (int64_t)batch * k.nc;
+    const dim3 cs_grid(chunk_state_blocks(k, nq));
     if (what == 0) {          // split-precision chunk states, then the entering states
-        hipLaunchKernelGGL((ssd_chunk_state_kernel<N, Q, 1>), cs_grid, dim3(kThreads), 0, s, k);
+        hipLaunchKernelGGL((ssd_chunk_state_kernel<N, Q, 1>), cs_grid, dim3(kThreads), 0, s, k, nq);
         const int64_t total = (int64_t)batch * k.H * kP * N / 4;
         hipLaunchKernelGGL(ssd_state_pass_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
                            k, N, total);
     } else if (what == 1) {   // fp32 pre-gate output
         const int nhg = (k.hpg + OutCfg<N>::HG - 1) / OutCfg<N>::HG;
-        const int64_t nq = (int64_t)batch * k.nc;
         const int64_t nblocks = (nq + 7) / 8 * 8 * (k.G * nhg * out_split<N, Q>());
         hipLaunchKernelGGL((ssd_chunk_out_kernel<N, Q, true>), dim3((unsigned)nblocks),
                            dim3(Q * 4 / out_split<N, Q>()), 0, s, k, nhg, nq);
     } else {                  // adjoint aggregates (exp(cs_t) weights)
-        hipLaunchKernelGGL((ssd_chunk_state_kernel<N, Q, 2>), cs_grid, dim3(kThreads), 0, s, k);
+        hipLaunchKernelGGL((ssd_chunk_state_kernel<N, Q, 2>), cs_grid, dim3(kThreads), 0, s, k, nq);
     }
 }
 
