@@ -110,7 +110,9 @@ ssm_status check_ssd_sizes(const ssm_ssd_args *a) {
     if ((a->seqlen + a->chunk - 1) / a->chunk > 65535)
         return fail(SSM_ENOTSUP, "ssd_chunked: at most 65535 chunks");
     // threads of the output kernel: 4 * chunk per (batch, chunk, pair of heads),
-    // the (batch, chunk) count rounded up to a multiple of 8
+    // the (batch, chunk) count rounded up to a multiple of 8. The chunk-state kernel's
+    // one-dimensional grid is no larger: 256 threads per (batch, chunk, 4 heads of a
+    // group), at most 256 * nheads per (batch, chunk).
     if ((a->batch * ((a->seqlen + a->chunk - 1) / a->chunk) + 7) * a->nheads * a->chunk * 4 >
         kMaxLaunchThreads)
         return fail(SSM_ENOTSUP, "ssd_chunked: batch * chunks * heads too large for one launch");
