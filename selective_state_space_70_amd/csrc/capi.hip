@@ -197,9 +197,9 @@ ssm_status check_step(const ssm_scan_step_args *a) {
     // batch * dim <= 2^34, tested by division so that the test itself cannot overflow
     if (a->dim > (1 << 30) || a->batch > ((int64_t)1 << 34) / a->dim)
         return fail(SSM_ENOTSUP, "selective_state_update: dim <= 2^30 and batch*dim <= 2^34 supported");
-    // one thread per 4 states of two channels (and the rest of its last block)
-    if (a->batch * a->dim * a->dstate / 8 + 256 > kMaxLaunchThreads)
-        return fail(SSM_ENOTSUP, "selective_state_update: batch*dim*dstate must be < 2^35");
+    // one thread per 4 states of a channel (and the rest of its last block)
+    if (a->batch * a->dim * a->dstate / 4 + 256 > kMaxLaunchThreads)
+        return fail(SSM_ENOTSUP, "selective_state_update: batch*dim*dstate must be < 2^34");
     if (a->batch == 0) return SSM_OK;
     if (!a->x || !a->delta || !a->Bm || !a->Cm || !a->A || !a->state || !a->y)
         return fail(SSM_EINVAL, "selective_state_update: x, delta, Bm, Cm, A, state and y are required");
@@ -229,8 +229,8 @@ ssm_status check_ssd_step(const ssm_ssd_step_args *a) {
     if (a->nheads > (1 << 20) || a->headdim > (1 << 20) || a->nheads * a->headdim > (1 << 30) ||
         a->batch > ((int64_t)1 << 34) / (a->nheads * a->headdim))
         return fail(SSM_ENOTSUP, "ssd_state_update: nheads*headdim <= 2^30 and batch*nheads*headdim <= 2^34");
-    if (a->batch * a->nheads * a->headdim * a->dstate / 8 + 256 > kMaxLaunchThreads)
-        return fail(SSM_ENOTSUP, "ssd_state_update: batch*nheads*headdim*dstate must be < 2^35");
+    if (a->batch * a->nheads * a->headdim * a->dstate / 4 + 256 > kMaxLaunchThreads)
+        return fail(SSM_ENOTSUP, "ssd_state_update: batch*nheads*headdim*dstate must be < 2^34");
     if (a->batch == 0) return SSM_OK;
     if (!a->x || !a->dt || !a->Bm || !a->Cm || !a->A || !a->state || !a->y)
         return fail(SSM_EINVAL, "ssd_state_update: x, dt, Bm, Cm, A, state and y are required");

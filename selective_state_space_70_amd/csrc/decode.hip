@@ -45,32 +45,42 @@ __global__ __launch_bounds__(256) void state_update_kernel(const StepK k) {
     const T *x = (const T *)k.x, *dtp = (const T *)k.dt, *z = (const T *)k.z;
     int64_t cs[U];
     bool ok[U];
-    float xv[U], dtx[U], dtv[U];
-    f32x4 st[U], bv[U], av[U];
-    int hs[U];
+    float xv[U], dtx[U], dtv[U], dsk[U], zv[U];
+    f32x4 st[U], bv[U], cv[U], av[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int64_t c = ((int64_t)blockIdx.x * U + u) * CPB + tid / G;
         ok[u] = c < k.channels;            // whole channel groups drop out together
         cs[u] = ok[u] ? c : 0;
     }
-    // every load of the U channels first, then the arithmetic
+    // Every load of the U channels first, then the arithmetic. C, D and z are loaded
+    // here too: the state stores below may alias any of them as far as the compiler
+    // knows, so a load placed after a store would wait for it to complete.
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int64_t c = cs[u];
         const int64_t b = c / k.D;
         const int d = (int)(c % k.D);
         const int h = HEADS ? d / k.P : d;     // parameter index: head or channel
-        hs[u] = h;
         const int64_t dt_idx = HEADS ? b * (k.D / k.P) + h : c;
         const int64_t row = (b * k.G + h / k.ppg) * N + 4 * q;     // (b, group, 4q..)
-        const T *Bm = (const T *)k.Bm + row;
-        dtv[u] = to_f32(dtp[dt_idx]) + (k.dt_bias ? k.dt_bias[h] : 0.0f);
+        const T *Bm = (const T *)k.Bm + row, *Cm = (const T *)k.Cm + row;
+        // optional inputs are read from a valid stand-in when absent (A has an entry
+        // for every head or channel, x one for every channel) and the value is dropped
+        // afterwards: the loads stay unconditional, with no branch whose join would
+        // wait for every load in flight
+        const float *biasp = k.dt_bias ? k.dt_bias : k.A, *dskp = k.Dskip ? k.Dskip : k.A;
+        const T *zp = z ? z : x;
+        const float bias = biasp[h], dskv = dskp[h];
+        dtv[u] = to_f32(dtp[dt_idx]) + (k.dt_bias ? bias : 0.0f);
         xv[u] = to_f32(x[c]);
+        dsk[u] = k.Dskip ? dskv : 0.0f;
+        zv[u] = to_f32(zp[c]);
         st[u] = *(const f32x4 *)(k.state + c * N + 4 * q);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             bv[u][i] = to_f32(Bm[i]);
+            cv[u][i] = to_f32(Cm[i]);
             av[u][i] = HEADS ? k.A[h] : k.A[(int64_t)d * N + 4 * q + i];
         }
     }
@@ -83,23 +93,20 @@ __global__ __launch_bounds__(256) void state_update_kernel(const StepK k) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int64_t c = cs[u];
-        const int64_t b = c / k.D;
-        const int h = hs[u];
-        const T *Cm = (const T *)k.Cm + (b * k.G + h / k.ppg) * N + 4 * q;
         f32x4 s = st[u];
         float part = 0.0f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const float decay = fast_exp2(dtv[u] * av[u][i] * kLog2e);
             s[i] = fmaf(decay, s[i], dtx[u] * bv[u][i]);
-            part = fmaf(to_f32(Cm[i]), s[i], part);
+            part = fmaf(cv[u][i], s[i], part);
         }
         if (ok[u]) *(f32x4 *)(k.state + c * N + 4 * q) = s;
 #pragma unroll
         for (int o = 1; o < G; o <<= 1) part += __shfl_xor(part, o, 64);
         if (ok[u] && q == 0) {
-            float out = fmaf(k.Dskip ? k.Dskip[h] : 0.0f, xv[u], part);
-            if (z) out *= silu_f32(to_f32(z[c]));
+            float out = fmaf(dsk[u], xv[u], part);
+            if (z) out *= silu_f32(zv[u]);
             store_val((T *)k.y + c, out);
         }
     }
@@ -107,7 +114,7 @@ __global__ __launch_bounds__(256) void state_update_kernel(const StepK k) {
 
 template <typename T, bool HEADS>
 void launch_step(const StepK &k, int N, hipStream_t s) {
-    constexpr int U = 2;                     // channel groups per thread (4 measured slower)
+    constexpr int U = 1;                     // channel groups per thread (2 and 4 measured slower)
     const int64_t cpb = 256 / (N / 4);       // channels per block
     const dim3 grid((unsigned)((k.channels + cpb * U - 1) / (cpb * U)));
     switch (N) {
