@@ -34,16 +34,20 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 template <typename T, int V>
 struct Vec;
 
+// load_raw fetches a lane's vector without converting it (so a block of rows can be
+// in flight in few registers); unpack converts it to fp32.
 template <>
 struct Vec<uint16_t, 8> {
-    __device__ __forceinline__ static void load(const uint16_t *p, float (&o)[8]) {
-        const u32x4 v = *(const u32x4 *)p;
+    typedef u32x4 Raw;
+    __device__ __forceinline__ static Raw load_raw(const uint16_t *p) { return *(const u32x4 *)p; }
+    __device__ __forceinline__ static void unpack(const Raw &v, float (&o)[8]) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             o[2 * i] = bf16_lo(v[i]);
             o[2 * i + 1] = bf16_hi(v[i]);
         }
     }
+    __device__ __forceinline__ static void load(const uint16_t *p, float (&o)[8]) { unpack(load_raw(p), o); }
     __device__ __forceinline__ static void store(uint16_t *p, const float (&o)[8]) {
         u32x4 v;
 #pragma unroll
@@ -55,11 +59,13 @@ struct Vec<uint16_t, 8> {
 
 template <>
 struct Vec<float, 4> {
-    __device__ __forceinline__ static void load(const float *p, float (&o)[4]) {
-        const f32x4 v = *(const f32x4 *)p;
+    typedef f32x4 Raw;
+    __device__ __forceinline__ static Raw load_raw(const float *p) { return *(const f32x4 *)p; }
+    __device__ __forceinline__ static void unpack(const Raw &v, float (&o)[4]) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[i] = v[i];
     }
+    __device__ __forceinline__ static void load(const float *p, float (&o)[4]) { unpack(load_raw(p), o); }
     __device__ __forceinline__ static void store(float *p, const float (&o)[4]) {
         *(f32x4 *)p = f32x4{o[0], o[1], o[2], o[3]};
     }
@@ -67,6 +73,9 @@ struct Vec<float, 4> {
 
 template <typename T>
 struct Vec<T, 1> {
+    typedef T Raw;
+    __device__ __forceinline__ static Raw load_raw(const T *p) { return *p; }
+    __device__ __forceinline__ static void unpack(const Raw &v, float (&o)[1]) { o[0] = to_f32(v); }
     __device__ __forceinline__ static void load(const T *p, float (&o)[1]) { o[0] = to_f32(*p); }
     __device__ __forceinline__ static void store(T *p, const float (&o)[1]) { store_val(p, o[0]); }
 };
@@ -104,11 +113,25 @@ __global__ __launch_bounds__(64) void conv1d_kernel(const ConvK k) {
         }
     }
 
+    // Rows come in blocks of U, each block's loads issued before the previous block's
+    // stores: the memory counter completes in order, so waiting for a load issued
+    // after a store would also wait for the store. Rows past the segment are clamped
+    // to its last row (valid, loaded again, not used), so the loads are unconditional.
+    typedef typename Vec<T, V>::Raw Raw;
+    auto load_block = [&](int64_t tb, Raw (&r)[U]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t row = std::min<int64_t>(tb + u, t1 - 1);
+            r[u] = Vec<T, V>::load_raw(x + (b * k.L + row) * k.D + d0);
+        }
+    };
+    Raw cur_raw[U], nxt_raw[U];
+    if (t0 < t1) load_block(t0, cur_raw);
     for (int64_t t = t0; t < t1; t += U) {
+        load_block(t + U, nxt_raw);
         float cur[U][V];
 #pragma unroll
-        for (int u = 0; u < U; ++u)
-            if (t + u < t1) Vec<T, V>::load(x + (b * k.L + t + u) * k.D + d0, cur[u]);
+        for (int u = 0; u < U; ++u) Vec<T, V>::unpack(cur_raw[u], cur[u]);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             if (t + u < t1) {
@@ -129,6 +152,8 @@ __global__ __launch_bounds__(64) void conv1d_kernel(const ConvK k) {
                 for (int v = 0; v < V; ++v) win[K - 2][v] = cur[u][v];
             }
         }
+#pragma unroll
+        for (int u = 0; u < U; ++u) cur_raw[u] = nxt_raw[u];
     }
     // the window now holds the inputs at t1-(K-1) .. t1-1
     if (k.xf && t1 == k.L) {
