@@ -34,6 +34,7 @@
 // LDS writes.
 #include <algorithm>
 #include <cstdio>
+#include <type_traits>
 
 #include "device_common.h"
 #include "internal.h"
@@ -252,10 +253,17 @@ __global__ __launch_bounds__(kThreads, (N > 128 || MODE != 0) ? 1 : 2) void ssd_
 }
 
 // ---------------------------------------------------------------- state passing
-// One thread per (b, h, p, 4 consecutive n). Loads of a group of chunks are
-// issued together so their latencies overlap.
+// One thread per (b, h, p, 4 consecutive n), sequential over chunks. The chunk states
+// of a group of K chunks are loaded together so their latencies overlap, and the
+// next group's loads go out before this group's stores: the memory counter completes
+// in order, so waiting for a load issued after a store would also wait for the store.
+// S16: the forward (bf16 chunk states, the last chunk's in fp32, bf16 entering states
+// only); otherwise the gradient pass (fp32 chunk states, and the fp32 entering states
+// written over them: chunk c's slot is rewritten only after chunk c has been loaded).
+template <bool S16>
 __global__ __launch_bounds__(256) void ssd_state_pass_kernel(const SSDK p, int N, int64_t total) {
     constexpr int K = 8;
+    typedef typename std::conditional<S16, u32x2, f32x4>::type Raw;
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= total) return;
     const int64_t per_bh = (int64_t)kP * N / 4;
@@ -271,32 +279,44 @@ __global__ __launch_bounds__(256) void ssd_state_pass_kernel(const SSDK p, int N
     const float *dec = p.decay + bh * p.nc;
     const int64_t cstride = (int64_t)p.H * kP * N;
     const int64_t base = (b * p.nc * p.H + h) * kP * N + pn;
-    for (int c0 = 0; c0 < p.nc; c0 += K) {
-        f32x4 sc[K];
-        float dc[K];
+    f32x4 last = f32x4{0.f, 0.f, 0.f, 0.f};   // the forward's last chunk state, fp32
+    if constexpr (S16) last = *(const f32x4 *)(p.states_last + bh * kP * N + pn);
+    // chunks past the end are clamped to the last one (loaded again, not used)
+    auto load_group = [&](int c0, Raw (&r)[K], float (&d)[K]) {
 #pragma unroll
         for (int u = 0; u < K; ++u) {
             const int cc = min(c0 + u, p.nc - 1);
-            if (p.states16 && cc == p.nc - 1) {   // the forward's last chunk, fp32
-                sc[u] = *(const f32x4 *)(p.states_last + bh * kP * N + pn);
-            } else if (p.states16) {              // bf16 chunk states (the forward)
-                const u32x2 v = *(const u32x2 *)(p.states16 + base + cc * cstride);
-                sc[u] = f32x4{bf16_lo(v[0]), bf16_hi(v[0]), bf16_lo(v[1]), bf16_hi(v[1])};
-            } else {
-                sc[u] = *(const f32x4 *)(p.states + base + cc * cstride);
-            }
-            dc[u] = dec[cc];
+            if constexpr (S16) r[u] = *(const u32x2 *)(p.states16 + base + cc * cstride);
+            else r[u] = *(const f32x4 *)(p.states + base + cc * cstride);
+            d[u] = dec[cc];
         }
+    };
+    Raw cur[K], nxt[K];
+    float dcur[K], dnxt[K];
+    load_group(0, cur, dcur);
+    for (int c0 = 0; c0 < p.nc; c0 += K) {
+        load_group(c0 + K, nxt, dnxt);
 #pragma unroll
         for (int u = 0; u < K; ++u) {
             if (c0 + u < p.nc) {
+                f32x4 sc;
+                if constexpr (S16) {
+                    const u32x2 v = cur[u];
+                    sc = c0 + u == p.nc - 1 ? last
+                                            : f32x4{bf16_lo(v[0]), bf16_hi(v[0]), bf16_lo(v[1]), bf16_hi(v[1])};
+                } else {
+                    sc = cur[u];
+                }
                 *(u32x2 *)(p.sin + base + (c0 + u) * cstride) = u32x2{pack_bf16(s[0], s[1]), pack_bf16(s[2], s[3])};
-                // fp32 copy; where it aliases the chunk states this overwrites a
-                // value this thread has already loaded
-                if (p.sin32) *(f32x4 *)(p.sin32 + base + (c0 + u) * cstride) = s;
+                if constexpr (!S16) *(f32x4 *)(p.sin32 + base + (c0 + u) * cstride) = s;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) s[e] = fmaf(dc[u], s[e], sc[u][e]);
+                for (int e = 0; e < 4; ++e) s[e] = fmaf(dcur[u], s[e], sc[e]);
             }
+        }
+#pragma unroll
+        for (int u = 0; u < K; ++u) {
+            cur[u] = nxt[u];
+            dcur[u] = dnxt[u];
         }
     }
     if (p.h_final) {
@@ -712,7 +732,7 @@ void launch_nq(const SSDK &k, int batch, hipStream_t s) {
     const int64_t nq = (int64_t)batch * k.nc;            // (batch, chunk) pairs
     hipLaunchKernelGGL((ssd_chunk_state_kernel<N, Q, 0>), dim3(chunk_state_blocks(k, nq)), dim3(kThreads), 0, s, k, nq);
     const int64_t total = (int64_t)batch * k.H * kP * N / 4;
-    hipLaunchKernelGGL(ssd_state_pass_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
+    hipLaunchKernelGGL(ssd_state_pass_kernel<true>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
                        k, N, total);
     const int nhg = (k.hpg + OutCfg<N>::HG - 1) / OutCfg<N>::HG;
     const int64_t nblocks = (nq + 7) / 8 * 8 * (k.G * nhg * out_split<N, Q>());
@@ -737,7 +757,7 @@ void recompute_nq(const SSDK &k, int batch, int what, hipStream_t s) {
     if (what == 0) {          // split-precision chunk states, then the entering states
         hipLaunchKernelGGL((ssd_chunk_state_kernel<N, Q, 1>), cs_grid, dim3(kThreads), 0, s, k, nq);
         const int64_t total = (int64_t)batch * k.H * kP * N / 4;
-        hipLaunchKernelGGL(ssd_state_pass_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
+        hipLaunchKernelGGL(ssd_state_pass_kernel<false>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
                            k, N, total);
     } else if (what == 1) {   // fp32 pre-gate output
         const int nhg = (k.hpg + OutCfg<N>::HG - 1) / OutCfg<N>::HG;
