@@ -229,33 +229,56 @@ __global__ __launch_bounds__(64) void bwd_carry_kernel(const BwdK p) {
     }
     const float *F = p.aggF + (size_t)chain * p.nch * (N + 1) * 64 + threadIdx.x;
     const float *Rg = p.aggR + (size_t)chain * p.nch * N * 64 + threadIdx.x;
+    // The aggregates of the next chunk are loaded one chunk ahead, before this chunk's
+    // stores: the chain is serial over chunks, and the memory counter completes in
+    // order, so a load issued after a store could not be waited for without the store.
+    // Chunk indices are clamped into the chain (loaded again, not used).
+    const int last = p.nch - 1;
+    float cur[N + 1], nxt[N + 1];   // end state from zero (n < N), summed step (N)
+    auto load_f = [&](int c, float (&r)[N + 1]) {
+        const float *f = F + (size_t)min(c, last) * (N + 1) * 64;
+#pragma unroll
+        for (int n = 0; n <= N; ++n) r[n] = f[n * 64];
+    };
+    load_f(0, cur);
     for (int c = 0; c < p.nch; ++c) {
+        load_f(c + 1, nxt);
         float *o = p.hin + (((int64_t)b * p.nch + c) * p.D + dc) * N;
         if (act) {
 #pragma unroll
             for (int n = 0; n < N; ++n) o[n] = h[n];
         }
-        if (c + 1 < p.nch) {
-            const float *f = F + (size_t)c * (N + 1) * 64;
-            const float ds = f[N * 64];
+        if (c < last) {
 #pragma unroll
-            for (int n = 0; n < N; ++n) h[n] = fmaf(fast_exp2(Al2[n] * ds), h[n], f[n * 64]);
+            for (int n = 0; n < N; ++n) h[n] = fmaf(fast_exp2(Al2[n] * cur[N]), h[n], cur[n]);
         }
+#pragma unroll
+        for (int n = 0; n <= N; ++n) cur[n] = nxt[n];
     }
 #pragma unroll
     for (int n = 0; n < N; ++n) h[n] = p.dh_final ? p.dh_final[ci * N + n] : 0.0f;
-    for (int c = p.nch - 1; c >= 0; --c) {
+    // backwards: chunk c needs its summed step and its adjoint aggregate (c > 0)
+    auto load_r = [&](int c, float (&r)[N + 1]) {
+        const int cc = max(c, 0);
+        const float *q = Rg + (size_t)cc * N * 64;
+#pragma unroll
+        for (int n = 0; n < N; ++n) r[n] = q[n * 64];
+        r[N] = F[(size_t)cc * (N + 1) * 64 + N * 64];
+    };
+    load_r(last, cur);
+    for (int c = last; c >= 0; --c) {
+        load_r(c - 1, nxt);
         float *o = p.uin + (((int64_t)b * p.nch + c) * p.D + dc) * N;
         if (act) {
 #pragma unroll
             for (int n = 0; n < N; ++n) o[n] = h[n];
         }
         if (c > 0) {
-            const float ds = F[(size_t)c * (N + 1) * 64 + N * 64];
-            const float *q = Rg + (size_t)c * N * 64;
 #pragma unroll
-            for (int n = 0; n < N; ++n) h[n] = fmaf(fast_exp2(Al2[n] * ds), h[n], q[n * 64]);
+            for (int n = 0; n < N; ++n) h[n] = fmaf(fast_exp2(Al2[n] * cur[N]), h[n], cur[n]);
         }
+#pragma unroll
+        for (int n = 0; n <= N; ++n) cur[n] = nxt[n];
     }
 }
 
