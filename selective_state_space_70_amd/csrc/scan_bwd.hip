@@ -429,29 +429,52 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_main_kernel(const BwdK p) 
     __syncthreads();
 
     // ---- per (step, channel): dx, ddelta, dz; per-channel and per-row sums
-    for (int q = tid; q < kChunk * CPG; q += NT) {
-        const int i = q / CPG, cc = q % CPG;
-        const int dd = d0 + cc;
-        if (i < nt && dd < p.D) {
-            const int64_t e = ((int64_t)b * p.L + t0 + i) * p.D + dd;
-            const f32x4 pr = pre[i][cc];
-            const float dt = pr[0], dyc = pr[2], xv = pr[3];
-            const float dsk = p.Dskip ? p.Dskip[dd] : 0.0f;
-            const float sB = post[1][i][cc], sA = post[2][i][cc];
-            float gdl = fmaf(xv, sB, sA);                     // d dt
-            if (p.softplus) gdl *= sigmoid_f32(to_f32(Dl[e]) + (p.bias ? p.bias[dd] : 0.0f));
-            store_val((T *)p.dx + e, fmaf(dyc, dsk, dt * sB));
-            store_val((T *)p.ddelta + e, gdl);
+    // Each thread takes EPI pairs of one channel. Every global value they need is loaded
+    // before the first store: the memory counter completes in order, so a load placed
+    // after a store could not be waited for without waiting for the store. Indices are
+    // clamped into the chunk and D, and absent parameters read a valid stand-in (A), so
+    // the loads are unconditional; the values of pairs outside are not used.
+    constexpr int EPI = kChunk * CPG / NT;
+    static_assert(kChunk * CPG % NT == 0 && NT % CPG == 0, "pairs tile the workgroup");
+    {
+        const int cc = tid % CPG, dd = d0 + cc, ddc = std::min(dd, p.D - 1);
+        const float *dskp = p.Dskip ? p.Dskip : p.A, *biasp = p.bias ? p.bias : p.A;
+        const float dskv = dskp[ddc], biasv = biasp[ddc];
+        const float dsk = p.Dskip ? dskv : 0.0f, bias = p.bias ? biasv : 0.0f;
+        float dlv[EPI], zvv[EPI], dyv[EPI];
+#pragma unroll
+        for (int k = 0; k < EPI; ++k) {
+            const int i = std::min(tid / CPG + k * (NT / CPG), nt - 1);
+            const int64_t e = ((int64_t)b * p.L + t0 + i) * p.D + ddc;
+            dlv[k] = to_f32(Dl[e]);
             if constexpr (HAS_Z) {
-                const float zv = to_f32(Z[e]), s = sigmoid_f32(zv);
-                const float dzf = to_f32(DY[e]) * s * fmaf(zv, 1.0f - s, 1.0f);
-                store_val((T *)p.dz + e, dzf * fmaf(dsk, xv, post[0][i][cc]));
+                zvv[k] = to_f32(Z[e]);
+                dyv[k] = to_f32(DY[e]);
             }
-            post[1][i][cc] = dyc * xv;                       // this pair's dDskip and dbias terms
-            post[2][i][cc] = gdl;
-        } else {
-            post[1][i][cc] = 0.0f;
-            post[2][i][cc] = 0.0f;
+        }
+#pragma unroll
+        for (int k = 0; k < EPI; ++k) {
+            const int i = tid / CPG + k * (NT / CPG);
+            if (i < nt && dd < p.D) {
+                const int64_t e = ((int64_t)b * p.L + t0 + i) * p.D + dd;
+                const f32x4 pr = pre[i][cc];
+                const float dt = pr[0], dyc = pr[2], xv = pr[3];
+                const float sB = post[1][i][cc], sA = post[2][i][cc];
+                float gdl = fmaf(xv, sB, sA);                     // d dt
+                if (p.softplus) gdl *= sigmoid_f32(dlv[k] + bias);
+                store_val((T *)p.dx + e, fmaf(dyc, dsk, dt * sB));
+                store_val((T *)p.ddelta + e, gdl);
+                if constexpr (HAS_Z) {
+                    const float zv = zvv[k], s = sigmoid_f32(zv);
+                    const float dzf = dyv[k] * s * fmaf(zv, 1.0f - s, 1.0f);
+                    store_val((T *)p.dz + e, dzf * fmaf(dsk, xv, post[0][i][cc]));
+                }
+                post[1][i][cc] = dyc * xv;                       // this pair's dDskip and dbias terms
+                post[2][i][cc] = gdl;
+            } else {
+                post[1][i][cc] = 0.0f;
+                post[2][i][cc] = 0.0f;
+            }
         }
     }
     __syncthreads();
