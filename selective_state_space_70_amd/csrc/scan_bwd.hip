@@ -383,30 +383,54 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_main_kernel(const BwdK p) 
     const int g = d0 / p.dpg;                 // every channel of the workgroup is in one group
     const T *X = (const T *)p.x, *Dl = (const T *)p.delta, *Z = (const T *)p.z, *DY = (const T *)p.dy;
 
-    // ---- stage per-step rows and per-(step, channel) quantities
-    for (int v = tid; v < kChunk * N; v += NT) {
-        const int i = v / N, nn = v % N;
-        f32x2 bc = f32x2{0.f, 0.f};
-        if (i < nt) {
+    // ---- stage per-step rows and per-(step, channel) quantities. Every load of a thread
+    // is issued before any is used, with indices clamped into the chunk and D and an
+    // absent bias read from A, so the latencies overlap instead of adding up per entry.
+    constexpr int BCI = kChunk * N / NT;          // (step, n) entries per thread
+    constexpr int PRI = kChunk * CPG / NT;        // (step, channel) pairs per thread
+    static_assert(kChunk * N % NT == 0 && kChunk * CPG % NT == 0 && NT % CPG == 0, "entries tile the workgroup");
+    {
+        T braw[BCI], craw[BCI];
+#pragma unroll
+        for (int k = 0; k < BCI; ++k) {
+            const int e = tid + k * NT, i = std::min(e / N, nt - 1), nn = e % N;
             const int64_t r = (((int64_t)b * p.L + t0 + i) * p.G + g) * N + nn;
-            bc = f32x2{to_f32(((const T *)p.Bm)[r]), to_f32(((const T *)p.Cm)[r])};
+            braw[k] = ((const T *)p.Bm)[r];
+            craw[k] = ((const T *)p.Cm)[r];
         }
-        BC[i][nn] = bc;
-    }
-    for (int v = tid; v < kChunk * CPG; v += NT) {
-        const int i = v / CPG, cc = v % CPG;
-        const int d = d0 + cc;
-        f32x4 q = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (i < nt && d < p.D) {
-            const int64_t e = ((int64_t)b * p.L + t0 + i) * p.D + d;
-            const float xv = to_f32(X[e]);
-            const float vv = to_f32(Dl[e]) + (p.bias ? p.bias[d] : 0.0f);
-            const float dt = p.softplus ? softplus_f32(vv) : vv;
-            float dyc = to_f32(DY[e]);
-            if constexpr (HAS_Z) dyc *= silu_f32(to_f32(Z[e]));
-            q = f32x4{dt, dt * xv, dyc, xv};
+        const int cc = tid % CPG, dd = d0 + cc, ddc = std::min(dd, p.D - 1);
+        const float *biasp = p.bias ? p.bias : p.A;
+        const float biasv = biasp[ddc];
+        const float bias = p.bias ? biasv : 0.0f;
+        T xr[PRI], dr[PRI], yr[PRI], zr[PRI];
+#pragma unroll
+        for (int k = 0; k < PRI; ++k) {
+            const int i = std::min(tid / CPG + k * (NT / CPG), nt - 1);
+            const int64_t e = ((int64_t)b * p.L + t0 + i) * p.D + ddc;
+            xr[k] = X[e];
+            dr[k] = Dl[e];
+            yr[k] = DY[e];
+            if constexpr (HAS_Z) zr[k] = Z[e];
         }
-        pre[i][cc] = q;
+#pragma unroll
+        for (int k = 0; k < BCI; ++k) {
+            const int e = tid + k * NT, i = e / N, nn = e % N;
+            BC[i][nn] = i < nt ? f32x2{to_f32(braw[k]), to_f32(craw[k])} : f32x2{0.f, 0.f};
+        }
+#pragma unroll
+        for (int k = 0; k < PRI; ++k) {
+            const int i = tid / CPG + k * (NT / CPG);
+            f32x4 q = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (i < nt && dd < p.D) {
+                const float xv = to_f32(xr[k]);
+                const float vv = to_f32(dr[k]) + bias;
+                const float dt = p.softplus ? softplus_f32(vv) : vv;
+                float dyc = to_f32(yr[k]);
+                if constexpr (HAS_Z) dyc *= silu_f32(to_f32(zr[k]));
+                q = f32x4{dt, dt * xv, dyc, xv};
+            }
+            pre[i][cc] = q;
+        }
     }
     __syncthreads();
 
