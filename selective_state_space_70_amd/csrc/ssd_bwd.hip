@@ -359,11 +359,23 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_bwd_row_kernel(const BwdK k) 
                 block_both(rb, GN, blk & 15, (blk >> 4) * 8, Bn, LDB, BT, LDT, (blk >> 4) * 8);
             const rsrc_t rx = make_rsrc_u(Xbase + (int64_t)s0 * xs + hfirst * kP,
                                         (uint32_t)(std::max(0, T - s0) * xs * 2));
+            // loads in batches of XB, each batch issued before any of its stores (a load
+            // under the head test would be waited for at the test's end, one at a time);
+            // a head past the group reads other x or zeros and is not stored
+            constexpr int XI = HS * 64 * 8 / kThreads, XB = XI < 4 ? XI : 4;
 #pragma unroll
-            for (int i = 0; i < HS * 64 * 8 / kThreads; ++i) {
-                const int v = tid + kThreads * i, j = v >> 9, row = (v >> 3) & 63, cv = v & 7;
-                if (j < nh)
-                    *(u32x4 *)&Xn[(j * 64 + row) * LDX + cv * 8] = load16(rx, (uint32_t)((row * xs + j * kP + cv * 8) * 2));
+            for (int i0 = 0; i0 < XI; i0 += XB) {
+                u32x4 xr[XB];
+#pragma unroll
+                for (int i = 0; i < XB; ++i) {
+                    const int v = tid + kThreads * (i0 + i), j = v >> 9, row = (v >> 3) & 63, cv = v & 7;
+                    xr[i] = load16(rx, (uint32_t)((row * xs + j * kP + cv * 8) * 2));
+                }
+#pragma unroll
+                for (int i = 0; i < XB; ++i) {
+                    const int v = tid + kThreads * (i0 + i), j = v >> 9, row = (v >> 3) & 63, cv = v & 7;
+                    if (j < nh) *(u32x4 *)&Xn[(j * 64 + row) * LDX + cv * 8] = xr[i];
+                }
             }
         }
         __syncthreads();
@@ -694,13 +706,17 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_bwd_col_kernel(const BwdK k) 
         const float *gh = k.gout + ((((int64_t)b * p.nc + c) * p.H + h) * kP) * N;
         // x_s in the accumulator layout (rows s0w + 4kb + i, p = 16q + r16) and as the
         // A operand, loaded before the staging barrier so their latency overlaps it
+        // (rows clamped into the chunk so the loads are unconditional and overlap; a
+        // load under a branch is waited for at the branch's end, one at a time)
         float xv[4][4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int sl = s0w + 4 * kb + i;
+            const int sl = s0w + 4 * kb + i, slc = std::min(sl, T - 1);
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                xv[i][q] = sl < T ? to_f32(p.x[(dbase + (int64_t)sl * xs) + h * kP + 16 * q + r16]) : 0.0f;
+            for (int q = 0; q < 4; ++q) {
+                const float xr = to_f32(p.x[(dbase + (int64_t)slc * xs) + h * kP + 16 * q + r16]);
+                xv[i][q] = sl < T ? xr : 0.0f;
+            }
         }
         bf16x8 xf[2];
         load_x(h, xf);

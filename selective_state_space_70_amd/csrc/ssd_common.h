@@ -100,17 +100,25 @@ __device__ __forceinline__ float head_dt_cs(const SSDK &p, int b, int h, int c, 
                                             float (&cs)[Q / 64]) {
     constexpr int SPL = Q / 64;
     const int lane = threadIdx.x & 63;
-    const float bias = p.dt_bias ? p.dt_bias[h] : 0.0f;
-    const float a = p.A[h];
+    // All loads first and unconditional (steps clamped to the sequence, an absent bias
+    // read from A), so their latencies overlap: a load under a branch is waited for
+    // at the branch's end, one at a time.
+    const float *biasp = p.dt_bias ? p.dt_bias : p.A;
+    const float biasv = biasp[h], a = p.A[h];
+    const float bias = p.dt_bias ? biasv : 0.0f;
+    float raw[SPL];
+#pragma unroll
+    for (int i = 0; i < SPL; ++i) {
+        const int64_t tg = std::min<int64_t>((int64_t)c * Q + lane * SPL + i, p.L - 1);
+        raw[i] = to_f32(p.dt[((int64_t)b * p.L + tg) * p.H + h]);
+    }
     float run = 0.0f;
 #pragma unroll
     for (int i = 0; i < SPL; ++i) {
         const int64_t tg = (int64_t)c * Q + lane * SPL + i;
-        float d = 0.0f;
-        if (tg < p.L) {
-            const float v = to_f32(p.dt[((int64_t)b * p.L + tg) * p.H + h]) + bias;
-            d = p.softplus ? softplus_f32(v) : v;
-        }
+        const float v = raw[i] + bias;
+        const float dt = p.softplus ? softplus_f32(v) : v;
+        const float d = tg < p.L ? dt : 0.0f;
         dtv[i] = d;
         run += a * d;
         cs[i] = run;
