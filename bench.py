@@ -52,7 +52,7 @@ ALU_SLOTS_PER_ELEM = 6
 # same counters read for a plain 256 MiB device copy (FETCH x2.0, WRITE x1.0;
 # see profiles/). Keyed by a hash of the scan kernel sources: any change to them
 # turns the figure into null until it is measured again.
-TRAFFIC = {("S2", "daea05a0c8365902"): 90300 * 1024 * 2 + 49920 * 1024}
+TRAFFIC = {("S2", "88dfb20c708a6bc5"): 90300 * 1024 * 2 + 49920 * 1024}
 METRIC = "scan effective HBM GB/s (% of peak) + Gelem/s over B·L·D·N"
 
 

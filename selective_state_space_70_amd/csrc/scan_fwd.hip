@@ -135,12 +135,14 @@ __device__ __forceinline__ void step_readout(const Chan<N> &c, bool softplus, T 
     }
     float yv = fmaf(c.dsk, xv, acc0 + acc1);
     if constexpr (HAS_Z) yv *= silu_f32(to_f32(zraw));
-    if (act) {
-        if constexpr (sizeof(T) == 2)
-            buf_store(yr, lo, soff, f32_to_bf16(yv));
-        else
-            buf_store(yr, lo, soff, yv);
-    }
+    // Unconditional: a lane past D stores at an offset beyond the buffer's range, which
+    // the hardware drops. With no branch around the stores the compiler knows how many
+    // are in flight, so waiting for the next block's loads does not wait for them.
+    const uint32_t voff = act ? lo : 0x80000000u;
+    if constexpr (sizeof(T) == 2)
+        buf_store(yr, voff, soff, f32_to_bf16(yv));
+    else
+        buf_store(yr, voff, soff, yv);
 }
 
 // Forward pass over [t0, t1) with readout. x/delta/z of the next block of U steps
