@@ -461,14 +461,19 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_main_kernel(const BwdK p) 
     constexpr int EPI = kChunk * CPG / NT;
     static_assert(kChunk * CPG % NT == 0 && NT % CPG == 0, "pairs tile the workgroup");
     {
-        const int cc = tid % CPG, dd = d0 + cc, ddc = std::min(dd, p.D - 1);
+        // The empty asm makes the epilogue's indices opaque, so their 64-bit addresses are
+        // formed here rather than hoisted above the sweep, where they were spilled and each
+        // load then waited on a scratch reload.
+        int et = tid;
+        asm volatile("" : "+v"(et));
+        const int cc = et % CPG, dd = d0 + cc, ddc = std::min(dd, p.D - 1);
         const float *dskp = p.Dskip ? p.Dskip : p.A, *biasp = p.bias ? p.bias : p.A;
         const float dskv = dskp[ddc], biasv = biasp[ddc];
         const float dsk = p.Dskip ? dskv : 0.0f, bias = p.bias ? biasv : 0.0f;
         float dlv[EPI], zvv[EPI], dyv[EPI];
 #pragma unroll
         for (int k = 0; k < EPI; ++k) {
-            const int i = std::min(tid / CPG + k * (NT / CPG), nt - 1);
+            const int i = std::min(et / CPG + k * (NT / CPG), nt - 1);
             const int64_t e = ((int64_t)b * p.L + t0 + i) * p.D + ddc;
             dlv[k] = to_f32(Dl[e]);
             if constexpr (HAS_Z) {
@@ -478,7 +483,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_main_kernel(const BwdK p) 
         }
 #pragma unroll
         for (int k = 0; k < EPI; ++k) {
-            const int i = tid / CPG + k * (NT / CPG);
+            const int i = et / CPG + k * (NT / CPG);
             if (i < nt && dd < p.D) {
                 const int64_t e = ((int64_t)b * p.L + t0 + i) * p.D + dd;
                 const f32x4 pr = pre[i][cc];
