@@ -213,10 +213,14 @@ __global__ __launch_bounds__(kThreads, (N > 128 || MODE != 0) ? 1 : 2) void ssd_
         // holds 8 consecutive n: n = 16i + 8(kb / 2) .. for even kb, n = 16i + 16 +
         // 8(kb / 2) .. for odd kb.
         if (head_ok) {
-            const int64_t o = (((int64_t)b * p.nc + c) * p.H + h) * (int64_t)kP * N;
+            // Opaque copies of the lane's indices keep the store addresses formed here:
+            // formed before the products, they were spilled and reloaded from scratch.
+            int hq = h, r16 = lane & 15, kb = lane >> 4;
+            asm volatile("" : "+v"(hq), "+v"(r16), "+v"(kb));
+            const int64_t o = (((int64_t)b * p.nc + c) * p.H + hq) * (int64_t)kP * N;
             if (MODE == 0 && c == p.nc - 1) {
                 // the last chunk's state only enters h_final: kept in fp32
-                float *out = p.states_last + ((int64_t)b * p.H + h) * (int64_t)kP * N;
+                float *out = p.states_last + ((int64_t)b * p.H + hq) * (int64_t)kP * N;
 #pragma unroll
                 for (int i = 0; i < NT; ++i)
 #pragma unroll
