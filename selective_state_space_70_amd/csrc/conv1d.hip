@@ -82,7 +82,7 @@ struct Vec<T, 1> {
 
 template <typename T, int K, int V>
 __global__ __launch_bounds__(64) void conv1d_kernel(const ConvK k) {
-    constexpr int U = 4;   // time steps whose loads are issued together
+    constexpr int U = 4;   // time steps whose loads are issued together (8 measured no faster)
     const int d0 = (blockIdx.x * 64 + threadIdx.x) * V;
     if (d0 >= k.D) return;
     const int64_t b = blockIdx.z;
