@@ -1,30 +1,31 @@
 """Benchmark of the selective-scan hot path on one MI355X.
 
-Default workload: the Mamba-130M-layer-shaped scan (batch 8, L 2048, D 1536,
-N 16, bf16 storage, fp32 state). One step = one selective_scan_fwd call over
-one batch of synthetic inputs already resident in HBM (every row of the path:
-stream in, softplus, discretise, recurrence, readout, gate, store, final state).
-Several input/output sets are rotated so that repeated steps cannot be served
-from the 256 MB Infinity Cache.
+Default workload: the long-context scan (batch 1, L 131072, D 2048, N 16,
+bf16 storage, fp32 state, dt in [1e-4, 1e-2]), the largest of the scan
+workloads. One step = one selective_scan_fwd call over one batch of synthetic
+inputs already resident in HBM (every row of the path: stream in, softplus,
+discretise, recurrence, readout, gate, store, final state). Several
+input/output sets are rotated so that repeated steps cannot be served from the
+256 MB Infinity Cache.
 
-Prints ONE JSON line on stdout. `value` is the effective HBM bandwidth over the
-algorithmic bytes (x, delta, z, y once per (b,t,d), B and C once per (b,t),
-parameters and the final state once), from the mean time per call;
-`ms_median` and `ms_min` are over the same timed calls. `copy_GBps` is a 512 MiB
-device-to-device copy timed in the same run (bytes read + written per second),
-the practical HBM rate, and `copy_frac` the scan's rate relative to it.
-`roofline` relates the dominant kernel's measured time to its bound;
-`cpu_baseline` is the fp64 oracle timed on the host cores over the same
-workload.
+Prints ONE JSON line on stdout (progress goes to stderr). `value` is the
+effective HBM bandwidth over the algorithmic bytes (x, delta, z, y once per
+(b,t,d), B and C once per (b,t), parameters and the final state once), from the
+mean time per call; `ms_median` and `ms_min` are over the same timed calls.
+`copy_GBps` is a 512 MiB device-to-device copy timed in the same run (bytes read
++ written per second), the practical HBM rate.
 
-The scan is bound by plain fp32 vector arithmetic, not by HBM: per (b,t,d,n)
-element the recurrence needs exp(dt A) (a multiply and an exponential, which
-issues at half rate: 2 slots), dt B x (a multiply once dt x is formed), the
-state FMA and the readout FMA, i.e. ALU_SLOTS_PER_ELEM = 6 issue slots. The
-peak is 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 39.3 T slots/s (no packed
-fp32). The dominant kernel is the apply pass (readout over every element); its
-duration is measured live with HIP events around selective_scan_apply calls on
-the stream the kernels run on.
+`roofline` is that of the dominant kernel, the apply pass (readout over every
+element): the call's algorithmic bytes divided by the kernel's mean duration,
+timed live with HIP events around selective_scan_apply calls on the stream the
+kernels run on, against the 8 TB/s HBM peak. `alu` relates the same duration to
+the fp32 vector issue rate (256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 39.3 T lane
+slots/s, no packed fp32), with the lane slots per element counted by rocprofv3
+(SQ_INSTS_VALU of the kernel at this workload, 64 lanes each). `S2`, `S3` and
+`S5` time the other bf16 workloads in the same run (S5: the chunked SSD form,
+with its matrix-core rate over the useful causal flop count). `parity` is the
+relative L2 error of the whole y and final-state tensors against the fp64
+oracle, which `cpu_baseline` also times on the host cores.
 """
 from __future__ import annotations
 
@@ -45,14 +46,14 @@ import workloads  # noqa: E402
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix peak, TFLOP/s
 ALU_PEAK_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12   # non-packed fp32 VALU issue slots, T/s
-ALU_SLOTS_PER_ELEM = 6
 
-# HBM bytes of one apply-pass launch on the default workload, from rocprofv3
-# --pmc FETCH_SIZE and WRITE_SIZE runs (KiB per dispatch) scaled by what the
-# same counters read for a plain 256 MiB device copy (FETCH x2.0, WRITE x1.0;
-# see profiles/). Keyed by a hash of the scan kernel sources: any change to them
-# turns the figure into null until it is measured again.
-TRAFFIC = {("S2", "88dfb20c708a6bc5"): 90300 * 1024 * 2 + 49920 * 1024}
+# Per-launch counter figures of the apply kernel, keyed by (workload, hash of the
+# scan kernel sources): any change to the sources turns them into null until they
+# are measured again. "traffic": HBM bytes from rocprofv3 --pmc FETCH_SIZE and
+# WRITE_SIZE runs (KiB per dispatch) scaled by what the same counters read for a
+# plain 256 MiB device copy (FETCH x2.0, WRITE x1.0). "valu": SQ_INSTS_VALU per
+# dispatch (wave instructions; 64 lane slots each).
+COUNTERS = {}
 METRIC = "scan effective HBM GB/s (% of peak) + Gelem/s over B·L·D·N"
 
 
@@ -122,12 +123,21 @@ def scan_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def time_scan(key, steps, warmup, torch, ssm, passes="all"):
+def _events(torch, n):
+    return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(n)]
+
+
+def time_scan(key, steps, warmup, torch, ssm, split=False, keep=False):
+    """Mean / median / min HIP-event time per selective_scan_fwd call on one scan
+    workload, rotating input/output sets. With `split` the chunk-state and apply
+    passes are also timed separately (same calls, one pass at a time); with
+    `keep` the outputs of the unrotated set come back to the host for parity."""
     cfg = workloads.CONFIGS[key]
     dev = torch.device("cuda:0")
+    log("%s: generating inputs" % key)
     base = workloads.make_inputs(key)
-    ws_set = scan_alg_bytes(cfg)
-    nsets = max(2, math.ceil(768e6 / ws_set))
+    nsets = max(2, math.ceil(768e6 / scan_alg_bytes(cfg)))
     sets = []
     for i in range(nsets):
         t = _device_inputs(base, torch, dev)
@@ -137,52 +147,66 @@ def time_scan(key, steps, warmup, torch, ssm, passes="all"):
         t["y"] = torch.empty_like(t["x"])
         t["hf"] = torch.empty((cfg.batch, cfg.dim, cfg.dstate), dtype=torch.float32, device=dev)
         sets.append(t)
+    ws = [torch.empty(max(1, ssm.scan_workspace_bytes(cfg.batch, cfg.seqlen, cfg.dim, cfg.dstate,
+                                                      sets[0]["x"].dtype)),
+                      dtype=torch.uint8, device=dev) for _ in range(nsets)]
+
     def call(i, which):
         t = sets[i % nsets]
         ssm.selective_scan_fwd(t["x"], t["delta"], t["A"], t["Bm"], t["Cm"], t["Dskip"], t["z"],
                                t["delta_bias"], None, out=t["y"], final_state_out=t["hf"],
                                workspace=ws[i % nsets], passes=which)
 
-    ws = [torch.empty(max(1, ssm.scan_workspace_bytes(cfg.batch, cfg.seqlen, cfg.dim, cfg.dstate,
-                                                      sets[0]["x"].dtype)),
-                      dtype=torch.uint8, device=dev) for _ in range(nsets)]
+    log("%s: timing %d calls" % (key, steps))
     for i in range(warmup):
         call(i, "all")
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
+    ev = _events(torch, steps)
     t0 = time.perf_counter()
     for i in range(steps):
         ev[i][0].record(stream)
         call(i, "all")
         ev[i][1].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per_call = [a.elapsed_time(b) for a, b in ev]
-    if passes != "split":
-        return cfg, wall, per_call
-    # the two passes timed separately (same inputs, workspace per set)
-    ev1 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
-    ev2 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
-    for i in range(steps):
-        ev1[i][0].record(stream)
-        call(i, "chunk_states")
-        ev1[i][1].record(stream)
-        ev2[i][0].record(stream)
-        call(i, "apply")
-        ev2[i][1].record(stream)
-    torch.cuda.synchronize()
-    states = [a.elapsed_time(b) for a, b in ev1]
-    apply_ = [a.elapsed_time(b) for a, b in ev2]
-    return cfg, wall, per_call, states, apply_
+    out = {"cfg": cfg, "wall": time.perf_counter() - t0,
+           "per_call": [a.elapsed_time(b) for a, b in ev]}
+    if split:
+        ev1, ev2 = _events(torch, steps), _events(torch, steps)
+        for i in range(steps):
+            ev1[i][0].record(stream)
+            call(i, "chunk_states")
+            ev1[i][1].record(stream)
+            ev2[i][0].record(stream)
+            call(i, "apply")
+            ev2[i][1].record(stream)
+        torch.cuda.synchronize()
+        out["states"] = [a.elapsed_time(b) for a, b in ev1]
+        out["apply"] = [a.elapsed_time(b) for a, b in ev2]
+    if keep:
+        out["inputs"] = base
+        out["y"] = sets[0]["y"].float().cpu().numpy()
+        out["hf"] = sets[0]["hf"].cpu().numpy()
+    del sets, ws
+    torch.cuda.empty_cache()
+    return out
 
 
-def time_ssd(steps, warmup, torch, ssm):
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def summary(per_call):
+    srt = sorted(per_call)
+    return sum(per_call) / len(per_call), srt[len(srt) // 2], srt[0]
+
+
+def time_ssd(steps, warmup, torch, ssm, keep=False):
+    """HIP-event time per ssd_chunked_fwd call on the SSD workload, rotating
+    input/output sets; with `keep` the unrotated set's outputs come back."""
     cfg = workloads.CONFIGS["S5"]
     dev = torch.device("cuda:0")
+    log("S5: generating inputs")
     base = workloads.make_inputs("S5")
     nsets = max(2, math.ceil(768e6 / ssd_alg_bytes(cfg)))
     sets = []
@@ -203,18 +227,25 @@ def time_ssd(steps, warmup, torch, ssm):
                             t["dt_bias"], None, chunk=cfg.chunk, out=t["y"],
                             final_state_out=t["hf"], workspace=ws)
 
+    log("S5: timing %d calls" % steps)
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
+    ev = _events(torch, steps)
     for i in range(steps):
         ev[i][0].record(stream)
         step(i)
         ev[i][1].record(stream)
     torch.cuda.synchronize()
-    return cfg, [a.elapsed_time(b) for a, b in ev]
+    out = {"cfg": cfg, "per_call": [a.elapsed_time(b) for a, b in ev]}
+    if keep:
+        out["inputs"] = base
+        out["y"] = sets[0]["y"].float().cpu().numpy()
+        out["hf"] = sets[0]["hf"].cpu().numpy()
+    del sets, ws
+    torch.cuda.empty_cache()
+    return out
 
 
 def measure_copy_rate(torch):
@@ -345,35 +376,77 @@ def time_bwd(key, steps, warmup, torch, ssm):
     return {"ms": round(ms, 4), "GB/s": round(alg / ms / 1e6, 1), "Gelem/s": round(cfg.elements / ms / 1e6, 1)}
 
 
-def cpu_baseline(key, budget_s=10.0):
+def cpu_baseline(key, inp, budget_s=10.0):
     """The fp64 oracle on the host cores over the same workload (all channels,
     whole sequence), repeated until ~budget_s of wall time; effective GB/s on the
-    same algorithmic-bytes count as the GPU figure."""
+    same algorithmic-bytes count as the GPU figure. Also one run on a single
+    thread over a sample of 64 channels (scaled to the whole workload). Returns
+    the baseline record and the oracle's (y, h_final) of the first run."""
     import oracle
     cfg = workloads.CONFIGS[key]
-    inp = workloads.make_inputs(key)
     threads = oracle.num_threads()
+    args = (inp["x"], inp["delta"], inp["A"], inp["Bm"], inp["Cm"], inp["Dskip"], inp["z"],
+            inp["delta_bias"])
+    log("%s: oracle on %d threads" % (key, threads))
     runs, t0 = 0, time.perf_counter()
+    ref = None
     while True:
-        oracle.selective_scan(inp["x"], inp["delta"], inp["A"], inp["Bm"], inp["Cm"],
-                              inp["Dskip"], inp["z"], inp["delta_bias"])
+        res = oracle.selective_scan(*args)
+        if ref is None:
+            ref = res
+        del res
         runs += 1
         el = time.perf_counter() - t0
         if el >= budget_s or runs >= 200:
             break
     per = el / runs
-    # one run on a single thread as well (the same call, OpenMP limited to 1)
     oracle.set_num_threads(1)
+    chans = np.arange(0, cfg.batch * cfg.dim, max(1, cfg.batch * cfg.dim // 64))[:64]
     t1 = time.perf_counter()
-    oracle.selective_scan(inp["x"], inp["delta"], inp["A"], inp["Bm"], inp["Cm"],
-                          inp["Dskip"], inp["z"], inp["delta_bias"])
-    single = time.perf_counter() - t1
+    oracle.selective_scan(*args, channels=chans)
+    single = (time.perf_counter() - t1) * (cfg.batch * cfg.dim) / len(chans)
     oracle.set_num_threads(threads)
-    return {"value": round(scan_alg_bytes(cfg) / per / 1e9, 3), "unit": "GB/s", "cores": threads,
-            "kind": "oracle", "cpu_model": cpu_model(),
-            "single_thread_s": round(single, 3),
-            "sample": "full %s workload (all %d channels x L %d), fp64 C recurrence, %d run(s), "
-                      "%.2f s per run" % (key, cfg.batch * cfg.dim, cfg.seqlen, runs, per)}
+    rec = {"value": round(scan_alg_bytes(cfg) / per / 1e9, 3), "unit": "GB/s", "cores": threads,
+           "kind": "oracle", "cpu_model": cpu_model(),
+           "single_thread_GBps": round(scan_alg_bytes(cfg) / single / 1e9, 4),
+           "sample": "full %s workload (all %d channels x L %d), fp64 C recurrence, %d run(s), "
+                     "%.2f s per run; single thread timed on 64 channels and scaled"
+                     % (key, cfg.batch * cfg.dim, cfg.seqlen, runs, per)}
+    return rec, ref
+
+
+def parity(key, got, inputs):
+    """Relative L2 error of the whole y and final-state tensors against the fp64
+    oracle on the same inputs."""
+    import oracle
+    if key == "S5":
+        yo, ho = oracle.ssd(inputs["x"], inputs["dt"], inputs["A"], inputs["Bm"], inputs["Cm"],
+                            inputs["Dskip"], None, inputs["dt_bias"], None)
+    else:
+        yo, ho = oracle.selective_scan(inputs["x"], inputs["delta"], inputs["A"], inputs["Bm"],
+                                       inputs["Cm"], inputs["Dskip"], inputs["z"],
+                                       inputs["delta_bias"])
+    return parity_of(got, (yo, ho))
+
+
+def parity_of(got, ref):
+    def rel(u, v):
+        u = u.reshape(-1)
+        v = v.reshape(-1)
+        num = den = 0.0
+        for i in range(0, u.size, 1 << 22):
+            a = u[i:i + (1 << 22)].astype(np.float64)
+            b = v[i:i + (1 << 22)]
+            num += float(np.dot(a - b, a - b))
+            den += float(np.dot(b, b))
+        return math.sqrt(num / den) if den else 0.0
+    return {"y_rel_l2": float("%.4g" % rel(got[0], ref[0])),
+            "state_rel_l2": float("%.4g" % rel(got[1], ref[1]))}
+
+
+def gpu_name(torch):
+    p = torch.cuda.get_device_properties(0)
+    return "%s (%s, %d CUs)" % (p.name, getattr(p, "gcnArchName", "?"), p.multi_processor_count)
 
 
 def cpu_model() -> str:
@@ -418,19 +491,28 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="S2", choices=["S1", "S2", "S3", "S4"])
+    ap.add_argument("--config", default="S4", choices=["S1", "S2", "S3", "S4"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-parity", action="store_true",
+                    help="skip the oracle runs that give the rel-L2 fields")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="only the headline workload (no other workloads, oracle or copy probe)")
     ap.add_argument("--extra", action="store_true",
-                    help="also time the other scan workloads and the SSD form (stderr + 'extra')")
+                    help="also time the decode steps, the short convolution and the gradients")
     ap.add_argument("--ssd-only", action="store_true",
                     help="time only the Mamba-2 SSD workload and print its own JSON line "
                          "(for profiling the SSD kernels; not the headline line)")
     ap.add_argument("--next-only", action="store_true",
-                    help="time only the decode steps and the short convolution (own JSON line)")
+                    help="time only the decode steps, the short convolution and the gradients "
+                         "(own JSON line)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run three plain 256 MiB device-to-device copies (the reference "
                          "kernel of known size that calibrates the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(--gpus %d requested)." % args.gpus, file=sys.stderr)
+        sys.exit(2)
     if args.copy_probe:
         import torch
         n = 256 * 1024 * 1024
@@ -442,10 +524,6 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": n, "copies": 3}))
         return
-    if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(--gpus %d requested)." % args.gpus, file=sys.stderr)
-        sys.exit(2)
 
     import torch
     import selective_state_space_70_amd as ssm
@@ -458,73 +536,108 @@ def main():
         return
 
     if args.ssd_only:
-        c5, pc5 = time_ssd(args.steps, args.warmup, torch, ssm)
-        m5 = sum(pc5) / len(pc5)
-        tf = ssd_alg_flops(c5) / m5 / 1e9
-        print(json.dumps({"workload": "S5 " + c5.name, "ms_per_call": round(m5, 5),
-                          "GB/s": round(ssd_alg_bytes(c5) / m5 / 1e6, 1), "TFLOP/s": round(tf, 1),
-                          "mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}), flush=True)
+        r5 = time_ssd(args.steps, args.warmup, torch, ssm)
+        print(json.dumps(dict({"workload": "S5 " + r5["cfg"].name}, **ssd_fields(r5))), flush=True)
         return
 
-    cfg, wall, per_call, t_states, t_apply = time_scan(args.config, args.steps, args.warmup, torch,
-                                                       ssm, passes="split")
-    ms = sum(per_call) / len(per_call)
-    srt = sorted(per_call)
-    ms_median, ms_min = srt[len(srt) // 2], srt[0]
-    copy_gbs = measure_copy_rate(torch)
-    ms_states = sum(t_states) / len(t_states)
-    ms_apply = sum(t_apply) / len(t_apply)
+    key = args.config
+    want_parity = not (args.no_parity or args.headline_only)
+    want_cpu = not (args.no_cpu_baseline or args.headline_only)
+    r = time_scan(key, args.steps, args.warmup, torch, ssm, split=True,
+                  keep=want_parity or want_cpu)
+    cfg = r["cfg"]
+    ms, ms_median, ms_min = summary(r["per_call"])
+    ms_states = sum(r["states"]) / len(r["states"])
+    ms_apply = sum(r["apply"]) / len(r["apply"])
     alg = scan_alg_bytes(cfg)
     gbs = alg / (ms * 1e-3) / 1e9
-    gelem = cfg.elements / (ms * 1e-3) / 1e9
-    slots = ALU_SLOTS_PER_ELEM * cfg.elements / (ms_apply * 1e-3) / 1e12
+    kern_gbs = alg / (ms_apply * 1e-3) / 1e9
     src_hash = scan_source_hash()
-    tr = TRAFFIC.get((args.config, src_hash))
+    cnt = COUNTERS.get((key, src_hash), {})
+    valu = cnt.get("valu")
+    slots = valu * 64 / cfg.elements if valu else None
     line = {
         "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
         "data": "synthetic",
-        "config": {"workload": "%s %s" % (args.config, cfg.name), "batch": cfg.batch,
+        "config": {"workload": "%s %s" % (key, cfg.name), "batch": cfg.batch,
                    "seq_len": cfg.seqlen, "dim": cfg.dim, "dstate": cfg.dstate,
-                   "storage": cfg.dtype, "state": "f32"},
+                   "storage": cfg.dtype, "compute": "f32", "state": "f32"},
+        "gpu": gpu_name(torch),
         "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4),
-        "copy_GBps": round(copy_gbs, 1),
-        "copy_frac": round(gbs / copy_gbs, 4),
         "ms_median": round(ms_median, 5), "ms_min": round(ms_min, 5),
-        "gelem_per_s": round(gelem, 2),
-        "wall_s_timed": round(wall, 4),
-        "roofline": {"bound": "alu", "achieved": round(slots, 3), "peak": round(ALU_PEAK_TSLOTS, 2),
-                     "unit": "T VALU issue slots/s (fp32, non-packed)",
-                     "frac": round(slots / ALU_PEAK_TSLOTS, 4),
-                     "traffic": tr,
+        "gelem_per_s": round(cfg.elements / (ms * 1e-3) / 1e9, 2),
+        "wall_s_timed": round(r["wall"], 4),
+        "roofline": {"bound": "hbm", "achieved": round(kern_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(kern_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": cnt.get("traffic"),
                      "kernel": "scan_main_kernel (selective_scan_apply)",
                      "kernel_ms": round(ms_apply, 5),
-                     "alg_per_unit": "%d slots per (b,t,d,n) element x %d elements"
-                                     % (ALU_SLOTS_PER_ELEM, cfg.elements),
+                     "alg_per_unit": "%d algorithmic bytes per call (x, delta, z, y per (b,t,d); "
+                                     "B, C per (b,t); parameters; final state), one launch per call"
+                                     % alg,
                      "source_hash": src_hash},
+        "alu": {"bound": "fp32 VALU issue", "peak": round(ALU_PEAK_TSLOTS, 2),
+                "unit": "T lane slots/s",
+                "slots_per_elem": round(slots, 3) if slots else None,
+                "achieved": round(slots * cfg.elements / (ms_apply * 1e-3) / 1e12, 2) if slots else None,
+                "frac": round(slots * cfg.elements / (ms_apply * 1e-3) / 1e12 / ALU_PEAK_TSLOTS, 4)
+                if slots else None,
+                "kernel": "scan_main_kernel"},
         "passes_ms": {"chunk_states": round(ms_states, 5), "apply": round(ms_apply, 5)},
     }
+    head_out = (r.get("y"), r.get("hf"))
+    head_in = r.get("inputs")
+    del r
+    if not args.headline_only:
+        line["copy_GBps"] = round(measure_copy_rate(torch), 1)
+        line["copy_frac"] = round(gbs / line["copy_GBps"], 4)
+        for k2 in ("S2", "S3"):
+            if k2 == key:
+                continue
+            r2 = time_scan(k2, max(10, args.steps // 2), 3, torch, ssm, keep=want_parity)
+            m2, _, mn2 = summary(r2["per_call"])
+            c2 = r2["cfg"]
+            line[k2] = {"ms": round(m2, 5), "ms_min": round(mn2, 5),
+                        "GB/s": round(scan_alg_bytes(c2) / m2 / 1e6, 1),
+                        "hbm_frac": round(scan_alg_bytes(c2) / m2 / 1e6 / HBM_PEAK_GBS, 4),
+                        "Gelem/s": round(c2.elements / m2 / 1e6, 1)}
+            if want_parity:
+                log("%s: oracle for parity" % k2)
+                line[k2]["parity"] = parity(k2, (r2["y"], r2["hf"]), r2["inputs"])
+            del r2
+        r5 = time_ssd(max(10, args.steps // 2), 3, torch, ssm, keep=want_parity)
+        line["S5"] = ssd_fields(r5)
+        if want_parity:
+            log("S5: oracle for parity")
+            line["S5"]["parity"] = parity("S5", (r5["y"], r5["hf"]), r5["inputs"])
+        del r5
     if args.extra:
-        extra = {}
-        for key in ("S3", "S4"):
-            c2, _, pc = time_scan(key, max(5, args.steps // 3), 2, torch, ssm)
-            m2 = sum(pc) / len(pc)
-            extra[key] = {"ms": round(m2, 4), "GB/s": round(scan_alg_bytes(c2) / m2 / 1e6, 1),
-                          "Gelem/s": round(c2.elements / m2 / 1e6, 1)}
-        c5, pc5 = time_ssd(max(5, args.steps // 3), 2, torch, ssm)
-        m5 = sum(pc5) / len(pc5)
-        extra["S5"] = {"ms": round(m5, 4), "GB/s": round(ssd_alg_bytes(c5) / m5 / 1e6, 1),
-                       "TFLOP/s": round(ssd_alg_flops(c5) / m5 / 1e9, 1),
-                       "mfma_frac": round(ssd_alg_flops(c5) / m5 / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4)}
-        extra.update(time_next_rows(max(10, args.steps), 3, torch, ssm))
+        extra = time_next_rows(max(10, args.steps), 3, torch, ssm)
         extra["bwd_S2"] = time_bwd("S2", max(10, args.steps // 2), 2, torch, ssm)
         extra["bwd_S5"] = time_ssd_bwd(max(10, args.steps // 2), 2, torch, ssm)
         line["extra"] = extra
-        print(json.dumps(extra), file=sys.stderr)
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(args.config)
+    if want_cpu:
+        rec, ref = cpu_baseline(key, head_in)
+        line["cpu_baseline"] = rec
+        if want_parity:
+            line["parity"] = parity_of(head_out, ref)
+        del ref
+    elif want_parity:
+        log("%s: oracle for parity" % key)
+        line["parity"] = parity(key, head_out, head_in)
     print(json.dumps(line), flush=True)
+
+
+def ssd_fields(r5):
+    c5 = r5["cfg"]
+    m5, _, mn5 = summary(r5["per_call"])
+    tf = ssd_alg_flops(c5) / m5 / 1e9
+    return {"ms": round(m5, 5), "ms_min": round(mn5, 5),
+            "GB/s": round(ssd_alg_bytes(c5) / m5 / 1e6, 1),
+            "hbm_frac": round(ssd_alg_bytes(c5) / m5 / 1e6 / HBM_PEAK_GBS, 4),
+            "TFLOP/s": round(tf, 1), "mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
 
 
 if __name__ == "__main__":

@@ -23,6 +23,20 @@ bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 size_t esize(ssm_dtype t) { return t == SSM_BF16 ? 2 : 4; }
 
+// The dtype field as the int a C caller stored. A C enum object may hold any int;
+// loading a value outside ssm_dtype's range through the C++ enum type is undefined,
+// so the checks read the bits, and only checked values are read as ssm_dtype.
+static_assert(sizeof(ssm_dtype) == sizeof(int), "ssm_dtype is int-sized");
+int dtype_bits(const ssm_dtype &f) {
+    int v;
+    std::memcpy(&v, &f, sizeof v);
+    return v;
+}
+bool dtype_ok(const ssm_dtype &f) {
+    const int v = dtype_bits(f);
+    return v == SSM_F32 || v == SSM_BF16;
+}
+
 constexpr int64_t kMaxRowBytes = (int64_t)1 << 31;
 // A launch's threads along one grid dimension (blocks * block size) must fit 32 bits;
 // the element-wise kernels use one thread per element (up to 256 per block).
@@ -37,8 +51,8 @@ ssm_status check_scan_sizes(const ssm_scan_args *a) {
         return fail(SSM_EINVAL, "selective_scan: need batch >= 0, seqlen >= 0, dim > 0, dstate > 0 "
                     "(got %lld, %lld, %lld, %lld)", (long long)a->batch, (long long)a->seqlen,
                     (long long)a->dim, (long long)a->dstate);
-    if (a->dtype != SSM_F32 && a->dtype != SSM_BF16)
-        return fail(SSM_EINVAL, "selective_scan: unknown dtype %d", (int)a->dtype);
+    if (!dtype_ok(a->dtype))
+        return fail(SSM_EINVAL, "selective_scan: unknown dtype %d", dtype_bits(a->dtype));
     if (a->dstate != 16 && a->dstate != 32 && a->dstate != 64)
         return fail(SSM_ENOTSUP, "selective_scan: dstate %lld not supported (16, 32, 64)",
                     (long long)a->dstate);
@@ -87,8 +101,8 @@ ssm_status check_ssd_sizes(const ssm_ssd_args *a) {
         a->chunk <= 0)
         return fail(SSM_EINVAL, "ssd_chunked: need batch, seqlen >= 0 and nheads, headdim, "
                     "dstate, chunk > 0");
-    if (a->dtype != SSM_F32 && a->dtype != SSM_BF16)
-        return fail(SSM_EINVAL, "ssd_chunked: unknown dtype %d", (int)a->dtype);
+    if (!dtype_ok(a->dtype))
+        return fail(SSM_EINVAL, "ssd_chunked: unknown dtype %d", dtype_bits(a->dtype));
     if (a->dtype != SSM_BF16)
         return fail(SSM_ENOTSUP, "ssd_chunked: only bf16 storage is implemented (matrix cores)");
     if (a->headdim != 64)
@@ -143,7 +157,8 @@ ssm_status check_ssd(const ssm_ssd_args *a) {
 ssm_ssd_args ssd_sizes_of(const ssm_ssd_bwd_args *a) {
     ssm_ssd_args f{};
     f.batch = a->batch; f.seqlen = a->seqlen; f.nheads = a->nheads; f.headdim = a->headdim;
-    f.dstate = a->dstate; f.chunk = a->chunk; f.ngroups = a->ngroups; f.dtype = a->dtype;
+    f.dstate = a->dstate; f.chunk = a->chunk; f.ngroups = a->ngroups;
+    std::memcpy(&f.dtype, &a->dtype, sizeof f.dtype);   // checked by check_ssd_sizes
     return f;
 }
 
@@ -187,8 +202,8 @@ ssm_status check_step(const ssm_scan_step_args *a) {
     if (!a) return fail(SSM_EINVAL, "selective_state_update: args is NULL");
     if (a->batch < 0 || a->dim <= 0 || a->dstate <= 0)
         return fail(SSM_EINVAL, "selective_state_update: need batch >= 0, dim > 0, dstate > 0");
-    if (a->dtype != SSM_F32 && a->dtype != SSM_BF16)
-        return fail(SSM_EINVAL, "selective_state_update: unknown dtype %d", (int)a->dtype);
+    if (!dtype_ok(a->dtype))
+        return fail(SSM_EINVAL, "selective_state_update: unknown dtype %d", dtype_bits(a->dtype));
     if (!step_dstate_ok(a->dstate))
         return fail(SSM_ENOTSUP, "selective_state_update: dstate %lld not supported (16..256, power of 2)",
                     (long long)a->dstate);
@@ -218,8 +233,8 @@ ssm_status check_ssd_step(const ssm_ssd_step_args *a) {
     if (!a) return fail(SSM_EINVAL, "ssd_state_update: args is NULL");
     if (a->batch < 0 || a->nheads <= 0 || a->headdim <= 0 || a->dstate <= 0)
         return fail(SSM_EINVAL, "ssd_state_update: need batch >= 0 and nheads, headdim, dstate > 0");
-    if (a->dtype != SSM_F32 && a->dtype != SSM_BF16)
-        return fail(SSM_EINVAL, "ssd_state_update: unknown dtype %d", (int)a->dtype);
+    if (!dtype_ok(a->dtype))
+        return fail(SSM_EINVAL, "ssd_state_update: unknown dtype %d", dtype_bits(a->dtype));
     if (!step_dstate_ok(a->dstate))
         return fail(SSM_ENOTSUP, "ssd_state_update: dstate %lld not supported (16..256, power of 2)",
                     (long long)a->dstate);
@@ -249,8 +264,8 @@ ssm_status check_conv(const ssm_conv_args *a) {
     if (!a) return fail(SSM_EINVAL, "causal_conv1d: args is NULL");
     if (a->batch < 0 || a->seqlen < 0 || a->dim <= 0 || a->width <= 0)
         return fail(SSM_EINVAL, "causal_conv1d: need batch, seqlen >= 0 and dim, width > 0");
-    if (a->dtype != SSM_F32 && a->dtype != SSM_BF16)
-        return fail(SSM_EINVAL, "causal_conv1d: unknown dtype %d", (int)a->dtype);
+    if (!dtype_ok(a->dtype))
+        return fail(SSM_EINVAL, "causal_conv1d: unknown dtype %d", dtype_bits(a->dtype));
     if (a->width < 2 || a->width > 4)
         return fail(SSM_ENOTSUP, "causal_conv1d: width %lld not supported (2, 3, 4)", (long long)a->width);
     if (a->batch > 65535 || a->dim > (1 << 30) || a->seqlen >= ((int64_t)1 << 31))
@@ -274,7 +289,8 @@ ssm_status check_bwd_sizes(const ssm_scan_bwd_args *a) {
     if (!a) return fail(SSM_EINVAL, "selective_scan_bwd: args is NULL");
     ssm_scan_args f{};
     f.batch = a->batch; f.seqlen = a->seqlen; f.dim = a->dim; f.dstate = a->dstate;
-    f.ngroups = a->ngroups; f.dtype = a->dtype;
+    f.ngroups = a->ngroups;
+    std::memcpy(&f.dtype, &a->dtype, sizeof f.dtype);   // checked by check_scan_sizes
     const ssm_status st = check_scan_sizes(&f);
     if (st != SSM_OK) return st;
     // chunks of 64 steps index the second grid dimension of the chunk kernels

@@ -8,6 +8,13 @@
 
 namespace ssm {
 
+// Steps per chunk of the scan gradients (a chunk's states live in VGPRs).
+constexpr int kScanBwdChunk = 64;
+// Heads per workgroup of the SSD-gradient column kernel (a dx accumulator each)
+// and row kernel.
+constexpr int kSsdBwdHeadsCol = 2;
+constexpr int kSsdBwdHeadsRow = 4;
+
 // How one selective-scan call is split along time.
 //   chunks     : number of time chunks G (1 = no split)
 //   chunk_len  : steps per chunk (the last one may be shorter)
@@ -36,6 +43,8 @@ struct SSDPlan {
 };
 
 SSDPlan ssd_plan(const ssm_ssd_args &a);
+// fp32 [B][H][P][N] after the decays: the last chunk's state (it feeds h_final only)
+size_t ssd_last_state_offset(const ssm_ssd_args &a, const SSDPlan &pl);
 ssm_status ssd_launch(const ssm_ssd_args &a, const SSDPlan &plan, hipStream_t stream,
                       char *err, size_t errlen);
 
@@ -54,7 +63,7 @@ struct SSDBwdPlan {
     size_t decay_offset;      // fp32 [B][H][nc]
     size_t hfin_offset;       // fp32 [B][H][P][N]: final state of the recompute
     size_t gout_offset;       // fp32 [B][nc][H][P][N]: adjoint aggregates, then adjoint at chunk ends
-    size_t kc_offset;         // fp32 [B][H][nc]: <adjoint, state> at each chunk end
+    size_t kc_offset;         // fp32 [B][H][nc][P N / 256]: per-wave shares of <adjoint, state> at each chunk end
     size_t y32_offset;        // fp32 (B, L, H, P): pre-gate output (only with z)
     size_t dych_offset;       // bf16 (B, L, H, P): dy silu(z), hi part (only with z)
     size_t dycl_offset;       // bf16 (B, L, H, P): lo part (only with z)

@@ -32,7 +32,7 @@
 namespace ssm {
 namespace {
 
-constexpr int kChunk = 64;   // steps per chunk (states of a chunk live in VGPRs)
+constexpr int kChunk = kScanBwdChunk;   // steps per chunk (states of a chunk live in VGPRs)
 constexpr int kWaves = 8;    // waves per workgroup of the main kernel
 
 struct BwdK {
@@ -577,23 +577,6 @@ void launch_bwd(const BwdK &k, hipStream_t s) {
 }
 
 }  // namespace
-
-ScanBwdPlan scan_bwd_plan(const ssm_scan_bwd_args &a) {
-    ScanBwdPlan pl{};
-    if (a.batch <= 0 || a.seqlen <= 0 || a.dim <= 0) return pl;
-    auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
-    const int64_t N = a.dstate;
-    pl.chunks = (a.seqlen + kChunk - 1) / kChunk;
-    const size_t chains = (size_t)a.batch * ((a.dim + 63) / 64);
-    pl.aggF_offset = 0;
-    pl.aggR_offset = up(chains * pl.chunks * (N + 1) * 64 * sizeof(float));
-    pl.hin_offset = pl.aggR_offset + up(chains * pl.chunks * N * 64 * sizeof(float));
-    const size_t st = (size_t)a.batch * pl.chunks * a.dim * N * sizeof(float);
-    pl.uin_offset = pl.hin_offset + up(st);
-    pl.dApart_offset = pl.uin_offset + up(st);
-    pl.bytes = pl.dApart_offset + up(st);
-    return pl;
-}
 
 ssm_status scan_bwd_launch(const ssm_scan_bwd_args &a, const ScanBwdPlan &plan, hipStream_t s, char *err,
                            size_t errlen) {

@@ -497,36 +497,6 @@ ssm_status launch_typed(const ScanK &k, hipStream_t s, int passes) {
 
 }  // namespace
 
-ScanPlan scan_plan(const ssm_scan_args &a) {
-    ScanPlan pl{};
-    pl.chunks = 1;
-    pl.chunk_len = a.seqlen;
-    if (a.seqlen <= 0 || a.batch <= 0 || a.dim <= 0) return pl;
-    // One wave per (b, 64 channels, chunk). Aim at ~4096 waves: four per SIMD on
-    // the 1024 SIMDs, all resident at once (the main pass fits four per SIMD),
-    // which balances the SIMDs and hides memory latency (never more than 4096, so
-    // no SIMD gets a fifth wave to run after the others); chunks stay >= 32 steps.
-    const int64_t waves = a.batch * ((a.dim + 63) / 64);
-    int64_t G = std::max<int64_t>(1, 4096 / waves);
-    G = std::min<int64_t>(G, std::max<int64_t>(1, a.seqlen / 32));
-    if (const char *env = std::getenv("SSM_SCAN_CHUNKS")) {  // tuning override
-        const long v = std::strtol(env, nullptr, 10);
-        if (v > 0) G = v;
-    }
-    G = std::max<int64_t>(1, std::min<int64_t>(G, std::min<int64_t>(a.seqlen, 65535)));
-    pl.chunk_len = (a.seqlen + G - 1) / G;
-    if (G > 1) pl.chunk_len = (pl.chunk_len + 3) / 4 * 4;
-    pl.chunks = (a.seqlen + pl.chunk_len - 1) / pl.chunk_len;
-    if (pl.chunks > 1) {
-        auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
-        const size_t chains = (size_t)a.batch * ((a.dim + 63) / 64);
-        const size_t G = (size_t)pl.chunks;
-        pl.agg_offset = 0;
-        pl.bytes = up(chains * (G - 1) * (a.dstate + 1) * 64 * sizeof(float));
-    }
-    return pl;
-}
-
 ssm_status scan_launch(const ssm_scan_args &a, const ScanPlan &plan, hipStream_t s, int passes,
                        char *err, size_t errlen) {
     if (a.batch == 0) return SSM_OK;

@@ -47,8 +47,8 @@
 namespace ssm {
 namespace {
 
-constexpr int kHsCol = 2;   // heads per workgroup, column kernel (a dx accumulator each)
-constexpr int kHsRow = 4;   // heads per workgroup, row kernel
+constexpr int kHsCol = kSsdBwdHeadsCol;
+constexpr int kHsRow = kSsdBwdHeadsRow;
 
 struct BwdK {
     SSDK f;
@@ -57,10 +57,11 @@ struct BwdK {
     const float *dh_final;
     uint16_t *dx, *ddt, *dz;
     float *dA, *dD, *dbias, *dh0;
-    float *sin32, *gout, *hfin, *kc;
+    float *sin32, *gout, *hfin, *kc;   // kc: [B][H][nc][kcw] per-wave shares of <Gout, S_end>
     float *q, *dtdd, *dd;
     float *dBp, *dCp, *dB, *dC;
     int32_t nsl_col, nsl_row, batch;
+    int32_t kcw;                       // waves per (b, h) in the reverse state pass: N / 4
 };
 
 typedef __attribute__((ext_vector_type(2))) float f32x2;
@@ -228,7 +229,9 @@ __global__ __launch_bounds__(256) void ssd_bwd_gate_kernel(const BwdK k, int64_t
 // One thread per (b, h, p, 4 n): the adjoint of the state entering chunk c is
 // Lam_c = R_c + decay_c Lam_{c+1} (Lam_nc = dh_final); Gout_c = Lam_{c+1} replaces
 // R_c in place, and <Gout_c, S_end,c> (S_end,c = Sin_{c+1}, or the final state)
-// is summed per (b, h, c) with one atomic per wave.
+// is summed per wave and stored as that wave's share (no atomics: the finish
+// kernel adds the kcw shares of a (b, h, c) in a fixed order, so d dt does not
+// depend on the order in which waves run).
 __global__ __launch_bounds__(256) void ssd_bwd_state_pass_kernel(const BwdK k, int N, int64_t total) {
     constexpr int K = 4;
     const SSDK &p = k.f;
@@ -239,6 +242,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_state_pass_kernel(const BwdK k, i
     const int64_t pn = (i % per_bh) * 4;
     const int64_t b = bh / p.H, h = bh % p.H;
     const int64_t hidx = bh * kP * N + pn;
+    const int64_t wslot = (i % per_bh) >> 6;   // this wave's share index within (b, h)
     f32x4 lam = f32x4{0.f, 0.f, 0.f, 0.f};
     if (k.dh_final) {
 #pragma unroll
@@ -265,7 +269,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_state_pass_kernel(const BwdK k, i
                 *(f32x4 *)(k.gout + base + c * cstride) = lam;
                 float part = lam[0] * se[u][0] + lam[1] * se[u][1] + lam[2] * se[u][2] + lam[3] * se[u][3];
                 part = wave_sum(part);
-                if ((threadIdx.x & 63) == 0) atomicAdd(k.kc + bh * p.nc + c, part);
+                if ((threadIdx.x & 63) == 0) k.kc[(bh * p.nc + c) * k.kcw + wslot] = part;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) lam[e] = fmaf(dc[u], lam[e], rc[u][e]);
             }
@@ -860,7 +864,10 @@ __global__ __launch_bounds__(Q) void ssd_bwd_finish_kernel(const BwdK k) {
     if (lane == 0) wt[wv] = v;
     __syncthreads();
     for (int w2 = wv + 1; w2 < Q / 64; ++w2) v += wt[w2];
-    const float da = v + k.kc[((int64_t)b * p.H + h) * p.nc + c];
+    float kcs = 0.0f;                           // <Gout, S_end>: shares in a fixed order
+    const float *kcp = k.kc + (((int64_t)b * p.H + h) * p.nc + c) * k.kcw;
+    for (int w2 = 0; w2 < k.kcw; ++w2) kcs += kcp[w2];
+    const float da = v + kcs;
     float dtv = 0.0f, dr = 0.0f;
     if (ok) {
         const float raw = to_f32(p.dt[o]) + (p.dt_bias ? p.dt_bias[h] : 0.0f);
@@ -923,42 +930,6 @@ void zero(float *a, int64_t n, hipStream_t s) {
 
 }  // namespace
 
-SSDBwdPlan ssd_bwd_plan(const ssm_ssd_bwd_args &a) {
-    SSDBwdPlan pl{};
-    if (a.batch <= 0 || a.seqlen <= 0 || a.chunk <= 0) return pl;
-    auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
-    const int64_t G = a.ngroups > 1 ? a.ngroups : 1;
-    const int64_t hpg = a.nheads / G;
-    pl.nchunks = (a.seqlen + a.chunk - 1) / a.chunk;
-    pl.hs_col = kHsCol;
-    pl.hs_row = kHsRow;
-    pl.slices_col = (hpg + kHsCol - 1) / kHsCol;
-    pl.slices_row = (hpg + kHsRow - 1) / kHsRow;
-    const size_t st = (size_t)a.batch * pl.nchunks * a.nheads * a.headdim * a.dstate;
-    const size_t blhp = (size_t)a.batch * a.seqlen * a.nheads * a.headdim;
-    const size_t blh = (size_t)a.batch * a.seqlen * a.nheads;
-    const size_t bln = (size_t)a.batch * a.seqlen * G * a.dstate;
-    size_t off = 0;
-    auto take = [&](size_t bytes) { const size_t o = off; off += up(bytes); return o; };
-    pl.sin32_offset = take(st * 4);
-    pl.sin_offset = take(st * 2);
-    pl.decay_offset = take((size_t)a.batch * a.nheads * pl.nchunks * 4);
-    pl.hfin_offset = take((size_t)a.batch * a.nheads * a.headdim * a.dstate * 4);
-    pl.gout_offset = take(st * 4);
-    pl.kc_offset = take((size_t)a.batch * a.nheads * pl.nchunks * 4);
-    const bool z = a.z != nullptr;
-    pl.y32_offset = take(z ? blhp * 4 : 0);
-    pl.dych_offset = take(z ? blhp * 2 : 0);
-    pl.dycl_offset = take(z ? blhp * 2 : 0);
-    pl.q_offset = take(blh * 4);
-    pl.dtdd_offset = take(blh * 4);
-    pl.dd_offset = take(blh * 4);
-    pl.dBp_offset = take((size_t)pl.slices_col * bln * 4);
-    pl.dCp_offset = take((size_t)pl.slices_row * bln * 4);
-    pl.bytes = off;
-    return pl;
-}
-
 ssm_status ssd_bwd_launch(const ssm_ssd_bwd_args &a, const SSDBwdPlan &plan, hipStream_t s, char *err,
                           size_t errlen) {
     if (a.batch == 0) return SSM_OK;
@@ -1014,11 +985,11 @@ ssm_status ssd_bwd_launch(const ssm_ssd_bwd_args &a, const SSDBwdPlan &plan, hip
         k.nsl_col = (int32_t)plan.slices_col;
         k.nsl_row = (int32_t)plan.slices_row;
         k.batch = (int32_t)a.batch;
+        k.kcw = (int32_t)(a.headdim * a.dstate / 256);   // (P N / 4) threads per (b, h) / 64
 
         zero(a.dA, a.nheads, s);
         zero(a.dDskip, a.nheads, s);
         zero(a.ddt_bias, a.nheads, s);
-        zero(k.kc, a.batch * a.nheads * plan.nchunks, s);
         // forward recompute: chunk states (split), entering states, final state
         ssd_recompute_launch(f, (int)a.batch, Q, N, 0, s);
         if (a.z) ssd_recompute_launch(f, (int)a.batch, Q, N, 1, s);   // fp32 pre-gate output

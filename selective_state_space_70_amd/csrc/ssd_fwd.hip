@@ -789,24 +789,6 @@ void ssd_recompute_launch(const SSDK &k, int batch, int Q, int N, int what, hipS
     else recompute_n<128>(k, batch, Q, what, s);
 }
 
-// fp32 [B][H][P][N] after the decays: the last chunk's state (it feeds h_final only)
-static size_t last_state_offset(const ssm_ssd_args &a, const SSDPlan &pl) {
-    return pl.decay_offset + (((size_t)a.batch * a.nheads * pl.nchunks * sizeof(float) + 255) & ~(size_t)255);
-}
-
-SSDPlan ssd_plan(const ssm_ssd_args &a) {
-    SSDPlan pl{};
-    if (a.batch <= 0 || a.seqlen <= 0 || a.chunk <= 0) return pl;
-    auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
-    pl.nchunks = (a.seqlen + a.chunk - 1) / a.chunk;
-    const size_t elems = (size_t)a.batch * pl.nchunks * a.nheads * a.dstate * a.headdim;
-    pl.states_offset = 0;
-    pl.sin_offset = up(elems * sizeof(uint16_t));     // bf16 chunk states first
-    pl.decay_offset = pl.sin_offset + up(elems * sizeof(uint16_t));
-    pl.bytes = last_state_offset(a, pl) + up((size_t)a.batch * a.nheads * a.headdim * a.dstate * sizeof(float));
-    return pl;
-}
-
 ssm_status ssd_launch(const ssm_ssd_args &a, const SSDPlan &plan, hipStream_t s, char *err,
                       size_t errlen) {
     if (a.batch == 0) return SSM_OK;
@@ -824,7 +806,7 @@ ssm_status ssd_launch(const ssm_ssd_args &a, const SSDPlan &plan, hipStream_t s,
         k.dt_bias = a.dt_bias; k.A = a.A; k.Dskip = a.Dskip; k.h0 = a.h0;
         k.y = (uint16_t *)a.y; k.h_final = a.h_final;
         k.states16 = (uint16_t *)((char *)a.workspace + plan.states_offset);
-        k.states_last = (float *)((char *)a.workspace + last_state_offset(a, plan));
+        k.states_last = (float *)((char *)a.workspace + ssd_last_state_offset(a, plan));
         k.sin = (uint16_t *)((char *)a.workspace + plan.sin_offset);
         k.decay = (float *)((char *)a.workspace + plan.decay_offset);
         k.L = a.seqlen; k.H = (int32_t)a.nheads; k.nc = (int32_t)plan.nchunks;

@@ -61,5 +61,23 @@ def sample_channels(total, count, seed):
     return np.array(sorted(picks), dtype=np.int64)
 
 
+def rel_l2_blocked(u, v, rows=1 << 22):
+    """||u - v||_2 / ||v||_2 over the whole tensor in fp64, accumulated over
+    blocks of the flattened arrays (full-size outputs do not need fp64 copies
+    of the whole tensor)."""
+    u = np.asarray(u).reshape(-1)
+    v = np.asarray(v).reshape(-1)
+    assert u.shape == v.shape, (u.shape, v.shape)
+    num = den = 0.0
+    for i in range(0, u.size, rows):
+        a = u[i:i + rows].astype(np.float64)
+        b = v[i:i + rows].astype(np.float64)
+        num += float(np.dot(a - b, a - b))
+        den += float(np.dot(b, b))
+    if den == 0.0:
+        return 0.0 if num == 0.0 else float("inf")
+    return float(np.sqrt(num / den))
+
+
 def report(name, ey, eh):
     print("%s: rel_l2 y %.3e  state %.3e" % (name, ey, eh), flush=True)

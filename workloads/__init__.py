@@ -96,21 +96,26 @@ _STREAMS = ["x", "delta", "z", "B", "C", "Dskip", "dt0", "h0", "A"]
 
 
 def round_bf16(a: np.ndarray) -> np.ndarray:
-    """Round float32 values to bfloat16 (nearest, ties to even); return float32."""
-    return _bits_to_f32(bf16_bits(a))
+    """Round float32 values to bfloat16 (nearest, ties to even); return float32
+    holding the rounded values. NaNs stay NaN (quiet bit set)."""
+    src = np.ascontiguousarray(a, dtype=np.float32)
+    out = np.empty_like(src)
+    su = src.reshape(-1).view(np.uint32)
+    ou = out.reshape(-1).view(np.uint32)
+    block = 1 << 24            # bounded temporaries for large arrays
+    for i in range(0, su.size, block):
+        u = su[i:i + block]
+        # add half an ulp of bf16 (plus the kept lsb for ties); no overflow below NaN
+        r = u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+        nan = (u & np.uint32(0x7FFFFFFF)) > np.uint32(0x7F800000)
+        r = np.where(nan, u | np.uint32(0x00400000), r)
+        ou[i:i + block] = r & np.uint32(0xFFFF0000)
+    return out
 
 
 def bf16_bits(a: np.ndarray) -> np.ndarray:
     """bfloat16 bit patterns (uint16) of float32 values, round-to-nearest-even."""
-    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    nan = (u & 0x7FFFFFFF) > 0x7F800000
-    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    r = np.where(nan, (u >> 16) | 0x40, r)
-    return r.astype(np.uint16)
-
-
-def _bits_to_f32(bits: np.ndarray) -> np.ndarray:
-    return (bits.astype(np.uint32) << 16).view(np.float32)
+    return (round_bf16(a).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
 
 
 def _rngs(seed: int):
