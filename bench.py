@@ -117,7 +117,8 @@ def scan_source_hash() -> str:
     import hashlib
     h = hashlib.sha1()
     csrc = os.path.join(ROOT, "selective_state_space_70_amd", "csrc")
-    for name in ("scan_fwd.hip", "device_common.h", "chain.h", "internal.h"):
+    for name in ("scan_kernels.h", "scan_fwd.hip", "scan_fwd_n16.hip", "device_common.h", "chain.h",
+                 "internal.h"):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]

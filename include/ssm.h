@@ -138,13 +138,14 @@ ssm_status selective_scan_fwd(const ssm_scan_args *args, hipStream_t stream);
 /* The same computation in its two passes, for callers that time or schedule them
  * separately (or exchange chunk states between devices of a sequence-sharded
  * scan, where the state entering a shard is that shard's h0):
- *   selective_scan_chunk_states: the end state of every time chunk but the last,
- *     started from a zero state, plus its summed step, into `workspace`
- *     (nothing when the call is not split in time).
- *   selective_scan_apply: carries h0 through those chunk maps to get the state
- *     entering each chunk, then runs every chunk again with readout: writes y
+ *   selective_scan_chunk_states: the affine map of every time chunk but the last
+ *     (its end state from a zero state and its decay), then the composition of
+ *     those maps from the start of the sequence to each chunk, into `workspace`
+ *     (nothing when the call is not split in time). Independent of h0.
+ *   selective_scan_apply: applies each chunk's composed map to h0 to get the
+ *     state entering it, then runs every chunk again with readout: writes y
  *     and h_final. Needs the workspace filled by selective_scan_chunk_states with
- *     the same arguments (same sizes, inputs and workspace).
+ *     the same arguments (same sizes, inputs and workspace; h0 may differ).
  * selective_scan_fwd == selective_scan_chunk_states followed by selective_scan_apply.
  * Errors as for selective_scan_fwd. */
 ssm_status selective_scan_chunk_states(const ssm_scan_args *args, hipStream_t stream);

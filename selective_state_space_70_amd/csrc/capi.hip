@@ -334,7 +334,6 @@ ssm_status check_workspace(void *ws, size_t have, size_t need, const char *who) 
 
 }  // namespace
 
-
 extern "C" {
 
 ssm_status selective_scan_validate(const ssm_scan_args *a) {

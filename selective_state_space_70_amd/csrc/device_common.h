@@ -66,6 +66,13 @@ __device__ __forceinline__ void buf_store(rsrc_t r, uint32_t voff, uint32_t soff
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, (int)voff, (int)soff, 0);
 }
 
+// The same wave-uniform value, opaque to the optimiser (an empty asm statement
+// that claims to change it; no instruction is emitted).
+__device__ __forceinline__ uint32_t opaque_u32(uint32_t v) {
+    asm volatile("" : "+s"(v));
+    return v;
+}
+
 __device__ __forceinline__ float fast_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
 __device__ __forceinline__ float fast_log2(float v) { return __builtin_amdgcn_logf(v); }
 __device__ __forceinline__ float fast_rcp(float v) { return __builtin_amdgcn_rcpf(v); }
@@ -74,11 +81,13 @@ __device__ __forceinline__ float fast_rcp(float v) { return __builtin_amdgcn_rcp
 // log1p(u) for u in (0, 1] is taken as log(w) + (u - (w - 1)) with w = 1 + u:
 // the second term is the exact rounding error of 1 + u, so small steps keep
 // their full relative precision (a plain log(1 + e^v) loses it below ~1e-3).
+// max(v, 0) is taken as (v + |v|) / 2, exact, folded into the last FMA (fmaxf would
+// cost a NaN-quieting instruction on top of the max).
 __device__ __forceinline__ float softplus_f32(float v) {
     const float u = fast_exp2(-fabsf(v) * kLog2e);
     const float w = 1.0f + u;
     const float c = u - (w - 1.0f);
-    return fmaxf(v, 0.0f) + fmaf(fast_log2(w), kLn2, c);
+    return fmaf(v + fabsf(v), 0.5f, fmaf(fast_log2(w), kLn2, c));
 }
 
 // silu(z) = z / (1 + e^{-z}); for z -> -inf the reciprocal of +inf is 0.

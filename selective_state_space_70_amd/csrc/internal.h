@@ -18,12 +18,15 @@ constexpr int kSsdBwdHeadsRow = 4;
 // How one selective-scan call is split along time.
 //   chunks     : number of time chunks G (1 = no split)
 //   chunk_len  : steps per chunk (the last one may be shorter)
-// Workspace (when G > 1), per chain of 64 channels: aggregates[G-1][N+1][64]
-// (fp32 end state from a zero state, then the summed step).
+// Workspace (when G > 1), per chain of 64 channels, two fp32 blocks [G-1][N+1][64]:
+// the aggregates (each chunk's end state from a zero state, then its decay: the
+// product of its steps' exp(dt A[0]) on the fast path, its summed step otherwise)
+// and the prefixes (the composed map entering chunks 1..G-1, same layout).
 struct ScanPlan {
     int64_t chunks;
     int64_t chunk_len;
     size_t agg_offset;
+    size_t pre_offset;
     size_t bytes;
 };
 

@@ -33,8 +33,10 @@ ScanPlan scan_plan(const ssm_scan_args &a) {
         auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
         const size_t chains = (size_t)a.batch * ((a.dim + 63) / 64);
         const size_t G = (size_t)pl.chunks;
+        const size_t blocks = up(chains * (G - 1) * (a.dstate + 1) * 64 * sizeof(float));
         pl.agg_offset = 0;
-        pl.bytes = up(chains * (G - 1) * (a.dstate + 1) * 64 * sizeof(float));
+        pl.pre_offset = blocks;
+        pl.bytes = 2 * blocks;
     }
     return pl;
 }

@@ -89,10 +89,12 @@ def test_general_A_rows():
     _check("general A bf16", inp2)
 
 
-@pytest.mark.parametrize("chunks,L", [(2, 517), (5, 517), (17, 517), (100, 2000)])
+@pytest.mark.parametrize("chunks,L", [(2, 517), (5, 517), (17, 517), (100, 2000), (300, 2400)])
 def test_forced_time_chunks(monkeypatch, chunks, L):
-    """The time split (chunk aggregates, look-back hand-off, rerun) with a ragged
-    last chunk; 100 chunks of 24 steps exercise look-back past 64 predecessors."""
+    """The time split (chunk aggregates, their prefix, rerun) with a ragged last
+    chunk. The prefix pass cuts a chain's chunks into 8 segments: 2 chunks leave
+    seven segments empty, 100 chunks give segments of 13, 300 chunks (8 steps
+    each) segments of 38, walked in several register batches."""
     monkeypatch.setenv("SSM_SCAN_CHUNKS", str(chunks))
     inp = workloads.scan_inputs(2, L, 70, 16, "f32", seed=chunks, with_h0=True)
     _check("G=%d" % chunks, inp)
