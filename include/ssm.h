@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 5
+#define SSM_ABI_VERSION 6
 
 typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
 
@@ -159,6 +159,24 @@ ssm_status selective_scan_validate(const ssm_scan_args *args);
  * sizes, dtype or state size are invalid). Reads only batch, seqlen, dim, dstate
  * and dtype; the pointers may be NULL. Host-only. */
 size_t selective_scan_workspace_bytes(const ssm_scan_args *args);
+
+/* selective_scan_fwd without a caller workspace and without any allocation, for
+ * callers that cannot allocate device memory (code under graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc). Its scratch space is a fixed
+ * device array of SSM_NOALLOC_SCRATCH_BYTES inside the library, one copy per GPU,
+ * held until the process ends; args->workspace and args->workspace_bytes are
+ * ignored. Same arguments, results (bit for bit) and errors as
+ * selective_scan_fwd, plus SSM_ENOTSUP, before anything is enqueued, when the call
+ * needs more scratch than that (selective_scan_workspace_bytes(args) >
+ * SSM_NOALLOC_SCRATCH_BYTES; with N = 16 the library's own time split never
+ * needs more), and SSM_EHIP when the
+ * array's address cannot be obtained on the current device. Every call on one GPU
+ * uses that GPU's one array: calls that overlap in time on one GPU (other
+ * streams, other threads) race and must be serialised by the caller. No part of
+ * the array needs to start at zero: every value a call reads was written earlier
+ * in the same call. */
+#define SSM_NOALLOC_SCRATCH_BYTES ((size_t)40 << 20)
+ssm_status selective_scan_fwd_noalloc(const ssm_scan_args *args, hipStream_t stream);
 
 /*
  * Gradients of the selective scan (training) for the loss

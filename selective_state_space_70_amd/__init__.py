@@ -116,9 +116,12 @@ def selective_scan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm
     h_final (batch, D, N) fp32 or None).
 
     ``passes`` selects the C entry point: "all" (selective_scan_fwd),
-    "chunk_states" (selective_scan_chunk_states: fills ``workspace`` only) or
+    "chunk_states" (selective_scan_chunk_states: fills ``workspace`` only),
     "apply" (selective_scan_apply: needs the ``workspace`` a "chunk_states" call
-    with the same arguments filled)."""
+    with the same arguments filled) or "noalloc" (selective_scan_fwd_noalloc:
+    the library's fixed scratch array instead of a workspace; ``out`` and, with
+    ``return_final_state``, ``final_state_out`` must be given, so that nothing
+    is allocated, here or in the library)."""
     if x.dim() != 3 or A.dim() != 2:
         raise ValueError("x must be (batch, L, D) and A (D, N)")
     if x.dtype not in _DT:
@@ -138,6 +141,8 @@ def selective_scan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm
     _need(Dskip, "Dskip", (D,), torch.float32, dev)
     _need(delta_bias, "delta_bias", (D,), torch.float32, dev)
     _need(h0, "h0", (batch, D, N), torch.float32, dev)
+    if passes == "noalloc" and (out is None or (return_final_state and final_state_out is None)):
+        raise ValueError("passes='noalloc' allocates nothing: pass out (and final_state_out)")
     y = out if out is not None else torch.empty((batch, L, D), dtype=x.dtype, device=dev)
     _need(y, "out", (batch, L, D), x.dtype, dev)
     hf = None
@@ -150,7 +155,9 @@ def selective_scan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm
     _capi.check(L_.selective_scan_validate(ctypes.byref(a)))
     need = L_.selective_scan_workspace_bytes(ctypes.byref(a))
     entry = {"all": L_.selective_scan_fwd, "chunk_states": L_.selective_scan_chunk_states,
-             "apply": L_.selective_scan_apply}[passes]
+             "apply": L_.selective_scan_apply, "noalloc": L_.selective_scan_fwd_noalloc}[passes]
+    if passes == "noalloc":
+        need = 0                      # the library's own scratch array
     if need:
         if workspace is None or workspace.numel() * workspace.element_size() < need:
             if passes == "apply":

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libssm.so")
-SOURCES = ["capi.hip", "plan.cpp", "scan_fwd.hip", "scan_fwd_n16.hip", "scan_fwd_n32.hip", "scan_fwd_n64.hip", "scan_bwd.hip", "ssd_fwd.hip", "ssd_bwd.hip", "decode.hip", "conv1d.hip"]
+SOURCES = ["capi.hip", "plan.cpp", "scan_fwd.hip", "scan_fwd_n16.hip", "scan_fwd_n32.hip", "scan_fwd_n64.hip", "scan_bwd.hip", "ssd_fwd.hip", "ssd_bwd.hip", "decode.hip", "conv1d.hip", "noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -334,6 +334,16 @@ ssm_status check_workspace(void *ws, size_t have, size_t need, const char *who) 
 
 }  // namespace
 
+namespace ssm {
+ssm_status set_last_error(ssm_status s, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+}  // namespace ssm
+
 extern "C" {
 
 ssm_status selective_scan_validate(const ssm_scan_args *a) {

@@ -96,6 +96,9 @@ ScanBwdPlan scan_bwd_plan(const ssm_scan_bwd_args &a);
 ssm_status scan_bwd_launch(const ssm_scan_bwd_args &a, const ScanBwdPlan &plan, hipStream_t stream,
                            char *err, size_t errlen);
 
+// Set the thread's ssm_last_error() text (printf format); returns `s`.
+ssm_status set_last_error(ssm_status s, const char *fmt, ...);
+
 // Decode steps and the short convolution: no workspace, one kernel each.
 ssm_status step_launch(const ssm_scan_step_args &a, hipStream_t stream, char *err, size_t errlen);
 ssm_status ssd_step_launch(const ssm_ssd_step_args &a, hipStream_t stream, char *err, size_t errlen);

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_names():
     lib = _capi.lib()
-    assert lib.ssm_abi_version() == _capi.ABI_VERSION == 5
+    assert lib.ssm_abi_version() == _capi.ABI_VERSION == 6
     names = [lib.ssm_status_str(s).decode() for s in range(4)]
     assert names == ["SSM_OK", "SSM_EINVAL", "SSM_ENOTSUP", "SSM_EHIP"]
     assert lib.ssm_status_str(99).decode() == "SSM_UNKNOWN"
@@ -160,6 +160,23 @@ def test_fwd_rejects_before_any_hip_call():
     assert lib.ssd_chunked_fwd(ctypes.byref(s), None) == _capi.SSM_EINVAL
     # batch == 0 is a no-op that returns before touching HIP
     assert lib.selective_scan_fwd(ctypes.byref(scan_args(batch=0)), None) == _capi.SSM_OK
+
+
+def test_noalloc_checks_on_the_host():
+    """selective_scan_fwd_noalloc: invalid arguments and calls that need more than
+    its fixed scratch array are refused before any HIP call; with N = 16 even the
+    largest split fits the array."""
+    lib = _capi.lib()
+    assert lib.selective_scan_fwd_noalloc(None, None) == _capi.SSM_EINVAL
+    assert lib.selective_scan_fwd_noalloc(ctypes.byref(scan_args(x=None)), None) == _capi.SSM_EINVAL
+    big = scan_args(batch=1, seqlen=131072, dim=256, dstate=64)
+    need = lib.selective_scan_workspace_bytes(ctypes.byref(big))
+    assert need > _capi.NOALLOC_SCRATCH_BYTES
+    assert lib.selective_scan_fwd_noalloc(ctypes.byref(big), None) == _capi.SSM_ENOTSUP
+    assert "scratch" in lib.ssm_last_error().decode()
+    for b, L, D in ((1, 131072, 64), (1, 131072, 2048), (8, 2048, 1536), (4, 8192, 5120), (3, 100000, 128)):
+        a = scan_args(batch=b, seqlen=L, dim=D, dstate=16)
+        assert lib.selective_scan_workspace_bytes(ctypes.byref(a)) <= _capi.NOALLOC_SCRATCH_BYTES
 
 
 def test_workspace_sizes():
