@@ -53,7 +53,12 @@ ALU_PEAK_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12   # non-packed fp32 VALU issue slo
 # WRITE_SIZE runs (KiB per dispatch) scaled by what the same counters read for a
 # plain 256 MiB device copy (FETCH x2.0, WRITE x1.0). "valu": SQ_INSTS_VALU per
 # dispatch (wave instructions; 64 lane slots each).
-COUNTERS = {}
+COUNTERS = {
+    # long-context scan, apply kernel: FETCH_SIZE 864125 KiB, WRITE_SIZE 524416 KiB
+    # per dispatch (12 dispatches), copy calibration FETCH x2.0 (131085 KiB read for
+    # a 256 MiB copy), WRITE x1.0; SQ_INSTS_VALU 3.688e8 per dispatch
+    ("S4", "e7d9a443c7ad4fb5"): {"traffic": 864125 * 1024 * 2 + 524416 * 1024, "valu": 368799000},
+}
 METRIC = "scan effective HBM GB/s (% of peak) + Gelem/s over B·L·D·N"
 
 
@@ -114,13 +119,18 @@ def _device_inputs(inp, torch, dev):
 
 
 def scan_source_hash() -> str:
+    """Hash of what decides the scan kernels' work: their sources and the host
+    function that splits a call along time."""
     import hashlib
     h = hashlib.sha1()
     csrc = os.path.join(ROOT, "selective_state_space_70_amd", "csrc")
-    for name in ("scan_kernels.h", "scan_fwd.hip", "scan_fwd_n16.hip", "device_common.h", "chain.h",
-                 "internal.h"):
+    for name in ("scan_kernels.h", "scan_fwd.hip", "scan_fwd_n16.hip", "device_common.h", "chain.h"):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
+    with open(os.path.join(csrc, "plan.cpp")) as f:
+        text = f.read()
+    a = text.index("ScanPlan scan_plan(")
+    h.update(text[a:text.index("\n}\n", a)].encode())
     return h.hexdigest()[:16]
 
 
