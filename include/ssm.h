@@ -245,7 +245,7 @@ size_t ssd_chunked_workspace_bytes(const ssm_ssd_args *args);
  * Computed chunk by chunk on the matrix cores (dx, dB, dC, the adjoint states);
  * the decay gradients come from fp32 sums of the chunk's (t, s) terms.
  * Forward inputs exactly as ssm_ssd_args (dtype BF16, P == 64, chunk in {64, 128,
- * 256}; N in {64, 128}). dy: (batch, L, H, P) bf16. dh_final: (batch, H, P, N) fp32,
+ * 256}; N in {64, 128, 256}). dy: (batch, L, H, P) bf16. dh_final: (batch, H, P, N) fp32,
  * nullable (0). Outputs, all written in full:
  *   dx: (batch, L, H, P) bf16; ddt: (batch, L, H) bf16 (gradient of the raw dt);
  *   dz: (batch, L, H, P) bf16, required iff z != NULL; dB, dC: (batch, L, G, N) fp32;

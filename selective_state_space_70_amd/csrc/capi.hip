@@ -167,8 +167,7 @@ ssm_status check_ssd_bwd_sizes(const ssm_ssd_bwd_args *a) {
     const ssm_ssd_args f = ssd_sizes_of(a);
     const ssm_status st = check_ssd_sizes(&f);
     if (st != SSM_OK) return st;
-    if (a->dstate != 64 && a->dstate != 128)
-        return fail(SSM_ENOTSUP, "ssd_chunked_bwd: dstate %lld not supported (64, 128)", (long long)a->dstate);
+
     // dB and dC partial sums are reduced one thread per element
     if (a->batch * a->seqlen * groups(a->ngroups) * a->dstate > kMaxLaunchThreads)
         return fail(SSM_ENOTSUP, "ssd_chunked_bwd: batch*seqlen*ngroups*dstate must be < 2^32");

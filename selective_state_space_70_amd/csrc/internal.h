@@ -53,7 +53,7 @@ ssm_status ssd_launch(const ssm_ssd_args &a, const SSDPlan &plan, hipStream_t st
 
 // Pieces of the SSD forward the gradient pass reruns (what: 0 = split-precision
 // chunk states and the entering states, 1 = fp32 pre-gate output, 2 = adjoint
-// aggregates with exp(cs_t) weights). N in {64, 128}.
+// aggregates with exp(cs_t) weights). N in {64, 128, 256}.
 struct SSDK;
 void ssd_recompute_launch(const SSDK &k, int batch, int Q, int N, int what, hipStream_t s);
 

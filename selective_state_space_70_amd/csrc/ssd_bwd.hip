@@ -289,8 +289,9 @@ __global__ __launch_bounds__(256) void ssd_bwd_state_pass_kernel(const BwdK k, i
 // (x_s.dyc_t) gives W (summed over s into q) and, weighted, the A operand of
 // dC += M3 B. Then per head the entering-state term exp(cs_t) dyc_t Sin (split
 // operands) adds to dC and, dotted with C_t, to q.
+// (At N = 256 one workgroup per CU: its LDS blocks take 113 KB.)
 template <int N, int Q, bool SPLIT>
-__global__ __launch_bounds__(kThreads, 2) void ssd_bwd_row_kernel(const BwdK k) {
+__global__ __launch_bounds__(kThreads, N > 128 ? 1 : 2) void ssd_bwd_row_kernel(const BwdK k) {
     constexpr int HS = kHsRow;
     constexpr int TBS = Q / 64, KN = N / 32, NT = N / 16;
     constexpr int LDB = N + 8, LDT = 64 + 8, LDX = kP + 8;
@@ -536,8 +537,9 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_bwd_row_kernel(const BwdK k) 
 // weighted, the A operands of dx += M1 dyc and dB += M2 C. Then per head the
 // chunk-end terms e_s B_s Gout and e_s x_s Gout (split Gout) complete dx, dd, dtdd
 // and dB.
+// (At N = 256 one workgroup per CU: its LDS blocks take 146 KB.)
 template <int N, int Q, bool SPLIT>
-__global__ __launch_bounds__(kThreads, 2) void ssd_bwd_col_kernel(const BwdK k) {
+__global__ __launch_bounds__(kThreads, N > 128 ? 1 : 2) void ssd_bwd_col_kernel(const BwdK k) {
     constexpr int HS = kHsCol;
     constexpr int TBS = Q / 64, KN = N / 32, NT = N / 16;
     constexpr int LDB = N + 8, LDT = 64 + 8, LDX = kP + 8, LDO = kP + 4;
@@ -1015,7 +1017,8 @@ ssm_status ssd_bwd_launch(const ssm_ssd_bwd_args &a, const SSDBwdPlan &plan, hip
         const int nrow = (int)(a.batch * plan.nchunks * G * plan.slices_row * tbs);
         const int ncol = (int)(a.batch * plan.nchunks * G * plan.slices_col * tbs);
         if (N == 64) launch_main_n<64>(k, Q, a.z != nullptr, nrow, ncol, s);
-        else launch_main_n<128>(k, Q, a.z != nullptr, nrow, ncol, s);
+        else if (N == 128) launch_main_n<128>(k, Q, a.z != nullptr, nrow, ncol, s);
+        else launch_main_n<256>(k, Q, a.z != nullptr, nrow, ncol, s);
         const int64_t bln = a.batch * a.seqlen * G * a.dstate;
         hipLaunchKernelGGL(ssd_bwd_reduce_kernel, dim3((unsigned)((bln / 4 + 255) / 256)), dim3(256), 0, s,
                            (const float *)k.dBp, (int)plan.slices_col, bln, a.dB);

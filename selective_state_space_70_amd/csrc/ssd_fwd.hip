@@ -786,7 +786,8 @@ void recompute_n(const SSDK &k, int batch, int Q, int what, hipStream_t s) {
 
 void ssd_recompute_launch(const SSDK &k, int batch, int Q, int N, int what, hipStream_t s) {
     if (N == 64) recompute_n<64>(k, batch, Q, what, s);
-    else recompute_n<128>(k, batch, Q, what, s);
+    else if (N == 128) recompute_n<128>(k, batch, Q, what, s);
+    else recompute_n<256>(k, batch, Q, what, s);
 }
 
 ssm_status ssd_launch(const ssm_ssd_args &a, const SSDPlan &plan, hipStream_t s, char *err,

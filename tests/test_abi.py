@@ -349,7 +349,7 @@ def ssd_bwd_args(**kw):
     ({"dz": None}, _capi.SSM_EINVAL),                     # z given, dz missing
     ({"dB": FAKE + 4}, _capi.SSM_EINVAL),                 # fp32 outputs are written as 16-byte vectors
     ({"dx": FAKE + 2}, _capi.SSM_EINVAL),
-    ({"dstate": 256}, _capi.SSM_ENOTSUP),
+    ({"dstate": 32}, _capi.SSM_ENOTSUP),
     ({"headdim": 32}, _capi.SSM_ENOTSUP),
     ({"chunk": 100}, _capi.SSM_ENOTSUP),
     ({"dtype": _capi.SSM_F32}, _capi.SSM_ENOTSUP),
@@ -371,7 +371,10 @@ def test_ssd_bwd_workspace():
     assert need >= st * 8 + 2 * 8192 * 64 * 64 * 8
     a.z = None
     assert lib.ssd_chunked_bwd_workspace_bytes(ctypes.byref(a)) < need
-    assert lib.ssd_chunked_bwd_workspace_bytes(ctypes.byref(ssd_bwd_args(dstate=256))) == 0
+    # N = 256: the state buffers double
+    assert lib.ssd_chunked_bwd_workspace_bytes(ctypes.byref(ssd_bwd_args(batch=2, seqlen=8192, nheads=64,
+                                                                          dstate=256))) >= 2 * st * 8
+    assert lib.ssd_chunked_bwd_workspace_bytes(ctypes.byref(ssd_bwd_args(dstate=32))) == 0
 
 
 def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):

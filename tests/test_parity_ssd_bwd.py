@@ -74,9 +74,17 @@ def test_lengths_and_chunks(L, chunk):
     _check("L=%d Q=%d" % (L, chunk), _case(2, L, 4, 128, seed=L + chunk), chunk)
 
 
-@pytest.mark.parametrize("N", [64, 128])
+@pytest.mark.parametrize("N", [64, 128, 256])
 def test_state_sizes(N):
     _check("N=%d" % N, _case(2, 200, 4, N, seed=N), 128)
+
+
+@pytest.mark.parametrize("chunk", [64, 128, 256])
+def test_large_state_gate_h0(chunk):
+    """N = 256 (the largest state the pages name for Mamba-2) at every chunk
+    length, with the gate, an initial state and a final-state gradient, an odd
+    head count and a ragged last chunk."""
+    _check("N=256 z h0 Q=%d" % chunk, _case(2, 333, 5, 256, seed=256 + chunk, z=True), chunk)
 
 
 @pytest.mark.parametrize("N,H", [(128, 4), (64, 5)])
