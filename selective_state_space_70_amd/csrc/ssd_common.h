@@ -48,6 +48,11 @@ __device__ __forceinline__ u32x4 load16(rsrc_t r, uint32_t voff) {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
 }
 
+// the same with a wave-uniform part of the offset in the instruction's scalar offset
+__device__ __forceinline__ u32x4 load16s(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) { return pack_bf16x2(lo, hi); }
 
 // (lo halves of a, b) and (hi halves of a, b) as packed bf16 pairs.
@@ -84,6 +89,7 @@ struct SSDK {
     float *sin32;       // optional fp32 copy of the entering states (may alias states)
     float *y32;         // fp32 pre-gate output (B, L, H, P) of the recompute variant
     const uint16_t *xlo;   // optional bf16 lo part of x (adjoint aggregates: dyc = hi + lo)
+    float *gsc;         // fp32 score blocks C B^T per (batch, chunk, group) (forward, N <= 128)
     int64_t L;
     int32_t H;
     int32_t nc;
@@ -92,26 +98,30 @@ struct SSDK {
     int32_t hpg;        // heads per group
 };
 
-// dt and the inclusive in-chunk cumulative log-decay A*dt for the steps of chunk
-// c of head h; lane l owns steps l*SPL .. l*SPL+SPL-1 (SPL = Q/64). Steps past the
-// sequence get dt = 0. Returns the chunk total (the last cs) to every lane.
+// The raw dt of chunk c of head h, as head_dt_cs reads it (steps clamped to the
+// sequence): lane l gets steps l*SPL .. l*SPL+SPL-1.
 template <int Q>
-__device__ __forceinline__ float head_dt_cs(const SSDK &p, int b, int h, int c, float (&dtv)[Q / 64],
-                                            float (&cs)[Q / 64]) {
+__device__ __forceinline__ void head_dt_raw(const SSDK &p, int b, int h, int c, float (&raw)[Q / 64]) {
     constexpr int SPL = Q / 64;
     const int lane = threadIdx.x & 63;
-    // All loads first and unconditional (steps clamped to the sequence, an absent bias
-    // read from A), so their latencies overlap: a load under a branch is waited for
-    // at the branch's end, one at a time.
-    const float *biasp = p.dt_bias ? p.dt_bias : p.A;
-    const float biasv = biasp[h], a = p.A[h];
-    const float bias = p.dt_bias ? biasv : 0.0f;
-    float raw[SPL];
 #pragma unroll
     for (int i = 0; i < SPL; ++i) {
         const int64_t tg = std::min<int64_t>((int64_t)c * Q + lane * SPL + i, p.L - 1);
         raw[i] = to_f32(p.dt[((int64_t)b * p.L + tg) * p.H + h]);
     }
+}
+
+// dt and the inclusive in-chunk cumulative log-decay A*dt from the raw dt of
+// head_dt_raw. Steps past the sequence get dt = 0. Returns the chunk total (the
+// last cs) to every lane.
+template <int Q>
+__device__ __forceinline__ float head_dt_cs_from(const SSDK &p, int h, int c, const float (&raw)[Q / 64],
+                                                 float (&dtv)[Q / 64], float (&cs)[Q / 64]) {
+    constexpr int SPL = Q / 64;
+    const int lane = threadIdx.x & 63;
+    const float *biasp = p.dt_bias ? p.dt_bias : p.A;   // unconditional loads (an absent bias reads A)
+    const float biasv = biasp[h], a = p.A[h];
+    const float bias = p.dt_bias ? biasv : 0.0f;
     float run = 0.0f;
 #pragma unroll
     for (int i = 0; i < SPL; ++i) {
@@ -133,6 +143,18 @@ __device__ __forceinline__ float head_dt_cs(const SSDK &p, int b, int h, int c, 
 #pragma unroll
     for (int i = 0; i < SPL; ++i) cs[i] += excl;
     return __shfl(incl, 63, 64);
+}
+
+// dt and the inclusive in-chunk cumulative log-decay A*dt for the steps of chunk
+// c of head h; lane l owns steps l*SPL .. l*SPL+SPL-1 (SPL = Q/64). All loads are
+// issued first (their latencies overlap: a load under a branch is waited for at
+// the branch's end, one at a time).
+template <int Q>
+__device__ __forceinline__ float head_dt_cs(const SSDK &p, int b, int h, int c, float (&dtv)[Q / 64],
+                                            float (&cs)[Q / 64]) {
+    float raw[Q / 64];
+    head_dt_raw<Q>(p, b, h, c, raw);
+    return head_dt_cs_from<Q>(p, h, c, raw, dtv, cs);
 }
 
 // position of chunk-local s (its block of 64 aside) in the permuted x rows

@@ -38,6 +38,7 @@
 
 #include "device_common.h"
 #include "internal.h"
+
 #include "ssd_common.h"
 
 namespace ssm {
@@ -720,6 +721,316 @@ void ssd_chunk_out_kernel(const SSDK p, int nhg, int64_t nq) {
     }
 }
 
+// ---------------------------------------------------------------- score blocks
+// G^T = B C^T of a chunk in 32 x 32 blocks (rows s of block sb, columns t of tile
+// tau, sb <= tau), on v_mfma_f32_32x32x16_bf16, kept in fp32 as the matrix cores
+// accumulate it. G depends on the group's B and C only, so it is formed once per
+// (batch, chunk, group) here and read by every head of the group.
+//
+// 32 x 32 fragments (lane l, c32 = l & 31, hf = l >> 5): A (32 x 16) row c32,
+// k = 8 hf + e; B (16 x 32) column c32, k = 8 hf + e; D (32 x 32, fp32) register v
+// holds row 8 (v >> 2) + 4 hf + (v & 3), column c32. A block is stored as 4 runs
+// of 256 floats, run i holding registers 4i .. 4i + 3 of lanes 0 .. 63 in order,
+// so that each of the 4 loads (and stores) of a lane's 16 values moves 1 KiB of
+// contiguous memory per wave. Block (tau, sb) of (batch, chunk, group) qg sits at
+// (qg NB + tau (tau + 1) / 2 + sb) 1024 floats, NB = Q/32 (Q/32 + 1) / 2. Tiles
+// with no step of the sequence are left out (and never read).
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+__device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8 &a, const bf16x8 &b, const f32x16 &c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int Q>
+constexpr int score_blocks() { return (Q / 32) * (Q / 32 + 1) / 2; }
+
+// one wave per (batch, chunk, group, tile tau)
+template <int N, int Q>
+__global__ __launch_bounds__(64) void ssd_score_kernel(const SSDK p, int64_t nq) {
+    constexpr int NT = Q / 32, NB = score_blocks<Q>(), KN = N / 16;
+    const int upc = p.G * NT;
+    const int id = blockIdx.x, k8 = id >> 3;
+    const int64_t q = (int64_t)(k8 / upc) * 8 + (id & 7);   // the tiles of a chunk share an XCD
+    if (q >= nq) return;
+    const int unit = k8 % upc;
+    const int gg = unit / NT, tau = unit % NT;
+    const int c = (int)(q % p.nc), b = (int)(q / p.nc);
+    const int lane = threadIdx.x, c32 = lane & 31, hf = lane >> 5;
+    const int64_t t_base = (int64_t)c * Q;
+    const int T = (int)std::min<int64_t>(Q, p.L - t_base);
+    if (32 * tau >= T) return;                                 // no step in this tile
+    const int GN = p.G * N;
+    const rsrc_t rC = make_rsrc_u(p.Cm + (((int64_t)b * p.L + t_base) * p.G + gg) * N, (uint32_t)(T * GN * 2));
+    const rsrc_t rB = make_rsrc_u(p.Bm + (((int64_t)b * p.L + t_base) * p.G + gg) * N, (uint32_t)(T * GN * 2));
+    bf16x8 cfr[KN], bfa[KN], bfb[KN];
+#pragma unroll
+    for (int kk = 0; kk < KN; ++kk)
+        cfr[kk] = as_bf16x8(load16(rC, (uint32_t)(((32 * tau + c32) * GN + 16 * kk + 8 * hf) * 2)));
+    auto load_b = [&](int sb, bf16x8 (&dst)[KN]) {
+#pragma unroll
+        for (int kk = 0; kk < KN; ++kk)
+            dst[kk] = as_bf16x8(load16(rB, (uint32_t)(((32 * sb + c32) * GN + 16 * kk + 8 * hf) * 2)));
+    };
+    float *out = p.gsc + ((q * p.G + gg) * NB + tau * (tau + 1) / 2) * 1024 + lane * 4;
+    auto block = [&](int sb, const bf16x8 (&bf)[KN]) {
+        f32x16 g = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < KN; ++kk) g = mfma32x32x16(bf[kk], cfr[kk], g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *(f32x4 *)(out + sb * 1024 + i * 256) = f32x4{g[4 * i], g[4 * i + 1], g[4 * i + 2], g[4 * i + 3]};
+    };
+    load_b(0, bfa);
+    for (int sb = 0;;) {
+        if (sb < tau) load_b(sb + 1, bfb);
+        block(sb, bfa);
+        if (++sb > tau) break;
+        if (sb < tau) load_b(sb + 1, bfa);
+        block(sb, bfb);
+        if (++sb > tau) break;
+    }
+}
+
+// ---------------------------------------------------------------- chunk output, one head
+// Per (batch, chunk, head): Q/64 waves; wave w owns the 32-row tiles w and
+// Q/32 - 1 - w of the chunk, whose causal work adds up to the same for every wave.
+// The head's x (transposed: the B operand of Y += M X) and entering state are
+// staged in LDS once; the score blocks come from the score kernel (L2), one block
+// ahead of their use. Two workgroups fit a CU, so one's loads overlap the other's
+// arithmetic.
+//
+// Decays as in the 16-row kernel, with r = 32 tau - 1 the step before a tile:
+// blocks of s before the tile take M = G o (w_s dt_s), w_s = exp(cs_r - cs_s)
+// from a table; their sum with the entering state (exp(cs_r) C Sin) is scaled by
+// a_t = exp(cs_t - cs_r) once; the tile's own block takes the exact
+// exp(cs_t - cs_s) dt_s [s <= t]. A D tile over (s, t) gives a lane the 16 values
+// s = 8g + 4hf + i of its t = c32, and registers 8kk .. 8kk + 7 are the A operand
+// (rows t, k = s) of a K-step over s = 16 kk .. 16 kk + 15 if position k = 8 hf + e
+// stands for s = 16 kk + 8 (e >> 2) + 4 hf + (e & 3): x is stored with bits 2 and
+// 3 of s swapped (pos_s32).
+__device__ __forceinline__ int pos_s32(int s) { return (s & ~12) | ((s & 4) << 1) | ((s & 8) >> 1); }
+
+template <int N, int Q>
+__global__ __launch_bounds__(Q, Q == 256 ? 3 : 1) void ssd_out_head_kernel(const SSDK p, int64_t nq) {
+    constexpr int NT = Q / 32;                // 32-row tiles
+    constexpr int NB = score_blocks<Q>();
+    constexpr int NTH = Q;                    // Q / 64 waves
+    constexpr int KN = N / 16;                // K-steps over the state dimension
+    constexpr int SPL = Q / 64;
+    constexpr int LDX = Q + 8;                // x^T rows (bf16), 16 bytes past a multiple of 128
+    constexpr int LDN = N + 8;                // Sin rows (bf16)
+    constexpr int RG = Q / 4;                 // 4-row groups of x
+    constexpr int XB = 8 * RG / NTH;          // 4-row x 8-p blocks of x per thread
+    constexpr int SV = kP * N / 8 / NTH;      // 16-byte vectors of Sin per thread
+    constexpr int SIN_BYTES = kP * LDN * 2;
+    constexpr int WTS_BYTES = NT * Q * 4;
+    static_assert(NT % 2 == 0 && (kP * N / 8) % NTH == 0 && (8 * RG) % NTH == 0, "staging split");
+    __shared__ __attribute__((aligned(16))) float cs2[Q];        // cs * log2(e)
+    __shared__ __attribute__((aligned(16))) float dts[Q];        // dt (0 past the end of the sequence)
+    __shared__ __attribute__((aligned(16))) uint16_t XT[kP][LDX];
+    // the entering state, then (once it is used) the decay table
+    __shared__ __attribute__((aligned(16))) uint8_t ubuf[SIN_BYTES > WTS_BYTES ? SIN_BYTES : WTS_BYTES];
+    uint16_t (*SinL)[LDN] = reinterpret_cast<uint16_t (*)[LDN]>(ubuf);
+    float (*wts)[Q] = reinterpret_cast<float (*)[Q]>(ubuf);      // tile tau: exp(cs_r - cs_s) dt_s, s < 32 tau
+
+    // block -> (chunk, head): q = 8 (k8 / H) + (id & 7), h = k8 % H, k8 = id >> 3; the
+    // heads of a chunk share an XCD (its B, C rows and score blocks in one L2)
+    const int id = blockIdx.x, k8 = id >> 3;
+    const int64_t q = (int64_t)(k8 / p.H) * 8 + (id & 7);
+    if (q >= nq) return;                                  // whole workgroup (uniform)
+    const int h = k8 % p.H, gg = h / p.hpg;
+    const int c = (int)(q % p.nc), b = (int)(q / p.nc);
+    const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c32 = lane & 31, hf = lane >> 5;
+    const int64_t t_base = (int64_t)c * Q;
+    const int T = (int)std::min<int64_t>(Q, p.L - t_base);
+    const int ta = wv, tb = NT - 1 - wv;                  // this wave's tiles (ta < tb)
+    const bool live_a = 32 * ta < T, live_b = 32 * tb < T;   // uniform
+    const int GN = p.G * N;
+    const int64_t xstride = (int64_t)p.H * kP;
+    // x^T row p holds position j at column j ^ (8 ((p >> 3) & 7)): the 8 rows that the
+    // 8 lanes of one x row write at once then start in different banks. For this lane's
+    // rows 32 pt + c32 that is j ^ xsw(pt).
+    auto xsw = [&](int pt) { return 32 * pt + (c32 & 24); };
+
+    // -- loads: x (4-row x 8-p blocks), the entering state, the C rows of both tiles
+    // (A operand of C Sin), dt. Rows past the sequence read as 0.
+    const rsrc_t rX = make_rsrc_u(p.x + ((int64_t)b * p.L + t_base) * xstride + h * kP, (uint32_t)(T * xstride * 2));
+    u32x4 xr[XB][4];
+#pragma unroll
+    for (int m = 0; m < XB; ++m) {
+        const int bi = tid + NTH * m;
+        const int rg = bi / 8, pg = bi % 8;              // 8 lanes read a row's 128 bytes
+        const uint32_t voff = (uint32_t)((4 * rg * xstride + pg * 8) * 2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xr[m][i] = load16s(rX, voff, (uint32_t)(i * xstride * 2));
+    }
+    const uint16_t *sin_h = p.sin + (((int64_t)b * p.nc + c) * p.H + h) * (int64_t)kP * N;
+    u32x4 sr[SV];
+#pragma unroll
+    for (int i = 0; i < SV; ++i) sr[i] = *(const u32x4 *)(sin_h + (tid + i * NTH) * 8);
+    const rsrc_t rC = make_rsrc_u(p.Cm + (((int64_t)b * p.L + t_base) * p.G + gg) * N, (uint32_t)(T * GN * 2));
+    bf16x8 cfa[KN], cfb[KN];
+#pragma unroll
+    for (int kk = 0; kk < KN; ++kk) {
+        cfa[kk] = as_bf16x8(load16(rC, (uint32_t)(((32 * ta + c32) * GN + 16 * kk + 8 * hf) * 2)));
+        cfb[kk] = as_bf16x8(load16(rC, (uint32_t)(((32 * tb + c32) * GN + 16 * kk + 8 * hf) * 2)));
+    }
+    if (wv == 0) {
+        float dtv[SPL], cs[SPL];
+        head_dt_cs<Q>(p, b, h, c, dtv, cs);
+#pragma unroll
+        for (int i = 0; i < SPL; ++i) {
+            cs2[lane * SPL + i] = cs[i] * kLog2e;
+            dts[lane * SPL + i] = dtv[i];
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < XB; ++m) {
+        const int bi = tid + NTH * m;
+        const int rg = bi / 8, pg = bi % 8;
+        store_transposed(xr[m], &XT[0][0], LDX, pg * 8, pos_s32(4 * rg) ^ (pg << 3));
+    }
+#pragma unroll
+    for (int i = 0; i < SV; ++i) {
+        const int v = tid + i * NTH;
+        *(u32x4 *)&SinL[v / (N / 8)][(v % (N / 8)) * 8] = sr[i];
+    }
+    __syncthreads();
+    // entering state: Y = exp(cs_r) C Sin for both tiles
+    f32x16 ya[2], yb[2];
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt) {
+        ya[pt] = f32x16{};
+        yb[pt] = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < KN; ++kk) {
+            const bf16x8 sf = as_bf16x8(*(const u32x4 *)&SinL[32 * pt + c32][16 * kk + 8 * hf]);
+            ya[pt] = mfma32x32x16(cfa[kk], sf, ya[pt]);
+            yb[pt] = mfma32x32x16(cfb[kk], sf, yb[pt]);
+        }
+    }
+    __syncthreads();                                      // Sin is read
+    // w_s dt_s of every tile after the first (over Sin)
+    for (int v = tid; v < (NT - 1) * Q; v += NTH) {
+        const int s = v % Q, ti = v / Q + 1;
+        if (s < 32 * ti) wts[ti][s] = fast_exp2(cs2[32 * ti - 1] - cs2[s]) * dts[s];
+    }
+    __syncthreads();                                      // the table is complete
+    if (!live_a) return;                                  // uniform; no barrier follows
+    if (ta > 0) {
+        const float er = fast_exp2(cs2[32 * ta - 1]);
+        ya[0] *= er;
+        ya[1] *= er;
+    }
+    {
+        const float er = fast_exp2(cs2[32 * tb - 1]);
+        yb[0] *= er;
+        yb[1] *= er;
+    }
+
+    const float dsk = p.Dskip ? p.Dskip[h] : 0.0f;
+    const float *gbase = p.gsc + ((q * p.G + gg) * NB) * 1024 + lane * 4;
+    auto gload = [&](int tau, int sb, f32x16 &dst) {
+        const float *src = gbase + (tau * (tau + 1) / 2 + sb) * 1024;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const f32x4 v = *(const f32x4 *)(src + i * 256);
+            dst[4 * i] = v[0]; dst[4 * i + 1] = v[1]; dst[4 * i + 2] = v[2]; dst[4 * i + 3] = v[3];
+        }
+    };
+    auto block = [&](f32x16 (&y)[2], int tau, int sb, const f32x16 &g) {
+        float mv[16];
+        if (sb == tau) {
+            // what came before the tile times a_t, then D x of its rows
+            const float cr = tau ? cs2[32 * tau - 1] : 0.0f;
+#pragma unroll
+            for (int pt = 0; pt < 2; ++pt) {
+#pragma unroll
+                for (int hv = 0; hv < 2; ++hv) {
+                    const u32x4 xv = *(const u32x4 *)&XT[32 * pt + c32][(32 * tau + 16 * hv + 8 * hf) ^ xsw(pt)];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int v = 8 * hv + e;
+                        const int tl = 8 * (v >> 2) + 4 * hf + (v & 3);
+                        const float xs = e & 1 ? bf16_hi(xv[e >> 1]) : bf16_lo(xv[e >> 1]);
+                        y[pt][v] = fmaf(dsk, xs, y[pt][v] * fast_exp2(cs2[32 * tau + tl] - cr));
+                    }
+                }
+            }
+            const float ct = cs2[32 * tau + c32];
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const int sl = 8 * gq + 4 * hf;           // within the 32 rows
+                const f32x4 c4 = *(const f32x4 *)&cs2[32 * sb + sl];
+                const f32x4 d4 = *(const f32x4 *)&dts[32 * sb + sl];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float m = g[4 * gq + i] * fast_exp2(ct - c4[i]) * d4[i];
+                    mv[4 * gq + i] = sl + i <= c32 ? m : 0.0f;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const f32x4 w4 = *(const f32x4 *)&wts[tau][32 * sb + 8 * gq + 4 * hf];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) mv[4 * gq + i] = g[4 * gq + i] * w4[i];
+            }
+        }
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+            const bf16x8 ma = as_bf16x8(u32x4{pack_bf16(mv[8 * kh], mv[8 * kh + 1]), pack_bf16(mv[8 * kh + 2], mv[8 * kh + 3]),
+                                              pack_bf16(mv[8 * kh + 4], mv[8 * kh + 5]), pack_bf16(mv[8 * kh + 6], mv[8 * kh + 7])});
+#pragma unroll
+            for (int pt = 0; pt < 2; ++pt)
+                y[pt] = mfma32x32x16(ma, as_bf16x8(*(const u32x4 *)&XT[32 * pt + c32][(32 * sb + 16 * kh + 8 * hf) ^ xsw(pt)]),
+                                     y[pt]);
+        }
+    };
+    // blocks (ta, j) and (tb, j) side by side for j <= ta (independent accumulators),
+    // then (tb, ta + 1 .. tb); each step's score blocks are loaded at the end of the
+    // previous step (three workgroups per CU hide the latency)
+    f32x16 ga, gb;
+    gload(ta, 0, ga);
+    if (live_b) gload(tb, 0, gb);
+    for (int j = 0; j <= ta; ++j) {
+        block(ya, ta, j, ga);
+        if (live_b) block(yb, tb, j, gb);
+        if (j < ta) gload(ta, j + 1, ga);
+        if (live_b) gload(tb, j + 1, gb);                 // j + 1 <= ta + 1 <= tb
+    }
+    if (live_b) {
+        for (int j = ta + 1; j <= tb; ++j) {
+            block(yb, tb, j, gb);
+            if (j < tb) gload(tb, j + 1, gb);
+        }
+    }
+
+    // -- y = (Y + D x) silu(z), rows t = 32 tau + 8 (v >> 2) + 4 hf + (v & 3), p = 32 pt + c32;
+    // rows past the sequence fall outside the buffer ranges (not written, z reads 0). The
+    // lane part of the offset sits in a VGPR, the row part 8 (v >> 2) + (v & 3) in the
+    // instruction's scalar offset.
+    const int64_t row0 = ((int64_t)b * p.L + t_base) * xstride + h * kP;
+    const rsrc_t rY = make_rsrc_u(p.y + row0, (uint32_t)(T * xstride * 2));
+    const rsrc_t rZ = make_rsrc_u(p.z ? p.z + row0 : p.x, p.z ? (uint32_t)(T * xstride * 2) : 0u);
+    auto store_tile = [&](const f32x16 (&y)[2], int tau) {
+#pragma unroll
+        for (int pt = 0; pt < 2; ++pt) {
+            const int voff = (int)(((32 * tau + 4 * hf) * xstride + 32 * pt + c32) * 2);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int soff = (int)((8 * (v >> 2) + (v & 3)) * xstride * 2);
+                float val = y[pt][v];
+                if (p.z) val *= silu_f32(to_f32((uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rZ, voff, soff, 0)));
+                __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(val), rY, voff, soff, 0);
+            }
+        }
+    };
+    store_tile(ya, ta);
+    if (live_b) store_tile(yb, tb);
+}
+
 __global__ __launch_bounds__(256) void ssd_copy_state_kernel(const float *h0, float *out, int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i < n) out[i] = h0 ? h0[i] : 0.0f;
@@ -731,6 +1042,23 @@ unsigned chunk_state_blocks(const SSDK &k, int64_t nq) {
     return (unsigned)((nq + 7) / 8 * 8 * (k.G * ((k.hpg + 3) / 4)));
 }
 
+// Chunk output. Up to N = 128 the forward forms the score blocks once per group and
+// runs the per-head kernel; at N = 256 (C fragments too large for its registers)
+// and for the fp32 recompute of the gradient pass, the 16-row kernel.
+template <int N, int Q, bool F32OUT>
+void launch_out(const SSDK &k, int64_t nq, hipStream_t s) {
+    if constexpr (N <= 128 && !F32OUT) {
+        const unsigned rounded = (unsigned)((nq + 7) / 8 * 8);
+        hipLaunchKernelGGL((ssd_score_kernel<N, Q>), dim3(rounded * (unsigned)(k.G * (Q / 32))), dim3(64), 0, s, k, nq);
+        hipLaunchKernelGGL((ssd_out_head_kernel<N, Q>), dim3(rounded * (unsigned)k.H), dim3(Q), 0, s, k, nq);
+    } else {
+        const int nhg = (k.hpg + OutCfg<N>::HG - 1) / OutCfg<N>::HG;
+        const int64_t nblocks = (nq + 7) / 8 * 8 * (k.G * nhg * out_split<N, Q>());
+        hipLaunchKernelGGL((ssd_chunk_out_kernel<N, Q, F32OUT>), dim3((unsigned)nblocks),
+                           dim3(Q * 4 / out_split<N, Q>()), 0, s, k, nhg, nq);
+    }
+}
+
 template <int N, int Q>
 void launch_nq(const SSDK &k, int batch, hipStream_t s) {
     const int64_t nq = (int64_t)batch * k.nc;            // (batch, chunk) pairs
@@ -738,10 +1066,7 @@ void launch_nq(const SSDK &k, int batch, hipStream_t s) {
     const int64_t total = (int64_t)batch * k.H * kP * N / 4;
     hipLaunchKernelGGL(ssd_state_pass_kernel<true>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
                        k, N, total);
-    const int nhg = (k.hpg + OutCfg<N>::HG - 1) / OutCfg<N>::HG;
-    const int64_t nblocks = (nq + 7) / 8 * 8 * (k.G * nhg * out_split<N, Q>());
-    hipLaunchKernelGGL((ssd_chunk_out_kernel<N, Q, false>), dim3((unsigned)nblocks),
-                       dim3(Q * 4 / out_split<N, Q>()), 0, s, k, nhg, nq);
+    launch_out<N, Q, false>(k, nq, s);
 }
 
 template <int N>
@@ -764,10 +1089,7 @@ void recompute_nq(const SSDK &k, int batch, int what, hipStream_t s) {
         hipLaunchKernelGGL(ssd_state_pass_kernel<false>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
                            k, N, total);
     } else if (what == 1) {   // fp32 pre-gate output
-        const int nhg = (k.hpg + OutCfg<N>::HG - 1) / OutCfg<N>::HG;
-        const int64_t nblocks = (nq + 7) / 8 * 8 * (k.G * nhg * out_split<N, Q>());
-        hipLaunchKernelGGL((ssd_chunk_out_kernel<N, Q, true>), dim3((unsigned)nblocks),
-                           dim3(Q * 4 / out_split<N, Q>()), 0, s, k, nhg, nq);
+        launch_out<N, Q, true>(k, nq, s);
     } else {                  // adjoint aggregates (exp(cs_t) weights)
         hipLaunchKernelGGL((ssd_chunk_state_kernel<N, Q, 2>), cs_grid, dim3(kThreads), 0, s, k, nq);
     }
@@ -810,6 +1132,7 @@ ssm_status ssd_launch(const ssm_ssd_args &a, const SSDPlan &plan, hipStream_t s,
         k.states_last = (float *)((char *)a.workspace + ssd_last_state_offset(a, plan));
         k.sin = (uint16_t *)((char *)a.workspace + plan.sin_offset);
         k.decay = (float *)((char *)a.workspace + plan.decay_offset);
+        k.gsc = plan.gsc_bytes ? (float *)((char *)a.workspace + plan.gsc_offset) : nullptr;
         k.L = a.seqlen; k.H = (int32_t)a.nheads; k.nc = (int32_t)plan.nchunks;
         k.softplus = a.dt_softplus ? 1 : 0;
         k.G = a.ngroups > 1 ? (int32_t)a.ngroups : 1;
