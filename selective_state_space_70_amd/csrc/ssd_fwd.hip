@@ -917,118 +917,136 @@ __global__ __launch_bounds__(Q, Q == 256 ? 3 : 1) void ssd_out_head_kernel(const
         if (s < 32 * ti) wts[ti][s] = fast_exp2(cs2[32 * ti - 1] - cs2[s]) * dts[s];
     }
     __syncthreads();                                      // the table is complete
-    if (!live_a) return;                                  // uniform; no barrier follows
-    if (ta > 0) {
-        const float er = fast_exp2(cs2[32 * ta - 1]);
-        ya[0] *= er;
-        ya[1] *= er;
-    }
-    {
-        const float er = fast_exp2(cs2[32 * tb - 1]);
-        yb[0] *= er;
-        yb[1] *= er;
-    }
-
-    const float dsk = p.Dskip ? p.Dskip[h] : 0.0f;
-    const float *gbase = p.gsc + ((q * p.G + gg) * NB) * 1024 + lane * 4;
-    auto gload = [&](int tau, int sb, f32x16 &dst) {
-        const float *src = gbase + (tau * (tau + 1) / 2 + sb) * 1024;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const f32x4 v = *(const f32x4 *)(src + i * 256);
-            dst[4 * i] = v[0]; dst[4 * i + 1] = v[1]; dst[4 * i + 2] = v[2]; dst[4 * i + 3] = v[3];
+    if (live_a) {                                         // uniform
+        if (ta > 0) {
+            const float er = fast_exp2(cs2[32 * ta - 1]);
+            ya[0] *= er;
+            ya[1] *= er;
         }
-    };
-    auto block = [&](f32x16 (&y)[2], int tau, int sb, const f32x16 &g) {
-        float mv[16];
-        if (sb == tau) {
-            // what came before the tile times a_t, then D x of its rows
-            const float cr = tau ? cs2[32 * tau - 1] : 0.0f;
+        {
+            const float er = fast_exp2(cs2[32 * tb - 1]);
+            yb[0] *= er;
+            yb[1] *= er;
+        }
+
+        const float dsk = p.Dskip ? p.Dskip[h] : 0.0f;
+        const float *gbase = p.gsc + ((q * p.G + gg) * NB) * 1024 + lane * 4;
+        auto gload = [&](int tau, int sb, f32x16 &dst) {
+            const float *src = gbase + (tau * (tau + 1) / 2 + sb) * 1024;
 #pragma unroll
-            for (int pt = 0; pt < 2; ++pt) {
+            for (int i = 0; i < 4; ++i) {
+                const f32x4 v = *(const f32x4 *)(src + i * 256);
+                dst[4 * i] = v[0]; dst[4 * i + 1] = v[1]; dst[4 * i + 2] = v[2]; dst[4 * i + 3] = v[3];
+            }
+        };
+        auto block = [&](f32x16 (&y)[2], int tau, int sb, const f32x16 &g) {
+            float mv[16];
+            if (sb == tau) {
+                // what came before the tile times a_t, then D x of its rows
+                const float cr = tau ? cs2[32 * tau - 1] : 0.0f;
 #pragma unroll
-                for (int hv = 0; hv < 2; ++hv) {
-                    const u32x4 xv = *(const u32x4 *)&XT[32 * pt + c32][(32 * tau + 16 * hv + 8 * hf) ^ xsw(pt)];
+                for (int pt = 0; pt < 2; ++pt) {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int v = 8 * hv + e;
-                        const int tl = 8 * (v >> 2) + 4 * hf + (v & 3);
-                        const float xs = e & 1 ? bf16_hi(xv[e >> 1]) : bf16_lo(xv[e >> 1]);
-                        y[pt][v] = fmaf(dsk, xs, y[pt][v] * fast_exp2(cs2[32 * tau + tl] - cr));
+                    for (int hv = 0; hv < 2; ++hv) {
+                        const u32x4 xv = *(const u32x4 *)&XT[32 * pt + c32][(32 * tau + 16 * hv + 8 * hf) ^ xsw(pt)];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const int v = 8 * hv + e;
+                            const int tl = 8 * (v >> 2) + 4 * hf + (v & 3);
+                            const float xs = e & 1 ? bf16_hi(xv[e >> 1]) : bf16_lo(xv[e >> 1]);
+                            y[pt][v] = fmaf(dsk, xs, y[pt][v] * fast_exp2(cs2[32 * tau + tl] - cr));
+                        }
                     }
                 }
-            }
-            const float ct = cs2[32 * tau + c32];
+                const float ct = cs2[32 * tau + c32];
 #pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                const int sl = 8 * gq + 4 * hf;           // within the 32 rows
-                const f32x4 c4 = *(const f32x4 *)&cs2[32 * sb + sl];
-                const f32x4 d4 = *(const f32x4 *)&dts[32 * sb + sl];
+                for (int gq = 0; gq < 4; ++gq) {
+                    const int sl = 8 * gq + 4 * hf;           // within the 32 rows
+                    const f32x4 c4 = *(const f32x4 *)&cs2[32 * sb + sl];
+                    const f32x4 d4 = *(const f32x4 *)&dts[32 * sb + sl];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float m = g[4 * gq + i] * fast_exp2(ct - c4[i]) * d4[i];
-                    mv[4 * gq + i] = sl + i <= c32 ? m : 0.0f;
+                    for (int i = 0; i < 4; ++i) {
+                        const float m = g[4 * gq + i] * fast_exp2(ct - c4[i]) * d4[i];
+                        mv[4 * gq + i] = sl + i <= c32 ? m : 0.0f;
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    const f32x4 w4 = *(const f32x4 *)&wts[tau][32 * sb + 8 * gq + 4 * hf];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) mv[4 * gq + i] = g[4 * gq + i] * w4[i];
                 }
             }
-        } else {
 #pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                const f32x4 w4 = *(const f32x4 *)&wts[tau][32 * sb + 8 * gq + 4 * hf];
+            for (int kh = 0; kh < 2; ++kh) {
+                const bf16x8 ma = as_bf16x8(u32x4{pack_bf16(mv[8 * kh], mv[8 * kh + 1]), pack_bf16(mv[8 * kh + 2], mv[8 * kh + 3]),
+                                                  pack_bf16(mv[8 * kh + 4], mv[8 * kh + 5]), pack_bf16(mv[8 * kh + 6], mv[8 * kh + 7])});
 #pragma unroll
-                for (int i = 0; i < 4; ++i) mv[4 * gq + i] = g[4 * gq + i] * w4[i];
+                for (int pt = 0; pt < 2; ++pt)
+                    y[pt] = mfma32x32x16(ma, as_bf16x8(*(const u32x4 *)&XT[32 * pt + c32][(32 * sb + 16 * kh + 8 * hf) ^ xsw(pt)]),
+                                         y[pt]);
+            }
+        };
+        // blocks (ta, j) and (tb, j) side by side for j <= ta (independent accumulators),
+        // then (tb, ta + 1 .. tb); each step's score blocks are loaded at the end of the
+        // previous step (three workgroups per CU hide the latency)
+        f32x16 ga, gb;
+        gload(ta, 0, ga);
+        if (live_b) gload(tb, 0, gb);
+        for (int j = 0; j <= ta; ++j) {
+            block(ya, ta, j, ga);
+            if (live_b) block(yb, tb, j, gb);
+            if (j < ta) gload(ta, j + 1, ga);
+            if (live_b) gload(tb, j + 1, gb);                 // j + 1 <= ta + 1 <= tb
+        }
+        if (live_b) {
+            for (int j = ta + 1; j <= tb; ++j) {
+                block(yb, tb, j, gb);
+                if (j < tb) gload(tb, j + 1, gb);
             }
         }
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-            const bf16x8 ma = as_bf16x8(u32x4{pack_bf16(mv[8 * kh], mv[8 * kh + 1]), pack_bf16(mv[8 * kh + 2], mv[8 * kh + 3]),
-                                              pack_bf16(mv[8 * kh + 4], mv[8 * kh + 5]), pack_bf16(mv[8 * kh + 6], mv[8 * kh + 7])});
-#pragma unroll
-            for (int pt = 0; pt < 2; ++pt)
-                y[pt] = mfma32x32x16(ma, as_bf16x8(*(const u32x4 *)&XT[32 * pt + c32][(32 * sb + 16 * kh + 8 * hf) ^ xsw(pt)]),
-                                     y[pt]);
-        }
-    };
-    // blocks (ta, j) and (tb, j) side by side for j <= ta (independent accumulators),
-    // then (tb, ta + 1 .. tb); each step's score blocks are loaded at the end of the
-    // previous step (three workgroups per CU hide the latency)
-    f32x16 ga, gb;
-    gload(ta, 0, ga);
-    if (live_b) gload(tb, 0, gb);
-    for (int j = 0; j <= ta; ++j) {
-        block(ya, ta, j, ga);
-        if (live_b) block(yb, tb, j, gb);
-        if (j < ta) gload(ta, j + 1, ga);
-        if (live_b) gload(tb, j + 1, gb);                 // j + 1 <= ta + 1 <= tb
-    }
-    if (live_b) {
-        for (int j = ta + 1; j <= tb; ++j) {
-            block(yb, tb, j, gb);
-            if (j < tb) gload(tb, j + 1, gb);
-        }
-    }
 
-    // -- y = (Y + D x) silu(z), rows t = 32 tau + 8 (v >> 2) + 4 hf + (v & 3), p = 32 pt + c32;
-    // rows past the sequence fall outside the buffer ranges (not written, z reads 0). The
-    // lane part of the offset sits in a VGPR, the row part 8 (v >> 2) + (v & 3) in the
-    // instruction's scalar offset.
+    }
+    __syncthreads();                                      // every wave is done with x^T
+    if (!live_a) return;                                  // uniform; no barrier follows
+
+    // -- y = (Y + D x) silu(z) through the wave's own 8 KiB of LDS (over x^T): written as
+    // fp32 rows of 64 p from the accumulator layout (row 8 (v >> 2) + 4 hf + (v & 3) of
+    // the tile, p = 32 pt + c32), read back as 4 consecutive p per lane (16 lanes per
+    // row), gated and stored as 8 contiguous bytes per lane. Rows past the sequence fall
+    // outside the buffer ranges (not written, z reads 0). The lane part of each offset
+    // sits in a VGPR, the row step in the instruction's scalar offset.
+    float (*Yw)[kP] = reinterpret_cast<float (*)[kP]>(&XT[0][0]) + wv * 32;
     const int64_t row0 = ((int64_t)b * p.L + t_base) * xstride + h * kP;
     const rsrc_t rY = make_rsrc_u(p.y + row0, (uint32_t)(T * xstride * 2));
     const rsrc_t rZ = make_rsrc_u(p.z ? p.z + row0 : p.x, p.z ? (uint32_t)(T * xstride * 2) : 0u);
-    auto store_tile = [&](const f32x16 (&y)[2], int tau) {
+    const int rl = lane >> 4, c4 = (lane & 15) * 4;
+    auto out_tile = [&](const f32x16 (&y)[2], int tau) {
 #pragma unroll
-        for (int pt = 0; pt < 2; ++pt) {
-            const int voff = (int)(((32 * tau + 4 * hf) * xstride + 32 * pt + c32) * 2);
+        for (int pt = 0; pt < 2; ++pt)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int soff = (int)((8 * (v >> 2) + (v & 3)) * xstride * 2);
-                float val = y[pt][v];
-                if (p.z) val *= silu_f32(to_f32((uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rZ, voff, soff, 0)));
-                __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(val), rY, voff, soff, 0);
+            for (int v = 0; v < 16; ++v) Yw[8 * (v >> 2) + 4 * hf + (v & 3)][32 * pt + c32] = y[pt][v];
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // the wave's own rows only
+        const int voff = (int)(((32 * tau + rl) * xstride + c4) * 2);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const f32x4 o = *(const f32x4 *)&Yw[rl + 4 * i][c4];
+            const int soff = (int)(4 * i * xstride * 2);
+            float g0 = o[0], g1 = o[1], g2 = o[2], g3 = o[3];
+            if (p.z) {
+                const u32x2 zz = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rZ, voff, soff, 0));
+                g0 *= silu_f32(bf16_lo(zz[0]));
+                g1 *= silu_f32(bf16_hi(zz[0]));
+                g2 *= silu_f32(bf16_lo(zz[1]));
+                g3 *= silu_f32(bf16_hi(zz[1]));
             }
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf16(g0, g1), pack_bf16(g2, g3)}, rY, voff, soff, 0);
         }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // read back before the next tile's writes
     };
-    store_tile(ya, ta);
-    if (live_b) store_tile(yb, tb);
+    out_tile(ya, ta);
+    if (live_b) out_tile(yb, tb);
 }
 
 __global__ __launch_bounds__(256) void ssd_copy_state_kernel(const float *h0, float *out, int64_t n) {
