@@ -102,11 +102,13 @@ __global__ __launch_bounds__(kThreads, (N > 128 || MODE != 0) ? 1 : 2) void ssd_
     }
 
     // One 64-row block of B (this pass's states) and of x (this wave's head) is
-    // loaded into registers while the previous one is multiplied. In the LDS
-    // transposes consecutive lanes take consecutive groups of 4 rows, so the
-    // 8-byte writes of 16 lanes cover all banks.
+    // loaded into registers while the previous one is multiplied. Consecutive lanes
+    // read consecutive 16-byte pieces of a row (16 lanes per B row, 8 per x row).
+    // In the transposed LDS copies, row r (a state n or a head-dim p) holds time
+    // position j at column j ^ sw(r), sw(r) = 8 ((r >> 3) & 7), so that the lanes
+    // writing 8 rows r, r + 8, .. at once start in different banks.
     const int GN = p.G * N;
-    const int sg = tid & 15, co = tid >> 4;           // B block of this thread: 4 rows x 8 states
+    const int sg = tid >> 4, co = tid & 15;           // B block of this thread: 4 rows x 8 states
     u32x4 breg[4], xreg[2][4], xlreg[MODE == 2 ? 2 : 1][4];
     const bool has_lo = MODE == 2 && p.xlo != nullptr;
     auto fetch = [&](int pass, int s0) {
@@ -119,7 +121,7 @@ __global__ __launch_bounds__(kThreads, (N > 128 || MODE != 0) ? 1 : 2) void ssd_
         for (int i = 0; i < 4; ++i) breg[i] = load16(rb, (uint32_t)(((sg * 4 + i) * GN + co * 8) * 2));
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
-            const int blk = lane + 64 * k, xg = blk & 15, po = blk >> 4;
+            const int blk = lane + 64 * k, xg = blk >> 3, po = blk & 7;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 xreg[k][i] = load16(rx, (uint32_t)(((xg * 4 + i) * p.H * kP + po * 8) * 2));
@@ -130,7 +132,7 @@ __global__ __launch_bounds__(kThreads, (N > 128 || MODE != 0) ? 1 : 2) void ssd_
                                             (uint32_t)(rows * p.H * kP * 2));
 #pragma unroll
                 for (int k = 0; k < 2; ++k) {
-                    const int blk = lane + 64 * k, xg = blk & 15, po = blk >> 4;
+                    const int blk = lane + 64 * k, xg = blk >> 3, po = blk & 7;
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         xlreg[k][i] = load16(rl, (uint32_t)(((xg * 4 + i) * p.H * kP + po * 8) * 2));
@@ -139,10 +141,10 @@ __global__ __launch_bounds__(kThreads, (N > 128 || MODE != 0) ? 1 : 2) void ssd_
         }
     };
     auto stash = [&](int s0) {
-        if (co < NP / 8) store_transposed(breg, &BT[0][0], LDT, co * 8, sg * 4);
+        if (co < NP / 8) store_transposed(breg, &BT[0][0], LDT, co * 8, (sg * 4) ^ ((co & 7) << 3));
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
-            const int blk = lane + 64 * k, xg = blk & 15, po = blk >> 4;
+            const int blk = lane + 64 * k, xg = blk >> 3, po = blk & 7;
             u32x4 r[4], rl[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -162,11 +164,12 @@ __global__ __launch_bounds__(kThreads, (N > 128 || MODE != 0) ? 1 : 2) void ssd_
                         rl[i][e] = pack_bf16(v0 - bf16_lo(r[i][e]), v1 - bf16_hi(r[i][e]));
                 }
             }
-            store_transposed(r, &XT[wv][0][0], LDT, po * 8, xg * 4);
-            if constexpr (SPLIT) store_transposed(rl, &XL[wv][0][0], LDT, po * 8, xg * 4);
+            store_transposed(r, &XT[wv][0][0], LDT, po * 8, (xg * 4) ^ (po << 3));
+            if constexpr (SPLIT) store_transposed(rl, &XL[wv][0][0], LDT, po * 8, (xg * 4) ^ (po << 3));
         }
     };
 
+    auto sw = [](int r) { return ((r >> 3) & 7) << 3; };
     constexpr int NBLK = Q / SB;
     fetch(0, 0);
     for (int pass = 0; pass < NPASS; ++pass) {
@@ -189,19 +192,19 @@ __global__ __launch_bounds__(kThreads, (N > 128 || MODE != 0) ? 1 : 2) void ssd_
                 const int sk = kk * 32 + kb * 8;
                 bf16x8 bfr[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) bfr[j] = as_bf16x8(*(const u32x4 *)&XT[wv][j * 16 + r16][sk]);
+                for (int j = 0; j < 4; ++j) bfr[j] = as_bf16x8(*(const u32x4 *)&XT[wv][j * 16 + r16][sk ^ sw(j * 16 + r16)]);
 #pragma unroll
                 for (int i = 0; i < NT; ++i) {
-                    const bf16x8 afr = as_bf16x8(*(const u32x4 *)&BT[i * 16 + r16][sk]);
+                    const bf16x8 afr = as_bf16x8(*(const u32x4 *)&BT[i * 16 + r16][sk ^ sw(i * 16 + r16)]);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(afr, bfr[j], acc[i][j]);
                 }
                 if constexpr (SPLIT) {
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) bfr[j] = as_bf16x8(*(const u32x4 *)&XL[wv][j * 16 + r16][sk]);
+                    for (int j = 0; j < 4; ++j) bfr[j] = as_bf16x8(*(const u32x4 *)&XL[wv][j * 16 + r16][sk ^ sw(j * 16 + r16)]);
 #pragma unroll
                     for (int i = 0; i < NT; ++i) {
-                        const bf16x8 afr = as_bf16x8(*(const u32x4 *)&BT[i * 16 + r16][sk]);
+                        const bf16x8 afr = as_bf16x8(*(const u32x4 *)&BT[i * 16 + r16][sk ^ sw(i * 16 + r16)]);
 #pragma unroll
                         for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(afr, bfr[j], acc[i][j]);
                     }
