@@ -32,6 +32,15 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8 &a, const bf16x8 &b, 
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4 &v) { return __builtin_bit_cast(bf16x8, v); }
 
+// v_mfma_f32_32x32x16_bf16 (lane l, c32 = l & 31, hf = l >> 5): A (32 x 16) row c32,
+// k = 8 hf + e; B (16 x 32) column c32, k = 8 hf + e; D (32 x 32, fp32) register v
+// holds row 8 (v >> 2) + 4 hf + (v & 3), column c32.
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+__device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8 &a, const bf16x8 &b, const f32x16 &c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
 // Buffer resource from a wave-uniform base and size. Every call site passes values
 // that are the same in all lanes of the wave; readfirstlane on the base as well
 // keeps the resource in SGPRs even where the compiler built the address with

@@ -12,24 +12,28 @@
 //   output            : y_t = sum_{s<=t} (C_t.B_s) exp(cs_t - cs_s) dt_s x_s
 //                            + exp(cs_t) C_t . Sin_c + D x_t,   then * silu(z_t)
 //
-// Three kernels per call (v_mfma_f32_16x16x32_bf16, fp32 accumulation):
-//   1. ssd_chunk_state: per (batch, chunk, 4 heads). B of the chunk is transposed
-//      into LDS once and shared by the 4 heads (one wave each); x is transposed
-//      and scaled by exp(cs_end - cs_s) dt_s while staging. S_c is written in bf16,
-//      layout [p][n] (fp32 in the gradient pass's recompute).
+// Three launches per call (matrix cores, fp32 accumulation):
+//   1. ssd_chunk_state: per (batch, chunk, 4 heads), v_mfma_f32_16x16x32_bf16. B
+//      of the chunk is transposed into LDS once and shared by the 4 heads (one wave
+//      each); x is transposed and scaled by exp(cs_end - cs_s) dt_s while staging.
+//      S_c is written in bf16, layout [p][n] (fp32 in the gradient pass's
+//      recompute). Up to N = 128 extra workgroups of the same launch form the score
+//      blocks G^T = B C^T of every (batch, chunk, group) once, in fp32, on
+//      v_mfma_f32_32x32x16_bf16: every head of the group reads them.
 //   2. ssd_state_pass: sequential over chunks per (batch, head, p, 4 n); writes the
 //      entering state of every chunk already rounded to bf16 in the [p][n] layout
-//      the output kernel reads as MFMA B fragments, and h_final in fp32.
-//   3. ssd_chunk_out: per (batch, chunk, pair of heads), one 16-row tile per wave
-//      (at chunk 256 split over two workgroups); B and x stream through LDS in
-//      64-row blocks of s, each loaded once per workgroup. For each block the
-//      transposed score tile G^T = B C^T is computed on the MFMA units, masked and
-//      scaled in registers and rounded to bf16 straight into the A operand of
-//      Y += M X (the 16x16 accumulator layout gives a lane 4 consecutive s of one t;
-//      two tiles give the 8 an A fragment holds, and X is staged with the same
-//      order of s, which the contraction over s does not care about). The carried
-//      state enters as Y = exp(cs_t) (C Sin) on the same units; D x and the gate
-//      are applied exactly in fp32 when the tile is written.
+//      the output kernels read as MFMA B fragments, and h_final in fp32.
+//   3. ssd_out_head (N <= 128): per (batch, chunk, head), Q/64 waves on 32 x 32
+//      tiles, each wave owning the tiles w and Q/32 - 1 - w (equal causal work).
+//      x is staged transposed in LDS once; each score block is read from L2, scaled
+//      by the decays in registers and rounded to bf16 straight into the A operand
+//      of Y += M X (x stored with the matching order of s, which the contraction
+//      over s does not care about). The carried state enters as exp(cs_t) (C Sin)
+//      on the same units; D x and the gate are applied in fp32 on the way out.
+//      ssd_chunk_out (N = 256, and the fp32 recompute of the gradient pass): per
+//      (batch, chunk, pair of heads), one 16-row tile per wave (at chunk 256 split
+//      over two workgroups); B and x stream through LDS in 64-row blocks of s, and
+//      the score tile is formed on the MFMA units for each block.
 // Transposes into LDS move 4 x 8 register blocks with byte permutes and 8-byte
 // LDS writes.
 #include <algorithm>
@@ -44,6 +48,64 @@
 namespace ssm {
 namespace {
 
+// ---------------------------------------------------------------- score blocks
+// G^T = B C^T of a chunk in 32 x 32 blocks (rows s of block sb, columns t of tile
+// tau, sb <= tau), on v_mfma_f32_32x32x16_bf16, kept in fp32 as the matrix cores
+// accumulate it. G depends on the group's B and C only, so it is formed once per
+// (batch, chunk, group), by extra workgroups of the chunk-state kernel, and read by
+// every head of the group.
+//
+// In the 32 x 32 accumulator layout (register v of lane l: row 8 (v >> 2) + 4 (l >> 5)
+// + (v & 3), column l & 31) a block is stored as 4 runs
+// of 256 floats, run i holding registers 4i .. 4i + 3 of lanes 0 .. 63 in order,
+// so that each of the 4 loads (and stores) of a lane's 16 values moves 1 KiB of
+// contiguous memory per wave. Block (tau, sb) of (batch, chunk, group) qg sits at
+// (qg NB + tau (tau + 1) / 2 + sb) 1024 floats, NB = Q/32 (Q/32 + 1) / 2. Tiles
+// with no step of the sequence are left out (and never read).
+template <int Q>
+constexpr int score_blocks() { return (Q / 32) * (Q / 32 + 1) / 2; }
+
+// Score blocks (tau, 0 .. tau) of (batch, chunk) q and group gg, by one wave.
+template <int N, int Q>
+__device__ __forceinline__ void score_tile(const SSDK &p, int64_t q, int gg, int tau) {
+    constexpr int NB = score_blocks<Q>(), KN = N / 16;
+    const int c = (int)(q % p.nc), b = (int)(q / p.nc);
+    const int lane = threadIdx.x & 63, c32 = lane & 31, hf = lane >> 5;
+    const int64_t t_base = (int64_t)c * Q;
+    const int T = (int)std::min<int64_t>(Q, p.L - t_base);
+    if (32 * tau >= T) return;                                 // no step in this tile (uniform)
+    const int GN = p.G * N;
+    const rsrc_t rC = make_rsrc_u(p.Cm + (((int64_t)b * p.L + t_base) * p.G + gg) * N, (uint32_t)(T * GN * 2));
+    const rsrc_t rB = make_rsrc_u(p.Bm + (((int64_t)b * p.L + t_base) * p.G + gg) * N, (uint32_t)(T * GN * 2));
+    bf16x8 cfr[KN], bfa[KN], bfb[KN];
+#pragma unroll
+    for (int kk = 0; kk < KN; ++kk)
+        cfr[kk] = as_bf16x8(load16(rC, (uint32_t)(((32 * tau + c32) * GN + 16 * kk + 8 * hf) * 2)));
+    auto load_b = [&](int sb, bf16x8 (&dst)[KN]) {
+#pragma unroll
+        for (int kk = 0; kk < KN; ++kk)
+            dst[kk] = as_bf16x8(load16(rB, (uint32_t)(((32 * sb + c32) * GN + 16 * kk + 8 * hf) * 2)));
+    };
+    float *out = p.gsc + ((q * p.G + gg) * NB + tau * (tau + 1) / 2) * 1024 + lane * 4;
+    auto block = [&](int sb, const bf16x8 (&bf)[KN]) {
+        f32x16 g = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < KN; ++kk) g = mfma32x32x16(bf[kk], cfr[kk], g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *(f32x4 *)(out + sb * 1024 + i * 256) = f32x4{g[4 * i], g[4 * i + 1], g[4 * i + 2], g[4 * i + 3]};
+    };
+    load_b(0, bfa);
+    for (int sb = 0;;) {
+        if (sb < tau) load_b(sb + 1, bfb);
+        block(sb, bfa);
+        if (++sb > tau) break;
+        if (sb < tau) load_b(sb + 1, bfa);
+        block(sb, bfb);
+        if (++sb > tau) break;
+    }
+}
+
 // ---------------------------------------------------------------- chunk states
 // MODE 0: S_c = sum_s exp(cs_end - cs_s) dt_s B_s (x) x_s, the weighted x rounded to
 //         bf16, S_c stored in bf16 (the forward: the entering states it feeds are
@@ -56,7 +118,7 @@ namespace {
 //         of the gradient pass).
 template <int N, int Q, int MODE>
 __global__ __launch_bounds__(kThreads, (N > 128 || MODE != 0) ? 1 : 2) void ssd_chunk_state_kernel(const SSDK p,
-                                                                                                int64_t nq) {
+                                                                                                int64_t nq, int nscore) {
     constexpr bool SPLIT = MODE != 0;
     constexpr int SB = 64;                    // time rows staged per step
     constexpr int LDT = SB + 8;               // padded LDS row (bf16)
@@ -73,10 +135,27 @@ __global__ __launch_bounds__(kThreads, (N > 128 || MODE != 0) ? 1 : 2) void ssd_
     // q % 8 = i % 8 here, so every head block of a chunk runs on one XCD: the chunk's
     // B rows come into one L2 instead of all eight. Neighbouring ids are neighbouring
     // chunks, so the workgroups of a chunk still run close together in time.
+    if constexpr (MODE == 0 && N <= 128) {
+        // the first nscore workgroups (a multiple of 8; dispatched first, so they run
+        // beside the chunk states) form the score blocks: one per (batch, chunk,
+        // group), on the XCD of the chunk; wave w takes tiles w and Q/32 - 1 - w
+        // (equal causal work)
+        if ((int)blockIdx.x < nscore) {
+            const int64_t sid = blockIdx.x;
+            const int64_t k8 = sid >> 3;
+            const int64_t q = (k8 / p.G) * 8 + (sid & 7);
+            const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+            if (q >= nq || 2 * w >= Q / 32) return;
+            score_tile<N, Q>(p, q, (int)(k8 % p.G), w);
+            score_tile<N, Q>(p, q, (int)(k8 % p.G), Q / 32 - 1 - w);
+            return;
+        }
+    }
     const int hb = (p.hpg + 3) / 4;                   // workgroups per group of heads
     const int upc = p.G * hb;                         // workgroups per (batch, chunk)
-    const int k8 = blockIdx.x >> 3;
-    const int64_t q = (int64_t)(k8 / upc) * 8 + (blockIdx.x & 7);
+    const int bid = (int)blockIdx.x - nscore;
+    const int k8 = bid >> 3;
+    const int64_t q = (int64_t)(k8 / upc) * 8 + (bid & 7);
     if (q >= nq) return;                              // whole workgroup (uniform)
     const int unit = k8 % upc;
     const int c = (int)(q % p.nc), b = (int)(q / p.nc);
@@ -724,83 +803,14 @@ void ssd_chunk_out_kernel(const SSDK p, int nhg, int64_t nq) {
     }
 }
 
-// ---------------------------------------------------------------- score blocks
-// G^T = B C^T of a chunk in 32 x 32 blocks (rows s of block sb, columns t of tile
-// tau, sb <= tau), on v_mfma_f32_32x32x16_bf16, kept in fp32 as the matrix cores
-// accumulate it. G depends on the group's B and C only, so it is formed once per
-// (batch, chunk, group) here and read by every head of the group.
-//
-// 32 x 32 fragments (lane l, c32 = l & 31, hf = l >> 5): A (32 x 16) row c32,
-// k = 8 hf + e; B (16 x 32) column c32, k = 8 hf + e; D (32 x 32, fp32) register v
-// holds row 8 (v >> 2) + 4 hf + (v & 3), column c32. A block is stored as 4 runs
-// of 256 floats, run i holding registers 4i .. 4i + 3 of lanes 0 .. 63 in order,
-// so that each of the 4 loads (and stores) of a lane's 16 values moves 1 KiB of
-// contiguous memory per wave. Block (tau, sb) of (batch, chunk, group) qg sits at
-// (qg NB + tau (tau + 1) / 2 + sb) 1024 floats, NB = Q/32 (Q/32 + 1) / 2. Tiles
-// with no step of the sequence are left out (and never read).
-typedef __attribute__((ext_vector_type(16))) float f32x16;
-
-__device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8 &a, const bf16x8 &b, const f32x16 &c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-template <int Q>
-constexpr int score_blocks() { return (Q / 32) * (Q / 32 + 1) / 2; }
-
-// one wave per (batch, chunk, group, tile tau)
-template <int N, int Q>
-__global__ __launch_bounds__(64) void ssd_score_kernel(const SSDK p, int64_t nq) {
-    constexpr int NT = Q / 32, NB = score_blocks<Q>(), KN = N / 16;
-    const int upc = p.G * NT;
-    const int id = blockIdx.x, k8 = id >> 3;
-    const int64_t q = (int64_t)(k8 / upc) * 8 + (id & 7);   // the tiles of a chunk share an XCD
-    if (q >= nq) return;
-    const int unit = k8 % upc;
-    const int gg = unit / NT, tau = unit % NT;
-    const int c = (int)(q % p.nc), b = (int)(q / p.nc);
-    const int lane = threadIdx.x, c32 = lane & 31, hf = lane >> 5;
-    const int64_t t_base = (int64_t)c * Q;
-    const int T = (int)std::min<int64_t>(Q, p.L - t_base);
-    if (32 * tau >= T) return;                                 // no step in this tile
-    const int GN = p.G * N;
-    const rsrc_t rC = make_rsrc_u(p.Cm + (((int64_t)b * p.L + t_base) * p.G + gg) * N, (uint32_t)(T * GN * 2));
-    const rsrc_t rB = make_rsrc_u(p.Bm + (((int64_t)b * p.L + t_base) * p.G + gg) * N, (uint32_t)(T * GN * 2));
-    bf16x8 cfr[KN], bfa[KN], bfb[KN];
-#pragma unroll
-    for (int kk = 0; kk < KN; ++kk)
-        cfr[kk] = as_bf16x8(load16(rC, (uint32_t)(((32 * tau + c32) * GN + 16 * kk + 8 * hf) * 2)));
-    auto load_b = [&](int sb, bf16x8 (&dst)[KN]) {
-#pragma unroll
-        for (int kk = 0; kk < KN; ++kk)
-            dst[kk] = as_bf16x8(load16(rB, (uint32_t)(((32 * sb + c32) * GN + 16 * kk + 8 * hf) * 2)));
-    };
-    float *out = p.gsc + ((q * p.G + gg) * NB + tau * (tau + 1) / 2) * 1024 + lane * 4;
-    auto block = [&](int sb, const bf16x8 (&bf)[KN]) {
-        f32x16 g = f32x16{};
-#pragma unroll
-        for (int kk = 0; kk < KN; ++kk) g = mfma32x32x16(bf[kk], cfr[kk], g);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            *(f32x4 *)(out + sb * 1024 + i * 256) = f32x4{g[4 * i], g[4 * i + 1], g[4 * i + 2], g[4 * i + 3]};
-    };
-    load_b(0, bfa);
-    for (int sb = 0;;) {
-        if (sb < tau) load_b(sb + 1, bfb);
-        block(sb, bfa);
-        if (++sb > tau) break;
-        if (sb < tau) load_b(sb + 1, bfa);
-        block(sb, bfb);
-        if (++sb > tau) break;
-    }
-}
-
 // ---------------------------------------------------------------- chunk output, one head
 // Per (batch, chunk, head): Q/64 waves; wave w owns the 32-row tiles w and
 // Q/32 - 1 - w of the chunk, whose causal work adds up to the same for every wave.
 // The head's x (transposed: the B operand of Y += M X) and entering state are
-// staged in LDS once; the score blocks come from the score kernel (L2), one block
-// ahead of their use. Two workgroups fit a CU, so one's loads overlap the other's
-// arithmetic.
+// staged in LDS once (the state's buffer then holds the decay table); the score
+// blocks come from L2 (formed by the chunk-state launch). At chunk 256 three
+// workgroups fit a CU (52 KiB of LDS, <= 168 VGPRs), so loads of some overlap the
+// arithmetic of others.
 //
 // Decays as in the 16-row kernel, with r = 32 tau - 1 the step before a tile:
 // blocks of s before the tile take M = G o (w_s dt_s), w_s = exp(cs_r - cs_s)
@@ -1070,7 +1080,6 @@ template <int N, int Q, bool F32OUT>
 void launch_out(const SSDK &k, int64_t nq, hipStream_t s) {
     if constexpr (N <= 128 && !F32OUT) {
         const unsigned rounded = (unsigned)((nq + 7) / 8 * 8);
-        hipLaunchKernelGGL((ssd_score_kernel<N, Q>), dim3(rounded * (unsigned)(k.G * (Q / 32))), dim3(64), 0, s, k, nq);
         hipLaunchKernelGGL((ssd_out_head_kernel<N, Q>), dim3(rounded * (unsigned)k.H), dim3(Q), 0, s, k, nq);
     } else {
         const int nhg = (k.hpg + OutCfg<N>::HG - 1) / OutCfg<N>::HG;
@@ -1083,7 +1092,11 @@ void launch_out(const SSDK &k, int64_t nq, hipStream_t s) {
 template <int N, int Q>
 void launch_nq(const SSDK &k, int batch, hipStream_t s) {
     const int64_t nq = (int64_t)batch * k.nc;            // (batch, chunk) pairs
-    hipLaunchKernelGGL((ssd_chunk_state_kernel<N, Q, 0>), dim3(chunk_state_blocks(k, nq)), dim3(kThreads), 0, s, k, nq);
+    // chunk states, and (up to N = 128) the score blocks of the output kernel in extra workgroups
+    const unsigned cs_blocks = chunk_state_blocks(k, nq);
+    const unsigned sc_blocks = N <= 128 ? (unsigned)((nq + 7) / 8 * 8 * k.G) : 0u;
+    hipLaunchKernelGGL((ssd_chunk_state_kernel<N, Q, 0>), dim3(cs_blocks + sc_blocks), dim3(kThreads), 0, s, k, nq,
+                       (int)sc_blocks);
     const int64_t total = (int64_t)batch * k.H * kP * N / 4;
     hipLaunchKernelGGL(ssd_state_pass_kernel<true>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
                        k, N, total);
@@ -1105,14 +1118,14 @@ void recompute_nq(const SSDK &k, int batch, int what, hipStream_t s) {
     const int64_t nq = (int64_t)batch * k.nc;
     const dim3 cs_grid(chunk_state_blocks(k, nq));
     if (what == 0) {          // split-precision chunk states, then the entering states
-        hipLaunchKernelGGL((ssd_chunk_state_kernel<N, Q, 1>), cs_grid, dim3(kThreads), 0, s, k, nq);
+        hipLaunchKernelGGL((ssd_chunk_state_kernel<N, Q, 1>), cs_grid, dim3(kThreads), 0, s, k, nq, 0);
         const int64_t total = (int64_t)batch * k.H * kP * N / 4;
         hipLaunchKernelGGL(ssd_state_pass_kernel<false>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
                            k, N, total);
     } else if (what == 1) {   // fp32 pre-gate output
         launch_out<N, Q, true>(k, nq, s);
     } else {                  // adjoint aggregates (exp(cs_t) weights)
-        hipLaunchKernelGGL((ssd_chunk_state_kernel<N, Q, 2>), cs_grid, dim3(kThreads), 0, s, k, nq);
+        hipLaunchKernelGGL((ssd_chunk_state_kernel<N, Q, 2>), cs_grid, dim3(kThreads), 0, s, k, nq, 0);
     }
 }
 
