@@ -393,10 +393,11 @@ __device__ __forceinline__ float pow_uniform(float r, int m) {
 // j < k: Sp_{k+1} = P_k o Sp_k + S_k, and Pp accumulates the decays (their
 // product in the fast path, where P_j[n] = R_j^(n+1); their summed step
 // otherwise). One workgroup per (chain, row): rows n < N carry Sp[n], row N
-// carries Pp. The chain's chunks are cut into kPrefixSeg segments, one per wave:
-// each wave composes its segment, the waves exchange the segment maps through
-// LDS, and each wave walks its segment again from the composed map of the
-// segments before it, writing the prefix for chunk k to pre[k-1]. Nothing in
+// carries Pp. The chain's chunks are cut into segments of about 16, one per wave
+// (at most kPrefixSeg; blockDim.x / 64 of them): each wave composes its segment,
+// the waves exchange the segment maps through LDS, and each wave walks its segment
+// again from the composed map of the segments before it, writing the prefix for
+// chunk k to pre[k-1]. Nothing in
 // it depends on h0, so a caller that learns h0 later (another device's share of
 // the sequence) can still run the apply pass with it.
 constexpr int kPrefixSeg = 8;
@@ -410,30 +411,36 @@ __global__ __launch_bounds__(64 * kPrefixSeg) void scan_prefix_kernel(const Scan
     const int d = (slot.chain % p.dblocks) * 64 + lane;
     const int dc = d < p.D ? d : p.D - 1;
     const int n = slot.pos;                                // uniform
-    const bool fast = __all(row_is_geometric<N>(p.A + (int64_t)dc * N));
-    const float al2 = p.A[(int64_t)dc * N + min(n, N - 1)] * kLog2e;
     const size_t blk = (size_t)(N + 1) * 64;
     const int K = p.chunks - 1;                            // aggregates of chunks 0..K-1
     const float *src = p.agg + (size_t)slot.chain * K * blk + lane;
     float *dst = p.pre + (size_t)slot.chain * K * blk + lane;
     const size_t row = (size_t)min(n, N) * 64, drow = (size_t)N * 64;
-    const int per = (K + kPrefixSeg - 1) / kPrefixSeg;
+    const int nseg = blockDim.x >> 6;
+    const int per = (K + nseg - 1) / nseg;
     const int j0 = min(K, w * per), j1 = min(K, j0 + per);
-    const float unit = fast ? 1.0f : 0.0f;                // identity of the decay combine
-    auto decay = [&](float rr) { return fast ? pow_uniform(rr, n + 1) : fast_exp2(al2 * rr); };
-    auto comb = [&](float a, float rr) { return fast ? a * rr : a + rr; };
     constexpr int U = 16;
-
-    // 1. this segment's map: decay combine Rs, state part Ss (rows < N)
-    float Rs = unit, Ss = 0.0f;
-    for (int jb = j0; jb < j1; jb += U) {
-        float sv[U], rv[U];
+    float sv[U], rv[U];
+    auto load_block = [&](int jb) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const size_t kk = (size_t)min(jb + u, K - 1) * blk;
             sv[u] = src[kk + row];
             rv[u] = src[kk + drow];
         }
+    };
+    // the segment's first block goes out before the A row is read and tested
+    load_block(j0);
+    const bool fast = __all(row_is_geometric<N>(p.A + (int64_t)dc * N));
+    const float al2 = p.A[(int64_t)dc * N + min(n, N - 1)] * kLog2e;
+    const float unit = fast ? 1.0f : 0.0f;                // identity of the decay combine
+    auto decay = [&](float rr) { return fast ? pow_uniform(rr, n + 1) : fast_exp2(al2 * rr); };
+    auto comb = [&](float a, float rr) { return fast ? a * rr : a + rr; };
+
+    // 1. this segment's map: decay combine Rs, state part Ss (rows < N)
+    float Rs = unit, Ss = 0.0f;
+    for (int jb = j0; jb < j1; jb += U) {
+        if (jb != j0) load_block(jb);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             if (jb + u < j1) {                             // uniform
@@ -453,14 +460,9 @@ __global__ __launch_bounds__(64 * kPrefixSeg) void scan_prefix_kernel(const Scan
         Rp = comb(Rp, segR[v][lane]);
     }
     // 3. walk the segment again from that map, writing each chunk's successor prefix
+    // (a segment of one block is still in the registers)
     for (int jb = j0; jb < j1; jb += U) {
-        float sv[U], rv[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const size_t kk = (size_t)min(jb + u, K - 1) * blk;
-            sv[u] = src[kk + row];
-            rv[u] = src[kk + drow];
-        }
+        if (j1 - j0 > U) load_block(jb);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             if (jb + u < j1) {
@@ -535,8 +537,8 @@ ssm_status launch_typed(const ScanK &k, hipStream_t s, int passes) {
     if (k.chunks > 1 && (passes & 1)) {
         hipLaunchKernelGGL((scan_chunk_state_kernel<T, N, SP>), dim3(chain_grid(chains, k.chunks - 1)),
                            dim3(64), 0, s, k);
-        hipLaunchKernelGGL((scan_prefix_kernel<N>), dim3(chain_grid(chains, N + 1)), dim3(64 * kPrefixSeg),
-                           0, s, k);
+        const int nseg = std::min(kPrefixSeg, std::max(1, (k.chunks - 1 + 15) / 16));
+        hipLaunchKernelGGL((scan_prefix_kernel<N>), dim3(chain_grid(chains, N + 1)), dim3(64 * nseg), 0, s, k);
     }
     if (!(passes & 2)) return SSM_OK;
     const int grid = chain_grid(chains, k.chunks);
