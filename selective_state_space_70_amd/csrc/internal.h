@@ -42,7 +42,7 @@ struct SSDPlan {
     size_t states_offset;   // fp32 [B][nchunks][H][P][N]: chunk states from a zero state
     size_t sin_offset;      // bf16 [B][nchunks][H][P][N]: state entering each chunk
     size_t decay_offset;    // fp32 [B][H][nchunks]
-    size_t gsc_offset;      // fp32 score blocks: [B][nchunks][G][blocks][1024] (N <= 128)
+    size_t gsc_offset;      // fp32 score blocks: [B][nchunks][G][blocks][1024]
     size_t gsc_bytes;
     size_t bytes;
 };

@@ -59,7 +59,7 @@ SSDPlan ssd_plan(const ssm_ssd_args &a) {
     // 32 x 32 fp32 blocks of C B^T on and below the diagonal of each chunk
     const size_t tiles = (size_t)(a.chunk + 31) / 32;
     const size_t G = a.ngroups > 1 ? (size_t)a.ngroups : 1;
-    pl.gsc_bytes = a.dstate <= 128 ? up((size_t)a.batch * pl.nchunks * G * (tiles * (tiles + 1) / 2) * 1024 * sizeof(float)) : 0;
+    pl.gsc_bytes = up((size_t)a.batch * pl.nchunks * G * (tiles * (tiles + 1) / 2) * 1024 * sizeof(float));
     pl.bytes = pl.gsc_offset + pl.gsc_bytes;
     return pl;
 }

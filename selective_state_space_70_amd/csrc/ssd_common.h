@@ -98,7 +98,7 @@ struct SSDK {
     float *sin32;       // optional fp32 copy of the entering states (may alias states)
     float *y32;         // fp32 pre-gate output (B, L, H, P) of the recompute variant
     const uint16_t *xlo;   // optional bf16 lo part of x (adjoint aggregates: dyc = hi + lo)
-    float *gsc;         // fp32 score blocks C B^T per (batch, chunk, group) (forward, N <= 128)
+    float *gsc;         // fp32 score blocks C B^T per (batch, chunk, group) (forward)
     int64_t L;
     int32_t H;
     int32_t nc;

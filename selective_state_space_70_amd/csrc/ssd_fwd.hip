@@ -17,20 +17,20 @@
 //      of the chunk is transposed into LDS once and shared by the 4 heads (one wave
 //      each); x is transposed and scaled by exp(cs_end - cs_s) dt_s while staging.
 //      S_c is written in bf16, layout [p][n] (fp32 in the gradient pass's
-//      recompute). Up to N = 128 extra workgroups of the same launch form the score
+//      recompute). In the forward, extra workgroups of the same launch form the score
 //      blocks G^T = B C^T of every (batch, chunk, group) once, in fp32, on
 //      v_mfma_f32_32x32x16_bf16: every head of the group reads them.
 //   2. ssd_state_pass: sequential over chunks per (batch, head, p, 4 n); writes the
 //      entering state of every chunk already rounded to bf16 in the [p][n] layout
 //      the output kernels read as MFMA B fragments, and h_final in fp32.
-//   3. ssd_out_head (N <= 128): per (batch, chunk, head), Q/64 waves on 32 x 32
+//   3. ssd_out_head (the forward): per (batch, chunk, head), Q/64 waves on 32 x 32
 //      tiles, each wave owning the tiles w and Q/32 - 1 - w (equal causal work).
 //      x is staged transposed in LDS once; each score block is read from L2, scaled
 //      by the decays in registers and rounded to bf16 straight into the A operand
 //      of Y += M X (x stored with the matching order of s, which the contraction
 //      over s does not care about). The carried state enters as exp(cs_t) (C Sin)
 //      on the same units; D x and the gate are applied in fp32 on the way out.
-//      ssd_chunk_out (N = 256, and the fp32 recompute of the gradient pass): per
+//      ssd_chunk_out (the fp32 pre-gate recompute of the gradient pass): per
 //      (batch, chunk, pair of heads), one 16-row tile per wave (at chunk 256 split
 //      over two workgroups); B and x stream through LDS in 64-row blocks of s, and
 //      the score tile is formed on the MFMA units for each block.
@@ -135,7 +135,7 @@ __global__ __launch_bounds__(kThreads, (N > 128 || MODE != 0) ? 1 : 2) void ssd_
     // q % 8 = i % 8 here, so every head block of a chunk runs on one XCD: the chunk's
     // B rows come into one L2 instead of all eight. Neighbouring ids are neighbouring
     // chunks, so the workgroups of a chunk still run close together in time.
-    if constexpr (MODE == 0 && N <= 128) {
+    if constexpr (MODE == 0) {
         // the first nscore workgroups (a multiple of 8; dispatched first, so they run
         // beside the chunk states) form the score blocks: one per (batch, chunk,
         // group), on the XCD of the chunk; wave w takes tiles w and Q/32 - 1 - w
@@ -824,7 +824,7 @@ void ssd_chunk_out_kernel(const SSDK p, int nhg, int64_t nq) {
 __device__ __forceinline__ int pos_s32(int s) { return (s & ~12) | ((s & 4) << 1) | ((s & 8) >> 1); }
 
 template <int N, int Q>
-__global__ __launch_bounds__(Q, Q == 256 ? 3 : 1) void ssd_out_head_kernel(const SSDK p, int64_t nq) {
+__global__ __launch_bounds__(Q, Q == 256 ? (N > 128 ? 2 : 3) : 1) void ssd_out_head_kernel(const SSDK p, int64_t nq) {
     constexpr int NT = Q / 32;                // 32-row tiles
     constexpr int NB = score_blocks<Q>();
     constexpr int NTH = Q;                    // Q / 64 waves
@@ -1073,12 +1073,12 @@ unsigned chunk_state_blocks(const SSDK &k, int64_t nq) {
     return (unsigned)((nq + 7) / 8 * 8 * (k.G * ((k.hpg + 3) / 4)));
 }
 
-// Chunk output. Up to N = 128 the forward forms the score blocks once per group and
-// runs the per-head kernel; at N = 256 (C fragments too large for its registers)
-// and for the fp32 recompute of the gradient pass, the 16-row kernel.
+// Chunk output. The forward runs the per-head kernel on the score blocks formed by
+// the chunk-state launch; the fp32 recompute of the gradient pass (which forms no
+// score blocks) runs the 16-row kernel.
 template <int N, int Q, bool F32OUT>
 void launch_out(const SSDK &k, int64_t nq, hipStream_t s) {
-    if constexpr (N <= 128 && !F32OUT) {
+    if constexpr (!F32OUT) {
         const unsigned rounded = (unsigned)((nq + 7) / 8 * 8);
         hipLaunchKernelGGL((ssd_out_head_kernel<N, Q>), dim3(rounded * (unsigned)k.H), dim3(Q), 0, s, k, nq);
     } else {
@@ -1094,7 +1094,7 @@ void launch_nq(const SSDK &k, int batch, hipStream_t s) {
     const int64_t nq = (int64_t)batch * k.nc;            // (batch, chunk) pairs
     // chunk states, and (up to N = 128) the score blocks of the output kernel in extra workgroups
     const unsigned cs_blocks = chunk_state_blocks(k, nq);
-    const unsigned sc_blocks = N <= 128 ? (unsigned)((nq + 7) / 8 * 8 * k.G) : 0u;
+    const unsigned sc_blocks = (unsigned)((nq + 7) / 8 * 8 * k.G);
     hipLaunchKernelGGL((ssd_chunk_state_kernel<N, Q, 0>), dim3(cs_blocks + sc_blocks), dim3(kThreads), 0, s, k, nq,
                        (int)sc_blocks);
     const int64_t total = (int64_t)batch * k.H * kP * N / 4;
