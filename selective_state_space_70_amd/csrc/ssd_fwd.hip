@@ -446,9 +446,9 @@ struct OutCfg {
 template <int N, int Q>
 constexpr int out_split() { return Q == 256 && N <= 128 ? 2 : 1; }
 
-// F32OUT: write the pre-gate output (C S + D x) in fp32 to y32 instead of the gated
-// bf16 y (the recompute the gradient pass needs for dz).
-template <int N, int Q, bool F32OUT>
+// It writes the pre-gate output (C S + D x) in fp32 to y32: the recompute the
+// gradient pass needs for dz (the forward's gated bf16 y comes from ssd_out_head).
+template <int N, int Q>
 __global__ __launch_bounds__((Q * 4 / out_split<N, Q>()), (out_split<N, Q>() == 2 ? 4 : 2))
 void ssd_chunk_out_kernel(const SSDK p, int nhg, int64_t nq) {
     constexpr int HG = OutCfg<N>::HG;
@@ -750,19 +750,8 @@ void ssd_chunk_out_kernel(const SSDK p, int nhg, int64_t nq) {
         }
     }
 
-    // y = Y + D x, gated by silu(z); z is fetched for every head at once. Each
-    // head's tile then goes through the wave's own LDS rows so that a lane writes
-    // rows of 8 bf16.
-    u32x4 zreg[HG][2];
-    if (!F32OUT && p.z && live) {
-#pragma unroll
-        for (int j = 0; j < HG; ++j)
-#pragma unroll
-            for (int rr = 0; rr < 2; ++rr) {
-                const int t = std::min(t0 + rr * 8 + (lane >> 3), T - 1), h = std::min(h0 + j, hend - 1);
-                zreg[j][rr] = *(const u32x4 *)(p.z + (((int64_t)b * p.L + t_base + t) * p.H + h) * kP + (lane & 7) * 8);
-            }
-    }
+    // y32 = Y + D x. Each head's tile goes through the wave's own LDS rows so that a
+    // lane writes rows of 8 fp32.
     __syncthreads();                                   // every wave is done with the B block
     if (!live) return;                                 // uniform; no barrier follows
 #pragma unroll
@@ -780,23 +769,10 @@ void ssd_chunk_out_kernel(const SSDK p, int nhg, int64_t nq) {
             const int t = t0 + row;
             const f32x4 o0 = *(const f32x4 *)&Ot[wv][row][c8];
             const f32x4 o1 = *(const f32x4 *)&Ot[wv][row][c8 + 4];
-            if (F32OUT && t < T) {
+            if (t < T) {
                 float *dst = p.y32 + (((int64_t)b * p.L + t_base + t) * p.H + h) * kP + c8;
                 *(f32x4 *)dst = o0;
                 *(f32x4 *)(dst + 4) = o1;
-            } else if (t < T) {
-                const float o[8] = {o0[0], o0[1], o0[2], o0[3], o1[0], o1[1], o1[2], o1[3]};
-                u32x4 outv;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    float y0 = o[2 * e], y1 = o[2 * e + 1];
-                    if (p.z) {
-                        y0 *= silu_f32(bf16_lo(zreg[j][rr][e]));
-                        y1 *= silu_f32(bf16_hi(zreg[j][rr][e]));
-                    }
-                    outv[e] = pack_bf16(y0, y1);
-                }
-                *(u32x4 *)(p.y + (((int64_t)b * p.L + t_base + t) * p.H + h) * kP + c8) = outv;
             }
         }
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -1076,23 +1052,24 @@ unsigned chunk_state_blocks(const SSDK &k, int64_t nq) {
 // Chunk output. The forward runs the per-head kernel on the score blocks formed by
 // the chunk-state launch; the fp32 recompute of the gradient pass (which forms no
 // score blocks) runs the 16-row kernel.
-template <int N, int Q, bool F32OUT>
+template <int N, int Q>
 void launch_out(const SSDK &k, int64_t nq, hipStream_t s) {
-    if constexpr (!F32OUT) {
-        const unsigned rounded = (unsigned)((nq + 7) / 8 * 8);
-        hipLaunchKernelGGL((ssd_out_head_kernel<N, Q>), dim3(rounded * (unsigned)k.H), dim3(Q), 0, s, k, nq);
-    } else {
-        const int nhg = (k.hpg + OutCfg<N>::HG - 1) / OutCfg<N>::HG;
-        const int64_t nblocks = (nq + 7) / 8 * 8 * (k.G * nhg * out_split<N, Q>());
-        hipLaunchKernelGGL((ssd_chunk_out_kernel<N, Q, F32OUT>), dim3((unsigned)nblocks),
-                           dim3(Q * 4 / out_split<N, Q>()), 0, s, k, nhg, nq);
-    }
+    const unsigned rounded = (unsigned)((nq + 7) / 8 * 8);
+    hipLaunchKernelGGL((ssd_out_head_kernel<N, Q>), dim3(rounded * (unsigned)k.H), dim3(Q), 0, s, k, nq);
+}
+
+template <int N, int Q>
+void launch_recompute_out(const SSDK &k, int64_t nq, hipStream_t s) {
+    const int nhg = (k.hpg + OutCfg<N>::HG - 1) / OutCfg<N>::HG;
+    const int64_t nblocks = (nq + 7) / 8 * 8 * (k.G * nhg * out_split<N, Q>());
+    hipLaunchKernelGGL((ssd_chunk_out_kernel<N, Q>), dim3((unsigned)nblocks), dim3(Q * 4 / out_split<N, Q>()), 0, s,
+                       k, nhg, nq);
 }
 
 template <int N, int Q>
 void launch_nq(const SSDK &k, int batch, hipStream_t s) {
     const int64_t nq = (int64_t)batch * k.nc;            // (batch, chunk) pairs
-    // chunk states, and (up to N = 128) the score blocks of the output kernel in extra workgroups
+    // chunk states, and the score blocks of the output kernel in extra workgroups
     const unsigned cs_blocks = chunk_state_blocks(k, nq);
     const unsigned sc_blocks = (unsigned)((nq + 7) / 8 * 8 * k.G);
     hipLaunchKernelGGL((ssd_chunk_state_kernel<N, Q, 0>), dim3(cs_blocks + sc_blocks), dim3(kThreads), 0, s, k, nq,
@@ -1100,7 +1077,7 @@ void launch_nq(const SSDK &k, int batch, hipStream_t s) {
     const int64_t total = (int64_t)batch * k.H * kP * N / 4;
     hipLaunchKernelGGL(ssd_state_pass_kernel<true>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
                        k, N, total);
-    launch_out<N, Q, false>(k, nq, s);
+    launch_out<N, Q>(k, nq, s);
 }
 
 template <int N>
@@ -1123,7 +1100,7 @@ void recompute_nq(const SSDK &k, int batch, int what, hipStream_t s) {
         hipLaunchKernelGGL(ssd_state_pass_kernel<false>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
                            k, N, total);
     } else if (what == 1) {   // fp32 pre-gate output
-        launch_out<N, Q, true>(k, nq, s);
+        launch_recompute_out<N, Q>(k, nq, s);
     } else {                  // adjoint aggregates (exp(cs_t) weights)
         hipLaunchKernelGGL((ssd_chunk_state_kernel<N, Q, 2>), cs_grid, dim3(kThreads), 0, s, k, nq, 0);
     }
