@@ -29,7 +29,7 @@ ssm_status scan_launch(const ssm_scan_args &a, const ScanPlan &plan, hipStream_t
         k.A = a.A; k.bias = a.delta_bias; k.Dskip = a.Dskip; k.h0 = a.h0;
         k.y = a.y; k.h_final = a.h_final;
         k.agg = plan.chunks > 1 ? (float *)((char *)a.workspace + plan.agg_offset) : nullptr;
-        k.pre = plan.chunks > 1 ? (float *)((char *)a.workspace + plan.pre_offset) : nullptr;
+        k.pre = plan.chunks > kWalkChunks ? (float *)((char *)a.workspace + plan.pre_offset) : nullptr;
         k.L = a.seqlen; k.chunk_len = plan.chunk_len; k.D = (int32_t)a.dim;
         k.batch = (int32_t)a.batch; k.chunks = (int32_t)plan.chunks;
         k.dblocks = (int32_t)((a.dim + 63) / 64);

@@ -401,6 +401,9 @@ __device__ __forceinline__ float pow_uniform(float r, int m) {
 // it depends on h0, so a caller that learns h0 later (another device's share of
 // the sequence) can still run the apply pass with it.
 constexpr int kPrefixSeg = 8;
+// Up to this many chunks the apply pass composes the chunk maps itself (at most
+// kWalkChunks - 1 per wave) and no prefix pass runs.
+constexpr int kWalkChunks = 24;
 
 template <int N>
 __global__ __launch_bounds__(64 * kPrefixSeg) void scan_prefix_kernel(const ScanK p) {
@@ -476,7 +479,7 @@ __global__ __launch_bounds__(64 * kPrefixSeg) void scan_prefix_kernel(const Scan
 
 // Pass 2: every chunk from its entering state, with readout, gate and store; the
 // last chunk writes h_final.
-template <typename T, int N, bool HAS_Z, bool FAST, bool SP>
+template <typename T, int N, bool HAS_Z, bool FAST, bool SP, bool WALK>
 __device__ __forceinline__ void scan_chunk(const ScanK &p, const Chan<N> &c, int chain, int k, int b,
                                            int dc, bool act) {
     const int t0 = (int)((int64_t)k * p.chunk_len);
@@ -485,7 +488,27 @@ __device__ __forceinline__ void scan_chunk(const ScanK &p, const Chan<N> &c, int
     float h[N];
 #pragma unroll
     for (int n = 0; n < N; ++n) h[n] = p.h0 ? p.h0[ci * N + n] : 0.0f;
-    if (k > 0) {
+    if (WALK && k > 0) {
+        // few chunks, no prefix pass: the maps of chunks 0..k-1 applied in order,
+        // h <- P_j o h + S_j, from the aggregates (k - 1 < kWalkChunks)
+        const float *ag = p.agg + (size_t)chain * (p.chunks - 1) * (N + 1) * 64 + threadIdx.x;
+        for (int j = 0; j < k; ++j) {
+            const float *a = ag + (size_t)j * (N + 1) * 64;
+            float sj[N];
+#pragma unroll
+            for (int n = 0; n < N; ++n) sj[n] = a[n * 64];
+            const float dj = a[N * 64];
+            float P[N];
+            if constexpr (FAST) {
+                powers<N>(dj, P);
+            } else {
+#pragma unroll
+                for (int n = 0; n < N; ++n) P[n] = fast_exp2(c.Al2[n] * dj);
+            }
+#pragma unroll
+            for (int n = 0; n < N; ++n) h[n] = fmaf(P[n], h[n], sj[n]);
+        }
+    } else if (!WALK && k > 0) {
         // the composed map of chunks 0..k-1 applied to h0: h = Pp o h0 + Sp
         const float *pr = p.pre + ((size_t)chain * (p.chunks - 1) + (k - 1)) * (N + 1) * 64 + threadIdx.x;
         float sp[N];
@@ -515,7 +538,9 @@ __device__ __forceinline__ void scan_chunk(const ScanK &p, const Chan<N> &c, int
     }
 }
 
-template <typename T, int N, bool HAS_Z, bool SP>
+// WALK: the call has too few chunks for a prefix pass (p.pre is null), and each
+// wave composes the maps of the chunks before its own.
+template <typename T, int N, bool HAS_Z, bool SP, bool WALK>
 __global__ __launch_bounds__(64) void scan_main_kernel(const ScanK p) {
     const ChainSlot slot = chain_slot(p.batch * p.dblocks, p.chunks);
     if (!slot.valid) return;
@@ -526,9 +551,9 @@ __global__ __launch_bounds__(64) void scan_main_kernel(const ScanK p) {
     const Chan<N> c = load_chan<N>(p, dc);
     // wave-uniform choice of the exact fast path
     if (__all(row_is_geometric<N>(p.A + (int64_t)dc * N)))
-        scan_chunk<T, N, HAS_Z, true, SP>(p, c, slot.chain, slot.pos, b, dc, act);
+        scan_chunk<T, N, HAS_Z, true, SP, WALK>(p, c, slot.chain, slot.pos, b, dc, act);
     else
-        scan_chunk<T, N, HAS_Z, false, SP>(p, c, slot.chain, slot.pos, b, dc, act);
+        scan_chunk<T, N, HAS_Z, false, SP, WALK>(p, c, slot.chain, slot.pos, b, dc, act);
 }
 
 template <typename T, int N, bool SP>
@@ -537,15 +562,21 @@ ssm_status launch_typed(const ScanK &k, hipStream_t s, int passes) {
     if (k.chunks > 1 && (passes & 1)) {
         hipLaunchKernelGGL((scan_chunk_state_kernel<T, N, SP>), dim3(chain_grid(chains, k.chunks - 1)),
                            dim3(64), 0, s, k);
-        const int nseg = std::min(kPrefixSeg, std::max(1, (k.chunks - 1 + 15) / 16));
-        hipLaunchKernelGGL((scan_prefix_kernel<N>), dim3(chain_grid(chains, N + 1)), dim3(64 * nseg), 0, s, k);
+        if (k.pre) {
+            const int nseg = std::min(kPrefixSeg, std::max(1, (k.chunks - 1 + 15) / 16));
+            hipLaunchKernelGGL((scan_prefix_kernel<N>), dim3(chain_grid(chains, N + 1)), dim3(64 * nseg), 0, s, k);
+        }
     }
     if (!(passes & 2)) return SSM_OK;
     const int grid = chain_grid(chains, k.chunks);
-    if (k.z)
-        hipLaunchKernelGGL((scan_main_kernel<T, N, true, SP>), dim3(grid), dim3(64), 0, s, k);
-    else
-        hipLaunchKernelGGL((scan_main_kernel<T, N, false, SP>), dim3(grid), dim3(64), 0, s, k);
+    const bool walk = k.pre == nullptr;                   // also a single chunk: nothing to compose
+    if (k.z) {
+        if (walk) hipLaunchKernelGGL((scan_main_kernel<T, N, true, SP, true>), dim3(grid), dim3(64), 0, s, k);
+        else hipLaunchKernelGGL((scan_main_kernel<T, N, true, SP, false>), dim3(grid), dim3(64), 0, s, k);
+    } else {
+        if (walk) hipLaunchKernelGGL((scan_main_kernel<T, N, false, SP, true>), dim3(grid), dim3(64), 0, s, k);
+        else hipLaunchKernelGGL((scan_main_kernel<T, N, false, SP, false>), dim3(grid), dim3(64), 0, s, k);
+    }
     return SSM_OK;
 }
 
