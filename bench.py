@@ -54,10 +54,10 @@ ALU_PEAK_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12   # non-packed fp32 VALU issue slo
 # plain 256 MiB device copy (FETCH x2.0, WRITE x1.0). "valu": SQ_INSTS_VALU per
 # dispatch (wave instructions; 64 lane slots each).
 COUNTERS = {
-    # long-context scan, apply kernel: FETCH_SIZE 864062 KiB, WRITE_SIZE 524416 KiB
+    # long-context scan, apply kernel: FETCH_SIZE 864175 KiB, WRITE_SIZE 524416 KiB
     # per dispatch (12 dispatches), copy calibration FETCH x2.0 (131085 KiB read for
     # a 256 MiB copy), WRITE x1.0; SQ_INSTS_VALU 3.688e8 per dispatch
-    ("S4", "231b4c6bc4d563c9"): {"traffic": 864062 * 1024 * 2 + 524416 * 1024, "valu": 368799488},
+    ("S4", "dae4e3f7dfb79270"): {"traffic": 864175 * 1024 * 2 + 524416 * 1024, "valu": 368799488},
 }
 METRIC = "scan effective HBM GB/s (% of peak) + Gelem/s over B·L·D·N"
 
