@@ -102,6 +102,14 @@ __device__ __forceinline__ void split8(const f32x4 &a, const f32x4 &b, u32x4 &hi
 }
 
 // ---------------------------------------------------------------- LDS staging
+// Natural-layout tiles written by block_both / block_split_both (B, C, dyc and Gout
+// rows) hold element (row R, column j) at column j ^ nsw(R). The 16 lanes that write
+// rows 4 rg + i of one column group at once then cover 8 bank groups instead of 2
+// (rows 4 apart of a 16-byte-aligned padded row fall on two). Every read of these
+// tiles applies the same XOR; it keeps 8-column groups whole, so 16-byte fragment
+// reads stay contiguous.
+__device__ __forceinline__ int nsw(int row) { return ((row >> 3) & 7) << 3; }
+
 // One 4 x 8 block of a bf16 tile (rows 4 rg .. +3 at row stride rs, columns gcol ..
 // +7) through a buffer resource (rows past its range read as 0), written to LDS in
 // natural layout nat[row][lcol ..] and/or transposed tr[lcol + c][perm_s(row)].
@@ -112,7 +120,7 @@ __device__ __forceinline__ void block_both(rsrc_t r, int64_t rs, int rg, int gco
     for (int i = 0; i < 4; ++i) v[i] = load16(r, (uint32_t)(((rg * 4 + i) * rs + gcol) * 2));
     if (nat) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) *(u32x4 *)&nat[(rg * 4 + i) * ld + lcol] = v[i];
+        for (int i = 0; i < 4; ++i) *(u32x4 *)&nat[(rg * 4 + i) * ld + (lcol ^ nsw(rg * 4 + i))] = v[i];
     }
     if (tr) store_transposed(v, tr, ldt, lcol, perm_s(rg * 4));
 }
@@ -130,8 +138,8 @@ __device__ __forceinline__ void block_split_both(const float *src, int64_t rs, i
     if (nat_hi) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            *(u32x4 *)&nat_hi[(rg * 4 + i) * ld + cg * 8] = hi[i];
-            *(u32x4 *)&nat_lo[(rg * 4 + i) * ld + cg * 8] = lo[i];
+            *(u32x4 *)&nat_hi[(rg * 4 + i) * ld + ((cg * 8) ^ nsw(rg * 4 + i))] = hi[i];
+            *(u32x4 *)&nat_lo[(rg * 4 + i) * ld + ((cg * 8) ^ nsw(rg * 4 + i))] = lo[i];
         }
     }
     if (tr_hi) {
@@ -392,7 +400,9 @@ __global__ __launch_bounds__(kThreads, N > 128 ? 1 : 2) void ssd_bwd_row_kernel(
             if (!diag || u <= wv) {
 #pragma unroll
                 for (int kk = 0; kk < KN; ++kk)
-                    cb[u] = mfma16x16x32(as_bf16x8(*(const u32x4 *)&Bn[(16 * u + r16) * LDB + 32 * kk + 8 * kb]), cfr[kk], cb[u]);
+                    cb[u] = mfma16x16x32(
+                        as_bf16x8(*(const u32x4 *)&Bn[(16 * u + r16) * LDB + ((32 * kk + 8 * kb) ^ nsw(16 * u + r16))]),
+                        cfr[kk], cb[u]);
             }
         }
 #pragma unroll
@@ -491,7 +501,8 @@ __global__ __launch_bounds__(kThreads, N > 128 ? 1 : 2) void ssd_bwd_row_kernel(
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
                 tmp[nt][i] *= e;
-                s = fmaf(to_f32(Cn[(wv * 16 + 4 * kb + i) * LDB + 16 * nt + r16]), tmp[nt][i], s);
+                const int R = wv * 16 + 4 * kb + i;
+                s = fmaf(to_f32(Cn[R * LDB + ((16 * nt + r16) ^ nsw(R))]), tmp[nt][i], s);
             }
             vp[i] = row16_sum(s);
         }
@@ -640,7 +651,9 @@ __global__ __launch_bounds__(kThreads, N > 128 ? 1 : 2) void ssd_bwd_col_kernel(
             if (!diag || u >= wv) {
 #pragma unroll
                 for (int kk = 0; kk < KN; ++kk)
-                    cb[u] = mfma16x16x32(as_bf16x8(*(const u32x4 *)&Cn[(16 * u + r16) * LDB + 32 * kk + 8 * kb]), bfr[kk], cb[u]);
+                    cb[u] = mfma16x16x32(
+                        as_bf16x8(*(const u32x4 *)&Cn[(16 * u + r16) * LDB + ((32 * kk + 8 * kb) ^ nsw(16 * u + r16))]),
+                        bfr[kk], cb[u]);
             }
         }
 #pragma unroll
@@ -658,7 +671,9 @@ __global__ __launch_bounds__(kThreads, N > 128 ? 1 : 2) void ssd_bwd_col_kernel(
                 if (!diag || u >= wv) {
 #pragma unroll
                     for (int kk = 0; kk < 2; ++kk) {
-                        dx4[u] = mfma16x16x32(as_bf16x8(*(const u32x4 *)&Dhj[(16 * u + r16) * LDX + 32 * kk + 8 * kb]), xf[kk], dx4[u]);
+                        dx4[u] = mfma16x16x32(
+                            as_bf16x8(*(const u32x4 *)&Dhj[(16 * u + r16) * LDX + ((32 * kk + 8 * kb) ^ nsw(16 * u + r16))]),
+                            xf[kk], dx4[u]);
                         if constexpr (SPLIT)
                             dx4[u] = mfma16x16x32(as_bf16x8(*(const u32x4 *)&Dlj[(16 * u + r16) * LDX + 32 * kk + 8 * kb]), xf[kk], dx4[u]);
                     }
@@ -743,7 +758,9 @@ __global__ __launch_bounds__(kThreads, N > 128 ? 1 : 2) void ssd_bwd_col_kernel(
             for (int q = 0; q < 4; ++q)
 #pragma unroll
                 for (int kk = 0; kk < KN; ++kk)
-                    xi[q] = mfma16x16x32(bfr[kk], as_bf16x8(*(const u32x4 *)&G1[(16 * q + r16) * LDB + 32 * kk + 8 * kb]), xi[q]);
+                    xi[q] = mfma16x16x32(
+                        bfr[kk], as_bf16x8(*(const u32x4 *)&G1[(16 * q + r16) * LDB + ((32 * kk + 8 * kb) ^ nsw(16 * q + r16))]),
+                        xi[q]);
             // x_s Gout: rows s, n = 16nt + r16
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
