@@ -785,8 +785,8 @@ void ssd_chunk_out_kernel(const SSDK p, int nhg, int64_t nq) {
 // The head's x (transposed: the B operand of Y += M X) and entering state are
 // staged in LDS once (the state's buffer then holds the decay table); the score
 // blocks come from L2 (formed by the chunk-state launch). At chunk 256 three
-// workgroups fit a CU (52 KiB of LDS, <= 168 VGPRs), so loads of some overlap the
-// arithmetic of others.
+// workgroups fit a CU up to N = 128 (52 KiB of LDS, <= 168 VGPRs) and two at
+// N = 256 (68 KiB), so loads of some overlap the arithmetic of others.
 //
 // Decays as in the 16-row kernel, with r = 32 tau - 1 the step before a tile:
 // blocks of s before the tile take M = G o (w_s dt_s), w_s = exp(cs_r - cs_s)
