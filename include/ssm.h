@@ -196,8 +196,9 @@ ssm_status selective_scan_fwd_noalloc(const ssm_scan_args *args, hipStream_t str
  *   dx, ddelta: (batch, L, D) dtype; dz: (batch, L, D) dtype, required iff z != NULL;
  *   dB, dC: (batch, L, G, N) fp32; dA: (D, N) fp32; dDskip, ddelta_bias: (D) fp32,
  *   nullable (not computed); dh0: (batch, D, N) fp32, nullable.
- * dB, dC, dA, dDskip and ddelta_bias are sums of float atomics: equal to the last
- * bits only up to summation order, run to run.
+ * Every gradient is deterministic: the sums over channels (dB, dC), chunks and
+ * batch rows (dA, dDskip, ddelta_bias) are formed from stored partials in a fixed
+ * order, so repeated calls give identical bits.
  */
 typedef struct ssm_scan_bwd_args {
     int64_t batch, seqlen, dim, dstate;   /* B, L, D, N */

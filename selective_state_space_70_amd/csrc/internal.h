@@ -92,6 +92,9 @@ struct ScanBwdPlan {
     size_t hin_offset;    // fp32 [B][chunk][D][N]
     size_t uin_offset;    // fp32 [B][chunk][D][N]
     size_t dApart_offset; // fp32 [B][chunk][D][N]: per-chunk shares of dA
+    size_t dDpart_offset; // fp32 [B][chunk][D]: per-chunk shares of dDskip
+    size_t dbpart_offset; // fp32 [B][chunk][D]: per-chunk shares of ddelta_bias
+    size_t bcpart_offset; // fp32 [B][L][waves along D][2N]: per-wave sums of dB_t, dC_t
     size_t bytes;
 };
 ScanBwdPlan scan_bwd_plan(const ssm_scan_bwd_args &a);

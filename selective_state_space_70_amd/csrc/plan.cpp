@@ -77,7 +77,12 @@ ScanBwdPlan scan_bwd_plan(const ssm_scan_bwd_args &a) {
     const size_t st = (size_t)a.batch * pl.chunks * a.dim * N * sizeof(float);
     pl.uin_offset = pl.hin_offset + up(st);
     pl.dApart_offset = pl.uin_offset + up(st);
-    pl.bytes = pl.dApart_offset + up(st);
+    const size_t cd = (size_t)a.batch * pl.chunks * a.dim * sizeof(float);
+    pl.dDpart_offset = pl.dApart_offset + up(st);
+    pl.dbpart_offset = pl.dDpart_offset + up(cd);
+    pl.bcpart_offset = pl.dbpart_offset + up(cd);
+    const int64_t waves = (a.dim + 64 * 16 / N - 1) / (64 * 16 / N);   // main-kernel waves along D
+    pl.bytes = pl.bcpart_offset + up((size_t)a.batch * a.seqlen * waves * 2 * N * sizeof(float));
     return pl;
 }
 

@@ -16,13 +16,14 @@
 //      h0 carried through the maps h -> exp(A sum dt) o h + S; the adjoint entering
 //      chunk c from the right is dh_final carried back through u -> exp(A sum dt) o u
 //      + Q. Both are stored per (batch, chunk, channel, n);
-//   3. bwd_main: per (chunk, 32/16/8 channels), lane = (channel, n) so that one
-//      lane holds one scalar state: the chunk is recomputed forward with every h_t
-//      kept in registers, then the adjoint sweeps it backwards. Sums over n (dx,
-//      dt, the readout) are DPP row reductions and permlane swaps; sums over
-//      channels (dB, dC, shared by the channels of a group) are permlane swaps,
-//      then LDS and global float atomics. Per-(t, channel) work (softplus, gate,
-//      dz, dx, ddelta) is done once per pair through LDS, not per lane.
+//   3. bwd_main: per (chunk, 64 * 16 / N channels), one wave, lane = (channel, 16
+//      states) so that the sums over n are in-lane, as in the forward scan: the
+//      chunk is walked forwards from its entering state, then recomputed in
+//      sub-blocks whose states stay in registers and swept backwards with the
+//      adjoint. dB and dC (sums over the channels of a group) are reduced across
+//      the wave by a butterfly and stored per (step, wave);
+//   4. fixed-order sums of the per-wave and per-chunk partials (dB, dC, dA, dDskip,
+//      ddelta_bias), so that every gradient is deterministic.
 #include <algorithm>
 #include <cstdio>
 
@@ -33,7 +34,6 @@ namespace ssm {
 namespace {
 
 constexpr int kChunk = kScanBwdChunk;   // steps per chunk (states of a chunk live in VGPRs)
-constexpr int kWaves = 8;    // waves per workgroup of the main kernel
 
 struct BwdK {
     const void *x, *delta, *z, *Bm, *Cm, *dy;
@@ -45,54 +45,17 @@ struct BwdK {
     float *hin;      // [batch][chunk][D][N]: state entering each chunk
     float *uin;      // [batch][chunk][D][N]: adjoint entering each chunk from the right
     float *dApart;   // [batch][chunk][D][N]: each chunk's share of dA
+    float *dDpart;   // [batch][chunk][D]: each chunk's share of dDskip
+    float *dbpart;   // [batch][chunk][D]: each chunk's share of ddelta_bias
+    float *bcpart;   // [batch][L][nblk][2N]: per (step, wave) sums of dB_t (n < N), dC_t (n >= N)
     int64_t L;
     int32_t D, batch, nch, dblocks, softplus, G, dpg;
+    int32_t nblk;    // waves of the main kernel along D: ceil(D / (64 * 16 / N))
 };
 
-// ---------------------------------------------------------------- cross-lane sums
-template <int CTRL>
-__device__ __forceinline__ float ror(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
-}
-// sum over the 16 lanes of a DPP row, in every lane of the row (rotations 1, 2, 4, 8)
-__device__ __forceinline__ float row_sum(float v) {
-    v += ror<0x121>(v);
-    v += ror<0x122>(v);
-    v += ror<0x124>(v);
-    v += ror<0x128>(v);
-    return v;
-}
-// Row-swap sums: v_permlane16_swap exchanges the odd rows of its first operand
-// with the even rows of its second, v_permlane32_swap the upper half of the first
-// with the lower half of the second. With v as both operands the two results add
-// up to v[l] + v[l ^ 16] (v[l] + v[l ^ 32]) in every lane. The two results are
-// copied out as integers before use: reinterpreting the second element of the
-// returned pair in place reads the first one with this compiler.
-__device__ __forceinline__ float pl16_sum(float v) {
-    const uint32_t u = __builtin_bit_cast(uint32_t, v);
-    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-    const uint32_t a = r[0], b = r[1];
-    return __uint_as_float(a) + __uint_as_float(b);
-}
-__device__ __forceinline__ float pl32_sum(float v) {
-    const uint32_t u = __builtin_bit_cast(uint32_t, v);
-    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    const uint32_t a = r[0], b = r[1];
-    return __uint_as_float(a) + __uint_as_float(b);
-}
-// sum over the N lanes of one channel (lane = channel * N + n), in every lane
-template <int N>
-__device__ __forceinline__ float sum_n(float v) {
-    v = row_sum(v);
-    if constexpr (N >= 32) v = pl16_sum(v);
-    if constexpr (N >= 64) v = pl32_sum(v);
-    return v;
-}
-// sum over the 64 / N channels of a wave at equal n, in every lane
-template <int N>
-__device__ __forceinline__ float sum_ch(float v) {
-    if constexpr (N <= 16) v = pl16_sum(v);
-    if constexpr (N <= 32) v = pl32_sum(v);
+// the same value, opaque to the optimiser (no instruction is emitted)
+__device__ __forceinline__ float opaque_f32(float v) {
+    asm volatile("" : "+v"(v));
     return v;
 }
 
@@ -283,247 +246,412 @@ __global__ __launch_bounds__(64) void bwd_carry_kernel(const BwdK p) {
 }
 
 // ---------------------------------------------------------------- 3. main
-typedef __attribute__((ext_vector_type(4))) float f32x4;
-typedef __attribute__((ext_vector_type(2))) float f32x2;
+// Lane = (channel, slice of 16 states): a lane keeps 16 states of one channel in
+// VGPRs (N / 16 lanes per channel), as the forward scan does, so the sums over n
+// (the readout, sum_n g B, sum_n A g a h) are in-lane. Per chunk:
+//   * a forward walk from the entering state stores the state at every kSeg-th
+//     step in LDS;
+//   * then, last segment first, each sub-block of kSB steps is recomputed from
+//     the state before it (the upper sub-block of a segment first walks the lower
+//     one), its states kept in registers, and swept backwards with the adjoint.
+// The recompute forms dC_t's per-lane terms dyc h_t, the readout and dz; the sweep
+// forms g_t, dx, ddelta, dA and dB_t's terms g dt x. dB_t and dC_t are sums over
+// the channels of a group: each is reduced across the wave's lanes by a butterfly
+// (permlane swaps across rows, DPP within rows) and stored as one partial per
+// (step, wave); bwd_reduce_bc_kernel adds the partials of a group in a fixed order.
+// dA, dDskip and ddelta_bias are stored per chunk and summed the same way, so
+// every gradient is deterministic.
+constexpr int kSL = 16;                  // states per lane
+constexpr int kSB = 8;                   // steps per sub-block
+constexpr int kSeg = 2 * kSB;            // steps between stored states
+constexpr int kNSeg = kChunk / kSeg;     // stored states per chunk (the first is the entering state)
+static_assert(kChunk % kSeg == 0, "segments tile the chunk");
 
-// Forward recompute and adjoint sweep of one chunk for lane (channel ch, state n).
-// Steps past the end of the sequence were staged with dt = dt x = dyc = 0: they
-// leave h and the adjoint unchanged and contribute nothing, so every chunk runs
-// all kChunk steps without guards. A first forward pass keeps h at the start of
-// each sub-block of SB steps; each sub-block, last first, is then recomputed with
-// its states and decays kept in registers and swept backwards. This holds 2 SB
-// values per lane instead of kChunk, which leaves room for more waves per SIMD.
-constexpr int kSB = 16;   // steps per sub-block of the backward sweep
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
+}
+// a[l] + a[l ^ 32] in lanes l < 32, b[l] + b[l ^ 32] in lanes l >= 32
+__device__ __forceinline__ float swap32_sum(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    const uint32_t u = r[0], w = r[1];
+    return __uint_as_float(u) + __uint_as_float(w);
+}
+// a[l] + a[l ^ 16] in even rows of 16 lanes, b[l] + b[l ^ 16] in odd rows
+__device__ __forceinline__ float swap16_sum(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    const uint32_t u = r[0], w = r[1];
+    return __uint_as_float(u) + __uint_as_float(w);
+}
+// Within rows of 16: a[l] + a[l + k] where lane bit k is 0, b[l] + b[l - k] where it
+// is 1 (row_shl:k reads lane l + k, row_shr:k lane l - k).
+template <int K>
+__device__ __forceinline__ float row_pair_sum(float a, float b, int lane) {
+    const float lo = a + dpp<0x100 + K>(a);
+    const float hi = b + dpp<0x110 + K>(b);
+    return (lane & K) ? hi : lo;
+}
 
-template <int N, int CPG>
-__device__ __forceinline__ void sweep(const f32x4 (*pre)[CPG], const f32x2 (*BC)[N], float (*post)[kChunk][CPG],
-                                      f32x2 (*bcw)[kSB][64], f32x2 (*bcacc)[N], int ch, int n, int lane, int wv,
-                                      float An, float hin, float &v, float &dAacc) {
-    constexpr int SB = kSB, NSB = kChunk / SB;
-    const float A2 = An * kLog2e;
-    float ck[NSB];
-    float h = hin;
+// Sum of x[0..15] over the lanes of the wave that hold the same slice (the
+// channels of the wave). Each halving step keeps, per lane, the half of the values
+// selected by one lane bit and adds the partner lane's copy of that half: bits 5
+// and 4 by permlane swaps, bits 3 and 2 within rows. Lane l returns value
+// (l >> 2) & 15; lane bits 1 and 0, where they index channels, are added last.
+template <int LPC>
+__device__ __forceinline__ float chan_sum16(const float (&x)[kSL], int lane) {
+    float y[8], z[4], w[2];
 #pragma unroll
-    for (int sb = 0; sb < NSB; ++sb) {
-        ck[sb] = h;
+    for (int i = 0; i < 8; ++i) y[i] = swap32_sum(x[i], x[i + 8]);
 #pragma unroll
-        for (int j = 0; j < SB; ++j) {
-            const int i = sb * SB + j;
-            const f32x4 q = pre[i][ch];
-            h = fmaf(fast_exp2(q[0] * A2), h, q[1] * BC[i][n][0]);
-            if (j % 8 == 7) __builtin_amdgcn_sched_barrier(0);   // bound how far loads run ahead
+    for (int i = 0; i < 4; ++i) z[i] = swap16_sum(y[i], y[i + 4]);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) w[i] = row_pair_sum<8>(z[i], z[i + 2], lane);
+    float u = row_pair_sum<4>(w[0], w[1], lane);
+    if constexpr (LPC <= 2) u += dpp<0x4E>(u);   // quad_perm [2,3,0,1]: lane bit 1
+    if constexpr (LPC == 1) u += dpp<0xB1>(u);   // quad_perm [1,0,3,2]: lane bit 0
+    return u;
+}
+
+// sum over the LPC lanes of one channel, in each of them
+template <int LPC>
+__device__ __forceinline__ float slice_sum(float v) {
+    if constexpr (LPC >= 2) v += dpp<0xB1>(v);
+    if constexpr (LPC >= 4) v += dpp<0x4E>(v);
+    return v;
+}
+
+template <typename T, int N, bool HAS_Z, bool FAST>
+__device__ __forceinline__ void bwd_chunk(const BwdK &p, float (*ck)[kSL][64], const int lane, const int b,
+                                          const int c, const int blk) {
+    constexpr int LPC = N / kSL;                 // lanes per channel
+    constexpr int CPW = 64 / LPC;                // channels per wave
+    const int s = lane % LPC;                    // slice: states 16 s .. 16 s + 15
+    const int d = blk * CPW + lane / LPC;
+    const bool act = d < p.D;
+    const int dc = act ? d : p.D - 1;
+    const int t0 = c * kChunk;
+    const int tlast = (int)p.L - 1;
+    const int g = __builtin_amdgcn_readfirstlane(blk * CPW) / p.dpg;   // the wave's group
+    const int GN = p.G * N;
+    const T *Brow = (const T *)p.Bm + ((int64_t)b * p.L * p.G + g) * N;
+    const T *Crow = (const T *)p.Cm + ((int64_t)b * p.L * p.G + g) * N;
+    const float *Arow = p.A + (int64_t)dc * N;
+    const float A0 = Arow[0], A0l2 = A0 * kLog2e;
+    float Al2[kSL];
+    if constexpr (!FAST) {
+#pragma unroll
+        for (int i = 0; i < kSL; ++i) Al2[i] = Arow[s * kSL + i] * kLog2e;
+    }
+    const float bias = p.bias ? p.bias[dc] : 0.0f;
+    const float dsk = p.Dskip ? p.Dskip[dc] : 0.0f;
+
+    // (b, t, d) streams as raw buffers over batch row b: the time row is a uniform
+    // byte offset, the lane adds its channel's offset. Stores from lanes that do not
+    // own their channel's output (past D, or slices > 0) go to an offset past the
+    // buffer, which the hardware drops.
+    const int64_t base = (int64_t)b * p.L * p.D;
+    const uint32_t bytes = (uint32_t)(p.L * p.D * (int64_t)sizeof(T));
+    const rsrc_t xr = make_rsrc((const T *)p.x + base, bytes);
+    const rsrc_t dr = make_rsrc((const T *)p.delta + base, bytes);
+    const rsrc_t zr = make_rsrc(HAS_Z ? (const T *)p.z + base : (const T *)p.x + base, bytes);
+    const rsrc_t yr = make_rsrc((const T *)p.dy + base, bytes);
+    const rsrc_t dxr = make_rsrc((T *)p.dx + base, bytes);
+    const rsrc_t ddr = make_rsrc((T *)p.ddelta + base, bytes);
+    const rsrc_t dzr = make_rsrc(HAS_Z ? (T *)p.dz + base : (T *)p.dx + base, bytes);
+    const uint32_t lo = (uint32_t)dc * sizeof(T);
+    const uint32_t rowb = (uint32_t)p.D * sizeof(T);
+    const uint32_t st_off = (act && s == 0) ? lo : 0x80000000u;
+    // butterfly results: lane l holds state 16 s + ((l >> 2) & 15)
+    const int wn = s * kSL + ((lane >> 2) & 15);
+    float *bcp = p.bcpart + (size_t)blk * 2 * N + wn;   // + ((b L + t) nblk) 2N
+
+    auto decays = [&](float dt, float (&a)[kSL]) {
+        if constexpr (FAST) {
+            powers_of<kSL>(fast_exp2(dt * A0l2), a);
+            if constexpr (LPC > 1) {   // states 16 s + i decay by r^(16 s) r^(i+1)
+                const float r16 = a[kSL - 1];
+                float bs = (s & 1) ? r16 : 1.0f;
+                if constexpr (LPC == 4) bs *= (s & 2) ? r16 * r16 : 1.0f;
+#pragma unroll
+                for (int i = 0; i < kSL; ++i) a[i] *= bs;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < kSL; ++i) a[i] = fast_exp2(dt * Al2[i]);
+        }
+    };
+    // The row offset passes through an empty asm statement at every use: loads from the
+    // constant address space are invariant, and the recompute's and the sweep's loads
+    // of one row would otherwise be merged and held in SGPRs across the sub-block.
+    auto load_row16 = [&](const T *row, int t, float (&v)[kSL]) {
+        const int64_t off = (int64_t)opaque_u32((uint32_t)min(t, tlast)) * GN;
+        if constexpr (LPC == 1) {
+            SharedRow<T, kSL>::load(row + off, v);
+        } else {
+            const T *q = row + off + s * kSL;
+#pragma unroll
+            for (int i = 0; i < kSL; ++i) v[i] = to_f32(q[i]);
+        }
+    };
+    // No branch inside a step: a branch would split the step into blocks across which
+    // the invariant row loads get hoisted (and the compiler turns a select of an
+    // expensive value into one). softplus is always formed and picked by a bit mask
+    // the optimiser cannot see through; steps past the sequence multiply by zero.
+    uint32_t spm = p.softplus ? 0xffffffffu : 0u;
+    asm volatile("" : "+v"(spm));
+    auto pick_sp = [&](float on, float off) {
+        return __uint_as_float((__float_as_uint(on) & spm) | (__float_as_uint(off) & ~spm));
+    };
+    auto step_dt = [&](T draw, float vm) {
+        const float v = to_f32(draw) + bias;
+        return pick_sp(softplus_f32(v), v) * vm;
+    };
+    // x, delta of the 8 steps from tb (clamped into the sequence)
+    auto load8 = [&](int tb, T (&xs)[kSB], T (&ds)[kSB]) {
+        const uint32_t rb = opaque_u32(rowb);
+#pragma unroll
+        for (int u = 0; u < kSB; ++u) {
+            const uint32_t so = (uint32_t)min(tb + u, tlast) * rb;
+            buf_load(xr, lo, so, xs[u]);
+            buf_load(dr, lo, so, ds[u]);
+        }
+    };
+    // h <- the state after the 8 steps from tb
+    auto adv8 = [&](int tb, const T (&xs)[kSB], const T (&ds)[kSB], float (&h)[kSL]) {
+#pragma unroll
+        for (int u = 0; u < kSB; ++u) {
+            const int t = (int)opaque_u32((uint32_t)(tb + u));
+            const float dt = step_dt(ds[u], t <= tlast ? 1.0f : 0.0f);
+            const float dtx = act ? dt * to_f32(xs[u]) : 0.0f;
+            float a[kSL], Bv[kSL];
+            decays(dt, a);
+            load_row16(Brow, t, Bv);
+#pragma unroll
+            for (int i = 0; i < kSL; ++i) h[i] = fmaf(a[i], h[i], dtx * Bv[i]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    float h[kSL], v[kSL], dA[kSL];
+    {
+        const int64_t si = (((int64_t)b * p.nch + c) * p.D + dc) * N + s * kSL;
+#pragma unroll
+        for (int i = 0; i < kSL; ++i) {
+            h[i] = p.hin[si + i];
+            v[i] = p.uin[si + i];
+            dA[i] = 0.0f;
         }
     }
+    float dD = 0.0f, dbias = 0.0f;
+
+    // ---- forward walk: the state at the start of every segment, into LDS
+    {
+        T xa[kSB], da[kSB], xb[kSB], db[kSB];
+        load8(t0, xa, da);
 #pragma unroll
-    for (int sb = NSB - 1; sb >= 0; --sb) {
-        __builtin_amdgcn_sched_barrier(0);
-        float hs[SB], as[SB];
-        float hh = ck[sb];
+        for (int i = 0; i < kSL; ++i) ck[0][i][lane] = h[i];
 #pragma unroll
-        for (int j = 0; j < SB; ++j) {
-            const int i = sb * SB + j;
-            const f32x4 q = pre[i][ch];
-            as[j] = fast_exp2(q[0] * A2);
-            hh = fmaf(as[j], hh, q[1] * BC[i][n][0]);
-            hs[j] = hh;
-            if (j % 8 == 7) __builtin_amdgcn_sched_barrier(0);
+        for (int k = 1; k < kNSeg; ++k) {
+            load8(t0 + kSeg * (k - 1) + kSB, xb, db);
+            adv8(t0 + kSeg * (k - 1), xa, da, h);
+            if (k + 1 < kNSeg) load8(t0 + kSeg * k, xa, da);
+            adv8(t0 + kSeg * (k - 1) + kSB, xb, db, h);
+#pragma unroll
+            for (int i = 0; i < kSL; ++i) ck[k][i][lane] = h[i];
         }
+    }
+
+    // ---- one sub-block of kSB steps from tb, entered with state hs: recompute, then sweep
+    auto sub_block = [&](int tb, const float (&hs)[kSL]) {
+        float sdt[kSB], sx[kSB], sdyc[kSB], spd[kSB], sdz[kSB];
+        {
+            T xs[kSB], ds[kSB], zs[kSB], ys[kSB];
+            const uint32_t rb = opaque_u32(rowb);
 #pragma unroll
-        for (int j = SB - 1; j >= 0; --j) {
-            const int i = sb * SB + j;
-            const f32x4 q = pre[i][ch];                   // dt, dt x, dyc, x
-            const f32x2 bc = BC[i][n];                    // B, C
-            const float gq = fmaf(bc[1], q[2], v);        // g_t
-            const float hp = j > 0 ? hs[j - 1] : ck[sb];  // h_{t-1}
-            const float gah = gq * as[j] * hp;
-            dAacc = fmaf(gah, q[0], dAacc);
-            const float yc = sum_n<N>(bc[1] * hs[j]);
-            const float sB = sum_n<N>(gq * bc[0]);
-            const float sA = sum_n<N>(An * gah);
-            if (n == 0) {
-                post[0][i][ch] = yc;
-                post[1][i][ch] = sB;
-                post[2][i][ch] = sA;
+            for (int u = 0; u < kSB; ++u) {
+                const uint32_t so = (uint32_t)min(tb + u, tlast) * rb;
+                buf_load(xr, lo, so, xs[u]);
+                buf_load(dr, lo, so, ds[u]);
+                buf_load(yr, lo, so, ys[u]);
+                if constexpr (HAS_Z) buf_load(zr, lo, so, zs[u]);
             }
-            bcw[wv][j][lane] = f32x2{gq * q[1], q[2] * hs[j]};   // this lane's terms of dB_t, dC_t
-            v = as[j] * gq;                               // the adjoint term for t-1
-            if (j % 4 == 0) __builtin_amdgcn_sched_barrier(0);
-        }
-        // sum the waves' shares of this sub-block (no atomics)
-        __syncthreads();
-        for (int q = threadIdx.x; q < SB * N; q += kWaves * 64) {
-            const int j = q / N, nn = q % N;
-            f32x2 acc = f32x2{0.f, 0.f};
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w)
-#pragma unroll
-                for (int c2 = 0; c2 < 64 / N; ++c2) acc += bcw[w][j][c2 * N + nn];
-            bcacc[sb * SB + j][nn] = acc;
+            for (int u = 0; u < kSB; ++u) {
+                const float vm = tb + u <= tlast ? 1.0f : 0.0f;
+                const float vv = to_f32(ds[u]) + bias;
+                sdt[u] = pick_sp(softplus_f32(vv), vv) * vm;
+                spd[u] = pick_sp(sigmoid_f32(vv), 1.0f);
+                sx[u] = to_f32(xs[u]);
+                const float dyv = to_f32(ys[u]);
+                float dyc = dyv;
+                sdz[u] = 0.0f;
+                if constexpr (HAS_Z) {
+                    const float zv = to_f32(zs[u]), sg = sigmoid_f32(zv);
+                    dyc = dyv * zv * sg;
+                    sdz[u] = dyv * sg * fmaf(zv, 1.0f - sg, 1.0f);
+                }
+                sdyc[u] = dyc * (act ? vm : 0.0f);
+            }
         }
-        __syncthreads();
+        // recompute: states of the sub-block, dC terms, readout, dz
+        float hb[kSB + 1][kSL];
+        float dCs[kSB];   // per step: this wave's share of dC_t (stored by the sweep)
+#pragma unroll
+        for (int i = 0; i < kSL; ++i) hb[0][i] = hs[i];
+#pragma unroll
+        for (int u = 0; u < kSB; ++u) {
+            const int t = (int)opaque_u32((uint32_t)(tb + u));   // per-step offsets formed in the step
+            float a[kSL], Bv[kSL], Cv[kSL];
+            decays(sdt[u], a);
+            load_row16(Brow, t, Bv);
+            load_row16(Crow, t, Cv);
+            const float dtx = act ? sdt[u] * sx[u] : 0.0f;
+            float dcv[kSL], yc = 0.0f;
+#pragma unroll
+            for (int i = 0; i < kSL; ++i) {
+                hb[u + 1][i] = fmaf(a[i], hb[u][i], dtx * Bv[i]);
+                dcv[i] = sdyc[u] * hb[u + 1][i];
+                yc = fmaf(Cv[i], hb[u + 1][i], yc);
+            }
+            dCs[u] = chan_sum16<LPC>(dcv, lane);
+            const bool valid = t <= tlast;
+            dD = fmaf(sdyc[u], sx[u], dD);
+            if constexpr (HAS_Z) {
+                yc = slice_sum<LPC>(yc);
+                const float dzv = sdz[u] * fmaf(dsk, sx[u], yc);
+                if constexpr (sizeof(T) == 2)
+                    buf_store(dzr, valid ? st_off : 0x80000000u, (uint32_t)min(t, tlast) * rowb, f32_to_bf16(dzv));
+                else
+                    buf_store(dzr, valid ? st_off : 0x80000000u, (uint32_t)min(t, tlast) * rowb, dzv);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // sweep backwards
+#pragma unroll
+        for (int u = kSB - 1; u >= 0; --u) {
+            const int t = (int)opaque_u32((uint32_t)(tb + u));   // per-step offsets formed in the step
+            float a[kSL], Bv[kSL], Cv[kSL];
+            // the decays are formed again (not kept from the recompute: 16 registers per step)
+            const float dt = opaque_f32(sdt[u]), dyc = sdyc[u];
+            decays(dt, a);
+            load_row16(Brow, t, Bv);
+            load_row16(Crow, t, Cv);
+            const float dtx = act ? dt * sx[u] : 0.0f;
+            float dbv[kSL], sB = 0.0f, sA = 0.0f, sM = 0.0f;
+#pragma unroll
+            for (int i = 0; i < kSL; ++i) {
+                const float gq = fmaf(Cv[i], dyc, v[i]);   // g_t
+                sB = fmaf(gq, Bv[i], sB);
+                dbv[i] = gq * dtx;
+                const float w = gq * a[i];
+                const float m = w * hb[u][i];               // g_t a_t h_{t-1}
+                dA[i] = fmaf(dt, m, dA[i]);
+                if constexpr (FAST) {
+                    sA = fmaf((float)(i + 1), m, sA);
+                    if constexpr (LPC > 1) sM += m;
+                } else {
+                    sA = fmaf(Al2[i], m, sA);
+                }
+                v[i] = w;                                   // adjoint term carried to t - 1
+            }
+            if constexpr (FAST) {
+                if constexpr (LPC > 1) sA = fmaf((float)(s * kSL), sM, sA);
+                sA *= A0;
+            } else {
+                sA *= kLn2;
+            }
+            sB = slice_sum<LPC>(sB);
+            sA = slice_sum<LPC>(sA);
+            const float dBt = chan_sum16<LPC>(dbv, lane);
+            const bool valid = t <= tlast;
+            // Steps past the sequence have zero shares and store them to the last row
+            // before its own shares are stored (the sweep runs backwards in time), so
+            // no branch is needed. Lanes that hold the same value store the same value.
+            float *q = bcp + ((int64_t)b * p.L + min(t, tlast)) * p.nblk * 2 * N;
+            q[0] = dBt;
+            q[N] = dCs[u];
+            const float dxv = fmaf(dt, sB, dsk * dyc);
+            const float ddl = fmaf(sx[u], sB, sA) * spd[u];
+            dbias += valid ? ddl : 0.0f;
+            const uint32_t so = (uint32_t)min(t, tlast) * rowb, vo = valid ? st_off : 0x80000000u;
+            if constexpr (sizeof(T) == 2) {
+                buf_store(dxr, vo, so, f32_to_bf16(dxv));
+                buf_store(ddr, vo, so, f32_to_bf16(ddl));
+            } else {
+                buf_store(dxr, vo, so, dxv);
+                buf_store(ddr, vo, so, ddl);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // ---- backward over the segments, last first
+#pragma unroll 1
+    for (int k = kNSeg - 1; k >= 0; --k) {
+        const int ts = t0 + kSeg * k;
+        if (ts > tlast) continue;                       // uniform: segment past the sequence
+        float hs[kSL];
+#pragma unroll
+        for (int i = 0; i < kSL; ++i) hs[i] = ck[k][i][lane];
+        if (ts + kSB <= tlast) {                        // the upper sub-block has steps
+            T xs[kSB], ds[kSB];
+            load8(ts, xs, ds);
+            float hm[kSL];
+#pragma unroll
+            for (int i = 0; i < kSL; ++i) hm[i] = hs[i];
+            adv8(ts, xs, ds, hm);
+            sub_block(ts + kSB, hm);
+        }
+        sub_block(ts, hs);
+    }
+
+    if (act && c == 0 && p.dh0) {
+        float *o = p.dh0 + ((int64_t)b * p.D + d) * N + s * kSL;
+#pragma unroll
+        for (int i = 0; i < kSL; ++i) o[i] = v[i];
+    }
+    if (act) {
+        float *o = p.dApart + (((int64_t)b * p.nch + c) * p.D + d) * N + s * kSL;
+#pragma unroll
+        for (int i = 0; i < kSL; ++i) o[i] = dA[i];
+        if (s == 0) {
+            const int64_t q = ((int64_t)b * p.nch + c) * p.D + d;
+            p.dDpart[q] = dD;
+            p.dbpart[q] = dbias;
+        }
     }
 }
 
-template <typename T, int N, bool HAS_Z>
-__global__ __launch_bounds__(kWaves * 64, 2) void bwd_main_kernel(const BwdK p) {
-    constexpr int CPW = 64 / N;               // channels per wave
-    constexpr int CPG = kWaves * CPW;         // channels per workgroup
-    constexpr int NT = kWaves * 64;
-    __shared__ f32x4 pre[kChunk][CPG];        // per (step, channel): dt, dt x, dyc, x
-    __shared__ float post[3][kChunk][CPG];    // readout C.h, sum_n g B, sum_n A g a h_prev
-    __shared__ f32x2 BC[kChunk][N];           // B_t[n], C_t[n]
-    __shared__ f32x2 bcw[kWaves][kSB][64];    // per lane: its dB_t, dC_t terms (one sub-block)
-    __shared__ f32x2 bcacc[kChunk][N];        // all channels of the workgroup
+// One launch per path: a wave whose 64 channels all have progression rows of A runs
+// in the FAST launch, any other wave in the general one (each launch's waves of the
+// other kind return at once), so each path gets its own register allocation.
+template <typename T, int N, bool HAS_Z, bool FAST>
+__global__ __launch_bounds__(64, FAST ? 2 : 1) void bwd_main_kernel(const BwdK p) {
+    __shared__ float ck[kNSeg][kSL][64];          // the state at the start of each segment
+    const int lane = threadIdx.x;
+    const int blk = blockIdx.x, c = blockIdx.y, b = blockIdx.z;
+    constexpr int CPW = 64 * kSL / N;
+    const int d = blk * CPW + lane / (N / kSL);
+    const int dc = d < p.D ? d : p.D - 1;
+    if (__all(geometric_row<N>(p.A + (int64_t)dc * N)) != FAST) return;   // wave-uniform
+    bwd_chunk<T, N, HAS_Z, FAST>(p, ck, lane, b, c, blk);
+}
 
-    const int c = blockIdx.y, b = blockIdx.z;
-    const int d0 = blockIdx.x * CPG;
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int t0 = c * kChunk;
-    const int nt = (int)std::min<int64_t>(kChunk, p.L - t0);   // steps in this chunk
-    const int g = d0 / p.dpg;                 // every channel of the workgroup is in one group
-    const T *X = (const T *)p.x, *Dl = (const T *)p.delta, *Z = (const T *)p.z, *DY = (const T *)p.dy;
-
-    // ---- stage per-step rows and per-(step, channel) quantities. Every load of a thread
-    // is issued before any is used, with indices clamped into the chunk and D and an
-    // absent bias read from A, so the latencies overlap instead of adding up per entry.
-    constexpr int BCI = kChunk * N / NT;          // (step, n) entries per thread
-    constexpr int PRI = kChunk * CPG / NT;        // (step, channel) pairs per thread
-    static_assert(kChunk * N % NT == 0 && kChunk * CPG % NT == 0 && NT % CPG == 0, "entries tile the workgroup");
-    {
-        T braw[BCI], craw[BCI];
-#pragma unroll
-        for (int k = 0; k < BCI; ++k) {
-            const int e = tid + k * NT, i = std::min(e / N, nt - 1), nn = e % N;
-            const int64_t r = (((int64_t)b * p.L + t0 + i) * p.G + g) * N + nn;
-            braw[k] = ((const T *)p.Bm)[r];
-            craw[k] = ((const T *)p.Cm)[r];
-        }
-        const int cc = tid % CPG, dd = d0 + cc, ddc = std::min(dd, p.D - 1);
-        const float *biasp = p.bias ? p.bias : p.A;
-        const float biasv = biasp[ddc];
-        const float bias = p.bias ? biasv : 0.0f;
-        T xr[PRI], dr[PRI], yr[PRI], zr[PRI];
-#pragma unroll
-        for (int k = 0; k < PRI; ++k) {
-            const int i = std::min(tid / CPG + k * (NT / CPG), nt - 1);
-            const int64_t e = ((int64_t)b * p.L + t0 + i) * p.D + ddc;
-            xr[k] = X[e];
-            dr[k] = Dl[e];
-            yr[k] = DY[e];
-            if constexpr (HAS_Z) zr[k] = Z[e];
-        }
-#pragma unroll
-        for (int k = 0; k < BCI; ++k) {
-            const int e = tid + k * NT, i = e / N, nn = e % N;
-            BC[i][nn] = i < nt ? f32x2{to_f32(braw[k]), to_f32(craw[k])} : f32x2{0.f, 0.f};
-        }
-#pragma unroll
-        for (int k = 0; k < PRI; ++k) {
-            const int i = tid / CPG + k * (NT / CPG);
-            f32x4 q = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (i < nt && dd < p.D) {
-                const float xv = to_f32(xr[k]);
-                const float vv = to_f32(dr[k]) + bias;
-                const float dt = p.softplus ? softplus_f32(vv) : vv;
-                float dyc = to_f32(yr[k]);
-                if constexpr (HAS_Z) dyc *= silu_f32(to_f32(zr[k]));
-                q = f32x4{dt, dt * xv, dyc, xv};
-            }
-            pre[i][cc] = q;
-        }
-    }
-    __syncthreads();
-
-    // ---- lane = (channel, n): recompute the chunk forward, then the adjoint backwards
-    const int ch = wv * CPW + lane / N, n = lane % N;
-    const int d = d0 + ch;
-    const bool act = d < p.D;
-    const int dc = act ? d : p.D - 1;
-    const float An = p.A[(int64_t)dc * N + n];
-    const int64_t si = (((int64_t)b * p.nch + c) * p.D + dc) * N + n;
-    const float hin = p.hin[si];
-    float v = p.uin[si];
-    float dAacc = 0.0f;
-    sweep<N, CPG>(pre, BC, post, bcw, bcacc, ch, n, lane, wv, An, hin, v, dAacc);
-    if (act) {
-        if (c == 0 && p.dh0) p.dh0[((int64_t)b * p.D + d) * N + n] = v;
-        // this chunk's share of dA, summed over (batch, chunk) by bwd_reduce_dA
-        p.dApart[(((int64_t)b * p.nch + c) * p.D + d) * N + n] = dAacc;
-    }
-    __syncthreads();
-
-    // ---- per (step, channel): dx, ddelta, dz; per-channel and per-row sums
-    // Each thread takes EPI pairs of one channel. Every global value they need is loaded
-    // before the first store: the memory counter completes in order, so a load placed
-    // after a store could not be waited for without waiting for the store. Indices are
-    // clamped into the chunk and D, and absent parameters read a valid stand-in (A), so
-    // the loads are unconditional; the values of pairs outside are not used.
-    constexpr int EPI = kChunk * CPG / NT;
-    static_assert(kChunk * CPG % NT == 0 && NT % CPG == 0, "pairs tile the workgroup");
-    {
-        // The empty asm makes the epilogue's indices opaque, so their 64-bit addresses are
-        // formed here rather than hoisted above the sweep, where they were spilled and each
-        // load then waited on a scratch reload.
-        int et = tid;
-        asm volatile("" : "+v"(et));
-        const int cc = et % CPG, dd = d0 + cc, ddc = std::min(dd, p.D - 1);
-        const float *dskp = p.Dskip ? p.Dskip : p.A, *biasp = p.bias ? p.bias : p.A;
-        const float dskv = dskp[ddc], biasv = biasp[ddc];
-        const float dsk = p.Dskip ? dskv : 0.0f, bias = p.bias ? biasv : 0.0f;
-        float dlv[EPI], zvv[EPI], dyv[EPI];
-#pragma unroll
-        for (int k = 0; k < EPI; ++k) {
-            const int i = std::min(et / CPG + k * (NT / CPG), nt - 1);
-            const int64_t e = ((int64_t)b * p.L + t0 + i) * p.D + ddc;
-            dlv[k] = to_f32(Dl[e]);
-            if constexpr (HAS_Z) {
-                zvv[k] = to_f32(Z[e]);
-                dyv[k] = to_f32(DY[e]);
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < EPI; ++k) {
-            const int i = et / CPG + k * (NT / CPG);
-            if (i < nt && dd < p.D) {
-                const int64_t e = ((int64_t)b * p.L + t0 + i) * p.D + dd;
-                const f32x4 pr = pre[i][cc];
-                const float dt = pr[0], dyc = pr[2], xv = pr[3];
-                const float sB = post[1][i][cc], sA = post[2][i][cc];
-                float gdl = fmaf(xv, sB, sA);                     // d dt
-                if (p.softplus) gdl *= sigmoid_f32(dlv[k] + bias);
-                store_val((T *)p.dx + e, fmaf(dyc, dsk, dt * sB));
-                store_val((T *)p.ddelta + e, gdl);
-                if constexpr (HAS_Z) {
-                    const float zv = zvv[k], s = sigmoid_f32(zv);
-                    const float dzf = dyv[k] * s * fmaf(zv, 1.0f - s, 1.0f);
-                    store_val((T *)p.dz + e, dzf * fmaf(dsk, xv, post[0][i][cc]));
-                }
-                post[1][i][cc] = dyc * xv;                       // this pair's dDskip and dbias terms
-                post[2][i][cc] = gdl;
-            } else {
-                post[1][i][cc] = 0.0f;
-                post[2][i][cc] = 0.0f;
-            }
-        }
-    }
-    __syncthreads();
-    for (int q = tid; q < nt * N; q += NT) {
-        const int i = q / N, nn = q % N;
-        const f32x2 acc = bcacc[i][nn];
-        const int64_t r = (((int64_t)b * p.L + t0 + i) * p.G + g) * N + nn;
-        atomicAdd(&p.dB[r], acc[0]);
-        atomicAdd(&p.dC[r], acc[1]);
-    }
-    for (int q = tid; q < CPG; q += NT) {
-        if (d0 + q < p.D) {
-            float sd = 0.0f, sb = 0.0f;
-            for (int i = 0; i < nt; ++i) {
-                sd += post[1][i][q];
-                sb += post[2][i][q];
-            }
-            if (p.dDskip) atomicAdd(&p.dDskip[d0 + q], sd);
-            if (p.dbias) atomicAdd(&p.dbias[d0 + q], sb);
-        }
+// dB, dC of (batch, step, group): the partials of the group's waves, added in order
+__global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(const float *part, float *dB, float *dC, int64_t total,
+                                                            int nblk, int G, int bpg, int N) {
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += stride) {
+        const int two_n = 2 * N;
+        const int idx = (int)(i % two_n);
+        const int64_t rest = i / two_n;
+        const int g = (int)(rest % G);
+        const int64_t row = rest / G;              // b L + t
+        const float *q = part + (row * nblk + (int64_t)g * bpg) * two_n + idx;
+        float acc = 0.0f;
+        for (int k = 0; k < bpg; ++k) acc += q[(int64_t)k * two_n];
+        const int n = idx < N ? idx : idx - N;
+        (idx < N ? dB : dC)[(row * G + g) * N + n] = acc;
     }
 }
 
@@ -559,21 +687,35 @@ void fill(float *p, int64_t n, hipStream_t s, const float *src = nullptr) {
 template <typename T, int N>
 void launch_bwd(const BwdK &k, hipStream_t s) {
     const int chains = k.batch * k.dblocks;
-    constexpr int CPG = kWaves * (64 / N);
     if (k.z) {
         hipLaunchKernelGGL((bwd_aggregate_kernel<T, N, true>), dim3(chains, k.nch), dim3(64), 0, s, k);
     } else {
         hipLaunchKernelGGL((bwd_aggregate_kernel<T, N, false>), dim3(chains, k.nch), dim3(64), 0, s, k);
     }
     hipLaunchKernelGGL((bwd_carry_kernel<N>), dim3(chains), dim3(64), 0, s, k);
-    const dim3 grid((unsigned)((k.D + CPG - 1) / CPG), (unsigned)k.nch, (unsigned)k.batch);
-    if (k.z)
-        hipLaunchKernelGGL((bwd_main_kernel<T, N, true>), grid, dim3(kWaves * 64), 0, s, k);
-    else
-        hipLaunchKernelGGL((bwd_main_kernel<T, N, false>), grid, dim3(kWaves * 64), 0, s, k);
+    const dim3 grid((unsigned)k.nblk, (unsigned)k.nch, (unsigned)k.batch);
+    if (k.z) {
+        hipLaunchKernelGGL((bwd_main_kernel<T, N, true, true>), grid, dim3(64), 0, s, k);
+        hipLaunchKernelGGL((bwd_main_kernel<T, N, true, false>), grid, dim3(64), 0, s, k);
+    } else {
+        hipLaunchKernelGGL((bwd_main_kernel<T, N, false, true>), grid, dim3(64), 0, s, k);
+        hipLaunchKernelGGL((bwd_main_kernel<T, N, false, false>), grid, dim3(64), 0, s, k);
+    }
+    const int64_t parts = (int64_t)k.batch * k.nch;
     const int64_t dn = (int64_t)k.D * N;
     hipLaunchKernelGGL(bwd_reduce_dA_kernel, dim3((unsigned)((dn + 255) / 256)), dim3(256), 0, s, k.dApart, k.dA,
-                       dn, (int64_t)k.batch * k.nch);
+                       dn, parts);
+    const unsigned dblk = (unsigned)((k.D + 255) / 256);
+    if (k.dDskip)
+        hipLaunchKernelGGL(bwd_reduce_dA_kernel, dim3(dblk), dim3(256), 0, s, k.dDpart, k.dDskip, (int64_t)k.D, parts);
+    if (k.dbias)
+        hipLaunchKernelGGL(bwd_reduce_dA_kernel, dim3(dblk), dim3(256), 0, s, k.dbpart, k.dbias, (int64_t)k.D, parts);
+    constexpr int CPW = 64 * kSL / N;
+    const int bpg = k.G > 1 ? k.dpg / CPW : k.nblk;
+    const int64_t total = (int64_t)k.batch * k.L * k.G * 2 * N;
+    const int64_t blocks = std::min<int64_t>((total + 255) / 256, 1 << 20);
+    hipLaunchKernelGGL(bwd_reduce_bc_kernel, dim3((unsigned)blocks), dim3(256), 0, s, k.bcpart, k.dB, k.dC, total,
+                       k.nblk, k.G, bpg, N);
 }
 
 }  // namespace
@@ -583,14 +725,12 @@ ssm_status scan_bwd_launch(const ssm_scan_bwd_args &a, const ScanBwdPlan &plan, 
     if (a.batch == 0) return SSM_OK;
     (void)hipGetLastError();
     const int64_t N = a.dstate;
-    // outputs accumulated with atomics start from zero
-    if (a.seqlen == 0) fill(a.dA, a.dim * N, s);
-    fill(a.dDskip, a.dim, s);
-    fill(a.ddelta_bias, a.dim, s);
     const int64_t G = a.ngroups > 1 ? a.ngroups : 1;
-    fill(a.dB, a.batch * a.seqlen * G * N, s);
-    fill(a.dC, a.batch * a.seqlen * G * N, s);
     if (a.seqlen == 0) {
+        // no step: the parameter gradients are zero and dh0 is dh_final
+        fill(a.dA, a.dim * N, s);
+        fill(a.dDskip, a.dim, s);
+        fill(a.ddelta_bias, a.dim, s);
         fill(a.dh0, a.batch * a.dim * N, s, a.dh_final);
     } else {
         BwdK k{};
@@ -604,11 +744,15 @@ ssm_status scan_bwd_launch(const ssm_scan_bwd_args &a, const ScanBwdPlan &plan, 
         k.hin = (float *)(ws + plan.hin_offset);
         k.uin = (float *)(ws + plan.uin_offset);
         k.dApart = (float *)(ws + plan.dApart_offset);
+        k.dDpart = (float *)(ws + plan.dDpart_offset);
+        k.dbpart = (float *)(ws + plan.dbpart_offset);
+        k.bcpart = (float *)(ws + plan.bcpart_offset);
         k.L = a.seqlen; k.D = (int32_t)a.dim; k.batch = (int32_t)a.batch; k.nch = (int32_t)plan.chunks;
         k.dblocks = (int32_t)((a.dim + 63) / 64);
         k.softplus = a.delta_softplus ? 1 : 0;
         k.G = (int32_t)G;
         k.dpg = (int32_t)(a.dim / G);
+        k.nblk = (int32_t)((a.dim + 64 * kSL / N - 1) / (64 * kSL / N));
         const bool bf = a.dtype == SSM_BF16;
         switch (a.dstate) {
             case 16: bf ? launch_bwd<uint16_t, 16>(k, s) : launch_bwd<float, 16>(k, s); break;
