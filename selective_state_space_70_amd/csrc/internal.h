@@ -94,7 +94,8 @@ struct ScanBwdPlan {
     size_t dApart_offset; // fp32 [B][chunk][D][N]: per-chunk shares of dA
     size_t dDpart_offset; // fp32 [B][chunk][D]: per-chunk shares of dDskip
     size_t dbpart_offset; // fp32 [B][chunk][D]: per-chunk shares of ddelta_bias
-    size_t bcpart_offset; // fp32 [B][L][waves along D][2N]: per-wave sums of dB_t, dC_t
+    size_t bcpart_offset; // fp32 [B L + 1][waves along D][2N]: per-wave sums of dB_t, dC_t (+ a spare row)
+    size_t fast_offset;   // int32 [ceil(D / 64)]: which path each 64 channels take
     size_t bytes;
 };
 ScanBwdPlan scan_bwd_plan(const ssm_scan_bwd_args &a);

@@ -82,7 +82,9 @@ ScanBwdPlan scan_bwd_plan(const ssm_scan_bwd_args &a) {
     pl.dbpart_offset = pl.dDpart_offset + up(cd);
     pl.bcpart_offset = pl.dbpart_offset + up(cd);
     const int64_t waves = (a.dim + 64 * 16 / N - 1) / (64 * 16 / N);   // main-kernel waves along D
-    pl.bytes = pl.bcpart_offset + up((size_t)a.batch * a.seqlen * waves * 2 * N * sizeof(float));
+    // one (step, wave) row per step and batch row, plus a spare row
+    pl.fast_offset = pl.bcpart_offset + up(((size_t)a.batch * a.seqlen + 1) * waves * 2 * N * sizeof(float));
+    pl.bytes = pl.fast_offset + up((size_t)((a.dim + 63) / 64) * sizeof(int32_t));
     return pl;
 }
 

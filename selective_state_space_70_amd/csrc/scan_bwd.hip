@@ -47,11 +47,26 @@ struct BwdK {
     float *dApart;   // [batch][chunk][D][N]: each chunk's share of dA
     float *dDpart;   // [batch][chunk][D]: each chunk's share of dDskip
     float *dbpart;   // [batch][chunk][D]: each chunk's share of ddelta_bias
-    float *bcpart;   // [batch][L][nblk][2N]: per (step, wave) sums of dB_t (n < N), dC_t (n >= N)
+    float *bcpart;   // [batch][L][nblk][2N]: per (step, wave) sums of dB_t (n < N), dC_t (n >= N);
+                     // then one spare row that steps past the sequence store to
+    int32_t *fast;   // [dblocks]: 1 where the 64 channels' rows of A are progressions
     int64_t L;
     int32_t D, batch, nch, dblocks, softplus, G, dpg;
     int32_t nblk;    // waves of the main kernel along D: ceil(D / (64 * 16 / N))
 };
+
+// Values made opaque at this point of the program (empty asm, no instruction): what
+// produces them is computed before it.
+template <int N>
+__device__ __forceinline__ void tie16(float (&v)[N]) {
+    static_assert(N % 16 == 0, "blocks of 16");
+#pragma unroll
+    for (int i = 0; i < N; i += 16)
+        asm volatile("" : "+v"(v[i]), "+v"(v[i + 1]), "+v"(v[i + 2]), "+v"(v[i + 3]), "+v"(v[i + 4]),
+                     "+v"(v[i + 5]), "+v"(v[i + 6]), "+v"(v[i + 7]), "+v"(v[i + 8]), "+v"(v[i + 9]),
+                     "+v"(v[i + 10]), "+v"(v[i + 11]), "+v"(v[i + 12]), "+v"(v[i + 13]), "+v"(v[i + 14]),
+                     "+v"(v[i + 15]));
+}
 
 // the same value, opaque to the optimiser (no instruction is emitted)
 __device__ __forceinline__ float opaque_f32(float v) {
@@ -99,51 +114,81 @@ __device__ __forceinline__ void aggregate_chunk(const BwdK &p, int b, int dc, in
     }
     float rho = 1.0f;   // FAST: product of r over the chunk so far
     dsum = 0.0f;
+    // softplus picked by a mask the optimiser cannot see through (no branch per step)
+    uint32_t spm = p.softplus ? 0xffffffffu : 0u;
+    asm volatile("" : "+v"(spm));
     constexpr int U = 8;   // steps whose loads are issued together
+    // the next block's loads are issued before the current block computes
+    T xn[U], vn[U], yn[U], zn[U];
+    auto load_block = [&](int tb) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t e = ((int64_t)b * p.L + min(tb + u, t1 - 1)) * p.D + dc;
+            xn[u] = X[e];
+            vn[u] = Dl[e];
+            yn[u] = DY[e];
+            if constexpr (HAS_Z) zn[u] = Z[e];
+        }
+    };
+    load_block(t0);
     for (int t = t0; t < t1; t += U) {
         float xs[U], vs[U], dys[U], zs[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t e = ((int64_t)b * p.L + min(t + u, t1 - 1)) * p.D + dc;
-            xs[u] = to_f32(X[e]);
-            vs[u] = to_f32(Dl[e]);
-            dys[u] = to_f32(DY[e]);
-            zs[u] = HAS_Z ? to_f32(Z[e]) : 0.0f;
+            xs[u] = to_f32(xn[u]);
+            vs[u] = to_f32(vn[u]);
+            dys[u] = to_f32(yn[u]);
+            zs[u] = HAS_Z ? to_f32(zn[u]) : 0.0f;
         }
+        if (t + U < t1) load_block(t + U);
+        // per-step scalars of the block first (independent across steps, so their
+        // exponentials and logarithms overlap); steps past the chunk are zeroed
+        float dts[U], dtxs[U], dycs[U], rs[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            if (t + u < t1) {
-                const float v = vs[u] + bias;
-                const float dt = p.softplus ? softplus_f32(v) : v;
-                float dyc = dys[u];
-                if constexpr (HAS_Z) dyc *= silu_f32(zs[u]);
-                float Bv[N], Cv[N];
-                SharedRow<T, N>::load(Brow + (t + u) * GN, Bv);
-                SharedRow<T, N>::load(Crow + (t + u) * GN, Cv);
-                const float dtx = dt * xs[u];
-                dsum += dt;
-                if constexpr (FAST) {
-                    const float r = fast_exp2(dt * Al2[0]);
-                    rho *= r;
-                    float a[N];
-                    powers_of<N>(r, a);
-                    float q = rho * dyc;                      // rho^(n+1) dyc, built up over n
+            const float vm = t + u < t1 ? 1.0f : 0.0f;
+            const float v = vs[u] + bias;
+            const float sp = softplus_f32(v);
+            dts[u] = __uint_as_float((__float_as_uint(sp) & spm) | (__float_as_uint(v) & ~spm)) * vm;
+            float dyc = dys[u] * vm;
+            if constexpr (HAS_Z) dyc *= silu_f32(zs[u]);
+            dycs[u] = dyc;
+            dtxs[u] = dts[u] * xs[u];
+            rs[u] = FAST ? fast_exp2(dts[u] * Al2[0]) : 1.0f;
+        }
+        // then the state updates, one step (and its B, C rows in SGPRs) at a time
 #pragma unroll
-                    for (int n = 0; n < N; ++n) {
-                        S[n] = fmaf(a[n], S[n], dtx * Bv[n]);
-                        Q[n] = fmaf(Cv[n], q, Q[n]);
-                        q *= rho;
-                    }
-                } else {
+        for (int u = 0; u < U; ++u) {
+            const int tu = (int)opaque_u32((uint32_t)min(t + u, t1 - 1));
+            float Bv[N], Cv[N];
+            SharedRow<T, N>::load(Brow + (int64_t)tu * GN, Bv);
+            SharedRow<T, N>::load(Crow + (int64_t)tu * GN, Cv);
+            const float dt = dts[u], dtx = dtxs[u], dyc = dycs[u];
+            dsum += dt;
+            if constexpr (FAST) {
+                const float r = rs[u];
+                rho *= r;
+                float a[N];
+                powers_of<N>(r, a);
+                float q = rho * dyc;                      // rho^(n+1) dyc, built up over n
 #pragma unroll
-                    for (int n = 0; n < N; ++n) {
-                        const float a = fast_exp2(dt * Al2[n]);
-                        S[n] = fmaf(a, S[n], dtx * Bv[n]);
-                        R[n] *= a;
-                        Q[n] = fmaf(R[n], Cv[n] * dyc, Q[n]);
-                    }
+                for (int n = 0; n < N; ++n) {
+                    S[n] = fmaf(a[n], S[n], dtx * Bv[n]);
+                    Q[n] = fmaf(Cv[n], q, Q[n]);
+                    q *= rho;
+                }
+            } else {
+#pragma unroll
+                for (int n = 0; n < N; ++n) {
+                    const float a = fast_exp2(dt * Al2[n]);
+                    S[n] = fmaf(a, S[n], dtx * Bv[n]);
+                    R[n] *= a;
+                    Q[n] = fmaf(R[n], Cv[n] * dyc, Q[n]);
                 }
             }
+            tie16(S);
+            tie16(Q);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 }
@@ -161,7 +206,10 @@ __global__ __launch_bounds__(64) void bwd_aggregate_kernel(const BwdK p) {
     for (int n = 0; n < N; ++n) Al2[n] = p.A[(int64_t)dc * N + n] * kLog2e;
     const float bias = p.bias ? p.bias[dc] : 0.0f;
     float S[N], Q[N], dsum;
-    if (__all(geometric_row<N>(p.A + (int64_t)dc * N)))   // wave-uniform choice
+    const bool fast = __all(geometric_row<N>(p.A + (int64_t)dc * N));   // wave-uniform choice
+    // which path these 64 channels take, for the main kernels
+    if (b == 0 && c == 0 && threadIdx.x == 0) p.fast[chain] = fast ? 1 : 0;
+    if (fast)
         aggregate_chunk<T, N, HAS_Z, true>(p, b, dc, t0, t1, Al2, bias, S, Q, dsum);
     else
         aggregate_chunk<T, N, HAS_Z, false>(p, b, dc, t0, t1, Al2, bias, S, Q, dsum);
@@ -416,18 +464,24 @@ __device__ __forceinline__ void bwd_chunk(const BwdK &p, float (*ck)[kSL][64], c
             buf_load(dr, lo, so, ds[u]);
         }
     };
-    // h <- the state after the 8 steps from tb
+    // h <- the state after the 8 steps from tb: the steps' scalars first (independent
+    // across steps, so their exponentials overlap), then the updates one step at a time
     auto adv8 = [&](int tb, const T (&xs)[kSB], const T (&ds)[kSB], float (&h)[kSL]) {
+        float dts[kSB], dtxs[kSB];
+#pragma unroll
+        for (int u = 0; u < kSB; ++u) {
+            dts[u] = step_dt(ds[u], tb + u <= tlast ? 1.0f : 0.0f);
+            dtxs[u] = act ? dts[u] * to_f32(xs[u]) : 0.0f;
+        }
 #pragma unroll
         for (int u = 0; u < kSB; ++u) {
             const int t = (int)opaque_u32((uint32_t)(tb + u));
-            const float dt = step_dt(ds[u], t <= tlast ? 1.0f : 0.0f);
-            const float dtx = act ? dt * to_f32(xs[u]) : 0.0f;
             float a[kSL], Bv[kSL];
-            decays(dt, a);
+            decays(dts[u], a);
             load_row16(Brow, t, Bv);
 #pragma unroll
-            for (int i = 0; i < kSL; ++i) h[i] = fmaf(a[i], h[i], dtx * Bv[i]);
+            for (int i = 0; i < kSL; ++i) h[i] = fmaf(a[i], h[i], dtxs[u] * Bv[i]);
+            tie16(h);   // the step's arithmetic stays in the step
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -495,7 +549,6 @@ __device__ __forceinline__ void bwd_chunk(const BwdK &p, float (*ck)[kSL][64], c
         }
         // recompute: states of the sub-block, dC terms, readout, dz
         float hb[kSB + 1][kSL];
-        float dCs[kSB];   // per step: this wave's share of dC_t (stored by the sweep)
 #pragma unroll
         for (int i = 0; i < kSL; ++i) hb[0][i] = hs[i];
 #pragma unroll
@@ -513,8 +566,11 @@ __device__ __forceinline__ void bwd_chunk(const BwdK &p, float (*ck)[kSL][64], c
                 dcv[i] = sdyc[u] * hb[u + 1][i];
                 yc = fmaf(Cv[i], hb[u + 1][i], yc);
             }
-            dCs[u] = chan_sum16<LPC>(dcv, lane);
+            const float dCt = chan_sum16<LPC>(dcv, lane);
             const bool valid = t <= tlast;
+            // a step past the sequence stores to the spare row after the last batch row;
+            // lanes that hold the same value store the same value
+            bcp[(valid ? (int64_t)b * p.L + t : (int64_t)p.batch * p.L) * p.nblk * 2 * N + N] = dCt;
             dD = fmaf(sdyc[u], sx[u], dD);
             if constexpr (HAS_Z) {
                 yc = slice_sum<LPC>(yc);
@@ -524,6 +580,7 @@ __device__ __forceinline__ void bwd_chunk(const BwdK &p, float (*ck)[kSL][64], c
                 else
                     buf_store(dzr, valid ? st_off : 0x80000000u, (uint32_t)min(t, tlast) * rowb, dzv);
             }
+            tie16(hb[u + 1]);
             __builtin_amdgcn_sched_barrier(0);
         }
         // sweep backwards
@@ -564,12 +621,7 @@ __device__ __forceinline__ void bwd_chunk(const BwdK &p, float (*ck)[kSL][64], c
             sA = slice_sum<LPC>(sA);
             const float dBt = chan_sum16<LPC>(dbv, lane);
             const bool valid = t <= tlast;
-            // Steps past the sequence have zero shares and store them to the last row
-            // before its own shares are stored (the sweep runs backwards in time), so
-            // no branch is needed. Lanes that hold the same value store the same value.
-            float *q = bcp + ((int64_t)b * p.L + min(t, tlast)) * p.nblk * 2 * N;
-            q[0] = dBt;
-            q[N] = dCs[u];
+            bcp[(valid ? (int64_t)b * p.L + t : (int64_t)p.batch * p.L) * p.nblk * 2 * N] = dBt;
             const float dxv = fmaf(dt, sB, dsk * dyc);
             const float ddl = fmaf(sx[u], sB, sA) * spd[u];
             dbias += valid ? ddl : 0.0f;
@@ -581,6 +633,8 @@ __device__ __forceinline__ void bwd_chunk(const BwdK &p, float (*ck)[kSL][64], c
                 buf_store(dxr, vo, so, dxv);
                 buf_store(ddr, vo, so, ddl);
             }
+            tie16(v);
+            tie16(dA);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -631,9 +685,7 @@ __global__ __launch_bounds__(64, FAST ? 2 : 1) void bwd_main_kernel(const BwdK p
     const int lane = threadIdx.x;
     const int blk = blockIdx.x, c = blockIdx.y, b = blockIdx.z;
     constexpr int CPW = 64 * kSL / N;
-    const int d = blk * CPW + lane / (N / kSL);
-    const int dc = d < p.D ? d : p.D - 1;
-    if (__all(geometric_row<N>(p.A + (int64_t)dc * N)) != FAST) return;   // wave-uniform
+    if ((p.fast[(blk * CPW) / 64] != 0) != FAST) return;   // the aggregate kernel's choice
     bwd_chunk<T, N, HAS_Z, FAST>(p, ck, lane, b, c, blk);
 }
 
@@ -655,24 +707,42 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(const float *part, f
     }
 }
 
-// dA[d, n] = sum over (batch, chunk) of the per-chunk shares
-__global__ __launch_bounds__(256) void bwd_reduce_dA_kernel(const float *part, float *dA, int64_t dn, int64_t parts) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= dn) return;
-    constexpr int U = 8;   // independent loads in flight
-    float acc[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) acc[u] = 0.0f;
-    int64_t k = 0;
-    for (; k + U <= parts; k += U) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) acc[u] += part[(k + u) * dn + i];
+// out_j[i] = sum over k < parts of part_j[k dn_j + i] for up to three arrays j (dA, dDskip,
+// ddelta_bias from their per-(batch, chunk) shares). A block takes 32 columns; its 8 rows
+// of threads each sum every 8th share, and row 0 adds the 8 results in order.
+struct ColSums {
+    const float *part[3];
+    float *out[3];
+    int64_t dn[3];
+    int64_t parts;
+};
+constexpr int kColW = 32, kColR = 8;
+__global__ __launch_bounds__(kColW * kColR) void bwd_colsum_kernel(const ColSums cs) {
+    __shared__ float acc[kColR][kColW];
+    const int j = blockIdx.y;
+    const int cx = threadIdx.x % kColW, r = threadIdx.x / kColW;
+    const int64_t dn = cs.dn[j];
+    const int64_t i = (int64_t)blockIdx.x * kColW + cx;
+    const float *part = cs.part[j] + (i < dn ? i : 0);
+    float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+    if (i < dn) {
+        int64_t k = r;
+        for (; k + 3 * kColR < cs.parts; k += 4 * kColR) {
+            s0 += part[k * dn];
+            s1 += part[(k + kColR) * dn];
+            s2 += part[(k + 2 * kColR) * dn];
+            s3 += part[(k + 3 * kColR) * dn];
+        }
+        for (; k < cs.parts; k += kColR) s0 += part[k * dn];
     }
-    for (; k < parts; ++k) acc[0] += part[k * dn + i];
-    float sum = 0.0f;
+    acc[r][cx] = (s0 + s1) + (s2 + s3);
+    __syncthreads();
+    if (r == 0 && i < dn) {
+        float t = 0.0f;
 #pragma unroll
-    for (int u = 0; u < U; ++u) sum += acc[u];
-    dA[i] = sum;
+        for (int q = 0; q < kColR; ++q) t += acc[q][cx];
+        cs.out[j][i] = t;
+    }
 }
 
 __global__ __launch_bounds__(256) void fill_kernel(float *p, int64_t n, const float *src) {
@@ -701,15 +771,21 @@ void launch_bwd(const BwdK &k, hipStream_t s) {
         hipLaunchKernelGGL((bwd_main_kernel<T, N, false, true>), grid, dim3(64), 0, s, k);
         hipLaunchKernelGGL((bwd_main_kernel<T, N, false, false>), grid, dim3(64), 0, s, k);
     }
-    const int64_t parts = (int64_t)k.batch * k.nch;
-    const int64_t dn = (int64_t)k.D * N;
-    hipLaunchKernelGGL(bwd_reduce_dA_kernel, dim3((unsigned)((dn + 255) / 256)), dim3(256), 0, s, k.dApart, k.dA,
-                       dn, parts);
-    const unsigned dblk = (unsigned)((k.D + 255) / 256);
-    if (k.dDskip)
-        hipLaunchKernelGGL(bwd_reduce_dA_kernel, dim3(dblk), dim3(256), 0, s, k.dDpart, k.dDskip, (int64_t)k.D, parts);
-    if (k.dbias)
-        hipLaunchKernelGGL(bwd_reduce_dA_kernel, dim3(dblk), dim3(256), 0, s, k.dbpart, k.dbias, (int64_t)k.D, parts);
+    ColSums cs{};
+    int nj = 0;
+    auto add = [&](const float *part, float *out, int64_t dn) {
+        if (!out) return;
+        cs.part[nj] = part;
+        cs.out[nj] = out;
+        cs.dn[nj] = dn;
+        ++nj;
+    };
+    add(k.dApart, k.dA, (int64_t)k.D * N);
+    add(k.dDpart, k.dDskip, k.D);
+    add(k.dbpart, k.dbias, k.D);
+    cs.parts = (int64_t)k.batch * k.nch;
+    hipLaunchKernelGGL(bwd_colsum_kernel, dim3((unsigned)(((int64_t)k.D * N + kColW - 1) / kColW), nj),
+                       dim3(kColW * kColR), 0, s, cs);
     constexpr int CPW = 64 * kSL / N;
     const int bpg = k.G > 1 ? k.dpg / CPW : k.nblk;
     const int64_t total = (int64_t)k.batch * k.L * k.G * 2 * N;
@@ -747,6 +823,7 @@ ssm_status scan_bwd_launch(const ssm_scan_bwd_args &a, const ScanBwdPlan &plan, 
         k.dDpart = (float *)(ws + plan.dDpart_offset);
         k.dbpart = (float *)(ws + plan.dbpart_offset);
         k.bcpart = (float *)(ws + plan.bcpart_offset);
+        k.fast = (int32_t *)(ws + plan.fast_offset);
         k.L = a.seqlen; k.D = (int32_t)a.dim; k.batch = (int32_t)a.batch; k.nch = (int32_t)plan.chunks;
         k.dblocks = (int32_t)((a.dim + 63) / 64);
         k.softplus = a.delta_softplus ? 1 : 0;
