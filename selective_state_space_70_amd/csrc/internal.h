@@ -89,8 +89,8 @@ struct ScanBwdPlan {
     int64_t chunks;
     size_t aggF_offset;   // fp32 [chain][chunk][N+1][64]
     size_t aggR_offset;   // fp32 [chain][chunk][N][64]
-    size_t hin_offset;    // fp32 [B][chunk][D][N]
-    size_t uin_offset;    // fp32 [B][chunk][D][N]
+    size_t hin_offset;    // fp32 [B][chunk][N][D]
+    size_t uin_offset;    // fp32 [B][chunk][N][D]
     size_t dApart_offset; // fp32 [B][chunk][D][N]: per-chunk shares of dA
     size_t dDpart_offset; // fp32 [B][chunk][D]: per-chunk shares of dDskip
     size_t dbpart_offset; // fp32 [B][chunk][D]: per-chunk shares of ddelta_bias

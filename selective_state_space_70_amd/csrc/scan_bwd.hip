@@ -12,10 +12,10 @@
 //   1. bwd_aggregate: per (64 channels, chunk), lane = channel, one pass forward
 //      through the chunk: end state from zero S_c, summed step, and the adjoint
 //      aggregate Q_c = sum_s (prod_{k=t0..s} a_k) C_s dyc_s;
-//   2. bwd_carry: per channel, sequential over chunks: h entering chunk c is
+//   2. bwd_carry: per (channel, n), sequential over chunks: h entering chunk c is
 //      h0 carried through the maps h -> exp(A sum dt) o h + S; the adjoint entering
 //      chunk c from the right is dh_final carried back through u -> exp(A sum dt) o u
-//      + Q. Both are stored per (batch, chunk, channel, n);
+//      + Q. Both are stored per (batch, chunk, n, channel);
 //   3. bwd_main: per (chunk, 64 * 16 / N channels), one wave, lane = (channel, 16
 //      states) so that the sums over n are in-lane, as in the forward scan: the
 //      chunk is walked forwards from its entering state, then recomputed in
@@ -42,8 +42,8 @@ struct BwdK {
     float *dB, *dC, *dA, *dDskip, *dbias, *dh0;
     float *aggF;     // [chain][chunk][N+1][64]: end state from zero, then summed dt
     float *aggR;     // [chain][chunk][N][64]: adjoint aggregate
-    float *hin;      // [batch][chunk][D][N]: state entering each chunk
-    float *uin;      // [batch][chunk][D][N]: adjoint entering each chunk from the right
+    float *hin;      // [batch][chunk][N][D]: state entering each chunk
+    float *uin;      // [batch][chunk][N][D]: adjoint entering each chunk from the right
     float *dApart;   // [batch][chunk][D][N]: each chunk's share of dA
     float *dDpart;   // [batch][chunk][D]: each chunk's share of dDskip
     float *dbpart;   // [batch][chunk][D]: each chunk's share of ddelta_bias
@@ -224,72 +224,57 @@ __global__ __launch_bounds__(64) void bwd_aggregate_kernel(const BwdK p) {
 }
 
 // ---------------------------------------------------------------- 2. carry
+// One wave per (64 channels, state n): h0 carried forwards and dh_final backwards
+// through the chunk maps, sequential over chunks. Each state is a chain of its own,
+// so 64 / N times more waves are in flight than with a wave per 64 channels; the
+// aggregates of kCarryK chunks are loaded together, so a wave waits for memory once
+// per kCarryK chunks. The entering states are stored n-major, [batch][chunk][n][D],
+// so that each store is one contiguous 256-byte row.
+constexpr int kCarryK = 16;
+
 template <int N>
 __global__ __launch_bounds__(64) void bwd_carry_kernel(const BwdK p) {
-    const int chain = blockIdx.x;
+    const int chain = blockIdx.x, n = blockIdx.y;
     const int b = chain / p.dblocks;
     const int d = (chain % p.dblocks) * 64 + threadIdx.x;
     const bool act = d < p.D;
     const int dc = act ? d : p.D - 1;
-    float Al2[N], h[N];
+    const float al2 = p.A[(int64_t)dc * N + n] * kLog2e;
     const int64_t ci = (int64_t)b * p.D + dc;
-#pragma unroll
-    for (int n = 0; n < N; ++n) {
-        Al2[n] = p.A[(int64_t)dc * N + n] * kLog2e;
-        h[n] = p.h0 ? p.h0[ci * N + n] : 0.0f;
-    }
-    const float *F = p.aggF + (size_t)chain * p.nch * (N + 1) * 64 + threadIdx.x;
-    const float *Rg = p.aggR + (size_t)chain * p.nch * N * 64 + threadIdx.x;
-    // The aggregates of the next chunk are loaded one chunk ahead, before this chunk's
-    // stores: the chain is serial over chunks, and the memory counter completes in
-    // order, so a load issued after a store could not be waited for without the store.
-    // Chunk indices are clamped into the chain (loaded again, not used).
+    const float *F = p.aggF + (size_t)chain * p.nch * (N + 1) * 64 + threadIdx.x;   // [chunk][N + 1][64]
+    const float *Rg = p.aggR + (size_t)chain * p.nch * N * 64 + threadIdx.x;        // [chunk][N][64]
+    const int64_t cstride = (int64_t)N * p.D;                                        // one chunk of hin / uin
+    float *hin = p.hin + ((int64_t)b * p.nch * N + n) * p.D + dc;
+    float *uin = p.uin + ((int64_t)b * p.nch * N + n) * p.D + dc;
     const int last = p.nch - 1;
-    float cur[N + 1], nxt[N + 1];   // end state from zero (n < N), summed step (N)
-    auto load_f = [&](int c, float (&r)[N + 1]) {
-        const float *f = F + (size_t)min(c, last) * (N + 1) * 64;
+    // Forwards, the state entering chunk c (chunk c < last maps h -> exp(A sum dt) h +
+    // S_c), and backwards, the adjoint entering chunk c from the right (chunk c > 0
+    // passes u -> exp(A sum dt) u + Q_c to chunk c - 1): two independent chains,
+    // walked side by side so that their loads and latencies overlap.
+    float h = p.h0 ? p.h0[ci * N + n] : 0.0f;
+    float u = p.dh_final ? p.dh_final[ci * N + n] : 0.0f;
+    for (int c0 = 0; c0 <= last; c0 += kCarryK) {
+        float sv[kCarryK], df[kCarryK], qv[kCarryK], db[kCarryK];
 #pragma unroll
-        for (int n = 0; n <= N; ++n) r[n] = f[n * 64];
-    };
-    load_f(0, cur);
-    for (int c = 0; c < p.nch; ++c) {
-        load_f(c + 1, nxt);
-        float *o = p.hin + (((int64_t)b * p.nch + c) * p.D + dc) * N;
-        if (act) {
-#pragma unroll
-            for (int n = 0; n < N; ++n) o[n] = h[n];
-        }
-        if (c < last) {
-#pragma unroll
-            for (int n = 0; n < N; ++n) h[n] = fmaf(fast_exp2(Al2[n] * cur[N]), h[n], cur[n]);
-        }
-#pragma unroll
-        for (int n = 0; n <= N; ++n) cur[n] = nxt[n];
-    }
-#pragma unroll
-    for (int n = 0; n < N; ++n) h[n] = p.dh_final ? p.dh_final[ci * N + n] : 0.0f;
-    // backwards: chunk c needs its summed step and its adjoint aggregate (c > 0)
-    auto load_r = [&](int c, float (&r)[N + 1]) {
-        const int cc = max(c, 0);
-        const float *q = Rg + (size_t)cc * N * 64;
-#pragma unroll
-        for (int n = 0; n < N; ++n) r[n] = q[n * 64];
-        r[N] = F[(size_t)cc * (N + 1) * 64 + N * 64];
-    };
-    load_r(last, cur);
-    for (int c = last; c >= 0; --c) {
-        load_r(c - 1, nxt);
-        float *o = p.uin + (((int64_t)b * p.nch + c) * p.D + dc) * N;
-        if (act) {
-#pragma unroll
-            for (int n = 0; n < N; ++n) o[n] = h[n];
-        }
-        if (c > 0) {
-#pragma unroll
-            for (int n = 0; n < N; ++n) h[n] = fmaf(fast_exp2(Al2[n] * cur[N]), h[n], cur[n]);
+        for (int k = 0; k < kCarryK; ++k) {
+            const size_t cf = (size_t)min(c0 + k, last);       // clamped: loaded, not used
+            const size_t cb = (size_t)max(last - c0 - k, 0);
+            sv[k] = F[cf * (N + 1) * 64 + n * 64];
+            df[k] = F[cf * (N + 1) * 64 + N * 64];
+            qv[k] = Rg[cb * N * 64 + n * 64];
+            db[k] = F[cb * (N + 1) * 64 + N * 64];
         }
 #pragma unroll
-        for (int n = 0; n <= N; ++n) cur[n] = nxt[n];
+        for (int k = 0; k < kCarryK; ++k) {
+            const int cf = c0 + k, cb = last - c0 - k;
+            if (cf > last) break;                              // uniform
+            if (act) {
+                hin[cf * cstride] = h;
+                uin[cb * cstride] = u;
+            }
+            if (cf < last) h = fmaf(fast_exp2(al2 * df[k]), h, sv[k]);
+            if (cb > 0) u = fmaf(fast_exp2(al2 * db[k]), u, qv[k]);
+        }
     }
 }
 
@@ -488,11 +473,12 @@ __device__ __forceinline__ void bwd_chunk(const BwdK &p, float (*ck)[kSL][64], c
 
     float h[kSL], v[kSL], dA[kSL];
     {
-        const int64_t si = (((int64_t)b * p.nch + c) * p.D + dc) * N + s * kSL;
+        // n-major: each state's row of the wave's channels is contiguous
+        const int64_t si = (((int64_t)b * p.nch + c) * N + s * kSL) * p.D + dc;
 #pragma unroll
         for (int i = 0; i < kSL; ++i) {
-            h[i] = p.hin[si + i];
-            v[i] = p.uin[si + i];
+            h[i] = p.hin[si + (int64_t)i * p.D];
+            v[i] = p.uin[si + (int64_t)i * p.D];
             dA[i] = 0.0f;
         }
     }
@@ -762,7 +748,7 @@ void launch_bwd(const BwdK &k, hipStream_t s) {
     } else {
         hipLaunchKernelGGL((bwd_aggregate_kernel<T, N, false>), dim3(chains, k.nch), dim3(64), 0, s, k);
     }
-    hipLaunchKernelGGL((bwd_carry_kernel<N>), dim3(chains), dim3(64), 0, s, k);
+    hipLaunchKernelGGL((bwd_carry_kernel<N>), dim3(chains, N), dim3(64), 0, s, k);
     const dim3 grid((unsigned)k.nblk, (unsigned)k.nch, (unsigned)k.batch);
     if (k.z) {
         hipLaunchKernelGGL((bwd_main_kernel<T, N, true, true>), grid, dim3(64), 0, s, k);
