@@ -509,7 +509,10 @@ def main():
     ap.add_argument("--headline-only", action="store_true",
                     help="only the headline workload (no other workloads, oracle or copy probe)")
     ap.add_argument("--extra", action="store_true",
-                    help="also time the decode steps, the short convolution and the gradients")
+                    help="(the default) also time the decode steps, the short convolution and the "
+                         "gradients, as the line's \"extra\" object")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the decode, convolution and gradient timings")
     ap.add_argument("--ssd-only", action="store_true",
                     help="time only the Mamba-2 SSD workload and print its own JSON line "
                          "(for profiling the SSD kernels; not the headline line)")
@@ -624,7 +627,7 @@ def main():
             log("S5: oracle for parity")
             line["S5"]["parity"] = parity("S5", (r5["y"], r5["hf"]), r5["inputs"])
         del r5
-    if args.extra:
+    if not (args.no_extra or args.headline_only):
         extra = time_next_rows(max(10, args.steps), 3, torch, ssm)
         extra["bwd_S2"] = time_bwd("S2", max(10, args.steps // 2), 2, torch, ssm)
         extra["bwd_S5"] = time_ssd_bwd(max(10, args.steps // 2), 2, torch, ssm)
