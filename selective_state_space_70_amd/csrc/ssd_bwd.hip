@@ -860,48 +860,81 @@ __global__ __launch_bounds__(kThreads, N > 128 ? 1 : 2) void ssd_bwd_col_kernel(
 }
 
 // ---------------------------------------------------------------- finish
-// One workgroup per (chunk, head, b), one thread per step: da_t = sum over t' >= t
-// in the chunk of (q - dtdd) plus <Gout, S_end>; d dt = dd + A da; dA, d bias.
+// One workgroup per (chunk, 64 heads, b); wave w takes the kFinSeg steps from
+// kFinSeg w of the chunk and lane = head, so every (step, head) array is read and
+// written as contiguous rows. da_t = sum over t' >= t in the chunk of (q - dtdd) plus
+// <Gout, S_end>: each wave sums its steps, the totals of the later waves come through
+// LDS, and each wave then walks its steps backwards. d dt = dd + A da; dA, d bias.
+constexpr int kFinSeg = 16;
+
 template <int Q>
-__global__ __launch_bounds__(Q) void ssd_bwd_finish_kernel(const BwdK k) {
+__global__ __launch_bounds__(Q / kFinSeg * 64) void ssd_bwd_finish_kernel(const BwdK k) {
+    constexpr int NW = Q / kFinSeg;
     const SSDK &p = k.f;
-    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int tl = threadIdx.x, lane = tl & 63, wv = tl >> 6;
-    const int64_t t = (int64_t)c * Q + tl;
-    const bool ok = t < p.L;
-    const int64_t o = ((int64_t)b * p.L + t) * p.H + h;
-    const float r = ok ? k.q[o] - k.dtdd[o] : 0.0f;
-    // inclusive suffix sum over the block (reversed index inside each wave, then
-    // the totals of the later waves)
-    __shared__ float wt[Q / 64];
-    float v = r;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const float u = __shfl_down(v, d, 64);
-        if (lane + d < 64) v += u;
-    }
-    if (lane == 0) wt[wv] = v;
-    __syncthreads();
-    for (int w2 = wv + 1; w2 < Q / 64; ++w2) v += wt[w2];
-    float kcs = 0.0f;                           // <Gout, S_end>: shares in a fixed order
+    const int c = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
+    const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int hh = hg * 64 + lane;
+    const bool hok = hh < p.H;
+    const int h = hok ? hh : p.H - 1;
+    const int64_t t0 = (int64_t)c * Q + kFinSeg * wv;      // this wave's first step
+    const int nt = (int)std::max<int64_t>(0, std::min<int64_t>(kFinSeg, p.L - t0));   // uniform
+    // element of step t0 + j, the step clamped into the sequence (loaded, not used past it)
+    auto at = [&](int j) { return ((int64_t)b * p.L + std::min<int64_t>(t0 + j, p.L - 1)) * p.H + h; };
+    // <Gout, S_end> has kcw shares: wave w adds shares w, w + NW, ... (issued first, so
+    // they overlap the loads below); the waves' parts are added through LDS in order
     const float *kcp = k.kc + (((int64_t)b * p.H + h) * p.nc + c) * k.kcw;
-    for (int w2 = 0; w2 < k.kcw; ++w2) kcs += kcp[w2];
-    const float da = v + kcs;
-    float dtv = 0.0f, dr = 0.0f;
-    if (ok) {
-        const float raw = to_f32(p.dt[o]) + (p.dt_bias ? p.dt_bias[h] : 0.0f);
-        dtv = p.softplus ? softplus_f32(raw) : raw;
-        const float ddt = k.dd[o] + p.A[h] * da;
-        dr = p.softplus ? ddt * sigmoid_f32(raw) : ddt;
-        k.ddt[o] = f32_to_bf16(dr);
+    float kpart = 0.0f;
+    for (int w2 = wv; w2 < k.kcw; w2 += NW) kpart += kcp[w2];
+    float r[kFinSeg], ddv[kFinSeg];
+    uint16_t dtr[kFinSeg];
+#pragma unroll
+    for (int j = 0; j < kFinSeg; ++j) {                    // every load of the wave goes out at once
+        const int64_t o = at(j);
+        r[j] = k.q[o];
+        ddv[j] = k.dtdd[o];
     }
-    __shared__ float red[2][Q / 64];
-    const float sa = wave_sum(ok ? dtv * da : 0.0f), sb2 = wave_sum(dr);
-    if (lane == 0) { red[0][wv] = sa; red[1][wv] = sb2; }
+#pragma unroll
+    for (int j = 0; j < kFinSeg; ++j) {
+        const int64_t o = at(j);
+        dtr[j] = p.dt[o];
+        r[j] = j < nt ? r[j] - ddv[j] : 0.0f;
+        ddv[j] = k.dd[o];
+    }
+    float seg = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kFinSeg; ++j) seg += r[j];
+    __shared__ float segs[NW][64];
+    __shared__ float kps[NW][64];
+    __shared__ float red[2][NW][64];
+    segs[wv][lane] = seg;
+    kps[wv][lane] = kpart;
     __syncthreads();
-    if (tl == 0) {
+    float v = 0.0f;
+    for (int w2 = 0; w2 < NW; ++w2) v += kps[w2][lane];
+    for (int w2 = NW - 1; w2 > wv; --w2) v += segs[w2][lane];
+    const float Ah = p.A[h], bias = p.dt_bias ? p.dt_bias[h] : 0.0f;
+    float sa = 0.0f, sb = 0.0f;
+#pragma unroll
+    for (int j = kFinSeg - 1; j >= 0; --j) {
+        if (j >= nt) continue;                              // uniform
+        v += r[j];                                          // da of step t0 + j
+        const float raw = to_f32(dtr[j]) + bias;
+        const float dtv = p.softplus ? softplus_f32(raw) : raw;
+        const float ddt = ddv[j] + Ah * v;
+        const float dr = p.softplus ? ddt * sigmoid_f32(raw) : ddt;
+        if (hok) k.ddt[at(j)] = f32_to_bf16(dr);
+        sa = fmaf(dtv, v, sa);
+        sb += dr;
+    }
+    red[0][wv][lane] = sa;
+    red[1][wv][lane] = sb;
+    __syncthreads();
+    if (wv == 0 && hok) {
         float a = 0.0f, bsum = 0.0f;
-        for (int w2 = 0; w2 < Q / 64; ++w2) { a += red[0][w2]; bsum += red[1][w2]; }
+        for (int w2 = 0; w2 < NW; ++w2) {
+            a += red[0][w2][lane];
+            bsum += red[1][w2][lane];
+        }
         atomicAdd(k.dA + h, a);
         if (k.dbias) atomicAdd(k.dbias + h, bsum);
     }
@@ -930,8 +963,9 @@ void launch_main(const BwdK &k, bool split, int nrow, int ncol, hipStream_t s) {
         hipLaunchKernelGGL((ssd_bwd_row_kernel<N, Q, false>), dim3((unsigned)nrow), dim3(kThreads), 0, s, k);
         hipLaunchKernelGGL((ssd_bwd_col_kernel<N, Q, false>), dim3((unsigned)ncol), dim3(kThreads), 0, s, k);
     }
-    hipLaunchKernelGGL((ssd_bwd_finish_kernel<Q>), dim3((unsigned)k.f.nc, (unsigned)k.f.H, (unsigned)k.batch),
-                       dim3(Q), 0, s, k);
+    hipLaunchKernelGGL((ssd_bwd_finish_kernel<Q>), dim3((unsigned)k.f.nc, (unsigned)((k.f.H + 63) / 64),
+                                                         (unsigned)k.batch),
+                       dim3(Q / kFinSeg * 64), 0, s, k);
 }
 
 template <int N>
