@@ -11,6 +11,7 @@
 // segment of a row leaves its window behind as the final state.
 #include <algorithm>
 #include <cstdio>
+#include <cstdlib>
 
 #include "device_common.h"
 #include "internal.h"
@@ -185,9 +186,14 @@ ssm_status conv_launch(const ssm_conv_args &a, hipStream_t s, char *err, size_t 
                       aligned16(a.final_state);
     const int V = wide ? vec : 1;
     const int64_t lanes = (a.dim + V - 1) / V;
-    // enough segments along time for ~256K lanes in flight; at least 8 steps each
-    const int64_t want = std::max<int64_t>(1, (262144 + a.batch * lanes - 1) / (a.batch * lanes));
-    const int64_t nseg_max = std::max<int64_t>(1, a.seqlen / 8);
+    // enough segments along time for ~256K lanes in flight, at least 32 steps each (a
+    // segment re-reads K-1 rows of history, and shorter segments made the B8 L2048
+    // D1536 case slower: 35.6 us at 8 steps, 29.8 us at 32)
+    int64_t lanes_target = 262144, min_seg = 32;
+    if (const char *env = std::getenv("SSM_CONV_LANES")) lanes_target = std::max(1L, std::atol(env));   // tuning override
+    if (const char *env = std::getenv("SSM_CONV_MIN_SEG")) min_seg = std::max(1L, std::atol(env));      // tuning override
+    const int64_t want = std::max<int64_t>(1, (lanes_target + a.batch * lanes - 1) / (a.batch * lanes));
+    const int64_t nseg_max = std::max<int64_t>(1, a.seqlen / min_seg);
     int64_t nseg = std::min<int64_t>(std::min<int64_t>(want, nseg_max), 65535);
     const int64_t seg_len = a.seqlen == 0 ? 0 : (a.seqlen + nseg - 1) / nseg;
     nseg = seg_len == 0 ? 1 : (a.seqlen + seg_len - 1) / seg_len;
