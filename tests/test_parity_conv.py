@@ -91,3 +91,18 @@ def test_mamba_130m_layer_shape():
     feeds; every output compared."""
     inp = workloads.conv_inputs(8, 2048, 1536, 4, "bf16", seed=6, with_state=True)
     _check("conv B8 L2048 D1536", inp)
+
+
+@pytest.mark.parametrize("min_seg,lanes", [(1, 1 << 22), (2, 1 << 22), (5, 1 << 20), (64, 1 << 15)])
+def test_segment_plan_overrides(monkeypatch, min_seg, lanes):
+    """The time split is a launch choice only: segments shorter than the window
+    (their history spans earlier segments), ragged last segments and a single
+    long segment give the oracle's result and the same bits as the default plan.
+    SSM_CONV_MIN_SEG / SSM_CONV_LANES are read at every call."""
+    inp = workloads.conv_inputs(3, 203, 136, 4, "bf16", seed=11, with_state=True)
+    y_def, fs_def = _run(inp)
+    monkeypatch.setenv("SSM_CONV_MIN_SEG", str(min_seg))
+    monkeypatch.setenv("SSM_CONV_LANES", str(lanes))
+    _check("conv segments min %d lanes %d" % (min_seg, lanes), inp)
+    y, fs = _run(inp)
+    assert np.array_equal(y, y_def) and np.array_equal(fs, fs_def)
