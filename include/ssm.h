@@ -20,9 +20,18 @@
  *     call returns a non-zero ssm_status and ssm_last_error() describes it.
  *   - Work is enqueued on `stream` (0 = the null stream) and the call returns
  *     without waiting for it. A device fault surfaces on that stream.
- *   - Outputs must not alias inputs or each other. The library keeps no
- *     mutable global state (the error text is thread-local), so concurrent
- *     calls from several host threads are safe if their buffers are disjoint.
+ *   - Outputs must not alias inputs or each other. Apart from the fixed scratch
+ *     array of selective_scan_fwd_noalloc (below), the library keeps no mutable
+ *     global state (the error text is thread-local), so concurrent calls from
+ *     several host threads are safe if their buffers are disjoint.
+ *   - Tuning overrides, read from the environment at every call and meant for
+ *     measurement only: SSM_SCAN_CHUNKS (time chunks of the scan's split, a
+ *     positive integer; it changes the workspace size and the rounding order of
+ *     the result, so query the size under the same setting and keep it fixed
+ *     between selective_scan_chunk_states and selective_scan_apply), SSM_CONV_LANES
+ *     and SSM_CONV_MIN_SEG (lanes in flight and the shortest time segment of
+ *     causal_conv1d_fwd; the result is bit-identical under any setting). Unset,
+ *     the library picks them itself.
  *   - Storage dtype SSM_BF16 means bfloat16 in memory; all arithmetic is fp32,
  *     the recurrent state is fp32, and bf16 outputs are rounded to nearest-even.
  *   - Byte offsets inside one batch row of a (batch, L, ...) tensor must fit in
