@@ -39,8 +39,9 @@ ssm_status scan_launch(const ssm_scan_args &a, const ScanPlan &plan, hipStream_t
 // SSD (scalar A per head) plan: chunk states and the carried state per chunk.
 struct SSDPlan {
     int64_t nchunks;
-    size_t states_offset;   // fp32 [B][nchunks][H][P][N]: chunk states from a zero state
-    size_t sin_offset;      // bf16 [B][nchunks][H][P][N]: state entering each chunk
+    size_t states_offset;   // bf16 [B][nchunks][H][P][N]: chunk states from a zero state
+    size_t sin_offset;      // the same buffer: the state entering each chunk, written
+                            // over the chunk states by the state pass
     size_t decay_offset;    // fp32 [B][H][nchunks]
     size_t gsc_offset;      // fp32 score blocks: [B][nchunks][G][blocks][1024]
     size_t gsc_bytes;

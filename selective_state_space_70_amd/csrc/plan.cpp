@@ -53,7 +53,10 @@ SSDPlan ssd_plan(const ssm_ssd_args &a) {
     pl.nchunks = (a.seqlen + a.chunk - 1) / a.chunk;
     const size_t elems = (size_t)a.batch * pl.nchunks * a.nheads * a.dstate * a.headdim;
     pl.states_offset = 0;
-    pl.sin_offset = up(elems * sizeof(uint16_t));     // bf16 chunk states first
+    // the entering states overwrite the bf16 chunk states in place (the state pass
+    // reads each element before it writes it): one buffer, and a smaller working set
+    // for the output launch that reads x again
+    pl.sin_offset = pl.states_offset;
     pl.decay_offset = pl.sin_offset + up(elems * sizeof(uint16_t));
     pl.gsc_offset = ssd_last_state_offset(a, pl) + up((size_t)a.batch * a.nheads * a.headdim * a.dstate * sizeof(float));
     // 32 x 32 fp32 blocks of C B^T on and below the diagonal of each chunk

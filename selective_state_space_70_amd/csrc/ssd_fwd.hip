@@ -383,17 +383,26 @@ __global__ __launch_bounds__(256) void ssd_state_pass_kernel(const SSDK p, int N
     load_group(0, cur, dcur);
     for (int c0 = 0; c0 < p.nc; c0 += K) {
         load_group(c0 + K, nxt, dnxt);
+        // In the forward the entering states overwrite the chunk states in place
+        // (sin == states16): each thread writes only the elements it read, and
+        // every chunk state of the group is unpacked (its load has returned) before
+        // the first store of the group is issued.
+        f32x4 scv[K];
+#pragma unroll
+        for (int u = 0; u < K; ++u) {
+            if constexpr (S16) {
+                const u32x2 v = cur[u];
+                scv[u] = c0 + u == p.nc - 1 ? last
+                                            : f32x4{bf16_lo(v[0]), bf16_hi(v[0]), bf16_lo(v[1]), bf16_hi(v[1])};
+            } else {
+                scv[u] = cur[u];
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < K; ++u) {
             if (c0 + u < p.nc) {
-                f32x4 sc;
-                if constexpr (S16) {
-                    const u32x2 v = cur[u];
-                    sc = c0 + u == p.nc - 1 ? last
-                                            : f32x4{bf16_lo(v[0]), bf16_hi(v[0]), bf16_lo(v[1]), bf16_hi(v[1])};
-                } else {
-                    sc = cur[u];
-                }
+                const f32x4 sc = scv[u];
                 *(u32x2 *)(p.sin + base + (c0 + u) * cstride) = u32x2{pack_bf16(s[0], s[1]), pack_bf16(s[2], s[3])};
                 if constexpr (!S16) *(f32x4 *)(p.sin32 + base + (c0 + u) * cstride) = s;
 #pragma unroll
