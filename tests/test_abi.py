@@ -190,10 +190,13 @@ def test_workspace_sizes():
     ws = lib.selective_scan_workspace_bytes(ctypes.byref(a))
     chains, chunks = 2048 // 64, 4096 // (2048 // 64)
     assert ws % 256 == 0 and ws >= chains * (chunks - 1) * 17 * 64 * 4
-    # SSD: fp32 chunk states (B * chunks * H * N * P) plus per-chunk decays
+    # SSD: bf16 chunk states (B * chunks * H * N * P; the entering states overwrite
+    # them in place), the last chunk's state in fp32 (B * H * P * N), per-chunk decays
+    # and the score blocks
     s = ssd_args(batch=2, seqlen=8192, nheads=64, dstate=128, chunk=256)
     need = lib.ssd_chunked_workspace_bytes(ctypes.byref(s))
-    assert need >= 2 * 32 * 64 * 128 * 64 * 4
+    assert need >= 2 * 32 * 64 * 128 * 64 * 2 + 2 * 64 * 64 * 128 * 4 + 2 * 64 * 32 * 4
+    assert need < 2 * (2 * 32 * 64 * 128 * 64 * 2)     # one buffer of states, not two
     assert lib.ssd_chunked_workspace_bytes(ctypes.byref(ssd_args(headdim=32))) == 0
 
 
