@@ -1039,7 +1039,12 @@ __global__ __launch_bounds__(Q, Q == 256 ? (N > 128 ? 2 : 3) : 1) void ssd_out_h
                 g2 *= silu_f32(bf16_lo(zz[1]));
                 g3 *= silu_f32(bf16_hi(zz[1]));
             }
-            __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf16(g0, g1), pack_bf16(g2, g3)}, rY, voff, soff, 0);
+            // y is not read again by this call: a non-temporal store (cache policy
+            // bit 2, `nt`) leaves the caches to x and the entering states that later
+            // workgroups still read (S5 call ~206 -> ~199 us)
+            constexpr int kYPolicy = 2;
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf16(g0, g1), pack_bf16(g2, g3)}, rY, voff, soff,
+                                                  kYPolicy);
         }
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // read back before the next tile's writes
     };
