@@ -54,7 +54,9 @@ struct Vec<uint16_t, 8> {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             v[i] = pack_bf16x2(o[2 * i], o[2 * i + 1]);
-        *(u32x4 *)p = v;
+        // y is not read back here: a non-temporal store keeps the caches for the x
+        // rows still to come (B8 L2048 D1536: 29.6 -> 27.7 us)
+        __builtin_nontemporal_store(v, (u32x4 *)p);
     }
 };
 
@@ -68,7 +70,7 @@ struct Vec<float, 4> {
     }
     __device__ __forceinline__ static void load(const float *p, float (&o)[4]) { unpack(load_raw(p), o); }
     __device__ __forceinline__ static void store(float *p, const float (&o)[4]) {
-        *(f32x4 *)p = f32x4{o[0], o[1], o[2], o[3]};
+        __builtin_nontemporal_store(f32x4{o[0], o[1], o[2], o[3]}, (f32x4 *)p);   // as the bf16 store
     }
 };
 
