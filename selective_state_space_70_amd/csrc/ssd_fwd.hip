@@ -861,12 +861,15 @@ __global__ __launch_bounds__(Q, Q == 256 ? (N > 128 ? 2 : 3) : 1) void ssd_out_h
         const int rg = bi / 8, pg = bi % 8;              // 8 lanes read a row's 128 bytes
         const uint32_t voff = (uint32_t)((4 * rg * xstride + pg * 8) * 2);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xr[m][i] = load16s(rX, voff, (uint32_t)(i * xstride * 2));
+        for (int i = 0; i < 4; ++i)   // x's last use in the call: a non-temporal load (cache policy 2)
+            xr[m][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rX, (int)voff,
+                                                                                       (int)(i * xstride * 2), 2));
     }
     const uint16_t *sin_h = p.sin + (((int64_t)b * p.nc + c) * p.H + h) * (int64_t)kP * N;
     u32x4 sr[SV];
 #pragma unroll
-    for (int i = 0; i < SV; ++i) sr[i] = *(const u32x4 *)(sin_h + (tid + i * NTH) * 8);
+    for (int i = 0; i < SV; ++i)   // read once: non-temporal, so the score blocks and C rows keep L2
+        sr[i] = __builtin_nontemporal_load((const u32x4 *)(sin_h + (tid + i * NTH) * 8));
     const rsrc_t rC = make_rsrc_u(p.Cm + (((int64_t)b * p.L + t_base) * p.G + gg) * N, (uint32_t)(T * GN * 2));
     bf16x8 cfa[KN], cfb[KN];
 #pragma unroll
